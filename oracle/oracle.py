@@ -1,0 +1,212 @@
+"""fp64 CPU oracle for the scalar-decay SSM forward pass (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are the only callers. The HIP library never
+imports, links or runs anything in this directory, and this directory imports
+nothing from the HIP library.
+
+The oracle is the plain definition of the layer, run token by token in fp64:
+
+    h_t = a_t h_{t-1} + B_t x_t^T,    y_t = C_t^T h_t,    a_t = exp(log_a_t)
+
+("Transformers are SSMs" paper card, wikillm.com/papers/2405.21060: Method 1,
+selective SSM as a matrix, paper sections 2-3; Method 2, scalar-identity case,
+paper section 5.1). The chunked SSD algorithm (paper card Method 5, paper
+section 6) is an exact rewrite of this recurrence, so the recurrence is the
+reference and not an approximation of it.
+
+Helpers here that are not the recurrence:
+  * ``chunk_segments`` -- the chunk grid used to read intermediate results
+    (chunks restart at every sequence start; the last chunk of a sequence may
+    be short).
+  * ``chunk_cumsum`` -- the cumulative log decay restarted in every chunk
+    (paper card Method 5 pseudocode, "decay_cumsum"), a plain fp64 cumsum.
+
+Every function in this file is pinned by ``tests/test_oracle.py`` against the
+quadratic dual form, closed forms, causal linear attention, packing,
+continuation and invariants; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+_lib = None
+
+# Mutant codes (see ssd_oracle.c); used only by the pin-strength tests.
+MUTANTS = {
+    "decay_after_input": 1,
+    "output_before_update": 2,
+    "swap_b_c": 3,
+    "decay_sign": 4,
+    "no_decay": 5,
+    "group_mod": 6,
+    "decay_next_token": 7,
+    "state_transpose": 8,
+}
+
+
+def build(force: bool = True) -> str:
+    """Compile ssd_oracle.c with gcc (fp64, OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-Wall", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.ssd_oracle_scan.restype = ctypes.c_int
+        lib.ssd_oracle_scan.argtypes = [ctypes.c_int] * 6 + [dp] * 4 + [ctypes.c_int, ip, dp, dp, dp, ip, dp,
+                                                                       ctypes.c_int, ctypes.c_int]
+        lib.ssd_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().ssd_oracle_max_threads())
+
+
+def _dptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _iptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def sequence_segments(rows: int, T: int, cu_seqlens: Optional[Sequence[int]] = None):
+    """(row, begin, end) triples of the independent sequences.
+
+    Without cu_seqlens every row is one sequence [0, T). With cu_seqlens (one
+    packed row) sequence s is [cu[s], cu[s+1]) of row 0 and starts from a zero
+    state: a packed batch behaves as separate runs (the pages' variable-length
+    training without padding, read as a reset at every boundary).
+    """
+    if cu_seqlens is None:
+        return [(r, 0, T) for r in range(rows)]
+    cu = [int(v) for v in cu_seqlens]
+    if rows != 1:
+        raise ValueError("packed sequences need a single row")
+    return [(0, cu[s], cu[s + 1]) for s in range(len(cu) - 1)]
+
+
+def chunk_segments(rows: int, T: int, Q: int, cu_seqlens: Optional[Sequence[int]] = None):
+    """Chunk grid: every sequence cut into chunks of Q tokens from its start.
+
+    Returns (row, begin, end) per chunk in sequence order, chunk order. The
+    last chunk of a sequence holds the remainder (paper card Method 5 cuts
+    the sequence into T/Q blocks; a short last chunk is the reading for
+    lengths that Q does not divide).
+    """
+    out = []
+    for (r, b, e) in sequence_segments(rows, T, cu_seqlens):
+        t = b
+        while t < e:
+            out.append((r, t, min(t + Q, e)))
+            t += Q
+    return out
+
+
+def scan(X, la, B, C, segments: Optional[Iterable] = None, init=None, want_y: bool = True,
+         want_final: bool = True, snap_slot=None, nsnaps: int = 0, threads: int = 0,
+         mutant: int = 0):
+    """Run the fp64 recurrence.
+
+    X [rows,T,H,P], la [rows,T,H], B and C [rows,T,G,N] (any float dtype; upcast
+    to fp64 exactly). ``segments`` defaults to one segment per row. ``init``
+    [nseg,H,P,N] is the starting state of each segment (zero when None).
+    Returns (Y [rows,T,H,P] or None, final [nseg,H,P,N] or None, snaps or None).
+    """
+    X = _f64(X)
+    la = _f64(la)
+    B = _f64(B)
+    C = _f64(C)
+    rows, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    if la.shape != (rows, T, H) or B.shape != (rows, T, G, N) or C.shape != B.shape:
+        raise ValueError("shape mismatch")
+    if segments is None:
+        segments = [(r, 0, T) for r in range(rows)]
+    seg = np.ascontiguousarray(np.asarray(list(segments), dtype=np.int32).reshape(-1, 3))
+    nseg = seg.shape[0]
+    Y = np.zeros((rows, T, H, P), np.float64) if want_y else None
+    fin = np.zeros((nseg, H, P, N), np.float64) if want_final else None
+    ini = None
+    if init is not None:
+        ini = _f64(init)
+        if ini.shape != (nseg, H, P, N):
+            raise ValueError("init must be [nseg,H,P,N]")
+    ss = None
+    snaps = None
+    if snap_slot is not None:
+        ss = np.ascontiguousarray(np.asarray(snap_slot, dtype=np.int32).reshape(rows * T))
+        snaps = np.zeros((max(nsnaps, 1), H, P, N), np.float64)
+    rc = _load().ssd_oracle_scan(rows, T, H, G, P, N, _dptr(X), _dptr(la), _dptr(B), _dptr(C), nseg,
+                                 _iptr(seg), _dptr(ini), _dptr(Y), _dptr(fin), _iptr(ss), _dptr(snaps),
+                                 int(threads), int(mutant))
+    if rc != 0:
+        raise ValueError("ssd_oracle_scan rejected its arguments")
+    return Y, fin, snaps
+
+
+def forward(X, la, B, C, cu_seqlens=None, threads: int = 0, mutant: int = 0):
+    """Y and final states of the layer from zero initial states.
+
+    final is [rows,H,P,N] without cu_seqlens and [S,H,P,N] with it.
+    """
+    X = _f64(X)
+    rows, T = X.shape[0], X.shape[1]
+    segs = sequence_segments(rows, T, cu_seqlens)
+    Y, fin, _ = scan(X, la, B, C, segments=segs, threads=threads, mutant=mutant)
+    return Y, fin
+
+
+def step(state, x, la, B, C):
+    """One recurrent step (the loop body of the recurrence) from ``state``.
+
+    state [b,H,P,N], x [b,H,P], la [b,H], B and C [b,G,N]. Returns (y [b,H,P],
+    new_state [b,H,P,N]); y is read from the updated state.
+    """
+    x = _f64(x)
+    b, H, P = x.shape
+    Y, fin, _ = scan(x[:, None], _f64(la)[:, None], _f64(B)[:, None], _f64(C)[:, None],
+                     segments=[(r, 0, 1) for r in range(b)], init=_f64(state))
+    return Y[:, 0], fin
+
+
+def chunk_cumsum(la, segments) -> np.ndarray:
+    """Cumulative log decay restarted at the start of every segment (fp64).
+
+    Same layout as la [rows,T,H]; tokens outside every segment are 0.
+    """
+    la = _f64(la)
+    out = np.zeros_like(la)
+    for (r, b, e) in segments:
+        out[r, b:e] = np.cumsum(la[r, b:e], axis=0)
+    return out

@@ -1,0 +1,303 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Every check here compares the oracle's token-by-token recurrence with
+something other than itself: hand-worked examples, the brute-force quadratic
+dual form, the chunked block decomposition at many chunk lengths, scalar closed
+forms, causal linear attention, packing/reset, continuation and invariants.
+``test_mutants_are_caught`` plants plausible mistakes in the oracle (on the CPU)
+and shows that each one fails at least one pin.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import oracle
+from ssd_forms import chunked_form, dual_form
+from ssd_chunked_scan_fwd_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _rand(T, H, P, N, G=1, seed=0, rows=1, la_scale=1.0):
+    d = synth.make_forward_inputs(rows, T, H, P, N, G, dtype=__import__("torch").float32, seed=seed)
+    X = d["X"].double().numpy()
+    la = d["log_a"].double().numpy() * la_scale
+    B = d["B"].double().numpy()
+    C = d["C"].double().numpy()
+    return X, la, B, C
+
+
+def _relmax(a, b):
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return np.max(np.abs(a - b)) / scale
+
+
+# ---------------------------------------------------------------- hand worked
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_hand_worked(case):
+    x = np.array(case["x"])[None]
+    a = np.array(case["a"])
+    with np.errstate(divide="ignore"):
+        la = np.log(a)[None]
+    B = np.array(case["B"])[None]
+    C = np.array(case["C"])[None]
+    Y, fin = oracle.forward(x, la, B, C)
+    np.testing.assert_allclose(Y[0], np.array(case["y"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(fin[0], np.array(case["final"]), rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------- dual form
+
+@settings(max_examples=25, deadline=None)
+@given(T=st.integers(1, 24), H=st.integers(1, 3), P=st.integers(1, 5), N=st.integers(1, 5),
+       gsel=st.integers(0, 2), seed=st.integers(0, 2 ** 31 - 1))
+def test_dual_form_bruteforce(T, H, P, N, gsel, seed):
+    G = [1, H, 1 if H % 2 else max(H // 2, 1)][gsel]
+    X, la, B, C = _rand(T, H, P, N, G, seed)
+    Y, fin = oracle.forward(X, la, B, C)
+    Yd, fd = dual_form(X[0], la[0], B[0], C[0])
+    assert _relmax(Y[0], Yd) <= 1e-12
+    assert _relmax(fin[0], fd) <= 1e-12
+
+
+def test_dual_form_multi_group():
+    # G = 2 groups of 2 heads: head h reads group h // 2
+    X, la, B, C = _rand(40, 4, 3, 4, G=2, seed=11)
+    Y, fin = oracle.forward(X, la, B, C)
+    Yd, fd = dual_form(X[0], la[0], B[0], C[0])
+    assert _relmax(Y[0], Yd) <= 1e-12
+    assert _relmax(fin[0], fd) <= 1e-12
+
+
+# ---------------------------------------------------------------- chunked form
+
+@pytest.mark.parametrize("Q", [1, 2, 3, 5, 16, 64])
+def test_chunked_form_every_chunk_length(Q):
+    T = 64
+    X, la, B, C = _rand(T, 3, 4, 6, seed=5)
+    Y, fin = oracle.forward(X, la, B, C)
+    Yc, fc, _, _ = chunked_form(X[0], la[0], B[0], C[0], Q)
+    assert _relmax(Y[0], Yc) <= 1e-12
+    assert _relmax(fin[0], fc) <= 1e-12
+
+
+def test_chunked_intermediates_match_oracle_snapshots():
+    """Chunk states = oracle restarted per chunk; start states = oracle state at chunk ends."""
+    T, Q, H, P, N = 50, 16, 2, 3, 4
+    X, la, B, C = _rand(T, H, P, N, seed=9)
+    _, _, starts, chunk_states = chunked_form(X[0], la[0], B[0], C[0], Q)
+    segs = oracle.chunk_segments(1, T, Q)
+    _, fin_restart, _ = oracle.scan(X, la, B, C, segments=segs, want_y=False)
+    assert _relmax(fin_restart, chunk_states) <= 1e-12
+    snap = -np.ones(T, np.int32)
+    for k, (_, b, e) in enumerate(segs[:-1]):
+        snap[e - 1] = k + 1
+    _, _, snaps = oracle.scan(X, la, B, C, want_y=False, snap_slot=snap, nsnaps=len(segs))
+    assert np.all(snaps[0] == 0)
+    assert _relmax(snaps[1:], starts[1:]) <= 1e-12
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("a", [0.3, 0.9, 0.999])
+def test_scalar_geometric_closed_form(a):
+    T = 200
+    x = np.ones((1, T, 1, 1))
+    la = np.full((1, T, 1), math.log(a))
+    one = np.ones((1, T, 1, 1))
+    Y, fin = oracle.forward(x, la, one, one)
+    t = np.arange(T)
+    expect = (1 - a ** (t + 1)) / (1 - a)
+    np.testing.assert_allclose(Y[0, :, 0, 0], expect, rtol=1e-13)
+    assert abs(fin[0, 0, 0, 0] - expect[-1]) <= 1e-13 * expect[-1]
+
+
+def test_scalar_no_decay_counts():
+    T = 300
+    one = np.ones((1, T, 1, 1))
+    Y, _ = oracle.forward(one, np.zeros((1, T, 1)), one, one)
+    np.testing.assert_array_equal(Y[0, :, 0, 0], np.arange(1, T + 1))
+
+
+def test_scalar_full_reset_passes_input():
+    T = 50
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((1, T, 1, 1))
+    one = np.ones((1, T, 1, 1))
+    Y, _ = oracle.forward(x, np.full((1, T, 1), -np.inf), one, one)
+    np.testing.assert_array_equal(Y, x)
+
+
+def test_scalar_recurrence_random_decays():
+    T = 100
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((1, T, 1, 1))
+    la = -rng.uniform(0, 2, (1, T, 1))
+    one = np.ones((1, T, 1, 1))
+    Y, _ = oracle.forward(x, la, one, one)
+    y = 0.0
+    for t in range(T):  # y_t = a_t y_{t-1} + x_t (1-SS multiplication)
+        y = math.exp(la[0, t, 0]) * y + x[0, t, 0, 0]
+        assert abs(Y[0, t, 0, 0] - y) <= 1e-13 * max(1.0, abs(y))
+
+
+# ---------------------------------------------------------------- linear attention
+
+def test_causal_linear_attention():
+    T, H, P, N = 37, 2, 5, 7
+    X, la, B, C = _rand(T, H, P, N, seed=21)
+    la[:] = 0.0
+    Y, _ = oracle.forward(X, la, B, C)
+    for h in range(H):
+        A = np.tril(C[0, :, 0, :] @ B[0, :, 0, :].T)
+        assert _relmax(Y[0, :, h, :], A @ X[0, :, h, :]) <= 1e-12
+
+
+# ---------------------------------------------------------------- packing / resets
+
+def test_packing_equals_separate_runs_and_resets():
+    lengths = [5, 17, 1, 9, 32]
+    T = sum(lengths)
+    H, P, N = 3, 4, 5
+    X, la, B, C = _rand(T, H, P, N, seed=8)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    Y, fin = oracle.forward(X, la, B, C, cu_seqlens=cu)
+    for s in range(len(lengths)):
+        b, e = cu[s], cu[s + 1]
+        Ys, fs = oracle.forward(X[:, b:e], la[:, b:e], B[:, b:e], C[:, b:e])
+        np.testing.assert_array_equal(Y[0, b:e], Ys[0])
+        np.testing.assert_array_equal(fin[s], fs[0])
+    # an unpacked run with a = 0 at every sequence start gives the same result
+    la_reset = la.copy()
+    la_reset[0, cu[1:-1]] = -np.inf
+    Yr, fr = oracle.forward(X, la_reset, B, C)
+    np.testing.assert_array_equal(Yr, Y)
+    np.testing.assert_array_equal(fr[0], fin[-1])
+
+
+def test_rows_are_independent():
+    X, la, B, C = _rand(20, 2, 3, 4, seed=12, rows=3)
+    Y, fin = oracle.forward(X, la, B, C)
+    for r in range(3):
+        Yr, fr = oracle.forward(X[r:r + 1], la[r:r + 1], B[r:r + 1], C[r:r + 1])
+        np.testing.assert_array_equal(Y[r], Yr[0])
+        np.testing.assert_array_equal(fin[r], fr[0])
+
+
+# ---------------------------------------------------------------- continuation / step
+
+def test_continuation_from_state():
+    T, T1 = 60, 23
+    X, la, B, C = _rand(T, 2, 4, 6, seed=13)
+    Y, fin = oracle.forward(X, la, B, C)
+    Y1, f1 = oracle.forward(X[:, :T1], la[:, :T1], B[:, :T1], C[:, :T1])
+    Y2, f2, _ = oracle.scan(X[:, T1:], la[:, T1:], B[:, T1:], C[:, T1:], init=f1)
+    np.testing.assert_array_equal(Y[0, :T1], Y1[0])
+    np.testing.assert_array_equal(Y[0, T1:], Y2[0])
+    np.testing.assert_array_equal(fin, f2)
+
+
+def test_step_matches_scan():
+    T = 12
+    X, la, B, C = _rand(T, 2, 3, 4, seed=14, rows=2)
+    Y, fin = oracle.forward(X, la, B, C)
+    state = np.zeros((2, 2, 3, 4))
+    for t in range(T):
+        y, state = oracle.step(state, X[:, t], la[:, t], B[:, t], C[:, t])
+        np.testing.assert_array_equal(y, Y[:, t])
+    np.testing.assert_array_equal(state, fin)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_linearity_in_x():
+    X, la, B, C = _rand(33, 2, 3, 4, seed=15)
+    X2, _, _, _ = _rand(33, 2, 3, 4, seed=16)
+    Y1, f1 = oracle.forward(X, la, B, C)
+    Y2, f2 = oracle.forward(X2, la, B, C)
+    Y3, f3 = oracle.forward(2.5 * X - 0.75 * X2, la, B, C)
+    assert _relmax(Y3, 2.5 * Y1 - 0.75 * Y2) <= 1e-12
+    assert _relmax(f3, 2.5 * f1 - 0.75 * f2) <= 1e-12
+
+
+def test_head_permutation_equivariance():
+    H = 5
+    X, la, B, C = _rand(29, H, 3, 4, seed=17)
+    perm = np.array([3, 0, 4, 1, 2])
+    Y, fin = oracle.forward(X, la, B, C)
+    Yp, fp = oracle.forward(X[:, :, perm], la[:, :, perm], B, C)
+    np.testing.assert_array_equal(Yp, Y[:, :, perm])
+    np.testing.assert_array_equal(fp, fin[:, perm])
+
+
+def test_gauge_b_scaled_c_unscaled():
+    X, la, B, C = _rand(31, 2, 3, 4, seed=18)
+    alpha = 3.0
+    Y, fin = oracle.forward(X, la, B, C)
+    Yg, fg = oracle.forward(X, la, alpha * B, C / alpha)
+    assert _relmax(Yg, Y) <= 1e-12
+    assert _relmax(fg, alpha * fin) <= 1e-12
+
+
+# ---------------------------------------------------------------- helpers
+
+def test_chunk_segments_cover_sequences():
+    cu = [0, 5, 300, 301, 517]
+    segs = oracle.chunk_segments(1, 517, 128, cu)
+    covered = np.zeros(517, int)
+    for (r, b, e) in segs:
+        assert r == 0 and 0 < e - b <= 128
+        covered[b:e] += 1
+        s = np.searchsorted(cu, b, side="right") - 1
+        assert e <= cu[s + 1] and (b - cu[s]) % 128 == 0
+    assert np.all(covered == 1)
+    assert len(segs) == sum(-(-(cu[i + 1] - cu[i]) // 128) for i in range(4))
+
+
+def test_chunk_cumsum_restarts():
+    la = -np.arange(1, 11, dtype=np.float64).reshape(1, 10, 1)
+    cs = oracle.chunk_cumsum(la, oracle.chunk_segments(1, 10, 4))
+    np.testing.assert_array_equal(cs[0, :, 0], [-1, -3, -6, -10, -5, -11, -18, -26, -9, -19])
+
+
+# ---------------------------------------------------------------- pin strength
+
+def _pins(mutant):
+    """Run the pins against a (possibly mutated) oracle; returns the names that fail."""
+    failed = []
+    m = mutant
+
+    def fwd(X, la, B, C, **kw):
+        return oracle.forward(X, la, B, C, mutant=m, **kw)
+
+    # hand-worked
+    for case in _golden_cases():
+        x = np.array(case["x"])[None]
+        with np.errstate(divide="ignore"):
+            la = np.log(np.array(case["a"]))[None]
+        Y, fin = fwd(x, la, np.array(case["B"])[None], np.array(case["C"])[None])
+        if not (np.allclose(Y[0], case["y"], atol=1e-12) and np.allclose(fin[0], case["final"], atol=1e-12)):
+            failed.append("hand:" + case["name"])
+    # dual form, including two groups of heads, P == N
+    X, la, B, C = _rand(17, 4, 4, 4, G=2, seed=99)
+    Y, fin = fwd(X, la, B, C)
+    Yd, fd = dual_form(X[0], la[0], B[0], C[0])
+    if _relmax(Y[0], Yd) > 1e-12 or _relmax(fin[0], fd) > 1e-12:
+        failed.append("dual")
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(oracle.MUTANTS))
+def test_mutants_are_caught(name):
+    assert _pins(0) == []
+    assert _pins(oracle.MUTANTS[name]), f"mutant {name} passed every pin"
