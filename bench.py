@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X chunked SSD forward pass (one GPU).
+
+One step = one ssd_fwd call (chunk_cumsum -> chunk_state -> state_passing ->
+chunk_scan) over the long-sequence workload: batch 1, T = 16384 tokens, H = 32
+heads, P = 64, N = 128, one B/C group, chunk Q = 128, bf16 inputs with fp32
+accumulation; inputs are seeded synthetic and resident in HBM before timing.
+
+Prints ONE JSON line with the headline throughput (tokens/s), the roofline of
+the dominant kernel (its algorithmic bytes / its average launch time, timed with
+HIP events on the launch stream), per-stage times, the decode-step throughput,
+and the fp64 CPU oracle timed on this host as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "SSD fwd tokens/s & % of bf16 MFMA peak at T=16K, H=32, P=64, N=128"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def stage_bytes(w, nslots: int, nseq: int) -> dict:
+    """Algorithmic HBM bytes of one launch of each stage (each tensor counted once)."""
+    esz = 2 if w.dtype == "bf16" else 4
+    tok = w.batch * w.T
+    X = tok * w.H * w.P * esz
+    BC = tok * w.G * w.N * esz
+    la = tok * w.H * 4
+    cs = nslots * w.H * w.Q * 4
+    table = nslots * 16
+    states = nslots * w.H * w.P * w.N * 4
+    starts = nslots * w.H * w.P * w.N * esz
+    final = nseq * w.H * w.P * w.N * 4
+    decay = nslots * w.H * 4
+    return {
+        "chunk_cumsum": la + cs + table,
+        "chunk_state": X + BC + cs + table + states,
+        "state_passing": states + decay + starts + final,
+        "chunk_scan": X + 2 * BC + cs + table + starts + X,   # X read, Y written
+    }
+
+
+def useful_flops(w, chunk_lengths) -> float:
+    """Useful flops of the forward pass with causal triangles counted exactly.
+
+    Per chunk of q tokens: C B^T lower triangle G*q(q+1)*N, (L o S) X H*q(q+1)*P,
+    right and left factors 4*H*q*P*N, centre factor 2*H*P*N.
+    """
+    f = 0.0
+    for q in chunk_lengths:
+        f += w.G * q * (q + 1) * w.N + w.H * q * (q + 1) * w.P + 4 * w.H * q * w.P * w.N + 2 * w.H * w.P * w.N
+    return f
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=4096)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the SSD forward path has no multi-GPU mode "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import ssd_chunked_scan_fwd_amd as ssd
+    from ssd_chunked_scan_fwd_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    ssd.lib()  # fail loudly when the HIP library is missing
+
+    w = synth.WORKLOADS[synth.HEADLINE]
+    log(f"[bench] workload {w.name}: generating inputs")
+    d = synth.workload_inputs(w)
+    X, la, B, C = (d[k].to(dev) for k in ("X", "log_a", "B", "C"))
+    shape = ssd.make_shape(X, B, None)
+    ws = ssd.Workspace(shape, w.Q, dev)
+    Y = torch.empty_like(X)
+    fin = torch.empty(w.batch, w.H, w.P, w.N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssd.fwd(X, la, B, C, chunk=w.Q, Y=Y, final_state=fin, workspace=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    ms_per_step = wall_ms
+    tokens = w.batch * w.T
+    value = tokens / (ms_per_step * 1e-3)
+
+    # per-stage average launch time, HIP events on the launch stream
+    log(f"[bench] per-stage timing, {args.stage_reps} reps")
+    stages = [
+        ("chunk_cumsum", lambda: ssd.chunk_cumsum(la, None, w.Q, shape, ws)),
+        ("chunk_state", lambda: ssd.chunk_state(X, B, None, w.Q, shape, ws)),
+        ("state_passing", lambda: ssd.state_passing(None, w.Q, fin, shape, ws)),
+        ("chunk_scan", lambda: ssd.chunk_scan(X, B, C, None, w.Q, Y, shape, ws)),
+    ]
+    acc = {name: 0.0 for name, _ in stages}
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
+    for _ in range(args.stage_reps):
+        for (name, fn), (a, b) in zip(stages, evs):
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        for (name, _), (a, b) in zip(stages, evs):
+            acc[name] += a.elapsed_time(b)
+    stage_us = {k: v * 1e3 / args.stage_reps for k, v in acc.items()}
+    nslots = ws.layout.nslots
+    sbytes = stage_bytes(w, nslots, w.batch)
+    dominant = max(stage_us, key=stage_us.get)
+    achieved = sbytes[dominant] / (stage_us[dominant] * 1e-6) / 1e9
+    chunk_lengths = [min(w.Q, w.T - k * w.Q) for k in range(-(-w.T // w.Q))] * w.batch
+    flops = useful_flops(w, chunk_lengths)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    compulsory = (tokens * w.H * w.P * 2 * 2 + tokens * w.G * w.N * 2 * 2 + tokens * w.H * 4 +
+                  w.batch * w.H * w.P * w.N * 4)
+    pipeline_bytes = sum(sbytes.values())
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded: X~N(0,1), log_a=-dt*A, dt~U(0.001,0.1), A~U(1,16), B,C~N(0,1)/sqrt(N))",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.T, "heads": w.H, "headdim": w.P,
+                   "dstate": w.N, "ngroups": w.G, "chunk": w.Q, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": sbytes[dominant], "avg_launch_us": round(stage_us[dominant], 3)},
+        "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "stage_bytes": sbytes,
+        "stage_gbs": {k: round(sbytes[k] / (stage_us[k] * 1e-6) / 1e9, 1) for k in stage_us},
+        "event_ms_per_step": round(ev_ms, 5),
+        "useful_tflops": round(tflops, 2),
+        "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
+        "compulsory_bytes": compulsory,
+        "compulsory_hbm_frac": round(compulsory / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "pipeline_bytes": pipeline_bytes,
+        "pipeline_hbm_frac": round(pipeline_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+    if not args.no_decode:
+        wd = synth.WORKLOADS["decode-b64-H80-N128"]
+        nsteps = min(args.decode_steps, wd.steps)
+        log(f"[bench] decode {wd.name}: {nsteps} steps")
+        dd = synth.make_decode_inputs(wd.batch, nsteps, wd.H, wd.P, wd.N, wd.G, wd.torch_dtype, wd.seed)
+        xs, las, Bs, Cs = (dd[k].to(dev) for k in ("x", "log_a", "B", "C"))
+        state = torch.zeros(wd.batch, wd.H, wd.P, wd.N, dtype=torch.float32, device=dev)
+        y = torch.empty(wd.batch, wd.H, wd.P, dtype=xs.dtype, device=dev)
+        for t in range(min(16, nsteps)):
+            ssd.step(state, xs[t], las[t], Bs[t], Cs[t], y=y)
+        state.zero_()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for t in range(nsteps):
+            ssd.step(state, xs[t], las[t], Bs[t], Cs[t], y=y)
+        b.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = a.elapsed_time(b)
+        per_step_bytes = wd.batch * wd.H * wd.P * wd.N * 4 * 2 + wd.batch * wd.H * (wd.P * 2 * 2 + 4) + \
+            wd.batch * wd.G * wd.N * 2 * 2
+        out["decode"] = {"workload": wd.name, "steps": nsteps, "ms": round(dec_ms, 3),
+                         "tokens_per_s": round(wd.batch * nsteps / (dec_ms * 1e-3), 1),
+                         "us_per_step": round(dec_ms * 1e3 / nsteps, 3),
+                         "gbs_per_step": round(per_step_bytes / (dec_ms * 1e-3 / nsteps) / 1e9, 1)}
+        del xs, las, Bs, Cs, state
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        cores = len(os.sched_getaffinity(0))
+        threads = min(cores, w.batch * w.H)
+        log(f"[bench] cpu baseline: fp64 oracle, full workload, {threads} threads")
+        Xd, lad, Bd, Cd = (d[k].double().numpy() for k in ("X", "log_a", "B", "C"))
+        c0 = time.perf_counter()
+        oracle.scan(Xd, lad, Bd, Cd, threads=threads)
+        c1 = time.perf_counter()
+        out["cpu_baseline"] = {"value": round(tokens / (c1 - c0), 1), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"whole {w.name} workload ({tokens} tokens x {w.H} heads), one run, "
+                                         f"{c1 - c0:.2f} s; fp64 token-by-token recurrence, OpenMP over "
+                                         f"(row, head) pairs"}
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,10 +1,13 @@
 """MI355X-native chunked SSD forward pass (the Mamba-2 layer's scan).
 
 The compute path is a C-ABI shared library of hand-written HIP kernels for
-gfx950 (``libssd_mi355x.so``, built in-tree); this package is a thin ctypes
-binding over it. Importing the package does not load the library: the first
-call does, and it raises if the library is missing.
+gfx950 (``libssd_mi355x.so``, built in-tree by ``build.py``); ``binding`` is a
+thin ctypes layer over it. Importing the package does not load the library:
+the first call does, and it raises if the library is missing.
 """
 from . import synth  # noqa: F401
+from .binding import (SSDError, Shape, Workspace, chunk_cumsum, chunk_scan, chunk_state, fwd,  # noqa: F401
+                      layout, lib, make_shape, state_passing, step, workspace_bytes)
 
-__all__ = ["synth"]
+__all__ = ["synth", "fwd", "step", "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "Workspace",
+           "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib"]

@@ -1,0 +1,231 @@
+"""ctypes binding of libssd_mi355x.so (the C ABI in include/ssd.h).
+
+Argument marshalling only: every step of the forward pass and of the decode
+step runs in the library's HIP kernels. torch provides device memory and the
+current stream. The library is loaded on first use; a missing library raises
+(there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_NAME = "libssd_mi355x.so"
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+_lib = None
+
+SSD_OK = 0
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARGUMENT", 2: "SSD_ERR_UNSUPPORTED",
+          3: "SSD_ERR_WORKSPACE_TOO_SMALL", 4: "SSD_ERR_HIP"}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+# Every symbol include/ssd.h declares.
+EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_fwd_layout", "ssd_fwd_workspace_bytes", "ssd_fwd",
+           "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_step")
+
+
+class SSDError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} returned {STATUS.get(status, status)}")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("nheads", ctypes.c_int32),
+                ("ngroups", ctypes.c_int32), ("headdim", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("slots_per_row", ctypes.c_int64), ("nslots", ctypes.c_int64), ("table_offset", ctypes.c_size_t),
+                ("cumsum_offset", ctypes.c_size_t), ("chunk_states_offset", ctypes.c_size_t),
+                ("start_states_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded library; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_NAME} is not built (python -m ssd_chunked_scan_fwd_amd.build)")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        shp = ctypes.POINTER(Shape)
+        L.ssd_abi_version.restype = i32
+        L.ssd_abi_version.argtypes = []
+        L.ssd_status_string.restype = ctypes.c_char_p
+        L.ssd_status_string.argtypes = [ctypes.c_int]
+        L.ssd_fwd_layout.restype = ctypes.c_int
+        L.ssd_fwd_layout.argtypes = [shp, i32, ctypes.POINTER(Layout)]
+        L.ssd_fwd_workspace_bytes.restype = ctypes.c_int
+        L.ssd_fwd_workspace_bytes.argtypes = [shp, i32, ctypes.POINTER(sz)]
+        L.ssd_fwd.restype = ctypes.c_int
+        L.ssd_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, shp, vp, sz, vp]
+        L.ssd_chunk_cumsum.restype = ctypes.c_int
+        L.ssd_chunk_cumsum.argtypes = [vp, vp, i32, shp, vp, sz, vp]
+        L.ssd_chunk_state.restype = ctypes.c_int
+        L.ssd_chunk_state.argtypes = [vp, vp, vp, i32, shp, vp, sz, vp]
+        L.ssd_state_passing.restype = ctypes.c_int
+        L.ssd_state_passing.argtypes = [vp, i32, vp, shp, vp, sz, vp]
+        L.ssd_chunk_scan.restype = ctypes.c_int
+        L.ssd_chunk_scan.argtypes = [vp, vp, vp, vp, i32, vp, shp, vp, sz, vp]
+        L.ssd_step.restype = ctypes.c_int
+        L.ssd_step.argtypes = [vp, vp, vp, vp, vp, vp, shp, vp]
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    if dt == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _call(fn: str, *args):
+    st = getattr(lib(), fn)(*args)
+    if st != SSD_OK:
+        raise SSDError(fn, st)
+
+
+def make_shape(X: torch.Tensor, B: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None) -> Shape:
+    b, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    S = 0 if cu_seqlens is None else cu_seqlens.numel() - 1
+    return Shape(b, T, H, G, P, N, S, _dtype_code(X.dtype))
+
+
+def layout(shape: Shape, chunk: int) -> Layout:
+    L = Layout()
+    _call("ssd_fwd_layout", ctypes.byref(shape), int(chunk), ctypes.byref(L))
+    return L
+
+
+def workspace_bytes(shape: Shape, chunk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _call("ssd_fwd_workspace_bytes", ctypes.byref(shape), int(chunk), ctypes.byref(n))
+    return int(n.value)
+
+
+class Workspace:
+    """A caller-owned workspace for one shape and chunk length, with typed views
+    of the stages' intermediate results (for inspection and tests)."""
+
+    def __init__(self, shape: Shape, chunk: int, device):
+        self.shape = shape
+        self.chunk = int(chunk)
+        self.layout = layout(shape, chunk)
+        self.buffer = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=device)
+
+    @property
+    def nbytes(self) -> int:
+        return self.buffer.numel()
+
+    def _view(self, off: int, count: int, dtype: torch.dtype, shape):
+        esz = torch.empty((), dtype=dtype).element_size()
+        return self.buffer[off:off + count * esz].view(dtype).view(*shape)
+
+    def table(self) -> torch.Tensor:
+        n = self.layout.nslots
+        return self._view(self.layout.table_offset, n * 4, torch.int32, (n, 4))
+
+    def cumsum(self) -> torch.Tensor:
+        s, n = self.shape, self.layout.nslots
+        return self._view(self.layout.cumsum_offset, n * s.nheads * self.chunk, torch.float32,
+                          (n, s.nheads, self.chunk))
+
+    def chunk_states(self) -> torch.Tensor:
+        s, n = self.shape, self.layout.nslots
+        return self._view(self.layout.chunk_states_offset, n * s.nheads * s.headdim * s.dstate, torch.float32,
+                          (n, s.nheads, s.headdim, s.dstate))
+
+    def start_states(self) -> torch.Tensor:
+        s, n = self.shape, self.layout.nslots
+        dt = torch.bfloat16 if s.dtype == DTYPE_BF16 else torch.float32
+        return self._view(self.layout.start_states_offset, n * s.nheads * s.headdim * s.dstate, dt,
+                          (n, s.nheads, s.headdim, s.dstate))
+
+
+def _check_inputs(X, log_a, B, C, cu_seqlens):
+    for name, t in (("X", X), ("B", B), ("C", C)):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if log_a is not None and (log_a.dtype != torch.float32 or not log_a.is_contiguous() or not log_a.is_cuda):
+        raise ValueError("log_a must be a contiguous fp32 device tensor")
+    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
+        raise ValueError("cu_seqlens must be an int32 device tensor")
+    if X is not None and B is not None and (X.dtype != B.dtype or (C is not None and C.dtype != X.dtype)):
+        raise ValueError("X, B and C must share one dtype")
+
+
+def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+        cu_seqlens: Optional[torch.Tensor] = None, chunk: int = 128, Y: Optional[torch.Tensor] = None,
+        final_state: Optional[torch.Tensor] = None, want_final: bool = True,
+        workspace: Optional[Workspace] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked SSD forward pass (ssd_fwd). Returns (Y, final_state or None)."""
+    _check_inputs(X, log_a, B, C, cu_seqlens)
+    shape = make_shape(X, B, cu_seqlens)
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and want_final:
+        nseq = X.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        final_state = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = Workspace(shape, chunk, X.device)
+    _call("ssd_fwd", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), int(chunk), _ptr(Y),
+          _ptr(final_state), ctypes.byref(shape), _ptr(workspace.buffer), workspace.nbytes, _stream(X.device))
+    return Y, final_state
+
+
+def chunk_cumsum(log_a, cu_seqlens, chunk, shape: Shape, ws: Workspace):
+    _call("ssd_chunk_cumsum", _ptr(log_a), _ptr(cu_seqlens), int(chunk), ctypes.byref(shape), _ptr(ws.buffer),
+          ws.nbytes, _stream(ws.buffer.device))
+
+
+def chunk_state(X, B, cu_seqlens, chunk, shape: Shape, ws: Workspace):
+    _call("ssd_chunk_state", _ptr(X), _ptr(B), _ptr(cu_seqlens), int(chunk), ctypes.byref(shape), _ptr(ws.buffer),
+          ws.nbytes, _stream(ws.buffer.device))
+
+
+def state_passing(cu_seqlens, chunk, final_state, shape: Shape, ws: Workspace):
+    _call("ssd_state_passing", _ptr(cu_seqlens), int(chunk), _ptr(final_state), ctypes.byref(shape),
+          _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
+
+
+def chunk_scan(X, B, C, cu_seqlens, chunk, Y, shape: Shape, ws: Workspace):
+    _call("ssd_chunk_scan", _ptr(X), _ptr(B), _ptr(C), _ptr(cu_seqlens), int(chunk), _ptr(Y), ctypes.byref(shape),
+          _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
+
+
+def step(state: torch.Tensor, x: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+         y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step (ssd_step): updates `state` in place and returns y."""
+    for name, t in (("state", state), ("x", x), ("B", B), ("C", C)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if state.dtype != torch.float32 or log_a.dtype != torch.float32:
+        raise ValueError("state and log_a must be fp32")
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    shape = Shape(b, 1, H, G, P, N, 0, _dtype_code(x.dtype))
+    if y is None:
+        y = torch.empty_like(x)
+    _call("ssd_step", _ptr(state), _ptr(x), _ptr(log_a), _ptr(B), _ptr(C), _ptr(y), ctypes.byref(shape),
+          _stream(x.device))
+    return y

@@ -1,0 +1,209 @@
+// ssd_api.cpp -- the C ABI declared in include/ssd.h.
+//
+// Every entry point validates its arguments on the host first (no HIP call
+// before validation succeeds), carves the caller's workspace, and enqueues the
+// stage kernels on the caller's stream. Nothing is allocated, nothing is
+// synchronised, and no C++ exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "ssd.h"
+#include "ssd_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = INT32_MAX;  // every tensor holds fewer than 2^31 elements
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+enum Stage { kCumsum = 1, kState = 2, kPassing = 4, kScan = 8, kAll = 15 };
+
+// Shape, dtype and size checks shared by every forward entry point.
+ssd_status check_shape(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
+  if (!s) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->batch < 1 || s->seqlen < 1 || s->nheads < 1 || s->ngroups < 1 || s->headdim < 1 || s->dstate < 1)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (s->nheads % s->ngroups) return SSD_ERR_INVALID_ARGUMENT;
+  if (chunk < 1) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->batch > 65535) return SSD_ERR_UNSUPPORTED;
+  if (cu) {
+    if (s->batch != 1 || s->num_seqs < 1 || s->num_seqs > s->seqlen) return SSD_ERR_INVALID_ARGUMENT;
+  } else if (s->num_seqs != 0) {
+    return SSD_ERR_INVALID_ARGUMENT;
+  }
+  if (s->dtype != SSD_DTYPE_F32 && s->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+  if (!pow2_in(s->headdim, 16, 128) || !pow2_in(s->dstate, 16, 256) || !pow2_in(chunk, 16, 256))
+    return SSD_ERR_UNSUPPORTED;
+  if (s->dtype == SSD_DTYPE_BF16) {
+    if (chunk < 32 || s->dstate < 32) return SSD_ERR_UNSUPPORTED;
+    if (ssd::chunk_scan_bf16_lds_bytes(s->headdim, s->dstate, chunk) > ssd::kMaxLdsBytes)
+      return SSD_ERR_UNSUPPORTED;
+  }
+  const int64_t bt = (int64_t)s->batch * s->seqlen;
+  if (bt * s->nheads * s->headdim > kMaxElems || bt * s->ngroups * s->dstate > kMaxElems)
+    return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+ssd_status make_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk, ssd_layout* out) {
+  ssd_layout L{};
+  const int64_t T = s->seqlen;
+  L.slots_per_row = cu ? (T / chunk + s->num_seqs) : ((T + chunk - 1) / chunk);
+  L.nslots = (int64_t)s->batch * L.slots_per_row;
+  const int64_t H = s->nheads, PN = (int64_t)s->headdim * s->dstate;
+  if (L.nslots * H * PN > kMaxElems || L.nslots * H * chunk > kMaxElems) return SSD_ERR_UNSUPPORTED;
+  const int64_t nseq = cu ? s->num_seqs : s->batch;
+  if (nseq * H * PN > kMaxElems) return SSD_ERR_UNSUPPORTED;
+  const size_t esz = s->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  size_t off = 0;
+  L.table_offset = off;
+  off = align256(off + (size_t)L.nslots * 16);
+  L.cumsum_offset = off;
+  off = align256(off + (size_t)L.nslots * H * chunk * 4);
+  L.chunk_states_offset = off;
+  off = align256(off + (size_t)L.nslots * H * PN * 4);
+  L.start_states_offset = off;
+  off = align256(off + (size_t)L.nslots * H * PN * esz);
+  L.total_bytes = off;
+  *out = L;
+  return SSD_OK;
+}
+
+struct Prepared {
+  ssd::FwdDims d;
+  ssd::Workspace ws;
+};
+
+// Full validation of a forward-stage call; fills `pp` on success.
+ssd_status prepare(int stages, const void* X, const float* log_a, const void* B, const void* C,
+                   const void* Y, const int32_t* cu, int32_t chunk, const ssd_shape* s, void* workspace,
+                   size_t workspace_bytes, Prepared* pp) {
+  ssd_status st = check_shape(s, cu, chunk);
+  if (st != SSD_OK) return st;
+  if ((stages & kCumsum) && !log_a) return SSD_ERR_INVALID_ARGUMENT;
+  if ((stages & (kState | kScan)) && (!X || !B)) return SSD_ERR_INVALID_ARGUMENT;
+  if ((stages & kScan) && (!C || !Y)) return SSD_ERR_INVALID_ARGUMENT;
+  ssd_layout L;
+  st = make_layout(s, cu, chunk, &L);
+  if (st != SSD_OK) return st;
+  if (!workspace) return SSD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < L.total_bytes) return SSD_ERR_WORKSPACE_TOO_SMALL;
+  char* base = static_cast<char*>(workspace);
+  pp->d = ssd::FwdDims{s->batch, s->seqlen, s->nheads, s->ngroups, s->headdim, s->dstate, chunk,
+                       cu ? s->num_seqs : 0, s->dtype == SSD_DTYPE_BF16 ? 1 : 0,
+                       (long)L.slots_per_row, (long)L.nslots};
+  pp->ws = ssd::Workspace{reinterpret_cast<int4*>(base + L.table_offset),
+                          reinterpret_cast<float*>(base + L.cumsum_offset),
+                          reinterpret_cast<float*>(base + L.chunk_states_offset),
+                          static_cast<void*>(base + L.start_states_offset)};
+  return SSD_OK;
+}
+
+ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(ssd_status status) {
+  switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_INVALID_ARGUMENT: return "SSD_ERR_INVALID_ARGUMENT";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_WORKSPACE_TOO_SMALL: return "SSD_ERR_WORKSPACE_TOO_SMALL";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+  }
+  return "SSD_ERR_UNKNOWN";
+}
+
+ssd_status ssd_fwd_layout(const ssd_shape* shape, int32_t chunk, ssd_layout* layout) {
+  if (!layout) return SSD_ERR_INVALID_ARGUMENT;
+  // The layout depends on whether rows are packed; num_seqs > 0 means packed.
+  const int32_t dummy = 0;
+  const int32_t* cu = (shape && shape->num_seqs > 0) ? &dummy : nullptr;
+  ssd_status st = check_shape(shape, cu, chunk);
+  if (st != SSD_OK) return st;
+  return make_layout(shape, cu, chunk, layout);
+}
+
+ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, size_t* bytes) {
+  if (!bytes) return SSD_ERR_INVALID_ARGUMENT;
+  ssd_layout L;
+  ssd_status st = ssd_fwd_layout(shape, chunk, &L);
+  if (st != SSD_OK) return st;
+  *bytes = L.total_bytes;
+  return SSD_OK;
+}
+
+ssd_status ssd_chunk_cumsum(const float* log_a, const int32_t* cu_seqlens, int32_t chunk, const ssd_shape* shape,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  Prepared pp;
+  ssd_status st = prepare(kCumsum, nullptr, log_a, nullptr, nullptr, nullptr, cu_seqlens, chunk, shape,
+                          workspace, workspace_bytes, &pp);
+  if (st != SSD_OK) return st;
+  return hip_status(ssd::launch_chunk_cumsum(pp.d, log_a, cu_seqlens, pp.ws, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_state(const void* X, const void* B, const int32_t* cu_seqlens, int32_t chunk,
+                           const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  Prepared pp;
+  ssd_status st = prepare(kState, X, nullptr, B, nullptr, nullptr, cu_seqlens, chunk, shape, workspace,
+                          workspace_bytes, &pp);
+  if (st != SSD_OK) return st;
+  return hip_status(ssd::launch_chunk_state(pp.d, X, B, pp.ws, (hipStream_t)stream));
+}
+
+ssd_status ssd_state_passing(const int32_t* cu_seqlens, int32_t chunk, float* final_state, const ssd_shape* shape,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Prepared pp;
+  ssd_status st = prepare(kPassing, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, chunk, shape,
+                          workspace, workspace_bytes, &pp);
+  if (st != SSD_OK) return st;
+  return hip_status(ssd::launch_state_passing(pp.d, cu_seqlens, final_state, pp.ws, (hipStream_t)stream));
+}
+
+ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int32_t* cu_seqlens, int32_t chunk,
+                          void* Y, const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  Prepared pp;
+  ssd_status st = prepare(kScan, X, nullptr, B, C, Y, cu_seqlens, chunk, shape, workspace, workspace_bytes, &pp);
+  if (st != SSD_OK) return st;
+  return hip_status(ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, (hipStream_t)stream));
+}
+
+ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
+                   int32_t chunk, void* Y, float* final_state, const ssd_shape* shape, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  Prepared pp;
+  ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, shape, workspace, workspace_bytes, &pp);
+  if (st != SSD_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = ssd::launch_chunk_cumsum(pp.d, log_a, cu_seqlens, pp.ws, s);
+  if (e == hipSuccess) e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s);
+  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, final_state, pp.ws, s);
+  if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s);
+  return hip_status(e);
+}
+
+ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C, void* y,
+                    const ssd_shape* shape, void* stream) {
+  if (!shape || !state || !x || !log_a || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+  const ssd_shape* s = shape;
+  if (s->batch < 1 || s->nheads < 1 || s->ngroups < 1 || s->headdim < 1 || s->dstate < 1)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (s->nheads % s->ngroups) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->dtype != SSD_DTYPE_F32 && s->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+  if (!pow2_in(s->headdim, 16, 128) || !pow2_in(s->dstate, 16, 256)) return SSD_ERR_UNSUPPORTED;
+  if (s->batch > 65535 || (int64_t)s->batch * s->nheads * s->headdim * s->dstate > kMaxElems)
+    return SSD_ERR_UNSUPPORTED;
+  return hip_status(ssd::launch_ssd_step(s->batch, s->nheads, s->ngroups, s->headdim, s->dstate,
+                                         s->dtype == SSD_DTYPE_BF16 ? 1 : 0, state, x, log_a, B, C, y,
+                                         (hipStream_t)stream));
+}
+
+}  // extern "C"

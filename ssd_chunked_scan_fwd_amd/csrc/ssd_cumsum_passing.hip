@@ -1,0 +1,251 @@
+// ssd_cumsum_passing.hip -- the two scalar-recurrence stages of the chunked SSD
+// forward pass on gfx950: the per-chunk cumulative log decay (chunk_cumsum)
+// and the inter-chunk state recurrence (state_passing).
+//
+// Source: "Transformers are SSMs" paper card (wikillm.com/papers/2405.21060),
+// Method 5 / paper section 6: the cumulative log decay restarted in every
+// chunk gives the 1-semiseparable mask and each chunk's total decay; the
+// "Center Factors" step carries states across chunks with a scalar recurrence.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// ----------------------------------------------------------------------------
+// chunk_cumsum: one workgroup per chunk slot. Locates the slot's tokens
+// (packed rows: sequence s owns slots floor(cu[s]/Q) + s + j), writes the slot
+// record, then for every head the inclusive prefix sum of log_a over the
+// chunk, scaled by log2(e) so that later stages use exp2. Positions past the
+// chunk's length repeat the chunk total (zero increments).
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ la,
+                                                           const int32_t* __restrict__ cu, int S,
+                                                           int T, int H, int Q, long slots_per_row,
+                                                           int4* __restrict__ table,
+                                                           float* __restrict__ cs) {
+  const int row = blockIdx.y;
+  const long sl = blockIdx.x;
+  const long slot = (long)row * slots_per_row + sl;
+
+  int seq, t0, len, kidx;
+  if (cu == nullptr) {
+    seq = row;
+    kidx = (int)sl;
+    t0 = kidx * Q;
+    len = min(Q, T - t0);
+  } else {
+    // base_s = floor(cu[s]/Q) + s is strictly increasing in s: binary search
+    // for the last sequence whose base is <= sl.
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const long base = cu[mid] / Q + mid;
+      if (base <= sl) lo = mid; else hi = mid - 1;
+    }
+    const int b = cu[lo], e = cu[lo + 1];
+    const long j = sl - (long)(b / Q + lo);
+    const int nch = (e - b + Q - 1) / Q;
+    seq = lo;
+    if (j < 0 || j >= nch) {
+      kidx = -1;
+      t0 = 0;
+      len = 0;
+    } else {
+      kidx = (int)j;
+      t0 = b + kidx * Q;
+      len = min(Q, e - t0);
+    }
+  }
+  const int tok0 = row * T + t0;  // token index flattened over rows
+  if (threadIdx.x == 0) table[slot] = make_int4(seq, tok0, len, kidx);
+  if (len <= 0) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int h = wave; h < H; h += 4) {
+    float carry = 0.f;  // inclusive sum up to the last valid token seen so far
+    float* out = cs + (slot * H + h) * (long)Q;
+    for (int jb = 0; jb < Q; jb += 64) {
+      const int j = jb + lane;
+      if (jb < len) {
+        float v = (j < len) ? la[(long)(tok0 + j) * H + h] : 0.f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float u = __shfl_up(v, d);
+          if (lane >= d) v += u;
+        }
+        v += carry;
+        carry = __shfl(v, min(len - jb, 64) - 1);
+        if (j < Q) out[j] = (j < len ? v : carry) * kLog2e;
+      } else if (j < Q) {
+        out[j] = carry * kLog2e;
+      }
+    }
+  }
+}
+
+hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32_t* cu,
+                               const Workspace& ws, hipStream_t stream) {
+  dim3 grid((unsigned)d.slots_per_row, (unsigned)d.batch);
+  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(256), 0, stream, log_a, cu, d.num_seqs, d.T, d.H,
+                     d.Q, d.slots_per_row, ws.table, ws.cs);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// state_passing: h = 0; for each chunk k of a sequence: start_k = h;
+// h = exp2(total_k) h + s_k. One thread owns 4 consecutive (p, n) elements of
+// one (sequence, head); the chunk loop is unrolled so that the loads of four
+// chunks are in flight together. Sequence s: packed rows own slots
+// floor(cu[s]/Q) + s ..; unpacked row s owns slots s*slots_per_row ...
+// ----------------------------------------------------------------------------
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ states,
+                                                            void* __restrict__ start,
+                                                            float* __restrict__ final_state,
+                                                            const float* __restrict__ cs,
+                                                            const int32_t* __restrict__ cu,
+                                                            long slots_per_row, int H, int PN, int Q) {
+  const int eblocks = (PN / 4 + 255) / 256;
+  const long unit = blockIdx.x;
+  const int e = (int)(unit % eblocks) * 1024 + threadIdx.x * 4;
+  const int h = (int)((unit / eblocks) % H);
+  const int s = (int)(unit / ((long)eblocks * H));
+  long base;
+  int nch;
+  if (cu) {
+    const int b = cu[s], en = cu[s + 1];
+    base = b / Q + s;
+    nch = (en - b + Q - 1) / Q;
+  } else {
+    base = (long)s * slots_per_row;
+    nch = (int)slots_per_row;
+  }
+  if (e >= PN) return;
+
+  f32x4 hc = {0.f, 0.f, 0.f, 0.f};
+  auto put = [&](long slot, f32x4 v) {
+    const long off = (slot * H + h) * (long)PN + e;
+    if (OUT_BF16) {
+      u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(start) + off) = w;
+    } else {
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(start) + off) = v;
+    }
+  };
+  int k = 0;
+  for (; k + 4 <= nch; k += 4) {
+    f32x4 sv[4];
+    float dv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long slot = base + k + u;
+      sv[u] = *reinterpret_cast<const f32x4*>(states + (slot * H + h) * (long)PN + e);
+      dv[u] = cs[(slot * H + h) * (long)Q + Q - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      put(base + k + u, hc);
+      const float a = fast_exp2(dv[u]);
+      hc = a * hc + sv[u];
+    }
+  }
+  for (; k < nch; ++k) {
+    const long slot = base + k;
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(states + (slot * H + h) * (long)PN + e);
+    const float a = fast_exp2(cs[(slot * H + h) * (long)Q + Q - 1]);
+    put(slot, hc);
+    hc = a * hc + sv;
+  }
+  if (final_state) *reinterpret_cast<f32x4*>(final_state + ((long)s * H + h) * PN + e) = hc;
+}
+
+hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, float* final_state,
+                                const Workspace& ws, hipStream_t stream) {
+  const int PN = d.P * d.N;
+  const int nseq = cu ? d.num_seqs : d.batch;
+  const long eblocks = (PN / 4 + 255) / 256;
+  dim3 grid((unsigned)(eblocks * d.H * nseq));
+  if (d.bf16) {
+    hipLaunchKernelGGL(state_passing_kernel<true>, grid, dim3(256), 0, stream, ws.chunk_states,
+                       ws.start_states, final_state, ws.cs, cu, d.slots_per_row, d.H, PN, d.Q);
+  } else {
+    hipLaunchKernelGGL(state_passing_kernel<false>, grid, dim3(256), 0, stream, ws.chunk_states,
+                       ws.start_states, final_state, ws.cs, cu, d.slots_per_row, d.H, PN, d.Q);
+  }
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// ssd_step: one decode step. One workgroup per (row, head); N/4 consecutive
+// lanes share a state row p, each owning 4 consecutive n. The state is read
+// and written once (fp32); y[p] = sum_n state'[p][n] C[n] is reduced across
+// the lanes of the row.
+// ----------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state,
+                                                       const void* __restrict__ x,
+                                                       const float* __restrict__ la,
+                                                       const void* __restrict__ Bv,
+                                                       const void* __restrict__ Cv,
+                                                       void* __restrict__ y, int H, int G, int P, int N) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int g = h / (H / G);
+  const int tpr = N >> 2;             // lanes per state row (4..64, power of two)
+  const int c4 = threadIdx.x & (tpr - 1);
+  const int p0 = threadIdx.x / tpr;
+  const int rpp = 256 / tpr;          // rows per pass
+  const long bh = (long)b * H + h;
+  const long bg = (long)b * G + g;
+  float* st = state + bh * (long)P * N;
+  const float a = fast_exp2(la[bh] * kLog2e);
+
+  float bb[4], cc[4];
+  if (BF16) {
+    const u32x2 wb = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(Bv) + bg * N + 4 * c4);
+    const u32x2 wc = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(Cv) + bg * N + 4 * c4);
+    bb[0] = bf16_lo(wb.x); bb[1] = bf16_hi(wb.x); bb[2] = bf16_lo(wb.y); bb[3] = bf16_hi(wb.y);
+    cc[0] = bf16_lo(wc.x); cc[1] = bf16_hi(wc.x); cc[2] = bf16_lo(wc.y); cc[3] = bf16_hi(wc.y);
+  } else {
+    const f32x4 fb = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Bv) + bg * N + 4 * c4);
+    const f32x4 fc = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(Cv) + bg * N + 4 * c4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { bb[i] = fb[i]; cc[i] = fc[i]; }
+  }
+
+  for (int p = p0; p < P; p += rpp) {
+    const float xp = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[bh * P + p])
+                          : reinterpret_cast<const float*>(x)[bh * P + p];
+    f32x4* sp = reinterpret_cast<f32x4*>(st + (long)p * N + 4 * c4);
+    f32x4 s = *sp;
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = a * s[i] + xp * bb[i];
+      part += s[i] * cc[i];
+    }
+    *sp = s;
+    for (int off = tpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (c4 == 0) {
+      if (BF16) reinterpret_cast<uint16_t*>(y)[bh * P + p] = f32_to_bf16(part);
+      else reinterpret_cast<float*>(y)[bh * P + p] = part;
+    }
+  }
+}
+
+hipError_t launch_ssd_step(int batch, int H, int G, int P, int N, int bf16, float* state,
+                           const void* x, const float* log_a, const void* B, const void* C, void* y,
+                           hipStream_t stream) {
+  dim3 grid((unsigned)H, (unsigned)batch);
+  if (bf16) {
+    hipLaunchKernelGGL(ssd_step_kernel<true>, grid, dim3(256), 0, stream, state, x, log_a, B, C, y, H, G,
+                       P, N);
+  } else {
+    hipLaunchKernelGGL(ssd_step_kernel<false>, grid, dim3(256), 0, stream, state, x, log_a, B, C, y, H,
+                       G, P, N);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,171 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its workspace, and rejects bad arguments on the host
+before any HIP call (each case below fails validation, so nothing is launched).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import ssd_chunked_scan_fwd_amd as ssd
+from ssd_chunked_scan_fwd_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ssd_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_binding_exports():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ssd.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\sT\s(ssd_[a-z_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_abi_version_and_status_strings():
+    L = ssd.lib()
+    assert L.ssd_abi_version() == 1
+    for code, name in binding.STATUS.items():
+        assert L.ssd_status_string(code).decode() == name
+
+
+def shape(**kw):
+    base = dict(batch=1, seqlen=16384, nheads=32, ngroups=1, headdim=64, dstate=128, num_seqs=0, dtype=1)
+    base.update(kw)
+    return binding.Shape(*[base[k] for k in ("batch", "seqlen", "nheads", "ngroups", "headdim", "dstate",
+                                              "num_seqs", "dtype")])
+
+
+def ws_bytes(sh, chunk):
+    n = ctypes.c_size_t(0)
+    st = ssd.lib().ssd_fwd_workspace_bytes(ctypes.byref(sh), chunk, ctypes.byref(n))
+    return st, n.value
+
+
+def _align(v):
+    return (v + 255) // 256 * 256
+
+
+def test_workspace_size_matches_layout():
+    sh = shape()
+    st, n = ws_bytes(sh, 128)
+    assert st == OK
+    slots = 16384 // 128
+    expect = _align(slots * 16) + _align(slots * 32 * 128 * 4) + _align(slots * 32 * 64 * 128 * 4) + \
+        _align(slots * 32 * 64 * 128 * 2)
+    assert n == expect
+    L = ssd.layout(sh, 128)
+    assert L.slots_per_row == slots and L.nslots == slots and L.total_bytes == n
+    # packed rows: floor(T/Q) + S slots
+    sp = shape(seqlen=32768, nheads=80, num_seqs=7)
+    Lp = ssd.layout(sp, 128)
+    assert Lp.slots_per_row == 32768 // 128 + 7
+    # ragged T: ceil(T/Q) slots per row
+    Lr = ssd.layout(shape(batch=3, seqlen=1000), 64)
+    assert Lr.slots_per_row == 16 and Lr.nslots == 48
+    # fp32 start states are 4 bytes
+    L32 = ssd.layout(shape(dtype=0, seqlen=256, nheads=2, headdim=16, dstate=16), 32)
+    assert L32.total_bytes - L32.start_states_offset == _align(8 * 2 * 16 * 16 * 4)
+
+
+@pytest.mark.parametrize("kw,chunk,code", [
+    (dict(seqlen=0), 128, INVALID),
+    (dict(batch=0), 128, INVALID),
+    (dict(nheads=6, ngroups=4), 128, INVALID),
+    (dict(headdim=0), 128, INVALID),
+    (dict(), 0, INVALID),
+    (dict(num_seqs=3), 128, INVALID),           # num_seqs without cu_seqlens (checked in ssd_fwd below)
+    (dict(headdim=48), 128, UNSUPPORTED),
+    (dict(headdim=256), 128, UNSUPPORTED),
+    (dict(dstate=512), 128, UNSUPPORTED),
+    (dict(dstate=16), 128, UNSUPPORTED),        # bf16 needs dstate >= 32
+    (dict(), 16, UNSUPPORTED),                  # bf16 needs chunk >= 32
+    (dict(), 96, UNSUPPORTED),
+    (dict(), 512, UNSUPPORTED),
+    (dict(dtype=7), 128, UNSUPPORTED),
+    (dict(headdim=128, dstate=256), 256, UNSUPPORTED),  # tiles exceed the 160 KiB LDS
+    (dict(batch=70000, seqlen=16, nheads=1), 32, UNSUPPORTED),
+    (dict(seqlen=1 << 20, nheads=64, headdim=64), 128, UNSUPPORTED),  # more than 2^31 elements
+])
+def test_fwd_rejects_bad_shapes(kw, chunk, code):
+    sh = shape(**kw)
+    L = ssd.lib()
+    st = L.ssd_fwd(FAKE, FAKE, FAKE, FAKE, None, chunk, FAKE, FAKE, ctypes.byref(sh), FAKE, 1 << 40, None)
+    assert st == code
+
+
+def test_fwd_rejects_null_pointers_and_small_workspace():
+    L = ssd.lib()
+    sh = shape()
+    _, need = ws_bytes(sh, 128)
+    args = [FAKE, FAKE, FAKE, FAKE, None, 128, FAKE, FAKE, ctypes.byref(sh), FAKE, need, None]
+    for i in (0, 1, 2, 3, 6, 9):  # X, log_a, B, C, Y, workspace
+        a = list(args)
+        a[i] = None
+        assert L.ssd_fwd(*a) == INVALID, i
+    a = list(args)
+    a[10] = need - 1
+    assert L.ssd_fwd(*a) == WS_SMALL
+    a = list(args)
+    a[8] = None
+    assert L.ssd_fwd(*a) == INVALID
+
+
+def test_packed_argument_rules():
+    L = ssd.lib()
+    sh = shape(batch=2, num_seqs=3)
+    assert L.ssd_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, None, ctypes.byref(sh), FAKE, 1 << 40, None) == INVALID
+    sh = shape(num_seqs=0)
+    assert L.ssd_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, None, ctypes.byref(sh), FAKE, 1 << 40, None) == INVALID
+    sh = shape(seqlen=4, num_seqs=5)
+    assert L.ssd_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 32, FAKE, None, ctypes.byref(sh), FAKE, 1 << 40, None) == INVALID
+
+
+def test_stage_entry_points_validate():
+    L = ssd.lib()
+    sh = shape()
+    _, need = ws_bytes(sh, 128)
+    assert L.ssd_chunk_cumsum(None, None, 128, ctypes.byref(sh), FAKE, need, None) == INVALID
+    assert L.ssd_chunk_state(None, FAKE, None, 128, ctypes.byref(sh), FAKE, need, None) == INVALID
+    assert L.ssd_chunk_state(FAKE, FAKE, None, 128, ctypes.byref(sh), FAKE, need - 256, None) == WS_SMALL
+    assert L.ssd_state_passing(None, 128, None, ctypes.byref(sh), None, need, None) == INVALID
+    assert L.ssd_chunk_scan(FAKE, FAKE, None, None, 128, FAKE, ctypes.byref(sh), FAKE, need, None) == INVALID
+    assert L.ssd_chunk_scan(FAKE, FAKE, FAKE, None, 128, None, ctypes.byref(sh), FAKE, need, None) == INVALID
+
+
+def test_step_validates():
+    L = ssd.lib()
+    sh = shape(batch=64, nheads=80)
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sh), None]
+    for i in range(6):
+        a = list(args)
+        a[i] = None
+        assert L.ssd_step(*a) == INVALID
+    bad = shape(batch=64, nheads=80, dstate=24)
+    assert L.ssd_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(bad), None) == UNSUPPORTED
+    bad = shape(batch=64, nheads=80, ngroups=3)
+    assert L.ssd_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(bad), None) == INVALID
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    X = torch.zeros(1, 64, 2, 16)
+    with pytest.raises(ValueError):
+        ssd.fwd(X, torch.zeros(1, 64, 2), torch.zeros(1, 64, 1, 16), torch.zeros(1, 64, 1, 16), chunk=32)

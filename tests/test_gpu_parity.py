@@ -1,0 +1,316 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test runs the library on seeded synthetic inputs and compares it element
+by element with ``oracle/`` on the same stored (rounded) input values. Sizes
+span several chunks and a ragged tail; the named workloads run at full size.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import ssd_chunked_scan_fwd_amd as ssd
+from ssd_chunked_scan_fwd_amd import synth
+from oracle import oracle
+from parity import assert_close, dtype_name, to_f64
+
+pytestmark = pytest.mark.gpu
+
+LOG2E = 1.4426950408889634
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ssd.lib()  # the HIP library must load: no fallback
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(d):
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def gpu_fwd(d, Q, **kw):
+    dd = to_dev(d)
+    Y, fin = ssd.fwd(dd["X"], dd["log_a"], dd["B"], dd["C"], cu_seqlens=dd.get("cu_seqlens"), chunk=Q, **kw)
+    torch.cuda.synchronize()
+    return Y, fin
+
+
+def oracle_fwd(d):
+    cu = d.get("cu_seqlens")
+    return oracle.forward(to_f64(d["X"]), to_f64(d["log_a"]), to_f64(d["B"]), to_f64(d["C"]),
+                          cu_seqlens=None if cu is None else cu.numpy())
+
+
+def check_fwd(d, Q, what):
+    say(f"[parity] {what}: X{tuple(d['X'].shape)} {d['X'].dtype} N={d['B'].shape[-1]} Q={Q}")
+    Y, fin = gpu_fwd(d, Q)
+    Yr, fr = oracle_fwd(d)
+    dt = dtype_name(d["X"])
+    ey = assert_close(to_f64(Y), Yr, dt, what + " Y")
+    ef = assert_close(to_f64(fin), fr, dt, what + " final")
+    say(f"[parity] {what}: Y {ey} final {ef}")
+    return Y, fin
+
+
+# ------------------------------------------------------------------ named workloads
+
+@pytest.mark.parametrize("name", ["tiny-fp32-T256", "b2-T2048-H24-N64", "long-T16384-H32-N128",
+                                  "sweep-b8-T4096-N64", "sweep-b8-T4096-N128", "sweep-b8-T4096-N256",
+                                  "packed-T32768-H80-N128"])
+def test_workload_full_size(name):
+    w = synth.WORKLOADS[name]
+    d = synth.workload_inputs(w)
+    check_fwd(d, w.Q, name)
+
+
+# ------------------------------------------------------------------ shapes and edge cases
+
+CASES = [
+    # (batch, T, H, P, N, G, dtype, Q)
+    (1, 200, 3, 64, 64, 1, torch.bfloat16, 64),     # ragged tail
+    (2, 100, 2, 32, 32, 2, torch.bfloat16, 32),     # G = H
+    (1, 50, 4, 16, 32, 2, torch.bfloat16, 64),      # T < Q, P = 16, two groups
+    (1, 333, 2, 128, 128, 1, torch.bfloat16, 128),  # P = 128
+    (1, 300, 2, 64, 256, 1, torch.bfloat16, 128),   # N = 256
+    (1, 600, 2, 64, 128, 1, torch.bfloat16, 256),   # Q = 256
+    (3, 129, 2, 32, 64, 1, torch.bfloat16, 128),    # one full chunk + 1 token
+    (1, 1, 2, 64, 64, 1, torch.bfloat16, 64),       # a single token
+    (1, 77, 3, 16, 16, 1, torch.float32, 16),       # fp32, Q = 16
+    (2, 500, 2, 128, 256, 2, torch.float32, 256),   # fp32, large tiles
+    (1, 300, 4, 32, 64, 4, torch.float32, 64),      # fp32, G = H
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}-T{}-H{}-P{}-N{}-G{}-{}-Q{}".format(
+    *c[:6], "bf16" if c[6] == torch.bfloat16 else "fp32", c[7]))
+def test_shapes(case):
+    b, T, H, P, N, G, dt, Q = case
+    d = synth.make_forward_inputs(b, T, H, P, N, G, dtype=dt, seed=1000 + T + N)
+    check_fwd(d, Q, f"shape {case}")
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_linear_attention_no_decay(dt):
+    d = synth.make_forward_inputs(1, 300, 2, 32, 64, 1, dtype=dt, seed=77)
+    d["log_a"].zero_()
+    check_fwd(d, 64, "log_a = 0")
+
+
+def test_strong_decay():
+    # dt up to 1, A up to 16: log a down to -16 per token (deep underflow inside chunks)
+    d = synth.make_forward_inputs(1, 512, 2, 64, 64, 1, dtype=torch.bfloat16, seed=78, dt_range=(0.1, 1.0))
+    check_fwd(d, 128, "strong decay")
+
+
+@pytest.mark.parametrize("Q", [32, 64, 128, 256])
+def test_chunk_size_invariance(Q):
+    d = synth.make_forward_inputs(2, 1000, 4, 64, 128, 1, dtype=torch.bfloat16, seed=5)
+    check_fwd(d, Q, f"chunk {Q}")
+
+
+@pytest.mark.parametrize("Q", [16, 32, 64])
+def test_chunk_size_invariance_fp32(Q):
+    d = synth.make_forward_inputs(1, 400, 2, 16, 16, 1, dtype=torch.float32, seed=6)
+    check_fwd(d, Q, f"fp32 chunk {Q}")
+
+
+# ------------------------------------------------------------------ packed sequences
+
+@pytest.mark.parametrize("dt,Q", [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.float32, 32)])
+def test_packed_ragged_lengths(dt, Q):
+    lengths = [1, 200, 64, 65, 3, 129, 1, 300]
+    d = synth.make_forward_inputs(1, sum(lengths), 3, 32, 64, 1, dtype=dt, seed=9, lengths=lengths)
+    check_fwd(d, Q, f"packed {lengths}")
+
+
+def test_packed_equals_separate_runs_bitwise():
+    lengths = [100, 37, 256, 5]
+    d = synth.make_forward_inputs(1, sum(lengths), 2, 64, 64, 1, dtype=torch.bfloat16, seed=10, lengths=lengths)
+    Y, fin = gpu_fwd(d, 64)
+    cu = d["cu_seqlens"].numpy()
+    for s in range(len(lengths)):
+        b, e = int(cu[s]), int(cu[s + 1])
+        ds = {k: d[k][:, b:e].contiguous() for k in ("X", "log_a", "B", "C")}
+        Ys, fs = gpu_fwd(ds, 64)
+        assert torch.equal(Y[:, b:e], Ys)
+        assert torch.equal(fin[s], fs[0])
+
+
+def test_many_short_sequences():
+    rng = np.random.default_rng(12)
+    lengths = list(rng.integers(1, 40, size=120))
+    d = synth.make_forward_inputs(1, int(sum(lengths)), 2, 64, 64, 1, dtype=torch.bfloat16, seed=12,
+                                  lengths=[int(v) for v in lengths])
+    check_fwd(d, 32, "120 short sequences")
+
+
+# ------------------------------------------------------------------ stage intermediates
+
+def stage_run(d, Q):
+    dd = to_dev(d)
+    X, la, B, C, cu = dd["X"], dd["log_a"], dd["B"], dd["C"], dd.get("cu_seqlens")
+    sh = ssd.make_shape(X, B, cu)
+    ws = ssd.Workspace(sh, Q, X.device)
+    nseq = X.shape[0] if cu is None else cu.numel() - 1
+    fin = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
+    Y = torch.empty_like(X)
+    ssd.chunk_cumsum(la, cu, Q, sh, ws)
+    ssd.chunk_state(X, B, cu, Q, sh, ws)
+    ssd.state_passing(cu, Q, fin, sh, ws)
+    ssd.chunk_scan(X, B, C, cu, Q, Y, sh, ws)
+    torch.cuda.synchronize()
+    return ws, Y, fin
+
+
+@pytest.mark.parametrize("packed,dt,Q", [(False, torch.bfloat16, 64), (True, torch.bfloat16, 64),
+                                         (False, torch.float32, 32), (True, torch.float32, 16)])
+def test_stage_intermediates(packed, dt, Q):
+    rows = 1 if packed else 2
+    lengths = [70, 1, 130, 64] if packed else None
+    T = sum(lengths) if packed else 200
+    d = synth.make_forward_inputs(rows, T, 3, 32, 64 if dt == torch.bfloat16 else 16, 1, dtype=dt, seed=21,
+                                  lengths=lengths)
+    say(f"[parity] stage intermediates packed={packed} {dt} Q={Q}")
+    ws, Y, fin = stage_run(d, Q)
+    X, la, B, C = (to_f64(d[k]) for k in ("X", "log_a", "B", "C"))
+    cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].numpy()
+    dts = dtype_name(d["X"])
+    table = ws.table().cpu().numpy()
+    chunks = oracle.chunk_segments(rows, T, Q, cu)
+    # slot of every chunk, from the documented slot numbering
+    slots = []
+    if cu is None:
+        spr = -(-T // Q)
+        slots = [r * spr + (b // Q) for (r, b, e) in chunks]
+    else:
+        for (r, b, e) in chunks:
+            s = int(np.searchsorted(cu, b, side="right") - 1)
+            slots.append(int(cu[s]) // Q + s + (b - int(cu[s])) // Q)
+    # table records
+    for (r, b, e), sl in zip(chunks, slots):
+        assert table[sl, 1] == r * T + b and table[sl, 2] == e - b
+    used = set(slots)
+    for sl in range(table.shape[0]):
+        if sl not in used:
+            assert table[sl, 2] == 0
+    # cumulative log decay, restarted per chunk, log2-scaled
+    cs_ref = oracle.chunk_cumsum(la, chunks)
+    cs_gpu = ws.cumsum().cpu().numpy()
+    for (r, b, e), sl in zip(chunks, slots):
+        ref = cs_ref[r, b:e].T * LOG2E                       # [H, q]
+        got = cs_gpu[sl, :, :e - b]
+        assert np.max(np.abs(got - ref)) <= 1e-4 + 1e-5 * np.max(np.abs(ref))
+        # padding positions repeat the chunk total
+        assert np.all(cs_gpu[sl, :, e - b:] == cs_gpu[sl, :, e - b - 1:e - b])
+    # right factors = oracle restarted at every chunk start
+    _, cst_ref, _ = oracle.scan(X, la, B, C, segments=chunks, want_y=False)
+    cst_gpu = ws.chunk_states().cpu().numpy()[slots]
+    assert_close(cst_gpu, cst_ref, dts, "chunk states")
+    # centre factors = oracle state entering each chunk (zero at sequence starts)
+    snap = -np.ones(rows * T, np.int32)
+    first = []
+    bounds = set() if cu is None else set(int(v) for v in cu)
+    for k, (r, b, e) in enumerate(chunks):
+        if k + 1 < len(chunks) and chunks[k + 1][0] == r and chunks[k + 1][1] == e and e not in bounds:
+            snap[r * T + e - 1] = k + 1
+    for k, (r, b, e) in enumerate(chunks):
+        is_first = (cu is None and b == 0) or (cu is not None and b in set(cu.tolist()))
+        first.append(is_first)
+    segs = oracle.sequence_segments(rows, T, cu)
+    _, _, snaps = oracle.scan(X, la, B, C, segments=segs, want_y=False, snap_slot=snap, nsnaps=len(chunks) + 1)
+    st_gpu = ws.start_states().float().cpu().numpy()[slots]
+    for k in range(len(chunks)):
+        if first[k]:
+            assert np.all(st_gpu[k] == 0)
+    idx = [k for k in range(len(chunks)) if not first[k]]
+    assert_close(st_gpu[idx], snaps[idx], dts, "start states")
+    # stage-by-stage equals ssd_fwd bitwise
+    Y2, fin2 = gpu_fwd(d, Q)
+    assert torch.equal(Y, Y2) and torch.equal(fin, fin2)
+
+
+def test_deterministic():
+    d = synth.make_forward_inputs(1, 1024, 4, 64, 128, 1, dtype=torch.bfloat16, seed=31)
+    Y1, f1 = gpu_fwd(d, 128)
+    Y2, f2 = gpu_fwd(d, 128)
+    assert torch.equal(Y1, Y2) and torch.equal(f1, f2)
+
+
+# ------------------------------------------------------------------ decode step
+
+@pytest.mark.parametrize("dt,N", [(torch.bfloat16, 128), (torch.float32, 16), (torch.bfloat16, 256),
+                                  (torch.bfloat16, 32)])
+def test_step_sequence(dt, N):
+    b, steps, H, P = 3, 40, 4, 64 if N != 16 else 16
+    d = synth.make_decode_inputs(b, steps, H, P, N, 2, dtype=dt, seed=50 + N)
+    say(f"[parity] step b={b} steps={steps} H={H} P={P} N={N} {dt}")
+    state = torch.zeros(b, H, P, N, dtype=torch.float32, device="cuda")
+    dd = to_dev(d)
+    ys = []
+    for t in range(steps):
+        ys.append(ssd.step(state, dd["x"][t], dd["log_a"][t], dd["B"][t], dd["C"][t]))
+    torch.cuda.synchronize()
+    Yg = torch.stack(ys, 1)                          # [b, steps, H, P]
+    X = to_f64(d["x"]).transpose(1, 0, 2, 3)
+    la = to_f64(d["log_a"]).transpose(1, 0, 2)
+    B = to_f64(d["B"]).transpose(1, 0, 2, 3)
+    C = to_f64(d["C"]).transpose(1, 0, 2, 3)
+    Yr, fr = oracle.forward(X, la, B, C)
+    dts = dtype_name(d["x"])
+    assert_close(to_f64(Yg), Yr, dts, "step y")
+    assert_close(to_f64(state), fr, dts, "step state")
+
+
+def test_prefill_then_decode_handoff():
+    """ssd_fwd over [0, T1) then ssd_step over [T1, T) equals the oracle over [0, T)."""
+    b, T, T1, H, P, N = 2, 300, 237, 4, 64, 128
+    d = synth.make_forward_inputs(b, T, H, P, N, 1, dtype=torch.bfloat16, seed=60)
+    dd = to_dev(d)
+    _, fin = ssd.fwd(dd["X"][:, :T1].contiguous(), dd["log_a"][:, :T1].contiguous(), dd["B"][:, :T1].contiguous(),
+                     dd["C"][:, :T1].contiguous(), chunk=128)
+    state = fin.clone()
+    ys = []
+    for t in range(T1, T):
+        ys.append(ssd.step(state, dd["X"][:, t].contiguous(), dd["log_a"][:, t].contiguous(),
+                           dd["B"][:, t].contiguous(), dd["C"][:, t].contiguous()))
+    torch.cuda.synchronize()
+    Yr, fr = oracle_fwd(d)
+    assert_close(to_f64(torch.stack(ys, 1)), Yr[:, T1:], "bf16", "handoff y")
+    assert_close(to_f64(state), fr, "bf16", "handoff final")
+
+
+def test_decode_workload_full_size_sampled():
+    """All 4096 steps at batch 64, 80 heads; the oracle follows 24 sampled (row, head) streams."""
+    w = synth.WORKLOADS["decode-b64-H80-N128"]
+    say(f"[parity] decode workload {w}")
+    d = synth.workload_inputs(w)
+    dd = to_dev(d)
+    state = torch.zeros(w.batch, w.H, w.P, w.N, dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(7)
+    pairs = [(int(r), int(h)) for r, h in zip(rng.integers(0, w.batch, 24), rng.integers(0, w.H, 24))]
+    ys = torch.empty(w.steps, len(pairs), w.P, dtype=torch.bfloat16, device="cuda")
+    rows = torch.tensor([p[0] for p in pairs], device="cuda")
+    heads = torch.tensor([p[1] for p in pairs], device="cuda")
+    y = torch.empty(w.batch, w.H, w.P, dtype=torch.bfloat16, device="cuda")
+    for t in range(w.steps):
+        ssd.step(state, dd["x"][t], dd["log_a"][t], dd["B"][t], dd["C"][t], y=y)
+        ys[t] = y[rows, heads]
+    torch.cuda.synchronize()
+    r = torch.tensor([p[0] for p in pairs])
+    h = torch.tensor([p[1] for p in pairs])
+    # each sampled stream as its own row of a one-head oracle run (index first, then upcast)
+    X = to_f64(d["x"][:, r, h, :]).transpose(1, 0, 2)[:, :, None, :]
+    la = to_f64(d["log_a"][:, r, h]).T[:, :, None]
+    B = to_f64(d["B"][:, r, 0, :]).transpose(1, 0, 2)[:, :, None, :]
+    C = to_f64(d["C"][:, r, 0, :]).transpose(1, 0, 2)[:, :, None, :]
+    Yr, fr = oracle.forward(X, la, B, C)
+    assert_close(to_f64(ys).transpose(1, 0, 2), Yr[:, :, 0, :], "bf16", "decode y")
+    assert_close(to_f64(state[rows, heads]), fr[:, 0], "bf16", "decode state")
