@@ -34,7 +34,7 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def stage_bytes(w, nslots: int, nseq: int) -> dict:
+def stage_bytes(w, nslots: int, nblocks: int, nseq: int) -> dict:
     """Algorithmic HBM bytes of one launch of each stage (each tensor counted once)."""
     esz = 2 if w.dtype == "bf16" else 4
     tok = w.batch * w.T
@@ -42,16 +42,16 @@ def stage_bytes(w, nslots: int, nseq: int) -> dict:
     BC = tok * w.G * w.N * esz
     la = tok * w.H * 4
     cs = nslots * w.H * w.Q * 4
-    table = nslots * 16
-    states = nslots * w.H * w.P * w.N * 4
-    starts = nslots * w.H * w.P * w.N * esz
+    tables = nslots * 16 + nblocks * 16
+    states = nblocks * w.H * w.P * w.N * 4
+    starts = nblocks * w.H * w.P * w.N * esz
     final = nseq * w.H * w.P * w.N * 4
-    decay = nslots * w.H * 4
+    decay = nblocks * w.H * 4
     return {
-        "chunk_cumsum": la + cs + table,
-        "chunk_state": X + BC + cs + table + states,
+        "chunk_cumsum": la + cs + tables,
+        "chunk_state": X + BC + cs + tables + states + decay,
         "state_passing": states + decay + starts + final,
-        "chunk_scan": X + 2 * BC + cs + table + starts + X,   # X read, Y written
+        "chunk_scan": X + 2 * BC + cs + tables + starts + X,   # X read, Y written
     }
 
 
@@ -76,6 +76,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=4096)
+    ap.add_argument("--state-block", type=int, default=0, help="chunks per state block (0: library default)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -100,13 +101,13 @@ def main() -> int:
     d = synth.workload_inputs(w)
     X, la, B, C = (d[k].to(dev) for k in ("X", "log_a", "B", "C"))
     shape = ssd.make_shape(X, B, None)
-    ws = ssd.Workspace(shape, w.Q, dev)
+    ws = ssd.Workspace(shape, w.Q, dev, args.state_block)
     Y = torch.empty_like(X)
     fin = torch.empty(w.batch, w.H, w.P, w.N, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        ssd.fwd(X, la, B, C, chunk=w.Q, Y=Y, final_state=fin, workspace=ws)
+        ssd.fwd(X, la, B, C, chunk=w.Q, state_block=ws.state_block, Y=Y, final_state=fin, workspace=ws)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -132,10 +133,10 @@ def main() -> int:
     # per-stage average launch time, HIP events on the launch stream
     log(f"[bench] per-stage timing, {args.stage_reps} reps")
     stages = [
-        ("chunk_cumsum", lambda: ssd.chunk_cumsum(la, None, w.Q, shape, ws)),
-        ("chunk_state", lambda: ssd.chunk_state(X, B, None, w.Q, shape, ws)),
-        ("state_passing", lambda: ssd.state_passing(None, w.Q, fin, shape, ws)),
-        ("chunk_scan", lambda: ssd.chunk_scan(X, B, C, None, w.Q, Y, shape, ws)),
+        ("chunk_cumsum", lambda: ssd.chunk_cumsum(la, None, shape, ws)),
+        ("chunk_state", lambda: ssd.chunk_state(X, B, None, shape, ws)),
+        ("state_passing", lambda: ssd.state_passing(None, fin, shape, ws)),
+        ("chunk_scan", lambda: ssd.chunk_scan(X, B, C, None, Y, shape, ws)),
     ]
     acc = {name: 0.0 for name, _ in stages}
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
@@ -148,8 +149,7 @@ def main() -> int:
         for (name, _), (a, b) in zip(stages, evs):
             acc[name] += a.elapsed_time(b)
     stage_us = {k: v * 1e3 / args.stage_reps for k, v in acc.items()}
-    nslots = ws.layout.nslots
-    sbytes = stage_bytes(w, nslots, w.batch)
+    sbytes = stage_bytes(w, ws.layout.nslots, ws.layout.nblocks, w.batch)
     dominant = max(stage_us, key=stage_us.get)
     achieved = sbytes[dominant] / (stage_us[dominant] * 1e-6) / 1e9
     chunk_lengths = [min(w.Q, w.T - k * w.Q) for k in range(-(-w.T // w.Q))] * w.batch
@@ -173,7 +173,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic (seeded: X~N(0,1), log_a=-dt*A, dt~U(0.001,0.1), A~U(1,16), B,C~N(0,1)/sqrt(N))",
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.T, "heads": w.H, "headdim": w.P,
-                   "dstate": w.N, "ngroups": w.G, "chunk": w.Q, "parallelism": "none (1 GPU)"},
+                   "dstate": w.N, "ngroups": w.G, "chunk": w.Q, "state_block": ws.state_block,
+                   "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": sbytes[dominant], "avg_launch_us": round(stage_us[dominant], 3)},

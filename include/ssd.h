@@ -42,9 +42,10 @@
  * not validated; log_a = -inf is not supported on the GPU.
  *
  * Supported sizes: headdim in {16, 32, 64, 128}; dstate in {16, 32, 64, 128,
- * 256}; chunk in {16, 32, 64, 128, 256}; for bf16, chunk >= 32 and dstate >= 32.
- * Other sizes return SSD_ERR_UNSUPPORTED. Every tensor must hold fewer than
- * 2^31 elements.
+ * 256}; chunk in {16, 32, 64, 128, 256}; state_block in {1, 2, 4, 8, 16}; for
+ * bf16, chunk >= 32 and dstate >= 32 and the chunk tiles must fit the 160 KiB
+ * LDS; for fp32, state_block = 1. Other sizes return SSD_ERR_UNSUPPORTED. Every
+ * tensor must hold fewer than 2^31 elements.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
@@ -80,26 +81,47 @@ typedef struct {
 } ssd_shape;
 
 /*
+ * Two-level chunking. Chunks of `chunk` tokens are the blocks of the
+ * quadratic form. State blocks of `state_block` consecutive chunks of one
+ * sequence are the units of the state recurrence: the right factor and the
+ * centre factor are computed per state block, and the chunk-scan stage carries
+ * the state through the chunks of each state block itself. state_block = 1 is
+ * exactly the pages' schedule (one chunk state per chunk); larger values give
+ * the same result up to rounding with less HBM traffic. fp32 tensors support
+ * state_block = 1 only. ssd_fwd chooses state_block itself
+ * (ssd_default_state_block); ssd_fwd_ex takes it as an argument.
+ *
  * Workspace of one forward call, carved from one caller buffer (offsets in
  * bytes from its start, each 256-byte aligned). nslots = batch * slots_per_row
- * chunk slots; a slot may be empty (packed rows leave gaps).
+ * chunk slots and nblocks = batch * blocks_per_row state-block slots; a slot
+ * may be empty (packed rows leave gaps).
  *   table        int32 [nslots][4]: sequence, first token (flattened: row * seqlen + t),
- *                length, chunk index in sequence
+ *                length (0: empty slot), chunk index in sequence
+ *   block_table  int32 [nblocks][4]: sequence, first chunk slot, number of chunks
+ *                (0: empty slot), 0
  *   cumsum       fp32  [nslots][H][chunk]: log2(e) * cumulative log_a, restarted per chunk,
  *                positions past the chunk's length repeat its total
- *   chunk_states fp32  [nslots][H][P][N]: right factors, state at the chunk end from a zero start
- *   start_states dtype [nslots][H][P][N]: centre factors, state entering the chunk
+ *   block_decay  fp32  [nblocks][H]: log2(e) * total log_a of each state block
+ *   block_states fp32  [nblocks][H][P][N]: right factors, state at the block end from a
+ *                zero start
+ *   start_states dtype [nblocks][H][P][N]: centre factors, state entering the block
  *                (bf16 for bf16 inputs, fp32 for fp32 inputs)
- * Packed rows: sequence s owns slots floor(cu[s]/chunk) + s + j for its chunks
- * j = 0 .. ceil(len_s/chunk) - 1. Unpacked rows: row r owns slots
- * r*slots_per_row + j with slots_per_row = ceil(seqlen/chunk).
+ * Packed rows: sequence s owns chunk slots floor(cu[s]/chunk) + s + j for its
+ * chunks j = 0 .. ceil(len_s/chunk) - 1, and state-block slots
+ * floor(cu[s]/(chunk*state_block)) + s + j. Unpacked rows: row r owns chunk
+ * slots r*slots_per_row + j with slots_per_row = ceil(seqlen/chunk), and block
+ * slots r*blocks_per_row + j with blocks_per_row = ceil(slots_per_row/state_block).
  */
 typedef struct {
   int64_t slots_per_row;
   int64_t nslots;
+  int64_t blocks_per_row;
+  int64_t nblocks;
   size_t table_offset;
+  size_t block_table_offset;
   size_t cumsum_offset;
-  size_t chunk_states_offset;
+  size_t block_decay_offset;
+  size_t block_states_offset;
   size_t start_states_offset;
   size_t total_bytes;
 } ssd_layout;
@@ -110,51 +132,65 @@ int32_t ssd_abi_version(void);
 /* Human-readable name of a status code (static storage). */
 const char* ssd_status_string(ssd_status status);
 
-/* Workspace layout and size of ssd_fwd for this shape and chunk length. */
-ssd_status ssd_fwd_layout(const ssd_shape* shape, int32_t chunk, ssd_layout* layout);
-ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, size_t* bytes);
+/* The state_block ssd_fwd uses for this shape and chunk length (1 for fp32). */
+int32_t ssd_default_state_block(const ssd_shape* shape, int32_t chunk);
+
+/* Workspace layout and size of a forward call for this shape, chunk length and
+ * state block (state_block <= 0 selects ssd_default_state_block). */
+ssd_status ssd_fwd_layout(const ssd_shape* shape, int32_t chunk, int32_t state_block, ssd_layout* layout);
+ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_t state_block,
+                                   size_t* bytes);
 
 /*
- * Forward pass: Y and final states from zero initial states.
- * Runs the four stages below in order on `stream`. final_state may be NULL.
+ * Forward pass: Y and final states from zero initial states, with the default
+ * state block. Runs the four stages below in order on `stream`. final_state
+ * may be NULL. The workspace must hold ssd_fwd_workspace_bytes(shape, chunk, 0).
  */
 ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void* C,
                    const int32_t* cu_seqlens, int32_t chunk, void* Y, float* final_state,
                    const ssd_shape* shape, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Forward pass with an explicit state block (state_block <= 0: the default). */
+ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const void* C,
+                      const int32_t* cu_seqlens, int32_t chunk, int32_t state_block, void* Y,
+                      float* final_state, const ssd_shape* shape, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /*
- * The four stages of ssd_fwd, callable one by one (same arguments, same
+ * The four stages of ssd_fwd_ex, callable one by one (same arguments, same
  * workspace; each stage reads what the previous stages wrote).
  *
  * ssd_chunk_cumsum -- segment sums of log a: the cumulative log decay
  *   restarted in every chunk, from which the 1-semiseparable mask
  *   L[i][j] = exp(cs_i - cs_j) (i >= j) and the chunk totals follow (paper card
  *   Method 5 pseudocode "decay_cumsum" and "chunk_decay"; Pitfalls: mask before
- *   exp). Writes table and cumsum.
- * ssd_chunk_state -- right factors: s_k = sum_j exp(cs_last - cs_j) x_j B_j^T
- *   per chunk and head, one batched matrix product per chunk (paper section 6,
- *   "Right Factors"). Writes chunk_states.
- * ssd_state_passing -- centre factors: h = 0; for each chunk k of a sequence,
- *   start_k = h, h = exp(A_k) h + s_k with A_k the chunk's total log decay
- *   (paper section 6, "Center Factors"); writes start_states and, when
+ *   exp). Writes table, block_table and cumsum.
+ * ssd_chunk_state -- right factors: s_m = sum_j exp(total decay from j to the
+ *   end of block m) x_j B_j^T per state block and head, batched matrix
+ *   products over tokens (paper section 6, "Right Factors"). Writes
+ *   block_states and block_decay.
+ * ssd_state_passing -- centre factors: h = 0; for each state block m of a
+ *   sequence, start_m = h, h = exp(A_m) h + s_m with A_m the block's total log
+ *   decay (paper section 6, "Center Factors"); writes start_states and, when
  *   final_state is not NULL, the state after each sequence.
  * ssd_chunk_scan -- diagonal blocks plus left factors: Y = (L o C B^T) X within
- *   the chunk plus exp(cs) C start^T for the carried-in state (paper section 6,
- *   "Diagonal Blocks" and "Left Factors"). Writes Y.
+ *   each chunk plus exp(cs) C h^T for the state h entering the chunk (paper
+ *   section 6, "Diagonal Blocks" and "Left Factors"); inside a state block the
+ *   stage advances h from chunk to chunk itself. Writes Y.
  */
 ssd_status ssd_chunk_cumsum(const float* log_a, const int32_t* cu_seqlens, int32_t chunk,
-                            const ssd_shape* shape, void* workspace, size_t workspace_bytes,
-                            void* stream);
+                            int32_t state_block, const ssd_shape* shape, void* workspace,
+                            size_t workspace_bytes, void* stream);
 ssd_status ssd_chunk_state(const void* X, const void* B, const int32_t* cu_seqlens, int32_t chunk,
-                           const ssd_shape* shape, void* workspace, size_t workspace_bytes,
-                           void* stream);
-ssd_status ssd_state_passing(const int32_t* cu_seqlens, int32_t chunk, float* final_state,
-                             const ssd_shape* shape, void* workspace, size_t workspace_bytes,
-                             void* stream);
+                           int32_t state_block, const ssd_shape* shape, void* workspace,
+                           size_t workspace_bytes, void* stream);
+ssd_status ssd_state_passing(const int32_t* cu_seqlens, int32_t chunk, int32_t state_block,
+                             float* final_state, const ssd_shape* shape, void* workspace,
+                             size_t workspace_bytes, void* stream);
 ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int32_t* cu_seqlens,
-                          int32_t chunk, void* Y, const ssd_shape* shape, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          int32_t chunk, int32_t state_block, void* Y, const ssd_shape* shape,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step for `batch` independent streams: the loop body of

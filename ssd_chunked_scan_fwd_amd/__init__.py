@@ -6,8 +6,8 @@ thin ctypes layer over it. Importing the package does not load the library:
 the first call does, and it raises if the library is missing.
 """
 from . import synth  # noqa: F401
-from .binding import (SSDError, Shape, Workspace, chunk_cumsum, chunk_scan, chunk_state, fwd,  # noqa: F401
-                      layout, lib, make_shape, state_passing, step, workspace_bytes)
+from .binding import (SSDError, Shape, Workspace, chunk_cumsum, chunk_scan, chunk_state,  # noqa: F401
+                      default_state_block, fwd, layout, lib, make_shape, state_passing, step, workspace_bytes)
 
 __all__ = ["synth", "fwd", "step", "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "Workspace",
-           "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib"]
+           "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib", "default_state_block"]

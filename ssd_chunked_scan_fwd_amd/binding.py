@@ -23,8 +23,9 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARGUMENT", 2: "SSD_ERR_UNSUPPORTED",
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # Every symbol include/ssd.h declares.
-EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_fwd_layout", "ssd_fwd_workspace_bytes", "ssd_fwd",
-           "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_step")
+EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "ssd_fwd_layout",
+           "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
+           "ssd_state_passing", "ssd_chunk_scan", "ssd_step")
 
 
 class SSDError(RuntimeError):
@@ -40,8 +41,10 @@ class Shape(ctypes.Structure):
 
 
 class Layout(ctypes.Structure):
-    _fields_ = [("slots_per_row", ctypes.c_int64), ("nslots", ctypes.c_int64), ("table_offset", ctypes.c_size_t),
-                ("cumsum_offset", ctypes.c_size_t), ("chunk_states_offset", ctypes.c_size_t),
+    _fields_ = [("slots_per_row", ctypes.c_int64), ("nslots", ctypes.c_int64), ("blocks_per_row", ctypes.c_int64),
+                ("nblocks", ctypes.c_int64), ("table_offset", ctypes.c_size_t),
+                ("block_table_offset", ctypes.c_size_t), ("cumsum_offset", ctypes.c_size_t),
+                ("block_decay_offset", ctypes.c_size_t), ("block_states_offset", ctypes.c_size_t),
                 ("start_states_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
 
 
@@ -62,20 +65,24 @@ def lib():
         L.ssd_abi_version.argtypes = []
         L.ssd_status_string.restype = ctypes.c_char_p
         L.ssd_status_string.argtypes = [ctypes.c_int]
+        L.ssd_default_state_block.restype = i32
+        L.ssd_default_state_block.argtypes = [shp, i32]
         L.ssd_fwd_layout.restype = ctypes.c_int
-        L.ssd_fwd_layout.argtypes = [shp, i32, ctypes.POINTER(Layout)]
+        L.ssd_fwd_layout.argtypes = [shp, i32, i32, ctypes.POINTER(Layout)]
         L.ssd_fwd_workspace_bytes.restype = ctypes.c_int
-        L.ssd_fwd_workspace_bytes.argtypes = [shp, i32, ctypes.POINTER(sz)]
+        L.ssd_fwd_workspace_bytes.argtypes = [shp, i32, i32, ctypes.POINTER(sz)]
         L.ssd_fwd.restype = ctypes.c_int
         L.ssd_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, shp, vp, sz, vp]
+        L.ssd_fwd_ex.restype = ctypes.c_int
+        L.ssd_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, shp, vp, sz, vp]
         L.ssd_chunk_cumsum.restype = ctypes.c_int
-        L.ssd_chunk_cumsum.argtypes = [vp, vp, i32, shp, vp, sz, vp]
+        L.ssd_chunk_cumsum.argtypes = [vp, vp, i32, i32, shp, vp, sz, vp]
         L.ssd_chunk_state.restype = ctypes.c_int
-        L.ssd_chunk_state.argtypes = [vp, vp, vp, i32, shp, vp, sz, vp]
+        L.ssd_chunk_state.argtypes = [vp, vp, vp, i32, i32, shp, vp, sz, vp]
         L.ssd_state_passing.restype = ctypes.c_int
-        L.ssd_state_passing.argtypes = [vp, i32, vp, shp, vp, sz, vp]
+        L.ssd_state_passing.argtypes = [vp, i32, i32, vp, shp, vp, sz, vp]
         L.ssd_chunk_scan.restype = ctypes.c_int
-        L.ssd_chunk_scan.argtypes = [vp, vp, vp, vp, i32, vp, shp, vp, sz, vp]
+        L.ssd_chunk_scan.argtypes = [vp, vp, vp, vp, i32, i32, vp, shp, vp, sz, vp]
         L.ssd_step.restype = ctypes.c_int
         L.ssd_step.argtypes = [vp, vp, vp, vp, vp, vp, shp, vp]
         _lib = L
@@ -111,26 +118,31 @@ def make_shape(X: torch.Tensor, B: torch.Tensor, cu_seqlens: Optional[torch.Tens
     return Shape(b, T, H, G, P, N, S, _dtype_code(X.dtype))
 
 
-def layout(shape: Shape, chunk: int) -> Layout:
+def default_state_block(shape: Shape, chunk: int) -> int:
+    return int(lib().ssd_default_state_block(ctypes.byref(shape), int(chunk)))
+
+
+def layout(shape: Shape, chunk: int, state_block: int = 0) -> Layout:
     L = Layout()
-    _call("ssd_fwd_layout", ctypes.byref(shape), int(chunk), ctypes.byref(L))
+    _call("ssd_fwd_layout", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(L))
     return L
 
 
-def workspace_bytes(shape: Shape, chunk: int) -> int:
+def workspace_bytes(shape: Shape, chunk: int, state_block: int = 0) -> int:
     n = ctypes.c_size_t(0)
-    _call("ssd_fwd_workspace_bytes", ctypes.byref(shape), int(chunk), ctypes.byref(n))
+    _call("ssd_fwd_workspace_bytes", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(n))
     return int(n.value)
 
 
 class Workspace:
-    """A caller-owned workspace for one shape and chunk length, with typed views
-    of the stages' intermediate results (for inspection and tests)."""
+    """A caller-owned workspace for one shape, chunk length and state block, with
+    typed views of the stages' intermediate results (for inspection and tests)."""
 
-    def __init__(self, shape: Shape, chunk: int, device):
+    def __init__(self, shape: Shape, chunk: int, device, state_block: int = 0):
         self.shape = shape
         self.chunk = int(chunk)
-        self.layout = layout(shape, chunk)
+        self.state_block = int(state_block) if state_block > 0 else default_state_block(shape, chunk)
+        self.layout = layout(shape, chunk, self.state_block)
         self.buffer = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=device)
 
     @property
@@ -145,18 +157,26 @@ class Workspace:
         n = self.layout.nslots
         return self._view(self.layout.table_offset, n * 4, torch.int32, (n, 4))
 
+    def block_table(self) -> torch.Tensor:
+        n = self.layout.nblocks
+        return self._view(self.layout.block_table_offset, n * 4, torch.int32, (n, 4))
+
     def cumsum(self) -> torch.Tensor:
         s, n = self.shape, self.layout.nslots
         return self._view(self.layout.cumsum_offset, n * s.nheads * self.chunk, torch.float32,
                           (n, s.nheads, self.chunk))
 
-    def chunk_states(self) -> torch.Tensor:
-        s, n = self.shape, self.layout.nslots
-        return self._view(self.layout.chunk_states_offset, n * s.nheads * s.headdim * s.dstate, torch.float32,
+    def block_decay(self) -> torch.Tensor:
+        s, n = self.shape, self.layout.nblocks
+        return self._view(self.layout.block_decay_offset, n * s.nheads, torch.float32, (n, s.nheads))
+
+    def block_states(self) -> torch.Tensor:
+        s, n = self.shape, self.layout.nblocks
+        return self._view(self.layout.block_states_offset, n * s.nheads * s.headdim * s.dstate, torch.float32,
                           (n, s.nheads, s.headdim, s.dstate))
 
     def start_states(self) -> torch.Tensor:
-        s, n = self.shape, self.layout.nslots
+        s, n = self.shape, self.layout.nblocks
         dt = torch.bfloat16 if s.dtype == DTYPE_BF16 else torch.float32
         return self._view(self.layout.start_states_offset, n * s.nheads * s.headdim * s.dstate, dt,
                           (n, s.nheads, s.headdim, s.dstate))
@@ -175,10 +195,13 @@ def _check_inputs(X, log_a, B, C, cu_seqlens):
 
 
 def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
-        cu_seqlens: Optional[torch.Tensor] = None, chunk: int = 128, Y: Optional[torch.Tensor] = None,
-        final_state: Optional[torch.Tensor] = None, want_final: bool = True,
+        cu_seqlens: Optional[torch.Tensor] = None, chunk: int = 128, state_block: int = 0,
+        Y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None, want_final: bool = True,
         workspace: Optional[Workspace] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunked SSD forward pass (ssd_fwd). Returns (Y, final_state or None)."""
+    """Chunked SSD forward pass (ssd_fwd_ex). Returns (Y, final_state or None).
+
+    state_block <= 0 uses the library's default (the workspace's, when one is given).
+    """
     _check_inputs(X, log_a, B, C, cu_seqlens)
     shape = make_shape(X, B, cu_seqlens)
     if Y is None:
@@ -187,30 +210,33 @@ def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         nseq = X.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
         final_state = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
     if workspace is None:
-        workspace = Workspace(shape, chunk, X.device)
-    _call("ssd_fwd", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), int(chunk), _ptr(Y),
-          _ptr(final_state), ctypes.byref(shape), _ptr(workspace.buffer), workspace.nbytes, _stream(X.device))
+        workspace = Workspace(shape, chunk, X.device, state_block)
+    elif state_block > 0 and state_block != workspace.state_block:
+        raise ValueError("state_block differs from the workspace's")
+    _call("ssd_fwd_ex", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), int(chunk), workspace.state_block,
+          _ptr(Y), _ptr(final_state), ctypes.byref(shape), _ptr(workspace.buffer), workspace.nbytes,
+          _stream(X.device))
     return Y, final_state
 
 
-def chunk_cumsum(log_a, cu_seqlens, chunk, shape: Shape, ws: Workspace):
-    _call("ssd_chunk_cumsum", _ptr(log_a), _ptr(cu_seqlens), int(chunk), ctypes.byref(shape), _ptr(ws.buffer),
-          ws.nbytes, _stream(ws.buffer.device))
-
-
-def chunk_state(X, B, cu_seqlens, chunk, shape: Shape, ws: Workspace):
-    _call("ssd_chunk_state", _ptr(X), _ptr(B), _ptr(cu_seqlens), int(chunk), ctypes.byref(shape), _ptr(ws.buffer),
-          ws.nbytes, _stream(ws.buffer.device))
-
-
-def state_passing(cu_seqlens, chunk, final_state, shape: Shape, ws: Workspace):
-    _call("ssd_state_passing", _ptr(cu_seqlens), int(chunk), _ptr(final_state), ctypes.byref(shape),
+def chunk_cumsum(log_a, cu_seqlens, shape: Shape, ws: Workspace):
+    _call("ssd_chunk_cumsum", _ptr(log_a), _ptr(cu_seqlens), ws.chunk, ws.state_block, ctypes.byref(shape),
           _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
 
 
-def chunk_scan(X, B, C, cu_seqlens, chunk, Y, shape: Shape, ws: Workspace):
-    _call("ssd_chunk_scan", _ptr(X), _ptr(B), _ptr(C), _ptr(cu_seqlens), int(chunk), _ptr(Y), ctypes.byref(shape),
+def chunk_state(X, B, cu_seqlens, shape: Shape, ws: Workspace):
+    _call("ssd_chunk_state", _ptr(X), _ptr(B), _ptr(cu_seqlens), ws.chunk, ws.state_block, ctypes.byref(shape),
           _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
+
+
+def state_passing(cu_seqlens, final_state, shape: Shape, ws: Workspace):
+    _call("ssd_state_passing", _ptr(cu_seqlens), ws.chunk, ws.state_block, _ptr(final_state), ctypes.byref(shape),
+          _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
+
+
+def chunk_scan(X, B, C, cu_seqlens, Y, shape: Shape, ws: Workspace):
+    _call("ssd_chunk_scan", _ptr(X), _ptr(B), _ptr(C), _ptr(cu_seqlens), ws.chunk, ws.state_block, _ptr(Y),
+          ctypes.byref(shape), _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
 
 
 def step(state: torch.Tensor, x: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

@@ -40,7 +40,8 @@ ssd_status check_shape(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
     return SSD_ERR_UNSUPPORTED;
   if (s->dtype == SSD_DTYPE_BF16) {
     if (chunk < 32 || s->dstate < 32) return SSD_ERR_UNSUPPORTED;
-    if (ssd::chunk_scan_bf16_lds_bytes(s->headdim, s->dstate, chunk) > ssd::kMaxLdsBytes)
+    if (ssd::chunk_scan_bf16_lds_bytes(s->headdim, s->dstate, chunk) > ssd::kMaxLdsBytes ||
+        ssd::chunk_state_bf16_lds_bytes(s->headdim, s->dstate) > ssd::kMaxLdsBytes)
       return SSD_ERR_UNSUPPORTED;
   }
   const int64_t bt = (int64_t)s->batch * s->seqlen;
@@ -49,25 +50,51 @@ ssd_status check_shape(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
   return SSD_OK;
 }
 
-ssd_status make_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk, ssd_layout* out) {
+int32_t default_state_block(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
+  if (s->dtype != SSD_DTYPE_BF16) return 1;
+  // Longer state blocks cut the right-factor and state traffic; keep at least
+  // about two (state block, head) workgroups per CU (256 CUs).
+  const int64_t T = s->seqlen;
+  const int64_t chunks = cu ? (T / chunk + s->num_seqs) : (int64_t)s->batch * ((T + chunk - 1) / chunk);
+  const int64_t units = chunks * s->nheads;
+  int32_t gs = 1;
+  while (gs < 8 && units / (2 * gs) >= 512) gs *= 2;
+  return gs;
+}
+
+ssd_status check_state_block(const ssd_shape* s, int32_t state_block) {
+  if (!pow2_in(state_block, 1, 16)) return SSD_ERR_UNSUPPORTED;
+  if (s->dtype != SSD_DTYPE_BF16 && state_block != 1) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+ssd_status make_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk, int32_t gs, ssd_layout* out) {
   ssd_layout L{};
   const int64_t T = s->seqlen;
+  const int64_t span = (int64_t)chunk * gs;
   L.slots_per_row = cu ? (T / chunk + s->num_seqs) : ((T + chunk - 1) / chunk);
   L.nslots = (int64_t)s->batch * L.slots_per_row;
+  L.blocks_per_row = cu ? (T / span + s->num_seqs) : ((L.slots_per_row + gs - 1) / gs);
+  L.nblocks = (int64_t)s->batch * L.blocks_per_row;
   const int64_t H = s->nheads, PN = (int64_t)s->headdim * s->dstate;
-  if (L.nslots * H * PN > kMaxElems || L.nslots * H * chunk > kMaxElems) return SSD_ERR_UNSUPPORTED;
+  if (L.nblocks * H * PN > kMaxElems || L.nslots * H * chunk > kMaxElems) return SSD_ERR_UNSUPPORTED;
   const int64_t nseq = cu ? s->num_seqs : s->batch;
   if (nseq * H * PN > kMaxElems) return SSD_ERR_UNSUPPORTED;
+  if (L.slots_per_row > INT32_MAX / 2 || L.nblocks * H > INT32_MAX) return SSD_ERR_UNSUPPORTED;
   const size_t esz = s->dtype == SSD_DTYPE_BF16 ? 2 : 4;
   size_t off = 0;
   L.table_offset = off;
   off = align256(off + (size_t)L.nslots * 16);
+  L.block_table_offset = off;
+  off = align256(off + (size_t)L.nblocks * 16);
   L.cumsum_offset = off;
   off = align256(off + (size_t)L.nslots * H * chunk * 4);
-  L.chunk_states_offset = off;
-  off = align256(off + (size_t)L.nslots * H * PN * 4);
+  L.block_decay_offset = off;
+  off = align256(off + (size_t)L.nblocks * H * 4);
+  L.block_states_offset = off;
+  off = align256(off + (size_t)L.nblocks * H * PN * 4);
   L.start_states_offset = off;
-  off = align256(off + (size_t)L.nslots * H * PN * esz);
+  off = align256(off + (size_t)L.nblocks * H * PN * esz);
   L.total_bytes = off;
   *out = L;
   return SSD_OK;
@@ -80,25 +107,30 @@ struct Prepared {
 
 // Full validation of a forward-stage call; fills `pp` on success.
 ssd_status prepare(int stages, const void* X, const float* log_a, const void* B, const void* C,
-                   const void* Y, const int32_t* cu, int32_t chunk, const ssd_shape* s, void* workspace,
-                   size_t workspace_bytes, Prepared* pp) {
+                   const void* Y, const int32_t* cu, int32_t chunk, int32_t gs, const ssd_shape* s,
+                   void* workspace, size_t workspace_bytes, Prepared* pp) {
   ssd_status st = check_shape(s, cu, chunk);
+  if (st != SSD_OK) return st;
+  if (gs <= 0) gs = default_state_block(s, cu, chunk);
+  st = check_state_block(s, gs);
   if (st != SSD_OK) return st;
   if ((stages & kCumsum) && !log_a) return SSD_ERR_INVALID_ARGUMENT;
   if ((stages & (kState | kScan)) && (!X || !B)) return SSD_ERR_INVALID_ARGUMENT;
   if ((stages & kScan) && (!C || !Y)) return SSD_ERR_INVALID_ARGUMENT;
   ssd_layout L;
-  st = make_layout(s, cu, chunk, &L);
+  st = make_layout(s, cu, chunk, gs, &L);
   if (st != SSD_OK) return st;
   if (!workspace) return SSD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < L.total_bytes) return SSD_ERR_WORKSPACE_TOO_SMALL;
   char* base = static_cast<char*>(workspace);
-  pp->d = ssd::FwdDims{s->batch, s->seqlen, s->nheads, s->ngroups, s->headdim, s->dstate, chunk,
+  pp->d = ssd::FwdDims{s->batch, s->seqlen, s->nheads, s->ngroups, s->headdim, s->dstate, chunk, gs,
                        cu ? s->num_seqs : 0, s->dtype == SSD_DTYPE_BF16 ? 1 : 0,
-                       (long)L.slots_per_row, (long)L.nslots};
+                       (long)L.slots_per_row, (long)L.nslots, (long)L.blocks_per_row, (long)L.nblocks};
   pp->ws = ssd::Workspace{reinterpret_cast<int4*>(base + L.table_offset),
+                          reinterpret_cast<int4*>(base + L.block_table_offset),
                           reinterpret_cast<float*>(base + L.cumsum_offset),
-                          reinterpret_cast<float*>(base + L.chunk_states_offset),
+                          reinterpret_cast<float*>(base + L.block_decay_offset),
+                          reinterpret_cast<float*>(base + L.block_states_offset),
                           static_cast<void*>(base + L.start_states_offset)};
   return SSD_OK;
 }
@@ -122,65 +154,79 @@ const char* ssd_status_string(ssd_status status) {
   return "SSD_ERR_UNKNOWN";
 }
 
-ssd_status ssd_fwd_layout(const ssd_shape* shape, int32_t chunk, ssd_layout* layout) {
+int32_t ssd_default_state_block(const ssd_shape* shape, int32_t chunk) {
+  const int32_t dummy = 0;
+  const int32_t* cu = (shape && shape->num_seqs > 0) ? &dummy : nullptr;
+  if (check_shape(shape, cu, chunk) != SSD_OK) return 1;
+  return default_state_block(shape, cu, chunk);
+}
+
+ssd_status ssd_fwd_layout(const ssd_shape* shape, int32_t chunk, int32_t state_block, ssd_layout* layout) {
   if (!layout) return SSD_ERR_INVALID_ARGUMENT;
   // The layout depends on whether rows are packed; num_seqs > 0 means packed.
   const int32_t dummy = 0;
   const int32_t* cu = (shape && shape->num_seqs > 0) ? &dummy : nullptr;
   ssd_status st = check_shape(shape, cu, chunk);
   if (st != SSD_OK) return st;
-  return make_layout(shape, cu, chunk, layout);
+  if (state_block <= 0) state_block = default_state_block(shape, cu, chunk);
+  st = check_state_block(shape, state_block);
+  if (st != SSD_OK) return st;
+  return make_layout(shape, cu, chunk, state_block, layout);
 }
 
-ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, size_t* bytes) {
+ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_t state_block, size_t* bytes) {
   if (!bytes) return SSD_ERR_INVALID_ARGUMENT;
   ssd_layout L;
-  ssd_status st = ssd_fwd_layout(shape, chunk, &L);
+  ssd_status st = ssd_fwd_layout(shape, chunk, state_block, &L);
   if (st != SSD_OK) return st;
   *bytes = L.total_bytes;
   return SSD_OK;
 }
 
-ssd_status ssd_chunk_cumsum(const float* log_a, const int32_t* cu_seqlens, int32_t chunk, const ssd_shape* shape,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+ssd_status ssd_chunk_cumsum(const float* log_a, const int32_t* cu_seqlens, int32_t chunk, int32_t state_block,
+                            const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
   Prepared pp;
-  ssd_status st = prepare(kCumsum, nullptr, log_a, nullptr, nullptr, nullptr, cu_seqlens, chunk, shape,
-                          workspace, workspace_bytes, &pp);
+  ssd_status st = prepare(kCumsum, nullptr, log_a, nullptr, nullptr, nullptr, cu_seqlens, chunk, state_block,
+                          shape, workspace, workspace_bytes, &pp);
   if (st != SSD_OK) return st;
   return hip_status(ssd::launch_chunk_cumsum(pp.d, log_a, cu_seqlens, pp.ws, (hipStream_t)stream));
 }
 
 ssd_status ssd_chunk_state(const void* X, const void* B, const int32_t* cu_seqlens, int32_t chunk,
-                           const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+                           int32_t state_block, const ssd_shape* shape, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   Prepared pp;
-  ssd_status st = prepare(kState, X, nullptr, B, nullptr, nullptr, cu_seqlens, chunk, shape, workspace,
-                          workspace_bytes, &pp);
+  ssd_status st = prepare(kState, X, nullptr, B, nullptr, nullptr, cu_seqlens, chunk, state_block, shape,
+                          workspace, workspace_bytes, &pp);
   if (st != SSD_OK) return st;
   return hip_status(ssd::launch_chunk_state(pp.d, X, B, pp.ws, (hipStream_t)stream));
 }
 
-ssd_status ssd_state_passing(const int32_t* cu_seqlens, int32_t chunk, float* final_state, const ssd_shape* shape,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+ssd_status ssd_state_passing(const int32_t* cu_seqlens, int32_t chunk, int32_t state_block, float* final_state,
+                             const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
   Prepared pp;
-  ssd_status st = prepare(kPassing, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, chunk, shape,
-                          workspace, workspace_bytes, &pp);
+  ssd_status st = prepare(kPassing, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, chunk, state_block,
+                          shape, workspace, workspace_bytes, &pp);
   if (st != SSD_OK) return st;
   return hip_status(ssd::launch_state_passing(pp.d, cu_seqlens, final_state, pp.ws, (hipStream_t)stream));
 }
 
 ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int32_t* cu_seqlens, int32_t chunk,
-                          void* Y, const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+                          int32_t state_block, void* Y, const ssd_shape* shape, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   Prepared pp;
-  ssd_status st = prepare(kScan, X, nullptr, B, C, Y, cu_seqlens, chunk, shape, workspace, workspace_bytes, &pp);
+  ssd_status st = prepare(kScan, X, nullptr, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
+                          workspace_bytes, &pp);
   if (st != SSD_OK) return st;
   return hip_status(ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, (hipStream_t)stream));
 }
 
-ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
-                   int32_t chunk, void* Y, float* final_state, const ssd_shape* shape, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
+                      int32_t chunk, int32_t state_block, void* Y, float* final_state, const ssd_shape* shape,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   Prepared pp;
-  ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, shape, workspace, workspace_bytes, &pp);
+  ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
+                          workspace_bytes, &pp);
   if (st != SSD_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = ssd::launch_chunk_cumsum(pp.d, log_a, cu_seqlens, pp.ws, s);
@@ -188,6 +234,13 @@ ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void*
   if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, final_state, pp.ws, s);
   if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s);
   return hip_status(e);
+}
+
+ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
+                   int32_t chunk, void* Y, float* final_state, const ssd_shape* shape, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return ssd_fwd_ex(X, log_a, B, C, cu_seqlens, chunk, 0, Y, final_state, shape, workspace, workspace_bytes,
+                    stream);
 }
 
 ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C, void* y,

@@ -1,8 +1,9 @@
 // ssd_chunk_scan.hip -- diagonal blocks and left factors of the chunked SSD
-// forward pass on gfx950.
+// forward pass on gfx950, with the state carried through each state block.
 //
-// For every chunk slot and head, with cs the log2-scaled cumulative decay:
-//   Y[i][p] = exp2(cs_i) sum_n C[i][n] start[p][n]                   (left factor)
+// For every chunk and head, with cs the log2-scaled cumulative decay and h the
+// state entering the chunk:
+//   Y[i][p] = exp2(cs_i) sum_n C[i][n] h[p][n]                        (left factor)
 //           + sum_{j <= i} exp2(cs_i - cs_j) (sum_n C[i][n] B[j][n]) X[j][p]
 //                                                                   (diagonal block)
 // ("Transformers are SSMs" paper card, Method 5 / paper section 6, "Diagonal
@@ -10,201 +11,423 @@
 // "decay_from_start", "Y_carry"). The mask is applied before the exponential
 // (paper card Pitfalls: "Mask before exp"), so no positive exponent is formed.
 //
-// bf16 path, one workgroup (4 waves) per (slot, head):
+// bf16 path, one workgroup of 8 waves per (state block, head), one workgroup
+// per CU. The block's entering state comes from the state-passing stage;
+// inside the block the workgroup walks its chunks in order and advances the
+// state itself, h <- exp2(A_k) h + sum_j exp2(cs_last - cs_j) X[j] B[j]^T (the
+// centre-factor recurrence of paper section 6 with the right factor of each
+// chunk), keeping h in fp32 MFMA accumulators. With one chunk per block this
+// is exactly the pages' schedule.
+//  * Decay factorisation per 16-row query tile with m = cs at its first row:
+//    for keys j before the tile, exp2(cs_i - cs_j) = u_i v_j with
+//    u_i = exp2(cs_i - m) <= 1 and v_j = exp2(m - cs_j) <= 1 (cs never
+//    increases), so neither factor overflows whatever the decay. Y_i =
+//    u_i (sum_{j before the tile} (S o V)_ij X_j + exp2(m) (C h^T)_i) + the
+//    key block holding the diagonal, which uses the exact masked
+//    exp2(cs_i - cs_j) and is added after the accumulator is scaled by u_i.
+//    Most of the per-element work is one multiply by a tabulated v_j.
 //  * S^T = B C^T is computed tile by tile on 16x16x32 bf16 MFMA. Its
 //    accumulator layout (lane = query row i, registers = 4 key rows j) is, after
-//    masking and decay, directly the A operand of the next MFMA Y += (L o S) X,
-//    so S never goes through LDS. L o S is carried as a bf16 hi/lo pair (two
-//    MFMAs on the same X fragment): one bf16 rounding of L o S alone would
-//    double the output error of the pass.
-//  * The carry C start^T goes into the same accumulator first and is scaled by
-//    exp2(cs_i) per row; only the lower triangle of S is formed.
-//  * B (token-major) and the start state are staged in LDS as they are; X is
-//    staged transposed. C fragments are read straight from global memory.
-//  * Query-row tiles are dealt to waves in a zig-zag so that the triangular work
-//    is balanced.
+//    masking and the v_j factor, directly the A operand of the next MFMA, so S
+//    never goes through LDS. S o V is carried as a bf16 hi/lo pair (two MFMAs
+//    on the same X fragment): one bf16 rounding alone would double the output
+//    error of the pass.
+//  * X, the decay-weighted X for the state update and B are staged token-major
+//    in LDS through registers (the next chunk's rows and C fragments in flight
+//    while the current chunk is computed); operands that contract over tokens
+//    use the gfx950 LDS transpose read. The state goes to LDS transposed, and
+//    output tiles leave through a small per-wave LDS transpose as 16-byte
+//    stores.
+//  * Query tiles are dealt so that each SIMD's pair of waves gets one short
+//    and one long row of the triangle; the state update is spread over all
+//    waves. Two barriers per chunk.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_stage.h"
 
 namespace ssd {
 
-size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q) {
-  return (size_t)Q * (N + 8) * 2 + (size_t)P * (Q + 8) * 2 + (size_t)P * (N + 8) * 2 + (size_t)Q * 4;
-}
+namespace {
+
+constexpr int kScanWaves = 8;
+constexpr int kScanThreads = kScanWaves * 64;
+constexpr int kYPitch = 20;      // per-wave output staging tile [32][kYPitch]
 
 template <int P, int N>
-__global__ __launch_bounds__(256) void chunk_scan_bf16_kernel(const uint16_t* __restrict__ X,
-                                                              const uint16_t* __restrict__ B,
-                                                              const uint16_t* __restrict__ C,
-                                                              const int4* __restrict__ table,
-                                                              const float* __restrict__ cs,
-                                                              const uint16_t* __restrict__ start,
-                                                              uint16_t* __restrict__ Y, int H, int G,
-                                                              int Q) {
+struct ScanCfg {
+  static constexpr int BP = lds_pitch(N);   // B rows
+  static constexpr int XP = lds_pitch(P);   // X rows, weighted X rows
+  static constexpr int HP = lds_pitch(P);   // transposed state rows [N][HP] (rows stored at perm32(n))
+  static constexpr int TP = P / 16, TN = N / 16, NB = N / 32;
+  static constexpr int WN = TN < 4 ? TN : 4;
+  static constexpr int WP = (kScanWaves / WN) < TP ? (kScanWaves / WN) : TP;
+  static constexpr int TPW = TP / WP, TNW = TN / WN;
+  static constexpr int CBN = N / 8, CBP = P / 8;
+  static constexpr int RB = (kPassRows * CBN + kScanThreads - 1) / kScanThreads;
+  static constexpr int RX = (kPassRows * CBP + kScanThreads - 1) / kScanThreads;
+};
+
+// Query tile of wave w in round k: SIMD s = w % 4 pairs tile s with tile 7 - s.
+__device__ __forceinline__ int scan_tile(int k, int w) { return 8 * k + (w < 4 ? w : 11 - w); }
+
+}  // namespace
+
+// Chunks of up to 128 tokens keep a separate decay-weighted copy of X; longer
+// chunks weight X in place after the outputs are done (two more barriers).
+static bool scan_in_place(int P, int N, int Q) { return Q > 128 || N > 128 || P > 64; }
+
+// The v_j table ([Q/16][Q] fp32) is kept for chunks of up to 128 tokens;
+// longer chunks compute v_j where it is used.
+size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q) {
+  const size_t nIt = Q / 16;
+  const size_t xcopies = scan_in_place(P, N, Q) ? 1 : 2;
+  const size_t el = (size_t)Q * lds_pitch(N) + xcopies * (size_t)Q * lds_pitch(P) + (size_t)N * lds_pitch(P) +
+                    (size_t)kScanWaves * 32 * kYPitch;
+  return el * 2 + ((Q > 128 ? 0 : nIt * Q) + 2 * Q + nIt) * 4 + 16 * 16;
+}
+
+// ITW: query tiles per wave (1 for chunks of up to 128 tokens, 2 for 256).
+template <int P, int N, int ITW>
+__global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
+    const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
+    const uint16_t* __restrict__ start, uint16_t* __restrict__ Y, int H, int G, int Q) {
+  using K = ScanCfg<P, N>;
   const long unit = blockIdx.x;
   const int h = (int)(unit % H);
-  const long slot = unit / H;
-  const SlotRec rec = load_slot(table, slot);
-  const int len = rec.len;
-  if (len <= 0) return;
+  const long m = unit / H;
+  const BlockRec blk = load_block(btable, m);
+  if (blk.nchunks <= 0) return;
   const int g = h / (H / G);
+  const int nIt = Q / 16;
 
-  constexpr int TP = P / 16;
-  constexpr int NB = N / 32;
-  constexpr int BP = N + 8;       // LDS pitch of B rows and start rows (elements)
-  const int XP = Q + 8;           // LDS pitch of X^T rows
-
+  // Weight X in place after the outputs when a second copy does not fit.
+  constexpr bool kInPlace = ITW > 1 || N > 128 || P > 64;
   extern __shared__ uint16_t lds[];
-  uint16_t* bs = lds;                       // [Q][BP]  B rows of the chunk
-  uint16_t* xt = bs + Q * BP;               // [P][XP]  X^T
-  uint16_t* st = xt + P * XP;               // [P][BP]  start state (bf16)
-  float* csl = reinterpret_cast<float*>(st + P * BP);  // [Q]
+  uint16_t* bs = lds;                                 // [Q][BP]  B rows
+  uint16_t* xs = bs + Q * K::BP;                      // [Q][XP]  X rows
+  uint16_t* xw = kInPlace ? xs : xs + Q * K::XP;      // [Q][XP]  X rows times exp2(cs_last - cs_j)
+  uint16_t* hsT = xw + Q * K::XP;                     // [N][HP]  state entering the chunk, transposed
+  uint16_t* ysw = hsT + N * K::HP;                    // [8][32][kYPitch] per-wave output staging
+  constexpr bool kVTable = ITW == 1;                  // tabulate v_j (chunks of up to 128 tokens)
+  int4* recs = reinterpret_cast<int4*>(ysw + kScanWaves * 32 * kYPitch);  // [16] chunk records of the block
+  float* Vt = reinterpret_cast<float*>(recs + 16);    // [nIt][Q] v_j per query tile
+  float* Ut = Vt + (kVTable ? nIt * Q : 0);           // [Q] u_i
+  float* Et = Ut + Q;                                 // [nIt] exp2(m) per query tile
+  float* csl = Et + nIt;                              // [Q] cumulative log2 decay
 
   const int tid = threadIdx.x;
-  const long tok0 = rec.tok0;
-  const float* csr = cs + (slot * H + h) * (long)Q;
-  for (int i = tid; i < Q; i += 256) csl[i] = csr[i];
-
-  // B rows (zero past the chunk's length)
-  {
-    constexpr int CB = N / 8;
-    const uint16_t* src = B + (tok0 * G + g) * N;
-    for (int idx = tid; idx < Q * CB; idx += 256) {
-      const int j = idx / CB, c = idx % CB;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (j < len) v = *reinterpret_cast<const u32x4*>(src + (long)j * G * N + c * 8);
-      *reinterpret_cast<u32x4*>(bs + j * BP + c * 8) = v;
-    }
-  }
-  // X^T via 8x8 register transposes (zero past the chunk's length)
-  {
-    constexpr int CB = P / 8;
-    const uint16_t* src = X + (tok0 * H + h) * P;
-    const long ld = (long)H * P;
-    const int nblk = (Q / 8) * CB;
-    for (int blk = tid; blk < nblk; blk += 256) {
-      const int cb = blk % CB, jb = blk / CB;
-      u32x4 in[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int j = jb * 8 + r;
-        in[r] = (j < len) ? *reinterpret_cast<const u32x4*>(src + (long)j * ld + cb * 8) : u32x4{0u, 0u, 0u, 0u};
-      }
-      u32x4 out[8];
-      transpose8x8_b16(in, out);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(xt + (cb * 8 + q) * XP + jb * 8) = out[q];
-    }
-  }
-  // start state [P][N]
-  {
-    constexpr int CB = N / 8;
-    const uint16_t* src = start + (slot * H + h) * (long)(P * N);
-    for (int idx = tid; idx < P * CB; idx += 256) {
-      const int p = idx / CB, c = idx % CB;
-      *reinterpret_cast<u32x4*>(st + p * BP + c * 8) = *reinterpret_cast<const u32x4*>(src + p * N + c * 8);
-    }
-  }
-  __syncthreads();
-
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int nIt = Q / 16;
-  const int rounds = (nIt + 3) / 4;
-  for (int rr = 0; rr < rounds; ++rr) {
-    const int it = (rr & 1) ? (4 * rr + 3 - wave) : (4 * rr + wave);
-    if (it >= nIt || it * 16 >= len) continue;
+  const long ldb = (long)G * N, ldx = (long)H * P;
+  uint16_t* ys = ysw + wave * 32 * kYPitch;
 
-    const int irow = it * 16 + l16;  // this lane's query row (A rows of C, S^T columns)
-    u32x4 cf[NB];
-    {
-      const uint16_t* crow = C + ((tok0 + irow) * G + g) * N + 8 * g4;
+  // Per-thread constant offsets (bytes) of its staged pieces within a chunk.
+  uint32_t boff[K::RB], xoff[K::RX];
+  int brow[K::RB], xrow[K::RX];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        cf[nb] = (irow < len) ? *reinterpret_cast<const u32x4*>(crow + nb * 32) : u32x4{0u, 0u, 0u, 0u};
+  for (int u = 0; u < K::RB; ++u) {
+    const int idx = tid + kScanThreads * u;
+    brow[u] = idx / K::CBN;
+    boff[u] = (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2);
+  }
+#pragma unroll
+  for (int u = 0; u < K::RX; ++u) {
+    const int idx = tid + kScanThreads * u;
+    xrow[u] = idx / K::CBP;
+    xoff[u] = (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2);
+  }
+
+  // State tiles of this wave and the state entering the block.
+  const int wn = wave % K::WN, wp = wave / K::WN;
+  const bool sact = wp < K::WP;
+  const int p0t = wp * K::TPW, n0t = wn * K::TNW;
+  f32x4 hacc[K::TPW][K::TNW];
+  {
+    const uint16_t* st0 = start + (m * H + h) * (long)(P * N);
+#pragma unroll
+    for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+      for (int b = 0; b < K::TNW; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hacc[a][b][r] = sact ? bf16_to_f32(st0[((p0t + a) * 16 + 4 * g4 + r) * N + (n0t + b) * 16 + l16]) : 0.f;
+  }
+
+  // Registers holding the next chunk.
+  u32x4 pb[K::RB], px[K::RX];
+  u32x4 pcf[ITW][K::NB];    // C fragments of this wave's query tiles
+  float pcs_t = 0.f, pcs_tm = 0.f, pcs_last = 0.f, pcs_e = 0.f;
+  constexpr int VE = kVTable ? 2 : 1;    // v-table entries per thread: nIt*Q <= VE*512
+  float pcs_v[VE], pcs_vm[VE];
+  float pcs_x[K::RX];
+
+  auto prefetch = [&](const SlotRec& r, long slot) {
+    const char* Bc = reinterpret_cast<const char*>(B + ((long)r.tok0 * G + g) * N);
+    const char* Xc = reinterpret_cast<const char*>(X + ((long)r.tok0 * H + h) * P);
+    const float* csr = cs + (slot * H + h) * (long)Q;
+    const int len = r.len;
+    const bool full = len >= kPassRows || len == Q;
+#pragma unroll
+    for (int u = 0; u < K::RB; ++u) {
+      const bool in = (tid + kScanThreads * u) < kPassRows * K::CBN;
+      pb[u] = (in && (full ? brow[u] < Q : brow[u] < len)) ? *reinterpret_cast<const u32x4*>(Bc + boff[u])
+                                                            : u32x4{0u, 0u, 0u, 0u};
     }
-
-    // Left factor: acc[i][p] = sum_n C[i][n] start[p][n], then scaled by exp2(cs_i).
-    f32x4 acc[TP];
 #pragma unroll
-    for (int pt = 0; pt < TP; ++pt) {
-      acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < K::RX; ++u) {
+      const bool in = (tid + kScanThreads * u) < kPassRows * K::CBP;
+      px[u] = (in && (full ? xrow[u] < Q : xrow[u] < len)) ? *reinterpret_cast<const u32x4*>(Xc + xoff[u])
+                                                            : u32x4{0u, 0u, 0u, 0u};
+      pcs_x[u] = csr[min(xrow[u], Q - 1)];
+    }
+    const uint16_t* Cc = C + ((long)r.tok0 * G + g) * N + 8 * g4;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const u32x4 sf = *reinterpret_cast<const u32x4*>(st + (pt * 16 + l16) * BP + nb * 32 + 8 * g4);
-        acc[pt] = mfma16x16x32(cf[nb], sf, acc[pt]);
+    for (int k = 0; k < ITW; ++k) {
+      const int it = scan_tile(k, wave);
+      const int irow = it * 16 + l16;
+#pragma unroll
+      for (int nb = 0; nb < K::NB; ++nb)
+        pcf[k][nb] = (it < nIt && irow < len) ? *reinterpret_cast<const u32x4*>(Cc + irow * ldb + nb * 32)
+                                              : u32x4{0u, 0u, 0u, 0u};
+    }
+    pcs_last = csr[Q - 1];
+    if (tid < Q) {
+      pcs_t = csr[tid];
+      pcs_tm = csr[tid & ~15];
+    }
+    if (tid < nIt) pcs_e = csr[16 * tid];
+#pragma unroll
+    for (int u = 0; u < VE; ++u) {
+      const int e = tid + kScanThreads * u;
+      if (kVTable && e < nIt * Q) {
+        pcs_v[u] = csr[e % Q];
+        pcs_vm[u] = csr[16 * (e / Q)];
       }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float e = fast_exp2(csl[it * 16 + 4 * g4 + r]);
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) acc[pt][r] *= e;
-    }
+  };
 
-    // Diagonal block over key blocks of 32 tokens j <= i. The masked, decayed
-    // block M = L o S is split into bf16 high and low parts (M = hi + lo to
-    // about 16 significant bits) and both are multiplied into X, so that M is
-    // not limited to bf16 precision.
-    const float cs_i = csl[irow];
-    for (int kb = 0; kb <= (it >> 1); ++kb) {
-      uint32_t mw[4], ml[4];
+  if (tid < blk.nchunks) recs[tid] = ctable[blk.slot0 + tid];
+  __syncthreads();
+  auto rec_of = [&](int c) {
+    const int4 v = recs[c];
+    return SlotRec{v.x, v.y, v.z, v.w};
+  };
+  SlotRec rec = rec_of(0);
+  prefetch(rec, blk.slot0);
+
+  for (int c = 0; c < blk.nchunks; ++c) {
+    const long slot = blk.slot0 + c;
+    const int len = rec.len;
+    const long tok0 = rec.tok0;
+    const float cs_last = pcs_last;
+
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+    // B, X and decay-weighted X rows of the first pass.
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int jt = 2 * kb + half;
-        if (jt > it) {
-          mw[2 * half] = 0u;
-          mw[2 * half + 1] = 0u;
-          ml[2 * half] = 0u;
-          ml[2 * half + 1] = 0u;
-          continue;
+    for (int u = 0; u < K::RB; ++u)
+      if ((tid + kScanThreads * u) < kPassRows * K::CBN && brow[u] < Q)
+        *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + kScanThreads * u) % K::CBN) * 8) = pb[u];
+#pragma unroll
+    for (int u = 0; u < K::RX; ++u) {
+      if ((tid + kScanThreads * u) < kPassRows * K::CBP && xrow[u] < Q) {
+        const int o = xrow[u] * K::XP + ((tid + kScanThreads * u) % K::CBP) * 8;
+        *reinterpret_cast<u32x4*>(xs + o) = px[u];
+        if (!kInPlace) {
+          const float w = fast_exp2(cs_last - pcs_x[u]);
+          u32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(px[u][q]) * w, bf16_hi(px[u][q]) * w);
+          *reinterpret_cast<u32x4*>(xw + o) = v;
         }
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const u32x4 bf = *reinterpret_cast<const u32x4*>(bs + (jt * 16 + l16) * BP + nb * 32 + 8 * g4);
-          s = mfma16x16x32(bf, cf[nb], s);
-        }
-        // s[r] = S[i = irow][j = jt*16 + 4*g4 + r]; mask first, then exp.
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = jt * 16 + 4 * g4 + r;
-          v[r] = (j <= irow) ? s[r] * fast_exp2(cs_i - csl[j]) : 0.f;
-        }
-        mw[2 * half] = pack_bf16x2(v[0], v[1]);
-        mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
-        ml[2 * half] = pack_bf16x2(v[0] - bf16_lo(mw[2 * half]), v[1] - bf16_hi(mw[2 * half]));
-        ml[2 * half + 1] = pack_bf16x2(v[2] - bf16_lo(mw[2 * half + 1]), v[3] - bf16_hi(mw[2 * half + 1]));
-      }
-      const u32x4 af = u32x4{mw[0], mw[1], mw[2], mw[3]};
-      const u32x4 al = u32x4{ml[0], ml[1], ml[2], ml[3]};
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        const uint16_t* xr = xt + (pt * 16 + l16) * XP + 32 * kb + 4 * g4;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(xr);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(xr + 16);
-        const u32x4 xf = u32x4{lo.x, lo.y, hi.x, hi.y};
-        acc[pt] = mfma16x16x32(af, xf, acc[pt]);
-        acc[pt] = mfma16x16x32(al, xf, acc[pt]);
       }
     }
+    // Decay tables: u_i, exp2(m) per query tile, v_j per (query tile, key).
+    if (tid < Q) {
+      Ut[tid] = fast_exp2(pcs_t - pcs_tm);
+      csl[tid] = pcs_t;
+    }
+    if (tid < nIt) Et[tid] = fast_exp2(pcs_e);
+#pragma unroll
+    for (int u = 0; u < VE; ++u) {
+      const int e = tid + kScanThreads * u;
+      if (kVTable && e < nIt * Q) Vt[e] = (e % Q) < 16 * (e / Q) ? fast_exp2(pcs_vm[u] - pcs_v[u]) : 0.f;
+    }
+    // Chunks longer than one pass: the remaining rows, synchronously.
+    for (int r0 = kPassRows; r0 < Q; r0 += kPassRows) {
+      const float* csr = cs + (slot * H + h) * (long)Q;
+      for (int idx = tid; idx < kPassRows * K::CBN; idx += kScanThreads) {
+        const int j = r0 + idx / K::CBN, cc = idx % K::CBN;
+        *reinterpret_cast<u32x4*>(bs + j * K::BP + cc * 8) =
+            j < len ? *reinterpret_cast<const u32x4*>(B + (tok0 * G + g) * N + j * ldb + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+      for (int idx = tid; idx < kPassRows * K::CBP; idx += kScanThreads) {
+        const int j = r0 + idx / K::CBP, cc = idx % K::CBP;
+        const u32x4 v0 = j < len ? *reinterpret_cast<const u32x4*>(X + (tok0 * H + h) * P + j * ldx + cc * 8)
+                                 : u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(xs + j * K::XP + cc * 8) = v0;
+        if (!kInPlace) {
+          const float w = fast_exp2(cs_last - csr[j]);
+          u32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(v0[q]) * w, bf16_hi(v0[q]) * w);
+          *reinterpret_cast<u32x4*>(xw + j * K::XP + cc * 8) = v;
+        }
+      }
+    }
+    // State entering the chunk, transposed to [n][p] in bf16.
+    if (sact) {
+#pragma unroll
+      for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+        for (int b = 0; b < K::TNW; ++b) {
+          const u32x2 v = {pack_bf16x2(hacc[a][b][0], hacc[a][b][1]), pack_bf16x2(hacc[a][b][2], hacc[a][b][3])};
+          *reinterpret_cast<u32x2*>(hsT + perm32((n0t + b) * 16 + l16) * K::HP + (p0t + a) * 16 + 4 * g4) = v;
+        }
+    }
+    u32x4 cf[ITW][K::NB];
+#pragma unroll
+    for (int k = 0; k < ITW; ++k)
+#pragma unroll
+      for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = pcf[k][nb];
+    if (c + 1 < blk.nchunks) {
+      rec = rec_of(c + 1);
+      prefetch(rec, slot + 1);
+    }
+    __syncthreads();
 
-    // Store rows i = it*16 + 4*g4 + r.
+    // ---------------- outputs of this chunk: Y_i = u_i (sum_j (S o V)_ij X_j + exp2(m) (C h^T)_i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = it * 16 + 4 * g4 + r;
-      if (i < len) {
-        uint16_t* yr = Y + ((tok0 + i) * H + h) * P + l16;
+    for (int k = 0; k < ITW; ++k) {
+      const int it = scan_tile(k, wave);
+      if (it >= nIt || it * 16 >= len) continue;
+      const int irow = it * 16 + l16;
+      f32x4 acc[K::TP];
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) yr[pt * 16] = f32_to_bf16(acc[pt][r]);
+      for (int pt = 0; pt < K::TP; ++pt) {
+        acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < K::NB; ++nb)
+          acc[pt] = mfma16x16x32(cf[k][nb], frag_k_rows_accpair(hsT, K::HP, nb * 32, pt * 16, lane), acc[pt]);
+      }
+      const float em = Et[it];
+#pragma unroll
+      for (int pt = 0; pt < K::TP; ++pt) acc[pt] *= em;
+      const float* vrow = Vt + it * Q + 4 * g4;
+      const f32x4 uu = *reinterpret_cast<const f32x4*>(Ut + it * 16 + 4 * g4);
+      const int kbd = it >> 1;  // key block holding the diagonal tile
+      for (int kb = 0; kb <= kbd; ++kb) {
+        if (kb == kbd) {
+          // Apply u_i now: the diagonal key block uses the exact masked decay.
+#pragma unroll
+          for (int pt = 0; pt < K::TP; ++pt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[pt][r] *= uu[r];
+        }
+        const float cs_i = csl[irow];
+        uint32_t mw[4], ml[4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int jt = 2 * kb + half;
+          if (jt > it) {
+            mw[2 * half] = mw[2 * half + 1] = 0u;
+            ml[2 * half] = ml[2 * half + 1] = 0u;
+            continue;
+          }
+          f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int nb = 0; nb < K::NB; ++nb)
+            sv = mfma16x16x32(frag_k_cols(bs, K::BP, jt * 16, nb * 32, lane), cf[k][nb], sv);
+          // sv[r] = S[i = irow][j = jt*16 + 4*g4 + r]
+          float v[4];
+          if (kb == kbd) {  // exact decay, mask first
+            const f32x4 cj = *reinterpret_cast<const f32x4*>(csl + jt * 16 + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              v[r] = (jt * 16 + 4 * g4 + r <= irow) ? sv[r] * fast_exp2(cs_i - cj[r]) : 0.f;
+          } else {          // v_j (table or computed); u_i applied to the accumulator
+            f32x4 vv;
+            if (kVTable) {
+              vv = *reinterpret_cast<const f32x4*>(vrow + jt * 16);
+            } else {
+              const f32x4 cj = *reinterpret_cast<const f32x4*>(csl + jt * 16 + 4 * g4);
+              const float mt = csl[16 * it];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) vv[r] = fast_exp2(mt - cj[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = sv[r] * vv[r];
+          }
+          mw[2 * half] = pack_bf16x2(v[0], v[1]);
+          mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
+          ml[2 * half] = pack_bf16x2(v[0] - bf16_lo(mw[2 * half]), v[1] - bf16_hi(mw[2 * half]));
+          ml[2 * half + 1] = pack_bf16x2(v[2] - bf16_lo(mw[2 * half + 1]), v[3] - bf16_hi(mw[2 * half + 1]));
+        }
+        const u32x4 ah = u32x4{mw[0], mw[1], mw[2], mw[3]};
+        const u32x4 al = u32x4{ml[0], ml[1], ml[2], ml[3]};
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) {
+          const u32x4 xf = frag_k_rows_accpair(xs, K::XP, 32 * kb, pt * 16, lane);
+          acc[pt] = mfma16x16x32(ah, xf, acc[pt]);
+          acc[pt] = mfma16x16x32(al, xf, acc[pt]);
+        }
+      }
+      // Out through the wave's staging tile as 16-byte rows.
+      const bool row_ok = it * 16 + l16 < len;
+      uint16_t* yrow = Y + ((tok0 + it * 16 + l16) * H + h) * P;
+#pragma unroll
+      for (int pp = 0; pp < (K::TP + 1) / 2; ++pp) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int pt = 2 * pp + q;
+          if (pt < K::TP) {
+            const u32x2 v = {pack_bf16x2(acc[pt][0], acc[pt][1]), pack_bf16x2(acc[pt][2], acc[pt][3])};
+            *reinterpret_cast<u32x2*>(ys + perm32(q * 16 + l16) * kYPitch + 4 * g4) = v;
+          }
+        }
+        const u32x4 out = frag_k_rows_accpair(ys, kYPitch, 0, 0, lane);  // token l16, p = 32pp + 8g4 ..
+        if (row_ok && pp * 32 + 8 * g4 < P) *reinterpret_cast<u32x4*>(yrow + pp * 32 + 8 * g4) = out;
+      }
+    }
+
+    // ---------------- state entering the next chunk of the block
+    if (kInPlace && c + 1 < blk.nchunks) {  // weight X in place once every wave is done with it
+      __syncthreads();
+      for (int idx = tid; idx < Q * K::CBP; idx += kScanThreads) {
+        const int j = idx / K::CBP, cc = idx % K::CBP;
+        const float w = fast_exp2(cs_last - csl[j]);
+        u32x4 v = *reinterpret_cast<const u32x4*>(xs + j * K::XP + cc * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(v[q]) * w, bf16_hi(v[q]) * w);
+        *reinterpret_cast<u32x4*>(xs + j * K::XP + cc * 8) = v;
+      }
+      __syncthreads();
+    }
+    if (c + 1 < blk.nchunks && sact) {
+      const float decay = fast_exp2(cs_last);
+#pragma unroll
+      for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+        for (int b = 0; b < K::TNW; ++b) hacc[a][b] *= decay;
+      const int nkb = (len + 31) / 32;
+      for (int kb = 0; kb < nkb; ++kb) {
+        u32x4 xa[K::TPW], bb[K::TNW];
+#pragma unroll
+        for (int a = 0; a < K::TPW; ++a) xa[a] = frag_k_rows_accpair(xw, K::XP, 32 * kb, (p0t + a) * 16, lane);
+#pragma unroll
+        for (int b = 0; b < K::TNW; ++b) bb[b] = frag_k_rows_accpair(bs, K::BP, 32 * kb, (n0t + b) * 16, lane);
+#pragma unroll
+        for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+          for (int b = 0; b < K::TNW; ++b) hacc[a][b] = mfma16x16x32(xa[a], bb[b], hacc[a][b]);
       }
     }
   }
 }
 
 // ----------------------------------------------------------------------------
-// fp32 path (plain FMA, fp32 accumulation). Query rows in blocks of 32; for
+// fp32 path (plain FMA, fp32 accumulation; one chunk per state block). Query
+// rows in blocks of 32; for
 // each key block j0 <= i0 the masked, decayed block of C B^T is formed in LDS
 // and multiplied into X.
 // ----------------------------------------------------------------------------
@@ -308,15 +531,15 @@ template <int P, int N>
 static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                                    const Workspace& ws, hipStream_t stream) {
   const size_t lds = chunk_scan_bf16_lds_bytes(P, N, d.Q);
-  auto kern = chunk_scan_bf16_kernel<P, N>;
+  auto kern = d.Q > 128 ? chunk_scan_bf16_kernel<P, N, 2> : chunk_scan_bf16_kernel<P, N, 1>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(d.nslots * d.H)), dim3(256), lds, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * d.H)), dim3(kScanThreads), lds, stream,
                      reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
-                     reinterpret_cast<const uint16_t*>(C), ws.table, ws.cs,
+                     reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs,
                      reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y), d.H,
                      d.G, d.Q);
   return hipGetLastError();

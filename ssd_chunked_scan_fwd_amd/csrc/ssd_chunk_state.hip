@@ -1,155 +1,207 @@
 // ssd_chunk_state.hip -- right factors of the chunked SSD forward pass on gfx950.
 //
-// For every chunk slot k and head h:
-//     s_k[p][n] = sum_j exp2(cs_last - cs_j) X[j][p] B[j][n]
-// the state at the chunk end from a zero start ("Transformers are SSMs" paper
-// card, Method 5 / paper section 6, "Right Factors": one batched matrix
-// product per chunk; pseudocode lines "decay_to_end" and "chunk_states").
+// For every state block m (Gs consecutive chunks of one sequence) and head h:
+//     s_m[p][n] = sum_j exp2(tail_j) X[j][p] B[j][n],
+// tail_j = log2-scaled total decay from token j to the end of the block. With
+// Gs = 1 this is exactly the chunk state of the pages' algorithm: the state at
+// the chunk end from a zero start ("Transformers are SSMs" paper card, Method 5
+// / paper section 6, "Right Factors": one batched matrix product per chunk;
+// pseudocode lines "decay_to_end" and "chunk_states"). With Gs > 1 it is the
+// same right factor for a longer block, which the chunk-scan stage refines
+// chunk by chunk.
 //
-// bf16 path: the contraction runs over tokens j, which are the slow dimension
-// of X [T][H][P] and B [T][G][N]. Both operands are staged into LDS
-// transposed (p-major and n-major) with an in-register 8x8 transpose, so that
-// every MFMA operand is one 16-byte LDS read. The decay is folded into X
-// before it is rounded to bf16. Products run on 16x16x32 bf16 MFMA with fp32
-// accumulation; the state is written in fp32.
+// bf16 path: one workgroup of 8 waves per (block, head). Token rows of X and B
+// are staged into LDS as they lie in HBM (token-major) through registers,
+// prefetching the next 128 rows while the current ones are multiplied; the
+// decay weight is applied to X in registers before it is rounded to bf16 and
+// stored. The contraction over tokens takes both MFMA operands with the gfx950
+// LDS transpose read.
+// Products run on 16x16x32 bf16 MFMA with fp32 accumulation; the block state
+// is written in fp32 together with the block's total log2 decay.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_stage.h"
 
 namespace ssd {
 
 namespace {
 
-constexpr int kSubTokens = 128;  // tokens staged per pass
+constexpr int kStateThreads = 512;  // 8 waves
 
-// Stage rows [j0, j0 + nb) of a token-major bf16 matrix (row stride `ld`
-// elements, `cols` columns starting at `src`) into dst[col][j] (pitch `pitch`),
-// zero-filling tokens nb .. qb-1. When `scale` is not null, row j is
-// multiplied by scale[j] before rounding back to bf16.
-template <int COLS>
-__device__ __forceinline__ void stage_transposed(uint16_t* __restrict__ dst, int pitch,
-                                                 const uint16_t* __restrict__ src, long ld, int nb,
-                                                 int qb, const float* scale) {
-  constexpr int CB = COLS / 8;
-  const int nblk = (qb / 8) * CB;
-  for (int blk = threadIdx.x; blk < nblk; blk += 256) {
-    const int cb = blk % CB;
-    const int jb = blk / CB;
-    u32x4 in[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int j = jb * 8 + r;
-      if (j < nb) {
-        u32x4 v = *reinterpret_cast<const u32x4*>(src + (long)j * ld + cb * 8);
-        if (scale) {
-          const float w = scale[j];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = pack_bf16x2(bf16_lo(v[c]) * w, bf16_hi(v[c]) * w);
-        }
-        in[r] = v;
-      } else {
-        in[r] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    u32x4 out[8];
-    transpose8x8_b16(in, out);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      *reinterpret_cast<u32x4*>(dst + (cb * 8 + q) * pitch + jb * 8) = out[q];
-  }
-}
+template <int P, int N>
+struct StateCfg {
+  static constexpr int BP = lds_pitch(N), XP = lds_pitch(P);
+  static constexpr int TP = P / 16, TN = N / 16;
+  static constexpr int WN = TN < 4 ? TN : 4;
+  static constexpr int WP = (8 / WN) < TP ? (8 / WN) : TP;
+  static constexpr int TPW = TP / WP, TNW = TN / WN;
+  static constexpr int CBN = N / 8, CBP = P / 8;
+  static constexpr int RB = (kPassRows * CBN + kStateThreads - 1) / kStateThreads;
+  static constexpr int RX = (kPassRows * CBP + kStateThreads - 1) / kStateThreads;
+};
 
 }  // namespace
 
+size_t chunk_state_bf16_lds_bytes(int P, int N) {
+  return ((size_t)kPassRows * lds_pitch(N) + (size_t)kPassRows * lds_pitch(P)) * 2 + 16 * 16 + 16 * 4;
+}
+
 template <int P, int N>
-__global__ __launch_bounds__(256) void chunk_state_bf16_kernel(const uint16_t* __restrict__ X,
-                                                               const uint16_t* __restrict__ B,
-                                                               const int4* __restrict__ table,
-                                                               const float* __restrict__ cs,
-                                                               float* __restrict__ states, int H,
-                                                               int G, int Q) {
+__global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk_state_bf16_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const int4* __restrict__ ctable,
+    const int4* __restrict__ btable, const float* __restrict__ cs, float* __restrict__ bstates,
+    float* __restrict__ bdecay, int H, int G, int Q) {
+  using K = StateCfg<P, N>;
   const long unit = blockIdx.x;
   const int h = (int)(unit % H);
-  const long slot = unit / H;
-  const SlotRec rec = load_slot(table, slot);
-  if (rec.len <= 0) return;
+  const long m = unit / H;
+  const BlockRec blk = load_block(btable, m);
+  if (blk.nchunks <= 0) return;
   const int g = h / (H / G);
 
-  constexpr int TP = P / 16, TN = N / 16;
-  constexpr int WN = TN < 4 ? TN : 4;
-  constexpr int WP = (4 / WN) < TP ? (4 / WN) : TP;
-  constexpr int TPW = TP / WP, TNW = TN / WN;
-
-  const int qb = Q < kSubTokens ? Q : kSubTokens;
-  const int pitch = qb + 8;
   extern __shared__ uint16_t lds[];
-  uint16_t* xt = lds;                  // [P][pitch]: X^T scaled by the decay to the chunk end
-  uint16_t* bt = lds + P * pitch;      // [N][pitch]: B^T
-  float* wsc = reinterpret_cast<float*>(bt + N * pitch);  // [qb] decay weights
+  uint16_t* bs = lds;                          // [128][BP] B rows of the pass
+  uint16_t* xw = bs + kPassRows * K::BP;       // [128][XP] X rows times their decay to the block end
+  int4* recs = reinterpret_cast<int4*>(xw + kPassRows * K::XP);   // [16] chunk records of the block
+  float* lastcs = reinterpret_cast<float*>(recs + 16);             // [16] chunk totals (log2)
 
-  const float* csr = cs + (slot * H + h) * (long)Q;
-  const float cs_last = csr[Q - 1];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int wn = wave % WN, wp = wave / WN;
-  const bool active = wp < WP;
+  const int wn = wave % K::WN, wp = wave / K::WN;
+  const bool active = wp < K::WP;
+  const int p0t = wp * K::TPW, n0t = wn * K::TNW;
+  const long ldb = (long)G * N, ldx = (long)H * P;
 
-  f32x4 acc[TPW][TNW];
+  uint32_t boff[K::RB], xoff[K::RX];
+  int brow[K::RB], xrow[K::RX];
 #pragma unroll
-  for (int a = 0; a < TPW; ++a)
+  for (int u = 0; u < K::RB; ++u) {
+    const int idx = tid + kStateThreads * u;
+    brow[u] = idx < kPassRows * K::CBN ? idx / K::CBN : kPassRows;
+    boff[u] = (uint32_t)(((brow[u] % kPassRows) * ldb + (idx % K::CBN) * 8) * 2);
+  }
 #pragma unroll
-    for (int b = 0; b < TNW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int j0 = 0; j0 < rec.len; j0 += qb) {
-    const int nb = min(qb, rec.len - j0);
-    for (int j = tid; j < nb; j += 256) wsc[j] = fast_exp2(cs_last - csr[j0 + j]);
-    __syncthreads();
-    const long tok = (long)rec.tok0 + j0;
-    stage_transposed<P>(xt, pitch, X + (tok * H + h) * P, (long)H * P, nb, qb, wsc);
-    stage_transposed<N>(bt, pitch, B + (tok * G + g) * N, (long)G * N, nb, qb, nullptr);
-    __syncthreads();
-    if (active) {
-      const int nkb = (nb + 31) / 32;
-      for (int kb = 0; kb < nkb; ++kb) {
-        u32x4 af[TPW], bfr[TNW];
-#pragma unroll
-        for (int a = 0; a < TPW; ++a)
-          af[a] = *reinterpret_cast<const u32x4*>(xt + ((wp * TPW + a) * 16 + l16) * pitch + kb * 32 + 8 * g4);
-#pragma unroll
-        for (int b = 0; b < TNW; ++b)
-          bfr[b] = *reinterpret_cast<const u32x4*>(bt + ((wn * TNW + b) * 16 + l16) * pitch + kb * 32 + 8 * g4);
-#pragma unroll
-        for (int a = 0; a < TPW; ++a)
-#pragma unroll
-          for (int b = 0; b < TNW; ++b) acc[a][b] = mfma16x16x32(af[a], bfr[b], acc[a][b]);
-      }
-    }
-    __syncthreads();
+  for (int u = 0; u < K::RX; ++u) {
+    const int idx = tid + kStateThreads * u;
+    xrow[u] = idx < kPassRows * K::CBP ? idx / K::CBP : kPassRows;
+    xoff[u] = (uint32_t)(((xrow[u] % kPassRows) * ldx + (idx % K::CBP) * 8) * 2);
   }
 
+  // The block's chunk records and totals, read once.
+  if (tid < blk.nchunks) {
+    recs[tid] = ctable[blk.slot0 + tid];
+    lastcs[tid] = cs[((blk.slot0 + tid) * H + h) * (long)Q + Q - 1];
+  }
+  __syncthreads();
+  // Total log2 decay of the block; the tail of chunk c is total - (A_0 + .. + A_c).
+  float total = 0.f;
+  for (int c = 0; c < blk.nchunks; ++c) total += lastcs[c];
+
+  f32x4 acc[K::TPW][K::TNW];
+#pragma unroll
+  for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+    for (int b = 0; b < K::TNW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One pass = rows r0 .. r0+127 of chunk c; the next pass is loaded while the
+  // current one is multiplied.
+  u32x4 pb[K::RB], px[K::RX];
+  float pcs[K::RX];
+  auto load_pass = [&](const SlotRec& r, long slot, int r0) {
+    const char* Bc = reinterpret_cast<const char*>(B + (((long)r.tok0 + r0) * G + g) * N);
+    const char* Xc = reinterpret_cast<const char*>(X + (((long)r.tok0 + r0) * H + h) * P);
+    const float* csr = cs + (slot * H + h) * (long)Q + r0;
+    const int rows = r.len - r0;
+#pragma unroll
+    for (int u = 0; u < K::RB; ++u)
+      pb[u] = brow[u] < rows ? *reinterpret_cast<const u32x4*>(Bc + boff[u]) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < K::RX; ++u) {
+      px[u] = xrow[u] < rows ? *reinterpret_cast<const u32x4*>(Xc + xoff[u]) : u32x4{0u, 0u, 0u, 0u};
+      pcs[u] = xrow[u] < rows ? csr[xrow[u]] : 0.f;
+    }
+  };
+
+  auto rec_of = [&](int c) {
+    const int4 v = recs[c];
+    return SlotRec{v.x, v.y, v.z, v.w};
+  };
+  SlotRec rec = rec_of(0);
+  load_pass(rec, blk.slot0, 0);
+  float prefix = 0.f;
+  for (int c = 0; c < blk.nchunks; ++c) {
+    const long slot = blk.slot0 + c;
+    const float a_last = lastcs[c];
+    prefix += a_last;
+    const float shift = (total - prefix) + a_last;  // weight of row j: exp2(shift - cs_j)
+    const SlotRec cur = rec;
+    for (int r0 = 0; r0 < cur.len; r0 += kPassRows) {
+      const int rows = min(kPassRows, cur.len - r0);
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < K::RB; ++u)
+        if (brow[u] < kPassRows)
+          *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + kStateThreads * u) % K::CBN) * 8) = pb[u];
+#pragma unroll
+      for (int u = 0; u < K::RX; ++u) {
+        if (xrow[u] < kPassRows) {
+          const float w = xrow[u] < rows ? fast_exp2(shift - pcs[u]) : 0.f;
+          u32x4 v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(px[u][q]) * w, bf16_hi(px[u][q]) * w);
+          *reinterpret_cast<u32x4*>(xw + xrow[u] * K::XP + ((tid + kStateThreads * u) % K::CBP) * 8) = v;
+        }
+      }
+      // prefetch the next pass: next rows of this chunk, else the next chunk
+      if (r0 + kPassRows < cur.len) {
+        load_pass(cur, slot, r0 + kPassRows);
+      } else if (c + 1 < blk.nchunks) {
+        rec = rec_of(c + 1);
+        load_pass(rec, slot + 1, 0);
+      }
+      __syncthreads();
+      if (active) {
+        const int nkb = (rows + 31) / 32;
+        for (int kb = 0; kb < nkb; ++kb) {
+          u32x4 xa[K::TPW], bb[K::TNW];
+#pragma unroll
+          for (int a = 0; a < K::TPW; ++a) xa[a] = frag_k_rows_accpair(xw, K::XP, 32 * kb, (p0t + a) * 16, lane);
+#pragma unroll
+          for (int b = 0; b < K::TNW; ++b) bb[b] = frag_k_rows_accpair(bs, K::BP, 32 * kb, (n0t + b) * 16, lane);
+#pragma unroll
+          for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+            for (int b = 0; b < K::TNW; ++b) acc[a][b] = mfma16x16x32(xa[a], bb[b], acc[a][b]);
+        }
+      }
+    }
+  }
+
+  if (tid == 0) bdecay[m * H + h] = total;
   if (!active) return;
-  float* out = states + (slot * H + h) * (long)(P * N);
+  float* out = bstates + (m * H + h) * (long)(P * N);
 #pragma unroll
-  for (int a = 0; a < TPW; ++a)
+  for (int a = 0; a < K::TPW; ++a)
 #pragma unroll
-    for (int b = 0; b < TNW; ++b)
+    for (int b = 0; b < K::TNW; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = (wp * TPW + a) * 16 + 4 * g4 + r;
-        const int n = (wn * TNW + b) * 16 + l16;
+        const int p = (p0t + a) * 16 + 4 * g4 + r;
+        const int n = (n0t + b) * 16 + l16;
         out[p * N + n] = acc[a][b][r];
       }
 }
 
 // ----------------------------------------------------------------------------
-// fp32 path (plain FMA, fp32 accumulation): tokens staged 32 at a time in LDS.
+// fp32 path (plain FMA, fp32 accumulation; one chunk per state block): tokens
+// staged 32 at a time in LDS.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __restrict__ X,
                                                               const float* __restrict__ B,
                                                               const int4* __restrict__ table,
                                                               const float* __restrict__ cs,
-                                                              float* __restrict__ states, int H, int G,
+                                                              float* __restrict__ states,
+                                                              float* __restrict__ bdecay, int H, int G,
                                                               int P, int N, int Q) {
   const long unit = blockIdx.x;
   const int h = (int)(unit % H);
@@ -163,6 +215,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
   float* bs = sm + JB * P;   // [JB][N]
   const float* csr = cs + (slot * H + h) * (long)Q;
   const float cs_last = csr[Q - 1];
+  if (threadIdx.x == 0) bdecay[slot * H + h] = cs_last;
   const int PN = P * N;
   constexpr int kPer = 8;  // outputs per thread per pass
   float* out = states + (slot * H + h) * (long)PN;
@@ -207,17 +260,16 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
 template <int P, int N>
 static hipError_t launch_state_bf16(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
                                     hipStream_t stream) {
-  const int qb = d.Q < kSubTokens ? d.Q : kSubTokens;
-  const size_t lds = (size_t)(P + N) * (qb + 8) * 2 + (size_t)qb * 4;
+  const size_t lds = chunk_state_bf16_lds_bytes(P, N);
   auto kern = chunk_state_bf16_kernel<P, N>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(d.nslots * d.H)), dim3(256), lds, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * d.H)), dim3(kStateThreads), lds, stream,
                      reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B), ws.table,
-                     ws.cs, ws.chunk_states, d.H, d.G, d.Q);
+                     ws.btable, ws.cs, ws.bstates, ws.bdecay, d.H, d.G, d.Q);
   return hipGetLastError();
 }
 
@@ -239,7 +291,7 @@ hipError_t launch_chunk_state(const FwdDims& d, const void* X, const void* B, co
     const size_t lds = (size_t)32 * (d.P + d.N) * 4;
     hipLaunchKernelGGL(chunk_state_f32_kernel, dim3((unsigned)(d.nslots * d.H)), dim3(256), lds, stream,
                        reinterpret_cast<const float*>(X), reinterpret_cast<const float*>(B), ws.table, ws.cs,
-                       ws.chunk_states, d.H, d.G, d.P, d.N, d.Q);
+                       ws.bstates, ws.bdecay, d.H, d.G, d.P, d.N, d.Q);
     return hipGetLastError();
   }
   switch (d.P) {

@@ -12,40 +12,71 @@
 namespace ssd {
 
 // ----------------------------------------------------------------------------
-// chunk_cumsum: one workgroup per chunk slot. Locates the slot's tokens
-// (packed rows: sequence s owns slots floor(cu[s]/Q) + s + j), writes the slot
-// record, then for every head the inclusive prefix sum of log_a over the
-// chunk, scaled by log2(e) so that later stages use exp2. Positions past the
-// chunk's length repeat the chunk total (zero increments).
+// chunk_cumsum: grid (slot x, head group y, row z). Workgroup x locates chunk
+// slot x (packed rows: sequence s owns slots floor(cu[s]/Q) + s + j) and block
+// slot x (sequence s owns block slots floor(cu[s]/(Gs*Q)) + s + j, each block
+// being Gs consecutive chunks); the head-group-0 workgroup writes both records.
+// Each of its four waves then takes one head and writes the inclusive prefix
+// sum of log_a over the chunk, scaled by log2(e) so that later stages use exp2.
+// Positions past the chunk's length repeat the chunk total exactly.
 // ----------------------------------------------------------------------------
+__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, long x, int span) {
+  // base_s = floor(cu[s]/span) + s is strictly increasing in s: the last s with base_s <= x.
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const long base = cu[mid] / span + mid;
+    if (base <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ la,
                                                            const int32_t* __restrict__ cu, int S,
-                                                           int T, int H, int Q, long slots_per_row,
-                                                           int4* __restrict__ table,
+                                                           int T, int H, int Q, int Gs, long slots_per_row,
+                                                           long blocks_per_row, int4* __restrict__ table,
+                                                           int4* __restrict__ btable,
                                                            float* __restrict__ cs) {
-  const int row = blockIdx.y;
-  const long sl = blockIdx.x;
-  const long slot = (long)row * slots_per_row + sl;
+  const int row = blockIdx.z;
+  const long x = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
 
+  if (blockIdx.y == 0 && threadIdx.x == 0 && x < blocks_per_row) {
+    int seq, first = 0, nch = 0;
+    if (cu == nullptr) {
+      seq = row;
+      first = (int)(x * Gs);
+      nch = (int)min((long)Gs, slots_per_row - x * Gs);
+      first += (int)(row * slots_per_row);
+    } else {
+      const int span = Gs * Q;
+      seq = find_seq(cu, S, x, span);
+      const int b = cu[seq], e = cu[seq + 1];
+      const long j = x - (long)(b / span + seq);
+      const int nblk = (e - b + span - 1) / span;
+      if (j >= 0 && j < nblk) {
+        const int nchs = (e - b + Q - 1) / Q;
+        first = b / Q + seq + (int)j * Gs;
+        nch = min(Gs, nchs - (int)j * Gs);
+      }
+    }
+    btable[row * blocks_per_row + x] = make_int4(seq, first, nch, 0);
+  }
+  if (x >= slots_per_row) return;
+
+  const long slot = (long)row * slots_per_row + x;
   int seq, t0, len, kidx;
   if (cu == nullptr) {
     seq = row;
-    kidx = (int)sl;
+    kidx = (int)x;
     t0 = kidx * Q;
     len = min(Q, T - t0);
   } else {
-    // base_s = floor(cu[s]/Q) + s is strictly increasing in s: binary search
-    // for the last sequence whose base is <= sl.
-    int lo = 0, hi = S - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      const long base = cu[mid] / Q + mid;
-      if (base <= sl) lo = mid; else hi = mid - 1;
-    }
-    const int b = cu[lo], e = cu[lo + 1];
-    const long j = sl - (long)(b / Q + lo);
+    seq = find_seq(cu, S, x, Q);
+    const int b = cu[seq], e = cu[seq + 1];
+    const long j = x - (long)(b / Q + seq);
     const int nch = (e - b + Q - 1) / Q;
-    seq = lo;
     if (j < 0 || j >= nch) {
       kidx = -1;
       t0 = 0;
@@ -57,75 +88,73 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
     }
   }
   const int tok0 = row * T + t0;  // token index flattened over rows
-  if (threadIdx.x == 0) table[slot] = make_int4(seq, tok0, len, kidx);
-  if (len <= 0) return;
+  if (blockIdx.y == 0 && threadIdx.x == 0) table[slot] = make_int4(seq, tok0, len, kidx);
+  const int h = blockIdx.y * 4 + wave;
+  if (len <= 0 || h >= H) return;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int h = wave; h < H; h += 4) {
-    float carry = 0.f;  // inclusive sum up to the last valid token seen so far
-    float* out = cs + (slot * H + h) * (long)Q;
-    for (int jb = 0; jb < Q; jb += 64) {
-      const int j = jb + lane;
-      if (jb < len) {
-        float v = (j < len) ? la[(long)(tok0 + j) * H + h] : 0.f;
+  float carry = 0.f;  // inclusive sum up to the last valid token seen so far
+  float* out = cs + (slot * H + h) * (long)Q;
+  for (int jb = 0; jb < Q; jb += 64) {
+    const int j = jb + lane;
+    if (jb < len) {
+      float v = (j < len) ? la[(long)(tok0 + j) * H + h] : 0.f;
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const float u = __shfl_up(v, d);
-          if (lane >= d) v += u;
-        }
-        v += carry;
-        carry = __shfl(v, min(len - jb, 64) - 1);
-        if (j < Q) out[j] = (j < len ? v : carry) * kLog2e;
-      } else if (j < Q) {
-        out[j] = carry * kLog2e;
+      for (int d = 1; d < 64; d <<= 1) {
+        const float u = __shfl_up(v, d);
+        if (lane >= d) v += u;
       }
+      v += carry;
+      carry = __shfl(v, min(len - jb, 64) - 1);
+      if (j < Q) out[j] = (j < len ? v : carry) * kLog2e;
+    } else if (j < Q) {
+      out[j] = carry * kLog2e;
     }
   }
 }
 
 hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32_t* cu,
                                const Workspace& ws, hipStream_t stream) {
-  dim3 grid((unsigned)d.slots_per_row, (unsigned)d.batch);
-  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(256), 0, stream, log_a, cu, d.num_seqs, d.T, d.H,
-                     d.Q, d.slots_per_row, ws.table, ws.cs);
+  const long gx = d.slots_per_row > d.blocks_per_row ? d.slots_per_row : d.blocks_per_row;
+  dim3 grid((unsigned)gx, (unsigned)((d.H + 3) / 4), (unsigned)d.batch);
+  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(256), 0, stream, log_a, cu, d.num_seqs, d.T, d.H, d.Q,
+                     d.state_block, d.slots_per_row, d.blocks_per_row, ws.table, ws.btable, ws.cs);
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
-// state_passing: h = 0; for each chunk k of a sequence: start_k = h;
-// h = exp2(total_k) h + s_k. One thread owns 4 consecutive (p, n) elements of
-// one (sequence, head); the chunk loop is unrolled so that the loads of four
-// chunks are in flight together. Sequence s: packed rows own slots
-// floor(cu[s]/Q) + s ..; unpacked row s owns slots s*slots_per_row ...
+// state_passing: h = 0; for each state block m of a sequence: start_m = h;
+// h = exp2(total_m) h + s_m. One thread owns 4 consecutive (p, n) elements of
+// one (sequence, head); the block loop is unrolled so that the loads of four
+// blocks are in flight together. Sequence s: packed rows own block slots
+// floor(cu[s]/(Gs*Q)) + s ..; unpacked row s owns s*blocks_per_row ...
 // ----------------------------------------------------------------------------
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ states,
+                                                            const float* __restrict__ bdecay,
                                                             void* __restrict__ start,
                                                             float* __restrict__ final_state,
-                                                            const float* __restrict__ cs,
                                                             const int32_t* __restrict__ cu,
-                                                            long slots_per_row, int H, int PN, int Q) {
+                                                            long blocks_per_row, int H, int PN, int span) {
   const int eblocks = (PN / 4 + 255) / 256;
   const long unit = blockIdx.x;
   const int e = (int)(unit % eblocks) * 1024 + threadIdx.x * 4;
   const int h = (int)((unit / eblocks) % H);
   const int s = (int)(unit / ((long)eblocks * H));
   long base;
-  int nch;
+  int nblk;
   if (cu) {
     const int b = cu[s], en = cu[s + 1];
-    base = b / Q + s;
-    nch = (en - b + Q - 1) / Q;
+    base = b / span + s;
+    nblk = (en - b + span - 1) / span;
   } else {
-    base = (long)s * slots_per_row;
-    nch = (int)slots_per_row;
+    base = (long)s * blocks_per_row;
+    nblk = (int)blocks_per_row;
   }
   if (e >= PN) return;
 
   f32x4 hc = {0.f, 0.f, 0.f, 0.f};
-  auto put = [&](long slot, f32x4 v) {
-    const long off = (slot * H + h) * (long)PN + e;
+  auto put = [&](long blk, f32x4 v) {
+    const long off = (blk * H + h) * (long)PN + e;
     if (OUT_BF16) {
       u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(start) + off) = w;
@@ -134,14 +163,14 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
     }
   };
   int k = 0;
-  for (; k + 4 <= nch; k += 4) {
+  for (; k + 4 <= nblk; k += 4) {
     f32x4 sv[4];
     float dv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const long slot = base + k + u;
-      sv[u] = *reinterpret_cast<const f32x4*>(states + (slot * H + h) * (long)PN + e);
-      dv[u] = cs[(slot * H + h) * (long)Q + Q - 1];
+      const long blk = base + k + u;
+      sv[u] = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
+      dv[u] = bdecay[blk * H + h];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -150,11 +179,11 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
       hc = a * hc + sv[u];
     }
   }
-  for (; k < nch; ++k) {
-    const long slot = base + k;
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(states + (slot * H + h) * (long)PN + e);
-    const float a = fast_exp2(cs[(slot * H + h) * (long)Q + Q - 1]);
-    put(slot, hc);
+  for (; k < nblk; ++k) {
+    const long blk = base + k;
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
+    const float a = fast_exp2(bdecay[blk * H + h]);
+    put(blk, hc);
     hc = a * hc + sv;
   }
   if (final_state) *reinterpret_cast<f32x4*>(final_state + ((long)s * H + h) * PN + e) = hc;
@@ -166,12 +195,13 @@ hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, float* fina
   const int nseq = cu ? d.num_seqs : d.batch;
   const long eblocks = (PN / 4 + 255) / 256;
   dim3 grid((unsigned)(eblocks * d.H * nseq));
+  const int span = d.state_block * d.Q;
   if (d.bf16) {
-    hipLaunchKernelGGL(state_passing_kernel<true>, grid, dim3(256), 0, stream, ws.chunk_states,
-                       ws.start_states, final_state, ws.cs, cu, d.slots_per_row, d.H, PN, d.Q);
+    hipLaunchKernelGGL(state_passing_kernel<true>, grid, dim3(256), 0, stream, ws.bstates, ws.bdecay,
+                       ws.start_states, final_state, cu, d.blocks_per_row, d.H, PN, span);
   } else {
-    hipLaunchKernelGGL(state_passing_kernel<false>, grid, dim3(256), 0, stream, ws.chunk_states,
-                       ws.start_states, final_state, ws.cs, cu, d.slots_per_row, d.H, PN, d.Q);
+    hipLaunchKernelGGL(state_passing_kernel<false>, grid, dim3(256), 0, stream, ws.bstates, ws.bdecay,
+                       ws.start_states, final_state, cu, d.blocks_per_row, d.H, PN, span);
   }
   return hipGetLastError();
 }

@@ -77,3 +77,81 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 in[8], u32x4 out[8]
 }
 
 }  // namespace ssd
+
+namespace ssd {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte pieces addressed by
+// lanes 4k + i / 4, k = 0..3. When the 16 lanes of a group address a 4-row by
+// 16-column block of 16-bit values (lane 4k + c: row k, columns 4c..4c+3), lane
+// i receives column i of the 4 rows.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand with k along the rows of a row-major LDS tile W (pitch in
+// elements): lane (c = l % 16, g = l / 16) receives W[row(s)][col0 + c] for
+// its 8 slots s. Natural order: row(s) = row0 + 8g + s (the MFMA's own k order).
+__device__ __forceinline__ u32x4 frag_k_rows_natural(const uint16_t* W, int pitch, int row0, int col0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const uint16_t* p0 = W + (row0 + 8 * g + (i >> 2)) * pitch + col0 + 4 * (i & 3);
+  const u32x2 lo = lds_read_tr16(p0);
+  const u32x2 hi = lds_read_tr16(p0 + 4 * pitch);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// Same, with the slot order of a 16x16 accumulator pair: slots 0..3 hold rows
+// row0 + 4g + 0..3 and slots 4..7 hold rows row0 + 16 + 4g + 0..3.
+__device__ __forceinline__ u32x4 frag_k_rows_accpair(const uint16_t* W, int pitch, int row0, int col0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const uint16_t* p0 = W + (row0 + 4 * g + (i >> 2)) * pitch + col0 + 4 * (i & 3);
+  const u32x2 lo = lds_read_tr16(p0);
+  const u32x2 hi = lds_read_tr16(p0 + 16 * pitch);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// MFMA operand with k along the columns: lane (r = l % 16, g = l / 16) reads
+// W[row0 + r][col0 + 8g .. col0 + 8g + 7] (one 16-byte read).
+__device__ __forceinline__ u32x4 frag_k_cols(const uint16_t* W, int pitch, int row0, int col0, int lane) {
+  return *reinterpret_cast<const u32x4*>(W + (row0 + (lane & 15)) * pitch + col0 + 8 * (lane >> 4));
+}
+
+// LDS row pitch (elements of 16 bits) for a row of `cols` values: an odd
+// multiple of 32 bytes, which makes 16-byte row reads of 16 consecutive rows and
+// the pair-order transpose read (frag_k_rows_accpair) free of bank conflicts
+// on gfx950.
+__host__ __device__ constexpr int lds_pitch(int cols) { return ((cols / 16) % 2 == 0) ? cols + 16 : cols + 32; }
+
+// Row permutation within blocks of 32 rows under which a pair-order transpose
+// read returns rows in natural order: data row 8g + 4t + k is stored at row
+// 16t + 4g + k. frag_k_rows_accpair on rows stored at perm32(r) yields, in slot
+// s of lane group g, data row 8g + s.
+__device__ __forceinline__ int perm32(int r) {
+  return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
+}
+
+// Scale the 8 bf16 values of an operand by 8 fp32 weights and round back to bf16.
+__device__ __forceinline__ u32x4 scale_frag(u32x4 v, const float* w) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r[c] = pack_bf16x2(bf16_lo(v[c]) * w[2 * c], bf16_hi(v[c]) * w[2 * c + 1]);
+  return r;
+}
+
+// Block-slot record written by the cumsum stage: sequence, first chunk slot,
+// number of chunks (0: empty block slot).
+struct BlockRec {
+  int seq;
+  int slot0;
+  int nchunks;
+};
+
+__device__ __forceinline__ BlockRec load_block(const int4* table, long b) {
+  int4 v = table[b];
+  return BlockRec{v.x, v.y, v.z};
+}
+
+}  // namespace ssd

@@ -53,9 +53,9 @@ def shape(**kw):
                                               "num_seqs", "dtype")])
 
 
-def ws_bytes(sh, chunk):
+def ws_bytes(sh, chunk, gs=1):
     n = ctypes.c_size_t(0)
-    st = ssd.lib().ssd_fwd_workspace_bytes(ctypes.byref(sh), chunk, ctypes.byref(n))
+    st = ssd.lib().ssd_fwd_workspace_bytes(ctypes.byref(sh), chunk, gs, ctypes.byref(n))
     return st, n.value
 
 
@@ -65,24 +65,47 @@ def _align(v):
 
 def test_workspace_size_matches_layout():
     sh = shape()
-    st, n = ws_bytes(sh, 128)
+    st, n = ws_bytes(sh, 128, 1)
     assert st == OK
     slots = 16384 // 128
-    expect = _align(slots * 16) + _align(slots * 32 * 128 * 4) + _align(slots * 32 * 64 * 128 * 4) + \
-        _align(slots * 32 * 64 * 128 * 2)
+    PN = 64 * 128
+    expect = _align(slots * 16) * 2 + _align(slots * 32 * 128 * 4) + _align(slots * 32 * 4) + \
+        _align(slots * 32 * PN * 4) + _align(slots * 32 * PN * 2)
     assert n == expect
-    L = ssd.layout(sh, 128)
-    assert L.slots_per_row == slots and L.nslots == slots and L.total_bytes == n
-    # packed rows: floor(T/Q) + S slots
+    L = ssd.layout(sh, 128, 1)
+    assert L.slots_per_row == slots and L.nslots == slots and L.nblocks == slots and L.total_bytes == n
+    # state blocks of 4 chunks: a quarter of the block arrays
+    L4 = ssd.layout(sh, 128, 4)
+    assert L4.nslots == slots and L4.nblocks == slots // 4
+    assert L4.total_bytes == _align(slots * 16) + _align(slots // 4 * 16) + _align(slots * 32 * 128 * 4) + \
+        _align(slots // 4 * 32 * 4) + _align(slots // 4 * 32 * PN * 4) + _align(slots // 4 * 32 * PN * 2)
+    # packed rows: floor(T/Q) + S chunk slots, floor(T/(Gs*Q)) + S block slots
     sp = shape(seqlen=32768, nheads=80, num_seqs=7)
-    Lp = ssd.layout(sp, 128)
-    assert Lp.slots_per_row == 32768 // 128 + 7
-    # ragged T: ceil(T/Q) slots per row
-    Lr = ssd.layout(shape(batch=3, seqlen=1000), 64)
-    assert Lr.slots_per_row == 16 and Lr.nslots == 48
+    Lp = ssd.layout(sp, 128, 8)
+    assert Lp.slots_per_row == 32768 // 128 + 7 and Lp.blocks_per_row == 32768 // 1024 + 7
+    # ragged T: ceil(T/Q) chunk slots and ceil(slots/Gs) block slots per row
+    Lr = ssd.layout(shape(batch=3, seqlen=1000), 64, 4)
+    assert Lr.slots_per_row == 16 and Lr.nslots == 48 and Lr.blocks_per_row == 4 and Lr.nblocks == 12
     # fp32 start states are 4 bytes
-    L32 = ssd.layout(shape(dtype=0, seqlen=256, nheads=2, headdim=16, dstate=16), 32)
+    L32 = ssd.layout(shape(dtype=0, seqlen=256, nheads=2, headdim=16, dstate=16), 32, 1)
     assert L32.total_bytes - L32.start_states_offset == _align(8 * 2 * 16 * 16 * 4)
+
+
+def test_default_state_block():
+    L = ssd.lib()
+    assert L.ssd_default_state_block(ctypes.byref(shape(dtype=0, seqlen=4096)), 64) == 1
+    gs = L.ssd_default_state_block(ctypes.byref(shape()), 128)
+    assert gs in (1, 2, 4, 8, 16)
+    assert ssd.layout(shape(), 128, 0).nblocks == 128 // gs
+    # small problems keep one chunk per state block
+    assert L.ssd_default_state_block(ctypes.byref(shape(seqlen=256, nheads=2)), 128) == 1
+
+
+@pytest.mark.parametrize("kw,gs,code", [(dict(), 3, UNSUPPORTED), (dict(), 32, UNSUPPORTED),
+                                         (dict(dtype=0, dstate=64), 2, UNSUPPORTED), (dict(), 16, OK)])
+def test_state_block_rules(kw, gs, code):
+    st, _ = ws_bytes(shape(**kw), 128, gs)
+    assert st == code
 
 
 @pytest.mark.parametrize("kw,chunk,code", [
@@ -109,12 +132,14 @@ def test_fwd_rejects_bad_shapes(kw, chunk, code):
     L = ssd.lib()
     st = L.ssd_fwd(FAKE, FAKE, FAKE, FAKE, None, chunk, FAKE, FAKE, ctypes.byref(sh), FAKE, 1 << 40, None)
     assert st == code
+    st = L.ssd_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, chunk, 1, FAKE, FAKE, ctypes.byref(sh), FAKE, 1 << 40, None)
+    assert st == code
 
 
 def test_fwd_rejects_null_pointers_and_small_workspace():
     L = ssd.lib()
     sh = shape()
-    _, need = ws_bytes(sh, 128)
+    _, need = ws_bytes(sh, 128, 0)
     args = [FAKE, FAKE, FAKE, FAKE, None, 128, FAKE, FAKE, ctypes.byref(sh), FAKE, need, None]
     for i in (0, 1, 2, 3, 6, 9):  # X, log_a, B, C, Y, workspace
         a = list(args)
@@ -141,13 +166,15 @@ def test_packed_argument_rules():
 def test_stage_entry_points_validate():
     L = ssd.lib()
     sh = shape()
-    _, need = ws_bytes(sh, 128)
-    assert L.ssd_chunk_cumsum(None, None, 128, ctypes.byref(sh), FAKE, need, None) == INVALID
-    assert L.ssd_chunk_state(None, FAKE, None, 128, ctypes.byref(sh), FAKE, need, None) == INVALID
-    assert L.ssd_chunk_state(FAKE, FAKE, None, 128, ctypes.byref(sh), FAKE, need - 256, None) == WS_SMALL
-    assert L.ssd_state_passing(None, 128, None, ctypes.byref(sh), None, need, None) == INVALID
-    assert L.ssd_chunk_scan(FAKE, FAKE, None, None, 128, FAKE, ctypes.byref(sh), FAKE, need, None) == INVALID
-    assert L.ssd_chunk_scan(FAKE, FAKE, FAKE, None, 128, None, ctypes.byref(sh), FAKE, need, None) == INVALID
+    _, need = ws_bytes(sh, 128, 2)
+    assert L.ssd_chunk_cumsum(None, None, 128, 2, ctypes.byref(sh), FAKE, need, None) == INVALID
+    assert L.ssd_chunk_state(None, FAKE, None, 128, 2, ctypes.byref(sh), FAKE, need, None) == INVALID
+    assert L.ssd_chunk_state(FAKE, FAKE, None, 128, 2, ctypes.byref(sh), FAKE, need - 256, None) == WS_SMALL
+    assert L.ssd_chunk_state(FAKE, FAKE, None, 128, 1, ctypes.byref(sh), FAKE, need, None) == WS_SMALL
+    assert L.ssd_state_passing(None, 128, 2, None, ctypes.byref(sh), None, need, None) == INVALID
+    assert L.ssd_chunk_scan(FAKE, FAKE, None, None, 128, 2, FAKE, ctypes.byref(sh), FAKE, need, None) == INVALID
+    assert L.ssd_chunk_scan(FAKE, FAKE, FAKE, None, 128, 2, None, ctypes.byref(sh), FAKE, need, None) == INVALID
+    assert L.ssd_chunk_scan(FAKE, FAKE, FAKE, None, 128, 5, FAKE, ctypes.byref(sh), FAKE, need, None) == UNSUPPORTED
 
 
 def test_step_validates():

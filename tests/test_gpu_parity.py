@@ -36,9 +36,10 @@ def to_dev(d):
     return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
 
-def gpu_fwd(d, Q, **kw):
+def gpu_fwd(d, Q, gs=0, **kw):
     dd = to_dev(d)
-    Y, fin = ssd.fwd(dd["X"], dd["log_a"], dd["B"], dd["C"], cu_seqlens=dd.get("cu_seqlens"), chunk=Q, **kw)
+    Y, fin = ssd.fwd(dd["X"], dd["log_a"], dd["B"], dd["C"], cu_seqlens=dd.get("cu_seqlens"), chunk=Q,
+                     state_block=gs, **kw)
     torch.cuda.synchronize()
     return Y, fin
 
@@ -49,9 +50,9 @@ def oracle_fwd(d):
                           cu_seqlens=None if cu is None else cu.numpy())
 
 
-def check_fwd(d, Q, what):
-    say(f"[parity] {what}: X{tuple(d['X'].shape)} {d['X'].dtype} N={d['B'].shape[-1]} Q={Q}")
-    Y, fin = gpu_fwd(d, Q)
+def check_fwd(d, Q, what, gs=0):
+    say(f"[parity] {what}: X{tuple(d['X'].shape)} {d['X'].dtype} N={d['B'].shape[-1]} Q={Q} state_block={gs}")
+    Y, fin = gpu_fwd(d, Q, gs)
     Yr, fr = oracle_fwd(d)
     dt = dtype_name(d["X"])
     ey = assert_close(to_f64(Y), Yr, dt, what + " Y")
@@ -68,7 +69,9 @@ def check_fwd(d, Q, what):
 def test_workload_full_size(name):
     w = synth.WORKLOADS[name]
     d = synth.workload_inputs(w)
-    check_fwd(d, w.Q, name)
+    check_fwd(d, w.Q, name)              # the library's default state block
+    if w.dtype == "bf16":
+        check_fwd(d, w.Q, name + " (one chunk per state block)", gs=1)
 
 
 # ------------------------------------------------------------------ shapes and edge cases
@@ -154,87 +157,125 @@ def test_many_short_sequences():
 
 # ------------------------------------------------------------------ stage intermediates
 
-def stage_run(d, Q):
+def stage_run(d, Q, gs):
     dd = to_dev(d)
     X, la, B, C, cu = dd["X"], dd["log_a"], dd["B"], dd["C"], dd.get("cu_seqlens")
     sh = ssd.make_shape(X, B, cu)
-    ws = ssd.Workspace(sh, Q, X.device)
+    ws = ssd.Workspace(sh, Q, X.device, gs)
     nseq = X.shape[0] if cu is None else cu.numel() - 1
     fin = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
     Y = torch.empty_like(X)
-    ssd.chunk_cumsum(la, cu, Q, sh, ws)
-    ssd.chunk_state(X, B, cu, Q, sh, ws)
-    ssd.state_passing(cu, Q, fin, sh, ws)
-    ssd.chunk_scan(X, B, C, cu, Q, Y, sh, ws)
+    ssd.chunk_cumsum(la, cu, sh, ws)
+    ssd.chunk_state(X, B, cu, sh, ws)
+    ssd.state_passing(cu, fin, sh, ws)
+    ssd.chunk_scan(X, B, C, cu, Y, sh, ws)
     torch.cuda.synchronize()
     return ws, Y, fin
 
 
-@pytest.mark.parametrize("packed,dt,Q", [(False, torch.bfloat16, 64), (True, torch.bfloat16, 64),
-                                         (False, torch.float32, 32), (True, torch.float32, 16)])
-def test_stage_intermediates(packed, dt, Q):
+def _slots(units, span, rows, T, cu):
+    """Documented slot numbering of chunks (span = Q) or state blocks (span = Gs*Q)."""
+    out = []
+    if cu is None:
+        per_row = -(-T // span) if span else 0
+        for (r, b, e) in units:
+            out.append(r * per_row + b // span)
+    else:
+        for (r, b, e) in units:
+            s = int(np.searchsorted(cu, b, side="right") - 1)
+            out.append(int(cu[s]) // span + s + (b - int(cu[s])) // span)
+    return out
+
+
+@pytest.mark.parametrize("packed,dt,Q,gs", [(False, torch.bfloat16, 64, 1), (True, torch.bfloat16, 64, 1),
+                                            (False, torch.bfloat16, 32, 4), (True, torch.bfloat16, 32, 2),
+                                            (False, torch.float32, 32, 1), (True, torch.float32, 16, 1)])
+def test_stage_intermediates(packed, dt, Q, gs):
     rows = 1 if packed else 2
-    lengths = [70, 1, 130, 64] if packed else None
+    lengths = [70, 1, 130, 64, 200] if packed else None
     T = sum(lengths) if packed else 200
     d = synth.make_forward_inputs(rows, T, 3, 32, 64 if dt == torch.bfloat16 else 16, 1, dtype=dt, seed=21,
                                   lengths=lengths)
-    say(f"[parity] stage intermediates packed={packed} {dt} Q={Q}")
-    ws, Y, fin = stage_run(d, Q)
+    say(f"[parity] stage intermediates packed={packed} {dt} Q={Q} state_block={gs}")
+    ws, Y, fin = stage_run(d, Q, gs)
     X, la, B, C = (to_f64(d[k]) for k in ("X", "log_a", "B", "C"))
     cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].numpy()
     dts = dtype_name(d["X"])
-    table = ws.table().cpu().numpy()
     chunks = oracle.chunk_segments(rows, T, Q, cu)
-    # slot of every chunk, from the documented slot numbering
-    slots = []
-    if cu is None:
-        spr = -(-T // Q)
-        slots = [r * spr + (b // Q) for (r, b, e) in chunks]
-    else:
-        for (r, b, e) in chunks:
-            s = int(np.searchsorted(cu, b, side="right") - 1)
-            slots.append(int(cu[s]) // Q + s + (b - int(cu[s])) // Q)
-    # table records
-    for (r, b, e), sl in zip(chunks, slots):
+    blocks = oracle.chunk_segments(rows, T, Q * gs, cu)
+    cslots = _slots(chunks, Q, rows, T, cu)
+    bslots = _slots(blocks, Q * gs, rows, T, cu)
+    # chunk records and state-block records
+    table = ws.table().cpu().numpy()
+    for (r, b, e), sl in zip(chunks, cslots):
         assert table[sl, 1] == r * T + b and table[sl, 2] == e - b
-    used = set(slots)
-    for sl in range(table.shape[0]):
-        if sl not in used:
-            assert table[sl, 2] == 0
+    for sl in set(range(table.shape[0])) - set(cslots):
+        assert table[sl, 2] == 0
+    btable = ws.block_table().cpu().numpy()
+    for (r, b, e), bl in zip(blocks, bslots):
+        first = cslots[[c[1] for c in chunks if c[0] == r].index(b) + sum(1 for c in chunks if c[0] < r)]
+        assert btable[bl, 1] == first and btable[bl, 2] == -(-(e - b) // Q)
+    for bl in set(range(btable.shape[0])) - set(bslots):
+        assert btable[bl, 2] == 0
     # cumulative log decay, restarted per chunk, log2-scaled
     cs_ref = oracle.chunk_cumsum(la, chunks)
     cs_gpu = ws.cumsum().cpu().numpy()
-    for (r, b, e), sl in zip(chunks, slots):
+    for (r, b, e), sl in zip(chunks, cslots):
         ref = cs_ref[r, b:e].T * LOG2E                       # [H, q]
         got = cs_gpu[sl, :, :e - b]
         assert np.max(np.abs(got - ref)) <= 1e-4 + 1e-5 * np.max(np.abs(ref))
-        # padding positions repeat the chunk total
-        assert np.all(cs_gpu[sl, :, e - b:] == cs_gpu[sl, :, e - b - 1:e - b])
-    # right factors = oracle restarted at every chunk start
-    _, cst_ref, _ = oracle.scan(X, la, B, C, segments=chunks, want_y=False)
-    cst_gpu = ws.chunk_states().cpu().numpy()[slots]
-    assert_close(cst_gpu, cst_ref, dts, "chunk states")
-    # centre factors = oracle state entering each chunk (zero at sequence starts)
+        assert np.all(cs_gpu[sl, :, e - b:] == cs_gpu[sl, :, e - b - 1:e - b])  # padding repeats the total
+    # block decay = total log2 decay of each block
+    bd = ws.block_decay().cpu().numpy()
+    for (r, b, e), bl in zip(blocks, bslots):
+        ref = la[r, b:e].sum(axis=0) * LOG2E
+        assert np.max(np.abs(bd[bl] - ref)) <= 1e-4 + 1e-5 * np.max(np.abs(ref))
+    # right factors = oracle restarted at every block start, read at the block end
+    _, bst_ref, _ = oracle.scan(X, la, B, C, segments=blocks, want_y=False)
+    assert_close(ws.block_states().cpu().numpy()[bslots], bst_ref, dts, "block states")
+    # centre factors = oracle state entering each block (zero at sequence starts)
+    bounds = set() if cu is None else set(int(v) for v in cu)
     snap = -np.ones(rows * T, np.int32)
     first = []
-    bounds = set() if cu is None else set(int(v) for v in cu)
-    for k, (r, b, e) in enumerate(chunks):
-        if k + 1 < len(chunks) and chunks[k + 1][0] == r and chunks[k + 1][1] == e and e not in bounds:
+    for k, (r, b, e) in enumerate(blocks):
+        first.append(b == 0 if cu is None else b in bounds)
+        if k + 1 < len(blocks) and blocks[k + 1][0] == r and blocks[k + 1][1] == e and e not in bounds:
             snap[r * T + e - 1] = k + 1
-    for k, (r, b, e) in enumerate(chunks):
-        is_first = (cu is None and b == 0) or (cu is not None and b in set(cu.tolist()))
-        first.append(is_first)
     segs = oracle.sequence_segments(rows, T, cu)
-    _, _, snaps = oracle.scan(X, la, B, C, segments=segs, want_y=False, snap_slot=snap, nsnaps=len(chunks) + 1)
-    st_gpu = ws.start_states().float().cpu().numpy()[slots]
-    for k in range(len(chunks)):
+    _, _, snaps = oracle.scan(X, la, B, C, segments=segs, want_y=False, snap_slot=snap, nsnaps=len(blocks) + 1)
+    st_gpu = ws.start_states().float().cpu().numpy()[bslots]
+    for k in range(len(blocks)):
         if first[k]:
             assert np.all(st_gpu[k] == 0)
-    idx = [k for k in range(len(chunks)) if not first[k]]
-    assert_close(st_gpu[idx], snaps[idx], dts, "start states")
-    # stage-by-stage equals ssd_fwd bitwise
-    Y2, fin2 = gpu_fwd(d, Q)
+    idx = [k for k in range(len(blocks)) if not first[k]]
+    if idx:
+        assert_close(st_gpu[idx], snaps[idx], dts, "start states")
+    # outputs, and stage-by-stage equals ssd_fwd_ex bitwise
+    Yr, fr = oracle_fwd(d)
+    assert_close(to_f64(Y), Yr, dts, "Y")
+    assert_close(to_f64(fin), fr, dts, "final")
+    Y2, fin2 = gpu_fwd(d, Q, gs)
     assert torch.equal(Y, Y2) and torch.equal(fin, fin2)
+
+
+@pytest.mark.parametrize("gs", [1, 2, 4, 8, 16])
+def test_state_block_invariance(gs):
+    d = synth.make_forward_inputs(2, 3000, 4, 64, 128, 1, dtype=torch.bfloat16, seed=44)
+    check_fwd(d, 128, f"state block {gs}", gs=gs)
+
+
+@pytest.mark.parametrize("gs", [2, 8])
+def test_state_block_packed(gs):
+    lengths = [1, 700, 64, 65, 3, 1290, 1, 300]
+    d = synth.make_forward_inputs(1, sum(lengths), 3, 64, 64, 1, dtype=torch.bfloat16, seed=45, lengths=lengths)
+    check_fwd(d, 64, f"packed state block {gs}", gs=gs)
+
+
+@pytest.mark.parametrize("P,N,Q,gs", [(16, 32, 32, 4), (32, 64, 64, 2), (128, 128, 64, 4), (64, 256, 64, 4),
+                                      (128, 64, 128, 2), (64, 128, 256, 2)])
+def test_state_block_shapes(P, N, Q, gs):
+    d = synth.make_forward_inputs(1, 1100, 2, P, N, 1, dtype=torch.bfloat16, seed=46 + P + N)
+    check_fwd(d, Q, f"P={P} N={N} Q={Q}", gs=gs)
 
 
 def test_deterministic():
