@@ -44,7 +44,7 @@
  * Supported sizes: headdim in {16, 32, 64, 128}; dstate in {16, 32, 64, 128,
  * 256}; chunk in {16, 32, 64, 128, 256}; state_block in {1, 2, 4, 8, 16}; for
  * bf16, chunk >= 32 and dstate >= 32 and the chunk tiles must fit the 160 KiB
- * LDS; for fp32, state_block = 1. Other sizes return SSD_ERR_UNSUPPORTED. Every
+ * LDS; for fp32, state_block = 1; chunk * (nheads + 1) * 4 bytes <= 160 KiB. Other sizes return SSD_ERR_UNSUPPORTED. Every
  * tensor must hold fewer than 2^31 elements.
  */
 #ifndef SSD_MI355X_H

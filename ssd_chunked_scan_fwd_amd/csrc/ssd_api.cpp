@@ -47,6 +47,8 @@ ssd_status check_shape(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
   const int64_t bt = (int64_t)s->batch * s->seqlen;
   if (bt * s->nheads * s->headdim > kMaxElems || bt * s->ngroups * s->dstate > kMaxElems)
     return SSD_ERR_UNSUPPORTED;
+  // the cumsum stage holds one chunk of log_a, [chunk][nheads + 1] fp32, in LDS
+  if ((int64_t)chunk * (s->nheads + 1) * 4 > (int64_t)ssd::kMaxLdsBytes) return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
 

@@ -314,50 +314,42 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 #pragma unroll
       for (int pt = 0; pt < K::TP; ++pt) acc[pt] *= em;
       const float* vrow = Vt + it * Q + 4 * g4;
-      const f32x4 uu = *reinterpret_cast<const f32x4*>(Ut + it * 16 + 4 * g4);
+      const float cs_i = csl[irow];
       const int kbd = it >> 1;  // key block holding the diagonal tile
-      for (int kb = 0; kb <= kbd; ++kb) {
-        if (kb == kbd) {
-          // Apply u_i now: the diagonal key block uses the exact masked decay.
+      // One key block of 32 tokens: S^T tiles of both halves (two interleaved
+      // MFMA chains), the decay factor, the bf16 hi/lo split, then Y += M X.
+      // diag: exact masked decay (a half above the diagonal masks to zero);
+      // otherwise the tabulated (or computed) v_j, u_i being applied later.
+      auto key_block = [&](int kb, bool diag) {
+        u32x4 bfr[2][K::NB];
 #pragma unroll
-          for (int pt = 0; pt < K::TP; ++pt)
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[pt][r] *= uu[r];
+          for (int nb = 0; nb < K::NB; ++nb) bfr[half][nb] = frag_k_cols(bs, K::BP, (2 * kb + half) * 16, nb * 32, lane);
+        f32x4 fac[2];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int j0 = (2 * kb + half) * 16 + 4 * g4;
+          if (diag || !kVTable) {
+            const f32x4 cj = *reinterpret_cast<const f32x4*>(csl + j0);
+            const float ref = diag ? cs_i : csl[16 * it];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) fac[half][r] = (!diag || j0 + r <= irow) ? fast_exp2(ref - cj[r]) : 0.f;
+          } else {
+            fac[half] = *reinterpret_cast<const f32x4*>(vrow + (2 * kb + half) * 16);
+          }
         }
-        const float cs_i = csl[irow];
+        f32x4 sv[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int nb = 0; nb < K::NB; ++nb)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) sv[half] = mfma16x16x32(bfr[half][nb], cf[k][nb], sv[half]);
         uint32_t mw[4], ml[4];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int jt = 2 * kb + half;
-          if (jt > it) {
-            mw[2 * half] = mw[2 * half + 1] = 0u;
-            ml[2 * half] = ml[2 * half + 1] = 0u;
-            continue;
-          }
-          f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int nb = 0; nb < K::NB; ++nb)
-            sv = mfma16x16x32(frag_k_cols(bs, K::BP, jt * 16, nb * 32, lane), cf[k][nb], sv);
-          // sv[r] = S[i = irow][j = jt*16 + 4*g4 + r]
           float v[4];
-          if (kb == kbd) {  // exact decay, mask first
-            const f32x4 cj = *reinterpret_cast<const f32x4*>(csl + jt * 16 + 4 * g4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              v[r] = (jt * 16 + 4 * g4 + r <= irow) ? sv[r] * fast_exp2(cs_i - cj[r]) : 0.f;
-          } else {          // v_j (table or computed); u_i applied to the accumulator
-            f32x4 vv;
-            if (kVTable) {
-              vv = *reinterpret_cast<const f32x4*>(vrow + jt * 16);
-            } else {
-              const f32x4 cj = *reinterpret_cast<const f32x4*>(csl + jt * 16 + 4 * g4);
-              const float mt = csl[16 * it];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) vv[r] = fast_exp2(mt - cj[r]);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = sv[r] * vv[r];
-          }
+          for (int r = 0; r < 4; ++r) v[r] = sv[half][r] * fac[half][r];
           mw[2 * half] = pack_bf16x2(v[0], v[1]);
           mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
           ml[2 * half] = pack_bf16x2(v[0] - bf16_lo(mw[2 * half]), v[1] - bf16_hi(mw[2 * half]));
@@ -365,13 +357,22 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
         }
         const u32x4 ah = u32x4{mw[0], mw[1], mw[2], mw[3]};
         const u32x4 al = u32x4{ml[0], ml[1], ml[2], ml[3]};
+        u32x4 xf[K::TP];
 #pragma unroll
-        for (int pt = 0; pt < K::TP; ++pt) {
-          const u32x4 xf = frag_k_rows_accpair(xs, K::XP, 32 * kb, pt * 16, lane);
-          acc[pt] = mfma16x16x32(ah, xf, acc[pt]);
-          acc[pt] = mfma16x16x32(al, xf, acc[pt]);
-        }
-      }
+        for (int pt = 0; pt < K::TP; ++pt) xf[pt] = frag_k_rows_accpair(xs, K::XP, 32 * kb, pt * 16, lane);
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) acc[pt] = mfma16x16x32(ah, xf[pt], acc[pt]);
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) acc[pt] = mfma16x16x32(al, xf[pt], acc[pt]);
+      };
+      for (int kb = 0; kb < kbd; ++kb) key_block(kb, false);
+      // u_i now: the diagonal key block uses the exact masked decay.
+      const f32x4 uu = *reinterpret_cast<const f32x4*>(Ut + it * 16 + 4 * g4);
+#pragma unroll
+      for (int pt = 0; pt < K::TP; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[pt][r] *= uu[r];
+      key_block(kbd, true);
       // Out through the wave's staging tile as 16-byte rows.
       const bool row_ok = it * 16 + l16 < len;
       uint16_t* yrow = Y + ((tok0 + it * 16 + l16) * H + h) * P;

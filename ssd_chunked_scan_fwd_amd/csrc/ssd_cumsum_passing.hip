@@ -12,13 +12,14 @@
 namespace ssd {
 
 // ----------------------------------------------------------------------------
-// chunk_cumsum: grid (slot x, head group y, row z). Workgroup x locates chunk
-// slot x (packed rows: sequence s owns slots floor(cu[s]/Q) + s + j) and block
-// slot x (sequence s owns block slots floor(cu[s]/(Gs*Q)) + s + j, each block
-// being Gs consecutive chunks); the head-group-0 workgroup writes both records.
-// Each of its four waves then takes one head and writes the inclusive prefix
-// sum of log_a over the chunk, scaled by log2(e) so that later stages use exp2.
-// Positions past the chunk's length repeat the chunk total exactly.
+// chunk_cumsum: grid (slot x, row y). Workgroup x locates chunk slot x (packed
+// rows: sequence s owns slots floor(cu[s]/Q) + s + j) and block slot x
+// (sequence s owns block slots floor(cu[s]/(Gs*Q)) + s + j, each block being Gs
+// consecutive chunks) and writes both records. It reads the chunk's log_a
+// rows (contiguous, [len][H]) into LDS, then each wave takes heads in turn and
+// (16 waves) writes the inclusive prefix sum over the chunk, scaled by log2(e) so that
+// later stages use exp2. Positions past the chunk's length repeat the chunk
+// total exactly.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, long x, int span) {
   // base_s = floor(cu[s]/span) + s is strictly increasing in s: the last s with base_s <= x.
@@ -31,18 +32,19 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, l
   return lo;
 }
 
-__global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restrict__ la,
+__global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const float* __restrict__ la,
                                                            const int32_t* __restrict__ cu, int S,
                                                            int T, int H, int Q, int Gs, long slots_per_row,
                                                            long blocks_per_row, int4* __restrict__ table,
                                                            int4* __restrict__ btable,
                                                            float* __restrict__ cs) {
-  const int row = blockIdx.z;
+  extern __shared__ float tile[];  // [Q][H + 1] log_a of the chunk, token-major
+  const int row = blockIdx.y;
   const long x = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  if (blockIdx.y == 0 && threadIdx.x == 0 && x < blocks_per_row) {
+  if (threadIdx.x == 0 && x < blocks_per_row) {
     int seq, first = 0, nch = 0;
     if (cu == nullptr) {
       seq = row;
@@ -88,26 +90,33 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
     }
   }
   const int tok0 = row * T + t0;  // token index flattened over rows
-  if (blockIdx.y == 0 && threadIdx.x == 0) table[slot] = make_int4(seq, tok0, len, kidx);
-  const int h = blockIdx.y * 4 + wave;
-  if (len <= 0 || h >= H) return;
+  if (threadIdx.x == 0) table[slot] = make_int4(seq, tok0, len, kidx);
+  if (len <= 0) return;
 
-  float carry = 0.f;  // inclusive sum up to the last valid token seen so far
-  float* out = cs + (slot * H + h) * (long)Q;
-  for (int jb = 0; jb < Q; jb += 64) {
-    const int j = jb + lane;
-    if (jb < len) {
-      float v = (j < len) ? la[(long)(tok0 + j) * H + h] : 0.f;
+  // The chunk's log_a rows are contiguous: read them coalesced into LDS.
+  const int HP = H + 1;
+  const float* src = la + (long)tok0 * H;
+  for (int idx = threadIdx.x; idx < len * H; idx += 1024) tile[(idx / H) * HP + idx % H] = src[idx];
+  __syncthreads();
+
+  for (int h = wave; h < H; h += 16) {
+    float carry = 0.f;  // inclusive sum up to the last valid token seen so far
+    float* out = cs + (slot * H + h) * (long)Q;
+    for (int jb = 0; jb < Q; jb += 64) {
+      const int j = jb + lane;
+      if (jb < len) {
+        float v = (j < len) ? tile[j * HP + h] : 0.f;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float u = __shfl_up(v, d);
-        if (lane >= d) v += u;
+        for (int d = 1; d < 64; d <<= 1) {
+          const float u = __shfl_up(v, d);
+          if (lane >= d) v += u;
+        }
+        v += carry;
+        carry = __shfl(v, min(len - jb, 64) - 1);
+        if (j < Q) out[j] = (j < len ? v : carry) * kLog2e;
+      } else if (j < Q) {
+        out[j] = carry * kLog2e;
       }
-      v += carry;
-      carry = __shfl(v, min(len - jb, 64) - 1);
-      if (j < Q) out[j] = (j < len ? v : carry) * kLog2e;
-    } else if (j < Q) {
-      out[j] = carry * kLog2e;
     }
   }
 }
@@ -115,17 +124,23 @@ __global__ __launch_bounds__(256) void chunk_cumsum_kernel(const float* __restri
 hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32_t* cu,
                                const Workspace& ws, hipStream_t stream) {
   const long gx = d.slots_per_row > d.blocks_per_row ? d.slots_per_row : d.blocks_per_row;
-  dim3 grid((unsigned)gx, (unsigned)((d.H + 3) / 4), (unsigned)d.batch);
-  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(256), 0, stream, log_a, cu, d.num_seqs, d.T, d.H, d.Q,
+  const size_t lds = (size_t)d.Q * (d.H + 1) * sizeof(float);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_cumsum_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)gx, (unsigned)d.batch);
+  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(1024), lds, stream, log_a, cu, d.num_seqs, d.T, d.H, d.Q,
                      d.state_block, d.slots_per_row, d.blocks_per_row, ws.table, ws.btable, ws.cs);
   return hipGetLastError();
 }
 
 // ----------------------------------------------------------------------------
 // state_passing: h = 0; for each state block m of a sequence: start_m = h;
-// h = exp2(total_m) h + s_m. One thread owns 4 consecutive (p, n) elements of
-// one (sequence, head); the block loop is unrolled so that the loads of four
-// blocks are in flight together. Sequence s: packed rows own block slots
+// h = exp2(total_m) h + s_m. One thread owns 2 consecutive (p, n) elements of
+// one (sequence, head); the block loop is unrolled so that the loads of
+// sixteen blocks are in flight together. Sequence s: packed rows own block slots
 // floor(cu[s]/(Gs*Q)) + s ..; unpacked row s owns s*blocks_per_row ...
 // ----------------------------------------------------------------------------
 template <bool OUT_BF16>
@@ -135,9 +150,9 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
                                                             float* __restrict__ final_state,
                                                             const int32_t* __restrict__ cu,
                                                             long blocks_per_row, int H, int PN, int span) {
-  const int eblocks = (PN / 4 + 255) / 256;
+  const int eblocks = (PN / 2 + 255) / 256;
   const long unit = blockIdx.x;
-  const int e = (int)(unit % eblocks) * 1024 + threadIdx.x * 4;
+  const int e = (int)(unit % eblocks) * 512 + threadIdx.x * 2;
   const int h = (int)((unit / eblocks) % H);
   const int s = (int)(unit / ((long)eblocks * H));
   long base;
@@ -152,28 +167,28 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
   }
   if (e >= PN) return;
 
-  f32x4 hc = {0.f, 0.f, 0.f, 0.f};
-  auto put = [&](long blk, f32x4 v) {
+  f32x2 hc = {0.f, 0.f};
+  auto put = [&](long blk, f32x2 v) {
     const long off = (blk * H + h) * (long)PN + e;
     if (OUT_BF16) {
-      u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(start) + off) = w;
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(start) + off) = pack_bf16x2(v[0], v[1]);
     } else {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(start) + off) = v;
+      *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(start) + off) = v;
     }
   };
+  constexpr int U = 16;  // blocks whose loads are in flight together
   int k = 0;
-  for (; k + 4 <= nblk; k += 4) {
-    f32x4 sv[4];
-    float dv[4];
+  for (; k + U <= nblk; k += U) {
+    f32x2 sv[U];
+    float dv[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const long blk = base + k + u;
-      sv[u] = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
+      sv[u] = *reinterpret_cast<const f32x2*>(states + (blk * H + h) * (long)PN + e);
       dv[u] = bdecay[blk * H + h];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       put(base + k + u, hc);
       const float a = fast_exp2(dv[u]);
       hc = a * hc + sv[u];
@@ -181,19 +196,19 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
   }
   for (; k < nblk; ++k) {
     const long blk = base + k;
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
+    const f32x2 sv = *reinterpret_cast<const f32x2*>(states + (blk * H + h) * (long)PN + e);
     const float a = fast_exp2(bdecay[blk * H + h]);
     put(blk, hc);
     hc = a * hc + sv;
   }
-  if (final_state) *reinterpret_cast<f32x4*>(final_state + ((long)s * H + h) * PN + e) = hc;
+  if (final_state) *reinterpret_cast<f32x2*>(final_state + ((long)s * H + h) * PN + e) = hc;
 }
 
 hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, float* final_state,
                                 const Workspace& ws, hipStream_t stream) {
   const int PN = d.P * d.N;
   const int nseq = cu ? d.num_seqs : d.batch;
-  const long eblocks = (PN / 4 + 255) / 256;
+  const long eblocks = (PN / 2 + 255) / 256;
   dim3 grid((unsigned)(eblocks * d.H * nseq));
   const int span = d.state_block * d.Q;
   if (d.bf16) {
