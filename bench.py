@@ -16,8 +16,10 @@ and the fp64 CPU oracle timed on this host as a baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +34,43 @@ METRIC = "SSD fwd tokens/s & % of bf16 MFMA peak at T=16K, H=32, P=64, N=128"
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
+
+
+# Sources each stage's kernel is built from: a counter-based traffic figure is
+# reported only while these files are unchanged since the counters were taken.
+CSRC = os.path.join(ROOT, "ssd_chunked_scan_fwd_amd", "csrc")
+STAGE_SOURCES = {
+    "chunk_cumsum": ["ssd_cumsum_passing.hip", "ssd_device.h"],
+    "state_passing": ["ssd_cumsum_passing.hip", "ssd_device.h"],
+    "chunk_state": ["ssd_chunk_state.hip", "ssd_device.h", "ssd_stage.h"],
+    "chunk_scan": ["ssd_chunk_scan.hip", "ssd_device.h", "ssd_stage.h"],
+}
+
+
+def source_digest(stage: str) -> str:
+    h = hashlib.sha256()
+    for f in STAGE_SOURCES[stage]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(stage: str, workload: str, state_block: int):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE and WRITE_SIZE passes
+    summarised under profiles/ (scaled by the copy-kernel calibration there), or
+    None when there is no summary for this kernel, workload and state block or
+    the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    try:
+        if fields["source_sha256"] != source_digest(stage) or int(fields["state_block"]) != state_block:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def stage_bytes(w, nslots: int, nblocks: int, nseq: int) -> dict:
@@ -75,10 +114,19 @@ def main() -> int:
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--state-block", type=int, default=0, help="chunks per state block (0: library default)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the run, launch one elementwise copy of MIB MiB (read MIB, write MIB): the "
+                         "calibration kernel of the FETCH_SIZE / WRITE_SIZE counter passes")
+    ap.add_argument("--print-digest", action="store_true", help="print the source digest of each stage and exit")
     args = ap.parse_args()
 
+    if args.print_digest:
+        for st in STAGE_SOURCES:
+            print(st, source_digest(st))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the SSD forward path has no multi-GPU mode "
               "(run with --gpus 1).", file=sys.stderr)
@@ -148,7 +196,7 @@ def main() -> int:
         torch.cuda.synchronize()
         for (name, _), (a, b) in zip(stages, evs):
             acc[name] += a.elapsed_time(b)
-    stage_us = {k: v * 1e3 / args.stage_reps for k, v in acc.items()}
+    stage_us = {k: v * 1e3 / max(args.stage_reps, 1) for k, v in acc.items()}
     sbytes = stage_bytes(w, ws.layout.nslots, ws.layout.nblocks, w.batch)
     dominant = max(stage_us, key=stage_us.get)
     achieved = sbytes[dominant] / (stage_us[dominant] * 1e-6) / 1e9
@@ -176,7 +224,8 @@ def main() -> int:
                    "dstate": w.N, "ngroups": w.G, "chunk": w.Q, "state_block": ws.state_block,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dominant, w.name, ws.state_block),
                      "bytes_per_launch": sbytes[dominant], "avg_launch_us": round(stage_us[dominant], 3)},
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
         "stage_bytes": sbytes,
@@ -217,20 +266,35 @@ def main() -> int:
                          "gbs_per_step": round(per_step_bytes / (dec_ms * 1e-3 / nsteps) / 1e9, 1)}
         del xs, las, Bs, Cs, state
 
+    if args.copy_probe > 0:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe} MiB read + {args.copy_probe} MiB written (torch.neg)")
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     if not args.no_cpu_baseline:
         from oracle import oracle
         cores = len(os.sched_getaffinity(0))
         threads = min(cores, w.batch * w.H)
-        log(f"[bench] cpu baseline: fp64 oracle, full workload, {threads} threads")
+        log(f"[bench] cpu baseline: fp64 oracle over the whole workload, {threads} threads, repeated for "
+            f">= {args.cpu_seconds:.0f} s")
         Xd, lad, Bd, Cd = (d[k].double().numpy() for k in ("X", "log_a", "B", "C"))
-        c0 = time.perf_counter()
-        oracle.scan(Xd, lad, Bd, Cd, threads=threads)
-        c1 = time.perf_counter()
-        out["cpu_baseline"] = {"value": round(tokens / (c1 - c0), 1), "unit": "tokens/s", "cores": threads,
+        runs, c0 = 0, time.perf_counter()
+        while True:
+            oracle.scan(Xd, lad, Bd, Cd, threads=threads)
+            runs += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        secs = time.perf_counter() - c0
+        out["cpu_baseline"] = {"value": round(tokens * runs / secs, 1), "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
-                               "sample": f"whole {w.name} workload ({tokens} tokens x {w.H} heads), one run, "
-                                         f"{c1 - c0:.2f} s; fp64 token-by-token recurrence, OpenMP over "
-                                         f"(row, head) pairs"}
+                               "sample": f"the whole {w.name} workload ({tokens} tokens x {w.H} heads) run "
+                                         f"{runs} times back to back, {secs:.1f} s in all; fp64 token-by-token "
+                                         f"recurrence, OpenMP over (row, head) pairs"}
 
     print(json.dumps(out), flush=True)
     return 0
