@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
     const uint16_t* __restrict__ start, uint16_t* __restrict__ Y, int H, int G, int Q) {
   using K = ScanCfg<P, N>;
-  const long unit = blockIdx.x;
+  const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long m = unit / H;
   const BlockRec blk = load_block(btable, m);
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
                                                              const float* __restrict__ start,
                                                              float* __restrict__ Y, int H, int G, int P,
                                                              int N, int Q) {
-  const long unit = blockIdx.x;
+  const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long slot = unit / H;
   const SlotRec rec = load_slot(table, slot);

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
     const int4* __restrict__ btable, const float* __restrict__ cs, float* __restrict__ bstates,
     float* __restrict__ bdecay, int H, int G, int Q) {
   using K = StateCfg<P, N>;
-  const long unit = blockIdx.x;
+  const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long m = unit / H;
   const BlockRec blk = load_block(btable, m);
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
                                                               float* __restrict__ states,
                                                               float* __restrict__ bdecay, int H, int G,
                                                               int P, int N, int Q) {
-  const long unit = blockIdx.x;
+  const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long slot = unit / H;
   const SlotRec rec = load_slot(table, slot);

@@ -46,6 +46,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// MI355X deals consecutive workgroups of a launch round-robin over its 8 XCDs,
+// each with its own L2. Renumber them so that XCD x runs one contiguous range
+// of units: the heads of one state block, which read the same B and C rows,
+// then share one L2 instead of each XCD fetching every block's B and C. The map
+// is a bijection of [0, n).
+constexpr int kXcds = 8;
+__device__ __forceinline__ long xcd_unit(long bid, long n) {
+  const long q = n / kXcds, r = n % kXcds;
+  const long x = bid % kXcds, local = bid / kXcds;
+  return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
 // Chunk-slot record written by the cumsum stage: sequence (row when unpacked),
 // first token in the row, number of tokens (0: empty slot), chunk index in sequence.
 struct SlotRec {
