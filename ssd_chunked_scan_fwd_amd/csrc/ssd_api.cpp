@@ -43,6 +43,9 @@ ssd_status check_shape(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
     if (ssd::chunk_scan_bf16_lds_bytes(s->headdim, s->dstate, chunk) > ssd::kMaxLdsBytes ||
         ssd::chunk_state_bf16_lds_bytes(s->headdim, s->dstate) > ssd::kMaxLdsBytes)
       return SSD_ERR_UNSUPPORTED;
+    // one chunk's rows of X, Y, B or C are addressed as one buffer range of fewer than 2^31 bytes
+    if ((int64_t)chunk * s->nheads * s->headdim * 2 > kMaxElems || (int64_t)chunk * s->ngroups * s->dstate * 2 > kMaxElems)
+      return SSD_ERR_UNSUPPORTED;
   }
   const int64_t bt = (int64_t)s->batch * s->seqlen;
   if (bt * s->nheads * s->headdim > kMaxElems || bt * s->ngroups * s->dstate > kMaxElems)

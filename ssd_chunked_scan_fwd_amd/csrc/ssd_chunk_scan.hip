@@ -122,20 +122,29 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   const long ldb = (long)G * N, ldx = (long)H * P;
   uint16_t* ys = ysw + wave * 32 * kYPitch;
 
-  // Per-thread constant offsets (bytes) of its staged pieces within a chunk.
+  // Per-thread constant byte offsets of its staged pieces within a chunk (rows
+  // past the chunk's length fall outside the chunk's buffer range and load 0).
   uint32_t boff[K::RB], xoff[K::RX];
   int brow[K::RB], xrow[K::RX];
 #pragma unroll
   for (int u = 0; u < K::RB; ++u) {
     const int idx = tid + kScanThreads * u;
     brow[u] = idx / K::CBN;
-    boff[u] = (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2);
+    boff[u] = idx < kPassRows * K::CBN ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
   }
 #pragma unroll
   for (int u = 0; u < K::RX; ++u) {
     const int idx = tid + kScanThreads * u;
     xrow[u] = idx / K::CBP;
-    xoff[u] = (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2);
+    xoff[u] = idx < kPassRows * K::CBP ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
+  }
+
+  // Byte offset of this lane's C fragment row in each of its query tiles.
+  uint32_t cfoff[ITW];
+#pragma unroll
+  for (int k = 0; k < ITW; ++k) {
+    const int it = scan_tile(k, wave);
+    cfoff[k] = it < nIt ? (uint32_t)(((it * 16 + l16) * ldb + 8 * g4) * 2) : kOffNone;
   }
 
   // State tiles of this wave and the state entering the block.
@@ -144,14 +153,15 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   const int p0t = wp * K::TPW, n0t = wn * K::TNW;
   f32x4 hacc[K::TPW][K::TNW];
   {
-    const uint16_t* st0 = start + (m * H + h) * (long)(P * N);
+    const rsrc_t rs = make_rsrc(start + (m * H + h) * (long)(P * N), (uint32_t)(P * N * 2));
 #pragma unroll
     for (int a = 0; a < K::TPW; ++a)
 #pragma unroll
       for (int b = 0; b < K::TNW; ++b)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          hacc[a][b][r] = sact ? bf16_to_f32(st0[((p0t + a) * 16 + 4 * g4 + r) * N + (n0t + b) * 16 + l16]) : 0.f;
+          hacc[a][b][r] = bf16_to_f32(buf_load_u16(
+              rs, sact ? (uint32_t)((((p0t + a) * 16 + 4 * g4 + r) * N + (n0t + b) * 16 + l16) * 2) : kOffNone));
   }
 
   // Registers holding the next chunk.
@@ -162,47 +172,36 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   float pcs_v[VE], pcs_vm[VE];
   float pcs_x[K::RX];
 
-  auto prefetch = [&](const SlotRec& r, long slot) {
-    const char* Bc = reinterpret_cast<const char*>(B + ((long)r.tok0 * G + g) * N);
-    const char* Xc = reinterpret_cast<const char*>(X + ((long)r.tok0 * H + h) * P);
-    const float* csr = cs + (slot * H + h) * (long)Q;
-    const int len = r.len;
-    const bool full = len >= kPassRows || len == Q;
+  // Loads of one chunk's B, X, C fragments and decay values into registers.
+  // Every load is issued unconditionally (ragged rows and surplus lanes read
+  // zeros through the buffer range); with valid == false nothing is read.
+  auto prefetch = [&](const SlotRec& r, long slot, bool valid) {
+    const int len = valid ? r.len : 0;
+    const rsrc_t rb = make_rsrc(B + ((long)r.tok0 * G + g) * N, (uint32_t)(len * ldb * 2));
+    const rsrc_t rx = make_rsrc(X + ((long)r.tok0 * H + h) * P, (uint32_t)(len * ldx * 2));
+    const rsrc_t rcc = make_rsrc(C + ((long)r.tok0 * G + g) * N, (uint32_t)(len * ldb * 2));
+    const rsrc_t rc = make_rsrc(cs + (slot * H + h) * (long)Q, valid ? (uint32_t)(Q * 4) : 0u);
 #pragma unroll
-    for (int u = 0; u < K::RB; ++u) {
-      const bool in = (tid + kScanThreads * u) < kPassRows * K::CBN;
-      pb[u] = (in && (full ? brow[u] < Q : brow[u] < len)) ? *reinterpret_cast<const u32x4*>(Bc + boff[u])
-                                                            : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(rb, boff[u]);
 #pragma unroll
     for (int u = 0; u < K::RX; ++u) {
-      const bool in = (tid + kScanThreads * u) < kPassRows * K::CBP;
-      px[u] = (in && (full ? xrow[u] < Q : xrow[u] < len)) ? *reinterpret_cast<const u32x4*>(Xc + xoff[u])
-                                                            : u32x4{0u, 0u, 0u, 0u};
-      pcs_x[u] = csr[min(xrow[u], Q - 1)];
+      px[u] = buf_load16(rx, xoff[u]);
+      pcs_x[u] = buf_load_f32(rc, (uint32_t)(min(xrow[u], Q - 1) * 4));
     }
-    const uint16_t* Cc = C + ((long)r.tok0 * G + g) * N + 8 * g4;
 #pragma unroll
-    for (int k = 0; k < ITW; ++k) {
-      const int it = scan_tile(k, wave);
-      const int irow = it * 16 + l16;
+    for (int k = 0; k < ITW; ++k)
 #pragma unroll
-      for (int nb = 0; nb < K::NB; ++nb)
-        pcf[k][nb] = (it < nIt && irow < len) ? *reinterpret_cast<const u32x4*>(Cc + irow * ldb + nb * 32)
-                                              : u32x4{0u, 0u, 0u, 0u};
-    }
-    pcs_last = csr[Q - 1];
-    if (tid < Q) {
-      pcs_t = csr[tid];
-      pcs_tm = csr[tid & ~15];
-    }
-    if (tid < nIt) pcs_e = csr[16 * tid];
+      for (int nb = 0; nb < K::NB; ++nb) pcf[k][nb] = buf_load16(rcc, cfoff[k] + nb * 64);
+    pcs_last = buf_load_f32(rc, (uint32_t)((Q - 1) * 4));
+    pcs_t = buf_load_f32(rc, (uint32_t)(tid * 4));            // zero for tid >= Q
+    pcs_tm = buf_load_f32(rc, (uint32_t)((tid & ~15) * 4));
+    pcs_e = buf_load_f32(rc, (uint32_t)(16 * tid * 4));        // zero for tid >= Q / 16
 #pragma unroll
     for (int u = 0; u < VE; ++u) {
       const int e = tid + kScanThreads * u;
-      if (kVTable && e < nIt * Q) {
-        pcs_v[u] = csr[e % Q];
-        pcs_vm[u] = csr[16 * (e / Q)];
+      if (kVTable) {
+        pcs_v[u] = buf_load_f32(rc, (uint32_t)((e % Q) * 4));
+        pcs_vm[u] = buf_load_f32(rc, (uint32_t)(16 * (e / Q) * 4));  // zero past the table
       }
     }
   };
@@ -211,10 +210,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   __syncthreads();
   auto rec_of = [&](int c) {
     const int4 v = recs[c];
-    return SlotRec{v.x, v.y, v.z, v.w};
+    return SlotRec{uniform(v.x), uniform(v.y), uniform(v.z), uniform(v.w)};
   };
   SlotRec rec = rec_of(0);
-  prefetch(rec, blk.slot0);
+  prefetch(rec, blk.slot0, true);
 
   for (int c = 0; c < blk.nchunks; ++c) {
     const long slot = blk.slot0 + c;
@@ -290,10 +289,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     for (int k = 0; k < ITW; ++k)
 #pragma unroll
       for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = pcf[k][nb];
-    if (c + 1 < blk.nchunks) {
-      rec = rec_of(c + 1);
-      prefetch(rec, slot + 1);
-    }
+    const bool more = c + 1 < blk.nchunks;
+    rec = rec_of(more ? c + 1 : c);
+    prefetch(rec, slot + (more ? 1 : 0), more);
     __syncthreads();
 
     // ---------------- outputs of this chunk: Y_i = u_i (sum_j (S o V)_ij X_j + exp2(m) (C h^T)_i)
@@ -373,9 +371,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[pt][r] *= uu[r];
       key_block(kbd, true);
-      // Out through the wave's staging tile as 16-byte rows.
-      const bool row_ok = it * 16 + l16 < len;
-      uint16_t* yrow = Y + ((tok0 + it * 16 + l16) * H + h) * P;
+      // Out through the wave's staging tile as 16-byte rows (rows past the
+      // chunk's length fall outside the buffer range and are dropped).
+      const rsrc_t ry = make_rsrc(Y + (tok0 * H + h) * P, (uint32_t)(len * ldx * 2));
 #pragma unroll
       for (int pp = 0; pp < (K::TP + 1) / 2; ++pp) {
 #pragma unroll
@@ -387,7 +385,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
           }
         }
         const u32x4 out = frag_k_rows_accpair(ys, kYPitch, 0, 0, lane);  // token l16, p = 32pp + 8g4 ..
-        if (row_ok && pp * 32 + 8 * g4 < P) *reinterpret_cast<u32x4*>(yrow + pp * 32 + 8 * g4) = out;
+        buf_store16(out, ry, pp * 32 + 8 * g4 < P ? (uint32_t)(((it * 16 + l16) * ldx + pp * 32 + 8 * g4) * 2) : kOffNone);
       }
     }
 

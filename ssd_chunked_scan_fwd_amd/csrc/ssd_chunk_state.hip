@@ -78,13 +78,13 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
   for (int u = 0; u < K::RB; ++u) {
     const int idx = tid + kStateThreads * u;
     brow[u] = idx < kPassRows * K::CBN ? idx / K::CBN : kPassRows;
-    boff[u] = (uint32_t)(((brow[u] % kPassRows) * ldb + (idx % K::CBN) * 8) * 2);
+    boff[u] = brow[u] < kPassRows ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
   }
 #pragma unroll
   for (int u = 0; u < K::RX; ++u) {
     const int idx = tid + kStateThreads * u;
     xrow[u] = idx < kPassRows * K::CBP ? idx / K::CBP : kPassRows;
-    xoff[u] = (uint32_t)(((xrow[u] % kPassRows) * ldx + (idx % K::CBP) * 8) * 2);
+    xoff[u] = xrow[u] < kPassRows ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
   }
 
   // The block's chunk records and totals, read once.
@@ -107,27 +107,29 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
   // current one is multiplied.
   u32x4 pb[K::RB], px[K::RX];
   float pcs[K::RX];
-  auto load_pass = [&](const SlotRec& r, long slot, int r0) {
-    const char* Bc = reinterpret_cast<const char*>(B + (((long)r.tok0 + r0) * G + g) * N);
-    const char* Xc = reinterpret_cast<const char*>(X + (((long)r.tok0 + r0) * H + h) * P);
-    const float* csr = cs + (slot * H + h) * (long)Q + r0;
-    const int rows = r.len - r0;
+  // Loads of one pass into registers, issued unconditionally: rows past the
+  // chunk's end and surplus lanes read zeros through the buffer range, and
+  // with valid == false nothing is read.
+  auto load_pass = [&](const SlotRec& r, long slot, int r0, bool valid) {
+    const int rows = valid ? r.len - r0 : 0;
+    const rsrc_t rb = make_rsrc(B + (((long)r.tok0 + r0) * G + g) * N, (uint32_t)(rows * ldb * 2));
+    const rsrc_t rx = make_rsrc(X + (((long)r.tok0 + r0) * H + h) * P, (uint32_t)(rows * ldx * 2));
+    const rsrc_t rc = make_rsrc(cs + (slot * H + h) * (long)Q + r0, valid ? (uint32_t)((Q - r0) * 4) : 0u);
 #pragma unroll
-    for (int u = 0; u < K::RB; ++u)
-      pb[u] = brow[u] < rows ? *reinterpret_cast<const u32x4*>(Bc + boff[u]) : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(rb, boff[u]);
 #pragma unroll
     for (int u = 0; u < K::RX; ++u) {
-      px[u] = xrow[u] < rows ? *reinterpret_cast<const u32x4*>(Xc + xoff[u]) : u32x4{0u, 0u, 0u, 0u};
-      pcs[u] = xrow[u] < rows ? csr[xrow[u]] : 0.f;
+      px[u] = buf_load16(rx, xoff[u]);
+      pcs[u] = buf_load_f32(rc, xrow[u] < kPassRows ? (uint32_t)(xrow[u] * 4) : kOffNone);
     }
   };
 
   auto rec_of = [&](int c) {
     const int4 v = recs[c];
-    return SlotRec{v.x, v.y, v.z, v.w};
+    return SlotRec{uniform(v.x), uniform(v.y), uniform(v.z), uniform(v.w)};
   };
   SlotRec rec = rec_of(0);
-  load_pass(rec, blk.slot0, 0);
+  load_pass(rec, blk.slot0, 0, true);
   float prefix = 0.f;
   for (int c = 0; c < blk.nchunks; ++c) {
     const long slot = blk.slot0 + c;
@@ -153,12 +155,10 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
         }
       }
       // prefetch the next pass: next rows of this chunk, else the next chunk
-      if (r0 + kPassRows < cur.len) {
-        load_pass(cur, slot, r0 + kPassRows);
-      } else if (c + 1 < blk.nchunks) {
-        rec = rec_of(c + 1);
-        load_pass(rec, slot + 1, 0);
-      }
+      const bool in_chunk = r0 + kPassRows < cur.len;
+      const bool more = in_chunk || c + 1 < blk.nchunks;
+      if (!in_chunk) rec = rec_of(more ? c + 1 : c);
+      load_pass(in_chunk ? cur : rec, in_chunk ? slot : slot + (more ? 1 : 0), in_chunk ? r0 + kPassRows : 0, more);
       __syncthreads();
       if (active) {
         const int nkb = (rows + 31) / 32;

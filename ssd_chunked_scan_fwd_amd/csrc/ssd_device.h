@@ -46,6 +46,33 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Buffer resources (raw, unswizzled): loads at byte offsets at or beyond
+// `bytes` return zero and touch no memory, and stores there are dropped. The
+// kernels use them so that ragged rows and surplus lanes need no branch around
+// a load: branches around loads make the compiler wait for every outstanding
+// load where the paths join, which would serialise prefetches. The base must
+// be the same in every lane; `bytes` must be below 2^31 (checked on the host).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;   // dword 3 of a raw buffer descriptor on gfx950
+constexpr uint32_t kOffNone = 0x80000000u;    // an offset no descriptor here covers
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // MI355X deals consecutive workgroups of a launch round-robin over its 8 XCDs,
 // each with its own L2. Renumber them so that XCD x runs one contiguous range
 // of units: the heads of one state block, which read the same B and C rows,
