@@ -425,6 +425,384 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// bf16 path, two heads per workgroup. When the heads of a B/C group come in
+// pairs and the tiles fit, one workgroup takes two heads of the same group
+// over one state block: B and C are staged once for both heads and S^T = B C^T
+// is formed once, so every key block costs 8 MFMAs of S^T and 8 of (S o V) X
+// per head instead of 16 per head. Per chunk the next chunk's loads are issued
+// in three groups spread over the output phase. The next key block's S^T is
+// issued before the current block's decay and hi/lo work, so its MFMAs run
+// under that VALU work. The decay-weighted X of the state update is formed in
+// registers from a per-chunk weight table instead of a second LDS copy.
+// ----------------------------------------------------------------------------
+namespace {
+
+template <int P, int N>
+struct PairCfg {
+  static constexpr int BP = lds_pitch(N);   // B rows
+  static constexpr int XP = lds_pitch(P);   // X rows of each head
+  static constexpr int HP = lds_pitch(P);   // transposed state rows of each head [N][HP] (rows at perm32(n))
+  static constexpr int TP = P / 16, TN = N / 16, NB = N / 32;
+  // State tiles: whole P tiles per wave first, so that each decay-weighted X
+  // fragment of the state update is formed by as few waves as possible.
+  static constexpr int WP = TP < kScanWaves ? TP : kScanWaves;
+  static constexpr int WN = TN < kScanWaves / WP ? TN : kScanWaves / WP;
+  static constexpr int TPW = TP / WP, TNW = TN / WN;
+  static constexpr int CBN = N / 8, CBP = P / 8;
+  static constexpr int RB = (kPassRows * CBN + kScanThreads - 1) / kScanThreads;
+  static constexpr int RX = (kPassRows * CBP + kScanThreads - 1) / kScanThreads;
+};
+
+}  // namespace
+
+static size_t pair_lds_elems(int P, int N, int Q) {
+  return (size_t)Q * lds_pitch(N) + 2 * (size_t)Q * lds_pitch(P) + 2 * (size_t)N * lds_pitch(P) +
+         (size_t)kScanWaves * 32 * kYPitch;
+}
+
+// LDS: the tiles above, 16 chunk records, cs and the state-update weights of
+// both heads ([2][Q] each) and one [2][Q] row of v_j per wave.
+static size_t chunk_scan_pair_lds_bytes(int P, int N, int Q) {
+  return pair_lds_elems(P, N, Q) * 2 + 16 * 16 + (size_t)(4 + 2 * kScanWaves) * Q * 4;
+}
+
+// Head pairs need an even number of heads per group; beyond P = 64 or N = 128
+// the doubled state tiles no longer fit the registers of 8 waves per CU.
+static constexpr bool pair_shape(int P, int N) { return P <= 64 && N <= 128; }
+
+static bool chunk_scan_pair_fits(int P, int N, int Q, int H, int G) {
+  return pair_shape(P, N) && (H / G) % 2 == 0 && Q <= 128 && chunk_scan_pair_lds_bytes(P, N, Q) <= kMaxLdsBytes;
+}
+
+template <int P, int N>
+__global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
+    const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
+    const uint16_t* __restrict__ start, uint16_t* __restrict__ Y, int H, int G, int Q) {
+  using K = PairCfg<P, N>;
+  const int HH = H / 2;
+  const long unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int h0 = 2 * (int)(unit % HH);
+  const long m = unit / HH;
+  const BlockRec blk = load_block(btable, m);
+  if (blk.nchunks <= 0) return;
+  const int g = h0 / (H / G);
+  const int nIt = Q / 16;
+
+  extern __shared__ uint16_t lds[];
+  uint16_t* bs = lds;                                   // [Q][BP]      B rows
+  uint16_t* xs = bs + Q * K::BP;                        // [2][Q][XP]   X rows of both heads
+  uint16_t* hsT = xs + 2 * Q * K::XP;                   // [2][N][HP]   entering states, transposed
+  uint16_t* ysw = hsT + 2 * N * K::HP;                  // [8][32][kYPitch] per-wave output staging
+  int4* recs = reinterpret_cast<int4*>(ysw + kScanWaves * 32 * kYPitch);  // [16] chunk records
+  float* csl = reinterpret_cast<float*>(recs + 16);     // [2][Q] cumulative log2 decay
+  float* wt = csl + 2 * Q;                              // [2][Q] exp2(cs_last - cs_j)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const long ldb = (long)G * N, ldx = (long)H * P;
+  uint16_t* ys = ysw + wave * 32 * kYPitch;
+  float* vt = wt + 2 * Q + wave * 2 * Q;                // [2][Q] v_j of this wave's query tile
+  const int it = scan_tile(0, wave);                    // this wave's query tile
+
+  // Per-thread constant byte offsets of the staged pieces within a chunk.
+  uint32_t boff[K::RB], xoff[K::RX];
+  int brow[K::RB], xrow[K::RX];
+#pragma unroll
+  for (int u = 0; u < K::RB; ++u) {
+    const int idx = tid + kScanThreads * u;
+    brow[u] = idx < kPassRows * K::CBN ? idx / K::CBN : kPassRows;
+    boff[u] = brow[u] < kPassRows ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
+  }
+#pragma unroll
+  for (int u = 0; u < K::RX; ++u) {
+    const int idx = tid + kScanThreads * u;
+    xrow[u] = idx < kPassRows * K::CBP ? idx / K::CBP : kPassRows;
+    xoff[u] = xrow[u] < kPassRows ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
+  }
+  const uint32_t cfoff = it < nIt ? (uint32_t)(((it * 16 + l16) * ldb + 8 * g4) * 2) : kOffNone;
+  const uint32_t csoff = tid < 2 * Q ? (uint32_t)(tid * 4) : kOffNone;
+
+  // State tiles of this wave, both heads, from the state entering the block.
+  const int wn = wave % K::WN, wp = wave / K::WN;
+  const bool sact = wp < K::WP;
+  const int p0t = wp * K::TPW, n0t = wn * K::TNW;
+  f32x4 hacc[2][K::TPW][K::TNW];
+#pragma unroll
+  for (int hd = 0; hd < 2; ++hd) {
+    const rsrc_t rs = make_rsrc(start + (m * H + h0 + hd) * (long)(P * N), (uint32_t)(P * N * 2));
+#pragma unroll
+    for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+      for (int b = 0; b < K::TNW; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hacc[hd][a][b][r] = bf16_to_f32(buf_load_u16(
+              rs, sact ? (uint32_t)((((p0t + a) * 16 + 4 * g4 + r) * N + (n0t + b) * 16 + l16) * 2) : kOffNone));
+  }
+
+  // Registers holding the next chunk, filled in three groups.
+  u32x4 pb[K::RB], px[2][K::RX], pcf[K::NB];
+  float pcs = 0.f, plast[2] = {0.f, 0.f};
+  struct Next {
+    rsrc_t rb, rx0, rx1, rc, rcs;
+  };
+  auto next_rsrc = [&](const SlotRec& r, long slot, bool valid) {
+    const int len = valid ? r.len : 0;
+    Next n;
+    n.rb = make_rsrc(B + ((long)r.tok0 * G + g) * N, (uint32_t)(len * ldb * 2));
+    n.rc = make_rsrc(C + ((long)r.tok0 * G + g) * N, (uint32_t)(len * ldb * 2));
+    n.rx0 = make_rsrc(X + ((long)r.tok0 * H + h0) * P, (uint32_t)(len * ldx * 2));
+    n.rx1 = make_rsrc(X + ((long)r.tok0 * H + h0 + 1) * P, (uint32_t)(len * ldx * 2));
+    n.rcs = make_rsrc(cs + (slot * H + h0) * (long)Q, valid ? (uint32_t)(2 * Q * 4) : 0u);
+    return n;
+  };
+  auto load_b = [&](const Next& n) {
+#pragma unroll
+    for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(n.rb, boff[u]);
+  };
+  auto load_x = [&](const Next& n) {
+#pragma unroll
+    for (int u = 0; u < K::RX; ++u) {
+      px[0][u] = buf_load16(n.rx0, xoff[u]);
+      px[1][u] = buf_load16(n.rx1, xoff[u]);
+    }
+    pcs = buf_load_f32(n.rcs, csoff);
+    plast[0] = buf_load_f32(n.rcs, (uint32_t)((Q - 1) * 4));
+    plast[1] = buf_load_f32(n.rcs, (uint32_t)((2 * Q - 1) * 4));
+  };
+  auto load_c = [&](const Next& n) {
+#pragma unroll
+    for (int nb = 0; nb < K::NB; ++nb) pcf[nb] = buf_load16(n.rc, cfoff + nb * 64);
+  };
+
+  if (tid < blk.nchunks) recs[tid] = ctable[blk.slot0 + tid];
+  __syncthreads();
+  auto rec_of = [&](int c) {
+    const int4 v = recs[c];
+    return SlotRec{uniform(v.x), uniform(v.y), uniform(v.z), uniform(v.w)};
+  };
+  SlotRec rec = rec_of(0);
+  {
+    const Next n0 = next_rsrc(rec, blk.slot0, true);
+    load_b(n0);
+    load_x(n0);
+    load_c(n0);
+  }
+
+  for (int c = 0; c < blk.nchunks; ++c) {
+    const int len = rec.len;
+    const long tok0 = rec.tok0;
+    const float cs_last0 = plast[0], cs_last1 = plast[1];
+
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+#pragma unroll
+    for (int u = 0; u < K::RB; ++u)
+      if (brow[u] < Q)
+        *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + kScanThreads * u) % K::CBN) * 8) = pb[u];
+#pragma unroll
+    for (int u = 0; u < K::RX; ++u)
+      if (xrow[u] < Q) {
+        const int o = xrow[u] * K::XP + ((tid + kScanThreads * u) % K::CBP) * 8;
+        *reinterpret_cast<u32x4*>(xs + o) = px[0][u];
+        *reinterpret_cast<u32x4*>(xs + Q * K::XP + o) = px[1][u];
+      }
+    if (tid < 2 * Q) {
+      csl[tid] = pcs;
+      wt[tid] = fast_exp2((tid < Q ? cs_last0 : cs_last1) - pcs);
+    }
+    if (sact) {
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+          for (int b = 0; b < K::TNW; ++b) {
+            const u32x2 v = {pack_bf16x2(hacc[hd][a][b][0], hacc[hd][a][b][1]),
+                             pack_bf16x2(hacc[hd][a][b][2], hacc[hd][a][b][3])};
+            *reinterpret_cast<u32x2*>(hsT + hd * N * K::HP + perm32((n0t + b) * 16 + l16) * K::HP + (p0t + a) * 16 +
+                                      4 * g4) = v;
+          }
+    }
+    u32x4 cf[K::NB];
+#pragma unroll
+    for (int nb = 0; nb < K::NB; ++nb) cf[nb] = pcf[nb];
+    const bool more = c + 1 < blk.nchunks;
+    const SlotRec nrec = rec_of(more ? c + 1 : c);
+    const Next nx = next_rsrc(nrec, blk.slot0 + c + (more ? 1 : 0), more);
+    __syncthreads();
+
+    // ---------------- outputs: Y_i = u_i (sum_j (S o V)_ij X_j + exp2(m) (C h^T)_i) per head
+    load_b(nx);
+    if (it < nIt && it * 16 < len) {
+      f32x4 acc[2][K::TP];
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) {
+          acc[hd][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int nb = 0; nb < K::NB; ++nb)
+            acc[hd][pt] = mfma16x16x32(cf[nb], frag_k_rows_accpair(hsT + hd * N * K::HP, K::HP, nb * 32, pt * 16, lane),
+                                       acc[hd][pt]);
+        }
+      const float mref[2] = {csl[16 * it], csl[Q + 16 * it]};
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        const float em = fast_exp2(mref[hd]);
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] *= em;
+      }
+      load_x(nx);
+      const int irow = it * 16 + l16;
+      const float csi[2] = {csl[irow], csl[Q + irow]};
+      const int kbd = it >> 1;  // key block holding the diagonal tile
+      // v_j = exp2(m - cs_j) of both heads for the keys before this tile
+      // (private to the wave: written and read by the same wave, in order).
+      if (kbd > 0) {
+        for (int e = lane; e < 2 * Q; e += 64) {
+          const int hd = e >= Q, j = e - hd * Q;
+          vt[e] = j < 16 * it ? fast_exp2(mref[hd] - csl[e]) : 0.f;
+        }
+      }
+
+      // S^T of one key block of 32 tokens (both 16-key halves).
+      auto s_block = [&](int kb, f32x4 sv[2]) {
+        u32x4 bfr[2][K::NB];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int nb = 0; nb < K::NB; ++nb) bfr[half][nb] = frag_k_cols(bs, K::BP, (2 * kb + half) * 16, nb * 32, lane);
+        sv[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sv[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < K::NB; ++nb)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) sv[half] = mfma16x16x32(bfr[half][nb], cf[nb], sv[half]);
+      };
+      // Decay, hi/lo split and Y += M X of one key block for both heads.
+      auto y_block = [&](int kb, const f32x4 sv[2], bool diag) {
+#pragma unroll
+        for (int hd = 0; hd < 2; ++hd) {
+          const float* cl = csl + hd * Q;
+          uint32_t mw[4], ml[4];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int j0 = (2 * kb + half) * 16 + 4 * g4;
+            float v[4];
+            if (diag) {
+              const f32x4 cj = *reinterpret_cast<const f32x4*>(cl + j0);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] = j0 + r <= irow ? sv[half][r] * fast_exp2(csi[hd] - cj[r]) : 0.f;
+            } else {
+              const f32x4 fj = *reinterpret_cast<const f32x4*>(vt + hd * Q + j0);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] = sv[half][r] * fj[r];
+            }
+            mw[2 * half] = pack_bf16x2(v[0], v[1]);
+            mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
+            ml[2 * half] = pack_bf16x2(v[0] - bf16_lo(mw[2 * half]), v[1] - bf16_hi(mw[2 * half]));
+            ml[2 * half + 1] = pack_bf16x2(v[2] - bf16_lo(mw[2 * half + 1]), v[3] - bf16_hi(mw[2 * half + 1]));
+          }
+          const u32x4 ah = u32x4{mw[0], mw[1], mw[2], mw[3]};
+          const u32x4 al = u32x4{ml[0], ml[1], ml[2], ml[3]};
+          u32x4 xf[K::TP];
+#pragma unroll
+          for (int pt = 0; pt < K::TP; ++pt)
+            xf[pt] = frag_k_rows_accpair(xs + hd * Q * K::XP, K::XP, 32 * kb, pt * 16, lane);
+#pragma unroll
+          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(ah, xf[pt], acc[hd][pt]);
+#pragma unroll
+          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(al, xf[pt], acc[hd][pt]);
+        }
+      };
+
+      // Key blocks before the diagonal (at most three for chunks of up to
+      // 128 tokens), unrolled with two S^T register sets: the next block's
+      // S^T is issued before this block's decay and hi/lo work.
+      f32x4 sa[2], sb[2];
+      s_block(0, sa);
+#pragma unroll
+      for (int kb = 0; kb < 3; ++kb) {
+        if (kb < kbd) {
+          s_block(kb + 1, (kb & 1) ? sa : sb);
+          y_block(kb, (kb & 1) ? sb : sa, false);
+        }
+      }
+      load_c(nx);
+      // u_i now: the diagonal key block uses the exact masked decay.
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        const f32x4 ci = *reinterpret_cast<const f32x4*>(csl + hd * Q + it * 16 + 4 * g4);
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[hd][pt][r] *= fast_exp2(ci[r] - mref[hd]);
+      }
+      const f32x4 sd[2] = {(kbd & 1) ? sb[0] : sa[0], (kbd & 1) ? sb[1] : sa[1]};
+      y_block(kbd, sd, true);
+
+      // Out through the wave's staging tile as 16-byte rows (rows past the
+      // chunk's length fall outside the buffer range and are dropped).
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        const rsrc_t ry = make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2));
+#pragma unroll
+        for (int pp = 0; pp < (K::TP + 1) / 2; ++pp) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int pt = 2 * pp + q;
+            if (pt < K::TP) {
+              const u32x2 v = {pack_bf16x2(acc[hd][pt][0], acc[hd][pt][1]), pack_bf16x2(acc[hd][pt][2], acc[hd][pt][3])};
+              *reinterpret_cast<u32x2*>(ys + perm32(q * 16 + l16) * kYPitch + 4 * g4) = v;
+            }
+          }
+          const u32x4 out = frag_k_rows_accpair(ys, kYPitch, 0, 0, lane);  // token l16, p = 32pp + 8g4 ..
+          buf_store16(out, ry,
+                      pp * 32 + 8 * g4 < P ? (uint32_t)(((it * 16 + l16) * ldx + pp * 32 + 8 * g4) * 2) : kOffNone);
+        }
+      }
+    } else {
+      load_x(nx);
+      load_c(nx);
+    }
+
+    // ---------------- state entering the next chunk of the block
+    if (more && sact) {
+      const float d0 = fast_exp2(cs_last0), d1 = fast_exp2(cs_last1);
+#pragma unroll
+      for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+        for (int b = 0; b < K::TNW; ++b) {
+          hacc[0][a][b] *= d0;
+          hacc[1][a][b] *= d1;
+        }
+      const int nkb = (len + 31) / 32;
+      for (int kb = 0; kb < nkb; ++kb) {
+        u32x4 bb[K::TNW];
+#pragma unroll
+        for (int b = 0; b < K::TNW; ++b) bb[b] = frag_k_rows_accpair(bs, K::BP, 32 * kb, (n0t + b) * 16, lane);
+#pragma unroll
+        for (int hd = 0; hd < 2; ++hd) {
+          const f32x4 wlo = *reinterpret_cast<const f32x4*>(wt + hd * Q + 32 * kb + 4 * g4);
+          const f32x4 whi = *reinterpret_cast<const f32x4*>(wt + hd * Q + 32 * kb + 16 + 4 * g4);
+          const float w8[8] = {wlo[0], wlo[1], wlo[2], wlo[3], whi[0], whi[1], whi[2], whi[3]};
+#pragma unroll
+          for (int a = 0; a < K::TPW; ++a) {
+            const u32x4 xa =
+                scale_frag(frag_k_rows_accpair(xs + hd * Q * K::XP, K::XP, 32 * kb, (p0t + a) * 16, lane), w8);
+#pragma unroll
+            for (int b = 0; b < K::TNW; ++b) hacc[hd][a][b] = mfma16x16x32(xa, bb[b], hacc[hd][a][b]);
+          }
+        }
+      }
+    }
+    rec = nrec;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // fp32 path (plain FMA, fp32 accumulation; one chunk per state block). Query
 // rows in blocks of 32; for
 // each key block j0 <= i0 the masked, decayed block of C B^T is formed in LDS
@@ -529,6 +907,23 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
 template <int P, int N>
 static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                                    const Workspace& ws, hipStream_t stream) {
+  if constexpr (pair_shape(P, N)) {
+    if (chunk_scan_pair_fits(P, N, d.Q, d.H, d.G)) {
+      const size_t lds = chunk_scan_pair_lds_bytes(P, N, d.Q);
+      auto kern = chunk_scan_pair_kernel<P, N>;
+      if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(kScanThreads), lds, stream,
+                         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
+                         reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs,
+                         reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y), d.H,
+                         d.G, d.Q);
+      return hipGetLastError();
+    }
+  }
   const size_t lds = chunk_scan_bf16_lds_bytes(P, N, d.Q);
   auto kern = d.Q > 128 ? chunk_scan_bf16_kernel<P, N, 2> : chunk_scan_bf16_kernel<P, N, 1>;
   if (lds > 64 * 1024) {
