@@ -660,12 +660,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       const int kbd = it >> 1;  // key block holding the diagonal tile
       // v_j = exp2(m - cs_j) of both heads for the keys before this tile
       // (private to the wave: written and read by the same wave, in order).
-      if (kbd > 0) {
-        for (int e = lane; e < 2 * Q; e += 64) {
-          const int hd = e >= Q, j = e - hd * Q;
-          vt[e] = j < 16 * it ? fast_exp2(mref[hd] - csl[e]) : 0.f;
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int q = 0; q < kPassRows / 64; ++q) {
+          const int j = lane + 64 * q;
+          if (j < 16 * it) vt[hd * Q + j] = fast_exp2(mref[hd] - csl[hd * Q + j]);
         }
-      }
 
       // S^T of one key block of 32 tokens (both 16-key halves).
       auto s_block = [&](int kb, f32x4 sv[2]) {
@@ -779,7 +780,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
           hacc[1][a][b] *= d1;
         }
       const int nkb = (len + 31) / 32;
-      for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+      for (int kb = 0; kb < kPassRows / 32; ++kb) {
+        if (kb >= nkb) break;
         u32x4 bb[K::TNW];
 #pragma unroll
         for (int b = 0; b < K::TNW; ++b) bb[b] = frag_k_rows_accpair(bs, K::BP, 32 * kb, (n0t + b) * 16, lane);
