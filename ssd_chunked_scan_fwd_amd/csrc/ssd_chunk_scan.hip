@@ -504,7 +504,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
   const long ldb = (long)G * N, ldx = (long)H * P;
   uint16_t* ys = ysw + wave * 32 * kYPitch;
   float* vt = wt + 2 * Q + wave * 2 * Q;                // [2][Q] v_j of this wave's query tile
-  const int it = scan_tile(0, wave);                    // this wave's query tile
+  // This wave's query tile: waves 0-3 (the first wave of each SIMD) take the
+  // long rows of the triangle, 7 - w, and waves 4-7 the short rows w - 4, so
+  // each SIMD pairs a long and a short row.
+  const int it = wave < 4 ? 7 - wave : wave - 4;
 
   // Per-thread constant byte offsets of the staged pieces within a chunk.
   uint32_t boff[K::RB], xoff[K::RX];
