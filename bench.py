@@ -109,9 +109,9 @@ def useful_flops(w, chunk_lengths) -> float:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200, help="untimed steps; the GPU clock settles under load")
+    ap.add_argument("--stage-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
@@ -178,24 +178,26 @@ def main() -> int:
     tokens = w.batch * w.T
     value = tokens / (ms_per_step * 1e-3)
 
-    # per-stage average launch time, HIP events on the launch stream
-    log(f"[bench] per-stage timing, {args.stage_reps} reps")
+    # per-stage average launch time: HIP events on the launch stream around
+    # stage_reps back-to-back launches of the stage's own entry point
+    log(f"[bench] per-stage timing, {args.stage_reps} launches each")
     stages = [
         ("chunk_cumsum", lambda: ssd.chunk_cumsum(la, None, shape, ws)),
         ("chunk_state", lambda: ssd.chunk_state(X, B, None, shape, ws)),
         ("state_passing", lambda: ssd.state_passing(None, fin, shape, ws)),
         ("chunk_scan", lambda: ssd.chunk_scan(X, B, C, None, Y, shape, ws)),
     ]
-    acc = {name: 0.0 for name, _ in stages}
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in stages]
-    for _ in range(args.stage_reps):
-        for (name, fn), (a, b) in zip(stages, evs):
-            a.record(stream)
+    acc = {}
+    for name, fn in stages:
+        for _ in range(min(20, args.stage_reps)):
             fn()
-            b.record(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.stage_reps):
+            fn()
+        b.record(stream)
         torch.cuda.synchronize()
-        for (name, _), (a, b) in zip(stages, evs):
-            acc[name] += a.elapsed_time(b)
+        acc[name] = a.elapsed_time(b)
     stage_us = {k: v * 1e3 / max(args.stage_reps, 1) for k, v in acc.items()}
     sbytes = stage_bytes(w, ws.layout.nslots, ws.layout.nblocks, w.batch)
     dominant = max(stage_us, key=stage_us.get)
