@@ -76,6 +76,9 @@ def test_workload_full_size(name):
 
 # ------------------------------------------------------------------ shapes and edge cases
 
+# The two-head chunk_scan kernel runs when the heads of a group come in pairs,
+# P <= 64, N <= 128 and Q <= 128; the single-head kernel covers the rest
+# (odd heads per group, P = 128, N = 256, Q = 256). The cases below exercise both.
 CASES = [
     # (batch, T, H, P, N, G, dtype, Q)
     (1, 200, 3, 64, 64, 1, torch.bfloat16, 64),     # ragged tail
@@ -98,6 +101,24 @@ def test_shapes(case):
     b, T, H, P, N, G, dt, Q = case
     d = synth.make_forward_inputs(b, T, H, P, N, G, dtype=dt, seed=1000 + T + N)
     check_fwd(d, Q, f"shape {case}")
+
+
+@pytest.mark.parametrize("P,N,Q,gs", [(64, 128, 128, 4), (32, 64, 64, 2), (16, 32, 32, 1)])
+def test_head_pairs_match_single_heads(P, N, Q, gs):
+    """A head pair through the two-head kernel (two heads, one group) against the
+    same heads run one at a time (one head per group, which takes the single-head
+    kernel): both within the oracle tolerance, and close to each other."""
+    d = synth.make_forward_inputs(1, 3 * Q + 17, 2, P, N, 1, dtype=torch.bfloat16, seed=4242 + P + N)
+    say(f"[parity] head pairs vs single heads P={P} N={N} Q={Q} gs={gs}")
+    Y2, f2 = check_fwd(d, Q, "head pair", gs)
+    for h in range(2):
+        dh = dict(d)
+        dh["X"] = d["X"][:, :, h:h + 1].contiguous()
+        dh["log_a"] = d["log_a"][:, :, h:h + 1].contiguous()
+        Y1, f1 = check_fwd(dh, Q, f"single head {h}", gs)
+        e = assert_close(to_f64(Y2[:, :, h:h + 1]), to_f64(Y1), "bf16", f"pair vs single head {h} Y")
+        assert e["rel_l2"] < 5e-3, e
+        assert_close(to_f64(f2[:, h:h + 1]), to_f64(f1), "bf16", f"pair vs single head {h} final")
 
 
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
