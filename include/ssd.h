@@ -151,11 +151,21 @@ ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void*
                    const ssd_shape* shape, void* workspace, size_t workspace_bytes,
                    void* stream);
 
-/* Forward pass with an explicit state block (state_block <= 0: the default). */
+/*
+ * Forward pass with an initial state and an explicit state block
+ * (state_block <= 0: the default).
+ *   initial_state  device, fp32 [batch or num_seqs, nheads, headdim, dstate]
+ *                  (the layout of final_state), or NULL for zero states:
+ *                  the state each row (packed: each sequence) starts from, h_0
+ *                  with h_1 = a_1 h_0 + B_1 x_1^T. A prompt can then be run in
+ *                  pieces, each piece starting from the previous piece's
+ *                  final_state, and handed on to ssd_step.
+ * The other arguments are those of ssd_fwd.
+ */
 ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const void* C,
-                      const int32_t* cu_seqlens, int32_t chunk, int32_t state_block, void* Y,
-                      float* final_state, const ssd_shape* shape, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      const int32_t* cu_seqlens, const float* initial_state, int32_t chunk,
+                      int32_t state_block, void* Y, float* final_state, const ssd_shape* shape,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The four stages of ssd_fwd_ex, callable one by one (same arguments, same
@@ -170,10 +180,11 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
  *   end of block m) x_j B_j^T per state block and head, batched matrix
  *   products over tokens (paper section 6, "Right Factors"). Writes
  *   block_states and block_decay.
- * ssd_state_passing -- centre factors: h = 0; for each state block m of a
- *   sequence, start_m = h, h = exp(A_m) h + s_m with A_m the block's total log
- *   decay (paper section 6, "Center Factors"); writes start_states and, when
- *   final_state is not NULL, the state after each sequence.
+ * ssd_state_passing -- centre factors: h = initial state (NULL: 0); for each
+ *   state block m of a sequence, start_m = h, h = exp(A_m) h + s_m with A_m the
+ *   block's total log decay (paper section 6, "Center Factors"); writes
+ *   start_states and, when final_state is not NULL, the state after each
+ *   sequence.
  * ssd_chunk_scan -- diagonal blocks plus left factors: Y = (L o C B^T) X within
  *   each chunk plus exp(cs) C h^T for the state h entering the chunk (paper
  *   section 6, "Diagonal Blocks" and "Left Factors"); inside a state block the
@@ -185,9 +196,9 @@ ssd_status ssd_chunk_cumsum(const float* log_a, const int32_t* cu_seqlens, int32
 ssd_status ssd_chunk_state(const void* X, const void* B, const int32_t* cu_seqlens, int32_t chunk,
                            int32_t state_block, const ssd_shape* shape, void* workspace,
                            size_t workspace_bytes, void* stream);
-ssd_status ssd_state_passing(const int32_t* cu_seqlens, int32_t chunk, int32_t state_block,
-                             float* final_state, const ssd_shape* shape, void* workspace,
-                             size_t workspace_bytes, void* stream);
+ssd_status ssd_state_passing(const int32_t* cu_seqlens, const float* initial_state, int32_t chunk,
+                             int32_t state_block, float* final_state, const ssd_shape* shape,
+                             void* workspace, size_t workspace_bytes, void* stream);
 ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int32_t* cu_seqlens,
                           int32_t chunk, int32_t state_block, void* Y, const ssd_shape* shape,
                           void* workspace, size_t workspace_bytes, void* stream);

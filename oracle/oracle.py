@@ -175,15 +175,15 @@ def scan(X, la, B, C, segments: Optional[Iterable] = None, init=None, want_y: bo
     return Y, fin, snaps
 
 
-def forward(X, la, B, C, cu_seqlens=None, threads: int = 0, mutant: int = 0):
-    """Y and final states of the layer from zero initial states.
+def forward(X, la, B, C, cu_seqlens=None, threads: int = 0, mutant: int = 0, init=None):
+    """Y and final states of the layer, from zero initial states or ``init``.
 
-    final is [rows,H,P,N] without cu_seqlens and [S,H,P,N] with it.
+    final (and init) is [rows,H,P,N] without cu_seqlens and [S,H,P,N] with it.
     """
     X = _f64(X)
     rows, T = X.shape[0], X.shape[1]
     segs = sequence_segments(rows, T, cu_seqlens)
-    Y, fin, _ = scan(X, la, B, C, segments=segs, threads=threads, mutant=mutant)
+    Y, fin, _ = scan(X, la, B, C, segments=segs, init=init, threads=threads, mutant=mutant)
     return Y, fin
 
 

@@ -74,13 +74,13 @@ def lib():
         L.ssd_fwd.restype = ctypes.c_int
         L.ssd_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, shp, vp, sz, vp]
         L.ssd_fwd_ex.restype = ctypes.c_int
-        L.ssd_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, shp, vp, sz, vp]
+        L.ssd_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, shp, vp, sz, vp]
         L.ssd_chunk_cumsum.restype = ctypes.c_int
         L.ssd_chunk_cumsum.argtypes = [vp, vp, i32, i32, shp, vp, sz, vp]
         L.ssd_chunk_state.restype = ctypes.c_int
         L.ssd_chunk_state.argtypes = [vp, vp, vp, i32, i32, shp, vp, sz, vp]
         L.ssd_state_passing.restype = ctypes.c_int
-        L.ssd_state_passing.argtypes = [vp, i32, i32, vp, shp, vp, sz, vp]
+        L.ssd_state_passing.argtypes = [vp, vp, i32, i32, vp, shp, vp, sz, vp]
         L.ssd_chunk_scan.restype = ctypes.c_int
         L.ssd_chunk_scan.argtypes = [vp, vp, vp, vp, i32, i32, vp, shp, vp, sz, vp]
         L.ssd_step.restype = ctypes.c_int
@@ -194,16 +194,29 @@ def _check_inputs(X, log_a, B, C, cu_seqlens):
         raise ValueError("X, B and C must share one dtype")
 
 
+def _check_state(t: Optional[torch.Tensor], shape: Shape, name: str):
+    if t is None:
+        return
+    nseq = shape.num_seqs if shape.num_seqs > 0 else shape.batch
+    want = (nseq, shape.nheads, shape.headdim, shape.dstate)
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != want:
+        raise ValueError(f"{name} must be a contiguous fp32 device tensor of shape {want}")
+
+
 def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         cu_seqlens: Optional[torch.Tensor] = None, chunk: int = 128, state_block: int = 0,
         Y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None, want_final: bool = True,
-        workspace: Optional[Workspace] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        workspace: Optional[Workspace] = None,
+        initial_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked SSD forward pass (ssd_fwd_ex). Returns (Y, final_state or None).
 
     state_block <= 0 uses the library's default (the workspace's, when one is given).
+    initial_state: fp32 [rows or sequences, H, P, N] the state each row (each
+    packed sequence) starts from; None for zero states.
     """
     _check_inputs(X, log_a, B, C, cu_seqlens)
     shape = make_shape(X, B, cu_seqlens)
+    _check_state(initial_state, shape, "initial_state")
     if Y is None:
         Y = torch.empty_like(X)
     if final_state is None and want_final:
@@ -213,7 +226,8 @@ def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
         workspace = Workspace(shape, chunk, X.device, state_block)
     elif state_block > 0 and state_block != workspace.state_block:
         raise ValueError("state_block differs from the workspace's")
-    _call("ssd_fwd_ex", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), int(chunk), workspace.state_block,
+    _call("ssd_fwd_ex", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), _ptr(initial_state), int(chunk),
+          workspace.state_block,
           _ptr(Y), _ptr(final_state), ctypes.byref(shape), _ptr(workspace.buffer), workspace.nbytes,
           _stream(X.device))
     return Y, final_state
@@ -229,9 +243,10 @@ def chunk_state(X, B, cu_seqlens, shape: Shape, ws: Workspace):
           _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
 
 
-def state_passing(cu_seqlens, final_state, shape: Shape, ws: Workspace):
-    _call("ssd_state_passing", _ptr(cu_seqlens), ws.chunk, ws.state_block, _ptr(final_state), ctypes.byref(shape),
-          _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
+def state_passing(cu_seqlens, final_state, shape: Shape, ws: Workspace, initial_state=None):
+    _check_state(initial_state, shape, "initial_state")
+    _call("ssd_state_passing", _ptr(cu_seqlens), _ptr(initial_state), ws.chunk, ws.state_block, _ptr(final_state),
+          ctypes.byref(shape), _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
 
 
 def chunk_scan(X, B, C, cu_seqlens, Y, shape: Shape, ws: Workspace):

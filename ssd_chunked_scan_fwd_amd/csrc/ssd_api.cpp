@@ -207,13 +207,15 @@ ssd_status ssd_chunk_state(const void* X, const void* B, const int32_t* cu_seqle
   return hip_status(ssd::launch_chunk_state(pp.d, X, B, pp.ws, (hipStream_t)stream));
 }
 
-ssd_status ssd_state_passing(const int32_t* cu_seqlens, int32_t chunk, int32_t state_block, float* final_state,
-                             const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+ssd_status ssd_state_passing(const int32_t* cu_seqlens, const float* initial_state, int32_t chunk,
+                             int32_t state_block, float* final_state, const ssd_shape* shape, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   Prepared pp;
   ssd_status st = prepare(kPassing, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, chunk, state_block,
                           shape, workspace, workspace_bytes, &pp);
   if (st != SSD_OK) return st;
-  return hip_status(ssd::launch_state_passing(pp.d, cu_seqlens, final_state, pp.ws, (hipStream_t)stream));
+  return hip_status(
+      ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, (hipStream_t)stream));
 }
 
 ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int32_t* cu_seqlens, int32_t chunk,
@@ -227,8 +229,8 @@ ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int
 }
 
 ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
-                      int32_t chunk, int32_t state_block, void* Y, float* final_state, const ssd_shape* shape,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      const float* initial_state, int32_t chunk, int32_t state_block, void* Y, float* final_state,
+                      const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
   Prepared pp;
   ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
                           workspace_bytes, &pp);
@@ -236,7 +238,7 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = ssd::launch_chunk_cumsum(pp.d, log_a, cu_seqlens, pp.ws, s);
   if (e == hipSuccess) e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s);
-  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, final_state, pp.ws, s);
+  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, s);
   if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s);
   return hip_status(e);
 }
@@ -244,8 +246,8 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
 ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
                    int32_t chunk, void* Y, float* final_state, const ssd_shape* shape, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  return ssd_fwd_ex(X, log_a, B, C, cu_seqlens, chunk, 0, Y, final_state, shape, workspace, workspace_bytes,
-                    stream);
+  return ssd_fwd_ex(X, log_a, B, C, cu_seqlens, nullptr, chunk, 0, Y, final_state, shape, workspace,
+                    workspace_bytes, stream);
 }
 
 ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C, void* y,

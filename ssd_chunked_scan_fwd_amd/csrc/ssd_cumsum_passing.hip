@@ -137,8 +137,8 @@ hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32
 }
 
 // ----------------------------------------------------------------------------
-// state_passing: h = 0; for each state block m of a sequence: start_m = h;
-// h = exp2(total_m) h + s_m. One thread owns 2 consecutive (p, n) elements of
+// state_passing: h = h0 (the sequence's initial state, or 0); for each state
+// block m of a sequence: start_m = h; h = exp2(total_m) h + s_m. One thread owns 2 consecutive (p, n) elements of
 // one (sequence, head); the block loop is unrolled so that the loads of
 // sixteen blocks are in flight together. Sequence s: packed rows own block slots
 // floor(cu[s]/(Gs*Q)) + s ..; unpacked row s owns s*blocks_per_row ...
@@ -148,6 +148,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
                                                             const float* __restrict__ bdecay,
                                                             void* __restrict__ start,
                                                             float* __restrict__ final_state,
+                                                            const float* __restrict__ init,
                                                             const int32_t* __restrict__ cu,
                                                             long blocks_per_row, int H, int PN, int span) {
   const int eblocks = (PN / 2 + 255) / 256;
@@ -168,6 +169,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
   if (e >= PN) return;
 
   f32x2 hc = {0.f, 0.f};
+  if (init) hc = *reinterpret_cast<const f32x2*>(init + ((long)s * H + h) * PN + e);
   auto put = [&](long blk, f32x2 v) {
     const long off = (blk * H + h) * (long)PN + e;
     if (OUT_BF16) {
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
   if (final_state) *reinterpret_cast<f32x2*>(final_state + ((long)s * H + h) * PN + e) = hc;
 }
 
-hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, float* final_state,
+hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float* init, float* final_state,
                                 const Workspace& ws, hipStream_t stream) {
   const int PN = d.P * d.N;
   const int nseq = cu ? d.num_seqs : d.batch;
@@ -213,10 +215,10 @@ hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, float* fina
   const int span = d.state_block * d.Q;
   if (d.bf16) {
     hipLaunchKernelGGL(state_passing_kernel<true>, grid, dim3(256), 0, stream, ws.bstates, ws.bdecay,
-                       ws.start_states, final_state, cu, d.blocks_per_row, d.H, PN, span);
+                       ws.start_states, final_state, init, cu, d.blocks_per_row, d.H, PN, span);
   } else {
     hipLaunchKernelGGL(state_passing_kernel<false>, grid, dim3(256), 0, stream, ws.bstates, ws.bdecay,
-                       ws.start_states, final_state, cu, d.blocks_per_row, d.H, PN, span);
+                       ws.start_states, final_state, init, cu, d.blocks_per_row, d.H, PN, span);
   }
   return hipGetLastError();
 }

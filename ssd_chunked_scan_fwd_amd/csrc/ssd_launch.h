@@ -34,7 +34,7 @@ hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32
                                const Workspace& ws, hipStream_t stream);
 hipError_t launch_chunk_state(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
                               hipStream_t stream);
-hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, float* final_state,
+hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float* init, float* final_state,
                                 const Workspace& ws, hipStream_t stream);
 hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                              const Workspace& ws, hipStream_t stream);

@@ -132,7 +132,7 @@ def test_fwd_rejects_bad_shapes(kw, chunk, code):
     L = ssd.lib()
     st = L.ssd_fwd(FAKE, FAKE, FAKE, FAKE, None, chunk, FAKE, FAKE, ctypes.byref(sh), FAKE, 1 << 40, None)
     assert st == code
-    st = L.ssd_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, chunk, 1, FAKE, FAKE, ctypes.byref(sh), FAKE, 1 << 40, None)
+    st = L.ssd_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, None, chunk, 1, FAKE, FAKE, ctypes.byref(sh), FAKE, 1 << 40, None)
     assert st == code
 
 
@@ -171,7 +171,7 @@ def test_stage_entry_points_validate():
     assert L.ssd_chunk_state(None, FAKE, None, 128, 2, ctypes.byref(sh), FAKE, need, None) == INVALID
     assert L.ssd_chunk_state(FAKE, FAKE, None, 128, 2, ctypes.byref(sh), FAKE, need - 256, None) == WS_SMALL
     assert L.ssd_chunk_state(FAKE, FAKE, None, 128, 1, ctypes.byref(sh), FAKE, need, None) == WS_SMALL
-    assert L.ssd_state_passing(None, 128, 2, None, ctypes.byref(sh), None, need, None) == INVALID
+    assert L.ssd_state_passing(None, None, 128, 2, None, ctypes.byref(sh), None, need, None) == INVALID
     assert L.ssd_chunk_scan(FAKE, FAKE, None, None, 128, 2, FAKE, ctypes.byref(sh), FAKE, need, None) == INVALID
     assert L.ssd_chunk_scan(FAKE, FAKE, FAKE, None, 128, 2, None, ctypes.byref(sh), FAKE, need, None) == INVALID
     assert L.ssd_chunk_scan(FAKE, FAKE, FAKE, None, 128, 5, FAKE, ctypes.byref(sh), FAKE, need, None) == UNSUPPORTED

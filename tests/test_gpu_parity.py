@@ -331,6 +331,60 @@ def test_step_sequence(dt, N):
     assert_close(to_f64(state), fr, dts, "step state")
 
 
+# ------------------------------------------------------------------ initial states
+
+def _init_states(n, H, P, N, seed, T0=200):
+    """Initial states at the scale the layer itself produces: the oracle's final
+    states after a seeded prefix of T0 tokens (the chunked-prefill use)."""
+    d = synth.make_forward_inputs(n, T0, H, P, N, 1, dtype=torch.float32, seed=seed)
+    _, fin = oracle.forward(to_f64(d["X"]), to_f64(d["log_a"]), to_f64(d["B"]), to_f64(d["C"]))
+    return torch.from_numpy(fin).float()
+
+
+@pytest.mark.parametrize("dt,Q,gs", [(torch.bfloat16, 64, 2), (torch.bfloat16, 128, 1), (torch.float32, 32, 1)])
+def test_initial_state(dt, Q, gs):
+    """ssd_fwd_ex from a given initial state per row against the oracle run from it."""
+    b, T, H, P, N = 2, 300, 4, 64, 64
+    d = synth.make_forward_inputs(b, T, H, P, N, 1, dtype=dt, seed=70 + Q)
+    h0 = _init_states(b, H, P, N, 71)
+    say(f"[parity] initial state {dt} Q={Q} gs={gs}")
+    Y, fin = gpu_fwd(d, Q, gs, initial_state=h0.cuda())
+    Yr, fr = oracle.forward(to_f64(d["X"]), to_f64(d["log_a"]), to_f64(d["B"]), to_f64(d["C"]), init=h0.double().numpy())
+    assert_close(to_f64(Y), Yr, dtype_name(d["X"]), "initial state Y")
+    assert_close(to_f64(fin), fr, dtype_name(d["X"]), "initial state final")
+
+
+def test_initial_state_packed():
+    """Packed sequences, each from its own initial state."""
+    d = synth.make_forward_inputs(1, 1500, 4, 64, 128, 1, dtype=torch.bfloat16, seed=72, varlen=(100, 700))
+    S = d["cu_seqlens"].numel() - 1
+    h0 = _init_states(S, 4, 64, 128, 73)
+    say(f"[parity] initial state packed S={S}")
+    Y, fin = gpu_fwd(d, 128, 2, initial_state=h0.cuda())
+    Yr, fr = oracle.forward(to_f64(d["X"]), to_f64(d["log_a"]), to_f64(d["B"]), to_f64(d["C"]),
+                            cu_seqlens=d["cu_seqlens"].numpy(), init=h0.double().numpy())
+    assert_close(to_f64(Y), Yr, "bf16", "packed initial state Y")
+    assert_close(to_f64(fin), fr, "bf16", "packed initial state final")
+
+
+def test_prefill_in_pieces():
+    """A prompt run in three pieces, each from the previous piece's final state,
+    equals the oracle over the whole prompt."""
+    b, T, H, P, N = 2, 1000, 4, 64, 128
+    cuts = [0, 333, 700, T]
+    d = synth.make_forward_inputs(b, T, H, P, N, 1, dtype=torch.bfloat16, seed=74)
+    dd = to_dev(d)
+    state, ys = None, []
+    for a, e in zip(cuts[:-1], cuts[1:]):
+        Y, state = ssd.fwd(*(dd[k][:, a:e].contiguous() for k in ("X", "log_a", "B", "C")), chunk=128,
+                           initial_state=state)
+        ys.append(Y)
+    torch.cuda.synchronize()
+    Yr, fr = oracle_fwd(d)
+    assert_close(to_f64(torch.cat(ys, 1)), Yr, "bf16", "pieces Y")
+    assert_close(to_f64(state), fr, "bf16", "pieces final")
+
+
 def test_prefill_then_decode_handoff():
     """ssd_fwd over [0, T1) then ssd_step over [T1, T) equals the oracle over [0, T)."""
     b, T, T1, H, P, N = 2, 300, 237, 4, 64, 128
