@@ -456,8 +456,7 @@ struct PairCfg {
 }  // namespace
 
 static size_t pair_lds_elems(int P, int N, int Q) {
-  return (size_t)Q * lds_pitch(N) + 2 * (size_t)Q * lds_pitch(P) + 2 * (size_t)N * lds_pitch(P) +
-         (size_t)kScanWaves * 32 * kYPitch;
+  return (size_t)Q * lds_pitch(N) + 2 * (size_t)Q * lds_pitch(P) + 2 * (size_t)N * lds_pitch(P);
 }
 
 // LDS: the tiles above, 16 chunk records, cs and the state-update weights of
@@ -493,8 +492,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
   uint16_t* bs = lds;                                   // [Q][BP]      B rows
   uint16_t* xs = bs + Q * K::BP;                        // [2][Q][XP]   X rows of both heads
   uint16_t* hsT = xs + 2 * Q * K::XP;                   // [2][N][HP]   entering states, transposed
-  uint16_t* ysw = hsT + 2 * N * K::HP;                  // [8][32][kYPitch] per-wave output staging
-  int4* recs = reinterpret_cast<int4*>(ysw + kScanWaves * 32 * kYPitch);  // [16] chunk records
+  int4* recs = reinterpret_cast<int4*>(hsT + 2 * N * K::HP);  // [16] chunk records
   float* csl = reinterpret_cast<float*>(recs + 16);     // [2][Q] cumulative log2 decay
   float* wt = csl + 2 * Q;                              // [2][Q] exp2(cs_last - cs_j)
 
@@ -502,7 +500,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const long ldb = (long)G * N, ldx = (long)H * P;
-  uint16_t* ys = ysw + wave * 32 * kYPitch;
   float* vt = wt + 2 * Q + wave * 2 * Q;                // [2][Q] v_j of this wave's query tile
   // This wave's query tile: waves 0-3 (the first wave of each SIMD) take the
   // long rows of the triangle, 7 - w, and waves 4-7 the short rows w - 4, so
@@ -647,7 +644,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
           acc[hd][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int nb = 0; nb < K::NB; ++nb)
-            acc[hd][pt] = mfma16x16x32(cf[nb], frag_k_rows_accpair(hsT + hd * N * K::HP, K::HP, nb * 32, pt * 16, lane),
+            acc[hd][pt] = mfma16x16x32(frag_k_rows_accpair(hsT + hd * N * K::HP, K::HP, nb * 32, pt * 16, lane), cf[nb],
                                        acc[hd][pt]);
         }
       const float mref[2] = {csl[16 * it], csl[Q + 16 * it]};
@@ -716,9 +713,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
           for (int pt = 0; pt < K::TP; ++pt)
             xf[pt] = frag_k_rows_accpair(xs + hd * Q * K::XP, K::XP, 32 * kb, pt * 16, lane);
 #pragma unroll
-          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(ah, xf[pt], acc[hd][pt]);
+          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(xf[pt], ah, acc[hd][pt]);
 #pragma unroll
-          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(al, xf[pt], acc[hd][pt]);
+          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(xf[pt], al, acc[hd][pt]);
         }
       };
 
@@ -738,33 +735,38 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       // u_i now: the diagonal key block uses the exact masked decay.
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd) {
-        const f32x4 ci = *reinterpret_cast<const f32x4*>(csl + hd * Q + it * 16 + 4 * g4);
+        const float u = fast_exp2(csi[hd] - mref[hd]);   // this lane's query row
 #pragma unroll
-        for (int pt = 0; pt < K::TP; ++pt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[hd][pt][r] *= fast_exp2(ci[r] - mref[hd]);
+        for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] *= u;
       }
       const f32x4 sd[2] = {(kbd & 1) ? sb[0] : sa[0], (kbd & 1) ? sb[1] : sa[1]};
       y_block(kbd, sd, true);
 
-      // Out through the wave's staging tile as 16-byte rows (rows past the
-      // chunk's length fall outside the buffer range and are dropped).
+      // Out: the accumulators hold Y^T tiles (lane: query row l16, 4
+      // consecutive p of P tile pt in lane group g4). For a pair of P tiles,
+      // v_permlane16_swap exchanges the halves of lane groups so that each
+      // lane holds 8 consecutive p of its token: group g4 gets
+      // p = 32q + 16 (g4 & 1) + 8 (g4 >> 1) .. + 7, stored as one 16-byte
+      // piece (rows past the chunk's length fall outside the buffer range and
+      // are dropped).
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd) {
         const rsrc_t ry = make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2));
+        const uint32_t row = (uint32_t)((it * 16 + l16) * ldx);
 #pragma unroll
-        for (int pp = 0; pp < (K::TP + 1) / 2; ++pp) {
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int pt = 2 * pp + q;
-            if (pt < K::TP) {
-              const u32x2 v = {pack_bf16x2(acc[hd][pt][0], acc[hd][pt][1]), pack_bf16x2(acc[hd][pt][2], acc[hd][pt][3])};
-              *reinterpret_cast<u32x2*>(ys + perm32(q * 16 + l16) * kYPitch + 4 * g4) = v;
-            }
-          }
-          const u32x4 out = frag_k_rows_accpair(ys, kYPitch, 0, 0, lane);  // token l16, p = 32pp + 8g4 ..
-          buf_store16(out, ry,
-                      pp * 32 + 8 * g4 < P ? (uint32_t)(((it * 16 + l16) * ldx + pp * 32 + 8 * g4) * 2) : kOffNone);
+        for (int q = 0; q < K::TP / 2; ++q) {
+          const f32x4 lo = acc[hd][2 * q], hi = acc[hd][2 * q + 1];
+          const auto sx = __builtin_amdgcn_permlane16_swap(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(hi[0], hi[1]),
+                                                           false, false);
+          const auto sy = __builtin_amdgcn_permlane16_swap(pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[2], hi[3]),
+                                                           false, false);
+          const u32x4 v = {sx[0], sy[0], sx[1], sy[1]};
+          buf_store16(v, ry, (row + 32 * q + 16 * (g4 & 1) + 8 * (g4 >> 1)) * 2);
+        }
+        if (K::TP % 2) {   // a single P tile (P = 16): 8-byte pieces
+          const f32x4 lo = acc[hd][K::TP - 1];
+          const u32x2 v = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+          buf_store8(v, ry, (row + (K::TP - 1) * 16 + 4 * g4) * 2);
         }
       }
     } else {

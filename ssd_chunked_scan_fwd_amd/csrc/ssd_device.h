@@ -71,6 +71,9 @@ __device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
+__device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // MI355X deals consecutive workgroups of a launch round-robin over its 8 XCDs,
