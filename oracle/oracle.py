@@ -22,9 +22,13 @@ Helpers here that are not the recurrence:
   * ``chunk_cumsum`` -- the cumulative log decay restarted in every chunk
     (paper card Method 5 pseudocode, "decay_cumsum"), a plain fp64 cumsum.
 
+The Mamba-2 functions (``softplus``, ``silu``, ``mamba2_discretize``,
+``mamba2_forward``, ``mamba2_step``) put the block's discretisation, skip and
+gate around that recurrence (paper card Method 6, Paper vs code 3, 7, 8).
+
 Every function in this file is pinned by ``tests/test_oracle.py`` against the
 quadratic dual form, closed forms, causal linear attention, packing,
-continuation and invariants; none is "parity unpinned".
+continuation, hand-worked examples and invariants; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -197,6 +201,105 @@ def step(state, x, la, B, C):
     b, H, P = x.shape
     Y, fin, _ = scan(x[:, None], _f64(la)[:, None], _f64(B)[:, None], _f64(C)[:, None],
                      segments=[(r, 0, 1) for r in range(b)], init=_f64(state))
+    return Y[:, 0], fin
+
+
+# ---------------------------------------------------------------------------
+# The Mamba-2 block's SSD call ("Transformers are SSMs" paper card,
+# wikillm.com/papers/2405.21060: Method 6, the block sketch; Paper vs code
+# items 3, 7 and 8; Pitfalls, "Discretisation is missing from the paper").
+# The block does not hand the layer log a and a scaled input; it hands raw
+# step sizes and per-head parameters, and finishes the output itself:
+#
+#   dt'  = softplus(dt + dt_bias)              per (row, token, head)
+#   log a = dt' * A,  A = -exp(A_log)          per head
+#   y    = SSM(a, B, C)(x * dt') + D * x       the skip uses the unscaled x
+#   y    = y * silu(z),  silu(v) = v / (1 + exp(-v))   the gate, when z is given
+#
+# Readings where the pages leave a step open: softplus is log(1 + e^v) with no
+# threshold; there is no clamp on dt'; the gate multiplies after the skip and
+# before any normalisation (the block sketch gates first, then normalises).
+# ---------------------------------------------------------------------------
+# Planted mistakes of the Mamba-2 arithmetic, used only by the pin-strength tests.
+MAMBA2_MUTANTS = {
+    "skip_uses_scaled_x": 1,
+    "gate_before_skip": 2,
+    "bias_ignored": 3,
+    "decay_rate_positive": 4,
+    "input_not_scaled": 5,
+    "gate_sigmoid": 6,
+    "decay_uses_raw_dt": 7,
+}
+
+
+def softplus(v) -> np.ndarray:
+    """log(1 + e^v) in fp64, evaluated without overflow (numpy's logaddexp(0, v))."""
+    return np.logaddexp(0.0, _f64(v))
+
+
+def silu(v) -> np.ndarray:
+    """v / (1 + e^-v) in fp64, written as v * sigmoid(v) with a stable sigmoid."""
+    v = _f64(v)
+    return v * (0.5 * (1.0 + np.tanh(0.5 * v)))
+
+
+def mamba2_discretize(dt, dt_bias, A_log, mutant: int = 0):
+    """Step sizes dt' = softplus(dt + dt_bias) and log decays dt' * A, A = -exp(A_log).
+
+    dt [..., H] (raw), dt_bias [H] or None (zero), A_log [H]. Returns (dt', log_a),
+    both fp64 with the shape of dt.
+    """
+    dt = _f64(dt)
+    bias = np.zeros(dt.shape[-1]) if dt_bias is None else _f64(dt_bias)
+    v = dt if mutant == MAMBA2_MUTANTS["bias_ignored"] else dt + bias
+    dtp = softplus(v)
+    A = np.exp(_f64(A_log))
+    A = A if mutant == MAMBA2_MUTANTS["decay_rate_positive"] else -A
+    la = (v if mutant == MAMBA2_MUTANTS["decay_uses_raw_dt"] else dtp) * A
+    return dtp, la
+
+
+def _mamba2_epilogue(Y, x, D, z, mutant):
+    if mutant == MAMBA2_MUTANTS["gate_before_skip"]:
+        if z is not None:
+            Y = Y * silu(z)
+        return Y + (0.0 if D is None else _f64(D)[None, None, :, None] * x)
+    if D is not None:
+        Y = Y + _f64(D)[None, None, :, None] * x
+    if z is not None:
+        g = _f64(z)
+        Y = Y * (0.5 * (1.0 + np.tanh(0.5 * g)) if mutant == MAMBA2_MUTANTS["gate_sigmoid"] else silu(g))
+    return Y
+
+
+def mamba2_forward(X, dt, dt_bias, A_log, D, z, B, C, cu_seqlens=None, init=None, threads: int = 0,
+                   mutant: int = 0):
+    """Y and final states of the Mamba-2 block's SSD call.
+
+    X [rows,T,H,P] (the block's x, unscaled), dt [rows,T,H] raw step sizes,
+    dt_bias [H] or None, A_log [H], D [H] or None (no skip), z [rows,T,H,P] or
+    None (no gate), B and C [rows,T,G,N]; cu_seqlens and init as in forward().
+    The recurrence itself is forward()'s, run on x * dt' with log a = dt' * A.
+    """
+    x = _f64(X)
+    dtp, la = mamba2_discretize(dt, dt_bias, A_log, mutant)
+    Xs = x if mutant == MAMBA2_MUTANTS["input_not_scaled"] else x * dtp[..., None]
+    Y, fin = forward(Xs, la, B, C, cu_seqlens=cu_seqlens, threads=threads, init=init)
+    if mutant == MAMBA2_MUTANTS["skip_uses_scaled_x"]:
+        x = x * dtp[..., None]
+    return _mamba2_epilogue(Y, x, D, z, mutant), fin
+
+
+def mamba2_step(state, x, dt, dt_bias, A_log, D, z, B, C):
+    """One Mamba-2 decode step from ``state``.
+
+    state [b,H,P,N], x [b,H,P], dt [b,H] raw, dt_bias/A_log/D [H] (D may be
+    None), z [b,H,P] or None, B and C [b,G,N]. Returns (y [b,H,P], new_state).
+    """
+    x = _f64(x)
+    Y, fin = mamba2_forward(x[:, None], _f64(dt)[:, None], dt_bias, A_log, D,
+                            None if z is None else _f64(z)[:, None], _f64(B)[:, None], _f64(C)[:, None],
+                            init=_f64(state))
     return Y[:, 0], fin
 
 

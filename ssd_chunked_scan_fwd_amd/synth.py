@@ -129,3 +129,61 @@ def workload_inputs(w: Workload, seed: Optional[int] = None):
     if w.steps:
         return make_decode_inputs(w.batch, w.steps, w.H, w.P, w.N, w.G, w.torch_dtype, s)
     return make_forward_inputs(w.batch, w.T, w.H, w.P, w.N, w.G, w.torch_dtype, s, varlen=w.varlen)
+
+
+# ---------------------------------------------------------------------------
+# Mamba-2 block inputs: the SSD call as the block makes it, with the raw step
+# sizes, the per-head parameters and the gate instead of a precomputed log a.
+#
+# Value recipe: x ~ N(0, 1); dt (raw, per row, token and head) ~ N(0, 0.5^2);
+# dt_bias = ln(u) with u log-uniform in [0.001, 0.1], so that the step sizes
+# land around the [0.001, 0.1] range of the pages' initialisation;
+# A_log = ln(U(1, 16)) (A initialised uniformly in [1, 16] and stored as its
+# log); D ~ U(0.5, 1.5); z ~ N(0, 1); B, C ~ N(0, 1) / sqrt(N). Draw order:
+# sequence lengths (packed only), x, dt, dt_bias, A_log, D, z, B, C. x, z, B
+# and C are drawn in fp32 and rounded to the workload dtype; dt, dt_bias, A_log
+# and D stay fp32.
+# ---------------------------------------------------------------------------
+def make_mamba2_inputs(batch: int, T: int, H: int, P: int, N: int, G: int = 1, dtype=torch.bfloat16,
+                       seed: int = 0, varlen: Optional[Tuple[int, int]] = None,
+                       lengths: Optional[List[int]] = None):
+    """Inputs of one Mamba-2 SSD call as CPU tensors.
+
+    Returns dict(X [b,T,H,P], dt [b,T,H] fp32, dt_bias [H], A_log [H], D [H]
+    (fp32), z [b,T,H,P], B [b,T,G,N], C [b,T,G,N], cu_seqlens int32 [S+1] or
+    None, lengths list or None).
+    """
+    rng = np.random.default_rng(seed)
+    cu = None
+    if varlen is not None or lengths is not None:
+        if batch != 1:
+            raise ValueError("packed sequences use a single row")
+        if lengths is None:
+            lengths = draw_lengths(rng, T, varlen[0], varlen[1])
+        if sum(lengths) != T:
+            raise ValueError("lengths must add up to T")
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    X = rng.standard_normal((batch, T, H, P), dtype=np.float32)
+    dt = rng.standard_normal((batch, T, H), dtype=np.float32) * np.float32(0.5)
+    dt_bias = rng.uniform(math.log(0.001), math.log(0.1), size=(H,)).astype(np.float32)
+    A_log = np.log(rng.uniform(1.0, 16.0, size=(H,))).astype(np.float32)
+    D = rng.uniform(0.5, 1.5, size=(H,)).astype(np.float32)
+    z = rng.standard_normal((batch, T, H, P), dtype=np.float32)
+    inv = np.float32(1.0 / math.sqrt(N))
+    Bm = rng.standard_normal((batch, T, G, N), dtype=np.float32) * inv
+    Cm = rng.standard_normal((batch, T, G, N), dtype=np.float32) * inv
+    return dict(X=_to_dtype(X, dtype), dt=torch.from_numpy(dt), dt_bias=torch.from_numpy(dt_bias),
+                A_log=torch.from_numpy(A_log), D=torch.from_numpy(D), z=_to_dtype(z, dtype),
+                B=_to_dtype(Bm, dtype), C=_to_dtype(Cm, dtype), cu_seqlens=cu, lengths=lengths)
+
+
+def make_mamba2_decode_inputs(batch: int, steps: int, H: int, P: int, N: int, G: int = 1,
+                              dtype=torch.bfloat16, seed: int = 0):
+    """Per-step inputs of the Mamba-2 decode step, stacked over steps (same recipe).
+
+    Returns dict(x [steps,b,H,P], dt [steps,b,H] fp32, dt_bias [H], A_log [H],
+    D [H], z [steps,b,H,P], B [steps,b,G,N], C [steps,b,G,N]).
+    """
+    d = make_mamba2_inputs(steps, batch, H, P, N, G, dtype, seed)
+    return dict(x=d["X"], dt=d["dt"], dt_bias=d["dt_bias"], A_log=d["A_log"], D=d["D"], z=d["z"],
+                B=d["B"], C=d["C"])

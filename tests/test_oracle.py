@@ -301,3 +301,148 @@ def _pins(mutant):
 def test_mutants_are_caught(name):
     assert _pins(0) == []
     assert _pins(oracle.MUTANTS[name]), f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------- Mamba-2 block call
+
+GOLDEN_M2 = os.path.join(os.path.dirname(__file__), "golden", "mamba2_hand_worked.json")
+
+
+def _m2_cases():
+    with open(GOLDEN_M2) as f:
+        return json.load(f)["cases"]
+
+
+def _m2_case_inputs(case):
+    x = np.array(case["x"])[None]
+    dt = np.array(case["dt"])[None]
+    bias = np.log(np.array(case["dt_bias_exp"]))
+    A_log = np.log(np.array(case["A_mag"]))
+    D = None if case["D"] is None else np.array(case["D"])
+    z = None if case["z_ln3"] is None else np.array(case["z_ln3"])[None] * math.log(3.0)
+    return x, dt, bias, A_log, D, z, np.array(case["B"])[None], np.array(case["C"])[None]
+
+
+def _m2_case_expected(case):
+    y = np.array(case["y_ln2"]) * math.log(2.0) + np.array(case["y_const"])
+    if case["gate_ln3"] is not None:
+        y = y * np.array(case["gate_ln3"]) * math.log(3.0)
+    return y, np.array(case["final_ln2"]) * math.log(2.0)
+
+
+def _m2_rand(T, H, P, N, G=1, seed=0, rows=1):
+    d = synth.make_mamba2_inputs(rows, T, H, P, N, G, dtype=__import__("torch").float32, seed=seed)
+    return {k: (v.double().numpy() if hasattr(v, "double") else v) for k, v in d.items()}
+
+
+@pytest.mark.parametrize("case", _m2_cases(), ids=lambda c: c["name"])
+def test_mamba2_hand_worked(case):
+    Y, fin = oracle.mamba2_forward(*_m2_case_inputs(case))
+    y, f = _m2_case_expected(case)
+    np.testing.assert_allclose(Y[0], y, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(fin[0], f, rtol=1e-14, atol=1e-14)
+
+
+def test_softplus_and_silu_closed_forms():
+    ln2 = math.log(2.0)
+    assert oracle.softplus(0.0)[0] == pytest.approx(ln2, rel=1e-15)
+    assert oracle.softplus(math.log(3.0))[0] == pytest.approx(2 * ln2, rel=1e-15)
+    v = np.linspace(-30, 30, 121)
+    np.testing.assert_allclose(oracle.softplus(v) - oracle.softplus(-v), v, atol=1e-13)  # softplus(v) - softplus(-v) = v
+    assert oracle.softplus(800.0)[0] == 800.0                      # no overflow at large v
+    assert oracle.softplus(-60.0)[0] == pytest.approx(math.exp(-60.0), rel=1e-14)
+    np.testing.assert_allclose(oracle.silu([0.0, math.log(3.0), -math.log(3.0)]),
+                               [0.0, 0.75 * math.log(3.0), -0.25 * math.log(3.0)], rtol=1e-15, atol=1e-300)
+    assert oracle.silu(-800.0)[0] == 0.0 and oracle.silu(800.0)[0] == 800.0
+
+
+def test_mamba2_discretize_closed_forms():
+    # raw + bias = 0 -> dt' = ln 2; A_log = ln 3 -> A = -3, log a = -3 ln 2.
+    dtp, la = oracle.mamba2_discretize(np.array([[1.0, 0.0]]), np.array([-1.0, 0.0]),
+                                       np.array([0.0, math.log(3.0)]))
+    np.testing.assert_allclose(dtp, [[math.log(2.0)] * 2], rtol=1e-15)
+    np.testing.assert_allclose(la, [[-math.log(2.0), -3 * math.log(2.0)]], rtol=1e-15)
+    dtp, la = oracle.mamba2_discretize(np.zeros((1, 1)), None, np.zeros(1))
+    assert dtp[0, 0] == pytest.approx(math.log(2.0)) and la[0, 0] == pytest.approx(-math.log(2.0))
+
+
+def test_mamba2_no_input_path_is_skip_times_gate():
+    # B = 0: the SSM contributes nothing, so y = D x silu(z) exactly, whatever dt and A.
+    d = _m2_rand(37, 3, 5, 4, seed=3)
+    Y, fin = oracle.mamba2_forward(d["X"], d["dt"], d["dt_bias"], d["A_log"], d["D"], d["z"],
+                                   np.zeros_like(d["B"]), d["C"])
+    ref = d["D"][None, None, :, None] * d["X"] * d["z"] / (1.0 + np.exp(-d["z"]))
+    np.testing.assert_allclose(Y, ref, rtol=1e-14, atol=1e-15)
+    assert not fin.any()
+
+
+def test_mamba2_first_token_closed_form():
+    # T = 1 from zero: h = dt' x B^T, y = (dt' (C . B) + D) x silu(z) per head.
+    d = _m2_rand(1, 4, 3, 6, G=2, seed=4)
+    Y, fin = oracle.mamba2_forward(d["X"], d["dt"], d["dt_bias"], d["A_log"], d["D"], d["z"], d["B"], d["C"])
+    dtp = np.log1p(np.exp(d["dt"][0, 0] + d["dt_bias"]))
+    for h in range(4):
+        g = h // 2
+        cb = float(np.dot(d["C"][0, 0, g], d["B"][0, 0, g]))
+        x = d["X"][0, 0, h]
+        zz = d["z"][0, 0, h]
+        want = (dtp[h] * cb + d["D"][h]) * x * zz / (1.0 + np.exp(-zz))
+        np.testing.assert_allclose(Y[0, 0, h], want, rtol=1e-13)
+        np.testing.assert_allclose(fin[0, h], dtp[h] * np.outer(x, d["B"][0, 0, g]), rtol=1e-13)
+
+
+def test_mamba2_vanishing_step_size():
+    # dt' -> 0 (raw step sizes far below zero): no state update and no decay, y = D x silu(z).
+    d = _m2_rand(20, 2, 4, 4, seed=5)
+    Y, fin = oracle.mamba2_forward(d["X"], np.full_like(d["dt"], -80.0), d["dt_bias"], d["A_log"], d["D"],
+                                   d["z"], d["B"], d["C"])
+    ref = d["D"][None, None, :, None] * d["X"] * d["z"] / (1.0 + np.exp(-d["z"]))
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-30)
+    assert np.abs(fin).max() < 1e-30
+
+
+def test_mamba2_dual_form():
+    # The quadratic dual form on x * dt' with log a = dt' A, plus the skip and the gate.
+    d = _m2_rand(19, 4, 3, 5, G=2, seed=6)
+    Y, fin = oracle.mamba2_forward(d["X"], d["dt"], d["dt_bias"], d["A_log"], d["D"], d["z"], d["B"], d["C"])
+    dtp = np.log1p(np.exp(d["dt"][0] + d["dt_bias"][None]))
+    Yd, fd = dual_form(d["X"][0] * dtp[..., None], dtp * -np.exp(d["A_log"])[None], d["B"][0], d["C"][0])
+    zz = d["z"][0]
+    Yd = (Yd + d["D"][None, :, None] * d["X"][0]) * zz / (1.0 + np.exp(-zz))
+    assert _relmax(Y[0], Yd) < 1e-12 and _relmax(fin[0], fd) < 1e-12
+
+
+def test_mamba2_steps_continue_the_forward_pass():
+    # A prompt through the forward pass, then decode steps, equals the longer prompt at once.
+    d = _m2_rand(12, 2, 3, 4, seed=7)
+    T0 = 8
+    Y, fin = oracle.mamba2_forward(d["X"], d["dt"], d["dt_bias"], d["A_log"], d["D"], d["z"], d["B"], d["C"])
+    _, st = oracle.mamba2_forward(d["X"][:, :T0], d["dt"][:, :T0], d["dt_bias"], d["A_log"], d["D"],
+                                  d["z"][:, :T0], d["B"][:, :T0], d["C"][:, :T0])
+    for t in range(T0, 12):
+        y, st = oracle.mamba2_step(st, d["X"][:, t], d["dt"][:, t], d["dt_bias"], d["A_log"], d["D"],
+                                   d["z"][:, t], d["B"][:, t], d["C"][:, t])
+        assert _relmax(y, Y[:, t]) < 1e-13
+    assert _relmax(st, fin) < 1e-13
+
+
+def _m2_pins(mutant):
+    failed = []
+    for case in _m2_cases():
+        Y, fin = oracle.mamba2_forward(*_m2_case_inputs(case), mutant=mutant)
+        y, f = _m2_case_expected(case)
+        if not (np.allclose(Y[0], y, atol=1e-12) and np.allclose(fin[0], f, atol=1e-12)):
+            failed.append("hand:" + case["name"])
+    d = _m2_rand(9, 2, 3, 4, seed=8)
+    Y, _ = oracle.mamba2_forward(d["X"], d["dt"], d["dt_bias"], d["A_log"], d["D"], d["z"],
+                                 np.zeros_like(d["B"]), d["C"], mutant=mutant)
+    ref = d["D"][None, None, :, None] * d["X"] * d["z"] / (1.0 + np.exp(-d["z"]))
+    if not np.allclose(Y, ref, rtol=1e-12, atol=1e-15):
+        failed.append("no_input_path")
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(oracle.MAMBA2_MUTANTS))
+def test_mamba2_mutants_are_caught(name):
+    assert _m2_pins(0) == []
+    assert _m2_pins(oracle.MAMBA2_MUTANTS[name]), f"mutant {name} passed every pin"
