@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
   SSD_OK = 0,
@@ -101,6 +101,9 @@ typedef struct {
  *                (0: empty slot), 0
  *   cumsum       fp32  [nslots][H][chunk]: log2(e) * cumulative log_a, restarted per chunk,
  *                positions past the chunk's length repeat its total
+ *   key_cumsum   fp32  [nslots][H][chunk]: ssd_fwd_mamba2 only, cumsum_j - log2(dt'_j), the
+ *                exponent of the weight of key token j (its decay and its input scale);
+ *                positions past the chunk's length repeat the chunk total
  *   block_decay  fp32  [nblocks][H]: log2(e) * total log_a of each state block
  *   block_states fp32  [nblocks][H][P][N]: right factors, state at the block end from a
  *                zero start
@@ -120,6 +123,7 @@ typedef struct {
   size_t table_offset;
   size_t block_table_offset;
   size_t cumsum_offset;
+  size_t key_cumsum_offset;
   size_t block_decay_offset;
   size_t block_states_offset;
   size_t start_states_offset;
@@ -204,6 +208,34 @@ ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The Mamba-2 block's SSD call (paper card Method 6, the block sketch; Paper vs
+ * code items 3, 7 and 8; Pitfalls, "Discretisation is missing from the
+ * paper"). Instead of log a and a pre-scaled input, the block hands over raw
+ * step sizes and per-head parameters, and the output is finished in the same
+ * pass:
+ *     dt'_t  = softplus(dt_t + dt_bias)          softplus(v) = log(1 + e^v)
+ *     log a_t = dt'_t * A,   A = -exp(A_log)
+ *     Y = SSM(a, B, C)(x * dt') + D * x           (the skip uses the unscaled x)
+ *     Y = Y * silu(z),   silu(v) = v / (1 + e^-v) (when z is given)
+ * final_state is the state of SSM(a, B, C)(x * dt'), as in ssd_fwd_ex, and
+ * initial_state works as there.
+ *   X        [batch, seqlen, nheads, headdim] dtype: the block's x, unscaled
+ *   dt       [batch, seqlen, nheads] fp32: raw step sizes (before bias and softplus)
+ *   dt_bias  [nheads] fp32, or NULL for zero
+ *   A_log    [nheads] fp32
+ *   D        [nheads] fp32, or NULL for no skip
+ *   z        [batch, seqlen, nheads, headdim] dtype, or NULL for no gate
+ * The other arguments are those of ssd_fwd_ex. The workspace layout is that of
+ * ssd_fwd_layout, including key_cumsum. No separate stages are exposed for
+ * this call. Errors as for ssd_fwd_ex; dt and A_log must not be NULL.
+ */
+ssd_status ssd_fwd_mamba2(const void* X, const float* dt, const float* dt_bias, const float* A_log,
+                          const float* D, const void* z, const void* B, const void* C,
+                          const int32_t* cu_seqlens, const float* initial_state, int32_t chunk,
+                          int32_t state_block, void* Y, float* final_state, const ssd_shape* shape,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step for `batch` independent streams: the loop body of
  * the recurrence with a constant-size state (paper card Method 8 and its cost
  * table: about N^2 work per step; the page-1 summary: generation needs only a
@@ -215,6 +247,19 @@ ssd_status ssd_chunk_scan(const void* X, const void* B, const void* C, const int
  */
 ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C,
                     void* y, const ssd_shape* shape, void* stream);
+
+/*
+ * The Mamba-2 block's decode step (the loop body of ssd_fwd_mamba2):
+ *   dt' = softplus(dt + dt_bias), state = exp(dt' A) state + (x dt') B^T,
+ *   y = C^T state + D x, y = y * silu(z).
+ *   state [batch, H, P, N] fp32 in place; x, z [batch, H, P] dtype (z may be NULL);
+ *   dt [batch, H] fp32 raw; dt_bias (may be NULL), A_log, D (may be NULL) [H] fp32;
+ *   B, C [batch, G, N] dtype; y [batch, H, P] dtype (written).
+ * A prompt run through ssd_fwd_mamba2 hands its final_state to this step.
+ */
+ssd_status ssd_step_mamba2(float* state, const void* x, const float* dt, const float* dt_bias,
+                           const float* A_log, const float* D, const void* z, const void* B,
+                           const void* C, void* y, const ssd_shape* shape, void* stream);
 
 #ifdef __cplusplus
 }

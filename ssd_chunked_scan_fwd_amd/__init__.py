@@ -7,7 +7,8 @@ the first call does, and it raises if the library is missing.
 """
 from . import synth  # noqa: F401
 from .binding import (SSDError, Shape, Workspace, chunk_cumsum, chunk_scan, chunk_state,  # noqa: F401
-                      default_state_block, fwd, layout, lib, make_shape, state_passing, step, workspace_bytes)
+                      default_state_block, fwd, fwd_mamba2, layout, lib, make_shape, state_passing, step,
+                      step_mamba2, workspace_bytes)
 
-__all__ = ["synth", "fwd", "step", "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "Workspace",
+__all__ = ["synth", "fwd", "step", "fwd_mamba2", "step_mamba2", "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan", "Workspace",
            "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib", "default_state_block"]

@@ -25,7 +25,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "ssd_fwd_layout",
            "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
-           "ssd_state_passing", "ssd_chunk_scan", "ssd_step")
+           "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2")
 
 
 class SSDError(RuntimeError):
@@ -44,7 +44,7 @@ class Layout(ctypes.Structure):
     _fields_ = [("slots_per_row", ctypes.c_int64), ("nslots", ctypes.c_int64), ("blocks_per_row", ctypes.c_int64),
                 ("nblocks", ctypes.c_int64), ("table_offset", ctypes.c_size_t),
                 ("block_table_offset", ctypes.c_size_t), ("cumsum_offset", ctypes.c_size_t),
-                ("block_decay_offset", ctypes.c_size_t), ("block_states_offset", ctypes.c_size_t),
+                ("key_cumsum_offset", ctypes.c_size_t), ("block_decay_offset", ctypes.c_size_t), ("block_states_offset", ctypes.c_size_t),
                 ("start_states_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
 
 
@@ -85,6 +85,10 @@ def lib():
         L.ssd_chunk_scan.argtypes = [vp, vp, vp, vp, i32, i32, vp, shp, vp, sz, vp]
         L.ssd_step.restype = ctypes.c_int
         L.ssd_step.argtypes = [vp, vp, vp, vp, vp, vp, shp, vp]
+        L.ssd_fwd_mamba2.restype = ctypes.c_int
+        L.ssd_fwd_mamba2.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, shp, vp, sz, vp]
+        L.ssd_step_mamba2.restype = ctypes.c_int
+        L.ssd_step_mamba2.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, shp, vp]
         _lib = L
     return _lib
 
@@ -164,6 +168,11 @@ class Workspace:
     def cumsum(self) -> torch.Tensor:
         s, n = self.shape, self.layout.nslots
         return self._view(self.layout.cumsum_offset, n * s.nheads * self.chunk, torch.float32,
+                          (n, s.nheads, self.chunk))
+
+    def key_cumsum(self) -> torch.Tensor:
+        s, n = self.shape, self.layout.nslots
+        return self._view(self.layout.key_cumsum_offset, n * s.nheads * self.chunk, torch.float32,
                           (n, s.nheads, self.chunk))
 
     def block_decay(self) -> torch.Tensor:
@@ -269,4 +278,72 @@ def step(state: torch.Tensor, x: torch.Tensor, log_a: torch.Tensor, B: torch.Ten
         y = torch.empty_like(x)
     _call("ssd_step", _ptr(state), _ptr(x), _ptr(log_a), _ptr(B), _ptr(C), _ptr(y), ctypes.byref(shape),
           _stream(x.device))
+    return y
+
+
+def _check_mamba2(X, dt, dt_bias, A_log, D, z, H: int):
+    lead = tuple(X.shape[:-1])
+    if dt.dtype != torch.float32 or not dt.is_cuda or not dt.is_contiguous() or tuple(dt.shape) != lead:
+        raise ValueError(f"dt must be a contiguous fp32 device tensor of shape {lead}")
+    for name, t, need in (("dt_bias", dt_bias, False), ("A_log", A_log, True), ("D", D, False)):
+        if t is None:
+            if need:
+                raise ValueError(f"{name} is required")
+            continue
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (H,):
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor of shape ({H},)")
+    if z is not None and (z.dtype != X.dtype or not z.is_cuda or not z.is_contiguous() or z.shape != X.shape):
+        raise ValueError("z must be a contiguous device tensor of X's shape and dtype")
+
+
+def fwd_mamba2(X: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+               dt_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+               z: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, chunk: int = 128,
+               state_block: int = 0, Y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+               want_final: bool = True, workspace: Optional[Workspace] = None,
+               initial_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """The Mamba-2 block's SSD call (ssd_fwd_mamba2). Returns (Y, final_state or None).
+
+    X is the block's x (unscaled), dt the raw step sizes [b, T, H] fp32; dt_bias,
+    A_log and D are fp32 [H]; z (the gate) has X's shape and dtype. The other
+    arguments are those of fwd().
+    """
+    _check_inputs(X, None, B, C, cu_seqlens)
+    _check_mamba2(X, dt, dt_bias, A_log, D, z, X.shape[2])
+    shape = make_shape(X, B, cu_seqlens)
+    _check_state(initial_state, shape, "initial_state")
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and want_final:
+        nseq = X.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        final_state = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = Workspace(shape, chunk, X.device, state_block)
+    elif state_block > 0 and state_block != workspace.state_block:
+        raise ValueError("state_block differs from the workspace's")
+    _call("ssd_fwd_mamba2", _ptr(X), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(D), _ptr(z), _ptr(B), _ptr(C),
+          _ptr(cu_seqlens), _ptr(initial_state), int(chunk), workspace.state_block, _ptr(Y), _ptr(final_state),
+          ctypes.byref(shape), _ptr(workspace.buffer), workspace.nbytes, _stream(X.device))
+    return Y, final_state
+
+
+def step_mamba2(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor,
+                C: torch.Tensor, dt_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+                z: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One Mamba-2 decode step (ssd_step_mamba2): updates `state` in place and returns y."""
+    for name, t in (("state", state), ("x", x), ("B", B), ("C", C)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if state.dtype != torch.float32:
+        raise ValueError("state must be fp32")
+    b, H, P = x.shape
+    _check_mamba2(x, dt, dt_bias, A_log, D, z, H)
+    G, N = B.shape[1], B.shape[2]
+    if tuple(state.shape) != (b, H, P, N):
+        raise ValueError(f"state must have shape {(b, H, P, N)}")
+    shape = Shape(b, 1, H, G, P, N, 0, _dtype_code(x.dtype))
+    if y is None:
+        y = torch.empty_like(x)
+    _call("ssd_step_mamba2", _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(D), _ptr(z),
+          _ptr(B), _ptr(C), _ptr(y), ctypes.byref(shape), _stream(x.device))
     return y

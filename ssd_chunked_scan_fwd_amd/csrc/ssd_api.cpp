@@ -94,6 +94,8 @@ ssd_status make_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk, int
   off = align256(off + (size_t)L.nblocks * 16);
   L.cumsum_offset = off;
   off = align256(off + (size_t)L.nslots * H * chunk * 4);
+  L.key_cumsum_offset = off;
+  off = align256(off + (size_t)L.nslots * H * chunk * 4);
   L.block_decay_offset = off;
   off = align256(off + (size_t)L.nblocks * H * 4);
   L.block_states_offset = off;
@@ -111,9 +113,11 @@ struct Prepared {
 };
 
 // Full validation of a forward-stage call; fills `pp` on success.
+// `mamba2`: the key-side exponent gets its own workspace array (written by
+// the discretising cumsum stage); plain calls read cs in its place.
 ssd_status prepare(int stages, const void* X, const float* log_a, const void* B, const void* C,
                    const void* Y, const int32_t* cu, int32_t chunk, int32_t gs, const ssd_shape* s,
-                   void* workspace, size_t workspace_bytes, Prepared* pp) {
+                   void* workspace, size_t workspace_bytes, Prepared* pp, bool mamba2 = false) {
   ssd_status st = check_shape(s, cu, chunk);
   if (st != SSD_OK) return st;
   if (gs <= 0) gs = default_state_block(s, cu, chunk);
@@ -134,6 +138,7 @@ ssd_status prepare(int stages, const void* X, const float* log_a, const void* B,
   pp->ws = ssd::Workspace{reinterpret_cast<int4*>(base + L.table_offset),
                           reinterpret_cast<int4*>(base + L.block_table_offset),
                           reinterpret_cast<float*>(base + L.cumsum_offset),
+                          reinterpret_cast<float*>(base + (mamba2 ? L.key_cumsum_offset : L.cumsum_offset)),
                           reinterpret_cast<float*>(base + L.block_decay_offset),
                           reinterpret_cast<float*>(base + L.block_states_offset),
                           static_cast<void*>(base + L.start_states_offset)};
@@ -141,6 +146,18 @@ ssd_status prepare(int stages, const void* X, const float* log_a, const void* B,
 }
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+// Shape checks of the decode steps.
+ssd_status check_step(const ssd_shape* s) {
+  if (s->batch < 1 || s->nheads < 1 || s->ngroups < 1 || s->headdim < 1 || s->dstate < 1)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if (s->nheads % s->ngroups) return SSD_ERR_INVALID_ARGUMENT;
+  if (s->dtype != SSD_DTYPE_F32 && s->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
+  if (!pow2_in(s->headdim, 16, 128) || !pow2_in(s->dstate, 16, 256)) return SSD_ERR_UNSUPPORTED;
+  if (s->batch > 65535 || (int64_t)s->batch * s->nheads * s->headdim * s->dstate > kMaxElems)
+    return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
 
 }  // namespace
 
@@ -250,17 +267,55 @@ ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void*
                     workspace_bytes, stream);
 }
 
+ssd_status ssd_fwd_mamba2(const void* X, const float* dt, const float* dt_bias, const float* A_log,
+                          const float* D, const void* z, const void* B, const void* C, const int32_t* cu_seqlens,
+                          const float* initial_state, int32_t chunk, int32_t state_block, void* Y,
+                          float* final_state, const ssd_shape* shape, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!dt || !A_log) return SSD_ERR_INVALID_ARGUMENT;
+  Prepared pp;
+  // log_a is not read on this path; dt stands in for the non-null check.
+  ssd_status st = prepare(kAll, X, dt, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
+                          workspace_bytes, &pp, true);
+  if (st != SSD_OK) return st;
+  ssd::Mamba2Args m2;
+  m2.dt = dt;
+  m2.dt_bias = dt_bias;
+  m2.A_log = A_log;
+  m2.D = D;
+  m2.z = z;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = ssd::launch_chunk_cumsum(pp.d, nullptr, cu_seqlens, pp.ws, s, m2);
+  if (e == hipSuccess) e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s);
+  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, s);
+  if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s, m2);
+  return hip_status(e);
+}
+
+ssd_status ssd_step_mamba2(float* state, const void* x, const float* dt, const float* dt_bias, const float* A_log,
+                           const float* D, const void* z, const void* B, const void* C, void* y,
+                           const ssd_shape* shape, void* stream) {
+  if (!shape || !state || !x || !dt || !A_log || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+  const ssd_shape* s = shape;
+  const ssd_status st = check_step(s);
+  if (st != SSD_OK) return st;
+  ssd::Mamba2Args m2;
+  m2.dt = dt;
+  m2.dt_bias = dt_bias;
+  m2.A_log = A_log;
+  m2.D = D;
+  m2.z = z;
+  return hip_status(ssd::launch_ssd_step(s->batch, s->nheads, s->ngroups, s->headdim, s->dstate,
+                                         s->dtype == SSD_DTYPE_BF16 ? 1 : 0, state, x, nullptr, B, C, y,
+                                         (hipStream_t)stream, m2));
+}
+
 ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C, void* y,
                     const ssd_shape* shape, void* stream) {
   if (!shape || !state || !x || !log_a || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
   const ssd_shape* s = shape;
-  if (s->batch < 1 || s->nheads < 1 || s->ngroups < 1 || s->headdim < 1 || s->dstate < 1)
-    return SSD_ERR_INVALID_ARGUMENT;
-  if (s->nheads % s->ngroups) return SSD_ERR_INVALID_ARGUMENT;
-  if (s->dtype != SSD_DTYPE_F32 && s->dtype != SSD_DTYPE_BF16) return SSD_ERR_UNSUPPORTED;
-  if (!pow2_in(s->headdim, 16, 128) || !pow2_in(s->dstate, 16, 256)) return SSD_ERR_UNSUPPORTED;
-  if (s->batch > 65535 || (int64_t)s->batch * s->nheads * s->headdim * s->dstate > kMaxElems)
-    return SSD_ERR_UNSUPPORTED;
+  const ssd_status st = check_step(s);
+  if (st != SSD_OK) return st;
   return hip_status(ssd::launch_ssd_step(s->batch, s->nheads, s->ngroups, s->headdim, s->dstate,
                                          s->dtype == SSD_DTYPE_BF16 ? 1 : 0, state, x, log_a, B, C, y,
                                          (hipStream_t)stream));

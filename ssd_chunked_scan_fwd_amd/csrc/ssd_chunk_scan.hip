@@ -35,9 +35,15 @@
 //  * X, the decay-weighted X for the state update and B are staged token-major
 //    in LDS through registers (the next chunk's rows and C fragments in flight
 //    while the current chunk is computed); operands that contract over tokens
-//    use the gfx950 LDS transpose read. The state goes to LDS transposed, and
-//    output tiles leave through a small per-wave LDS transpose as 16-byte
-//    stores.
+//    use the gfx950 LDS transpose read. The state goes to LDS transposed.
+//    The waves accumulate Y^T (MFMA operands swapped: lane = query row,
+//    registers = consecutive channels), so after one v_permlane16_swap each
+//    lane stores 16 contiguous bytes of its token's row straight to HBM.
+//  * Mamba-2 block calls: the key-side weights read ck = cs - log2(dt')
+//    instead of cs, so x enters unscaled and dt' rides in the weights; the skip
+//    D x_i is added on the diagonal of the diagonal key block's L o S; the gate
+//    multiplies by silu(z) in fp32 before the one rounding of Y (paper card
+//    Method 6 block sketch; Paper vs code items 3 and 7).
 //  * Query tiles are dealt so that each SIMD's pair of waves gets one short
 //    and one long row of the triangle; the state update is spread over all
 //    waves. Two barriers per chunk.
@@ -51,7 +57,6 @@ namespace {
 
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = kScanWaves * 64;
-constexpr int kYPitch = 20;      // per-wave output staging tile [32][kYPitch]
 
 template <int P, int N>
 struct ScanCfg {
@@ -70,6 +75,74 @@ struct ScanCfg {
 // Query tile of wave w in round k: SIMD s = w % 4 pairs tile s with tile 7 - s.
 __device__ __forceinline__ int scan_tile(int k, int w) { return 8 * k + (w < 4 ? w : 11 - w); }
 
+// Output of one wave's transposed tile: acc[pt][r] holds Y[token][pt * 16 +
+// 4 * g4 + r] for the lane's token (query row l16 of the tile), and `row` is
+// the element offset of that token's row in Y (and in z). For a pair of P
+// tiles, v_permlane16_swap exchanges the halves of lane groups so that each
+// lane holds 8 consecutive channels of its token: group g4 gets
+// p = 32 q + 16 (g4 & 1) + 8 (g4 >> 1) .. + 7, stored as one 16-byte piece (rows
+// past the chunk's length fall outside the buffer range and are dropped). A
+// single P tile (P = 16) leaves as 8-byte pieces. With GATE the values are
+// multiplied by silu(z) in fp32 before the one rounding to bf16 (the Mamba-2
+// block's output gate, paper card Method 6), z read in the same pieces.
+template <int TP>
+struct ZPieces {
+  u32x4 q[TP / 2 > 0 ? TP / 2 : 1];
+  u32x2 t;
+};
+
+__device__ __forceinline__ uint32_t yT_piece(uint32_t row, int q, int g4) {
+  return row + 32 * q + 16 * (g4 & 1) + 8 * (g4 >> 1);
+}
+
+template <int TP>
+__device__ __forceinline__ void load_zT(ZPieces<TP>& z, rsrc_t rz, uint32_t row, int g4) {
+#pragma unroll
+  for (int q = 0; q < TP / 2; ++q) z.q[q] = buf_load16(rz, yT_piece(row, q, g4) * 2);
+  if (TP % 2) z.t = buf_load8(rz, (row + (TP - 1) * 16 + 4 * g4) * 2);
+}
+
+template <int TP, bool GATE>
+__device__ __forceinline__ void store_yT(const f32x4 (&acc)[TP], rsrc_t ry, uint32_t row, int g4,
+                                         const ZPieces<TP>& z) {
+#pragma unroll
+  for (int q = 0; q < TP / 2; ++q) {
+    const f32x4 lo = acc[2 * q], hi = acc[2 * q + 1];
+    u32x4 v;
+    if (GATE) {
+      float y[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo[r]), __float_as_uint(hi[r]), false, false);
+        y[r] = __uint_as_float(sw[0]);
+        y[4 + r] = __uint_as_float(sw[1]);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        v[w] = pack_bf16x2(y[2 * w] * silu_f32(bf16_lo(z.q[q][w])), y[2 * w + 1] * silu_f32(bf16_hi(z.q[q][w])));
+    } else {
+      const auto sx = __builtin_amdgcn_permlane16_swap(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(hi[0], hi[1]), false,
+                                                       false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[2], hi[3]), false,
+                                                       false);
+      v = u32x4{sx[0], sy[0], sx[1], sy[1]};
+    }
+    buf_store16(v, ry, yT_piece(row, q, g4) * 2);
+  }
+  if (TP % 2) {
+    const f32x4 lo = acc[TP - 1];
+    u32x2 v;
+    if (GATE) {
+      v = u32x2{pack_bf16x2(lo[0] * silu_f32(bf16_lo(z.t[0])), lo[1] * silu_f32(bf16_hi(z.t[0]))),
+                pack_bf16x2(lo[2] * silu_f32(bf16_lo(z.t[1])), lo[3] * silu_f32(bf16_hi(z.t[1])))};
+    } else {
+      v = u32x2{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
+    }
+    buf_store8(v, ry, (row + (TP - 1) * 16 + 4 * g4) * 2);
+  }
+}
+
+
 }  // namespace
 
 // Chunks of up to 128 tokens keep a separate decay-weighted copy of X; longer
@@ -77,21 +150,21 @@ __device__ __forceinline__ int scan_tile(int k, int w) { return 8 * k + (w < 4 ?
 static bool scan_in_place(int P, int N, int Q) { return Q > 128 || N > 128 || P > 64; }
 
 // The v_j table ([Q/16][Q] fp32) is kept for chunks of up to 128 tokens;
-// longer chunks compute v_j where it is used.
+// longer chunks compute v_j where it is used. cs and ck take [Q] each.
 size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q) {
   const size_t nIt = Q / 16;
   const size_t xcopies = scan_in_place(P, N, Q) ? 1 : 2;
-  const size_t el = (size_t)Q * lds_pitch(N) + xcopies * (size_t)Q * lds_pitch(P) + (size_t)N * lds_pitch(P) +
-                    (size_t)kScanWaves * 32 * kYPitch;
-  return el * 2 + ((Q > 128 ? 0 : nIt * Q) + 2 * Q + nIt) * 4 + 16 * 16;
+  const size_t el = (size_t)Q * lds_pitch(N) + xcopies * (size_t)Q * lds_pitch(P) + (size_t)N * lds_pitch(P);
+  return el * 2 + ((Q > 128 ? 0 : nIt * Q) + 2 * Q) * 4 + 16 * 16;
 }
 
 // ITW: query tiles per wave (1 for chunks of up to 128 tokens, 2 for 256).
-template <int P, int N, int ITW>
+template <int P, int N, int ITW, bool GATE>
 __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
-    const uint16_t* __restrict__ start, uint16_t* __restrict__ Y, int H, int G, int Q) {
+    const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q) {
   using K = ScanCfg<P, N>;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
@@ -108,19 +181,17 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   uint16_t* xs = bs + Q * K::BP;                      // [Q][XP]  X rows
   uint16_t* xw = kInPlace ? xs : xs + Q * K::XP;      // [Q][XP]  X rows times exp2(cs_last - cs_j)
   uint16_t* hsT = xw + Q * K::XP;                     // [N][HP]  state entering the chunk, transposed
-  uint16_t* ysw = hsT + N * K::HP;                    // [8][32][kYPitch] per-wave output staging
   constexpr bool kVTable = ITW == 1;                  // tabulate v_j (chunks of up to 128 tokens)
-  int4* recs = reinterpret_cast<int4*>(ysw + kScanWaves * 32 * kYPitch);  // [16] chunk records of the block
-  float* Vt = reinterpret_cast<float*>(recs + 16);    // [nIt][Q] v_j per query tile
-  float* Ut = Vt + (kVTable ? nIt * Q : 0);           // [Q] u_i
-  float* Et = Ut + Q;                                 // [nIt] exp2(m) per query tile
-  float* csl = Et + nIt;                              // [Q] cumulative log2 decay
+  int4* recs = reinterpret_cast<int4*>(hsT + N * K::HP);  // [16] chunk records of the block
+  float* Vt = reinterpret_cast<float*>(recs + 16);    // [nIt][Q] v_j = exp2(m - ck_j) per query tile
+  float* csl = Vt + (kVTable ? nIt * Q : 0);          // [Q] cumulative log2 decay cs
+  float* ckl = csl + Q;                               // [Q] key-side exponent ck
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const long ldb = (long)G * N, ldx = (long)H * P;
-  uint16_t* ys = ysw + wave * 32 * kYPitch;
+  const float Dh = Dskip ? Dskip[h] : 0.f;            // skip weight, on the diagonal of L o S
 
   // Per-thread constant byte offsets of its staged pieces within a chunk (rows
   // past the chunk's length fall outside the chunk's buffer range and load 0).
@@ -167,7 +238,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   // Registers holding the next chunk.
   u32x4 pb[K::RB], px[K::RX];
   u32x4 pcf[ITW][K::NB];    // C fragments of this wave's query tiles
-  float pcs_t = 0.f, pcs_tm = 0.f, pcs_last = 0.f, pcs_e = 0.f;
+  float pcs_t = 0.f, pck_t = 0.f, pcs_last = 0.f;
   constexpr int VE = kVTable ? 2 : 1;    // v-table entries per thread: nIt*Q <= VE*512
   float pcs_v[VE], pcs_vm[VE];
   float pcs_x[K::RX];
@@ -181,12 +252,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     const rsrc_t rx = make_rsrc(X + ((long)r.tok0 * H + h) * P, (uint32_t)(len * ldx * 2));
     const rsrc_t rcc = make_rsrc(C + ((long)r.tok0 * G + g) * N, (uint32_t)(len * ldb * 2));
     const rsrc_t rc = make_rsrc(cs + (slot * H + h) * (long)Q, valid ? (uint32_t)(Q * 4) : 0u);
+    const rsrc_t rk = make_rsrc(ck + (slot * H + h) * (long)Q, valid ? (uint32_t)(Q * 4) : 0u);
 #pragma unroll
     for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(rb, boff[u]);
 #pragma unroll
     for (int u = 0; u < K::RX; ++u) {
       px[u] = buf_load16(rx, xoff[u]);
-      pcs_x[u] = buf_load_f32(rc, (uint32_t)(min(xrow[u], Q - 1) * 4));
+      pcs_x[u] = buf_load_f32(rk, (uint32_t)(min(xrow[u], Q - 1) * 4));
     }
 #pragma unroll
     for (int k = 0; k < ITW; ++k)
@@ -194,13 +266,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
       for (int nb = 0; nb < K::NB; ++nb) pcf[k][nb] = buf_load16(rcc, cfoff[k] + nb * 64);
     pcs_last = buf_load_f32(rc, (uint32_t)((Q - 1) * 4));
     pcs_t = buf_load_f32(rc, (uint32_t)(tid * 4));            // zero for tid >= Q
-    pcs_tm = buf_load_f32(rc, (uint32_t)((tid & ~15) * 4));
-    pcs_e = buf_load_f32(rc, (uint32_t)(16 * tid * 4));        // zero for tid >= Q / 16
+    pck_t = buf_load_f32(rk, (uint32_t)(tid * 4));
 #pragma unroll
     for (int u = 0; u < VE; ++u) {
       const int e = tid + kScanThreads * u;
       if (kVTable) {
-        pcs_v[u] = buf_load_f32(rc, (uint32_t)((e % Q) * 4));
+        pcs_v[u] = buf_load_f32(rk, (uint32_t)((e % Q) * 4));
         pcs_vm[u] = buf_load_f32(rc, (uint32_t)(16 * (e / Q) * 4));  // zero past the table
       }
     }
@@ -241,12 +312,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
         }
       }
     }
-    // Decay tables: u_i, exp2(m) per query tile, v_j per (query tile, key).
+    // cs, ck and the v_j table per (query tile, key).
     if (tid < Q) {
-      Ut[tid] = fast_exp2(pcs_t - pcs_tm);
       csl[tid] = pcs_t;
+      ckl[tid] = pck_t;
     }
-    if (tid < nIt) Et[tid] = fast_exp2(pcs_e);
 #pragma unroll
     for (int u = 0; u < VE; ++u) {
       const int e = tid + kScanThreads * u;
@@ -254,7 +324,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     }
     // Chunks longer than one pass: the remaining rows, synchronously.
     for (int r0 = kPassRows; r0 < Q; r0 += kPassRows) {
-      const float* csr = cs + (slot * H + h) * (long)Q;
+      const float* ckr = ck + (slot * H + h) * (long)Q;
       for (int idx = tid; idx < kPassRows * K::CBN; idx += kScanThreads) {
         const int j = r0 + idx / K::CBN, cc = idx % K::CBN;
         *reinterpret_cast<u32x4*>(bs + j * K::BP + cc * 8) =
@@ -266,7 +336,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
                                  : u32x4{0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(xs + j * K::XP + cc * 8) = v0;
         if (!kInPlace) {
-          const float w = fast_exp2(cs_last - csr[j]);
+          const float w = fast_exp2(cs_last - ckr[j]);
           u32x4 v;
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(v0[q]) * w, bf16_hi(v0[q]) * w);
@@ -300,15 +370,17 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
       const int it = scan_tile(k, wave);
       if (it >= nIt || it * 16 >= len) continue;
       const int irow = it * 16 + l16;
+      // Y^T accumulators: lane = query row l16, registers = 4 consecutive p.
       f32x4 acc[K::TP];
 #pragma unroll
       for (int pt = 0; pt < K::TP; ++pt) {
         acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int nb = 0; nb < K::NB; ++nb)
-          acc[pt] = mfma16x16x32(cf[k][nb], frag_k_rows_accpair(hsT, K::HP, nb * 32, pt * 16, lane), acc[pt]);
+          acc[pt] = mfma16x16x32(frag_k_rows_accpair(hsT, K::HP, nb * 32, pt * 16, lane), cf[k][nb], acc[pt]);
       }
-      const float em = Et[it];
+      const float mref = csl[16 * it];
+      const float em = fast_exp2(mref);
 #pragma unroll
       for (int pt = 0; pt < K::TP; ++pt) acc[pt] *= em;
       const float* vrow = Vt + it * Q + 4 * g4;
@@ -329,8 +401,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
         for (int half = 0; half < 2; ++half) {
           const int j0 = (2 * kb + half) * 16 + 4 * g4;
           if (diag || !kVTable) {
-            const f32x4 cj = *reinterpret_cast<const f32x4*>(csl + j0);
-            const float ref = diag ? cs_i : csl[16 * it];
+            const f32x4 cj = *reinterpret_cast<const f32x4*>(ckl + j0);
+            const float ref = diag ? cs_i : mref;
 #pragma unroll
             for (int r = 0; r < 4; ++r) fac[half][r] = (!diag || j0 + r <= irow) ? fast_exp2(ref - cj[r]) : 0.f;
           } else {
@@ -345,9 +417,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
         uint32_t mw[4], ml[4];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+          const int j0 = (2 * kb + half) * 16 + 4 * g4;
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = sv[half][r] * fac[half][r];
+          for (int r = 0; r < 4; ++r) v[r] = sv[half][r] * fac[half][r] + (diag && j0 + r == irow ? Dh : 0.f);
           mw[2 * half] = pack_bf16x2(v[0], v[1]);
           mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
           ml[2 * half] = pack_bf16x2(v[0] - bf16_lo(mw[2 * half]), v[1] - bf16_hi(mw[2 * half]));
@@ -359,34 +432,20 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 #pragma unroll
         for (int pt = 0; pt < K::TP; ++pt) xf[pt] = frag_k_rows_accpair(xs, K::XP, 32 * kb, pt * 16, lane);
 #pragma unroll
-        for (int pt = 0; pt < K::TP; ++pt) acc[pt] = mfma16x16x32(ah, xf[pt], acc[pt]);
+        for (int pt = 0; pt < K::TP; ++pt) acc[pt] = mfma16x16x32(xf[pt], ah, acc[pt]);
 #pragma unroll
-        for (int pt = 0; pt < K::TP; ++pt) acc[pt] = mfma16x16x32(al, xf[pt], acc[pt]);
+        for (int pt = 0; pt < K::TP; ++pt) acc[pt] = mfma16x16x32(xf[pt], al, acc[pt]);
       };
       for (int kb = 0; kb < kbd; ++kb) key_block(kb, false);
-      // u_i now: the diagonal key block uses the exact masked decay.
-      const f32x4 uu = *reinterpret_cast<const f32x4*>(Ut + it * 16 + 4 * g4);
+      const uint32_t yrow = (uint32_t)(irow * ldx);
+      ZPieces<K::TP> zp;
+      if (GATE) load_zT<K::TP>(zp, make_rsrc(Z + (tok0 * H + h) * P, (uint32_t)(len * ldx * 2)), yrow, g4);
+      // u_i now (this lane's query row): the diagonal key block uses the exact masked decay.
+      const float u = fast_exp2(cs_i - mref);
 #pragma unroll
-      for (int pt = 0; pt < K::TP; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[pt][r] *= uu[r];
+      for (int pt = 0; pt < K::TP; ++pt) acc[pt] *= u;
       key_block(kbd, true);
-      // Out through the wave's staging tile as 16-byte rows (rows past the
-      // chunk's length fall outside the buffer range and are dropped).
-      const rsrc_t ry = make_rsrc(Y + (tok0 * H + h) * P, (uint32_t)(len * ldx * 2));
-#pragma unroll
-      for (int pp = 0; pp < (K::TP + 1) / 2; ++pp) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int pt = 2 * pp + q;
-          if (pt < K::TP) {
-            const u32x2 v = {pack_bf16x2(acc[pt][0], acc[pt][1]), pack_bf16x2(acc[pt][2], acc[pt][3])};
-            *reinterpret_cast<u32x2*>(ys + perm32(q * 16 + l16) * kYPitch + 4 * g4) = v;
-          }
-        }
-        const u32x4 out = frag_k_rows_accpair(ys, kYPitch, 0, 0, lane);  // token l16, p = 32pp + 8g4 ..
-        buf_store16(out, ry, pp * 32 + 8 * g4 < P ? (uint32_t)(((it * 16 + l16) * ldx + pp * 32 + 8 * g4) * 2) : kOffNone);
-      }
+      store_yT<K::TP, GATE>(acc, make_rsrc(Y + (tok0 * H + h) * P, (uint32_t)(len * ldx * 2)), yrow, g4, zp);
     }
 
     // ---------------- state entering the next chunk of the block
@@ -394,7 +453,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
       __syncthreads();
       for (int idx = tid; idx < Q * K::CBP; idx += kScanThreads) {
         const int j = idx / K::CBP, cc = idx % K::CBP;
-        const float w = fast_exp2(cs_last - csl[j]);
+        const float w = fast_exp2(cs_last - ckl[j]);
         u32x4 v = *reinterpret_cast<const u32x4*>(xs + j * K::XP + cc * 8);
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(v[q]) * w, bf16_hi(v[q]) * w);
@@ -459,10 +518,10 @@ static size_t pair_lds_elems(int P, int N, int Q) {
   return (size_t)Q * lds_pitch(N) + 2 * (size_t)Q * lds_pitch(P) + 2 * (size_t)N * lds_pitch(P);
 }
 
-// LDS: the tiles above, 16 chunk records, cs and the state-update weights of
-// both heads ([2][Q] each) and one [2][Q] row of v_j per wave.
+// LDS: the tiles above, 16 chunk records, cs, ck and the state-update weights
+// of both heads ([2][Q] each) and one [2][Q] row of v_j per wave.
 static size_t chunk_scan_pair_lds_bytes(int P, int N, int Q) {
-  return pair_lds_elems(P, N, Q) * 2 + 16 * 16 + (size_t)(4 + 2 * kScanWaves) * Q * 4;
+  return pair_lds_elems(P, N, Q) * 2 + 16 * 16 + (size_t)(6 + 2 * kScanWaves) * Q * 4;
 }
 
 // Head pairs need an even number of heads per group; beyond P = 64 or N = 128
@@ -473,11 +532,12 @@ static bool chunk_scan_pair_fits(int P, int N, int Q, int H, int G) {
   return pair_shape(P, N) && (H / G) % 2 == 0 && Q <= 128 && chunk_scan_pair_lds_bytes(P, N, Q) <= kMaxLdsBytes;
 }
 
-template <int P, int N>
+template <int P, int N, bool GATE>
 __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
-    const uint16_t* __restrict__ start, uint16_t* __restrict__ Y, int H, int G, int Q) {
+    const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q) {
   using K = PairCfg<P, N>;
   const int HH = H / 2;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
@@ -493,14 +553,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
   uint16_t* xs = bs + Q * K::BP;                        // [2][Q][XP]   X rows of both heads
   uint16_t* hsT = xs + 2 * Q * K::XP;                   // [2][N][HP]   entering states, transposed
   int4* recs = reinterpret_cast<int4*>(hsT + 2 * N * K::HP);  // [16] chunk records
-  float* csl = reinterpret_cast<float*>(recs + 16);     // [2][Q] cumulative log2 decay
-  float* wt = csl + 2 * Q;                              // [2][Q] exp2(cs_last - cs_j)
+  float* csl = reinterpret_cast<float*>(recs + 16);     // [2][Q] cumulative log2 decay cs
+  float* wt = csl + 2 * Q;                              // [2][Q] exp2(cs_last - ck_j)
+  float* ckl = wt + 2 * Q;                              // [2][Q] key-side exponent ck
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   const long ldb = (long)G * N, ldx = (long)H * P;
-  float* vt = wt + 2 * Q + wave * 2 * Q;                // [2][Q] v_j of this wave's query tile
+  float* vt = ckl + 2 * Q + wave * 2 * Q;               // [2][Q] v_j of this wave's query tile
+  // Skip weights of both heads (zero without a skip): D x_i rides on the
+  // diagonal of the diagonal key block's L o S.
+  const float Dh[2] = {Dskip ? Dskip[h0] : 0.f, Dskip ? Dskip[h0 + 1] : 0.f};
   // This wave's query tile: waves 0-3 (the first wave of each SIMD) take the
   // long rows of the triangle, 7 - w, and waves 4-7 the short rows w - 4, so
   // each SIMD pairs a long and a short row.
@@ -544,9 +608,9 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
 
   // Registers holding the next chunk, filled in three groups.
   u32x4 pb[K::RB], px[2][K::RX], pcf[K::NB];
-  float pcs = 0.f, plast[2] = {0.f, 0.f};
+  float pcs = 0.f, pck = 0.f, plast[2] = {0.f, 0.f};
   struct Next {
-    rsrc_t rb, rx0, rx1, rc, rcs;
+    rsrc_t rb, rx0, rx1, rc, rcs, rck;
   };
   auto next_rsrc = [&](const SlotRec& r, long slot, bool valid) {
     const int len = valid ? r.len : 0;
@@ -556,6 +620,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
     n.rx0 = make_rsrc(X + ((long)r.tok0 * H + h0) * P, (uint32_t)(len * ldx * 2));
     n.rx1 = make_rsrc(X + ((long)r.tok0 * H + h0 + 1) * P, (uint32_t)(len * ldx * 2));
     n.rcs = make_rsrc(cs + (slot * H + h0) * (long)Q, valid ? (uint32_t)(2 * Q * 4) : 0u);
+    n.rck = make_rsrc(ck + (slot * H + h0) * (long)Q, valid ? (uint32_t)(2 * Q * 4) : 0u);
     return n;
   };
   auto load_b = [&](const Next& n) {
@@ -569,6 +634,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       px[1][u] = buf_load16(n.rx1, xoff[u]);
     }
     pcs = buf_load_f32(n.rcs, csoff);
+    pck = buf_load_f32(n.rck, csoff);
     plast[0] = buf_load_f32(n.rcs, (uint32_t)((Q - 1) * 4));
     plast[1] = buf_load_f32(n.rcs, (uint32_t)((2 * Q - 1) * 4));
   };
@@ -610,7 +676,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       }
     if (tid < 2 * Q) {
       csl[tid] = pcs;
-      wt[tid] = fast_exp2((tid < Q ? cs_last0 : cs_last1) - pcs);
+      ckl[tid] = pck;
+      wt[tid] = fast_exp2((tid < Q ? cs_last0 : cs_last1) - pck);
     }
     if (sact) {
 #pragma unroll
@@ -658,14 +725,14 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       const int irow = it * 16 + l16;
       const float csi[2] = {csl[irow], csl[Q + irow]};
       const int kbd = it >> 1;  // key block holding the diagonal tile
-      // v_j = exp2(m - cs_j) of both heads for the keys before this tile
+      // v_j = exp2(m - ck_j) of both heads for the keys before this tile
       // (private to the wave: written and read by the same wave, in order).
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd)
 #pragma unroll
         for (int q = 0; q < kPassRows / 64; ++q) {
           const int j = lane + 64 * q;
-          if (j < 16 * it) vt[hd * Q + j] = fast_exp2(mref[hd] - csl[hd * Q + j]);
+          if (j < 16 * it) vt[hd * Q + j] = fast_exp2(mref[hd] - ckl[hd * Q + j]);
         }
 
       // S^T of one key block of 32 tokens (both 16-key halves).
@@ -686,16 +753,17 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       auto y_block = [&](int kb, const f32x4 sv[2], bool diag) {
 #pragma unroll
         for (int hd = 0; hd < 2; ++hd) {
-          const float* cl = csl + hd * Q;
+          const float* kl = ckl + hd * Q;
           uint32_t mw[4], ml[4];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const int j0 = (2 * kb + half) * 16 + 4 * g4;
             float v[4];
             if (diag) {
-              const f32x4 cj = *reinterpret_cast<const f32x4*>(cl + j0);
+              const f32x4 cj = *reinterpret_cast<const f32x4*>(kl + j0);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) v[r] = j0 + r <= irow ? sv[half][r] * fast_exp2(csi[hd] - cj[r]) : 0.f;
+              for (int r = 0; r < 4; ++r)
+                v[r] = (j0 + r <= irow ? sv[half][r] * fast_exp2(csi[hd] - cj[r]) : 0.f) + (j0 + r == irow ? Dh[hd] : 0.f);
             } else {
               const f32x4 fj = *reinterpret_cast<const f32x4*>(vt + hd * Q + j0);
 #pragma unroll
@@ -732,6 +800,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
         }
       }
       load_c(nx);
+      const uint32_t yrow = (uint32_t)((it * 16 + l16) * ldx);
+      ZPieces<K::TP> zp[2];
+      if (GATE) {
+#pragma unroll
+        for (int hd = 0; hd < 2; ++hd)
+          load_zT<K::TP>(zp[hd], make_rsrc(Z + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow, g4);
+      }
       // u_i now: the diagonal key block uses the exact masked decay.
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd) {
@@ -743,32 +818,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       y_block(kbd, sd, true);
 
       // Out: the accumulators hold Y^T tiles (lane: query row l16, 4
-      // consecutive p of P tile pt in lane group g4). For a pair of P tiles,
-      // v_permlane16_swap exchanges the halves of lane groups so that each
-      // lane holds 8 consecutive p of its token: group g4 gets
-      // p = 32q + 16 (g4 & 1) + 8 (g4 >> 1) .. + 7, stored as one 16-byte
-      // piece (rows past the chunk's length fall outside the buffer range and
-      // are dropped).
+      // consecutive p of P tile pt in lane group g4).
 #pragma unroll
-      for (int hd = 0; hd < 2; ++hd) {
-        const rsrc_t ry = make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2));
-        const uint32_t row = (uint32_t)((it * 16 + l16) * ldx);
-#pragma unroll
-        for (int q = 0; q < K::TP / 2; ++q) {
-          const f32x4 lo = acc[hd][2 * q], hi = acc[hd][2 * q + 1];
-          const auto sx = __builtin_amdgcn_permlane16_swap(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(hi[0], hi[1]),
-                                                           false, false);
-          const auto sy = __builtin_amdgcn_permlane16_swap(pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[2], hi[3]),
-                                                           false, false);
-          const u32x4 v = {sx[0], sy[0], sx[1], sy[1]};
-          buf_store16(v, ry, (row + 32 * q + 16 * (g4 & 1) + 8 * (g4 >> 1)) * 2);
-        }
-        if (K::TP % 2) {   // a single P tile (P = 16): 8-byte pieces
-          const f32x4 lo = acc[hd][K::TP - 1];
-          const u32x2 v = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3])};
-          buf_store8(v, ry, (row + (K::TP - 1) * 16 + 4 * g4) * 2);
-        }
-      }
+      for (int hd = 0; hd < 2; ++hd)
+        store_yT<K::TP, GATE>(acc[hd], make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow, g4,
+                              zp[hd]);
     } else {
       load_x(nx);
       load_c(nx);
@@ -821,9 +875,12 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
                                                              const float* __restrict__ C,
                                                              const int4* __restrict__ table,
                                                              const float* __restrict__ cs,
+                                                             const float* __restrict__ ck,
                                                              const float* __restrict__ start,
-                                                             float* __restrict__ Y, int H, int G, int P,
-                                                             int N, int Q) {
+                                                             float* __restrict__ Y,
+                                                             const float* __restrict__ Z,
+                                                             const float* __restrict__ Dskip, int H, int G,
+                                                             int P, int N, int Q) {
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long slot = unit / H;
@@ -837,9 +894,15 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
   float* bj = ci + IB * N;         // [IB][N]
   float* xj = bj + IB * N;         // [IB][P]
   float* m = xj + IB * P;          // [IB][IB]
-  float* csl = m + IB * IB;        // [Q]
+  float* csl = m + IB * IB;        // [Q] cs
+  float* ckl = csl + Q;            // [Q] key-side exponent ck
   const float* csr = cs + (slot * H + h) * (long)Q;
-  for (int i = threadIdx.x; i < Q; i += 256) csl[i] = csr[i];
+  const float* ckr = ck + (slot * H + h) * (long)Q;
+  for (int i = threadIdx.x; i < Q; i += 256) {
+    csl[i] = csr[i];
+    ckl[i] = ckr[i];
+  }
+  const float Dh = Dskip ? Dskip[h] : 0.f;
   const long tok0 = rec.tok0;
   const float* sth = start + (slot * H + h) * (long)(P * N);
   constexpr int kMaxPer = IB * 128 / 256;  // IB*P <= 4096 outputs per block
@@ -883,7 +946,7 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
         if (j0 + j <= i0 + i && i < ni && j < nj) {
           float s = 0.f;
           for (int n = 0; n < N; ++n) s = fmaf(ci[i * N + n], bj[j * N + n], s);
-          v = s * fast_exp2(csl[i0 + i] - csl[j0 + j]);
+          v = s * fast_exp2(csl[i0 + i] - ckl[j0 + j]) + (j0 + j == i0 + i ? Dh : 0.f);
         }
         m[idx] = v;
       }
@@ -904,7 +967,8 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
       const int e = threadIdx.x + 256 * k;
       if (k < per && e < IB * P) {
         const int i = e / P, p = e % P;
-        if (i < ni) Y[((tok0 + i0 + i) * H + h) * P + p] = acc[k];
+        const long o = ((tok0 + i0 + i) * H + h) * P + p;
+        if (i < ni) Y[o] = Z ? acc[k] * silu_f32(Z[o]) : acc[k];
       }
     }
   }
@@ -912,13 +976,13 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
 
 // ----------------------------------------------------------------------------
 
-template <int P, int N>
+template <int P, int N, bool GATE>
 static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
-                                   const Workspace& ws, hipStream_t stream) {
+                                   const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
   if constexpr (pair_shape(P, N)) {
     if (chunk_scan_pair_fits(P, N, d.Q, d.H, d.G)) {
       const size_t lds = chunk_scan_pair_lds_bytes(P, N, d.Q);
-      auto kern = chunk_scan_pair_kernel<P, N>;
+      auto kern = chunk_scan_pair_kernel<P, N, GATE>;
       if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -926,14 +990,14 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
       }
       hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(kScanThreads), lds, stream,
                          reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
-                         reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs,
-                         reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y), d.H,
-                         d.G, d.Q);
+                         reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
+                         reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
+                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q);
       return hipGetLastError();
     }
   }
   const size_t lds = chunk_scan_bf16_lds_bytes(P, N, d.Q);
-  auto kern = d.Q > 128 ? chunk_scan_bf16_kernel<P, N, 2> : chunk_scan_bf16_kernel<P, N, 1>;
+  auto kern = d.Q > 128 ? chunk_scan_bf16_kernel<P, N, 2, GATE> : chunk_scan_bf16_kernel<P, N, 1, GATE>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -941,28 +1005,35 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * d.H)), dim3(kScanThreads), lds, stream,
                      reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
-                     reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs,
-                     reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y), d.H,
-                     d.G, d.Q);
+                     reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
+                     reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
+                     reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q);
   return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_scan_gate(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
+                                   const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
+  return m2.z ? launch_scan_bf16<P, N, true>(d, X, B, C, Y, ws, stream, m2)
+              : launch_scan_bf16<P, N, false>(d, X, B, C, Y, ws, stream, m2);
 }
 
 template <int P>
 static hipError_t dispatch_scan_n(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
-                                  const Workspace& ws, hipStream_t stream) {
+                                  const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
   switch (d.N) {
-    case 32: return launch_scan_bf16<P, 32>(d, X, B, C, Y, ws, stream);
-    case 64: return launch_scan_bf16<P, 64>(d, X, B, C, Y, ws, stream);
-    case 128: return launch_scan_bf16<P, 128>(d, X, B, C, Y, ws, stream);
-    case 256: return launch_scan_bf16<P, 256>(d, X, B, C, Y, ws, stream);
+    case 32: return launch_scan_gate<P, 32>(d, X, B, C, Y, ws, stream, m2);
+    case 64: return launch_scan_gate<P, 64>(d, X, B, C, Y, ws, stream, m2);
+    case 128: return launch_scan_gate<P, 128>(d, X, B, C, Y, ws, stream, m2);
+    case 256: return launch_scan_gate<P, 256>(d, X, B, C, Y, ws, stream, m2);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
-                             const Workspace& ws, hipStream_t stream) {
+                             const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
   if (!d.bf16) {
-    const size_t lds = ((size_t)32 * (2 * d.N + d.P) + 32 * 32 + d.Q) * 4;
+    const size_t lds = ((size_t)32 * (2 * d.N + d.P) + 32 * 32 + 2 * d.Q) * 4;
     if (lds > 64 * 1024) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_scan_f32_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -970,16 +1041,16 @@ hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, con
     }
     hipLaunchKernelGGL(chunk_scan_f32_kernel, dim3((unsigned)(d.nslots * d.H)), dim3(256), lds, stream,
                        reinterpret_cast<const float*>(X), reinterpret_cast<const float*>(B),
-                       reinterpret_cast<const float*>(C), ws.table, ws.cs,
-                       reinterpret_cast<const float*>(ws.start_states), reinterpret_cast<float*>(Y), d.H, d.G,
-                       d.P, d.N, d.Q);
+                       reinterpret_cast<const float*>(C), ws.table, ws.cs, ws.ck,
+                       reinterpret_cast<const float*>(ws.start_states), reinterpret_cast<float*>(Y),
+                       reinterpret_cast<const float*>(m2.z), m2.D, d.H, d.G, d.P, d.N, d.Q);
     return hipGetLastError();
   }
   switch (d.P) {
-    case 16: return dispatch_scan_n<16>(d, X, B, C, Y, ws, stream);
-    case 32: return dispatch_scan_n<32>(d, X, B, C, Y, ws, stream);
-    case 64: return dispatch_scan_n<64>(d, X, B, C, Y, ws, stream);
-    case 128: return dispatch_scan_n<128>(d, X, B, C, Y, ws, stream);
+    case 16: return dispatch_scan_n<16>(d, X, B, C, Y, ws, stream, m2);
+    case 32: return dispatch_scan_n<32>(d, X, B, C, Y, ws, stream, m2);
+    case 64: return dispatch_scan_n<64>(d, X, B, C, Y, ws, stream, m2);
+    case 128: return dispatch_scan_n<128>(d, X, B, C, Y, ws, stream, m2);
     default: return hipErrorInvalidValue;
   }
 }

@@ -10,6 +10,12 @@
 // same right factor for a longer block, which the chunk-scan stage refines
 // chunk by chunk.
 //
+// Key-side weights: the weight of token j is exp2(tail_j) times the token's
+// input scale. The exponent is read from `ck`, which equals the cumulative
+// decay cs for plain calls and cs_j - log2(dt_j) for the Mamba-2 block's call,
+// whose input is x * dt (paper card, Paper vs code item 7): the step size
+// rides in the weight, so x itself is staged unscaled.
+//
 // bf16 path: one workgroup of 8 waves per (block, head). Token rows of X and B
 // are staged into LDS as they lie in HBM (token-major) through registers,
 // prefetching the next 128 rows while the current ones are multiplied; the
@@ -49,8 +55,8 @@ size_t chunk_state_bf16_lds_bytes(int P, int N) {
 template <int P, int N>
 __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk_state_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const int4* __restrict__ ctable,
-    const int4* __restrict__ btable, const float* __restrict__ cs, float* __restrict__ bstates,
-    float* __restrict__ bdecay, int H, int G, int Q) {
+    const int4* __restrict__ btable, const float* __restrict__ cs, const float* __restrict__ ck,
+    float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q) {
   using K = StateCfg<P, N>;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
     const int rows = valid ? r.len - r0 : 0;
     const rsrc_t rb = make_rsrc(B + (((long)r.tok0 + r0) * G + g) * N, (uint32_t)(rows * ldb * 2));
     const rsrc_t rx = make_rsrc(X + (((long)r.tok0 + r0) * H + h) * P, (uint32_t)(rows * ldx * 2));
-    const rsrc_t rc = make_rsrc(cs + (slot * H + h) * (long)Q + r0, valid ? (uint32_t)((Q - r0) * 4) : 0u);
+    const rsrc_t rc = make_rsrc(ck + (slot * H + h) * (long)Q + r0, valid ? (uint32_t)((Q - r0) * 4) : 0u);
 #pragma unroll
     for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(rb, boff[u]);
 #pragma unroll
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
     const long slot = blk.slot0 + c;
     const float a_last = lastcs[c];
     prefix += a_last;
-    const float shift = (total - prefix) + a_last;  // weight of row j: exp2(shift - cs_j)
+    const float shift = (total - prefix) + a_last;  // weight of row j: exp2(shift - ck_j)
     const SlotRec cur = rec;
     for (int r0 = 0; r0 < cur.len; r0 += kPassRows) {
       const int rows = min(kPassRows, cur.len - r0);
@@ -200,6 +206,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
                                                               const float* __restrict__ B,
                                                               const int4* __restrict__ table,
                                                               const float* __restrict__ cs,
+                                                              const float* __restrict__ ck,
                                                               float* __restrict__ states,
                                                               float* __restrict__ bdecay, int H, int G,
                                                               int P, int N, int Q) {
@@ -213,8 +220,8 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
   extern __shared__ float sm[];
   float* xs = sm;            // [JB][P], scaled by the decay to the chunk end
   float* bs = sm + JB * P;   // [JB][N]
-  const float* csr = cs + (slot * H + h) * (long)Q;
-  const float cs_last = csr[Q - 1];
+  const float* ckr = ck + (slot * H + h) * (long)Q;
+  const float cs_last = cs[(slot * H + h) * (long)Q + Q - 1];
   if (threadIdx.x == 0) bdecay[slot * H + h] = cs_last;
   const int PN = P * N;
   constexpr int kPer = 8;  // outputs per thread per pass
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
       __syncthreads();
       for (int idx = threadIdx.x; idx < JB * P; idx += 256) {
         const int j = idx / P, p = idx % P;
-        xs[idx] = j < nb ? X[((tok + j) * H + h) * P + p] * fast_exp2(cs_last - csr[j0 + j]) : 0.f;
+        xs[idx] = j < nb ? X[((tok + j) * H + h) * P + p] * fast_exp2(cs_last - ckr[j0 + j]) : 0.f;
       }
       for (int idx = threadIdx.x; idx < JB * N; idx += 256) {
         const int j = idx / N, n = idx % N;
@@ -269,7 +276,7 @@ static hipError_t launch_state_bf16(const FwdDims& d, const void* X, const void*
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * d.H)), dim3(kStateThreads), lds, stream,
                      reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B), ws.table,
-                     ws.btable, ws.cs, ws.bstates, ws.bdecay, d.H, d.G, d.Q);
+                     ws.btable, ws.cs, ws.ck, ws.bstates, ws.bdecay, d.H, d.G, d.Q);
   return hipGetLastError();
 }
 
@@ -291,7 +298,7 @@ hipError_t launch_chunk_state(const FwdDims& d, const void* X, const void* B, co
     const size_t lds = (size_t)32 * (d.P + d.N) * 4;
     hipLaunchKernelGGL(chunk_state_f32_kernel, dim3((unsigned)(d.nslots * d.H)), dim3(256), lds, stream,
                        reinterpret_cast<const float*>(X), reinterpret_cast<const float*>(B), ws.table, ws.cs,
-                       ws.bstates, ws.bdecay, d.H, d.G, d.P, d.N, d.Q);
+                       ws.ck, ws.bstates, ws.bdecay, d.H, d.G, d.P, d.N, d.Q);
     return hipGetLastError();
   }
   switch (d.P) {

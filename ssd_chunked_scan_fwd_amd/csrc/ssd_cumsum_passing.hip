@@ -20,6 +20,13 @@ namespace ssd {
 // (16 waves) writes the inclusive prefix sum over the chunk, scaled by log2(e) so that
 // later stages use exp2. Positions past the chunk's length repeat the chunk
 // total exactly.
+//
+// The Mamba-2 block's call (dt != null) discretises first, per token and head
+// (paper card Method 6 block sketch; Paper vs code items 7-8): the step size
+// dt' = softplus(dt + dt_bias) goes into LDS, log a = dt' A with
+// A = -exp(A_log) is scanned as above, and the key-side exponent
+// ck_j = cs_j - log2(dt'_j) is written beside cs, so that every later weight
+// exp2(. - ck_j) carries the input scale dt'_j with it.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, long x, int span) {
   // base_s = floor(cu[s]/span) + s is strictly increasing in s: the last s with base_s <= x.
@@ -32,13 +39,20 @@ __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, l
   return lo;
 }
 
+// log(1 + e^v); beyond v = 20 the correction log1p(e^-v) < 3e-9 is below fp32 resolution.
+__device__ __forceinline__ float softplus_f32(float v) { return v > 20.f ? v : log1pf(expf(v)); }
+
 __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const float* __restrict__ la,
                                                            const int32_t* __restrict__ cu, int S,
                                                            int T, int H, int Q, int Gs, long slots_per_row,
                                                            long blocks_per_row, int4* __restrict__ table,
                                                            int4* __restrict__ btable,
-                                                           float* __restrict__ cs) {
-  extern __shared__ float tile[];  // [Q][H + 1] log_a of the chunk, token-major
+                                                           float* __restrict__ cs,
+                                                           const float* __restrict__ dt,
+                                                           const float* __restrict__ dt_bias,
+                                                           const float* __restrict__ A_log,
+                                                           float* __restrict__ ck) {
+  extern __shared__ float tile[];  // [Q][H + 1] log_a (or dt') of the chunk, token-major
   const int row = blockIdx.y;
   const long x = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -93,19 +107,27 @@ __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const float* __restr
   if (threadIdx.x == 0) table[slot] = make_int4(seq, tok0, len, kidx);
   if (len <= 0) return;
 
-  // The chunk's log_a rows are contiguous: read them coalesced into LDS.
+  // The chunk's rows are contiguous: read them coalesced into LDS.
+  const bool m2 = dt != nullptr;
   const int HP = H + 1;
-  const float* src = la + (long)tok0 * H;
-  for (int idx = threadIdx.x; idx < len * H; idx += 1024) tile[(idx / H) * HP + idx % H] = src[idx];
+  const float* src = (m2 ? dt : la) + (long)tok0 * H;
+  for (int idx = threadIdx.x; idx < len * H; idx += 1024) {
+    float v = src[idx];
+    if (m2) v = softplus_f32(v + (dt_bias ? dt_bias[idx % H] : 0.f));
+    tile[(idx / H) * HP + idx % H] = v;
+  }
   __syncthreads();
 
   for (int h = wave; h < H; h += 16) {
+    const float A = m2 ? -expf(A_log[h]) : 1.f;
     float carry = 0.f;  // inclusive sum up to the last valid token seen so far
     float* out = cs + (slot * H + h) * (long)Q;
+    float* outk = m2 ? ck + (slot * H + h) * (long)Q : nullptr;
     for (int jb = 0; jb < Q; jb += 64) {
       const int j = jb + lane;
       if (jb < len) {
-        float v = (j < len) ? tile[j * HP + h] : 0.f;
+        const float t = (j < len) ? tile[j * HP + h] : 0.f;  // log a, or dt'
+        float v = m2 ? t * A : t;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
           const float u = __shfl_up(v, d);
@@ -113,16 +135,21 @@ __global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const float* __restr
         }
         v += carry;
         carry = __shfl(v, min(len - jb, 64) - 1);
-        if (j < Q) out[j] = (j < len ? v : carry) * kLog2e;
+        if (j < Q) {
+          const float c = (j < len ? v : carry) * kLog2e;
+          out[j] = c;
+          if (m2) outk[j] = j < len ? c - log2f(t) : c;
+        }
       } else if (j < Q) {
         out[j] = carry * kLog2e;
+        if (m2) outk[j] = carry * kLog2e;
       }
     }
   }
 }
 
 hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32_t* cu,
-                               const Workspace& ws, hipStream_t stream) {
+                               const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
   const long gx = d.slots_per_row > d.blocks_per_row ? d.slots_per_row : d.blocks_per_row;
   const size_t lds = (size_t)d.Q * (d.H + 1) * sizeof(float);
   if (lds > 64 * 1024) {
@@ -132,7 +159,8 @@ hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32
   }
   dim3 grid((unsigned)gx, (unsigned)d.batch);
   hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(1024), lds, stream, log_a, cu, d.num_seqs, d.T, d.H, d.Q,
-                     d.state_block, d.slots_per_row, d.blocks_per_row, ws.table, ws.btable, ws.cs);
+                     d.state_block, d.slots_per_row, d.blocks_per_row, ws.table, ws.btable, ws.cs, m2.dt,
+                     m2.dt_bias, m2.A_log, ws.ck);
   return hipGetLastError();
 }
 
@@ -227,7 +255,10 @@ hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float
 // ssd_step: one decode step. One workgroup per (row, head); N/4 consecutive
 // lanes share a state row p, each owning 4 consecutive n. The state is read
 // and written once (fp32); y[p] = sum_n state'[p][n] C[n] is reduced across
-// the lanes of the row.
+// the lanes of the row. The Mamba-2 block's step (dt != null) discretises
+// first, dt' = softplus(dt + dt_bias), a = exp(dt' A) with A = -exp(A_log),
+// feeds x dt' into the state, and finishes y with the skip D x and the gate
+// silu(z) (paper card Method 6 block sketch; Paper vs code items 3, 7).
 // ----------------------------------------------------------------------------
 template <bool BF16>
 __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state,
@@ -235,7 +266,12 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
                                                        const float* __restrict__ la,
                                                        const void* __restrict__ Bv,
                                                        const void* __restrict__ Cv,
-                                                       void* __restrict__ y, int H, int G, int P, int N) {
+                                                       void* __restrict__ y, int H, int G, int P, int N,
+                                                       const float* __restrict__ dt,
+                                                       const float* __restrict__ dt_bias,
+                                                       const float* __restrict__ A_log,
+                                                       const float* __restrict__ Dskip,
+                                                       const void* __restrict__ zv) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int g = h / (H / G);
@@ -246,7 +282,15 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
   const long bh = (long)b * H + h;
   const long bg = (long)b * G + g;
   float* st = state + bh * (long)P * N;
-  const float a = fast_exp2(la[bh] * kLog2e);
+  float a, xscale = 1.f, Dh = 0.f;
+  if (dt) {
+    const float dtp = softplus_f32(dt[bh] + (dt_bias ? dt_bias[h] : 0.f));
+    a = fast_exp2(dtp * -expf(A_log[h]) * kLog2e);
+    xscale = dtp;
+    Dh = Dskip ? Dskip[h] : 0.f;
+  } else {
+    a = fast_exp2(la[bh] * kLog2e);
+  }
 
   float bb[4], cc[4];
   if (BF16) {
@@ -264,16 +308,23 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
   for (int p = p0; p < P; p += rpp) {
     const float xp = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[bh * P + p])
                           : reinterpret_cast<const float*>(x)[bh * P + p];
+    const float xs = xp * xscale;
     f32x4* sp = reinterpret_cast<f32x4*>(st + (long)p * N + 4 * c4);
     f32x4 s = *sp;
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s[i] = a * s[i] + xp * bb[i];
+      s[i] = a * s[i] + xs * bb[i];
       part += s[i] * cc[i];
     }
     *sp = s;
     for (int off = tpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    part += Dh * xp;
+    if (zv) {
+      const float zp = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(zv)[bh * P + p])
+                            : reinterpret_cast<const float*>(zv)[bh * P + p];
+      part *= silu_f32(zp);
+    }
     if (c4 == 0) {
       if (BF16) reinterpret_cast<uint16_t*>(y)[bh * P + p] = f32_to_bf16(part);
       else reinterpret_cast<float*>(y)[bh * P + p] = part;
@@ -283,14 +334,14 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
 
 hipError_t launch_ssd_step(int batch, int H, int G, int P, int N, int bf16, float* state,
                            const void* x, const float* log_a, const void* B, const void* C, void* y,
-                           hipStream_t stream) {
+                           hipStream_t stream, const Mamba2Args& m2) {
   dim3 grid((unsigned)H, (unsigned)batch);
   if (bf16) {
     hipLaunchKernelGGL(ssd_step_kernel<true>, grid, dim3(256), 0, stream, state, x, log_a, B, C, y, H, G,
-                       P, N);
+                       P, N, m2.dt, m2.dt_bias, m2.A_log, m2.D, m2.z);
   } else {
     hipLaunchKernelGGL(ssd_step_kernel<false>, grid, dim3(256), 0, stream, state, x, log_a, B, C, y, H,
-                       G, P, N);
+                       G, P, N, m2.dt, m2.dt_bias, m2.A_log, m2.D, m2.z);
   }
   return hipGetLastError();
 }

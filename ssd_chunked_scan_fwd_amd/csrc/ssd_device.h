@@ -37,6 +37,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// silu(v) = v / (1 + e^-v), with the hardware exp2 and reciprocal (a few ulp
+// of fp32); v far below zero gives -0 through 1 / inf.
+__device__ __forceinline__ float silu_f32(float v) {
+  return v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-v * kLog2e));
+}
+
 // One 16x16x32 bf16 MFMA with fp32 accumulation (gfx950).
 // A: lane l holds row (l % 16), 8 consecutive k of slot group (l / 16).
 // B: lane l holds column (l % 16), the same 8 k. D: lane l holds column
@@ -67,6 +73,9 @@ __device__ __forceinline__ float buf_load_f32(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ uint16_t buf_load_u16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 __device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);

@@ -24,23 +24,36 @@ struct FwdDims {
 struct Workspace {
   int4* table;            // [nslots] chunk records
   int4* btable;           // [nblocks] state-block records
-  float* cs;              // [nslots][H][Q]
+  float* cs;              // [nslots][H][Q] cumulative log2 decay, restarted per chunk
+  float* ck;              // [nslots][H][Q] exponent of the key-side weights: cs itself for plain
+                          // calls, cs_j - log2(dt_j) for the Mamba-2 block's call
   float* bdecay;          // [nblocks][H] total log2 decay of each block
   float* bstates;         // [nblocks][H][P][N] right factors of each block
   void* start_states;     // [nblocks][H][P][N] state entering each block
 };
 
+// The Mamba-2 block's per-head parameters and gate (device pointers). With dt
+// set, the cumsum stage takes raw step sizes instead of log a; D and z shape
+// the chunk-scan output (null: no skip, no gate).
+struct Mamba2Args {
+  const float* dt = nullptr;       // [rows * T][H] raw step sizes
+  const float* dt_bias = nullptr;  // [H] or null (zero)
+  const float* A_log = nullptr;    // [H], A = -exp(A_log)
+  const float* D = nullptr;        // [H] or null
+  const void* z = nullptr;         // like X, or null
+};
+
 hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32_t* cu,
-                               const Workspace& ws, hipStream_t stream);
+                               const Workspace& ws, hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});
 hipError_t launch_chunk_state(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
                               hipStream_t stream);
 hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float* init, float* final_state,
                                 const Workspace& ws, hipStream_t stream);
 hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
-                             const Workspace& ws, hipStream_t stream);
+                             const Workspace& ws, hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});
 hipError_t launch_ssd_step(int batch, int H, int G, int P, int N, int bf16, float* state,
                            const void* x, const float* log_a, const void* B, const void* C, void* y,
-                           hipStream_t stream);
+                           hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});
 
 // Bytes of dynamic LDS the bf16 kernels need (host-side checks).
 size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q);

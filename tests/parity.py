@@ -6,6 +6,15 @@ Tolerances (written here once, used by every parity test):
     max_i |d_i| / rms(ref) <= 5e-2 (the per-element bound on unit-scale output,
     with the output scaled by its RMS).
 Both are applied separately to Y and to the final states.
+
+Gated outputs (the Mamba-2 block's y = u * silu(z), u = SSM output + skip):
+the gate scales each element by s_i = silu(z_i), which stretches the tails of
+the output (|y_i| far above rms(y) wherever |s_i| is large), so the output's own
+bf16 rounding alone can exceed 5e-2 rms(y). The unit scale of element i is
+carried through the gate instead: with r = rms(u_ref),
+  * bf16: ||d||_2 / ||ref||_2 <= 2e-2 and max_i |d_i| / (|s_i| r + |ref_i|) <= 5e-2;
+  * fp32: max_i |d_i| / (|s_i| r + |ref_i|) <= 1e-4.
+With s = 1 this is the ungated bar with an allowance relative to |ref_i|.
 """
 from __future__ import annotations
 
@@ -47,3 +56,28 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 def dtype_name(t: torch.Tensor) -> str:
     return "fp32" if t.dtype == torch.float32 else "bf16"
+
+
+def gated_errors(gpu, ref, ref_ungated, s):
+    g = np.asarray(gpu, np.float64).ravel()
+    r = np.asarray(ref, np.float64).ravel()
+    u = np.asarray(ref_ungated, np.float64).ravel()
+    sc = np.abs(np.asarray(s, np.float64).ravel())
+    d = np.abs(g - r)
+    ru = float(np.sqrt(np.mean(u * u))) if u.size else 0.0
+    den = sc * ru + np.abs(r) + 1e-30
+    return dict(
+        rel_l2=float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)),
+        max_gated=float(np.max(d / den)) if d.size else 0.0,
+        finite=bool(np.all(np.isfinite(g))),
+    )
+
+
+def assert_close_gated(gpu, ref, ref_ungated, s, dtype: str, what: str = ""):
+    e = gated_errors(gpu, ref, ref_ungated, s)
+    assert e["finite"], f"{what}: non-finite values"
+    if dtype == "fp32":
+        assert e["max_gated"] <= FP32_MAXREL, f"{what}: {e}"
+    else:
+        assert e["rel_l2"] <= BF16_RELL2 and e["max_gated"] <= BF16_MAXABS_UNIT, f"{what}: {e}"
+    return e

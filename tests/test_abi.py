@@ -22,7 +22,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ssd_[a-z_]+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ssd_[a-z_0-9]+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_binding_exports():
@@ -35,13 +35,13 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", binding.library_path()], capture_output=True, text=True,
                          check=True).stdout
-    exported = set(re.findall(r"\sT\s(ssd_[a-z_]+)$", out, flags=re.M))
+    exported = set(re.findall(r"\sT\s(ssd_[a-z_0-9]+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
 
 
 def test_abi_version_and_status_strings():
     L = ssd.lib()
-    assert L.ssd_abi_version() == 1
+    assert L.ssd_abi_version() == 2
     for code, name in binding.STATUS.items():
         assert L.ssd_status_string(code).decode() == name
 
@@ -69,15 +69,18 @@ def test_workspace_size_matches_layout():
     assert st == OK
     slots = 16384 // 128
     PN = 64 * 128
-    expect = _align(slots * 16) * 2 + _align(slots * 32 * 128 * 4) + _align(slots * 32 * 4) + \
+    expect = _align(slots * 16) * 2 + _align(slots * 32 * 128 * 4) * 2 + _align(slots * 32 * 4) + \
         _align(slots * 32 * PN * 4) + _align(slots * 32 * PN * 2)
     assert n == expect
     L = ssd.layout(sh, 128, 1)
     assert L.slots_per_row == slots and L.nslots == slots and L.nblocks == slots and L.total_bytes == n
+    # the key-side exponent (Mamba-2 calls) follows cumsum, same size
+    assert L.key_cumsum_offset - L.cumsum_offset == _align(slots * 32 * 128 * 4)
+    assert L.block_decay_offset - L.key_cumsum_offset == _align(slots * 32 * 128 * 4)
     # state blocks of 4 chunks: a quarter of the block arrays
     L4 = ssd.layout(sh, 128, 4)
     assert L4.nslots == slots and L4.nblocks == slots // 4
-    assert L4.total_bytes == _align(slots * 16) + _align(slots // 4 * 16) + _align(slots * 32 * 128 * 4) + \
+    assert L4.total_bytes == _align(slots * 16) + _align(slots // 4 * 16) + _align(slots * 32 * 128 * 4) * 2 + \
         _align(slots // 4 * 32 * 4) + _align(slots // 4 * 32 * PN * 4) + _align(slots // 4 * 32 * PN * 2)
     # packed rows: floor(T/Q) + S chunk slots, floor(T/(Gs*Q)) + S block slots
     sp = shape(seqlen=32768, nheads=80, num_seqs=7)
@@ -196,3 +199,41 @@ def test_binding_refuses_host_tensors():
     X = torch.zeros(1, 64, 2, 16)
     with pytest.raises(ValueError):
         ssd.fwd(X, torch.zeros(1, 64, 2), torch.zeros(1, 64, 1, 16), torch.zeros(1, 64, 1, 16), chunk=32)
+
+
+def test_mamba2_entry_points_validate():
+    L = ssd.lib()
+    sh = shape()
+    _, need = ws_bytes(sh, 128, 0)
+    # X, dt, dt_bias, A_log, D, z, B, C, cu, init, chunk, gs, Y, final, shape, ws, bytes, stream
+    args = [FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, None, None, 128, 0, FAKE, None, ctypes.byref(sh), FAKE,
+            need, None]
+    for i in (0, 1, 3, 6, 7, 12, 15):  # X, dt, A_log, B, C, Y, workspace are required
+        a = list(args)
+        a[i] = None
+        assert L.ssd_fwd_mamba2(*a) == INVALID, i
+    a = list(args)
+    a[16] = need - 1
+    assert L.ssd_fwd_mamba2(*a) == WS_SMALL
+    a = list(args)
+    a[10] = 48
+    assert L.ssd_fwd_mamba2(*a) == UNSUPPORTED
+    st = shape(batch=64, nheads=80)
+    # state, x, dt, dt_bias, A_log, D, z, B, C, y, shape, stream
+    sargs = [FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, FAKE, ctypes.byref(st), None]
+    for i in (0, 1, 2, 4, 7, 8, 9):
+        a = list(sargs)
+        a[i] = None
+        assert L.ssd_step_mamba2(*a) == INVALID, i
+    bad = shape(batch=64, nheads=80, headdim=48)
+    a = list(sargs)
+    a[10] = ctypes.byref(bad)
+    assert L.ssd_step_mamba2(*a) == UNSUPPORTED
+
+
+def test_mamba2_binding_checks_parameters():
+    import torch
+    X = torch.zeros(1, 64, 2, 16)
+    with pytest.raises(ValueError):
+        ssd.fwd_mamba2(X, torch.zeros(1, 64, 2), torch.zeros(2), torch.zeros(1, 64, 1, 16), torch.zeros(1, 64, 1, 16),
+                       chunk=32)
