@@ -9,9 +9,11 @@ accumulation; inputs are seeded synthetic and resident in HBM before timing.
 Prints ONE JSON line with the headline throughput (tokens/s), the roofline of
 the dominant kernel (its algorithmic bytes / its average launch time, timed with
 HIP events on the launch stream), per-stage times, the decode-step throughput,
-and the fp64 CPU oracle timed on this host as a baseline.
+the Mamba-2 block's call on the same shape (ssd_fwd_mamba2: raw step sizes,
+dt_bias, A_log, the D skip and the silu(z) gate) and its decode step, and the
+fp64 CPU oracle timed on this host as a baseline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-mamba2]
 """
 from __future__ import annotations
 
@@ -114,6 +116,7 @@ def main() -> int:
     ap.add_argument("--stage-reps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba-2 block-call timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--state-block", type=int, default=0, help="chunks per state block (0: library default)")
@@ -241,6 +244,34 @@ def main() -> int:
         "pipeline_hbm_frac": round(pipeline_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
+    if not args.no_mamba2:
+        # The Mamba-2 block's call on the same shape: raw step sizes, dt_bias,
+        # A_log, the D skip and the silu(z) gate, all inside the four kernels.
+        log(f"[bench] mamba2 block call on {w.name}: {args.steps} steps")
+        m = synth.make_mamba2_inputs(w.batch, w.T, w.H, w.P, w.N, w.G, w.torch_dtype, w.seed)
+        mX, mdt, mbias, mAl, mD, mz, mB, mC = (m[k].to(dev) for k in ("X", "dt", "dt_bias", "A_log", "D", "z", "B",
+                                                                      "C"))
+
+        def mstep():
+            ssd.fwd_mamba2(mX, mdt, mAl, mB, mC, dt_bias=mbias, D=mD, z=mz, chunk=w.Q, state_block=ws.state_block,
+                           Y=Y, final_state=fin, workspace=ws)
+
+        for _ in range(min(args.warmup, 50)):
+            mstep()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(args.steps):
+            mstep()
+        b.record(stream)
+        torch.cuda.synchronize()
+        m_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        out["mamba2"] = {"workload": w.name + " (Mamba-2 call: dt, dt_bias, A_log, D, z)", "steps": args.steps,
+                         "ms_per_step": round(m_ms, 5), "event_ms_per_step": round(a.elapsed_time(b) / args.steps, 5),
+                         "tokens_per_s": round(tokens / (m_ms * 1e-3), 1)}
+        del mX, mdt, mbias, mAl, mD, mz, mB, mC
+
     if not args.no_decode:
         wd = synth.WORKLOADS["decode-b64-H80-N128"]
         nsteps = min(args.decode_steps, wd.steps)
@@ -266,7 +297,24 @@ def main() -> int:
                          "tokens_per_s": round(wd.batch * nsteps / (dec_ms * 1e-3), 1),
                          "us_per_step": round(dec_ms * 1e3 / nsteps, 3),
                          "gbs_per_step": round(per_step_bytes / (dec_ms * 1e-3 / nsteps) / 1e9, 1)}
-        del xs, las, Bs, Cs, state
+        del xs, las, Bs, Cs
+        if not args.no_mamba2:
+            md = synth.make_mamba2_decode_inputs(wd.batch, nsteps, wd.H, wd.P, wd.N, wd.G, wd.torch_dtype, wd.seed)
+            xs, dts, zs, Bs, Cs = (md[k].to(dev) for k in ("x", "dt", "z", "B", "C"))
+            bias, Al, Dk = (md[k].to(dev) for k in ("dt_bias", "A_log", "D"))
+            state.zero_()
+            for t in range(min(16, nsteps)):
+                ssd.step_mamba2(state, xs[t], dts[t], Al, Bs[t], Cs[t], dt_bias=bias, D=Dk, z=zs[t], y=y)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for t in range(nsteps):
+                ssd.step_mamba2(state, xs[t], dts[t], Al, Bs[t], Cs[t], dt_bias=bias, D=Dk, z=zs[t], y=y)
+            b.record(stream)
+            torch.cuda.synchronize()
+            m_ms = a.elapsed_time(b)
+            out["decode"]["mamba2_us_per_step"] = round(m_ms * 1e3 / nsteps, 3)
+            del xs, dts, zs, Bs, Cs
+        del state
 
     if args.copy_probe > 0:
         n = args.copy_probe * (1 << 20) // 4
