@@ -147,8 +147,11 @@ ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_
 
 /*
  * Forward pass: Y and final states from zero initial states, with the default
- * state block. Runs the four stages below in order on `stream`. final_state
- * may be NULL. The workspace must hold ssd_fwd_workspace_bytes(shape, chunk, 0).
+ * state block. Computes what the four stages below compute, in three launches
+ * on `stream`: the chunk-state launch also writes the records and segment sums
+ * that ssd_chunk_cumsum writes, for every slot that holds a chunk (table rows
+ * of slots that hold no chunk are left as they were). final_state may be NULL.
+ * The workspace must hold ssd_fwd_workspace_bytes(shape, chunk, 0).
  */
 ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void* C,
                    const int32_t* cu_seqlens, int32_t chunk, void* Y, float* final_state,
@@ -173,7 +176,9 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
 
 /*
  * The four stages of ssd_fwd_ex, callable one by one (same arguments, same
- * workspace; each stage reads what the previous stages wrote).
+ * workspace; each stage reads what the previous stages wrote). Run in order,
+ * they give the same Y, final state and workspace contents as ssd_fwd_ex,
+ * bit for bit.
  *
  * ssd_chunk_cumsum -- segment sums of log a: the cumulative log decay
  *   restarted in every chunk, from which the 1-semiseparable mask

@@ -41,7 +41,7 @@ ssd_status check_shape(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
   if (s->dtype == SSD_DTYPE_BF16) {
     if (chunk < 32 || s->dstate < 32) return SSD_ERR_UNSUPPORTED;
     if (ssd::chunk_scan_bf16_lds_bytes(s->headdim, s->dstate, chunk) > ssd::kMaxLdsBytes ||
-        ssd::chunk_state_bf16_lds_bytes(s->headdim, s->dstate) > ssd::kMaxLdsBytes)
+        ssd::chunk_state_bf16_lds_bytes(s->headdim, s->dstate, 16 * 256) > ssd::kMaxLdsBytes)
       return SSD_ERR_UNSUPPORTED;
     // one chunk's rows of X, Y, B or C are addressed as one buffer range of fewer than 2^31 bytes
     if ((int64_t)chunk * s->nheads * s->headdim * 2 > kMaxElems || (int64_t)chunk * s->ngroups * s->dstate * 2 > kMaxElems)
@@ -252,9 +252,10 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
   ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
                           workspace_bytes, &pp);
   if (st != SSD_OK) return st;
+  // Three launches: chunk_state computes the records and segment sums itself.
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = ssd::launch_chunk_cumsum(pp.d, log_a, cu_seqlens, pp.ws, s);
-  if (e == hipSuccess) e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s);
+  const ssd::SegArgs sa = ssd::seg_args(pp.d, log_a, cu_seqlens, ssd::Mamba2Args{});
+  hipError_t e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s, &sa);
   if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, s);
   if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s);
   return hip_status(e);
@@ -285,8 +286,8 @@ ssd_status ssd_fwd_mamba2(const void* X, const float* dt, const float* dt_bias, 
   m2.D = D;
   m2.z = z;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = ssd::launch_chunk_cumsum(pp.d, nullptr, cu_seqlens, pp.ws, s, m2);
-  if (e == hipSuccess) e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s);
+  const ssd::SegArgs sa = ssd::seg_args(pp.d, nullptr, cu_seqlens, m2);
+  hipError_t e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s, &sa);
   if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, s);
   if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s, m2);
   return hip_status(e);

@@ -26,6 +26,7 @@
 // is written in fp32 together with the block's total log2 decay.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_segsum.h"
 #include "ssd_stage.h"
 
 namespace ssd {
@@ -48,20 +49,34 @@ struct StateCfg {
 
 }  // namespace
 
-size_t chunk_state_bf16_lds_bytes(int P, int N) {
-  return ((size_t)kPassRows * lds_pitch(N) + (size_t)kPassRows * lds_pitch(P)) * 2 + 16 * 16 + 16 * 4;
+// The fused form (segment sums computed here) also keeps the key-side
+// exponents of the block's chunks, [Gs * Q] fp32.
+size_t chunk_state_bf16_lds_bytes(int P, int N, int block_tokens) {
+  return ((size_t)kPassRows * lds_pitch(N) + (size_t)kPassRows * lds_pitch(P)) * 2 + 16 * 16 + 16 * 4 +
+         (size_t)block_tokens * 4;
 }
 
-template <int P, int N>
+// FUSED: the workgroup also writes its block's records and the segment sums of
+// its head (the work of chunk_cumsum, for the slots its block covers): head 0
+// writes the records, and wave w takes chunks w, w + 8, ... of the block.
+template <int P, int N, bool FUSED>
 __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk_state_bf16_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const int4* __restrict__ ctable,
-    const int4* __restrict__ btable, const float* __restrict__ cs, const float* __restrict__ ck,
-    float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q) {
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, int4* __restrict__ ctable,
+    int4* __restrict__ btable, float* __restrict__ cs, float* __restrict__ ck,
+    float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q, int Gs, SegArgs sa) {
   using K = StateCfg<P, N>;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long m = unit / H;
-  const BlockRec blk = load_block(btable, m);
+  BlockRec blk;
+  if constexpr (FUSED) {
+    const int row = (int)(m / sa.blocks_per_row);
+    const int4 b = block_record(sa.cu, sa.S, row, m - row * sa.blocks_per_row, Q, Gs, sa.slots_per_row);
+    if (h == 0 && threadIdx.x == 0) btable[m] = b;
+    blk = BlockRec{b.x, b.y, b.z};
+  } else {
+    blk = load_block(btable, m);
+  }
   if (blk.nchunks <= 0) return;
   const int g = h / (H / G);
 
@@ -70,6 +85,7 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
   uint16_t* xw = bs + kPassRows * K::BP;       // [128][XP] X rows times their decay to the block end
   int4* recs = reinterpret_cast<int4*>(xw + kPassRows * K::XP);   // [16] chunk records of the block
   float* lastcs = reinterpret_cast<float*>(recs + 16);             // [16] chunk totals (log2)
+  float* ckl = lastcs + 16;                                        // [Gs][Q] key-side exponents (FUSED)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -93,22 +109,20 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
     xoff[u] = xrow[u] < kPassRows ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
   }
 
-  // The block's chunk records and totals, read once.
+  // The block's chunk records and totals.
   if (tid < blk.nchunks) {
-    recs[tid] = ctable[blk.slot0 + tid];
-    lastcs[tid] = cs[((blk.slot0 + tid) * H + h) * (long)Q + Q - 1];
+    if constexpr (FUSED) {
+      const long slot = blk.slot0 + tid;
+      const int row = (int)(slot / sa.slots_per_row);
+      const int4 r = chunk_record(sa.cu, sa.S, row, slot - row * sa.slots_per_row, sa.T, Q, sa.slots_per_row);
+      recs[tid] = r;
+      if (h == 0) ctable[slot] = r;
+    } else {
+      recs[tid] = ctable[blk.slot0 + tid];
+      lastcs[tid] = cs[((blk.slot0 + tid) * H + h) * (long)Q + Q - 1];
+    }
   }
   __syncthreads();
-  // Total log2 decay of the block; the tail of chunk c is total - (A_0 + .. + A_c).
-  float total = 0.f;
-  for (int c = 0; c < blk.nchunks; ++c) total += lastcs[c];
-
-  f32x4 acc[K::TPW][K::TNW];
-#pragma unroll
-  for (int a = 0; a < K::TPW; ++a)
-#pragma unroll
-    for (int b = 0; b < K::TNW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   // One pass = rows r0 .. r0+127 of chunk c; the next pass is loaded while the
   // current one is multiplied.
   u32x4 pb[K::RB], px[K::RX];
@@ -120,13 +134,14 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
     const int rows = valid ? r.len - r0 : 0;
     const rsrc_t rb = make_rsrc(B + (((long)r.tok0 + r0) * G + g) * N, (uint32_t)(rows * ldb * 2));
     const rsrc_t rx = make_rsrc(X + (((long)r.tok0 + r0) * H + h) * P, (uint32_t)(rows * ldx * 2));
-    const rsrc_t rc = make_rsrc(ck + (slot * H + h) * (long)Q + r0, valid ? (uint32_t)((Q - r0) * 4) : 0u);
 #pragma unroll
     for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(rb, boff[u]);
 #pragma unroll
-    for (int u = 0; u < K::RX; ++u) {
-      px[u] = buf_load16(rx, xoff[u]);
-      pcs[u] = buf_load_f32(rc, xrow[u] < kPassRows ? (uint32_t)(xrow[u] * 4) : kOffNone);
+    for (int u = 0; u < K::RX; ++u) px[u] = buf_load16(rx, xoff[u]);
+    if constexpr (!FUSED) {
+      const rsrc_t rc = make_rsrc(ck + (slot * H + h) * (long)Q + r0, valid ? (uint32_t)((Q - r0) * 4) : 0u);
+#pragma unroll
+      for (int u = 0; u < K::RX; ++u) pcs[u] = buf_load_f32(rc, xrow[u] < kPassRows ? (uint32_t)(xrow[u] * 4) : kOffNone);
     }
   };
 
@@ -136,6 +151,37 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
   };
   SlotRec rec = rec_of(0);
   load_pass(rec, blk.slot0, 0, true);
+  if constexpr (FUSED) {
+    // Segment sums of this head's chunks: to the workspace for the chunk-scan
+    // stage, the key-side exponents to LDS for the weights below.
+    const bool m2 = sa.dt != nullptr;
+    const float A = m2 ? -expf(sa.A_log[h]) : 1.f;
+    const float bias = (m2 && sa.dt_bias) ? sa.dt_bias[h] : 0.f;
+    for (int c = wave; c < blk.nchunks; c += kStateThreads / 64) {
+      const int4 r = recs[c];
+      const long slot = blk.slot0 + c;
+      const float* src = (m2 ? sa.dt : sa.la) + (long)r.y * H + h;
+      const float tot = wave_segsum(
+          [&](int j) {
+            const float v = src[(long)j * H];
+            return m2 ? softplus_f32(v + bias) : v;
+          },
+          r.z, Q, m2, A, cs + (slot * H + h) * (long)Q, m2 ? ck + (slot * H + h) * (long)Q : nullptr, ckl + c * Q,
+          lane);
+      if (lane == 0) lastcs[c] = tot;
+    }
+    __syncthreads();
+  }
+  // Total log2 decay of the block; the tail of chunk c is total - (A_0 + .. + A_c).
+  float total = 0.f;
+  for (int c = 0; c < blk.nchunks; ++c) total += lastcs[c];
+
+  f32x4 acc[K::TPW][K::TNW];
+#pragma unroll
+  for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+    for (int b = 0; b < K::TNW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   float prefix = 0.f;
   for (int c = 0; c < blk.nchunks; ++c) {
     const long slot = blk.slot0 + c;
@@ -153,7 +199,8 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
 #pragma unroll
       for (int u = 0; u < K::RX; ++u) {
         if (xrow[u] < kPassRows) {
-          const float w = xrow[u] < rows ? fast_exp2(shift - pcs[u]) : 0.f;
+          const float kj = FUSED ? ckl[c * Q + min(r0 + xrow[u], Q - 1)] : pcs[u];
+          const float w = xrow[u] < rows ? fast_exp2(shift - kj) : 0.f;
           u32x4 v;
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(px[u][q]) * w, bf16_hi(px[u][q]) * w);
@@ -202,18 +249,32 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
 // fp32 path (plain FMA, fp32 accumulation; one chunk per state block): tokens
 // staged 32 at a time in LDS.
 // ----------------------------------------------------------------------------
+template <bool FUSED>
 __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __restrict__ X,
                                                               const float* __restrict__ B,
-                                                              const int4* __restrict__ table,
-                                                              const float* __restrict__ cs,
-                                                              const float* __restrict__ ck,
+                                                              int4* __restrict__ table,
+                                                              int4* __restrict__ btable,
+                                                              float* __restrict__ cs,
+                                                              float* __restrict__ ck,
                                                               float* __restrict__ states,
                                                               float* __restrict__ bdecay, int H, int G,
-                                                              int P, int N, int Q) {
+                                                              int P, int N, int Q, SegArgs sa) {
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long slot = unit / H;
-  const SlotRec rec = load_slot(table, slot);
+  SlotRec rec;
+  if constexpr (FUSED) {  // records and segment sums of this slot (one chunk per state block)
+    const int row = (int)(slot / sa.slots_per_row);
+    const long x = slot - row * sa.slots_per_row;
+    const int4 r = chunk_record(sa.cu, sa.S, row, x, sa.T, Q, sa.slots_per_row);
+    if (h == 0 && threadIdx.x == 0) {
+      table[slot] = r;
+      btable[slot] = block_record(sa.cu, sa.S, row, x, Q, 1, sa.slots_per_row);
+    }
+    rec = SlotRec{r.x, r.y, r.z, r.w};
+  } else {
+    rec = load_slot(table, slot);
+  }
   if (rec.len <= 0) return;
   const int g = h / (H / G);
   constexpr int JB = 32;
@@ -221,7 +282,30 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
   float* xs = sm;            // [JB][P], scaled by the decay to the chunk end
   float* bs = sm + JB * P;   // [JB][N]
   const float* ckr = ck + (slot * H + h) * (long)Q;
-  const float cs_last = cs[(slot * H + h) * (long)Q + Q - 1];
+  float cs_last;
+  if constexpr (FUSED) {
+    float* ckl = bs + JB * N;  // [Q] key-side exponents
+    __shared__ float tot;
+    if (threadIdx.x < 64) {
+      const bool m2 = sa.dt != nullptr;
+      const float A = m2 ? -expf(sa.A_log[h]) : 1.f;
+      const float bias = (m2 && sa.dt_bias) ? sa.dt_bias[h] : 0.f;
+      const float* src = (m2 ? sa.dt : sa.la) + (long)rec.tok0 * H + h;
+      const float t = wave_segsum(
+          [&](int j) {
+            const float v = src[(long)j * H];
+            return m2 ? softplus_f32(v + bias) : v;
+          },
+          rec.len, Q, m2, A, cs + (slot * H + h) * (long)Q, m2 ? ck + (slot * H + h) * (long)Q : nullptr, ckl,
+          threadIdx.x);
+      if (threadIdx.x == 0) tot = t;
+    }
+    __syncthreads();
+    ckr = ckl;
+    cs_last = tot;
+  } else {
+    cs_last = cs[(slot * H + h) * (long)Q + Q - 1];
+  }
   if (threadIdx.x == 0) bdecay[slot * H + h] = cs_last;
   const int PN = P * N;
   constexpr int kPer = 8;  // outputs per thread per pass
@@ -264,11 +348,11 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
 
 // ----------------------------------------------------------------------------
 
-template <int P, int N>
+template <int P, int N, bool FUSED>
 static hipError_t launch_state_bf16(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
-                                    hipStream_t stream) {
-  const size_t lds = chunk_state_bf16_lds_bytes(P, N);
-  auto kern = chunk_state_bf16_kernel<P, N>;
+                                    hipStream_t stream, const SegArgs& sa) {
+  const size_t lds = chunk_state_bf16_lds_bytes(P, N, FUSED ? d.state_block * d.Q : 0);
+  auto kern = chunk_state_bf16_kernel<P, N, FUSED>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -276,36 +360,49 @@ static hipError_t launch_state_bf16(const FwdDims& d, const void* X, const void*
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * d.H)), dim3(kStateThreads), lds, stream,
                      reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B), ws.table,
-                     ws.btable, ws.cs, ws.ck, ws.bstates, ws.bdecay, d.H, d.G, d.Q);
+                     ws.btable, ws.cs, ws.ck, ws.bstates, ws.bdecay, d.H, d.G, d.Q, d.state_block, sa);
   return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_state_fuse(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
+                                    hipStream_t stream, const SegArgs* seg) {
+  return seg ? launch_state_bf16<P, N, true>(d, X, B, ws, stream, *seg)
+             : launch_state_bf16<P, N, false>(d, X, B, ws, stream, SegArgs{});
 }
 
 template <int P>
 static hipError_t dispatch_state_n(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, const SegArgs* seg) {
   switch (d.N) {
-    case 32: return launch_state_bf16<P, 32>(d, X, B, ws, stream);
-    case 64: return launch_state_bf16<P, 64>(d, X, B, ws, stream);
-    case 128: return launch_state_bf16<P, 128>(d, X, B, ws, stream);
-    case 256: return launch_state_bf16<P, 256>(d, X, B, ws, stream);
+    case 32: return launch_state_fuse<P, 32>(d, X, B, ws, stream, seg);
+    case 64: return launch_state_fuse<P, 64>(d, X, B, ws, stream, seg);
+    case 128: return launch_state_fuse<P, 128>(d, X, B, ws, stream, seg);
+    case 256: return launch_state_fuse<P, 256>(d, X, B, ws, stream, seg);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_chunk_state(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, const SegArgs* seg) {
   if (!d.bf16) {
-    const size_t lds = (size_t)32 * (d.P + d.N) * 4;
-    hipLaunchKernelGGL(chunk_state_f32_kernel, dim3((unsigned)(d.nslots * d.H)), dim3(256), lds, stream,
-                       reinterpret_cast<const float*>(X), reinterpret_cast<const float*>(B), ws.table, ws.cs,
-                       ws.ck, ws.bstates, ws.bdecay, d.H, d.G, d.P, d.N, d.Q);
+    const size_t lds = ((size_t)32 * (d.P + d.N) + (seg ? d.Q : 0)) * 4;
+    auto kern = seg ? chunk_state_f32_kernel<true> : chunk_state_f32_kernel<false>;
+    if (lds > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)(d.nslots * d.H)), dim3(256), lds, stream,
+                       reinterpret_cast<const float*>(X), reinterpret_cast<const float*>(B), ws.table, ws.btable,
+                       ws.cs, ws.ck, ws.bstates, ws.bdecay, d.H, d.G, d.P, d.N, d.Q, seg ? *seg : SegArgs{});
     return hipGetLastError();
   }
   switch (d.P) {
-    case 16: return dispatch_state_n<16>(d, X, B, ws, stream);
-    case 32: return dispatch_state_n<32>(d, X, B, ws, stream);
-    case 64: return dispatch_state_n<64>(d, X, B, ws, stream);
-    case 128: return dispatch_state_n<128>(d, X, B, ws, stream);
+    case 16: return dispatch_state_n<16>(d, X, B, ws, stream, seg);
+    case 32: return dispatch_state_n<32>(d, X, B, ws, stream, seg);
+    case 64: return dispatch_state_n<64>(d, X, B, ws, stream, seg);
+    case 128: return dispatch_state_n<128>(d, X, B, ws, stream, seg);
     default: return hipErrorInvalidValue;
   }
 }

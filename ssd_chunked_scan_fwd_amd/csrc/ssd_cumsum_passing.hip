@@ -8,143 +8,51 @@
 // "Center Factors" step carries states across chunks with a scalar recurrence.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_segsum.h"
 
 namespace ssd {
 
 // ----------------------------------------------------------------------------
-// chunk_cumsum: grid (slot x, row y). Workgroup x locates chunk slot x (packed
-// rows: sequence s owns slots floor(cu[s]/Q) + s + j) and block slot x
-// (sequence s owns block slots floor(cu[s]/(Gs*Q)) + s + j, each block being Gs
-// consecutive chunks) and writes both records. It reads the chunk's log_a
-// rows (contiguous, [len][H]) into LDS, then each wave takes heads in turn and
-// (16 waves) writes the inclusive prefix sum over the chunk, scaled by log2(e) so that
-// later stages use exp2. Positions past the chunk's length repeat the chunk
-// total exactly.
-//
-// The Mamba-2 block's call (dt != null) discretises first, per token and head
-// (paper card Method 6 block sketch; Paper vs code items 7-8): the step size
-// dt' = softplus(dt + dt_bias) goes into LDS, log a = dt' A with
-// A = -exp(A_log) is scanned as above, and the key-side exponent
-// ck_j = cs_j - log2(dt'_j) is written beside cs, so that every later weight
-// exp2(. - ck_j) carries the input scale dt'_j with it.
+// chunk_cumsum: grid (slot x, row y). Workgroup x writes the record of chunk
+// slot x and of state-block slot x (chunk_record, block_record), reads the
+// chunk's log_a rows (contiguous, [len][H]) into LDS, and its 16 waves take
+// heads in turn and write the segment sums (wave_segsum). The Mamba-2 call
+// stages dt' = softplus(dt + dt_bias) instead and also writes ck.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int S, long x, int span) {
-  // base_s = floor(cu[s]/span) + s is strictly increasing in s: the last s with base_s <= x.
-  int lo = 0, hi = S - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    const long base = cu[mid] / span + mid;
-    if (base <= x) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// log(1 + e^v); beyond v = 20 the correction log1p(e^-v) < 3e-9 is below fp32 resolution.
-__device__ __forceinline__ float softplus_f32(float v) { return v > 20.f ? v : log1pf(expf(v)); }
-
-__global__ __launch_bounds__(1024) void chunk_cumsum_kernel(const float* __restrict__ la,
-                                                           const int32_t* __restrict__ cu, int S,
-                                                           int T, int H, int Q, int Gs, long slots_per_row,
-                                                           long blocks_per_row, int4* __restrict__ table,
-                                                           int4* __restrict__ btable,
-                                                           float* __restrict__ cs,
-                                                           const float* __restrict__ dt,
-                                                           const float* __restrict__ dt_bias,
-                                                           const float* __restrict__ A_log,
-                                                           float* __restrict__ ck) {
+__global__ __launch_bounds__(1024) void chunk_cumsum_kernel(SegArgs sa, int H, int Q, int Gs,
+                                                           int4* __restrict__ table, int4* __restrict__ btable,
+                                                           float* __restrict__ cs, float* __restrict__ ck) {
   extern __shared__ float tile[];  // [Q][H + 1] log_a (or dt') of the chunk, token-major
   const int row = blockIdx.y;
   const long x = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  if (threadIdx.x == 0 && x < blocks_per_row) {
-    int seq, first = 0, nch = 0;
-    if (cu == nullptr) {
-      seq = row;
-      first = (int)(x * Gs);
-      nch = (int)min((long)Gs, slots_per_row - x * Gs);
-      first += (int)(row * slots_per_row);
-    } else {
-      const int span = Gs * Q;
-      seq = find_seq(cu, S, x, span);
-      const int b = cu[seq], e = cu[seq + 1];
-      const long j = x - (long)(b / span + seq);
-      const int nblk = (e - b + span - 1) / span;
-      if (j >= 0 && j < nblk) {
-        const int nchs = (e - b + Q - 1) / Q;
-        first = b / Q + seq + (int)j * Gs;
-        nch = min(Gs, nchs - (int)j * Gs);
-      }
-    }
-    btable[row * blocks_per_row + x] = make_int4(seq, first, nch, 0);
-  }
-  if (x >= slots_per_row) return;
+  if (threadIdx.x == 0 && x < sa.blocks_per_row)
+    btable[row * sa.blocks_per_row + x] = block_record(sa.cu, sa.S, row, x, Q, Gs, sa.slots_per_row);
+  if (x >= sa.slots_per_row) return;
 
-  const long slot = (long)row * slots_per_row + x;
-  int seq, t0, len, kidx;
-  if (cu == nullptr) {
-    seq = row;
-    kidx = (int)x;
-    t0 = kidx * Q;
-    len = min(Q, T - t0);
-  } else {
-    seq = find_seq(cu, S, x, Q);
-    const int b = cu[seq], e = cu[seq + 1];
-    const long j = x - (long)(b / Q + seq);
-    const int nch = (e - b + Q - 1) / Q;
-    if (j < 0 || j >= nch) {
-      kidx = -1;
-      t0 = 0;
-      len = 0;
-    } else {
-      kidx = (int)j;
-      t0 = b + kidx * Q;
-      len = min(Q, e - t0);
-    }
-  }
-  const int tok0 = row * T + t0;  // token index flattened over rows
-  if (threadIdx.x == 0) table[slot] = make_int4(seq, tok0, len, kidx);
+  const long slot = (long)row * sa.slots_per_row + x;
+  const int4 rec = chunk_record(sa.cu, sa.S, row, x, sa.T, Q, sa.slots_per_row);
+  if (threadIdx.x == 0) table[slot] = rec;
+  const int tok0 = rec.y, len = rec.z;
   if (len <= 0) return;
 
   // The chunk's rows are contiguous: read them coalesced into LDS.
-  const bool m2 = dt != nullptr;
+  const bool m2 = sa.dt != nullptr;
   const int HP = H + 1;
-  const float* src = (m2 ? dt : la) + (long)tok0 * H;
+  const float* src = (m2 ? sa.dt : sa.la) + (long)tok0 * H;
   for (int idx = threadIdx.x; idx < len * H; idx += 1024) {
     float v = src[idx];
-    if (m2) v = softplus_f32(v + (dt_bias ? dt_bias[idx % H] : 0.f));
+    if (m2) v = softplus_f32(v + (sa.dt_bias ? sa.dt_bias[idx % H] : 0.f));
     tile[(idx / H) * HP + idx % H] = v;
   }
   __syncthreads();
 
   for (int h = wave; h < H; h += 16) {
-    const float A = m2 ? -expf(A_log[h]) : 1.f;
-    float carry = 0.f;  // inclusive sum up to the last valid token seen so far
-    float* out = cs + (slot * H + h) * (long)Q;
-    float* outk = m2 ? ck + (slot * H + h) * (long)Q : nullptr;
-    for (int jb = 0; jb < Q; jb += 64) {
-      const int j = jb + lane;
-      if (jb < len) {
-        const float t = (j < len) ? tile[j * HP + h] : 0.f;  // log a, or dt'
-        float v = m2 ? t * A : t;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const float u = __shfl_up(v, d);
-          if (lane >= d) v += u;
-        }
-        v += carry;
-        carry = __shfl(v, min(len - jb, 64) - 1);
-        if (j < Q) {
-          const float c = (j < len ? v : carry) * kLog2e;
-          out[j] = c;
-          if (m2) outk[j] = j < len ? c - log2f(t) : c;
-        }
-      } else if (j < Q) {
-        out[j] = carry * kLog2e;
-        if (m2) outk[j] = carry * kLog2e;
-      }
-    }
+    const float A = m2 ? -expf(sa.A_log[h]) : 1.f;
+    wave_segsum([&](int j) { return tile[j * HP + h]; }, len, Q, m2, A, cs + (slot * H + h) * (long)Q,
+                m2 ? ck + (slot * H + h) * (long)Q : nullptr, nullptr, lane);
   }
 }
 
@@ -157,10 +65,10 @@ hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
+  const SegArgs sa = seg_args(d, log_a, cu, m2);
   dim3 grid((unsigned)gx, (unsigned)d.batch);
-  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(1024), lds, stream, log_a, cu, d.num_seqs, d.T, d.H, d.Q,
-                     d.state_block, d.slots_per_row, d.blocks_per_row, ws.table, ws.btable, ws.cs, m2.dt,
-                     m2.dt_bias, m2.A_log, ws.ck);
+  hipLaunchKernelGGL(chunk_cumsum_kernel, grid, dim3(1024), lds, stream, sa, d.H, d.Q, d.state_block, ws.table,
+                     ws.btable, ws.cs, ws.ck);
   return hipGetLastError();
 }
 

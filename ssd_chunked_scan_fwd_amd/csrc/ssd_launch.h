@@ -43,10 +43,29 @@ struct Mamba2Args {
   const void* z = nullptr;         // like X, or null
 };
 
+// Arguments of the segment sums: the log decay, or the Mamba-2 step sizes,
+// and what locates chunk and block slots.
+struct SegArgs {
+  const float* la;       // [rows * T][H] log a (plain calls)
+  const float* dt;       // [rows * T][H] raw step sizes (Mamba-2 calls), else null
+  const float* dt_bias;  // [H] or null
+  const float* A_log;    // [H]
+  const int32_t* cu;     // packed sequence starts, or null
+  int S, T;
+  long slots_per_row, blocks_per_row;
+};
+
+inline SegArgs seg_args(const FwdDims& d, const float* log_a, const int32_t* cu, const Mamba2Args& m2) {
+  return SegArgs{log_a, m2.dt, m2.dt_bias, m2.A_log, cu, d.num_seqs, d.T, d.slots_per_row, d.blocks_per_row};
+}
+
 hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32_t* cu,
                                const Workspace& ws, hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});
+// With `seg` given, chunk_state computes the records and segment sums itself
+// (the fused form that ssd_fwd* run); without it, it reads them from the
+// workspace as written by launch_chunk_cumsum.
 hipError_t launch_chunk_state(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
-                              hipStream_t stream);
+                              hipStream_t stream, const SegArgs* seg = nullptr);
 hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float* init, float* final_state,
                                 const Workspace& ws, hipStream_t stream);
 hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
@@ -57,7 +76,7 @@ hipError_t launch_ssd_step(int batch, int H, int G, int P, int N, int bf16, floa
 
 // Bytes of dynamic LDS the bf16 kernels need (host-side checks).
 size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q);
-size_t chunk_state_bf16_lds_bytes(int P, int N);
+size_t chunk_state_bf16_lds_bytes(int P, int N, int block_tokens);  // block_tokens: Gs*Q when fused, else 0
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 
 }  // namespace ssd
