@@ -13,6 +13,10 @@ the Mamba-2 block's call on the same shape (ssd_fwd_mamba2: raw step sizes,
 dt_bias, A_log, the D skip and the silu(z) gate) and its decode step, and the
 fp64 CPU oracle timed on this host as a baseline.
 
+Per-stage times come from each stage's own entry point (the four-launch form
+of the stage API); the step itself runs three launches, chunk_state computing
+the segment sums itself.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-mamba2]
 """
 from __future__ import annotations
@@ -42,10 +46,12 @@ def log(msg: str) -> None:
 # reported only while these files are unchanged since the counters were taken.
 CSRC = os.path.join(ROOT, "ssd_chunked_scan_fwd_amd", "csrc")
 STAGE_SOURCES = {
-    "chunk_cumsum": ["ssd_cumsum_passing.hip", "ssd_device.h"],
+    "chunk_cumsum": ["ssd_cumsum_passing.hip", "ssd_device.h", "ssd_segsum.h"],
     "state_passing": ["ssd_cumsum_passing.hip", "ssd_device.h"],
-    "chunk_state": ["ssd_chunk_state.hip", "ssd_device.h", "ssd_stage.h"],
+    "chunk_state": ["ssd_chunk_state.hip", "ssd_device.h", "ssd_stage.h", "ssd_segsum.h"],
+    "chunk_state_fused": ["ssd_chunk_state.hip", "ssd_device.h", "ssd_stage.h", "ssd_segsum.h"],
     "chunk_scan": ["ssd_chunk_scan.hip", "ssd_device.h", "ssd_stage.h"],
+    "chunk_scan_gated": ["ssd_chunk_scan.hip", "ssd_device.h", "ssd_stage.h"],
 }
 
 
@@ -91,8 +97,11 @@ def stage_bytes(w, nslots: int, nblocks: int, nseq: int) -> dict:
     return {
         "chunk_cumsum": la + cs + tables,
         "chunk_state": X + BC + cs + tables + states + decay,
+        "chunk_state_fused": X + BC + la + cs + tables + states + decay,   # writes cs and the tables
         "state_passing": states + decay + starts + final,
         "chunk_scan": X + 2 * BC + cs + tables + starts + X,   # X read, Y written
+        # the Mamba-2 call's gated chunk_scan: also z in and the key-side exponents
+        "chunk_scan_gated": X + 2 * BC + 2 * cs + tables + starts + X + X,
     }
 
 
@@ -204,13 +213,17 @@ def main() -> int:
     stage_us = {k: v * 1e3 / max(args.stage_reps, 1) for k, v in acc.items()}
     sbytes = stage_bytes(w, ws.layout.nslots, ws.layout.nblocks, w.batch)
     dominant = max(stage_us, key=stage_us.get)
+    # The step runs three launches: chunk_state in its fused form (segment sums
+    # computed in the kernel), state_passing, chunk_scan. The fused kernel has no
+    # entry point of its own; its time is the step's event time less the other two.
+    fused_us = ev_ms * 1e3 - stage_us["state_passing"] - stage_us["chunk_scan"]
     achieved = sbytes[dominant] / (stage_us[dominant] * 1e-6) / 1e9
     chunk_lengths = [min(w.Q, w.T - k * w.Q) for k in range(-(-w.T // w.Q))] * w.batch
     flops = useful_flops(w, chunk_lengths)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     compulsory = (tokens * w.H * w.P * 2 * 2 + tokens * w.G * w.N * 2 * 2 + tokens * w.H * 4 +
                   w.batch * w.H * w.P * w.N * 4)
-    pipeline_bytes = sum(sbytes.values())
+    pipeline_bytes = sbytes["chunk_state_fused"] + sbytes["state_passing"] + sbytes["chunk_scan"]   # the step's launches
 
     out = {
         "metric": METRIC,
@@ -232,7 +245,9 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(dominant, w.name, ws.state_block),
                      "bytes_per_launch": sbytes[dominant], "avg_launch_us": round(stage_us[dominant], 3)},
+        "launches_per_step": ["chunk_state (fused with the segment sums)", "state_passing", "chunk_scan"],
         "stages_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "chunk_state_fused_us_derived": round(fused_us, 3),
         "stage_bytes": sbytes,
         "stage_gbs": {k: round(sbytes[k] / (stage_us[k] * 1e-6) / 1e9, 1) for k in stage_us},
         "event_ms_per_step": round(ev_ms, 5),
