@@ -192,6 +192,15 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
     for (int r0 = 0; r0 < cur.len; r0 += kPassRows) {
       const int rows = min(kPassRows, cur.len - r0);
       __syncthreads();
+      // Row weights first: in the fused form they come from LDS and need not
+      // wait for the pass loads.
+      float wr[K::RX];
+#pragma unroll
+      for (int u = 0; u < K::RX; ++u) {
+        const float kj = FUSED ? ckl[c * Q + min(r0 + min(xrow[u], kPassRows - 1), Q - 1)] : pcs[u];
+        const float e = fast_exp2(shift - kj);
+        wr[u] = xrow[u] < rows ? e : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < K::RB; ++u)
         if (brow[u] < kPassRows)
@@ -199,8 +208,7 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
 #pragma unroll
       for (int u = 0; u < K::RX; ++u) {
         if (xrow[u] < kPassRows) {
-          const float kj = FUSED ? ckl[c * Q + min(r0 + xrow[u], Q - 1)] : pcs[u];
-          const float w = xrow[u] < rows ? fast_exp2(shift - kj) : 0.f;
+          const float w = wr[u];
           u32x4 v;
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(px[u][q]) * w, bf16_hi(px[u][q]) * w);
@@ -215,7 +223,9 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
       __syncthreads();
       if (active) {
         const int nkb = (rows + 31) / 32;
-        for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+        for (int kb = 0; kb < kPassRows / 32; ++kb) {
+          if (kb >= nkb) break;
           u32x4 xa[K::TPW], bb[K::TNW];
 #pragma unroll
           for (int a = 0; a < K::TPW; ++a) xa[a] = frag_k_rows_accpair(xw, K::XP, 32 * kb, (p0t + a) * 16, lane);

@@ -77,11 +77,22 @@ __device__ __forceinline__ int4 block_record(const int32_t* __restrict__ cu, int
 template <class F>
 __device__ __forceinline__ float wave_segsum(F tval, int len, int Q, bool m2, float A, float* __restrict__ out,
                                              float* __restrict__ outk, float* __restrict__ lk, int lane) {
+  // Every value is fetched before the scan, so their latencies overlap.
+  constexpr int kMaxPieces = 256 / 64;
+  float tv[kMaxPieces];
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    const int j = 64 * i + lane;
+    tv[i] = (j < len && j < Q) ? tval(j) : 0.f;
+  }
   float carry = 0.f;  // inclusive sum up to the last valid token seen so far
-  for (int jb = 0; jb < Q; jb += 64) {
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    const int jb = 64 * i;
+    if (jb >= Q) break;
     const int j = jb + lane;
     if (jb < len) {
-      const float t = (j < len) ? tval(j) : 0.f;
+      const float t = tv[i];
       float v = m2 ? t * A : t;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
