@@ -28,6 +28,10 @@
  * sequence starts from a zero state, as if run alone (the pages' training on
  * variable-length sequences without padding; a reset is a_t = 0 at the start).
  *
+ * Alignment: initial_state and final_state must be 16-byte aligned (states
+ * move in 16-byte pieces); other tensors need their element alignment, and
+ * the workspace 256 bytes.
+ *
  * Ownership and streams: every pointer is a caller-owned buffer; device
  * pointers for all tensors, host pointers for `shape` and `layout`. The
  * library allocates nothing, keeps no mutable global state, never

@@ -117,7 +117,8 @@ struct Prepared {
 // the discretising cumsum stage); plain calls read cs in its place.
 ssd_status prepare(int stages, const void* X, const float* log_a, const void* B, const void* C,
                    const void* Y, const int32_t* cu, int32_t chunk, int32_t gs, const ssd_shape* s,
-                   void* workspace, size_t workspace_bytes, Prepared* pp, bool mamba2 = false) {
+                   void* workspace, size_t workspace_bytes, Prepared* pp, bool mamba2 = false,
+                   const float* initial_state = nullptr, const float* final_state = nullptr) {
   ssd_status st = check_shape(s, cu, chunk);
   if (st != SSD_OK) return st;
   if (gs <= 0) gs = default_state_block(s, cu, chunk);
@@ -126,10 +127,12 @@ ssd_status prepare(int stages, const void* X, const float* log_a, const void* B,
   if ((stages & kCumsum) && !log_a) return SSD_ERR_INVALID_ARGUMENT;
   if ((stages & (kState | kScan)) && (!X || !B)) return SSD_ERR_INVALID_ARGUMENT;
   if ((stages & kScan) && (!C || !Y)) return SSD_ERR_INVALID_ARGUMENT;
+  // the state-passing stage moves states in 16-byte pieces
+  if (((uintptr_t)initial_state | (uintptr_t)final_state) & 15) return SSD_ERR_INVALID_ARGUMENT;
   ssd_layout L;
   st = make_layout(s, cu, chunk, gs, &L);
   if (st != SSD_OK) return st;
-  if (!workspace) return SSD_ERR_INVALID_ARGUMENT;
+  if (!workspace || ((uintptr_t)workspace & 255)) return SSD_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < L.total_bytes) return SSD_ERR_WORKSPACE_TOO_SMALL;
   char* base = static_cast<char*>(workspace);
   pp->d = ssd::FwdDims{s->batch, s->seqlen, s->nheads, s->ngroups, s->headdim, s->dstate, chunk, gs,
@@ -229,7 +232,7 @@ ssd_status ssd_state_passing(const int32_t* cu_seqlens, const float* initial_sta
                              size_t workspace_bytes, void* stream) {
   Prepared pp;
   ssd_status st = prepare(kPassing, nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens, chunk, state_block,
-                          shape, workspace, workspace_bytes, &pp);
+                          shape, workspace, workspace_bytes, &pp, false, initial_state, final_state);
   if (st != SSD_OK) return st;
   return hip_status(
       ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, (hipStream_t)stream));
@@ -250,7 +253,7 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
                       const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
   Prepared pp;
   ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
-                          workspace_bytes, &pp);
+                          workspace_bytes, &pp, false, initial_state, final_state);
   if (st != SSD_OK) return st;
   // Three launches: chunk_state computes the records and segment sums itself.
   hipStream_t s = (hipStream_t)stream;
@@ -277,7 +280,7 @@ ssd_status ssd_fwd_mamba2(const void* X, const float* dt, const float* dt_bias, 
   Prepared pp;
   // log_a is not read on this path; dt stands in for the non-null check.
   ssd_status st = prepare(kAll, X, dt, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
-                          workspace_bytes, &pp, true);
+                          workspace_bytes, &pp, true, initial_state, final_state);
   if (st != SSD_OK) return st;
   ssd::Mamba2Args m2;
   m2.dt = dt;

@@ -74,11 +74,14 @@ hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32
 
 // ----------------------------------------------------------------------------
 // state_passing: h = h0 (the sequence's initial state, or 0); for each state
-// block m of a sequence: start_m = h; h = exp2(total_m) h + s_m. One thread owns 2 consecutive (p, n) elements of
-// one (sequence, head); the block loop is unrolled so that the loads of
-// sixteen blocks are in flight together. Sequence s: packed rows own block slots
+// block m of a sequence: start_m = h; h = exp2(total_m) h + s_m. One thread owns
+// 4 consecutive (p, n) elements of one (sequence, head) and moves them with
+// 16-byte loads; the block loop is unrolled so that the loads of sixteen blocks
+// are in flight together. Sequence s: packed rows own block slots
 // floor(cu[s]/(Gs*Q)) + s ..; unpacked row s owns s*blocks_per_row ...
 // ----------------------------------------------------------------------------
+constexpr int kPassElems = 4;   // (p, n) elements per thread
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ states,
                                                             const float* __restrict__ bdecay,
@@ -87,9 +90,9 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
                                                             const float* __restrict__ init,
                                                             const int32_t* __restrict__ cu,
                                                             long blocks_per_row, int H, int PN, int span) {
-  const int eblocks = (PN / 2 + 255) / 256;
+  const int eblocks = (PN / kPassElems + 255) / 256;
   const long unit = blockIdx.x;
-  const int e = (int)(unit % eblocks) * 512 + threadIdx.x * 2;
+  const int e = (int)(unit % eblocks) * (256 * kPassElems) + threadIdx.x * kPassElems;
   const int h = (int)((unit / eblocks) % H);
   const int s = (int)(unit / ((long)eblocks * H));
   long base;
@@ -104,25 +107,26 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
   }
   if (e >= PN) return;
 
-  f32x2 hc = {0.f, 0.f};
-  if (init) hc = *reinterpret_cast<const f32x2*>(init + ((long)s * H + h) * PN + e);
-  auto put = [&](long blk, f32x2 v) {
+  f32x4 hc = {0.f, 0.f, 0.f, 0.f};
+  if (init) hc = *reinterpret_cast<const f32x4*>(init + ((long)s * H + h) * PN + e);
+  auto put = [&](long blk, f32x4 v) {
     const long off = (blk * H + h) * (long)PN + e;
     if (OUT_BF16) {
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(start) + off) = pack_bf16x2(v[0], v[1]);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(start) + off) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     } else {
-      *reinterpret_cast<f32x2*>(reinterpret_cast<float*>(start) + off) = v;
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(start) + off) = v;
     }
   };
   constexpr int U = 16;  // blocks whose loads are in flight together
   int k = 0;
   for (; k + U <= nblk; k += U) {
-    f32x2 sv[U];
+    f32x4 sv[U];
     float dv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const long blk = base + k + u;
-      sv[u] = *reinterpret_cast<const f32x2*>(states + (blk * H + h) * (long)PN + e);
+      sv[u] = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
       dv[u] = bdecay[blk * H + h];
     }
 #pragma unroll
@@ -134,19 +138,19 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
   }
   for (; k < nblk; ++k) {
     const long blk = base + k;
-    const f32x2 sv = *reinterpret_cast<const f32x2*>(states + (blk * H + h) * (long)PN + e);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
     const float a = fast_exp2(bdecay[blk * H + h]);
     put(blk, hc);
     hc = a * hc + sv;
   }
-  if (final_state) *reinterpret_cast<f32x2*>(final_state + ((long)s * H + h) * PN + e) = hc;
+  if (final_state) *reinterpret_cast<f32x4*>(final_state + ((long)s * H + h) * PN + e) = hc;
 }
 
 hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float* init, float* final_state,
                                 const Workspace& ws, hipStream_t stream) {
   const int PN = d.P * d.N;
   const int nseq = cu ? d.num_seqs : d.batch;
-  const long eblocks = (PN / 2 + 255) / 256;
+  const long eblocks = (PN / kPassElems + 255) / 256;
   dim3 grid((unsigned)(eblocks * d.H * nseq));
   const int span = d.state_block * d.Q;
   if (d.bf16) {

@@ -237,3 +237,18 @@ def test_mamba2_binding_checks_parameters():
     with pytest.raises(ValueError):
         ssd.fwd_mamba2(X, torch.zeros(1, 64, 2), torch.zeros(2), torch.zeros(1, 64, 1, 16), torch.zeros(1, 64, 1, 16),
                        chunk=32)
+
+
+def test_alignment_rules():
+    L = ssd.lib()
+    sh = shape()
+    _, need = ws_bytes(sh, 128, 0)
+    odd = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    # workspace must be 256-byte aligned
+    assert L.ssd_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, None, 128, 0, FAKE, None, ctypes.byref(sh), odd, need,
+                        None) == INVALID
+    # states move in 16-byte pieces
+    assert L.ssd_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, odd, 128, 0, FAKE, None, ctypes.byref(sh), FAKE, need,
+                        None) == INVALID
+    assert L.ssd_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, None, 128, 0, FAKE, odd, ctypes.byref(sh), FAKE, need,
+                        None) == INVALID
