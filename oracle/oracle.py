@@ -26,6 +26,9 @@ The Mamba-2 functions (``softplus``, ``silu``, ``mamba2_discretize``,
 ``mamba2_forward``, ``mamba2_step``) put the block's discretisation, skip and
 gate around that recurrence (paper card Method 6, Paper vs code 3, 7, 8).
 
+``backward`` is reverse mode through the same recurrence (its adjoint), the
+plain definition of the gradients; the pages give no backward algorithm.
+
 Every function in this file is pinned by ``tests/test_oracle.py`` against the
 quadratic dual form, closed forms, causal linear attention, packing,
 continuation, hand-worked examples and invariants; none is "parity unpinned".
@@ -301,6 +304,73 @@ def mamba2_step(state, x, dt, dt_bias, A_log, D, z, B, C):
                             None if z is None else _f64(z)[:, None], _f64(B)[:, None], _f64(C)[:, None],
                             init=_f64(state))
     return Y[:, 0], fin
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (reverse mode through the recurrence). The pages motivate the
+# layer by training but give no backward algorithm; the plain definition of
+# the gradient is the adjoint of the recurrence h_t = a_t h_{t-1} + B_t x_t^T,
+# y_t = C_t^T h_t (paper card Method 1; Method 2 for the scalar a_t). For
+# L = <dY, Y> + <dfinal, h_last>, with lam_t = dL/dh_t:
+#   lam_last = dfinal + C_last dY_last^T,  lam_t = a_{t+1} lam_{t+1} + C_t dY_t^T
+#   dx_t = lam_t^T B_t,  dB_t = lam_t x_t,  dC_t = h_t dY_t,
+#   d log a_t = a_t <lam_t, h_{t-1}>,  d h_init = a_first lam_first.
+# ---------------------------------------------------------------------------
+BACKWARD_MUTANTS = {
+    "decay_before_input": 1,    # lam decayed before C_t dY_t^T is added
+    "log_a_uses_h_t": 2,        # <lam_t, h_t> in place of <lam_t, h_{t-1}>
+    "final_ignored": 3,         # dfinal dropped
+    "dC_previous_state": 4,     # dC_t from h_{t-1}
+    "dx_reads_C": 5,            # dx_t = lam_t^T C_t
+}
+
+
+def backward(X, la, B, C, dY, dfinal=None, cu_seqlens=None, init=None, mutant: int = 0):
+    """Gradients of L = <dY, Y> + <dfinal, final> through the layer.
+
+    X [rows,T,H,P], la [rows,T,H], B and C [rows,T,G,N], dY like X; dfinal and
+    init [rows or S,H,P,N] (the final-state layout, element (p, n) = h[n][p]) or
+    None. Returns dict(dX, dlog_a, dB, dC, dinit), fp64, dB and dC summed over
+    the heads of each group. Keeps every state in memory: small cases only.
+    """
+    X, la, B, C, dY = (_f64(a) for a in (X, la, B, C, dY))
+    rows, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    grp = np.arange(H) // (H // G)
+    segs = sequence_segments(rows, T, cu_seqlens)
+    dX = np.zeros_like(X)
+    dla = np.zeros_like(la)
+    dB = np.zeros_like(B)
+    dC = np.zeros_like(C)
+    dinit = np.zeros((len(segs), H, P, N))
+    for si, (r, b, e) in enumerate(segs):
+        # forward, keeping h_t for every t of the sequence: hs[k] = h_{b+k-1}
+        hs = np.zeros((e - b + 1, H, N, P))
+        if init is not None:
+            hs[0] = np.transpose(_f64(init)[si], (0, 2, 1))
+        for t in range(b, e):
+            a = np.exp(la[r, t])[:, None, None]
+            hs[t - b + 1] = a * hs[t - b] + np.einsum("hn,hp->hnp", B[r, t, grp], X[r, t])
+        lam = np.zeros((H, N, P))
+        if dfinal is not None and mutant != BACKWARD_MUTANTS["final_ignored"]:
+            lam = np.transpose(_f64(dfinal)[si], (0, 2, 1)).copy()
+        for t in range(e - 1, b - 1, -1):
+            a = np.exp(la[r, t])[:, None, None]
+            h_prev, h_t = hs[t - b], hs[t - b + 1]
+            if mutant == BACKWARD_MUTANTS["decay_before_input"]:
+                lam = a * lam
+            lam = lam + np.einsum("hn,hp->hnp", C[r, t, grp], dY[r, t])
+            Bt = C[r, t, grp] if mutant == BACKWARD_MUTANTS["dx_reads_C"] else B[r, t, grp]
+            dX[r, t] = np.einsum("hnp,hn->hp", lam, Bt)
+            np.add.at(dB[r, t], grp, np.einsum("hnp,hp->hn", lam, X[r, t]))
+            hc = h_prev if mutant == BACKWARD_MUTANTS["dC_previous_state"] else h_t
+            np.add.at(dC[r, t], grp, np.einsum("hnp,hp->hn", hc, dY[r, t]))
+            hl = h_t if mutant == BACKWARD_MUTANTS["log_a_uses_h_t"] else h_prev
+            dla[r, t] = a[:, 0, 0] * np.einsum("hnp,hnp->h", lam, hl)
+            if mutant != BACKWARD_MUTANTS["decay_before_input"]:
+                lam = a * lam
+        dinit[si] = np.transpose(lam, (0, 2, 1))
+    return dict(dX=dX, dlog_a=dla, dB=dB, dC=dC, dinit=dinit)
 
 
 def chunk_cumsum(la, segments) -> np.ndarray:

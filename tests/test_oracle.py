@@ -446,3 +446,112 @@ def _m2_pins(mutant):
 def test_mamba2_mutants_are_caught(name):
     assert _m2_pins(0) == []
     assert _m2_pins(oracle.MAMBA2_MUTANTS[name]), f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------- backward (reverse mode)
+
+def _bwd_case(T=9, H=2, P=3, N=4, G=1, seed=11, rows=1, lengths=None):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((rows, T, H, P))
+    la = -rng.uniform(0.05, 0.8, size=(rows, T, H))
+    B = rng.standard_normal((rows, T, G, N))
+    C = rng.standard_normal((rows, T, G, N))
+    dY = rng.standard_normal((rows, T, H, P))
+    S = rows if lengths is None else len(lengths)
+    dfin = rng.standard_normal((S, H, P, N))
+    init = rng.standard_normal((S, H, P, N))
+    cu = None if lengths is None else np.concatenate([[0], np.cumsum(lengths)])
+    return X, la, B, C, dY, dfin, init, cu
+
+
+def _loss(X, la, B, C, dY, dfin, init, cu):
+    Y, fin = oracle.forward(X, la, B, C, cu_seqlens=cu, init=init)
+    return float(np.sum(dY * Y) + np.sum(dfin * fin))
+
+
+def _fd_errors(g, case):
+    """Central differences of the loss along one random direction per input, against <grad, v>."""
+    X, la, B, C, dY, dfin, init, cu = case
+    rng = np.random.default_rng(5)
+    args = dict(X=X, la=la, B=B, C=C, init=init)
+    grads = dict(X=g["dX"], la=g["dlog_a"], B=g["dB"], C=g["dC"], init=g["dinit"])
+    out = {}
+    eps = 1e-6
+    for k in args:
+        v = rng.standard_normal(args[k].shape)
+        ap, am = dict(args), dict(args)
+        ap[k] = args[k] + eps * v
+        am[k] = args[k] - eps * v
+        fd = (_loss(ap["X"], ap["la"], ap["B"], ap["C"], dY, dfin, ap["init"], cu) -
+              _loss(am["X"], am["la"], am["B"], am["C"], dY, dfin, am["init"], cu)) / (2 * eps)
+        an = float(np.sum(grads[k] * v))
+        out[k] = abs(fd - an) / max(abs(fd), 1e-12)
+    return out
+
+
+@pytest.mark.parametrize("G,H", [(1, 2), (2, 4), (3, 3)])
+def test_backward_matches_finite_differences(G, H):
+    case = _bwd_case(H=H, G=G, seed=20 + G)
+    X, la, B, C, dY, dfin, init, cu = case
+    g = oracle.backward(X, la, B, C, dY, dfinal=dfin, init=init)
+    for k, e in _fd_errors(g, case).items():
+        assert e < 1e-7, (k, e)
+
+
+def test_backward_packed_finite_differences_and_separate_runs():
+    lengths = [3, 1, 6, 2]
+    case = _bwd_case(T=sum(lengths), H=2, G=1, seed=31, lengths=lengths)
+    X, la, B, C, dY, dfin, init, cu = case
+    g = oracle.backward(X, la, B, C, dY, dfinal=dfin, cu_seqlens=cu, init=init)
+    for k, e in _fd_errors(g, case).items():
+        assert e < 1e-7, (k, e)
+    for s in range(len(lengths)):
+        b, e = int(cu[s]), int(cu[s + 1])
+        gs = oracle.backward(X[:, b:e], la[:, b:e], B[:, b:e], C[:, b:e], dY[:, b:e], dfinal=dfin[s:s + 1],
+                             init=init[s:s + 1])
+        for k in ("dX", "dlog_a", "dB", "dC"):
+            np.testing.assert_allclose(g[k][:, b:e], gs[k], rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(g["dinit"][s], gs["dinit"][0], rtol=1e-13, atol=1e-13)
+
+
+def test_backward_scalar_closed_form():
+    # N = P = 1, B = C = 1, a = 1/2: y_t = sum_{j<=t} 2^-(t-j) x_j, so with dY = 1 and no
+    # final-state gradient dx_j = sum_{t=j}^{T-1} 2^-(t-j) = 2 (1 - 2^-(T-j)).
+    T = 6
+    X = np.arange(1.0, T + 1).reshape(1, T, 1, 1)
+    la = np.full((1, T, 1), math.log(0.5))
+    one = np.ones((1, T, 1, 1))
+    g = oracle.backward(X, la, one, one, np.ones_like(X))
+    want = [2 * (1 - 2.0 ** -(T - j)) for j in range(T)]
+    np.testing.assert_allclose(g["dX"][0, :, 0, 0], want, rtol=1e-14)
+    np.testing.assert_allclose(g["dB"][0, :, 0, 0], np.array(want) * X[0, :, 0, 0], rtol=1e-14)
+
+
+def test_backward_log_decay_identity():
+    # d/dcs_k of <dY, M X> is dY_k . y_k - x_k . dx_k (the two exponents of every
+    # L_ij = exp(cs_i - cs_j)), plus <dfinal, h_last> at the last token, and
+    # log a_t enters every cs_k with k >= t: d log a = reverse cumsum of that.
+    case = _bwd_case(T=12, H=3, G=1, seed=41)
+    X, la, B, C, dY, dfin, init, cu = case
+    g = oracle.backward(X, la, B, C, dY, dfinal=dfin, init=init)
+    Y, fin = oracle.forward(X, la, B, C, init=init)
+    gk = np.sum(dY * Y, axis=-1) - np.sum(X * g["dX"], axis=-1)
+    gk[:, -1] += np.sum(dfin * fin, axis=(-2, -1))
+    want = np.flip(np.cumsum(np.flip(gk, axis=1), axis=1), axis=1)
+    np.testing.assert_allclose(g["dlog_a"], want, rtol=1e-11, atol=1e-11)
+
+
+def _bwd_pins(mutant):
+    failed = []
+    case = _bwd_case(T=8, H=2, G=1, seed=51)
+    X, la, B, C, dY, dfin, init, cu = case
+    g = oracle.backward(X, la, B, C, dY, dfinal=dfin, init=init, mutant=mutant)
+    errs = _fd_errors(g, case)
+    failed += [k for k, e in errs.items() if e > 1e-7]
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(oracle.BACKWARD_MUTANTS))
+def test_backward_mutants_are_caught(name):
+    assert _bwd_pins(0) == []
+    assert _bwd_pins(oracle.BACKWARD_MUTANTS[name]), f"mutant {name} passed every pin"
