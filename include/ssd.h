@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum {
   SSD_OK = 0,
@@ -243,6 +243,43 @@ ssd_status ssd_fwd_mamba2(const void* X, const float* dt, const float* dt_bias, 
                           const int32_t* cu_seqlens, const float* initial_state, int32_t chunk,
                           int32_t state_block, void* Y, float* final_state, const ssd_shape* shape,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass: the gradients of L = <dY, Y> + <dfinal_state, final_state>
+ * with respect to X, log_a, B, C and the initial state, for a forward pass
+ * with the same arguments. The pages give no backward algorithm; this one is
+ * the transpose of the forward terms (paper card Method 5 blocks; Method 3-4
+ * duality):
+ *   dX    = M^T dY with M = L o (C B^T): the same chunked algorithm run over
+ *           each sequence reversed in time, with B and C exchanged and the log
+ *           decays shifted by one token, starting from dfinal_state;
+ *   dB, dC: the chunked algorithm with the roles of x, B, C and dY exchanged
+ *           (state dimension P, head dimension N), per head, summed over the
+ *           heads of each group;
+ *   dlog_a[t] = a_t <lam_t, h_{t-1}>, the sum of dY_i . M_ij x_j over the
+ *           pairs i >= t > j, computed chunk by chunk: the pairs inside the
+ *           chunk in fp32, and the pairs that reach across its ends through
+ *           the chunk's entering state (a forward run) and the adjoint at its
+ *           end (the reversed run), with no cancellation between long sums;
+ *   dinitial_state = a_first * (adjoint of the first state).
+ * Arguments as for ssd_fwd_ex, plus
+ *   dY             [batch, seqlen, nheads, headdim] dtype
+ *   dfinal_state   fp32, final-state layout, or NULL (zero)
+ * Outputs: dX (dtype, X's layout), dlog_a (fp32, log_a's layout), dB and dC
+ * (dtype, B's layout), dinitial_state (fp32, may be NULL: not written).
+ * Supported: the forward's sizes with dstate <= 128, headdim + dstate <= 192
+ * and, for bf16, headdim >= 32 (the exchanged roles must themselves be
+ * supported sizes), and the log-decay tiles within the LDS (fp32 with
+ * headdim 64 and dstate 128 needs chunk <= 64). The forward outputs are not
+ * needed: every term is recomputed from the inputs. The workspace holds
+ * ssd_bwd_workspace_bytes(shape, chunk, state_block) bytes; dB and dC are
+ * summed over heads in fp32 and rounded once.
+ */
+ssd_status ssd_bwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_t state_block, size_t* bytes);
+ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
+                   const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
+                   int32_t state_block, void* dX, float* dlog_a, void* dB, void* dC, float* dinitial_state,
+                   const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step for `batch` independent streams: the loop body of

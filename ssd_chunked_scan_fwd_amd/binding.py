@@ -25,7 +25,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 # Every symbol include/ssd.h declares.
 EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "ssd_fwd_layout",
            "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
-           "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2")
+           "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2",
+           "ssd_bwd_workspace_bytes", "ssd_bwd")
 
 
 class SSDError(RuntimeError):
@@ -87,6 +88,10 @@ def lib():
         L.ssd_step.argtypes = [vp, vp, vp, vp, vp, vp, shp, vp]
         L.ssd_fwd_mamba2.restype = ctypes.c_int
         L.ssd_fwd_mamba2.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, shp, vp, sz, vp]
+        L.ssd_bwd_workspace_bytes.restype = ctypes.c_int
+        L.ssd_bwd_workspace_bytes.argtypes = [shp, i32, i32, ctypes.POINTER(sz)]
+        L.ssd_bwd.restype = ctypes.c_int
+        L.ssd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, shp, vp, sz, vp]
         L.ssd_step_mamba2.restype = ctypes.c_int
         L.ssd_step_mamba2.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, shp, vp]
         _lib = L
@@ -347,3 +352,38 @@ def step_mamba2(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: t
     _call("ssd_step_mamba2", _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(D), _ptr(z),
           _ptr(B), _ptr(C), _ptr(y), ctypes.byref(shape), _stream(x.device))
     return y
+
+
+def bwd_workspace_bytes(shape: Shape, chunk: int, state_block: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _call("ssd_bwd_workspace_bytes", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(n))
+    return int(n.value)
+
+
+def bwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor, dY: torch.Tensor,
+        cu_seqlens: Optional[torch.Tensor] = None, chunk: int = 128, state_block: int = 0,
+        initial_state: Optional[torch.Tensor] = None, dfinal_state: Optional[torch.Tensor] = None,
+        want_dinit: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Backward pass (ssd_bwd): gradients of <dY, Y> + <dfinal_state, final_state>
+    for the forward pass with these inputs. Returns dict(dX, dlog_a, dB, dC, dinit or None)."""
+    _check_inputs(X, log_a, B, C, cu_seqlens)
+    if dY.dtype != X.dtype or not dY.is_cuda or not dY.is_contiguous() or dY.shape != X.shape:
+        raise ValueError("dY must be a contiguous device tensor of X's shape and dtype")
+    shape = make_shape(X, B, cu_seqlens)
+    _check_state(initial_state, shape, "initial_state")
+    _check_state(dfinal_state, shape, "dfinal_state")
+    nbytes = bwd_workspace_bytes(shape, chunk, state_block)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    dX = torch.empty_like(X)
+    dla = torch.empty_like(log_a)
+    dB = torch.empty_like(B)
+    dC = torch.empty_like(C)
+    dinit = None
+    if want_dinit:
+        nseq = X.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        dinit = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
+    _call("ssd_bwd", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), _ptr(initial_state), _ptr(dY),
+          _ptr(dfinal_state), int(chunk), int(state_block), _ptr(dX), _ptr(dla), _ptr(dB), _ptr(dC), _ptr(dinit),
+          ctypes.byref(shape), _ptr(workspace), workspace.numel(), _stream(X.device))
+    return dict(dX=dX, dlog_a=dla, dB=dB, dC=dC, dinit=dinit)

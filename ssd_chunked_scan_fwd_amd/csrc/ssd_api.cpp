@@ -150,6 +150,94 @@ ssd_status prepare(int stages, const void* X, const float* log_a, const void* B,
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
+// One forward pass (three launches) on prepared dimensions and workspace.
+hipError_t run_forward(const Prepared& pp, const void* X, const float* log_a, const void* B, const void* C,
+                       const int32_t* cu, const float* init, void* Y, float* final_state, hipStream_t s) {
+  const ssd::SegArgs sa = ssd::seg_args(pp.d, log_a, cu, ssd::Mamba2Args{});
+  hipError_t e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s, &sa);
+  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu, init, final_state, pp.ws, s);
+  if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s);
+  return e;
+}
+
+// Backward workspace (offsets 256-aligned): the padded reversed copies, the
+// head broadcasts, fp32 per-head partials, and three forward workspaces: the
+// reversed run's and the forward chunk-state run's (both one chunk per state
+// block, kept for the log-decay gradient) and one shared by the two
+// role-exchanged runs.
+struct BwdLayout {
+  size_t cur, rev_dy, rev_x, dx_rev, rev_b, rev_c, bcast, part, la_rev, states_t, lam_first;
+  size_t fwd_a, fwd_f, fwd_s, total;
+  size_t a_bytes, f_bytes, s_bytes;
+  int Tr;          // tokens per row of the padded reversed layout (packed: an upper bound)
+};
+
+// The role-exchanged runs (dB, dC) have headdim N, dstate P and one group per head.
+ssd_shape swapped_shape(const ssd_shape* s) {
+  ssd_shape w = *s;
+  w.ngroups = s->nheads;
+  w.headdim = s->dstate;
+  w.dstate = s->headdim;
+  return w;
+}
+
+ssd_status make_bwd_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk, int32_t gs, BwdLayout* out) {
+  ssd_status st = check_shape(s, cu, chunk);
+  if (st != SSD_OK) return st;
+  const ssd_shape w = swapped_shape(s);
+  st = check_shape(&w, cu, chunk);  // dstate <= 128 and, for bf16, headdim >= 32
+  if (st != SSD_OK) return st;
+  if (gs <= 0) gs = default_state_block(s, cu, chunk);
+  st = check_state_block(s, gs);
+  if (st != SSD_OK) return st;
+  const int64_t P = s->headdim, N = s->dstate, H = s->nheads, G = s->ngroups;
+  if (P + N > 192 || chunk > 256) return SSD_ERR_UNSUPPORTED;  // the log-decay kernel's register rows
+  if (ssd::dlog_chunk_lds_bytes((int)P, (int)N, chunk, s->dtype == SSD_DTYPE_BF16 ? 2 : 4) > ssd::kMaxLdsBytes)
+    return SSD_ERR_UNSUPPORTED;
+  const int64_t T = s->seqlen;
+  const int64_t Tr = cu ? T + (int64_t)s->num_seqs * (chunk - 1) : T + (chunk - T % chunk) % chunk;
+  if ((int64_t)s->batch * Tr > INT32_MAX / 2) return SSD_ERR_UNSUPPORTED;
+  ssd_shape sr = *s;
+  sr.seqlen = (int32_t)Tr;
+  ssd_shape wr = w;
+  wr.seqlen = (int32_t)Tr;
+  ssd_layout La, Lf, Ls1, Ls2;
+  if ((st = check_shape(&sr, cu, chunk)) != SSD_OK) return st;
+  if ((st = make_layout(&sr, cu, chunk, 1, &La)) != SSD_OK) return st;
+  if ((st = make_layout(s, cu, chunk, 1, &Lf)) != SSD_OK) return st;
+  if ((st = make_layout(&wr, cu, chunk, default_state_block(&wr, cu, chunk), &Ls1)) != SSD_OK) return st;
+  if ((st = make_layout(&w, cu, chunk, default_state_block(&w, cu, chunk), &Ls2)) != SSD_OK) return st;
+  const size_t esz = s->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  const size_t tok = (size_t)s->batch * T, tokr = (size_t)s->batch * Tr;
+  const size_t tmax = tok > tokr ? tok : tokr;
+  const size_t nseq = cu ? s->num_seqs : s->batch;
+  if ((int64_t)tmax * H * (P > N ? P : N) > kMaxElems) return SSD_ERR_UNSUPPORTED;
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+  L.cur = take((nseq + 1) * 4);
+  L.rev_dy = take(tokr * H * P * esz);
+  L.rev_x = take(tokr * H * P * esz);
+  L.dx_rev = take(tokr * H * P * esz);
+  L.rev_b = take(tokr * G * N * esz);
+  L.rev_c = take(tokr * G * N * esz);
+  L.bcast = take(tmax * H * N * esz);
+  L.part = take(tmax * H * N * 4);
+  L.la_rev = take(tokr * H * 4);
+  L.states_t = take(nseq * H * P * N * 4);
+  L.lam_first = take(nseq * H * P * N * 4);
+  L.a_bytes = La.total_bytes;
+  L.f_bytes = Lf.total_bytes;
+  L.s_bytes = Ls1.total_bytes > Ls2.total_bytes ? Ls1.total_bytes : Ls2.total_bytes;
+  L.fwd_a = take(L.a_bytes);
+  L.fwd_f = take(L.f_bytes);
+  L.fwd_s = take(L.s_bytes);
+  L.total = off;
+  L.Tr = (int)Tr;
+  *out = L;
+  return SSD_OK;
+}
+
 // Shape checks of the decode steps.
 ssd_status check_step(const ssd_shape* s) {
   if (s->batch < 1 || s->nheads < 1 || s->ngroups < 1 || s->headdim < 1 || s->dstate < 1)
@@ -161,7 +249,6 @@ ssd_status check_step(const ssd_shape* s) {
     return SSD_ERR_UNSUPPORTED;
   return SSD_OK;
 }
-
 }  // namespace
 
 extern "C" {
@@ -269,6 +356,109 @@ ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void*
                    size_t workspace_bytes, void* stream) {
   return ssd_fwd_ex(X, log_a, B, C, cu_seqlens, nullptr, chunk, 0, Y, final_state, shape, workspace,
                     workspace_bytes, stream);
+}
+
+ssd_status ssd_bwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_t state_block, size_t* bytes) {
+  if (!bytes || !shape) return SSD_ERR_INVALID_ARGUMENT;
+  const int32_t dummy = 0;
+  const int32_t* cu = shape->num_seqs > 0 ? &dummy : nullptr;
+  BwdLayout L;
+  const ssd_status st = make_bwd_layout(shape, cu, chunk, state_block, &L);
+  if (st != SSD_OK) return st;
+  *bytes = L.total;
+  return SSD_OK;
+}
+
+ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
+                   const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
+                   int32_t state_block, void* dX, float* dlog_a, void* dB, void* dC, float* dinitial_state,
+                   const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !log_a || !B || !C || !dY || !dX || !dlog_a || !dB || !dC || !shape) return SSD_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)initial_state | (uintptr_t)dfinal_state | (uintptr_t)dinitial_state) & 15)
+    return SSD_ERR_INVALID_ARGUMENT;
+  const ssd_shape* s = shape;
+  BwdLayout L;
+  ssd_status st = make_bwd_layout(s, cu_seqlens, chunk, state_block, &L);
+  if (st != SSD_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & 255)) return SSD_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < L.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+  char* w = static_cast<char*>(workspace);
+  const bool packed = cu_seqlens != nullptr;
+  int32_t* cur = packed ? reinterpret_cast<int32_t*>(w + L.cur) : nullptr;
+  const int rows = s->batch, T = s->seqlen, Tr = L.Tr, H = s->nheads, G = s->ngroups, P = s->headdim, N = s->dstate;
+  const int S = packed ? s->num_seqs : 0;
+  const long nseq = packed ? s->num_seqs : s->batch;
+  const bool bf16 = s->dtype == SSD_DTYPE_BF16;
+  const int esz = bf16 ? 2 : 4;
+  // Dimensions of the four internal runs.
+  ssd_shape sr = *s;
+  sr.seqlen = Tr;
+  const ssd_shape sw = swapped_shape(s);
+  ssd_shape swr = sw;
+  swr.seqlen = Tr;
+  Prepared pa, pf, pbr, pbf;  // reversed dX run, forward state run, role-exchanged runs (reversed, forward)
+  if ((st = prepare(kAll, X, log_a, B, C, dX, cur ? cur : nullptr, chunk, 1, &sr, w + L.fwd_a, L.a_bytes, &pa)) != SSD_OK)
+    return st;
+  if ((st = prepare(kAll, X, log_a, B, C, dX, cu_seqlens, chunk, 1, s, w + L.fwd_f, L.f_bytes, &pf)) != SSD_OK) return st;
+  if ((st = prepare(kAll, X, log_a, B, C, dX, cur, chunk, 0, &swr, w + L.fwd_s, L.s_bytes, &pbr)) != SSD_OK) return st;
+  if ((st = prepare(kAll, X, log_a, B, C, dX, cu_seqlens, chunk, 0, &sw, w + L.fwd_s, L.s_bytes, &pbf)) != SSD_OK)
+    return st;
+  pbr.d.y_f32 = pbf.d.y_f32 = 1;  // per-head partials in fp32, rounded once after the group sum
+  hipStream_t hs = (hipStream_t)stream;
+  void* rev_dy = w + L.rev_dy;
+  void* rev_x = w + L.rev_x;
+  void* dx_rev = w + L.dx_rev;
+  void* rev_b = w + L.rev_b;
+  void* rev_c = w + L.rev_c;
+  void* bcast = w + L.bcast;
+  float* part = reinterpret_cast<float*>(w + L.part);
+  float* la_rev = reinterpret_cast<float*>(w + L.la_rev);
+  float* states_t = reinterpret_cast<float*>(w + L.states_t);
+  float* lam_first = reinterpret_cast<float*>(w + L.lam_first);
+
+  hipError_t e = hipSuccess;
+  if (packed) e = ssd::launch_padded_offsets(cu_seqlens, cur, S, chunk, hs);
+  // The padded reversed copies and decays.
+  if (e == hipSuccess) e = ssd::launch_gather_rows(dY, rev_dy, cu_seqlens, cur, S, rows, T, Tr, H, H, P * esz, 1, hs);
+  if (e == hipSuccess) e = ssd::launch_gather_rows(X, rev_x, cu_seqlens, cur, S, rows, T, Tr, H, H, P * esz, 1, hs);
+  if (e == hipSuccess) e = ssd::launch_gather_rows(B, rev_b, cu_seqlens, cur, S, rows, T, Tr, G, G, N * esz, 1, hs);
+  if (e == hipSuccess) e = ssd::launch_gather_rows(C, rev_c, cu_seqlens, cur, S, rows, T, Tr, G, G, N * esz, 1, hs);
+  if (e == hipSuccess) e = ssd::launch_reverse_log_decay(log_a, la_rev, cu_seqlens, cur, S, rows, T, Tr, H, hs);
+  // dX = M^T dY: the reversed run with B and C exchanged, from the final-state
+  // gradient; its chunk start states are the adjoints at the forward chunk ends.
+  if (e == hipSuccess)
+    e = run_forward(pa, rev_dy, la_rev, rev_c, rev_b, cur, dfinal_state, dx_rev, dinitial_state ? lam_first : nullptr,
+                    hs);
+  if (e == hipSuccess) e = ssd::launch_gather_rows(dx_rev, dX, cu_seqlens, cur, S, rows, T, Tr, H, H, P * esz, 2, hs);
+  // The forward chunk start states (one chunk per state block) and segment sums.
+  if (e == hipSuccess) {
+    const ssd::SegArgs sa = ssd::seg_args(pf.d, log_a, cu_seqlens, ssd::Mamba2Args{});
+    e = ssd::launch_chunk_state(pf.d, X, B, pf.ws, hs, &sa);
+  }
+  if (e == hipSuccess) e = ssd::launch_state_passing(pf.d, cu_seqlens, initial_state, nullptr, pf.ws, hs);
+  // d log a by chunks, from both runs' chunk start states.
+  if (e == hipSuccess) {
+    ssd::DlogArgs da{X, dY, B, C, log_a, pf.ws.table, pf.ws.btable, pf.ws.cs, pf.ws.start_states, pa.ws.start_states,
+                     cu_seqlens, cur, pf.d.slots_per_row, pa.d.slots_per_row, pf.d.nslots, dlog_a, H, G, P, N, chunk,
+                     bf16 ? 1 : 0};
+    e = ssd::launch_dlog_chunks(da, hs);
+  }
+  // dB: reversed run with x-role C (broadcast to heads), B-role dY, C-role x.
+  if (e == hipSuccess) e = ssd::launch_gather_rows(C, bcast, cu_seqlens, cur, S, rows, T, Tr, G, H, N * esz, 1, hs);
+  if (e == hipSuccess && dfinal_state) e = ssd::launch_transpose_states(dfinal_state, states_t, nseq * H, P, N, hs);
+  if (e == hipSuccess)
+    e = run_forward(pbr, bcast, la_rev, rev_dy, rev_x, cur, dfinal_state ? states_t : nullptr, part, nullptr, hs);
+  if (e == hipSuccess) e = ssd::launch_group_sum(part, dB, cu_seqlens, cur, S, rows, T, Tr, H, G, N, bf16, true, hs);
+  // dC: forward-time run with x-role B (broadcast to heads), B-role x, C-role dY.
+  if (e == hipSuccess) e = ssd::launch_gather_rows(B, bcast, cu_seqlens, cur, S, rows, T, Tr, G, H, N * esz, 0, hs);
+  if (e == hipSuccess && initial_state) e = ssd::launch_transpose_states(initial_state, states_t, nseq * H, P, N, hs);
+  if (e == hipSuccess)
+    e = run_forward(pbf, bcast, log_a, X, dY, cu_seqlens, initial_state ? states_t : nullptr, part, nullptr, hs);
+  if (e == hipSuccess) e = ssd::launch_group_sum(part, dC, cu_seqlens, cur, S, rows, T, Tr, H, G, N, bf16, false, hs);
+  // d h_init = a_first * (adjoint of the first state).
+  if (e == hipSuccess && dinitial_state)
+    e = ssd::launch_dinit(log_a, lam_first, dinitial_state, cu_seqlens, (int)nseq, T, H, P * N, hs);
+  return hip_status(e);
 }
 
 ssd_status ssd_fwd_mamba2(const void* X, const float* dt, const float* dt_bias, const float* A_log,

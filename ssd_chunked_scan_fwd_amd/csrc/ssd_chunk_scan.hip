@@ -95,6 +95,14 @@ __device__ __forceinline__ uint32_t yT_piece(uint32_t row, int q, int g4) {
   return row + 32 * q + 16 * (g4 & 1) + 8 * (g4 >> 1);
 }
 
+// fp32 output of a transposed tile (lane: 4 consecutive channels of its token
+// per P tile), for partial results that are summed before their one rounding.
+template <int TP>
+__device__ __forceinline__ void store_yT_f32(const f32x4 (&acc)[TP], rsrc_t ry, uint32_t row, int g4) {
+#pragma unroll
+  for (int pt = 0; pt < TP; ++pt) buf_store16(__builtin_bit_cast(u32x4, acc[pt]), ry, (row + pt * 16 + 4 * g4) * 4);
+}
+
 template <int TP>
 __device__ __forceinline__ void load_zT(ZPieces<TP>& z, rsrc_t rz, uint32_t row, int g4) {
 #pragma unroll
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
     const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
-    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q) {
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q, int yf32) {
   using K = ScanCfg<P, N>;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
@@ -445,7 +453,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 #pragma unroll
       for (int pt = 0; pt < K::TP; ++pt) acc[pt] *= u;
       key_block(kbd, true);
-      store_yT<K::TP, GATE>(acc, make_rsrc(Y + (tok0 * H + h) * P, (uint32_t)(len * ldx * 2)), yrow, g4, zp);
+      if (yf32)
+        store_yT_f32<K::TP>(acc, make_rsrc(reinterpret_cast<float*>(Y) + (tok0 * H + h) * P, (uint32_t)(len * ldx * 4)),
+                            yrow, g4);
+      else
+        store_yT<K::TP, GATE>(acc, make_rsrc(Y + (tok0 * H + h) * P, (uint32_t)(len * ldx * 2)), yrow, g4, zp);
     }
 
     // ---------------- state entering the next chunk of the block
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
     const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
-    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q) {
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q, int yf32) {
   using K = PairCfg<P, N>;
   const int HH = H / 2;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
@@ -821,8 +833,13 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       // consecutive p of P tile pt in lane group g4).
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd)
-        store_yT<K::TP, GATE>(acc[hd], make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow, g4,
-                              zp[hd]);
+        if (yf32)
+          store_yT_f32<K::TP>(acc[hd],
+                              make_rsrc(reinterpret_cast<float*>(Y) + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 4)),
+                              yrow, g4);
+        else
+          store_yT<K::TP, GATE>(acc[hd], make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow,
+                                g4, zp[hd]);
     } else {
       load_x(nx);
       load_c(nx);
@@ -992,7 +1009,7 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
                          reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
                          reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
                          reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
-                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q);
+                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q, d.y_f32);
       return hipGetLastError();
     }
   }
@@ -1007,7 +1024,7 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
                      reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
                      reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
                      reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
-                     reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q);
+                     reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q, d.y_f32);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ struct FwdDims {
   long nslots;
   long blocks_per_row;    // state-block slots per row
   long nblocks;
+  int y_f32 = 0;          // bf16 inputs only: write Y in fp32 (partials the backward pass sums)
 };
 
 struct Workspace {
@@ -73,6 +74,38 @@ hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, con
 hipError_t launch_ssd_step(int batch, int H, int G, int P, int N, int bf16, float* state,
                            const void* x, const float* log_a, const void* B, const void* C, void* y,
                            hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});
+
+// Backward-pass helpers (ssd_bwd.hip). The reversed runs use a padded reversed
+// layout: each sequence reversed in time behind (Q - len mod Q) mod Q zero
+// tokens, so that its chunks line up with the forward chunks; cur[] holds the
+// packed sequence starts of that layout (unpacked rows have Tr tokens each).
+hipError_t launch_padded_offsets(const int32_t* cu, int32_t* cur, int S, int Q, hipStream_t stream);
+// mode 0: same layout; 1: forward -> padded reversed; 2: padded reversed -> forward.
+hipError_t launch_gather_rows(const void* in, void* out, const int32_t* cu, const int32_t* cur, int S, int rows, int T,
+                              int Tr, int Hin, int Hout, int row_bytes, int mode, hipStream_t stream);
+hipError_t launch_group_sum(const float* in, void* out, const int32_t* cu, const int32_t* cur, int S, int rows, int T,
+                            int Tr, int H, int G, int D, bool bf16, bool from_reversed, hipStream_t stream);
+hipError_t launch_reverse_log_decay(const float* la, float* out, const int32_t* cu, const int32_t* cur, int S,
+                                    int rows, int T, int Tr, int H, hipStream_t stream);
+hipError_t launch_transpose_states(const float* in, float* out, long nmat, int A, int Bd, hipStream_t stream);
+hipError_t launch_dinit(const float* la, const float* lam_first, float* dinit, const int32_t* cu, int nseq, int T,
+                        int H, int PN, hipStream_t stream);
+
+struct DlogArgs {
+  const void *X, *dY, *B, *C;   // forward layout, dtype
+  const float* la;
+  const int4* ftable;           // forward run (one chunk per state block): chunk records,
+  const int4* fbtable;          //   block records (written for every slot),
+  const float* fcs;             //   segment sums,
+  const void* fstart;           //   chunk start states
+  const void* rstart;           // reversed run: chunk start states (padded reversed slots)
+  const int32_t *cu, *cur;
+  long spr, spr_r, nslots;      // chunk slots per row (forward, reversed), forward slots
+  float* dla;
+  int H, G, P, N, Q, bf16;
+};
+hipError_t launch_dlog_chunks(const DlogArgs& a, hipStream_t stream);
+size_t dlog_chunk_lds_bytes(int P, int N, int Q, int esz);
 
 // Bytes of dynamic LDS the bf16 kernels need (host-side checks).
 size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q);

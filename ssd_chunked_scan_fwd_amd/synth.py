@@ -187,3 +187,12 @@ def make_mamba2_decode_inputs(batch: int, steps: int, H: int, P: int, N: int, G:
     d = make_mamba2_inputs(steps, batch, H, P, N, G, dtype, seed)
     return dict(x=d["X"], dt=d["dt"], dt_bias=d["dt_bias"], A_log=d["A_log"], D=d["D"], z=d["z"],
                 B=d["B"], C=d["C"])
+
+
+def make_cotangents(batch: int, T: int, H: int, P: int, N: int, nseq: int, dtype=torch.bfloat16, seed: int = 0):
+    """Seeded output gradients for a backward call: dY [b,T,H,P] ~ N(0, 1) in the
+    workload dtype and dfinal [nseq,H,P,N] ~ N(0, 1) fp32 (the final-state layout)."""
+    rng = np.random.default_rng(seed)
+    dY = rng.standard_normal((batch, T, H, P), dtype=np.float32)
+    dfin = rng.standard_normal((nseq, H, P, N), dtype=np.float32)
+    return dict(dY=_to_dtype(dY, dtype), dfinal=torch.from_numpy(dfin))

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = ssd.lib()
-    assert L.ssd_abi_version() == 2
+    assert L.ssd_abi_version() == 3
     for code, name in binding.STATUS.items():
         assert L.ssd_status_string(code).decode() == name
 
@@ -252,3 +252,23 @@ def test_alignment_rules():
                         None) == INVALID
     assert L.ssd_fwd_ex(FAKE, FAKE, FAKE, FAKE, None, None, 128, 0, FAKE, odd, ctypes.byref(sh), FAKE, need,
                         None) == INVALID
+
+
+def test_bwd_validates():
+    L = ssd.lib()
+    sh = shape(seqlen=4096, nheads=8)
+    n = ctypes.c_size_t(0)
+    assert L.ssd_bwd_workspace_bytes(ctypes.byref(sh), 128, 0, ctypes.byref(n)) == OK and n.value > 0
+    # X, log_a, B, C, cu, init, dY, dfinal, chunk, gs, dX, dlog_a, dB, dC, dinit, shape, ws, bytes, stream
+    args = [FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, 128, 0, FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(sh),
+            FAKE, n.value, None]
+    for i in (0, 1, 2, 3, 6, 10, 11, 12, 13, 15, 16):
+        a = list(args)
+        a[i] = None
+        assert L.ssd_bwd(*a) == INVALID, i
+    a = list(args)
+    a[17] = n.value - 1
+    assert L.ssd_bwd(*a) == WS_SMALL
+    # dstate 256 has no exchanged-role run (headdim 256), and bf16 headdim 16 none either (dstate 16)
+    for bad in (shape(seqlen=512, nheads=8, dstate=256), shape(seqlen=512, nheads=8, headdim=16)):
+        assert L.ssd_bwd_workspace_bytes(ctypes.byref(bad), 128, 0, ctypes.byref(n)) == UNSUPPORTED
