@@ -10,14 +10,15 @@ Prints ONE JSON line with the headline throughput (tokens/s), the roofline of
 the dominant kernel (its algorithmic bytes / its average launch time, timed with
 HIP events on the launch stream), per-stage times, the decode-step throughput,
 the Mamba-2 block's call on the same shape (ssd_fwd_mamba2: raw step sizes,
-dt_bias, A_log, the D skip and the silu(z) gate) and its decode step, and the
-fp64 CPU oracle timed on this host as a baseline.
+dt_bias, A_log, the D skip and the silu(z) gate) and its decode step, the
+backward pass (ssd_bwd) on the same shape, and the fp64 CPU oracle timed on
+this host as a baseline.
 
 Per-stage times come from each stage's own entry point (the four-launch form
 of the stage API); the step itself runs three launches, chunk_state computing
 the segment sums itself.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-mamba2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-mamba2] [--no-bwd]
 """
 from __future__ import annotations
 
@@ -126,6 +127,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba-2 block-call timing")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--bwd-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--state-block", type=int, default=0, help="chunks per state block (0: library default)")
@@ -286,6 +289,37 @@ def main() -> int:
                          "ms_per_step": round(m_ms, 5), "event_ms_per_step": round(a.elapsed_time(b) / args.steps, 5),
                          "tokens_per_s": round(tokens / (m_ms * 1e-3), 1)}
         del mX, mdt, mbias, mAl, mD, mz, mB, mC
+
+    if not args.no_bwd:
+        # The backward pass (ssd_bwd) on the same shape: dX, d log a, dB, dC
+        # and the initial-state gradient from dY and a final-state cotangent.
+        nb = max(1, min(args.bwd_steps, args.steps))
+        log(f"[bench] backward pass on {w.name}: {nb} steps")
+        ct = synth.make_cotangents(w.batch, w.T, w.H, w.P, w.N, w.batch, w.torch_dtype, w.seed + 1)
+        dY, dfin = ct["dY"].to(dev), ct["dfinal"].to(dev)
+        bws = torch.empty(ssd.bwd_workspace_bytes(shape, w.Q, ws.state_block),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            return ssd.bwd(X, la, B, C, dY, chunk=w.Q, state_block=ws.state_block, dfinal_state=dfin,
+                           want_dinit=True, workspace=bws)
+
+        for _ in range(min(args.warmup, 20)):
+            bstep()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(stream)
+        for _ in range(nb):
+            bstep()
+        b.record(stream)
+        torch.cuda.synchronize()
+        b_ms = (time.perf_counter() - t0) * 1e3 / nb
+        out["bwd"] = {"workload": w.name + " (backward: dX, dlog_a, dB, dC, dinit)", "steps": nb,
+                      "ms_per_step": round(b_ms, 5), "event_ms_per_step": round(a.elapsed_time(b) / nb, 5),
+                      "tokens_per_s": round(tokens / (b_ms * 1e-3), 1),
+                      "vs_forward": round(b_ms / ms_per_step, 3)}
+        del dY, dfin, bws
 
     if not args.no_decode:
         wd = synth.WORKLOADS["decode-b64-H80-N128"]

@@ -165,11 +165,18 @@ hipError_t run_forward(const Prepared& pp, const void* X, const float* log_a, co
 // reversed run's and the forward chunk-state run's (both one chunk per state
 // block, kept for the log-decay gradient) and one shared by the two
 // role-exchanged runs.
+//
+// bf16 shapes that the fused chunk kernel covers need only the reversed dY and
+// C, the two state runs and, when a chunk's heads are split over several
+// workgroups, fp32 partials of dB and dC per head slice.
 struct BwdLayout {
   size_t cur, rev_dy, rev_x, dx_rev, rev_b, rev_c, bcast, part, la_rev, states_t, lam_first;
+  size_t part_b, part_c;
   size_t fwd_a, fwd_f, fwd_s, total;
   size_t a_bytes, f_bytes, s_bytes;
   int Tr;          // tokens per row of the padded reversed layout (packed: an upper bound)
+  bool fused;      // the fused chunk kernel computes dX, d log a, dB and dC
+  int nsl;         // head slices per (chunk, group) in the fused kernel
 };
 
 // The role-exchanged runs (dB, dC) have headdim N, dstate P and one group per head.
@@ -184,16 +191,19 @@ ssd_shape swapped_shape(const ssd_shape* s) {
 ssd_status make_bwd_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk, int32_t gs, BwdLayout* out) {
   ssd_status st = check_shape(s, cu, chunk);
   if (st != SSD_OK) return st;
-  const ssd_shape w = swapped_shape(s);
-  st = check_shape(&w, cu, chunk);  // dstate <= 128 and, for bf16, headdim >= 32
-  if (st != SSD_OK) return st;
   if (gs <= 0) gs = default_state_block(s, cu, chunk);
   st = check_state_block(s, gs);
   if (st != SSD_OK) return st;
   const int64_t P = s->headdim, N = s->dstate, H = s->nheads, G = s->ngroups;
-  if (P + N > 192 || chunk > 256) return SSD_ERR_UNSUPPORTED;  // the log-decay kernel's register rows
-  if (ssd::dlog_chunk_lds_bytes((int)P, (int)N, chunk, s->dtype == SSD_DTYPE_BF16 ? 2 : 4) > ssd::kMaxLdsBytes)
-    return SSD_ERR_UNSUPPORTED;
+  const bool fused = ssd::bwd_chunk_supported((int)P, (int)N, chunk, s->dtype == SSD_DTYPE_BF16);
+  const ssd_shape w = swapped_shape(s);
+  if (!fused) {
+    st = check_shape(&w, cu, chunk);  // dstate <= 128 and, for bf16, headdim >= 32
+    if (st != SSD_OK) return st;
+    if (P + N > 192 || chunk > 256) return SSD_ERR_UNSUPPORTED;  // the log-decay kernel's register rows
+    if (ssd::dlog_chunk_lds_bytes((int)P, (int)N, chunk, s->dtype == SSD_DTYPE_BF16 ? 2 : 4) > ssd::kMaxLdsBytes)
+      return SSD_ERR_UNSUPPORTED;
+  }
   const int64_t T = s->seqlen;
   const int64_t Tr = cu ? T + (int64_t)s->num_seqs * (chunk - 1) : T + (chunk - T % chunk) % chunk;
   if ((int64_t)s->batch * Tr > INT32_MAX / 2) return SSD_ERR_UNSUPPORTED;
@@ -201,37 +211,49 @@ ssd_status make_bwd_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk,
   sr.seqlen = (int32_t)Tr;
   ssd_shape wr = w;
   wr.seqlen = (int32_t)Tr;
-  ssd_layout La, Lf, Ls1, Ls2;
+  ssd_layout La, Lf, Ls1{}, Ls2{};
   if ((st = check_shape(&sr, cu, chunk)) != SSD_OK) return st;
   if ((st = make_layout(&sr, cu, chunk, 1, &La)) != SSD_OK) return st;
   if ((st = make_layout(s, cu, chunk, 1, &Lf)) != SSD_OK) return st;
-  if ((st = make_layout(&wr, cu, chunk, default_state_block(&wr, cu, chunk), &Ls1)) != SSD_OK) return st;
-  if ((st = make_layout(&w, cu, chunk, default_state_block(&w, cu, chunk), &Ls2)) != SSD_OK) return st;
+  if (!fused) {
+    if ((st = make_layout(&wr, cu, chunk, default_state_block(&wr, cu, chunk), &Ls1)) != SSD_OK) return st;
+    if ((st = make_layout(&w, cu, chunk, default_state_block(&w, cu, chunk), &Ls2)) != SSD_OK) return st;
+  }
   const size_t esz = s->dtype == SSD_DTYPE_BF16 ? 2 : 4;
   const size_t tok = (size_t)s->batch * T, tokr = (size_t)s->batch * Tr;
   const size_t tmax = tok > tokr ? tok : tokr;
   const size_t nseq = cu ? s->num_seqs : s->batch;
   if ((int64_t)tmax * H * (P > N ? P : N) > kMaxElems) return SSD_ERR_UNSUPPORTED;
   BwdLayout L{};
+  L.fused = fused;
+  L.nsl = fused ? ssd::bwd_chunk_slices(Lf.nslots, (int)G, (int)H) : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
   L.cur = take((nseq + 1) * 4);
   L.rev_dy = take(tokr * H * P * esz);
-  L.rev_x = take(tokr * H * P * esz);
-  L.dx_rev = take(tokr * H * P * esz);
-  L.rev_b = take(tokr * G * N * esz);
   L.rev_c = take(tokr * G * N * esz);
-  L.bcast = take(tmax * H * N * esz);
-  L.part = take(tmax * H * N * 4);
   L.la_rev = take(tokr * H * 4);
-  L.states_t = take(nseq * H * P * N * 4);
   L.lam_first = take(nseq * H * P * N * 4);
+  if (fused) {
+    if (L.nsl > 1) {
+      if ((int64_t)L.nsl * tok * G * N > kMaxElems) return SSD_ERR_UNSUPPORTED;
+      L.part_b = take((size_t)L.nsl * tok * G * N * 4);
+      L.part_c = take((size_t)L.nsl * tok * G * N * 4);
+    }
+  } else {
+    L.rev_x = take(tokr * H * P * esz);
+    L.dx_rev = take(tokr * H * P * esz);
+    L.rev_b = take(tokr * G * N * esz);
+    L.bcast = take(tmax * H * N * esz);
+    L.part = take(tmax * H * N * 4);
+    L.states_t = take(nseq * H * P * N * 4);
+  }
   L.a_bytes = La.total_bytes;
   L.f_bytes = Lf.total_bytes;
   L.s_bytes = Ls1.total_bytes > Ls2.total_bytes ? Ls1.total_bytes : Ls2.total_bytes;
   L.fwd_a = take(L.a_bytes);
   L.fwd_f = take(L.f_bytes);
-  L.fwd_s = take(L.s_bytes);
+  if (!fused) L.fwd_s = take(L.s_bytes);
   L.total = off;
   L.Tr = (int)Tr;
   *out = L;
@@ -390,9 +412,78 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
   const long nseq = packed ? s->num_seqs : s->batch;
   const bool bf16 = s->dtype == SSD_DTYPE_BF16;
   const int esz = bf16 ? 2 : 4;
-  // Dimensions of the four internal runs.
+  hipStream_t hs = (hipStream_t)stream;
+  void* rev_dy = w + L.rev_dy;
+  void* rev_c = w + L.rev_c;
+  float* la_rev = reinterpret_cast<float*>(w + L.la_rev);
+  float* lam_first = reinterpret_cast<float*>(w + L.lam_first);
   ssd_shape sr = *s;
   sr.seqlen = Tr;
+  if (L.fused) {
+    // Two state runs with one chunk per state block, then one kernel for the
+    // four gradients of every chunk.
+    Prepared pa, pf;
+    if ((st = prepare(kAll, dY, log_a, C, B, dX, cur, chunk, 1, &sr, w + L.fwd_a, L.a_bytes, &pa)) != SSD_OK)
+      return st;
+    if ((st = prepare(kAll, X, log_a, B, C, dX, cu_seqlens, chunk, 1, s, w + L.fwd_f, L.f_bytes, &pf)) != SSD_OK)
+      return st;
+    hipError_t e = hipSuccess;
+    if (packed) e = ssd::launch_padded_offsets(cu_seqlens, cur, S, chunk, hs);
+    if (e == hipSuccess) e = ssd::launch_gather_rows(dY, rev_dy, cu_seqlens, cur, S, rows, T, Tr, H, H, P * esz, 1, hs);
+    if (e == hipSuccess) e = ssd::launch_gather_rows(C, rev_c, cu_seqlens, cur, S, rows, T, Tr, G, G, N * esz, 1, hs);
+    if (e == hipSuccess) e = ssd::launch_reverse_log_decay(log_a, la_rev, cu_seqlens, cur, S, rows, T, Tr, H, hs);
+    // Adjoint states: the reversed run over dY (x role) and C (B role) from the
+    // final-state gradient; its chunk start states are the adjoints at the
+    // forward chunk ends.
+    if (e == hipSuccess) {
+      const ssd::SegArgs sa = ssd::seg_args(pa.d, la_rev, cur, ssd::Mamba2Args{});
+      e = ssd::launch_chunk_state(pa.d, rev_dy, rev_c, pa.ws, hs, &sa);
+    }
+    if (e == hipSuccess)
+      e = ssd::launch_state_passing(pa.d, cur, dfinal_state, dinitial_state ? lam_first : nullptr, pa.ws, hs);
+    // Forward chunk start states and segment sums.
+    if (e == hipSuccess) {
+      const ssd::SegArgs sa = ssd::seg_args(pf.d, log_a, cu_seqlens, ssd::Mamba2Args{});
+      e = ssd::launch_chunk_state(pf.d, X, B, pf.ws, hs, &sa);
+    }
+    if (e == hipSuccess) e = ssd::launch_state_passing(pf.d, cu_seqlens, initial_state, nullptr, pf.ws, hs);
+    if (e == hipSuccess) {
+      ssd::BwdChunkArgs a{};
+      a.X = X;
+      a.dY = dY;
+      a.B = B;
+      a.C = C;
+      a.la = log_a;
+      a.ftable = pf.ws.table;
+      a.fbtable = pf.ws.btable;
+      a.fcs = pf.ws.cs;
+      a.fstart = pf.ws.start_states;
+      a.rstart = pa.ws.start_states;
+      a.cu = cu_seqlens;
+      a.cur = cur;
+      a.spr = pf.d.slots_per_row;
+      a.spr_r = pa.d.slots_per_row;
+      a.nslots = pf.d.nslots;
+      a.tokens = (long)rows * T;
+      a.dX = dX;
+      a.dla = dlog_a;
+      a.dB = dB;
+      a.dC = dC;
+      a.part_b = L.nsl > 1 ? reinterpret_cast<float*>(w + L.part_b) : nullptr;
+      a.part_c = L.nsl > 1 ? reinterpret_cast<float*>(w + L.part_c) : nullptr;
+      a.H = H;
+      a.G = G;
+      a.P = P;
+      a.N = N;
+      a.Q = chunk;
+      a.nsl = L.nsl;
+      e = ssd::launch_bwd_chunks(a, hs);
+    }
+    if (e == hipSuccess && dinitial_state)
+      e = ssd::launch_dinit(log_a, lam_first, dinitial_state, cu_seqlens, (int)nseq, T, H, P * N, hs);
+    return hip_status(e);
+  }
+  // Dimensions of the four internal runs of the general path.
   const ssd_shape sw = swapped_shape(s);
   ssd_shape swr = sw;
   swr.seqlen = Tr;
@@ -404,17 +495,12 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
   if ((st = prepare(kAll, X, log_a, B, C, dX, cu_seqlens, chunk, 0, &sw, w + L.fwd_s, L.s_bytes, &pbf)) != SSD_OK)
     return st;
   pbr.d.y_f32 = pbf.d.y_f32 = 1;  // per-head partials in fp32, rounded once after the group sum
-  hipStream_t hs = (hipStream_t)stream;
-  void* rev_dy = w + L.rev_dy;
   void* rev_x = w + L.rev_x;
   void* dx_rev = w + L.dx_rev;
   void* rev_b = w + L.rev_b;
-  void* rev_c = w + L.rev_c;
   void* bcast = w + L.bcast;
   float* part = reinterpret_cast<float*>(w + L.part);
-  float* la_rev = reinterpret_cast<float*>(w + L.la_rev);
   float* states_t = reinterpret_cast<float*>(w + L.states_t);
-  float* lam_first = reinterpret_cast<float*>(w + L.lam_first);
 
   hipError_t e = hipSuccess;
   if (packed) e = ssd::launch_padded_offsets(cu_seqlens, cur, S, chunk, hs);

@@ -1,0 +1,535 @@
+// ssd_bwd_chunk.hip -- the backward pass of one chunk in one kernel (bf16, MFMA).
+//
+// The output of the chunked algorithm is y = M x with M = L o (C B^T) inside a
+// chunk plus the contributions that pass through the chunk-entering state
+// ("Transformers are SSMs" paper card, Method 5, the four terms of the chunked
+// algorithm). Its reverse mode for one chunk and head, with h the state
+// entering the chunk, lam the adjoint leaving it (the gradient reaching the
+// chunk's last state from later outputs, decayed onto it), cs the cumulative
+// log decay inside the chunk, e_s = 2^{cs_last - cs_s} and W = L o (dY X^T):
+//   dX = (L o C B^T)^T dY + diag(e) B lam^T
+//   dC = W B               + diag(2^cs) dY h      (summed over the group's heads)
+//   dB = W^T C             + diag(e) X lam        (summed over the group's heads)
+//   d log a_t = sum over pairs (s, u) with s < t <= u of M_us (dY_u . x_s),
+// the pairs being both inside the chunk, s before it (through h), u after it
+// (through lam) or both outside. The last form is a_t <lam_t, h_{t-1}> written
+// out: every token pair whose decay product contains a_t contributes once.
+//
+// One workgroup (4 waves) takes one chunk, one group and a slice of its heads:
+// B, C and C B^T are loaded once, dB and dC accumulate over the slice's heads in
+// registers, and each head's X, dY, h and lam pass through LDS once. The
+// products run as 16x16x32 bf16 MFMAs with fp32 accumulation, transposed so
+// that each lane holds four consecutive output channels of one token. Wave w
+// owns the 16-token strips w and QT-1-w (QT = Q / 16 strips), which balances the
+// triangular work of the causal mask.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+constexpr int kBwdThreads = 256;
+
+template <int P, int N, int Q>
+struct BwdCfg {
+  static constexpr int QT = Q / 16;         // 16-token strips
+  static constexpr int SPW = QT / 4;        // strips per wave
+  static constexpr int NT = N / 16, PT = P / 16;
+  static constexpr int pN = lds_pitch(N), pP = lds_pitch(P), pQ = lds_pitch(Q);
+  // 16-bit LDS tiles: B, C [Q][pN]; X, dY [Q][pP]; one region R that holds in
+  // turn W (bf16, [Q][pQ], row u, column s) and the states h, lam ([P][pN] each).
+  static constexpr int offB = 0, offC = Q * pN, offX = 2 * Q * pN, offY = offX + Q * pP, offR = offY + Q * pP;
+  static constexpr int rElems = (Q * pQ > 2 * P * pN) ? Q * pQ : 2 * P * pN;
+  static constexpr int halfElems = offR + rElems;
+  // fp32 after the tiles: cs [2][Q] (two heads in flight), column partials [4][Q],
+  // row sums, b and c terms [Q] each, the state dot products [4].
+  static constexpr int floats = 2 * Q + 4 * Q + 3 * Q + 4;
+  static constexpr size_t lds_bytes = (size_t)halfElems * 2 + (size_t)floats * 4;
+  static_assert(Q == 64 || Q == 128, "chunk of 64 or 128 tokens");
+  static_assert(P % 32 == 0 && N % 32 == 0, "head and state sizes in multiples of 32");
+  static_assert(halfElems % 8 == 0, "fp32 area 16-byte aligned");
+};
+
+// The 8 bf16 values of an operand scaled by one factor, rounded back to bf16.
+__device__ __forceinline__ u32x4 scale_frag1(u32x4 v, float f) {
+  u32x4 r;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r[c] = pack_bf16x2(bf16_lo(v[c]) * f, bf16_hi(v[c]) * f);
+  return r;
+}
+
+// Dot product of 4 fp32 values with 4 bf16 values (two words).
+__device__ __forceinline__ float dot4_bf16(f32x4 a, u32x2 b) {
+  return a[0] * bf16_lo(b.x) + a[1] * bf16_hi(b.x) + a[2] * bf16_lo(b.y) + a[3] * bf16_hi(b.y);
+}
+
+// Tile staging: ROWS x COLS 16-bit values from global memory (row stride
+// `gstride` bytes; offsets past the descriptor's range read as zero) into
+// registers, then into LDS with row pitch PITCH.
+template <int ROWS, int COLS>
+struct Stage {
+  static constexpr int kPieces = ROWS * COLS / 8 / kBwdThreads;  // 16-byte pieces per thread
+  static_assert(kPieces * 8 * kBwdThreads == ROWS * COLS, "tile of whole pieces per thread");
+  u32x4 v[kPieces];
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t gstride, int tid) {
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int i = tid + k * kBwdThreads;
+      v[k] = buf_load16(r, (uint32_t)(i / (COLS / 8)) * gstride + (uint32_t)(i % (COLS / 8)) * 16);
+    }
+  }
+  template <int PITCH>
+  __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int i = tid + k * kBwdThreads;
+      *reinterpret_cast<u32x4*>(dst + (i / (COLS / 8)) * PITCH + (i % (COLS / 8)) * 8) = v[k];
+    }
+  }
+};
+
+template <int P, int N, int Q>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Bm,
+    const uint16_t* __restrict__ Cm, const float* __restrict__ la, const int4* __restrict__ ftable,
+    const int4* __restrict__ fbtable, const float* __restrict__ fcs, const uint16_t* __restrict__ fstart,
+    const uint16_t* __restrict__ rstart, const int32_t* __restrict__ cu, const int32_t* __restrict__ cur, long spr,
+    long spr_r, uint16_t* __restrict__ dX, float* __restrict__ dla, void* __restrict__ dBo, void* __restrict__ dCo,
+    long tokens, int H, int G, int nsl) {
+  using K = BwdCfg<P, N, Q>;
+  constexpr int QT = K::QT, SPW = K::SPW, NT = K::NT, PT = K::PT;
+  constexpr int pN = K::pN, pP = K::pP, pQ = K::pQ;
+  const long unit = xcd_unit(blockIdx.x, gridDim.x);
+  const int sl = (int)(unit % nsl);
+  const long rest = unit / nsl;
+  const int g = (int)(rest % G);
+  const long slot = rest / G;
+  // One chunk per state block in the forward state run: its block table is
+  // written for every slot, its chunk table only for slots that hold a chunk.
+  if (fbtable[slot].z <= 0) return;
+  const int4 rec = ftable[slot];
+  const int len = rec.z;
+  if (len <= 0) return;
+  const int seq = rec.x, tok0 = rec.y, jc = rec.w;
+  const int hpg = H / G;
+  const int hbeg = g * hpg + (int)((long)sl * hpg / nsl);
+  const int hend = g * hpg + (int)((long)(sl + 1) * hpg / nsl);
+  // The reversed run's slot of this chunk: reversed chunk nch - 1 - jc.
+  int nch;
+  long rslot;
+  if (cu == nullptr) {
+    nch = (int)spr;
+    rslot = (long)seq * spr_r + (nch - 1 - jc);
+  } else {
+    nch = (cu[seq + 1] - cu[seq] + Q - 1) / Q;
+    rslot = cur[seq] / Q + seq + (nch - 1 - jc);
+  }
+  const bool last_chunk = jc == nch - 1;
+
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* Bs = lds + K::offB;
+  uint16_t* Cs = lds + K::offC;
+  uint16_t* Xs = lds + K::offX;
+  uint16_t* Ys = lds + K::offY;
+  uint16_t* R = lds + K::offR;
+  uint16_t* Hs = R;
+  uint16_t* Ls = R + P * pN;
+  float* csl = reinterpret_cast<float*>(lds + K::halfElems);  // [2][Q]
+  float* colp = csl + 2 * Q;                                  // [4][Q]
+  float* rowv = colp + 4 * Q;
+  float* bv = rowv + Q;
+  float* cv = bv + Q;
+  float* red = cv + Q;  // [4]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, g4 = lane >> 4;
+  auto strip = [&](int k) { return k == 0 ? w : QT - 1 - w; };
+
+  const uint32_t xstride = (uint32_t)(H * P * 2), bstride = (uint32_t)(G * N * 2);
+  auto x_rsrc = [&](const uint16_t* base, int h) {
+    return make_rsrc(base + ((long)tok0 * H + h) * P, (uint32_t)len * xstride);
+  };
+  auto state_rsrc = [&](const uint16_t* base, long s, int h) {
+    return make_rsrc(base + (s * H + h) * (long)(P * N), (uint32_t)(P * N * 2));
+  };
+
+  // ---- prologue: B, C, the first head's X, dY and segment sums
+  {
+    Stage<Q, N> sb, sc;
+    sb.load(make_rsrc(Bm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride), bstride, tid);
+    sc.load(make_rsrc(Cm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride), bstride, tid);
+    Stage<Q, P> sx, sy;
+    sx.load(x_rsrc(X, hbeg), xstride, tid);
+    sy.load(x_rsrc(dY, hbeg), xstride, tid);
+    if (tid < Q) csl[tid] = fcs[(slot * H + hbeg) * (long)Q + tid];
+    sb.template store<pN>(Bs, tid);
+    sc.template store<pN>(Cs, tid);
+    sx.template store<pP>(Xs, tid);
+    sy.template store<pP>(Ys, tid);
+  }
+  __syncthreads();
+
+  // C B^T of the wave's tiles, transposed (row s, column u), kept for every head.
+  f32x4 m1[SPW][QT];
+#pragma unroll
+  for (int k = 0; k < SPW; ++k) {
+    const int i = strip(k);
+#pragma unroll
+    for (int j = 0; j < QT; ++j) {
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+      if (j <= i) {
+#pragma unroll
+        for (int kk = 0; kk < N / 32; ++kk)
+          a = mfma16x16x32(frag_k_cols(Bs, pN, 16 * j, 32 * kk, lane), frag_k_cols(Cs, pN, 16 * i, 32 * kk, lane), a);
+      }
+      m1[k][j] = a;
+    }
+  }
+
+  f32x4 dc[SPW][NT], db[SPW][NT];  // dC^T, dB^T: row n, column token
+#pragma unroll
+  for (int k = 0; k < SPW; ++k)
+#pragma unroll
+    for (int m = 0; m < NT; ++m) dc[k][m] = db[k][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int h = hbeg; h < hend; ++h) {
+    const float* cs = csl + ((h - hbeg) & 1) * Q;
+    // The states of this head, staged in registers until R is free.
+    Stage<P, N> sh, sl_;
+    sh.load(state_rsrc(fstart, slot, h), (uint32_t)(N * 2), tid);
+    sl_.load(state_rsrc(rstart, rslot, h), (uint32_t)(N * 2), tid);
+    const float anext = last_chunk ? 1.f : fast_exp2(la[(long)(tok0 + len) * H + h] * kLog2e);
+
+    // (R is free: the barriers that close the previous head follow its last read.)
+    for (int q = lane; q < Q; q += 64) colp[w * Q + q] = 0.f;  // this wave's row only
+
+    // ---- dY X^T, the mask, W = L o dY X^T (to R) and the pair sums of d log a
+    uint32_t w1p[SPW][QT][2];  // L o C B^T, bf16 pairs, written to R after W is used
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int i = strip(k);
+      const int u = 16 * i + c;
+      const float csu = cs[u];
+      float rs = 0.f;
+#pragma unroll
+      for (int j = 0; j < QT; ++j) {
+        w1p[k][j][0] = w1p[k][j][1] = 0u;
+        if (j <= i) {
+          f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < P / 32; ++kk)
+            m2 = mfma16x16x32(frag_k_cols(Xs, pP, 16 * j, 32 * kk, lane), frag_k_cols(Ys, pP, 16 * i, 32 * kk, lane),
+                              m2);
+          const f32x4 css = *reinterpret_cast<const f32x4*>(cs + 16 * j + 4 * g4);
+          float w1[4], w2[4], sv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int s = 16 * j + 4 * g4 + r;
+            const float l = s <= u ? fast_exp2(csu - css[r]) : 0.f;
+            w1[r] = l * m1[k][j][r];
+            w2[r] = l * m2[r];
+            sv[r] = s < u ? w1[r] * m2[r] : 0.f;
+            rs += sv[r];
+          }
+          w1p[k][j][0] = pack_bf16x2(w1[0], w1[1]);
+          w1p[k][j][1] = pack_bf16x2(w1[2], w1[3]);
+          *reinterpret_cast<u32x2*>(R + u * pQ + 16 * j + 4 * g4) =
+              u32x2{pack_bf16x2(w2[0], w2[1]), pack_bf16x2(w2[2], w2[3])};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) sv[r] += __shfl_xor(sv[r], off);
+          }
+          if (c == 0) {
+            f32x4* cp = reinterpret_cast<f32x4*>(colp + w * Q + 16 * j + 4 * g4);
+            *cp += f32x4{sv[0], sv[1], sv[2], sv[3]};
+          }
+        } else if (j == i + 1 && (i & 1) == 0) {
+          // above the diagonal, inside the 32-token blocks the products read
+          *reinterpret_cast<u32x2*>(R + u * pQ + 16 * j + 4 * g4) = u32x2{0u, 0u};
+        }
+      }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      if (g4 == 0) rowv[u] = rs;
+    }
+    __syncthreads();
+
+    // ---- dC^T += B^T W^T and dB^T += C^T W (W in R)
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int i = strip(k);
+#pragma unroll
+      for (int kk = 0; kk < QT / 2; ++kk) {
+        if (kk <= i / 2) {
+          const u32x4 bop = frag_k_cols(R, pQ, 16 * i, 32 * kk, lane);
+#pragma unroll
+          for (int m = 0; m < NT; ++m)
+            dc[k][m] = mfma16x16x32(frag_k_rows_natural(Bs, pN, 32 * kk, 16 * m, lane), bop, dc[k][m]);
+        }
+        if (kk >= i / 2) {
+          const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * i, lane);
+#pragma unroll
+          for (int m = 0; m < NT; ++m)
+            db[k][m] = mfma16x16x32(frag_k_rows_natural(Cs, pN, 32 * kk, 16 * m, lane), bop, db[k][m]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- L o C B^T to R; dX^T = dY^T (L o C B^T)
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int i = strip(k);
+      const int u = 16 * i + c;
+#pragma unroll
+      for (int j = 0; j < QT; ++j) {
+        if (j <= i || (j == i + 1 && (i & 1) == 0))
+          *reinterpret_cast<u32x2*>(R + u * pQ + 16 * j + 4 * g4) = u32x2{w1p[k][j][0], w1p[k][j][1]};
+      }
+    }
+    __syncthreads();
+    f32x4 dx[SPW][PT];
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int j = strip(k);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) dx[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < QT / 2; ++kk) {
+        if (kk >= j / 2) {
+          const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * j, lane);
+#pragma unroll
+          for (int pt = 0; pt < PT; ++pt)
+            dx[k][pt] = mfma16x16x32(frag_k_rows_natural(Ys, pP, 32 * kk, 16 * pt, lane), bop, dx[k][pt]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- the states to R, and <lam, h> for the pairs that span the chunk
+    sh.template store<pN>(Hs, tid);
+    sl_.template store<pN>(Ls, tid);
+    {
+      float d = 0.f;
+#pragma unroll
+      for (int k = 0; k < Stage<P, N>::kPieces; ++k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          d += bf16_lo(sh.v[k][q]) * bf16_lo(sl_.v[k][q]) + bf16_hi(sh.v[k][q]) * bf16_hi(sl_.v[k][q]);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) d += __shfl_xor(d, off);
+      if (lane == 0) red[w] = d;
+    }
+    __syncthreads();
+
+    // The next head's inputs, staged in registers while this head finishes.
+    const bool more = h + 1 < hend;
+    Stage<Q, P> nx, ny;
+    float ncs = 0.f;
+    if (more) {
+      nx.load(x_rsrc(X, h + 1), xstride, tid);
+      ny.load(x_rsrc(dY, h + 1), xstride, tid);
+      if (tid < Q) ncs = fcs[(slot * H + h + 1) * (long)Q + tid];
+    }
+
+    // ---- terms through the states
+    const float cs_last = cs[Q - 1];
+    const rsrc_t rdx = x_rsrc(dX, h);
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int i = strip(k);
+      const int u = 16 * i + c;  // the lane's token (u as a query, s as a key)
+      const float fu = fast_exp2(cs[u]);
+      const float es = anext * fast_exp2(cs_last - cs[u]);
+      // b_u = 2^{cs_u} dY_u . (h C_u)
+      f32x4 t[PT];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) t[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < N / 32; ++kk) {
+        const u32x4 bop = frag_k_cols(Cs, pN, 16 * i, 32 * kk, lane);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) t[pt] = mfma16x16x32(frag_k_cols(Hs, pN, 16 * pt, 32 * kk, lane), bop, t[pt]);
+      }
+      float b = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+        b += dot4_bf16(t[pt], *reinterpret_cast<const u32x2*>(Ys + u * pP + 16 * pt + 4 * g4));
+      b += __shfl_xor(b, 16);
+      b += __shfl_xor(b, 32);
+      if (g4 == 0) bv[u] = b * fu;
+      // dX_off = e_s lam B_s; c_s = x_s . dX_off
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) t[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < N / 32; ++kk) {
+        const u32x4 bop = frag_k_cols(Bs, pN, 16 * i, 32 * kk, lane);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) t[pt] = mfma16x16x32(frag_k_cols(Ls, pN, 16 * pt, 32 * kk, lane), bop, t[pt]);
+      }
+      float cc = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        t[pt] *= es;
+        cc += dot4_bf16(t[pt], *reinterpret_cast<const u32x2*>(Xs + u * pP + 16 * pt + 4 * g4));
+        dx[k][pt] += t[pt];
+      }
+      cc += __shfl_xor(cc, 16);
+      cc += __shfl_xor(cc, 32);
+      if (g4 == 0) cv[u] = cc;
+      // dC^T += h^T (2^cs dY)^T ; dB^T += lam^T (e X)^T
+#pragma unroll
+      for (int kk = 0; kk < P / 32; ++kk) {
+        const u32x4 yop = scale_frag1(frag_k_cols(Ys, pP, 16 * i, 32 * kk, lane), fu);
+        const u32x4 xop = scale_frag1(frag_k_cols(Xs, pP, 16 * i, 32 * kk, lane), es);
+#pragma unroll
+        for (int m = 0; m < NT; ++m) {
+          dc[k][m] = mfma16x16x32(frag_k_rows_natural(Hs, pN, 32 * kk, 16 * m, lane), yop, dc[k][m]);
+          db[k][m] = mfma16x16x32(frag_k_rows_natural(Ls, pN, 32 * kk, 16 * m, lane), xop, db[k][m]);
+        }
+      }
+      // dX of the lane's token, four consecutive channels per P tile
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+        buf_store8(u32x2{pack_bf16x2(dx[k][pt][0], dx[k][pt][1]), pack_bf16x2(dx[k][pt][2], dx[k][pt][3])}, rdx,
+                   (uint32_t)u * xstride + (uint32_t)(16 * pt + 4 * g4) * 2);
+    }
+    __syncthreads();
+
+    // ---- d log a of the chunk's tokens: sum_{k<t} (col_k - row_k + c_k) + sum_{u>=t} b_u + D
+    if (w == 0) {
+      constexpr int EPL = Q / 64;
+      float v[EPL], bb[EPL], pv[EPL], pb[EPL];
+      float sv = 0.f, sb = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int t = lane * EPL + e;
+        v[e] = colp[t] + colp[Q + t] + colp[2 * Q + t] + colp[3 * Q + t] - rowv[t] + cv[t];
+        bb[e] = bv[t];
+        pv[e] = sv;
+        pb[e] = sb;
+        sv += v[e];
+        sb += bb[e];
+      }
+      float iv = sv, ib = sb;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float tv = __shfl_up(iv, d), tb = __shfl_up(ib, d);
+        if (lane >= d) {
+          iv += tv;
+          ib += tb;
+        }
+      }
+      const float totb = __shfl(ib, 63);
+      const float ev = iv - sv, eb = ib - sb;
+      const float dspan = anext * fast_exp2(cs_last) * (red[0] + red[1] + red[2] + red[3]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int t = lane * EPL + e;
+        if (t < len) dla[(long)(tok0 + t) * H + h] = ev + pv[e] + (totb - eb - pb[e]) + dspan;
+      }
+    }
+    if (more) {
+      nx.template store<pP>(Xs, tid);
+      ny.template store<pP>(Ys, tid);
+      if (tid < Q) csl[((h + 1 - hbeg) & 1) * Q + tid] = ncs;
+    }
+    __syncthreads();
+  }
+
+  // ---- dB, dC of the slice's heads: bf16 when one slice covers the group,
+  // else fp32 partials [nsl][tokens][G][N] that a reduction sums.
+#pragma unroll
+  for (int k = 0; k < SPW; ++k) {
+    const int u = 16 * strip(k) + c;
+    if (nsl == 1) {
+      const rsrc_t rb = make_rsrc(reinterpret_cast<uint16_t*>(dBo) + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
+      const rsrc_t rc = make_rsrc(reinterpret_cast<uint16_t*>(dCo) + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const uint32_t off = (uint32_t)u * bstride + (uint32_t)(16 * m + 4 * g4) * 2;
+        buf_store8(u32x2{pack_bf16x2(db[k][m][0], db[k][m][1]), pack_bf16x2(db[k][m][2], db[k][m][3])}, rb, off);
+        buf_store8(u32x2{pack_bf16x2(dc[k][m][0], dc[k][m][1]), pack_bf16x2(dc[k][m][2], dc[k][m][3])}, rc, off);
+      }
+    } else {
+      const long base = ((long)sl * tokens + tok0) * G * N + (long)g * N;
+      const uint32_t fstride = (uint32_t)(G * N * 4);
+      const rsrc_t rb = make_rsrc(reinterpret_cast<float*>(dBo) + base, (uint32_t)len * fstride);
+      const rsrc_t rc = make_rsrc(reinterpret_cast<float*>(dCo) + base, (uint32_t)len * fstride);
+#pragma unroll
+      for (int m = 0; m < NT; ++m) {
+        const uint32_t off = (uint32_t)u * fstride + (uint32_t)(16 * m + 4 * g4) * 4;
+        buf_store16(__builtin_bit_cast(u32x4, db[k][m]), rb, off);
+        buf_store16(__builtin_bit_cast(u32x4, dc[k][m]), rc, off);
+      }
+    }
+  }
+}
+
+// out[t][g][n] = sum over slices of part[sl][t][g][n], rounded to bf16 (four per thread).
+__global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                        long n4, int nsl) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 a = reinterpret_cast<const f32x4*>(part)[i];
+  for (int s = 1; s < nsl; ++s) a += reinterpret_cast<const f32x4*>(part)[(long)s * n4 + i];
+  reinterpret_cast<u32x2*>(out)[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+}
+
+template <int P, int N, int Q>
+static hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, hipStream_t stream) {
+  using K = BwdCfg<P, N, Q>;
+  auto kern = bwd_chunk_kernel<P, N, Q>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)K::lds_bytes);
+  if (e != hipSuccess) return e;
+  const long grid = a.nslots * a.G * a.nsl;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), K::lds_bytes, stream,
+                     reinterpret_cast<const uint16_t*>(a.X), reinterpret_cast<const uint16_t*>(a.dY),
+                     reinterpret_cast<const uint16_t*>(a.B), reinterpret_cast<const uint16_t*>(a.C), a.la, a.ftable,
+                     a.fbtable, a.fcs, reinterpret_cast<const uint16_t*>(a.fstart),
+                     reinterpret_cast<const uint16_t*>(a.rstart), a.cu, a.cur, a.spr, a.spr_r,
+                     reinterpret_cast<uint16_t*>(a.dX), a.dla, a.nsl == 1 ? a.dB : a.part_b,
+                     a.nsl == 1 ? a.dC : a.part_c, a.tokens, a.H, a.G, a.nsl);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.nsl == 1) return e;
+  const long n4 = a.tokens * a.G * a.N / 4;
+  const unsigned blocks = (unsigned)((n4 + 255) / 256);
+  hipLaunchKernelGGL(slice_sum_kernel, dim3(blocks), dim3(256), 0, stream, a.part_b,
+                     reinterpret_cast<uint16_t*>(a.dB), n4, a.nsl);
+  hipLaunchKernelGGL(slice_sum_kernel, dim3(blocks), dim3(256), 0, stream, a.part_c,
+                     reinterpret_cast<uint16_t*>(a.dC), n4, a.nsl);
+  return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_bwd_chunk_q(const BwdChunkArgs& a, hipStream_t stream) {
+  switch (a.Q) {
+    case 64: return launch_bwd_chunk_t<P, N, 64>(a, stream);
+    case 128: return launch_bwd_chunk_t<P, N, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The (P, N) pairs built: P in {32, 64} with N in {64, 128}, and P = 128 with N = 64.
+bool bwd_chunk_supported(int P, int N, int Q, bool bf16) {
+  if (!bf16 || (Q != 64 && Q != 128)) return false;
+  return ((P == 32 || P == 64) && (N == 64 || N == 128)) || (P == 128 && N == 64);
+}
+
+int bwd_chunk_slices(long nslots, int G, int H) {
+  const int hpg = H / G;
+  const long wgs = nslots * G;
+  long nsl = (256 + wgs - 1) / wgs;  // at least one workgroup per compute unit
+  if (nsl > hpg) nsl = hpg;
+  return nsl < 1 ? 1 : (int)nsl;
+}
+
+hipError_t launch_bwd_chunks(const BwdChunkArgs& a, hipStream_t stream) {
+  if (!bwd_chunk_supported(a.P, a.N, a.Q, true)) return hipErrorInvalidValue;
+  if (a.P == 32) return a.N == 64 ? launch_bwd_chunk_q<32, 64>(a, stream) : launch_bwd_chunk_q<32, 128>(a, stream);
+  if (a.P == 64) return a.N == 64 ? launch_bwd_chunk_q<64, 64>(a, stream) : launch_bwd_chunk_q<64, 128>(a, stream);
+  return launch_bwd_chunk_q<128, 64>(a, stream);
+}
+
+}  // namespace ssd

@@ -57,6 +57,9 @@ namespace {
 
 constexpr int kScanWaves = 8;
 constexpr int kScanThreads = kScanWaves * 64;
+// Output forms of the bf16 kernels: plain bf16, bf16 through the silu(z) gate,
+// or fp32 (per-head partials that the backward pass sums before rounding).
+constexpr int kOutPlain = 0, kOutGated = 1, kOutF32 = 2;
 
 template <int P, int N>
 struct ScanCfg {
@@ -167,12 +170,14 @@ size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q) {
 }
 
 // ITW: query tiles per wave (1 for chunks of up to 128 tokens, 2 for 256).
-template <int P, int N, int ITW, bool GATE>
+template <int P, int N, int ITW, int OUT>
 __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
     const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
-    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q, int yf32) {
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q) {
+  constexpr bool GATE = OUT == kOutGated;  // silu(z) gate on the output
+  constexpr bool YF32 = OUT == kOutF32;    // fp32 output (partials summed before one rounding)
   using K = ScanCfg<P, N>;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
@@ -453,7 +458,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 #pragma unroll
       for (int pt = 0; pt < K::TP; ++pt) acc[pt] *= u;
       key_block(kbd, true);
-      if (yf32)
+      if constexpr (YF32)
         store_yT_f32<K::TP>(acc, make_rsrc(reinterpret_cast<float*>(Y) + (tok0 * H + h) * P, (uint32_t)(len * ldx * 4)),
                             yrow, g4);
       else
@@ -544,12 +549,14 @@ static bool chunk_scan_pair_fits(int P, int N, int Q, int H, int G) {
   return pair_shape(P, N) && (H / G) % 2 == 0 && Q <= 128 && chunk_scan_pair_lds_bytes(P, N, Q) <= kMaxLdsBytes;
 }
 
-template <int P, int N, bool GATE>
+template <int P, int N, int OUT>
 __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
     const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
-    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q, int yf32) {
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q) {
+  constexpr bool GATE = OUT == kOutGated;  // silu(z) gate on the output
+  constexpr bool YF32 = OUT == kOutF32;    // fp32 output (partials summed before one rounding)
   using K = PairCfg<P, N>;
   const int HH = H / 2;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
@@ -833,7 +840,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
       // consecutive p of P tile pt in lane group g4).
 #pragma unroll
       for (int hd = 0; hd < 2; ++hd)
-        if (yf32)
+        if constexpr (YF32)
           store_yT_f32<K::TP>(acc[hd],
                               make_rsrc(reinterpret_cast<float*>(Y) + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 4)),
                               yrow, g4);
@@ -993,13 +1000,13 @@ __global__ __launch_bounds__(256) void chunk_scan_f32_kernel(const float* __rest
 
 // ----------------------------------------------------------------------------
 
-template <int P, int N, bool GATE>
+template <int P, int N, int OUT>
 static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                                    const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
   if constexpr (pair_shape(P, N)) {
     if (chunk_scan_pair_fits(P, N, d.Q, d.H, d.G)) {
       const size_t lds = chunk_scan_pair_lds_bytes(P, N, d.Q);
-      auto kern = chunk_scan_pair_kernel<P, N, GATE>;
+      auto kern = chunk_scan_pair_kernel<P, N, OUT>;
       if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1009,12 +1016,12 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
                          reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
                          reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
                          reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
-                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q, d.y_f32);
+                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q);
       return hipGetLastError();
     }
   }
   const size_t lds = chunk_scan_bf16_lds_bytes(P, N, d.Q);
-  auto kern = d.Q > 128 ? chunk_scan_bf16_kernel<P, N, 2, GATE> : chunk_scan_bf16_kernel<P, N, 1, GATE>;
+  auto kern = d.Q > 128 ? chunk_scan_bf16_kernel<P, N, 2, OUT> : chunk_scan_bf16_kernel<P, N, 1, OUT>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1024,15 +1031,16 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
                      reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
                      reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
                      reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
-                     reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q, d.y_f32);
+                     reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q);
   return hipGetLastError();
 }
 
 template <int P, int N>
 static hipError_t launch_scan_gate(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                                    const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
-  return m2.z ? launch_scan_bf16<P, N, true>(d, X, B, C, Y, ws, stream, m2)
-              : launch_scan_bf16<P, N, false>(d, X, B, C, Y, ws, stream, m2);
+  if (d.y_f32) return launch_scan_bf16<P, N, kOutF32>(d, X, B, C, Y, ws, stream, m2);
+  return m2.z ? launch_scan_bf16<P, N, kOutGated>(d, X, B, C, Y, ws, stream, m2)
+              : launch_scan_bf16<P, N, kOutPlain>(d, X, B, C, Y, ws, stream, m2);
 }
 
 template <int P>

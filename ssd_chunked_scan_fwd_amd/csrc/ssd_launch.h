@@ -107,6 +107,29 @@ struct DlogArgs {
 hipError_t launch_dlog_chunks(const DlogArgs& a, hipStream_t stream);
 size_t dlog_chunk_lds_bytes(int P, int N, int Q, int esz);
 
+// The fused backward chunk kernel (bf16; ssd_bwd_chunk.hip): dX, d log a and
+// dB, dC of each chunk from the forward run's chunk-entering states (fstart)
+// and the reversed run's (rstart), one chunk per state block in both.
+struct BwdChunkArgs {
+  const void *X, *dY, *B, *C;   // forward layout, bf16
+  const float* la;
+  const int4* ftable;           // forward run: chunk records,
+  const int4* fbtable;          //   block records (written for every slot),
+  const float* fcs;             //   segment sums,
+  const void* fstart;           //   chunk start states (bf16)
+  const void* rstart;           // reversed run: chunk start states (bf16, padded reversed slots)
+  const int32_t *cu, *cur;
+  long spr, spr_r, nslots, tokens;
+  void* dX;
+  float* dla;
+  void *dB, *dC;                // bf16 [tokens][G][N]
+  float *part_b, *part_c;       // fp32 [nsl][tokens][G][N] when nsl > 1
+  int H, G, P, N, Q, nsl;
+};
+bool bwd_chunk_supported(int P, int N, int Q, bool bf16);
+int bwd_chunk_slices(long nslots, int G, int H);  // head slices per (chunk, group)
+hipError_t launch_bwd_chunks(const BwdChunkArgs& a, hipStream_t stream);
+
 // Bytes of dynamic LDS the bf16 kernels need (host-side checks).
 size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q);
 size_t chunk_state_bf16_lds_bytes(int P, int N, int block_tokens);  // block_tokens: Gs*Q when fused, else 0
