@@ -19,20 +19,19 @@
 // B, C and C B^T are loaded once, dB and dC accumulate over the slice's heads in
 // registers, and each head's X, dY, h and lam pass through LDS once. The
 // products run as 16x16x32 bf16 MFMAs with fp32 accumulation, transposed so
-// that each lane holds four consecutive output channels of one token. Wave w
-// owns the 16-token strips w and QT-1-w (QT = Q / 16 strips), which balances the
-// triangular work of the causal mask.
+// that each lane holds four consecutive output channels of one token. There is
+// one wave per 16-token strip (Q / 16 waves); wave i takes the strip's tokens as
+// queries for dC and as keys for dB, whose causal halves together cost the same
+// for every strip.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 
-constexpr int kBwdThreads = 256;
-
 template <int P, int N, int Q>
 struct BwdCfg {
-  static constexpr int QT = Q / 16;         // 16-token strips
-  static constexpr int SPW = QT / 4;        // strips per wave
+  static constexpr int QT = Q / 16;         // 16-token strips, one per wave
+  static constexpr int NW = QT, NTHR = 64 * NW;
   static constexpr int NT = N / 16, PT = P / 16;
   static constexpr int pN = lds_pitch(N), pP = lds_pitch(P), pQ = lds_pitch(Q);
   // 16-bit LDS tiles: B, C [Q][pN]; X, dY [Q][pP]; one region R that holds in
@@ -40,13 +39,14 @@ struct BwdCfg {
   static constexpr int offB = 0, offC = Q * pN, offX = 2 * Q * pN, offY = offX + Q * pP, offR = offY + Q * pP;
   static constexpr int rElems = (Q * pQ > 2 * P * pN) ? Q * pQ : 2 * P * pN;
   static constexpr int halfElems = offR + rElems;
-  // fp32 after the tiles: cs [2][Q] (two heads in flight), column partials [4][Q],
-  // row sums, b and c terms [Q] each, the state dot products [4].
-  static constexpr int floats = 2 * Q + 4 * Q + 3 * Q + 4;
+  // fp32 after the tiles: cs [2][Q] (two heads in flight), pair-sum partials
+  // [NW][Q], b and c terms [Q] each, the state dot products [NW].
+  static constexpr int floats = 2 * Q + NW * Q + 2 * Q + NW;
   static constexpr size_t lds_bytes = (size_t)halfElems * 2 + (size_t)floats * 4;
   static_assert(Q == 64 || Q == 128, "chunk of 64 or 128 tokens");
   static_assert(P % 32 == 0 && N % 32 == 0, "head and state sizes in multiples of 32");
   static_assert(halfElems % 8 == 0, "fp32 area 16-byte aligned");
+  static_assert(lds_bytes <= kMaxLdsBytes, "LDS of one workgroup");
 };
 
 // The 8 bf16 values of an operand scaled by one factor, rounded back to bf16.
@@ -57,38 +57,61 @@ __device__ __forceinline__ u32x4 scale_frag1(u32x4 v, float f) {
   return r;
 }
 
+// Sums across lanes without the LDS crossbar: over the 16 lanes of each DPP
+// row (quad swaps, then the half-row and row mirrors, which pair lanes of
+// different quads and halves), and over the four rows (gfx950 row swaps).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum_row16(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x141>(v);  // row_half_mirror
+  v += dpp_f32<0x140>(v);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float sum_rows4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Dot product of 4 fp32 values with 4 bf16 values (two words).
 __device__ __forceinline__ float dot4_bf16(f32x4 a, u32x2 b) {
   return a[0] * bf16_lo(b.x) + a[1] * bf16_hi(b.x) + a[2] * bf16_lo(b.y) + a[3] * bf16_hi(b.y);
 }
 
-// Tile staging: ROWS x COLS 16-bit values from global memory (row stride
-// `gstride` bytes; offsets past the descriptor's range read as zero) into
-// registers, then into LDS with row pitch PITCH.
-template <int ROWS, int COLS>
+// Tile staging by NTHR threads: ROWS x COLS 16-bit values from global memory
+// (row stride `gstride` bytes; offsets past the descriptor's range read as
+// zero) into registers, then into LDS with row pitch PITCH.
+template <int ROWS, int COLS, int NTHR>
 struct Stage {
-  static constexpr int kPieces = ROWS * COLS / 8 / kBwdThreads;  // 16-byte pieces per thread
-  static_assert(kPieces * 8 * kBwdThreads == ROWS * COLS, "tile of whole pieces per thread");
+  static constexpr int kTotal = ROWS * COLS / 8;                 // 16-byte pieces
+  static constexpr int kPieces = (kTotal + NTHR - 1) / NTHR;     // per thread
+  static_assert(kTotal % NTHR == 0 || kTotal < NTHR, "whole pieces per thread");
   u32x4 v[kPieces];
   __device__ __forceinline__ void load(rsrc_t r, uint32_t gstride, int tid) {
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
-      const int i = tid + k * kBwdThreads;
-      v[k] = buf_load16(r, (uint32_t)(i / (COLS / 8)) * gstride + (uint32_t)(i % (COLS / 8)) * 16);
+      const int i = tid + k * NTHR;
+      v[k] = buf_load16(r, i < kTotal ? (uint32_t)(i / (COLS / 8)) * gstride + (uint32_t)(i % (COLS / 8)) * 16
+                                      : kOffNone);
     }
   }
   template <int PITCH>
   __device__ __forceinline__ void store(uint16_t* dst, int tid) const {
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
-      const int i = tid + k * kBwdThreads;
-      *reinterpret_cast<u32x4*>(dst + (i / (COLS / 8)) * PITCH + (i % (COLS / 8)) * 8) = v[k];
+      const int i = tid + k * NTHR;
+      if (i < kTotal) *reinterpret_cast<u32x4*>(dst + (i / (COLS / 8)) * PITCH + (i % (COLS / 8)) * 8) = v[k];
     }
   }
 };
 
 template <int P, int N, int Q>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
+__global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Bm,
     const uint16_t* __restrict__ Cm, const float* __restrict__ la, const int4* __restrict__ ftable,
     const int4* __restrict__ fbtable, const float* __restrict__ fcs, const uint16_t* __restrict__ fstart,
@@ -96,7 +119,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
     long spr_r, uint16_t* __restrict__ dX, float* __restrict__ dla, void* __restrict__ dBo, void* __restrict__ dCo,
     long tokens, int H, int G, int nsl) {
   using K = BwdCfg<P, N, Q>;
-  constexpr int QT = K::QT, SPW = K::SPW, NT = K::NT, PT = K::PT;
+  constexpr int QT = K::QT, NW = K::NW, NTHR = K::NTHR, NT = K::NT, PT = K::PT;
   constexpr int pN = K::pN, pP = K::pP, pQ = K::pQ;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int sl = (int)(unit % nsl);
@@ -134,15 +157,16 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
   uint16_t* Hs = R;
   uint16_t* Ls = R + P * pN;
   float* csl = reinterpret_cast<float*>(lds + K::halfElems);  // [2][Q]
-  float* colp = csl + 2 * Q;                                  // [4][Q]
-  float* rowv = colp + 4 * Q;
-  float* bv = rowv + Q;
+  float* colp = csl + 2 * Q;                                  // [NW][Q]
+  float* bv = colp + NW * Q;
   float* cv = bv + Q;
-  float* red = cv + Q;  // [4]
+  float* red = cv + Q;  // [NW]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g4 = lane >> 4;
-  auto strip = [&](int k) { return k == 0 ? w : QT - 1 - w; };
+  // The wave's strip: tokens 16 i .. 16 i + 15 as queries (u) and as keys (s).
+  const int i = uniform(w);
+  const int u = 16 * i + c;  // the lane's token in the transposed tiles
 
   const uint32_t xstride = (uint32_t)(H * P * 2), bstride = (uint32_t)(G * N * 2);
   auto x_rsrc = [&](const uint16_t* base, int h) {
@@ -154,10 +178,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
 
   // ---- prologue: B, C, the first head's X, dY and segment sums
   {
-    Stage<Q, N> sb, sc;
+    Stage<Q, N, NTHR> sb, sc;
     sb.load(make_rsrc(Bm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride), bstride, tid);
     sc.load(make_rsrc(Cm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride), bstride, tid);
-    Stage<Q, P> sx, sy;
+    Stage<Q, P, NTHR> sx, sy;
     sx.load(x_rsrc(X, hbeg), xstride, tid);
     sy.load(x_rsrc(dY, hbeg), xstride, tid);
     if (tid < Q) csl[tid] = fcs[(slot * H + hbeg) * (long)Q + tid];
@@ -168,140 +192,132 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
   }
   __syncthreads();
 
+  // The causal tiles (query strip ti, key block tj <= ti) of the pair products
+  // are shared out evenly: waves i and QT-1-i split the QT+1 tiles of their two
+  // strips (HALF+1 and HALF). Tile t of this wave:
+  constexpr int HALF = QT / 2, TPW = HALF + 1;
+  const bool lowhalf = i < HALF;
+  auto tile_i = [&](int t) { return lowhalf ? (t <= i ? i : QT - 1 - i) : i; };
+  auto tile_j = [&](int t) { return lowhalf ? (t <= i ? t : t - i - 1) : i - HALF + 1 + t; };
+  auto tile_ok = [&](int t) { return lowhalf || t < HALF; };
+
   // C B^T of the wave's tiles, transposed (row s, column u), kept for every head.
-  f32x4 m1[SPW][QT];
+  f32x4 m1[TPW];
 #pragma unroll
-  for (int k = 0; k < SPW; ++k) {
-    const int i = strip(k);
+  for (int t = 0; t < TPW; ++t) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if (tile_ok(t)) {
+      const int ti = tile_i(t), tj = tile_j(t);
 #pragma unroll
-    for (int j = 0; j < QT; ++j) {
-      f32x4 a = {0.f, 0.f, 0.f, 0.f};
-      if (j <= i) {
-#pragma unroll
-        for (int kk = 0; kk < N / 32; ++kk)
-          a = mfma16x16x32(frag_k_cols(Bs, pN, 16 * j, 32 * kk, lane), frag_k_cols(Cs, pN, 16 * i, 32 * kk, lane), a);
-      }
-      m1[k][j] = a;
+      for (int kk = 0; kk < N / 32; ++kk)
+        a = mfma16x16x32(frag_k_cols(Bs, pN, 16 * tj, 32 * kk, lane), frag_k_cols(Cs, pN, 16 * ti, 32 * kk, lane),
+                         a);
     }
+    m1[t] = a;
   }
 
-  f32x4 dc[SPW][NT], db[SPW][NT];  // dC^T, dB^T: row n, column token
+  f32x4 dc[NT], db[NT];  // dC^T, dB^T of the strip: row n, column token
 #pragma unroll
-  for (int k = 0; k < SPW; ++k)
-#pragma unroll
-    for (int m = 0; m < NT; ++m) dc[k][m] = db[k][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < NT; ++m) dc[m] = db[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int h = hbeg; h < hend; ++h) {
     const float* cs = csl + ((h - hbeg) & 1) * Q;
     // The states of this head, staged in registers until R is free.
-    Stage<P, N> sh, sl_;
+    Stage<P, N, NTHR> sh, sl_;
     sh.load(state_rsrc(fstart, slot, h), (uint32_t)(N * 2), tid);
     sl_.load(state_rsrc(rstart, rslot, h), (uint32_t)(N * 2), tid);
     const float anext = last_chunk ? 1.f : fast_exp2(la[(long)(tok0 + len) * H + h] * kLog2e);
-
     // (R is free: the barriers that close the previous head follow its last read.)
     for (int q = lane; q < Q; q += 64) colp[w * Q + q] = 0.f;  // this wave's row only
 
-    // ---- dY X^T, the mask, W = L o dY X^T (to R) and the pair sums of d log a
-    uint32_t w1p[SPW][QT][2];  // L o C B^T, bf16 pairs, written to R after W is used
+    // ---- dY X^T, the mask, W = L o dY X^T (to R) and the pair sums of d log a:
+    // column sums (key s, queries u > s) enter colp[w][s] with plus sign, row
+    // sums (query u, keys s < u) with minus sign; only their difference is used.
+    uint32_t w1p[TPW][2];  // L o C B^T, bf16 pairs, written to R after W is used
+    {
+      float rsa = 0.f, rsb = 0.f;  // row sums of the strips i and QT-1-i
 #pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-      const int i = strip(k);
-      const int u = 16 * i + c;
-      const float csu = cs[u];
-      float rs = 0.f;
+      for (int t = 0; t < TPW; ++t) {
+        w1p[t][0] = w1p[t][1] = 0u;
+        if (!tile_ok(t)) continue;
+        const int ti = tile_i(t), tj = tile_j(t);
+        const int uu = 16 * ti + c;
+        f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < QT; ++j) {
-        w1p[k][j][0] = w1p[k][j][1] = 0u;
-        if (j <= i) {
-          f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < P / 32; ++kk)
+          m2 = mfma16x16x32(frag_k_cols(Xs, pP, 16 * tj, 32 * kk, lane), frag_k_cols(Ys, pP, 16 * ti, 32 * kk, lane),
+                            m2);
+        const float csu = cs[uu];
+        const f32x4 css = *reinterpret_cast<const f32x4*>(cs + 16 * tj + 4 * g4);
+        float w1[4], w2[4], sv[4], rs = 0.f;
 #pragma unroll
-          for (int kk = 0; kk < P / 32; ++kk)
-            m2 = mfma16x16x32(frag_k_cols(Xs, pP, 16 * j, 32 * kk, lane), frag_k_cols(Ys, pP, 16 * i, 32 * kk, lane),
-                              m2);
-          const f32x4 css = *reinterpret_cast<const f32x4*>(cs + 16 * j + 4 * g4);
-          float w1[4], w2[4], sv[4];
+        for (int r = 0; r < 4; ++r) {
+          const int s = 16 * tj + 4 * g4 + r;
+          const float l = s <= uu ? fast_exp2(csu - css[r]) : 0.f;
+          w1[r] = l * m1[t][r];
+          w2[r] = l * m2[r];
+          sv[r] = s < uu ? w1[r] * m2[r] : 0.f;
+          rs += sv[r];
+        }
+        if (ti == i) rsa += rs; else rsb += rs;
+        w1p[t][0] = pack_bf16x2(w1[0], w1[1]);
+        w1p[t][1] = pack_bf16x2(w1[2], w1[3]);
+        *reinterpret_cast<u32x2*>(R + uu * pQ + 16 * tj + 4 * g4) =
+            u32x2{pack_bf16x2(w2[0], w2[1]), pack_bf16x2(w2[2], w2[3])};
+        if (ti == tj && (ti & 1) == 0)  // above the diagonal, inside the 32-token blocks the products read
+          *reinterpret_cast<u32x2*>(R + uu * pQ + 16 * tj + 16 + 4 * g4) = u32x2{0u, 0u};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int s = 16 * j + 4 * g4 + r;
-            const float l = s <= u ? fast_exp2(csu - css[r]) : 0.f;
-            w1[r] = l * m1[k][j][r];
-            w2[r] = l * m2[r];
-            sv[r] = s < u ? w1[r] * m2[r] : 0.f;
-            rs += sv[r];
-          }
-          w1p[k][j][0] = pack_bf16x2(w1[0], w1[1]);
-          w1p[k][j][1] = pack_bf16x2(w1[2], w1[3]);
-          *reinterpret_cast<u32x2*>(R + u * pQ + 16 * j + 4 * g4) =
-              u32x2{pack_bf16x2(w2[0], w2[1]), pack_bf16x2(w2[2], w2[3])};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) sv[r] += __shfl_xor(sv[r], off);
-          }
-          if (c == 0) {
-            f32x4* cp = reinterpret_cast<f32x4*>(colp + w * Q + 16 * j + 4 * g4);
-            *cp += f32x4{sv[0], sv[1], sv[2], sv[3]};
-          }
-        } else if (j == i + 1 && (i & 1) == 0) {
-          // above the diagonal, inside the 32-token blocks the products read
-          *reinterpret_cast<u32x2*>(R + u * pQ + 16 * j + 4 * g4) = u32x2{0u, 0u};
+        for (int r = 0; r < 4; ++r) sv[r] = sum_row16(sv[r]);
+        if (c == 0) {
+          f32x4* cp = reinterpret_cast<f32x4*>(colp + w * Q + 16 * tj + 4 * g4);
+          *cp += f32x4{sv[0], sv[1], sv[2], sv[3]};
         }
       }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      if (g4 == 0) rowv[u] = rs;
-    }
-    __syncthreads();
-
-    // ---- dC^T += B^T W^T and dB^T += C^T W (W in R)
-#pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-      const int i = strip(k);
-#pragma unroll
-      for (int kk = 0; kk < QT / 2; ++kk) {
-        if (kk <= i / 2) {
-          const u32x4 bop = frag_k_cols(R, pQ, 16 * i, 32 * kk, lane);
-#pragma unroll
-          for (int m = 0; m < NT; ++m)
-            dc[k][m] = mfma16x16x32(frag_k_rows_natural(Bs, pN, 32 * kk, 16 * m, lane), bop, dc[k][m]);
-        }
-        if (kk >= i / 2) {
-          const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * i, lane);
-#pragma unroll
-          for (int m = 0; m < NT; ++m)
-            db[k][m] = mfma16x16x32(frag_k_rows_natural(Cs, pN, 32 * kk, 16 * m, lane), bop, db[k][m]);
-        }
+      rsa = sum_rows4(rsa);
+      rsb = sum_rows4(rsb);
+      if (g4 == 0) {
+        colp[w * Q + u] -= rsa;
+        if (lowhalf) colp[w * Q + 16 * (QT - 1 - i) + c] -= rsb;
       }
     }
     __syncthreads();
 
-    // ---- L o C B^T to R; dX^T = dY^T (L o C B^T)
+    // ---- dC^T += B^T W^T (keys up to the strip) and dB^T += C^T W (queries from the strip)
 #pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-      const int i = strip(k);
-      const int u = 16 * i + c;
+    for (int kk = 0; kk < QT / 2; ++kk) {
+      if (kk <= i / 2) {
+        const u32x4 bop = frag_k_cols(R, pQ, 16 * i, 32 * kk, lane);
 #pragma unroll
-      for (int j = 0; j < QT; ++j) {
-        if (j <= i || (j == i + 1 && (i & 1) == 0))
-          *reinterpret_cast<u32x2*>(R + u * pQ + 16 * j + 4 * g4) = u32x2{w1p[k][j][0], w1p[k][j][1]};
+        for (int m = 0; m < NT; ++m)
+          dc[m] = mfma16x16x32(frag_k_rows_natural(Bs, pN, 32 * kk, 16 * m, lane), bop, dc[m]);
+      }
+      if (kk >= i / 2) {
+        const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * i, lane);
+#pragma unroll
+        for (int m = 0; m < NT; ++m)
+          db[m] = mfma16x16x32(frag_k_rows_natural(Cs, pN, 32 * kk, 16 * m, lane), bop, db[m]);
       }
     }
     __syncthreads();
-    f32x4 dx[SPW][PT];
+
+    // ---- L o C B^T to R (the zero blocks above the diagonal stay); dX^T = dY^T (L o C B^T)
 #pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-      const int j = strip(k);
+    for (int t = 0; t < TPW; ++t) {
+      if (tile_ok(t))
+        *reinterpret_cast<u32x2*>(R + (16 * tile_i(t) + c) * pQ + 16 * tile_j(t) + 4 * g4) =
+            u32x2{w1p[t][0], w1p[t][1]};
+    }
+    __syncthreads();
+    f32x4 dx[PT];
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) dx[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int pt = 0; pt < PT; ++pt) dx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < QT / 2; ++kk) {
-        if (kk >= j / 2) {
-          const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * j, lane);
+    for (int kk = 0; kk < QT / 2; ++kk) {
+      if (kk >= i / 2) {
+        const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * i, lane);
 #pragma unroll
-          for (int pt = 0; pt < PT; ++pt)
-            dx[k][pt] = mfma16x16x32(frag_k_rows_natural(Ys, pP, 32 * kk, 16 * pt, lane), bop, dx[k][pt]);
-        }
+        for (int pt = 0; pt < PT; ++pt)
+          dx[pt] = mfma16x16x32(frag_k_rows_natural(Ys, pP, 32 * kk, 16 * pt, lane), bop, dx[pt]);
       }
     }
     __syncthreads();
@@ -312,19 +328,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
     {
       float d = 0.f;
 #pragma unroll
-      for (int k = 0; k < Stage<P, N>::kPieces; ++k)
+      for (int k = 0; k < Stage<P, N, NTHR>::kPieces; ++k)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           d += bf16_lo(sh.v[k][q]) * bf16_lo(sl_.v[k][q]) + bf16_hi(sh.v[k][q]) * bf16_hi(sl_.v[k][q]);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) d += __shfl_xor(d, off);
+      d = sum_rows4(sum_row16(d));
       if (lane == 0) red[w] = d;
     }
     __syncthreads();
 
     // The next head's inputs, staged in registers while this head finishes.
     const bool more = h + 1 < hend;
-    Stage<Q, P> nx, ny;
+    Stage<Q, P, NTHR> nx, ny;
     float ncs = 0.f;
     if (more) {
       nx.load(x_rsrc(X, h + 1), xstride, tid);
@@ -334,11 +349,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
 
     // ---- terms through the states
     const float cs_last = cs[Q - 1];
-    const rsrc_t rdx = x_rsrc(dX, h);
-#pragma unroll
-    for (int k = 0; k < SPW; ++k) {
-      const int i = strip(k);
-      const int u = 16 * i + c;  // the lane's token (u as a query, s as a key)
+    {
       const float fu = fast_exp2(cs[u]);
       const float es = anext * fast_exp2(cs_last - cs[u]);
       // b_u = 2^{cs_u} dY_u . (h C_u)
@@ -355,8 +366,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt)
         b += dot4_bf16(t[pt], *reinterpret_cast<const u32x2*>(Ys + u * pP + 16 * pt + 4 * g4));
-      b += __shfl_xor(b, 16);
-      b += __shfl_xor(b, 32);
+      b = sum_rows4(b);
       if (g4 == 0) bv[u] = b * fu;
       // dX_off = e_s lam B_s; c_s = x_s . dX_off
 #pragma unroll
@@ -372,10 +382,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
       for (int pt = 0; pt < PT; ++pt) {
         t[pt] *= es;
         cc += dot4_bf16(t[pt], *reinterpret_cast<const u32x2*>(Xs + u * pP + 16 * pt + 4 * g4));
-        dx[k][pt] += t[pt];
+        dx[pt] += t[pt];
       }
-      cc += __shfl_xor(cc, 16);
-      cc += __shfl_xor(cc, 32);
+      cc = sum_rows4(cc);
       if (g4 == 0) cv[u] = cc;
       // dC^T += h^T (2^cs dY)^T ; dB^T += lam^T (e X)^T
 #pragma unroll
@@ -384,14 +393,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
         const u32x4 xop = scale_frag1(frag_k_cols(Xs, pP, 16 * i, 32 * kk, lane), es);
 #pragma unroll
         for (int m = 0; m < NT; ++m) {
-          dc[k][m] = mfma16x16x32(frag_k_rows_natural(Hs, pN, 32 * kk, 16 * m, lane), yop, dc[k][m]);
-          db[k][m] = mfma16x16x32(frag_k_rows_natural(Ls, pN, 32 * kk, 16 * m, lane), xop, db[k][m]);
+          dc[m] = mfma16x16x32(frag_k_rows_natural(Hs, pN, 32 * kk, 16 * m, lane), yop, dc[m]);
+          db[m] = mfma16x16x32(frag_k_rows_natural(Ls, pN, 32 * kk, 16 * m, lane), xop, db[m]);
         }
       }
       // dX of the lane's token, four consecutive channels per P tile
+      const rsrc_t rdx = x_rsrc(dX, h);
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt)
-        buf_store8(u32x2{pack_bf16x2(dx[k][pt][0], dx[k][pt][1]), pack_bf16x2(dx[k][pt][2], dx[k][pt][3])}, rdx,
+        buf_store8(u32x2{pack_bf16x2(dx[pt][0], dx[pt][1]), pack_bf16x2(dx[pt][2], dx[pt][3])}, rdx,
                    (uint32_t)u * xstride + (uint32_t)(16 * pt + 4 * g4) * 2);
     }
     __syncthreads();
@@ -404,7 +414,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int t = lane * EPL + e;
-        v[e] = colp[t] + colp[Q + t] + colp[2 * Q + t] + colp[3 * Q + t] - rowv[t] + cv[t];
+        float col = 0.f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) col += colp[k * Q + t];
+        v[e] = col + cv[t];
         bb[e] = bv[t];
         pv[e] = sv;
         pb[e] = sb;
@@ -422,7 +435,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
       }
       const float totb = __shfl(ib, 63);
       const float ev = iv - sv, eb = ib - sb;
-      const float dspan = anext * fast_exp2(cs_last) * (red[0] + red[1] + red[2] + red[3]);
+      float dsum = 0.f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) dsum += red[k];
+      const float dspan = anext * fast_exp2(cs_last) * dsum;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int t = lane * EPL + e;
@@ -439,29 +455,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_chunk_kernel(
 
   // ---- dB, dC of the slice's heads: bf16 when one slice covers the group,
   // else fp32 partials [nsl][tokens][G][N] that a reduction sums.
+  if (nsl == 1) {
+    const rsrc_t rb = make_rsrc(reinterpret_cast<uint16_t*>(dBo) + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
+    const rsrc_t rc = make_rsrc(reinterpret_cast<uint16_t*>(dCo) + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
 #pragma unroll
-  for (int k = 0; k < SPW; ++k) {
-    const int u = 16 * strip(k) + c;
-    if (nsl == 1) {
-      const rsrc_t rb = make_rsrc(reinterpret_cast<uint16_t*>(dBo) + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
-      const rsrc_t rc = make_rsrc(reinterpret_cast<uint16_t*>(dCo) + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
+    for (int m = 0; m < NT; ++m) {
+      const uint32_t off = (uint32_t)u * bstride + (uint32_t)(16 * m + 4 * g4) * 2;
+      buf_store8(u32x2{pack_bf16x2(db[m][0], db[m][1]), pack_bf16x2(db[m][2], db[m][3])}, rb, off);
+      buf_store8(u32x2{pack_bf16x2(dc[m][0], dc[m][1]), pack_bf16x2(dc[m][2], dc[m][3])}, rc, off);
+    }
+  } else {
+    const long base = ((long)sl * tokens + tok0) * G * N + (long)g * N;
+    const uint32_t fstride = (uint32_t)(G * N * 4);
+    const rsrc_t rb = make_rsrc(reinterpret_cast<float*>(dBo) + base, (uint32_t)len * fstride);
+    const rsrc_t rc = make_rsrc(reinterpret_cast<float*>(dCo) + base, (uint32_t)len * fstride);
 #pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        const uint32_t off = (uint32_t)u * bstride + (uint32_t)(16 * m + 4 * g4) * 2;
-        buf_store8(u32x2{pack_bf16x2(db[k][m][0], db[k][m][1]), pack_bf16x2(db[k][m][2], db[k][m][3])}, rb, off);
-        buf_store8(u32x2{pack_bf16x2(dc[k][m][0], dc[k][m][1]), pack_bf16x2(dc[k][m][2], dc[k][m][3])}, rc, off);
-      }
-    } else {
-      const long base = ((long)sl * tokens + tok0) * G * N + (long)g * N;
-      const uint32_t fstride = (uint32_t)(G * N * 4);
-      const rsrc_t rb = make_rsrc(reinterpret_cast<float*>(dBo) + base, (uint32_t)len * fstride);
-      const rsrc_t rc = make_rsrc(reinterpret_cast<float*>(dCo) + base, (uint32_t)len * fstride);
-#pragma unroll
-      for (int m = 0; m < NT; ++m) {
-        const uint32_t off = (uint32_t)u * fstride + (uint32_t)(16 * m + 4 * g4) * 4;
-        buf_store16(__builtin_bit_cast(u32x4, db[k][m]), rb, off);
-        buf_store16(__builtin_bit_cast(u32x4, dc[k][m]), rc, off);
-      }
+    for (int m = 0; m < NT; ++m) {
+      const uint32_t off = (uint32_t)u * fstride + (uint32_t)(16 * m + 4 * g4) * 4;
+      buf_store16(__builtin_bit_cast(u32x4, db[m]), rb, off);
+      buf_store16(__builtin_bit_cast(u32x4, dc[m]), rc, off);
     }
   }
 }
@@ -484,7 +496,7 @@ static hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, hipStream_t stream) 
                                      (int)K::lds_bytes);
   if (e != hipSuccess) return e;
   const long grid = a.nslots * a.G * a.nsl;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), K::lds_bytes, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(K::NTHR), K::lds_bytes, stream,
                      reinterpret_cast<const uint16_t*>(a.X), reinterpret_cast<const uint16_t*>(a.dY),
                      reinterpret_cast<const uint16_t*>(a.B), reinterpret_cast<const uint16_t*>(a.C), a.la, a.ftable,
                      a.fbtable, a.fcs, reinterpret_cast<const uint16_t*>(a.fstart),
