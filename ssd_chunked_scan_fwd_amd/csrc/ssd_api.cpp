@@ -171,12 +171,13 @@ hipError_t run_forward(const Prepared& pp, const void* X, const float* log_a, co
 // workgroups, fp32 partials of dB and dC per head slice.
 struct BwdLayout {
   size_t cur, rev_dy, rev_x, dx_rev, rev_b, rev_c, bcast, part, la_rev, states_t, lam_first;
-  size_t part_b, part_c;
+  size_t part_b, part_c, cstart_f, cstart_r;
   size_t fwd_a, fwd_f, fwd_s, total;
   size_t a_bytes, f_bytes, s_bytes;
   int Tr;          // tokens per row of the padded reversed layout (packed: an upper bound)
   bool fused;      // the fused chunk kernel computes dX, d log a, dB and dC
   int nsl;         // head slices per (chunk, group) in the fused kernel
+  int gs;          // state block of the two state runs (fused path; 1 otherwise)
 };
 
 // The role-exchanged runs (dB, dC) have headdim N, dstate P and one group per head.
@@ -212,9 +213,12 @@ ssd_status make_bwd_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk,
   ssd_shape wr = w;
   wr.seqlen = (int32_t)Tr;
   ssd_layout La, Lf, Ls1{}, Ls2{};
+  // The fused path runs the state runs in state blocks and expands the block
+  // states to chunk states; the general path runs them one chunk per block.
+  const int run_gs = fused ? gs : 1;
   if ((st = check_shape(&sr, cu, chunk)) != SSD_OK) return st;
-  if ((st = make_layout(&sr, cu, chunk, 1, &La)) != SSD_OK) return st;
-  if ((st = make_layout(s, cu, chunk, 1, &Lf)) != SSD_OK) return st;
+  if ((st = make_layout(&sr, cu, chunk, run_gs, &La)) != SSD_OK) return st;
+  if ((st = make_layout(s, cu, chunk, run_gs, &Lf)) != SSD_OK) return st;
   if (!fused) {
     if ((st = make_layout(&wr, cu, chunk, default_state_block(&wr, cu, chunk), &Ls1)) != SSD_OK) return st;
     if ((st = make_layout(&w, cu, chunk, default_state_block(&w, cu, chunk), &Ls2)) != SSD_OK) return st;
@@ -226,6 +230,7 @@ ssd_status make_bwd_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk,
   if ((int64_t)tmax * H * (P > N ? P : N) > kMaxElems) return SSD_ERR_UNSUPPORTED;
   BwdLayout L{};
   L.fused = fused;
+  L.gs = run_gs;
   L.nsl = fused ? ssd::bwd_chunk_slices(Lf.nslots, (int)G, (int)H) : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
@@ -235,6 +240,10 @@ ssd_status make_bwd_layout(const ssd_shape* s, const int32_t* cu, int32_t chunk,
   L.la_rev = take(tokr * H * 4);
   L.lam_first = take(nseq * H * P * N * 4);
   if (fused) {
+    if (run_gs > 1) {
+      L.cstart_f = take((size_t)Lf.nslots * H * P * N * esz);
+      L.cstart_r = take((size_t)La.nslots * H * P * N * esz);
+    }
     if (L.nsl > 1) {
       if ((int64_t)L.nsl * tok * G * N > kMaxElems) return SSD_ERR_UNSUPPORTED;
       L.part_b = take((size_t)L.nsl * tok * G * N * 4);
@@ -423,10 +432,14 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
     // Two state runs with one chunk per state block, then one kernel for the
     // four gradients of every chunk.
     Prepared pa, pf;
-    if ((st = prepare(kAll, dY, log_a, C, B, dX, cur, chunk, 1, &sr, w + L.fwd_a, L.a_bytes, &pa)) != SSD_OK)
+    if ((st = prepare(kAll, dY, log_a, C, B, dX, cur, chunk, L.gs, &sr, w + L.fwd_a, L.a_bytes, &pa)) != SSD_OK)
       return st;
-    if ((st = prepare(kAll, X, log_a, B, C, dX, cu_seqlens, chunk, 1, s, w + L.fwd_f, L.f_bytes, &pf)) != SSD_OK)
+    if ((st = prepare(kAll, X, log_a, B, C, dX, cu_seqlens, chunk, L.gs, s, w + L.fwd_f, L.f_bytes, &pf)) != SSD_OK)
       return st;
+    // States entering every chunk: the runs' own block states when a block is
+    // one chunk, else expanded from them.
+    void* rstart = L.gs > 1 ? w + L.cstart_r : pa.ws.start_states;
+    void* fstart = L.gs > 1 ? w + L.cstart_f : pf.ws.start_states;
     hipError_t e = hipSuccess;
     if (packed) e = ssd::launch_padded_offsets(cu_seqlens, cur, S, chunk, hs);
     if (e == hipSuccess) e = ssd::launch_gather_rows(dY, rev_dy, cu_seqlens, cur, S, rows, T, Tr, H, H, P * esz, 1, hs);
@@ -441,12 +454,14 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
     }
     if (e == hipSuccess)
       e = ssd::launch_state_passing(pa.d, cur, dfinal_state, dinitial_state ? lam_first : nullptr, pa.ws, hs);
+    if (e == hipSuccess && L.gs > 1) e = ssd::launch_chunk_starts(pa.d, rev_dy, rev_c, pa.ws, rstart, hs);
     // Forward chunk start states and segment sums.
     if (e == hipSuccess) {
       const ssd::SegArgs sa = ssd::seg_args(pf.d, log_a, cu_seqlens, ssd::Mamba2Args{});
       e = ssd::launch_chunk_state(pf.d, X, B, pf.ws, hs, &sa);
     }
     if (e == hipSuccess) e = ssd::launch_state_passing(pf.d, cu_seqlens, initial_state, nullptr, pf.ws, hs);
+    if (e == hipSuccess && L.gs > 1) e = ssd::launch_chunk_starts(pf.d, X, B, pf.ws, fstart, hs);
     if (e == hipSuccess) {
       ssd::BwdChunkArgs a{};
       a.X = X;
@@ -454,13 +469,13 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
       a.B = B;
       a.C = C;
       a.la = log_a;
-      a.ftable = pf.ws.table;
-      a.fbtable = pf.ws.btable;
       a.fcs = pf.ws.cs;
-      a.fstart = pf.ws.start_states;
-      a.rstart = pa.ws.start_states;
+      a.fstart = fstart;
+      a.rstart = rstart;
       a.cu = cu_seqlens;
       a.cur = cur;
+      a.S = S;
+      a.T = T;
       a.spr = pf.d.slots_per_row;
       a.spr_r = pa.d.slots_per_row;
       a.nslots = pf.d.nslots;

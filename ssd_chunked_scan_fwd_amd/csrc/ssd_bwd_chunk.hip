@@ -25,6 +25,7 @@
 // for every strip.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_segsum.h"
 
 namespace ssd {
 
@@ -113,11 +114,10 @@ struct Stage {
 template <int P, int N, int Q>
 __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Bm,
-    const uint16_t* __restrict__ Cm, const float* __restrict__ la, const int4* __restrict__ ftable,
-    const int4* __restrict__ fbtable, const float* __restrict__ fcs, const uint16_t* __restrict__ fstart,
-    const uint16_t* __restrict__ rstart, const int32_t* __restrict__ cu, const int32_t* __restrict__ cur, long spr,
-    long spr_r, uint16_t* __restrict__ dX, float* __restrict__ dla, void* __restrict__ dBo, void* __restrict__ dCo,
-    long tokens, int H, int G, int nsl) {
+    const uint16_t* __restrict__ Cm, const float* __restrict__ la, const float* __restrict__ fcs,
+    const uint16_t* __restrict__ fstart, const uint16_t* __restrict__ rstart, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ cur, int S, int T, long spr, long spr_r, uint16_t* __restrict__ dX,
+    float* __restrict__ dla, void* __restrict__ dBo, void* __restrict__ dCo, long tokens, int H, int G, int nsl) {
   using K = BwdCfg<P, N, Q>;
   constexpr int QT = K::QT, NW = K::NW, NTHR = K::NTHR, NT = K::NT, PT = K::PT;
   constexpr int pN = K::pN, pP = K::pP, pQ = K::pQ;
@@ -126,10 +126,9 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
   const long rest = unit / nsl;
   const int g = (int)(rest % G);
   const long slot = rest / G;
-  // One chunk per state block in the forward state run: its block table is
-  // written for every slot, its chunk table only for slots that hold a chunk.
-  if (fbtable[slot].z <= 0) return;
-  const int4 rec = ftable[slot];
+  // The chunk of this slot (none for the slots between packed sequences).
+  const int4 rec = cu == nullptr ? chunk_record(nullptr, 0, (int)(slot / spr), slot % spr, T, Q, spr)
+                                 : chunk_record(cu, S, 0, slot, T, Q, spr);
   const int len = rec.z;
   if (len <= 0) return;
   const int seq = rec.x, tok0 = rec.y, jc = rec.w;
@@ -478,6 +477,135 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
   }
 }
 
+// The state entering every chunk, from the states entering the state blocks:
+// h_0 = the block's entering state and h_{j+1} = a_j h_j + S_j, where a_j is
+// chunk j's total decay and S_j = sum_t 2^{cs_last - cs_t} x_t B_t^T its state
+// term (paper card Method 5: the chunk-state and state-passing terms, here
+// taken one chunk at a time inside a block). h stays in fp32 registers; each
+// h_j is written in bf16. One workgroup per (state block, head), 4 waves, each
+// holding N/64 row tiles of h^T (row n, column p) so that a lane stores four
+// consecutive n of one p.
+template <int P, int N, int Q>
+__global__ __launch_bounds__(256, 2) void chunk_starts_kernel(const uint16_t* __restrict__ X,
+                                                             const uint16_t* __restrict__ Bm,
+                                                             const int4* __restrict__ table,
+                                                             const int4* __restrict__ btable,
+                                                             const float* __restrict__ cs,
+                                                             const uint16_t* __restrict__ bstart,
+                                                             uint16_t* __restrict__ out, int H, int G) {
+  constexpr int PT = P / 16, NTW = N / 64, pN = lds_pitch(N), pP = lds_pitch(P);
+  static_assert(N % 64 == 0 && P % 16 == 0, "state tiles over four waves");
+  const long blk = blockIdx.x / H;
+  const int h = (int)(blockIdx.x % H);
+  const int4 br = btable[blk];
+  const int nch = br.z;
+  if (nch <= 0) return;
+  const long slot0 = br.y;
+  const int g = h / (H / G);
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* Xs = lds;                                        // [Q][pP]
+  uint16_t* Bs = Xs + Q * pP;                                // [Q][pN]
+  float* wt = reinterpret_cast<float*>(Bs + Q * pN);         // [Q] weights 2^{cs_last - cs_t}
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, g4 = lane >> 4;
+  const uint32_t xstride = (uint32_t)(H * P * 2), bstride = (uint32_t)(G * N * 2);
+
+  f32x4 hs[NTW][PT];  // h^T: row n = 16 (NTW w + a) + 4 g4 + r, column p = 16 pt + c
+  {
+    const rsrc_t rs = make_rsrc(bstart + (blk * H + h) * (long)(P * N), (uint32_t)(P * N * 2));
+#pragma unroll
+    for (int a = 0; a < NTW; ++a)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        const u32x2 v = buf_load8(rs, (uint32_t)((16 * pt + c) * N + 16 * (NTW * w + a) + 4 * g4) * 2);
+        hs[a][pt] = f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+      }
+  }
+  for (int j = 0; j < nch; ++j) {
+    const long slot = slot0 + j;
+    {
+      const rsrc_t ro = make_rsrc(out + (slot * H + h) * (long)(P * N), (uint32_t)(P * N * 2));
+#pragma unroll
+      for (int a = 0; a < NTW; ++a)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+          buf_store8(u32x2{pack_bf16x2(hs[a][pt][0], hs[a][pt][1]), pack_bf16x2(hs[a][pt][2], hs[a][pt][3])}, ro,
+                     (uint32_t)((16 * pt + c) * N + 16 * (NTW * w + a) + 4 * g4) * 2);
+    }
+    if (j == nch - 1) break;
+    const int4 rec = table[slot];
+    const int tok0 = rec.y, len = rec.z;
+    const rsrc_t rx = make_rsrc(X + ((long)tok0 * H + h) * P, (uint32_t)len * xstride);
+    const rsrc_t rb = make_rsrc(Bm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
+    for (int i = tid; i < Q * P / 8; i += 256)
+      *reinterpret_cast<u32x4*>(Xs + (i / (P / 8)) * pP + (i % (P / 8)) * 8) =
+          buf_load16(rx, (uint32_t)(i / (P / 8)) * xstride + (uint32_t)(i % (P / 8)) * 16);
+    for (int i = tid; i < Q * N / 8; i += 256)
+      *reinterpret_cast<u32x4*>(Bs + (i / (N / 8)) * pN + (i % (N / 8)) * 8) =
+          buf_load16(rb, (uint32_t)(i / (N / 8)) * bstride + (uint32_t)(i % (N / 8)) * 16);
+    const float* csj = cs + (slot * H + h) * (long)Q;
+    const float cs_last = csj[Q - 1];  // positions past the chunk's end repeat its total
+    for (int i = tid; i < Q; i += 256) wt[i] = fast_exp2(cs_last - csj[i]);
+    __syncthreads();
+    const float aj = fast_exp2(cs_last);
+#pragma unroll
+    for (int a = 0; a < NTW; ++a)
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) hs[a][pt] *= aj;
+#pragma unroll
+    for (int kk = 0; kk < Q / 32; ++kk) {
+      float wk[8];
+      *reinterpret_cast<f32x4*>(wk) = *reinterpret_cast<const f32x4*>(wt + 32 * kk + 8 * g4);
+      *reinterpret_cast<f32x4*>(wk + 4) = *reinterpret_cast<const f32x4*>(wt + 32 * kk + 8 * g4 + 4);
+      u32x4 bo[PT];
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) bo[pt] = frag_k_rows_natural(Xs, pP, 32 * kk, 16 * pt, lane);
+#pragma unroll
+      for (int a = 0; a < NTW; ++a) {
+        const u32x4 ao = scale_frag(frag_k_rows_natural(Bs, pN, 32 * kk, 16 * (NTW * w + a), lane), wk);
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) hs[a][pt] = mfma16x16x32(ao, bo[pt], hs[a][pt]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int P, int N, int Q>
+static hipError_t launch_chunk_starts_t(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
+                                        void* out, hipStream_t stream) {
+  constexpr size_t lds = (size_t)Q * (lds_pitch(P) + lds_pitch(N)) * 2 + (size_t)Q * 4;
+  auto kern = chunk_starts_kernel<P, N, Q>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * d.H)), dim3(256), lds, stream,
+                     reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B), ws.table, ws.btable,
+                     ws.cs, reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(out), d.H,
+                     d.G);
+  return hipGetLastError();
+}
+
+template <int P, int N>
+static hipError_t launch_chunk_starts_q(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
+                                        void* out, hipStream_t stream) {
+  switch (d.Q) {
+    case 64: return launch_chunk_starts_t<P, N, 64>(d, X, B, ws, out, stream);
+    case 128: return launch_chunk_starts_t<P, N, 128>(d, X, B, ws, out, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_chunk_starts(const FwdDims& d, const void* X, const void* B, const Workspace& ws, void* out,
+                               hipStream_t stream) {
+  if (!d.bf16 || !bwd_chunk_supported(d.P, d.N, d.Q, true)) return hipErrorInvalidValue;
+  if (d.P == 32) return d.N == 64 ? launch_chunk_starts_q<32, 64>(d, X, B, ws, out, stream)
+                                  : launch_chunk_starts_q<32, 128>(d, X, B, ws, out, stream);
+  if (d.P == 64) return d.N == 64 ? launch_chunk_starts_q<64, 64>(d, X, B, ws, out, stream)
+                                  : launch_chunk_starts_q<64, 128>(d, X, B, ws, out, stream);
+  return launch_chunk_starts_q<128, 64>(d, X, B, ws, out, stream);
+}
+
 // out[t][g][n] = sum over slices of part[sl][t][g][n], rounded to bf16 (four per thread).
 __global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
                                                         long n4, int nsl) {
@@ -498,9 +626,9 @@ static hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, hipStream_t stream) 
   const long grid = a.nslots * a.G * a.nsl;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(K::NTHR), K::lds_bytes, stream,
                      reinterpret_cast<const uint16_t*>(a.X), reinterpret_cast<const uint16_t*>(a.dY),
-                     reinterpret_cast<const uint16_t*>(a.B), reinterpret_cast<const uint16_t*>(a.C), a.la, a.ftable,
-                     a.fbtable, a.fcs, reinterpret_cast<const uint16_t*>(a.fstart),
-                     reinterpret_cast<const uint16_t*>(a.rstart), a.cu, a.cur, a.spr, a.spr_r,
+                     reinterpret_cast<const uint16_t*>(a.B), reinterpret_cast<const uint16_t*>(a.C), a.la, a.fcs,
+                     reinterpret_cast<const uint16_t*>(a.fstart), reinterpret_cast<const uint16_t*>(a.rstart), a.cu,
+                     a.cur, a.S, a.T, a.spr, a.spr_r,
                      reinterpret_cast<uint16_t*>(a.dX), a.dla, a.nsl == 1 ? a.dB : a.part_b,
                      a.nsl == 1 ? a.dC : a.part_c, a.tokens, a.H, a.G, a.nsl);
   e = hipGetLastError();

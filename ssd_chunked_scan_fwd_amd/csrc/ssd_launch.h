@@ -113,12 +113,11 @@ size_t dlog_chunk_lds_bytes(int P, int N, int Q, int esz);
 struct BwdChunkArgs {
   const void *X, *dY, *B, *C;   // forward layout, bf16
   const float* la;
-  const int4* ftable;           // forward run: chunk records,
-  const int4* fbtable;          //   block records (written for every slot),
-  const float* fcs;             //   segment sums,
+  const float* fcs;             // forward run: segment sums,
   const void* fstart;           //   chunk start states (bf16)
   const void* rstart;           // reversed run: chunk start states (bf16, padded reversed slots)
   const int32_t *cu, *cur;
+  int S, T;                     // packed sequences, tokens per row
   long spr, spr_r, nslots, tokens;
   void* dX;
   float* dla;
@@ -129,6 +128,10 @@ struct BwdChunkArgs {
 bool bwd_chunk_supported(int P, int N, int Q, bool bf16);
 int bwd_chunk_slices(long nslots, int G, int H);  // head slices per (chunk, group)
 hipError_t launch_bwd_chunks(const BwdChunkArgs& a, hipStream_t stream);
+// The bf16 state entering every chunk slot ([nslots][H][P][N]) from a run's
+// block-entering states (start_states), for the shapes of the fused kernel.
+hipError_t launch_chunk_starts(const FwdDims& d, const void* X, const void* B, const Workspace& ws, void* out,
+                               hipStream_t stream);
 
 // Bytes of dynamic LDS the bf16 kernels need (host-side checks).
 size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q);
