@@ -88,7 +88,7 @@ __device__ __forceinline__ float dot4_bf16(f32x4 a, u32x2 b) {
 // (row stride `gstride` bytes; offsets past the descriptor's range read as
 // zero) into registers, then into LDS with row pitch PITCH.
 template <int ROWS, int COLS, int NTHR>
-struct Stage {
+struct StageT {
   static constexpr int kTotal = ROWS * COLS / 8;                 // 16-byte pieces
   static constexpr int kPieces = (kTotal + NTHR - 1) / NTHR;     // per thread
   static_assert(kTotal % NTHR == 0 || kTotal < NTHR, "whole pieces per thread");
@@ -177,10 +177,10 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
 
   // ---- prologue: B, C, the first head's X, dY and segment sums
   {
-    Stage<Q, N, NTHR> sb, sc;
+    StageT<Q, N, NTHR> sb, sc;
     sb.load(make_rsrc(Bm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride), bstride, tid);
     sc.load(make_rsrc(Cm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride), bstride, tid);
-    Stage<Q, P, NTHR> sx, sy;
+    StageT<Q, P, NTHR> sx, sy;
     sx.load(x_rsrc(X, hbeg), xstride, tid);
     sy.load(x_rsrc(dY, hbeg), xstride, tid);
     if (tid < Q) csl[tid] = fcs[(slot * H + hbeg) * (long)Q + tid];
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
   for (int h = hbeg; h < hend; ++h) {
     const float* cs = csl + ((h - hbeg) & 1) * Q;
     // The states of this head, staged in registers until R is free.
-    Stage<P, N, NTHR> sh, sl_;
+    StageT<P, N, NTHR> sh, sl_;
     sh.load(state_rsrc(fstart, slot, h), (uint32_t)(N * 2), tid);
     sl_.load(state_rsrc(rstart, rslot, h), (uint32_t)(N * 2), tid);
     const float anext = last_chunk ? 1.f : fast_exp2(la[(long)(tok0 + len) * H + h] * kLog2e);
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     {
       float d = 0.f;
 #pragma unroll
-      for (int k = 0; k < Stage<P, N, NTHR>::kPieces; ++k)
+      for (int k = 0; k < StageT<P, N, NTHR>::kPieces; ++k)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           d += bf16_lo(sh.v[k][q]) * bf16_lo(sl_.v[k][q]) + bf16_hi(sh.v[k][q]) * bf16_hi(sl_.v[k][q]);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
 
     // The next head's inputs, staged in registers while this head finishes.
     const bool more = h + 1 < hend;
-    Stage<Q, P, NTHR> nx, ny;
+    StageT<Q, P, NTHR> nx, ny;
     float ncs = 0.f;
     if (more) {
       nx.load(x_rsrc(X, h + 1), xstride, tid);
@@ -521,6 +521,15 @@ __global__ __launch_bounds__(256, 2) void chunk_starts_kernel(const uint16_t* __
         hs[a][pt] = f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
       }
   }
+  // Chunk j + 1's X and B are fetched into registers while chunk j is multiplied.
+  StageT<Q, P, 256> sx;
+  StageT<Q, N, 256> sb;
+  auto fetch = [&](long slot) {
+    const int4 rec = table[slot];
+    sx.load(make_rsrc(X + ((long)rec.y * H + h) * P, (uint32_t)rec.z * xstride), xstride, tid);
+    sb.load(make_rsrc(Bm + ((long)rec.y * G + g) * N, (uint32_t)rec.z * bstride), bstride, tid);
+  };
+  if (nch > 1) fetch(slot0);
   for (int j = 0; j < nch; ++j) {
     const long slot = slot0 + j;
     {
@@ -533,20 +542,13 @@ __global__ __launch_bounds__(256, 2) void chunk_starts_kernel(const uint16_t* __
                      (uint32_t)((16 * pt + c) * N + 16 * (NTW * w + a) + 4 * g4) * 2);
     }
     if (j == nch - 1) break;
-    const int4 rec = table[slot];
-    const int tok0 = rec.y, len = rec.z;
-    const rsrc_t rx = make_rsrc(X + ((long)tok0 * H + h) * P, (uint32_t)len * xstride);
-    const rsrc_t rb = make_rsrc(Bm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride);
-    for (int i = tid; i < Q * P / 8; i += 256)
-      *reinterpret_cast<u32x4*>(Xs + (i / (P / 8)) * pP + (i % (P / 8)) * 8) =
-          buf_load16(rx, (uint32_t)(i / (P / 8)) * xstride + (uint32_t)(i % (P / 8)) * 16);
-    for (int i = tid; i < Q * N / 8; i += 256)
-      *reinterpret_cast<u32x4*>(Bs + (i / (N / 8)) * pN + (i % (N / 8)) * 8) =
-          buf_load16(rb, (uint32_t)(i / (N / 8)) * bstride + (uint32_t)(i % (N / 8)) * 16);
+    sx.template store<pP>(Xs, tid);
+    sb.template store<pN>(Bs, tid);
     const float* csj = cs + (slot * H + h) * (long)Q;
     const float cs_last = csj[Q - 1];  // positions past the chunk's end repeat its total
     for (int i = tid; i < Q; i += 256) wt[i] = fast_exp2(cs_last - csj[i]);
     __syncthreads();
+    if (j + 2 < nch) fetch(slot + 1);
     const float aj = fast_exp2(cs_last);
 #pragma unroll
     for (int a = 0; a < NTW; ++a)
