@@ -39,8 +39,12 @@ template <int P, int N>
 struct StateCfg {
   static constexpr int BP = lds_pitch(N), XP = lds_pitch(P);
   static constexpr int TP = P / 16, TN = N / 16;
-  static constexpr int WN = TN < 4 ? TN : 4;
-  static constexpr int WP = (8 / WN) < TP ? (8 / WN) : TP;
+  // MFMA waves: with large states, four waves of 2 x 4 tiles read fewer
+  // fragments from LDS per product than eight waves of 2 x 2 (the pass loop is
+  // bound by LDS reads); all eight waves stage the rows.
+  static constexpr int MW = (P * N == 8192) ? 4 : 8;
+  static constexpr int WN = TN < 4 ? TN : (MW == 4 ? 2 : 4);
+  static constexpr int WP = (MW / WN) < TP ? (MW / WN) : TP;
   static constexpr int TPW = TP / WP, TNW = TN / WN;
   static constexpr int CBN = N / 8, CBP = P / 8;
   static constexpr int RB = (kPassRows * CBN + kStateThreads - 1) / kStateThreads;
