@@ -79,6 +79,19 @@ __device__ __forceinline__ float sum_rows4(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// MFMA operand with k along the columns of a row-major LDS tile, in the slot
+// order of frag_k_rows_accpair: lane (r = l % 16, g = l / 16) reads
+// W[row0 + r][col0 + 4g .. 4g + 3] and W[row0 + r][col0 + 16 + 4g .. 16 + 4g + 3].
+// Paired with a pair-order transposed read of the other operand (whose reads
+// are free of bank conflicts at the lds_pitch pitches), the contraction runs
+// over the same 32 k in a permuted order.
+__device__ __forceinline__ u32x4 frag_k_cols_pair(const uint16_t* W, int pitch, int row0, int col0, int lane) {
+  const uint16_t* p = W + (row0 + (lane & 15)) * pitch + col0 + 4 * (lane >> 4);
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
 // Dot product of 4 fp32 values with 4 bf16 values (two words).
 __device__ __forceinline__ float dot4_bf16(f32x4 a, u32x2 b) {
   return a[0] * bf16_lo(b.x) + a[1] * bf16_hi(b.x) + a[2] * bf16_lo(b.y) + a[3] * bf16_hi(b.y);
@@ -285,16 +298,16 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
 #pragma unroll
     for (int kk = 0; kk < QT / 2; ++kk) {
       if (kk <= i / 2) {
-        const u32x4 bop = frag_k_cols(R, pQ, 16 * i, 32 * kk, lane);
+        const u32x4 bop = frag_k_cols_pair(R, pQ, 16 * i, 32 * kk, lane);
 #pragma unroll
         for (int m = 0; m < NT; ++m)
-          dc[m] = mfma16x16x32(frag_k_rows_natural(Bs, pN, 32 * kk, 16 * m, lane), bop, dc[m]);
+          dc[m] = mfma16x16x32(frag_k_rows_accpair(Bs, pN, 32 * kk, 16 * m, lane), bop, dc[m]);
       }
       if (kk >= i / 2) {
-        const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * i, lane);
+        const u32x4 bop = frag_k_rows_accpair(R, pQ, 32 * kk, 16 * i, lane);
 #pragma unroll
         for (int m = 0; m < NT; ++m)
-          db[m] = mfma16x16x32(frag_k_rows_natural(Cs, pN, 32 * kk, 16 * m, lane), bop, db[m]);
+          db[m] = mfma16x16x32(frag_k_rows_accpair(Cs, pN, 32 * kk, 16 * m, lane), bop, db[m]);
       }
     }
     __syncthreads();
@@ -313,10 +326,10 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
 #pragma unroll
     for (int kk = 0; kk < QT / 2; ++kk) {
       if (kk >= i / 2) {
-        const u32x4 bop = frag_k_rows_natural(R, pQ, 32 * kk, 16 * i, lane);
+        const u32x4 bop = frag_k_rows_accpair(R, pQ, 32 * kk, 16 * i, lane);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt)
-          dx[pt] = mfma16x16x32(frag_k_rows_natural(Ys, pP, 32 * kk, 16 * pt, lane), bop, dx[pt]);
+          dx[pt] = mfma16x16x32(frag_k_rows_accpair(Ys, pP, 32 * kk, 16 * pt, lane), bop, dx[pt]);
       }
     }
     __syncthreads();
@@ -388,12 +401,12 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
       // dC^T += h^T (2^cs dY)^T ; dB^T += lam^T (e X)^T
 #pragma unroll
       for (int kk = 0; kk < P / 32; ++kk) {
-        const u32x4 yop = scale_frag1(frag_k_cols(Ys, pP, 16 * i, 32 * kk, lane), fu);
-        const u32x4 xop = scale_frag1(frag_k_cols(Xs, pP, 16 * i, 32 * kk, lane), es);
+        const u32x4 yop = scale_frag1(frag_k_cols_pair(Ys, pP, 16 * i, 32 * kk, lane), fu);
+        const u32x4 xop = scale_frag1(frag_k_cols_pair(Xs, pP, 16 * i, 32 * kk, lane), es);
 #pragma unroll
         for (int m = 0; m < NT; ++m) {
-          dc[m] = mfma16x16x32(frag_k_rows_natural(Hs, pN, 32 * kk, 16 * m, lane), yop, dc[m]);
-          db[m] = mfma16x16x32(frag_k_rows_natural(Ls, pN, 32 * kk, 16 * m, lane), xop, db[m]);
+          dc[m] = mfma16x16x32(frag_k_rows_accpair(Hs, pN, 32 * kk, 16 * m, lane), yop, dc[m]);
+          db[m] = mfma16x16x32(frag_k_rows_accpair(Ls, pN, 32 * kk, 16 * m, lane), xop, db[m]);
         }
       }
       // dX of the lane's token, four consecutive channels per P tile
@@ -556,15 +569,16 @@ __global__ __launch_bounds__(256, 2) void chunk_starts_kernel(const uint16_t* __
       for (int pt = 0; pt < PT; ++pt) hs[a][pt] *= aj;
 #pragma unroll
     for (int kk = 0; kk < Q / 32; ++kk) {
+      // token order of the pair-order reads: 4 g4 + (0..3), then 16 + 4 g4 + (0..3)
       float wk[8];
-      *reinterpret_cast<f32x4*>(wk) = *reinterpret_cast<const f32x4*>(wt + 32 * kk + 8 * g4);
-      *reinterpret_cast<f32x4*>(wk + 4) = *reinterpret_cast<const f32x4*>(wt + 32 * kk + 8 * g4 + 4);
+      *reinterpret_cast<f32x4*>(wk) = *reinterpret_cast<const f32x4*>(wt + 32 * kk + 4 * g4);
+      *reinterpret_cast<f32x4*>(wk + 4) = *reinterpret_cast<const f32x4*>(wt + 32 * kk + 16 + 4 * g4);
       u32x4 bo[PT];
 #pragma unroll
-      for (int pt = 0; pt < PT; ++pt) bo[pt] = frag_k_rows_natural(Xs, pP, 32 * kk, 16 * pt, lane);
+      for (int pt = 0; pt < PT; ++pt) bo[pt] = frag_k_rows_accpair(Xs, pP, 32 * kk, 16 * pt, lane);
 #pragma unroll
       for (int a = 0; a < NTW; ++a) {
-        const u32x4 ao = scale_frag(frag_k_rows_natural(Bs, pN, 32 * kk, 16 * (NTW * w + a), lane), wk);
+        const u32x4 ao = scale_frag(frag_k_rows_accpair(Bs, pN, 32 * kk, 16 * (NTW * w + a), lane), wk);
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) hs[a][pt] = mfma16x16x32(ao, bo[pt], hs[a][pt]);
       }
