@@ -126,3 +126,37 @@ def test_bwd_state_block_invariance():
     g8 = check_bwd(d, 128, "gs 8", gs=8, seed=11)
     for k in ("dX", "dB", "dC", "dlog_a"):
         assert_close(to_f64(g8[k]), to_f64(g1[k]), "bf16", f"gs 8 vs gs 1 {k}")
+
+
+def test_bwd_headline_sampled_heads():
+    """The headline workload at full size (T = 16384, H = 32, P = 64, N = 128, Q = 128, default state
+    block, as bench.py times it). dX and d log a of two sampled heads depend on those heads alone, so
+    the oracle runs on them only; dB and dC sum over heads, so a second GPU call with dY and the
+    final-state gradient zero outside the sampled heads gives their share, which the oracle's dB
+    and dC on the two heads must match."""
+    w = synth.WORKLOADS[synth.HEADLINE]
+    d = synth.workload_inputs(w)
+    X, la, B, C = (d[k] for k in ("X", "log_a", "B", "C"))
+    b, T, H, P = X.shape
+    N = B.shape[-1]
+    heads = [0, 17]
+    ct = synth.make_cotangents(b, T, H, P, N, b, dtype=X.dtype, seed=12)
+    dfin = _dfinal_states(b, H, P, N, seed=13)
+    say(f"[bwd] headline sampled heads {heads}: X{tuple(X.shape)} Q={w.Q}")
+    dev = lambda t: t.cuda()
+    Xg, lag, Bg, Cg = dev(X), dev(la), dev(B), dev(C)
+    g = ssd.bwd(Xg, lag, Bg, Cg, dev(ct["dY"]), chunk=w.Q, dfinal_state=dev(dfin))
+    mask = torch.zeros(H, dtype=torch.bool)
+    mask[heads] = True
+    dY_s = ct["dY"].clone()
+    dY_s[:, :, ~mask] = 0
+    dfin_s = dfin.clone()
+    dfin_s[:, ~mask] = 0
+    g_s = ssd.bwd(Xg, lag, Bg, Cg, dev(dY_s), chunk=w.Q, dfinal_state=dev(dfin_s))
+    torch.cuda.synchronize()
+    r = oracle.backward(to_f64(X[:, :, heads]), to_f64(la[:, :, heads]), to_f64(B), to_f64(C),
+                        to_f64(ct["dY"][:, :, heads]), dfinal=to_f64(dfin[:, heads]))
+    assert_close(to_f64(g["dX"][:, :, heads]), r["dX"], "bf16", "headline dX")
+    assert_close(to_f64(g["dlog_a"][:, :, heads]), r["dlog_a"], "bf16", "headline dlog_a")
+    assert_close(to_f64(g_s["dB"]), r["dB"], "bf16", "headline dB (sampled heads)")
+    assert_close(to_f64(g_s["dC"]), r["dC"], "bf16", "headline dC (sampled heads)")
