@@ -128,6 +128,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba-2 block-call timing")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-chain", action="store_true", help="skip the cooperative state-chain timing")
     ap.add_argument("--bwd-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=4096)
@@ -289,6 +290,23 @@ def main() -> int:
                          "ms_per_step": round(m_ms, 5), "event_ms_per_step": round(a.elapsed_time(b) / args.steps, 5),
                          "tokens_per_s": round(tokens / (m_ms * 1e-3), 1)}
         del mX, mdt, mbias, mAl, mD, mz, mB, mC
+
+    if not args.no_chain:
+        # The state chain as one cooperative launch (ssd_set_state_chain(1)),
+        # against the default two launches: the same step, timed the same way.
+        prev = ssd.set_state_chain(1)
+        for _ in range(min(args.warmup, 50)):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        c_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        ssd.set_state_chain(prev)
+        out["state_chain_cooperative"] = {"ms_per_step": round(c_ms, 5),
+                                          "note": "chunk_state and state_passing as one cooperative launch; "
+                                                  "not the default (slower on this stack)"}
 
     if not args.no_bwd:
         # The backward pass (ssd_bwd) on the same shape: dX, d log a, dB, dC

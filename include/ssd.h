@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum {
   SSD_OK = 0,
@@ -150,9 +150,26 @@ ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_
                                    size_t* bytes);
 
 /*
+ * How the forward and backward calls run the state chain (the right factors
+ * and the centre-factor recurrence over state blocks; paper card Method 5,
+ * "Right Factors" and "Centre Factors"):
+ *   mode 0 (the default): two launches, chunk_state then state_passing;
+ *   mode 1: one cooperative launch, with a grid-wide barrier between the right
+ *          factors and the recurrence, when the whole grid can be resident on
+ *          the device and `stream` is not being captured into a graph (bf16,
+ *          headdim * dstate in {4096, 8192, 16384}, headdim >= 32,
+ *          dstate >= 64); otherwise two launches. The cooperative launch
+ *          itself costs more than the launch it saves on ROCm 7 (about
+ *          74 us per call at T = 16384, H = 32), hence not the default.
+ * Both give bit-identical results. Process-wide; returns the previous mode.
+ */
+int32_t ssd_set_state_chain(int32_t mode);
+
+/*
  * Forward pass: Y and final states from zero initial states, with the default
- * state block. Computes what the four stages below compute, in three launches
- * on `stream`: the chunk-state launch also writes the records and segment sums
+ * state block. Computes what the four stages below compute, in two or three
+ * launches on `stream` (the state chain, see ssd_set_state_chain, then the
+ * chunk scan): the chunk-state work also writes the records and segment sums
  * that ssd_chunk_cumsum writes, for every slot that holds a chunk (table rows
  * of slots that hold no chunk are left as they were). final_state may be NULL.
  * The workspace must hold ssd_fwd_workspace_bytes(shape, chunk, 0).

@@ -26,7 +26,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "ssd_fwd_layout",
            "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
            "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2",
-           "ssd_bwd_workspace_bytes", "ssd_bwd")
+           "ssd_bwd_workspace_bytes", "ssd_bwd", "ssd_set_state_chain")
 
 
 class SSDError(RuntimeError):
@@ -94,6 +94,8 @@ def lib():
         L.ssd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, shp, vp, sz, vp]
         L.ssd_step_mamba2.restype = ctypes.c_int
         L.ssd_step_mamba2.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, shp, vp]
+        L.ssd_set_state_chain.restype = i32
+        L.ssd_set_state_chain.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -352,6 +354,12 @@ def step_mamba2(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: t
     _call("ssd_step_mamba2", _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(D), _ptr(z),
           _ptr(B), _ptr(C), _ptr(y), ctypes.byref(shape), _stream(x.device))
     return y
+
+
+def set_state_chain(mode: int) -> int:
+    """ssd_set_state_chain: 1 runs the state chain as one cooperative launch when
+    it fits (the default), 0 always as two launches. Returns the previous mode."""
+    return int(lib().ssd_set_state_chain(int(mode)))
 
 
 def bwd_workspace_bytes(shape: Shape, chunk: int, state_block: int = 0) -> int:

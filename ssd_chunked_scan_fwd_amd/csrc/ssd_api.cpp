@@ -9,6 +9,8 @@
 #include <climits>
 #include <cstdint>
 
+#include <atomic>
+
 #include "ssd.h"
 #include "ssd_launch.h"
 
@@ -150,12 +152,29 @@ ssd_status prepare(int stages, const void* X, const float* log_a, const void* B,
 
 ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
 
-// One forward pass (three launches) on prepared dimensions and workspace.
+// Whether the state chain may run as one cooperative launch (ssd_set_state_chain; off by
+// default: on ROCm 7 the cooperative launch costs more than the launch it saves).
+std::atomic<int> g_state_chain{0};
+
+// The state chain: chunk_state (with the segment sums) and state_passing, as
+// one cooperative launch when allowed and the grid fits, else two launches.
+hipError_t run_state_chain(const Prepared& pp, const void* X, const void* B, const ssd::SegArgs& sa,
+                           const int32_t* cu, const float* init, float* final_state, hipStream_t s) {
+  bool launched = false;
+  hipError_t e = hipSuccess;
+  if (g_state_chain.load(std::memory_order_relaxed))
+    e = ssd::launch_chunk_state_chain(pp.d, X, B, pp.ws, s, sa, init, final_state, &launched);
+  if (e != hipSuccess || launched) return e;
+  e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s, &sa);
+  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu, init, final_state, pp.ws, s);
+  return e;
+}
+
+// One forward pass (the state chain, then chunk_scan) on prepared dimensions and workspace.
 hipError_t run_forward(const Prepared& pp, const void* X, const float* log_a, const void* B, const void* C,
                        const int32_t* cu, const float* init, void* Y, float* final_state, hipStream_t s) {
   const ssd::SegArgs sa = ssd::seg_args(pp.d, log_a, cu, ssd::Mamba2Args{});
-  hipError_t e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s, &sa);
-  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu, init, final_state, pp.ws, s);
+  hipError_t e = run_state_chain(pp, X, B, sa, cu, init, final_state, s);
   if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s);
   return e;
 }
@@ -373,13 +392,9 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
   ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, state_block, shape, workspace,
                           workspace_bytes, &pp, false, initial_state, final_state);
   if (st != SSD_OK) return st;
-  // Three launches: chunk_state computes the records and segment sums itself.
-  hipStream_t s = (hipStream_t)stream;
-  const ssd::SegArgs sa = ssd::seg_args(pp.d, log_a, cu_seqlens, ssd::Mamba2Args{});
-  hipError_t e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s, &sa);
-  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, s);
-  if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s);
-  return hip_status(e);
+  // chunk_state computes the records and segment sums itself.
+  return hip_status(run_forward(pp, X, log_a, B, C, cu_seqlens, initial_state, Y, final_state,
+                                (hipStream_t)stream));
 }
 
 ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
@@ -450,17 +465,14 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
     // forward chunk ends.
     if (e == hipSuccess) {
       const ssd::SegArgs sa = ssd::seg_args(pa.d, la_rev, cur, ssd::Mamba2Args{});
-      e = ssd::launch_chunk_state(pa.d, rev_dy, rev_c, pa.ws, hs, &sa);
+      e = run_state_chain(pa, rev_dy, rev_c, sa, cur, dfinal_state, dinitial_state ? lam_first : nullptr, hs);
     }
-    if (e == hipSuccess)
-      e = ssd::launch_state_passing(pa.d, cur, dfinal_state, dinitial_state ? lam_first : nullptr, pa.ws, hs);
     if (e == hipSuccess && L.gs > 1) e = ssd::launch_chunk_starts(pa.d, rev_dy, rev_c, pa.ws, rstart, hs);
     // Forward chunk start states and segment sums.
     if (e == hipSuccess) {
       const ssd::SegArgs sa = ssd::seg_args(pf.d, log_a, cu_seqlens, ssd::Mamba2Args{});
-      e = ssd::launch_chunk_state(pf.d, X, B, pf.ws, hs, &sa);
+      e = run_state_chain(pf, X, B, sa, cu_seqlens, initial_state, nullptr, hs);
     }
-    if (e == hipSuccess) e = ssd::launch_state_passing(pf.d, cu_seqlens, initial_state, nullptr, pf.ws, hs);
     if (e == hipSuccess && L.gs > 1) e = ssd::launch_chunk_starts(pf.d, X, B, pf.ws, fstart, hs);
     if (e == hipSuccess) {
       ssd::BwdChunkArgs a{};
@@ -581,8 +593,7 @@ ssd_status ssd_fwd_mamba2(const void* X, const float* dt, const float* dt_bias, 
   m2.z = z;
   hipStream_t s = (hipStream_t)stream;
   const ssd::SegArgs sa = ssd::seg_args(pp.d, nullptr, cu_seqlens, m2);
-  hipError_t e = ssd::launch_chunk_state(pp.d, X, B, pp.ws, s, &sa);
-  if (e == hipSuccess) e = ssd::launch_state_passing(pp.d, cu_seqlens, initial_state, final_state, pp.ws, s);
+  hipError_t e = run_state_chain(pp, X, B, sa, cu_seqlens, initial_state, final_state, s);
   if (e == hipSuccess) e = ssd::launch_chunk_scan(pp.d, X, B, C, Y, pp.ws, s, m2);
   return hip_status(e);
 }
@@ -604,6 +615,8 @@ ssd_status ssd_step_mamba2(float* state, const void* x, const float* dt, const f
                                          s->dtype == SSD_DTYPE_BF16 ? 1 : 0, state, x, nullptr, B, C, y,
                                          (hipStream_t)stream, m2));
 }
+
+int32_t ssd_set_state_chain(int32_t mode) { return g_state_chain.exchange(mode ? 1 : 0); }
 
 ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C, void* y,
                     const ssd_shape* shape, void* stream) {

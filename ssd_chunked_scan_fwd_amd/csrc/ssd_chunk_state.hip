@@ -24,8 +24,11 @@
 // LDS transpose read.
 // Products run on 16x16x32 bf16 MFMA with fp32 accumulation; the block state
 // is written in fp32 together with the block's total log2 decay.
+#include <hip/hip_cooperative_groups.h>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_passing.h"
 #include "ssd_segsum.h"
 #include "ssd_stage.h"
 
@@ -64,12 +67,12 @@ size_t chunk_state_bf16_lds_bytes(int P, int N, int block_tokens) {
 // its head (the work of chunk_cumsum, for the slots its block covers): head 0
 // writes the records, and wave w takes chunks w, w + 8, ... of the block.
 template <int P, int N, bool FUSED>
-__global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk_state_bf16_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, int4* __restrict__ ctable,
-    int4* __restrict__ btable, float* __restrict__ cs, float* __restrict__ ck,
-    float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q, int Gs, SegArgs sa) {
+__device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X, const uint16_t* __restrict__ B,
+                                                  int4* __restrict__ ctable, int4* __restrict__ btable,
+                                                  float* __restrict__ cs, float* __restrict__ ck,
+                                                  float* __restrict__ bstates, float* __restrict__ bdecay, int H,
+                                                  int G, int Q, int Gs, const SegArgs& sa, long unit) {
   using K = StateCfg<P, N>;
-  const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int h = (int)(unit % H);
   const long m = unit / H;
   BlockRec blk;
@@ -259,6 +262,39 @@ __global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk
       }
 }
 
+template <int P, int N, bool FUSED>
+__global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk_state_bf16_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, int4* __restrict__ ctable,
+    int4* __restrict__ btable, float* __restrict__ cs, float* __restrict__ ck,
+    float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q, int Gs, SegArgs sa) {
+  chunk_state_block<P, N, FUSED>(X, B, ctable, btable, cs, ck, bstates, bdecay, H, G, Q, Gs, sa,
+                                 xcd_unit(blockIdx.x, gridDim.x));
+}
+
+// The state chain in one launch: every workgroup computes its block's right
+// factor as above, a grid-wide barrier (cooperative launch: all workgroups are
+// resident) makes them visible, and the same grid then runs the centre-factor
+// recurrence of every (sequence, head) and 4 state elements (pass_states),
+// writing the block-entering states and the final states.
+template <int P, int N>
+__global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk_state_chain_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, int4* __restrict__ ctable,
+    int4* __restrict__ btable, float* __restrict__ cs, float* __restrict__ ck,
+    float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q, int Gs, SegArgs sa,
+    void* __restrict__ start, float* __restrict__ final_state, const float* __restrict__ init, int nseq) {
+  chunk_state_block<P, N, true>(X, B, ctable, btable, cs, ck, bstates, bdecay, H, G, Q, Gs, sa,
+                                xcd_unit(blockIdx.x, gridDim.x));
+  cooperative_groups::this_grid().sync();
+  constexpr int PN = P * N, E4 = PN / kPassElems;
+  const long total = (long)nseq * H * E4;
+  const long stride = (long)gridDim.x * blockDim.x;
+  for (long i = (long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const long r = i / E4;
+    pass_states<true>(bstates, bdecay, start, final_state, init, sa.cu, sa.blocks_per_row, H, PN, Gs * Q,
+                      (int)(r / H), (int)(r % H), (int)(i % E4) * kPassElems);
+  }
+}
+
 // ----------------------------------------------------------------------------
 // fp32 path (plain FMA, fp32 accumulation; one chunk per state block): tokens
 // staged 32 at a time in LDS.
@@ -394,6 +430,82 @@ static hipError_t dispatch_state_n(const FwdDims& d, const void* X, const void* 
     case 128: return launch_state_fuse<P, 128>(d, X, B, ws, stream, seg);
     case 256: return launch_state_fuse<P, 256>(d, X, B, ws, stream, seg);
     default: return hipErrorInvalidValue;
+  }
+}
+
+template <int P, int N>
+static hipError_t launch_chain_t(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
+                                 hipStream_t stream, const SegArgs& sa, const float* init, float* final_state,
+                                 bool* launched) {
+  const size_t lds = chunk_state_bf16_lds_bytes(P, N, d.state_block * d.Q);
+  auto kern = chunk_state_chain_kernel<P, N>;
+  // Resident workgroups per CU for this kernel and LDS size (asked once).
+  static int per_cu = -1;
+  static size_t per_cu_lds = 0;
+  if (per_cu < 0 || per_cu_lds != lds) {
+    if (lds > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kStateThreads, lds);
+    if (e != hipSuccess) return e;
+    per_cu = n;
+    per_cu_lds = lds;
+  }
+  static int ncu = 0;
+  if (ncu == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+  }
+  const long grid = d.nblocks * d.H;
+  if (grid > (long)per_cu * ncu) return hipSuccess;  // not all resident: the caller runs two launches
+  const uint16_t* Xp = reinterpret_cast<const uint16_t*>(X);
+  const uint16_t* Bp = reinterpret_cast<const uint16_t*>(B);
+  int4* table = ws.table;
+  int4* btable = ws.btable;
+  float* cs = ws.cs;
+  float* ck = ws.ck;
+  float* bstates = ws.bstates;
+  float* bdecay = ws.bdecay;
+  int H = d.H, G = d.G, Q = d.Q, Gs = d.state_block;
+  SegArgs sac = sa;
+  void* start = ws.start_states;
+  float* fin = final_state;
+  const float* ini = init;
+  int nseq = sa.cu ? d.num_seqs : d.batch;
+  void* args[] = {&Xp, &Bp, &table, &btable, &cs, &ck, &bstates, &bdecay, &H, &G, &Q, &Gs, &sac, &start, &fin, &ini,
+                  &nseq};
+  hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)grid),
+                                            dim3(kStateThreads), args, (unsigned)lds, stream);
+  if (e == hipSuccess) *launched = true;
+  return e;
+}
+
+bool chunk_state_chain_fits(const FwdDims& d) {
+  return d.bf16 && (d.P * d.N == 8192 || d.P * d.N == 4096 || d.P * d.N == 16384) && d.P >= 32 && d.N >= 64;
+}
+
+hipError_t launch_chunk_state_chain(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
+                                    hipStream_t stream, const SegArgs& sa, const float* init, float* final_state,
+                                    bool* launched) {
+  *launched = false;
+  if (!chunk_state_chain_fits(d)) return hipSuccess;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return e;
+  if (cap != hipStreamCaptureStatusNone) return hipSuccess;  // graphs take the two-launch form
+  switch (d.P * 1000 + d.N) {
+    case 32064: return launch_chain_t<32, 64>(d, X, B, ws, stream, sa, init, final_state, launched);
+    case 32128: return launch_chain_t<32, 128>(d, X, B, ws, stream, sa, init, final_state, launched);
+    case 64064: return launch_chain_t<64, 64>(d, X, B, ws, stream, sa, init, final_state, launched);
+    case 64128: return launch_chain_t<64, 128>(d, X, B, ws, stream, sa, init, final_state, launched);
+    case 128064: return launch_chain_t<128, 64>(d, X, B, ws, stream, sa, init, final_state, launched);
+    case 128128: return launch_chain_t<128, 128>(d, X, B, ws, stream, sa, init, final_state, launched);
+    default: return hipSuccess;
   }
 }
 

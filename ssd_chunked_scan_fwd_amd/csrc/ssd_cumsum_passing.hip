@@ -8,6 +8,7 @@
 // "Center Factors" step carries states across chunks with a scalar recurrence.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+#include "ssd_passing.h"
 #include "ssd_segsum.h"
 
 namespace ssd {
@@ -73,15 +74,11 @@ hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32
 }
 
 // ----------------------------------------------------------------------------
-// state_passing: h = h0 (the sequence's initial state, or 0); for each state
-// block m of a sequence: start_m = h; h = exp2(total_m) h + s_m. One thread owns
-// 4 consecutive (p, n) elements of one (sequence, head) and moves them with
-// 16-byte loads; the block loop is unrolled so that the loads of sixteen blocks
-// are in flight together. Sequence s: packed rows own block slots
-// floor(cu[s]/(Gs*Q)) + s ..; unpacked row s owns s*blocks_per_row ...
+// state_passing: the centre-factor recurrence over each sequence's state blocks
+// (pass_states). One thread owns 4 consecutive (p, n) elements of one
+// (sequence, head) and moves them with 16-byte loads; the block loop is
+// unrolled so that the loads of sixteen blocks are in flight together.
 // ----------------------------------------------------------------------------
-constexpr int kPassElems = 4;   // (p, n) elements per thread
-
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ states,
                                                             const float* __restrict__ bdecay,
@@ -95,55 +92,8 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
   const int e = (int)(unit % eblocks) * (256 * kPassElems) + threadIdx.x * kPassElems;
   const int h = (int)((unit / eblocks) % H);
   const int s = (int)(unit / ((long)eblocks * H));
-  long base;
-  int nblk;
-  if (cu) {
-    const int b = cu[s], en = cu[s + 1];
-    base = b / span + s;
-    nblk = (en - b + span - 1) / span;
-  } else {
-    base = (long)s * blocks_per_row;
-    nblk = (int)blocks_per_row;
-  }
   if (e >= PN) return;
-
-  f32x4 hc = {0.f, 0.f, 0.f, 0.f};
-  if (init) hc = *reinterpret_cast<const f32x4*>(init + ((long)s * H + h) * PN + e);
-  auto put = [&](long blk, f32x4 v) {
-    const long off = (blk * H + h) * (long)PN + e;
-    if (OUT_BF16) {
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(start) + off) =
-          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-    } else {
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(start) + off) = v;
-    }
-  };
-  constexpr int U = 16;  // blocks whose loads are in flight together
-  int k = 0;
-  for (; k + U <= nblk; k += U) {
-    f32x4 sv[U];
-    float dv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const long blk = base + k + u;
-      sv[u] = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
-      dv[u] = bdecay[blk * H + h];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      put(base + k + u, hc);
-      const float a = fast_exp2(dv[u]);
-      hc = a * hc + sv[u];
-    }
-  }
-  for (; k < nblk; ++k) {
-    const long blk = base + k;
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(states + (blk * H + h) * (long)PN + e);
-    const float a = fast_exp2(bdecay[blk * H + h]);
-    put(blk, hc);
-    hc = a * hc + sv;
-  }
-  if (final_state) *reinterpret_cast<f32x4*>(final_state + ((long)s * H + h) * PN + e) = hc;
+  pass_states<OUT_BF16>(states, bdecay, start, final_state, init, cu, blocks_per_row, H, PN, span, s, h, e);
 }
 
 hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float* init, float* final_state,

@@ -69,6 +69,13 @@ hipError_t launch_chunk_state(const FwdDims& d, const void* X, const void* B, co
                               hipStream_t stream, const SegArgs* seg = nullptr);
 hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float* init, float* final_state,
                                 const Workspace& ws, hipStream_t stream);
+// chunk_state (fused with the segment sums) and state_passing in one
+// cooperative launch, when every workgroup of the grid can be resident and the
+// stream is not being captured; *launched says whether it ran (else the caller
+// runs the two launches).
+hipError_t launch_chunk_state_chain(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
+                                    hipStream_t stream, const SegArgs& sa, const float* init, float* final_state,
+                                    bool* launched);
 hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                              const Workspace& ws, hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});
 hipError_t launch_ssd_step(int batch, int H, int G, int P, int N, int bf16, float* state,

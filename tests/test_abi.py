@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = ssd.lib()
-    assert L.ssd_abi_version() == 3
+    assert L.ssd_abi_version() == 4
     for code, name in binding.STATUS.items():
         assert L.ssd_status_string(code).decode() == name
 
@@ -272,3 +272,11 @@ def test_bwd_validates():
     # dstate 256 has no exchanged-role run (headdim 256), and bf16 headdim 16 none either (dstate 16)
     for bad in (shape(seqlen=512, nheads=8, dstate=256), shape(seqlen=512, nheads=8, headdim=16)):
         assert L.ssd_bwd_workspace_bytes(ctypes.byref(bad), 128, 0, ctypes.byref(n)) == UNSUPPORTED
+
+
+def test_state_chain_mode_switch():
+    # process-wide switch; nothing is launched
+    prev = ssd.set_state_chain(0)
+    assert prev in (0, 1)
+    assert ssd.set_state_chain(1) == 0
+    assert ssd.set_state_chain(prev) == 1
