@@ -15,14 +15,19 @@
 // (through lam) or both outside. The last form is a_t <lam_t, h_{t-1}> written
 // out: every token pair whose decay product contains a_t contributes once.
 //
-// One workgroup (4 waves) takes one chunk, one group and a slice of its heads:
-// B, C and C B^T are loaded once, dB and dC accumulate over the slice's heads in
-// registers, and each head's X, dY, h and lam pass through LDS once. The
+// One workgroup (Q/16 waves) takes one chunk, one group and a slice of its
+// heads: B, C and C B^T are loaded once, dB and dC accumulate over the slice's
+// heads in registers, and each head's X, dY, h and lam pass through LDS once
+// (the next head's are fetched while the current one's state terms are
+// computed). The
 // products run as 16x16x32 bf16 MFMAs with fp32 accumulation, transposed so
-// that each lane holds four consecutive output channels of one token. There is
-// one wave per 16-token strip (Q / 16 waves); wave i takes the strip's tokens as
-// queries for dC and as keys for dB, whose causal halves together cost the same
-// for every strip.
+// that each lane holds four consecutive output channels of one token. Wave w
+// owns one 16-token strip, as keys (dX, dB: queries from the strip on) and as
+// queries (dC: keys up to the strip); the pair tiles of both roles are computed
+// by the owner in the orientation whose accumulator layout is directly the
+// B operand of the next product, so L o C B^T and L o dY X^T never go through
+// LDS. Waves w and w + Q/32 share a SIMD and own strips w and Q/16 - 1 - w,
+// which evens out the causal work.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 #include "ssd_segsum.h"
@@ -34,15 +39,13 @@ struct BwdCfg {
   static constexpr int QT = Q / 16;         // 16-token strips, one per wave
   static constexpr int NW = QT, NTHR = 64 * NW;
   static constexpr int NT = N / 16, PT = P / 16;
-  static constexpr int pN = lds_pitch(N), pP = lds_pitch(P), pQ = lds_pitch(Q);
-  // 16-bit LDS tiles: B, C [Q][pN]; X, dY [Q][pP]; one region R that holds in
-  // turn W (bf16, [Q][pQ], row u, column s) and the states h, lam ([P][pN] each).
-  static constexpr int offB = 0, offC = Q * pN, offX = 2 * Q * pN, offY = offX + Q * pP, offR = offY + Q * pP;
-  static constexpr int rElems = (Q * pQ > 2 * P * pN) ? Q * pQ : 2 * P * pN;
-  static constexpr int halfElems = offR + rElems;
-  // fp32 after the tiles: cs [2][Q] (two heads in flight), pair-sum partials
-  // [NW][Q], b and c terms [Q] each, the state dot products [NW].
-  static constexpr int floats = 2 * Q + NW * Q + 2 * Q + NW;
+  static constexpr int pN = lds_pitch(N), pP = lds_pitch(P);
+  // 16-bit LDS tiles: B, C [Q][pN]; X, dY [Q][pP]; the states h, lam [P][pN].
+  static constexpr int offB = 0, offC = Q * pN, offX = 2 * Q * pN, offY = offX + Q * pP, offH = offY + Q * pP,
+                       offL = offH + P * pN, halfElems = offL + P * pN;
+  // fp32 after the tiles, two heads in flight: cs [2][Q], the per-token pair
+  // terms v and b [2][Q] each, the state dot products [2][NW].
+  static constexpr int floats = 6 * Q + 2 * NW;
   static constexpr size_t lds_bytes = (size_t)halfElems * 2 + (size_t)floats * 4;
   static_assert(Q == 64 || Q == 128, "chunk of 64 or 128 tokens");
   static_assert(P % 32 == 0 && N % 32 == 0, "head and state sizes in multiples of 32");
@@ -132,8 +135,8 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     const int32_t* __restrict__ cur, int S, int T, long spr, long spr_r, uint16_t* __restrict__ dX,
     float* __restrict__ dla, void* __restrict__ dBo, void* __restrict__ dCo, long tokens, int H, int G, int nsl) {
   using K = BwdCfg<P, N, Q>;
-  constexpr int QT = K::QT, NW = K::NW, NTHR = K::NTHR, NT = K::NT, PT = K::PT;
-  constexpr int pN = K::pN, pP = K::pP, pQ = K::pQ;
+  constexpr int QT = K::QT, NW = K::NW, NTHR = K::NTHR, NT = K::NT, PT = K::PT, HALF = QT / 2;
+  constexpr int pN = K::pN, pP = K::pP;
   const long unit = xcd_unit(blockIdx.x, gridDim.x);
   const int sl = (int)(unit % nsl);
   const long rest = unit / nsl;
@@ -165,20 +168,17 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
   uint16_t* Cs = lds + K::offC;
   uint16_t* Xs = lds + K::offX;
   uint16_t* Ys = lds + K::offY;
-  uint16_t* R = lds + K::offR;
-  uint16_t* Hs = R;
-  uint16_t* Ls = R + P * pN;
+  uint16_t* Hs = lds + K::offH;
+  uint16_t* Ls = lds + K::offL;
   float* csl = reinterpret_cast<float*>(lds + K::halfElems);  // [2][Q]
-  float* colp = csl + 2 * Q;                                  // [NW][Q]
-  float* bv = colp + NW * Q;
-  float* cv = bv + Q;
-  float* red = cv + Q;  // [NW]
+  float* vb = csl + 2 * Q;                                    // [2][Q] col_k - row_k + c_k
+  float* bb = vb + 2 * Q;                                     // [2][Q] b_u
+  float* red = bb + 2 * Q;                                    // [2][NW]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g4 = lane >> 4;
-  // The wave's strip: tokens 16 i .. 16 i + 15 as queries (u) and as keys (s).
-  const int i = uniform(w);
-  const int u = 16 * i + c;  // the lane's token in the transposed tiles
+  const int i = uniform(w < HALF ? w : QT - 1 - (w - HALF));  // the wave's strip
+  const int u = 16 * i + c;  // the lane's token (a query in the query tiles, a key in the key tiles)
 
   const uint32_t xstride = (uint32_t)(H * P * 2), bstride = (uint32_t)(G * N * 2);
   auto x_rsrc = [&](const uint16_t* base, int h) {
@@ -187,8 +187,19 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
   auto state_rsrc = [&](const uint16_t* base, long s, int h) {
     return make_rsrc(base + (s * H + h) * (long)(P * N), (uint32_t)(P * N * 2));
   };
+  // <lam, h> of a head from its staged states: this wave's part to red.
+  auto state_dot = [&](const StageT<P, N, NTHR>& sh, const StageT<P, N, NTHR>& sl2, float* dst) {
+    float d = 0.f;
+#pragma unroll
+    for (int k = 0; k < StageT<P, N, NTHR>::kPieces; ++k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        d += bf16_lo(sh.v[k][q]) * bf16_lo(sl2.v[k][q]) + bf16_hi(sh.v[k][q]) * bf16_hi(sl2.v[k][q]);
+    d = sum_rows4(sum_row16(d));
+    if (lane == 0) dst[w] = d;
+  };
 
-  // ---- prologue: B, C, the first head's X, dY and segment sums
+  // ---- prologue: B, C and the first head's X, dY, states and segment sums
   {
     StageT<Q, N, NTHR> sb, sc;
     sb.load(make_rsrc(Bm + ((long)tok0 * G + g) * N, (uint32_t)len * bstride), bstride, tid);
@@ -196,174 +207,151 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     StageT<Q, P, NTHR> sx, sy;
     sx.load(x_rsrc(X, hbeg), xstride, tid);
     sy.load(x_rsrc(dY, hbeg), xstride, tid);
+    StageT<P, N, NTHR> sh, sl2;
+    sh.load(state_rsrc(fstart, slot, hbeg), (uint32_t)(N * 2), tid);
+    sl2.load(state_rsrc(rstart, rslot, hbeg), (uint32_t)(N * 2), tid);
     if (tid < Q) csl[tid] = fcs[(slot * H + hbeg) * (long)Q + tid];
     sb.template store<pN>(Bs, tid);
     sc.template store<pN>(Cs, tid);
     sx.template store<pP>(Xs, tid);
     sy.template store<pP>(Ys, tid);
+    sh.template store<pN>(Hs, tid);
+    sl2.template store<pN>(Ls, tid);
+    state_dot(sh, sl2, red);
   }
   __syncthreads();
 
-  // The causal tiles (query strip ti, key block tj <= ti) of the pair products
-  // are shared out evenly: waves i and QT-1-i split the QT+1 tiles of their two
-  // strips (HALF+1 and HALF). Tile t of this wave:
-  constexpr int HALF = QT / 2, TPW = HALF + 1;
-  const bool lowhalf = i < HALF;
-  auto tile_i = [&](int t) { return lowhalf ? (t <= i ? i : QT - 1 - i) : i; };
-  auto tile_j = [&](int t) { return lowhalf ? (t <= i ? t : t - i - 1) : i - HALF + 1 + t; };
-  auto tile_ok = [&](int t) { return lowhalf || t < HALF; };
-
-  // C B^T of the wave's tiles, transposed (row s, column u), kept for every head.
-  f32x4 m1[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
+  // C B^T of one tile, recomputed for every head (registers are the limit):
+  // key orientation (query tile t as rows u, the strip as column s) or query
+  // orientation (key tile t as rows s, the strip as column u).
+  auto cbt = [&](int t, bool key) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
-    if (tile_ok(t)) {
-      const int ti = tile_i(t), tj = tile_j(t);
 #pragma unroll
-      for (int kk = 0; kk < N / 32; ++kk)
-        a = mfma16x16x32(frag_k_cols(Bs, pN, 16 * tj, 32 * kk, lane), frag_k_cols(Cs, pN, 16 * ti, 32 * kk, lane),
-                         a);
-    }
-    m1[t] = a;
-  }
+    for (int kk = 0; kk < N / 32; ++kk)
+      a = key ? mfma16x16x32(frag_k_cols(Cs, pN, 16 * t, 32 * kk, lane), frag_k_cols(Bs, pN, 16 * i, 32 * kk, lane), a)
+              : mfma16x16x32(frag_k_cols(Bs, pN, 16 * t, 32 * kk, lane), frag_k_cols(Cs, pN, 16 * i, 32 * kk, lane), a);
+    return a;
+  };
 
   f32x4 dc[NT], db[NT];  // dC^T, dB^T of the strip: row n, column token
 #pragma unroll
   for (int m = 0; m < NT; ++m) dc[m] = db[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int h = hbeg; h < hend; ++h) {
-    const float* cs = csl + ((h - hbeg) & 1) * Q;
-    // The states of this head, staged in registers until R is free.
-    StageT<P, N, NTHR> sh, sl_;
-    sh.load(state_rsrc(fstart, slot, h), (uint32_t)(N * 2), tid);
-    sl_.load(state_rsrc(rstart, rslot, h), (uint32_t)(N * 2), tid);
+    const int hb = (h - hbeg) & 1;
+    const float* cs = csl + hb * Q;
     const float anext = last_chunk ? 1.f : fast_exp2(la[(long)(tok0 + len) * H + h] * kLog2e);
-    // (R is free: the barriers that close the previous head follow its last read.)
-    for (int q = lane; q < Q; q += 64) colp[w * Q + q] = 0.f;  // this wave's row only
+    const float csu = cs[u];
 
-    // ---- dY X^T, the mask, W = L o dY X^T (to R) and the pair sums of d log a:
-    // column sums (key s, queries u > s) enter colp[w][s] with plus sign, row
-    // sums (query u, keys s < u) with minus sign; only their difference is used.
-    uint32_t w1p[TPW][2];  // L o C B^T, bf16 pairs, written to R after W is used
-    {
-      float rsa = 0.f, rsb = 0.f;  // row sums of the strips i and QT-1-i
-#pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        w1p[t][0] = w1p[t][1] = 0u;
-        if (!tile_ok(t)) continue;
-        const int ti = tile_i(t), tj = tile_j(t);
-        const int uu = 16 * ti + c;
-        f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < P / 32; ++kk)
-          m2 = mfma16x16x32(frag_k_cols(Xs, pP, 16 * tj, 32 * kk, lane), frag_k_cols(Ys, pP, 16 * ti, 32 * kk, lane),
-                            m2);
-        const float csu = cs[uu];
-        const f32x4 css = *reinterpret_cast<const f32x4*>(cs + 16 * tj + 4 * g4);
-        float w1[4], w2[4], sv[4], rs = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int s = 16 * tj + 4 * g4 + r;
-          const float l = s <= uu ? fast_exp2(csu - css[r]) : 0.f;
-          w1[r] = l * m1[t][r];
-          w2[r] = l * m2[r];
-          sv[r] = s < uu ? w1[r] * m2[r] : 0.f;
-          rs += sv[r];
-        }
-        if (ti == i) rsa += rs; else rsb += rs;
-        w1p[t][0] = pack_bf16x2(w1[0], w1[1]);
-        w1p[t][1] = pack_bf16x2(w1[2], w1[3]);
-        *reinterpret_cast<u32x2*>(R + uu * pQ + 16 * tj + 4 * g4) =
-            u32x2{pack_bf16x2(w2[0], w2[1]), pack_bf16x2(w2[2], w2[3])};
-        if (ti == tj && (ti & 1) == 0)  // above the diagonal, inside the 32-token blocks the products read
-          *reinterpret_cast<u32x2*>(R + uu * pQ + 16 * tj + 16 + 4 * g4) = u32x2{0u, 0u};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sv[r] = sum_row16(sv[r]);
-        if (c == 0) {
-          f32x4* cp = reinterpret_cast<f32x4*>(colp + w * Q + 16 * tj + 4 * g4);
-          *cp += f32x4{sv[0], sv[1], sv[2], sv[3]};
-        }
-      }
-      rsa = sum_rows4(rsa);
-      rsb = sum_rows4(rsb);
-      if (g4 == 0) {
-        colp[w * Q + u] -= rsa;
-        if (lowhalf) colp[w * Q + 16 * (QT - 1 - i) + c] -= rsb;
-      }
-    }
-    __syncthreads();
-
-    // ---- dC^T += B^T W^T (keys up to the strip) and dB^T += C^T W (queries from the strip)
-#pragma unroll
-    for (int kk = 0; kk < QT / 2; ++kk) {
-      if (kk <= i / 2) {
-        const u32x4 bop = frag_k_cols_pair(R, pQ, 16 * i, 32 * kk, lane);
-#pragma unroll
-        for (int m = 0; m < NT; ++m)
-          dc[m] = mfma16x16x32(frag_k_rows_accpair(Bs, pN, 32 * kk, 16 * m, lane), bop, dc[m]);
-      }
-      if (kk >= i / 2) {
-        const u32x4 bop = frag_k_rows_accpair(R, pQ, 32 * kk, 16 * i, lane);
-#pragma unroll
-        for (int m = 0; m < NT; ++m)
-          db[m] = mfma16x16x32(frag_k_rows_accpair(Cs, pN, 32 * kk, 16 * m, lane), bop, db[m]);
-      }
-    }
-    __syncthreads();
-
-    // ---- L o C B^T to R (the zero blocks above the diagonal stay); dX^T = dY^T (L o C B^T)
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      if (tile_ok(t))
-        *reinterpret_cast<u32x2*>(R + (16 * tile_i(t) + c) * pQ + 16 * tile_j(t) + 4 * g4) =
-            u32x2{w1p[t][0], w1p[t][1]};
-    }
-    __syncthreads();
+    // ---- the strip as keys: query tiles ut >= i in pairs (one 32-token k block
+    // of the pair-order operands). W1 = L o C B^T (bf16 hi and lo parts) and
+    // W2 = L o dY X^T feed dX^T += dY^T W1 and dB^T += C^T W2; the column
+    // sums of S = W1 o dY X^T (queries u > s) feed d log a.
     f32x4 dx[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) dx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float colsum = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < QT / 2; ++kk) {
-      if (kk >= i / 2) {
-        const u32x4 bop = frag_k_rows_accpair(R, pQ, 32 * kk, 16 * i, lane);
+    for (int kk = 0; kk < HALF; ++kk) {
+      if (2 * kk + 1 < i) continue;
+      uint32_t w1h[4], w1l[4], w2[4];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt)
-          dx[pt] = mfma16x16x32(frag_k_rows_accpair(Ys, pP, 32 * kk, 16 * pt, lane), bop, dx[pt]);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int ut = 2 * kk + hf;
+        w1h[2 * hf] = w1h[2 * hf + 1] = w1l[2 * hf] = w1l[2 * hf + 1] = w2[2 * hf] = w2[2 * hf + 1] = 0u;
+        if (ut < i) continue;  // queries before the strip: zero
+        f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < P / 32; ++kp)
+          m2 = mfma16x16x32(frag_k_cols(Ys, pP, 16 * ut, 32 * kp, lane), frag_k_cols(Xs, pP, 16 * i, 32 * kp, lane),
+                            m2);
+        const f32x4 csq = *reinterpret_cast<const f32x4*>(cs + 16 * ut + 4 * g4);
+        const f32x4 mk = cbt(ut, true);
+        float a1[4], a2[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int uq = 16 * ut + 4 * g4 + r;  // query row; the key is the lane's token
+          const float l = uq >= u ? fast_exp2(csq[r] - csu) : 0.f;
+          a1[r] = l * mk[r];
+          a2[r] = l * m2[r];
+          colsum += uq > u ? a1[r] * m2[r] : 0.f;
+        }
+        w1h[2 * hf] = pack_bf16x2(a1[0], a1[1]);
+        w1h[2 * hf + 1] = pack_bf16x2(a1[2], a1[3]);
+        w1l[2 * hf] = pack_bf16x2(a1[0] - bf16_lo(w1h[2 * hf]), a1[1] - bf16_hi(w1h[2 * hf]));
+        w1l[2 * hf + 1] = pack_bf16x2(a1[2] - bf16_lo(w1h[2 * hf + 1]), a1[3] - bf16_hi(w1h[2 * hf + 1]));
+        w2[2 * hf] = pack_bf16x2(a2[0], a2[1]);
+        w2[2 * hf + 1] = pack_bf16x2(a2[2], a2[3]);
       }
-    }
-    __syncthreads();
-
-    // ---- the states to R, and <lam, h> for the pairs that span the chunk
-    sh.template store<pN>(Hs, tid);
-    sl_.template store<pN>(Ls, tid);
-    {
-      float d = 0.f;
+      const u32x4 bh = {w1h[0], w1h[1], w1h[2], w1h[3]}, bl = {w1l[0], w1l[1], w1l[2], w1l[3]};
+      const u32x4 b2 = {w2[0], w2[1], w2[2], w2[3]};
 #pragma unroll
-      for (int k = 0; k < StageT<P, N, NTHR>::kPieces; ++k)
+      for (int pt = 0; pt < PT; ++pt) {
+        const u32x4 ya = frag_k_rows_accpair(Ys, pP, 32 * kk, 16 * pt, lane);
+        dx[pt] = mfma16x16x32(ya, bh, dx[pt]);
+        dx[pt] = mfma16x16x32(ya, bl, dx[pt]);
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          d += bf16_lo(sh.v[k][q]) * bf16_lo(sl_.v[k][q]) + bf16_hi(sh.v[k][q]) * bf16_hi(sl_.v[k][q]);
-      d = sum_rows4(sum_row16(d));
-      if (lane == 0) red[w] = d;
+      for (int m = 0; m < NT; ++m) db[m] = mfma16x16x32(frag_k_rows_accpair(Cs, pN, 32 * kk, 16 * m, lane), b2, db[m]);
     }
-    __syncthreads();
 
-    // The next head's inputs, staged in registers while this head finishes.
+    // ---- the strip as queries: key tiles st <= i in pairs. W2 = L o dY X^T in
+    // this orientation feeds dC^T += B^T W2^T; the row sums of S (keys s < u)
+    // feed d log a.
+    float rowsum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < HALF; ++kk) {
+      if (2 * kk > i) continue;
+      uint32_t w2q[4];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int st = 2 * kk + hf;
+        w2q[2 * hf] = w2q[2 * hf + 1] = 0u;
+        if (st > i) continue;  // keys after the strip: zero
+        f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kp = 0; kp < P / 32; ++kp)
+          m2 = mfma16x16x32(frag_k_cols(Xs, pP, 16 * st, 32 * kp, lane), frag_k_cols(Ys, pP, 16 * i, 32 * kp, lane),
+                            m2);
+        const f32x4 csk = *reinterpret_cast<const f32x4*>(cs + 16 * st + 4 * g4);
+        const f32x4 mq = cbt(st, false);
+        float a2[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sk = 16 * st + 4 * g4 + r;  // key row; the query is the lane's token
+          const float l = sk <= u ? fast_exp2(csu - csk[r]) : 0.f;
+          a2[r] = l * m2[r];
+          rowsum += sk < u ? l * mq[r] * m2[r] : 0.f;
+        }
+        w2q[2 * hf] = pack_bf16x2(a2[0], a2[1]);
+        w2q[2 * hf + 1] = pack_bf16x2(a2[2], a2[3]);
+      }
+      const u32x4 bq = {w2q[0], w2q[1], w2q[2], w2q[3]};
+#pragma unroll
+      for (int m = 0; m < NT; ++m) dc[m] = mfma16x16x32(frag_k_rows_accpair(Bs, pN, 32 * kk, 16 * m, lane), bq, dc[m]);
+    }
+    colsum = sum_rows4(colsum);
+    rowsum = sum_rows4(rowsum);
+
+    // The next head's inputs, fetched into registers while this head's state
+    // terms are computed.
     const bool more = h + 1 < hend;
     StageT<Q, P, NTHR> nx, ny;
+    StageT<P, N, NTHR> nh, nl;
     float ncs = 0.f;
     if (more) {
       nx.load(x_rsrc(X, h + 1), xstride, tid);
       ny.load(x_rsrc(dY, h + 1), xstride, tid);
+      nh.load(state_rsrc(fstart, slot, h + 1), (uint32_t)(N * 2), tid);
+      nl.load(state_rsrc(rstart, rslot, h + 1), (uint32_t)(N * 2), tid);
       if (tid < Q) ncs = fcs[(slot * H + h + 1) * (long)Q + tid];
     }
 
     // ---- terms through the states
     const float cs_last = cs[Q - 1];
     {
-      const float fu = fast_exp2(cs[u]);
-      const float es = anext * fast_exp2(cs_last - cs[u]);
+      const float fu = fast_exp2(csu);
+      const float es = anext * fast_exp2(cs_last - csu);
       // b_u = 2^{cs_u} dY_u . (h C_u)
       f32x4 t[PT];
 #pragma unroll
@@ -379,7 +367,6 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
       for (int pt = 0; pt < PT; ++pt)
         b += dot4_bf16(t[pt], *reinterpret_cast<const u32x2*>(Ys + u * pP + 16 * pt + 4 * g4));
       b = sum_rows4(b);
-      if (g4 == 0) bv[u] = b * fu;
       // dX_off = e_s lam B_s; c_s = x_s . dX_off
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) t[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -397,7 +384,10 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
         dx[pt] += t[pt];
       }
       cc = sum_rows4(cc);
-      if (g4 == 0) cv[u] = cc;
+      if (g4 == 0) {
+        vb[hb * Q + u] = colsum - rowsum + cc;
+        bb[hb * Q + u] = b * fu;
+      }
       // dC^T += h^T (2^cs dY)^T ; dB^T += lam^T (e X)^T
 #pragma unroll
       for (int kk = 0; kk < P / 32; ++kk) {
@@ -416,25 +406,24 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
         buf_store8(u32x2{pack_bf16x2(dx[pt][0], dx[pt][1]), pack_bf16x2(dx[pt][2], dx[pt][3])}, rdx,
                    (uint32_t)u * xstride + (uint32_t)(16 * pt + 4 * g4) * 2);
     }
-    __syncthreads();
+    __syncthreads();  // this head's tiles are no longer read; its pair terms are complete
 
     // ---- d log a of the chunk's tokens: sum_{k<t} (col_k - row_k + c_k) + sum_{u>=t} b_u + D
     if (w == 0) {
       constexpr int EPL = Q / 64;
-      float v[EPL], bb[EPL], pv[EPL], pb[EPL];
+      const float* vh = vb + hb * Q;
+      const float* bh = bb + hb * Q;
+      float v[EPL], bv[EPL], pv[EPL], pb[EPL];
       float sv = 0.f, sb = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int t = lane * EPL + e;
-        float col = 0.f;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) col += colp[k * Q + t];
-        v[e] = col + cv[t];
-        bb[e] = bv[t];
+        v[e] = vh[t];
+        bv[e] = bh[t];
         pv[e] = sv;
         pb[e] = sb;
         sv += v[e];
-        sb += bb[e];
+        sb += bv[e];
       }
       float iv = sv, ib = sb;
 #pragma unroll
@@ -449,7 +438,7 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
       const float ev = iv - sv, eb = ib - sb;
       float dsum = 0.f;
 #pragma unroll
-      for (int k = 0; k < NW; ++k) dsum += red[k];
+      for (int k = 0; k < NW; ++k) dsum += red[hb * NW + k];
       const float dspan = anext * fast_exp2(cs_last) * dsum;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
@@ -460,7 +449,10 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     if (more) {
       nx.template store<pP>(Xs, tid);
       ny.template store<pP>(Ys, tid);
-      if (tid < Q) csl[((h + 1 - hbeg) & 1) * Q + tid] = ncs;
+      nh.template store<pN>(Hs, tid);
+      nl.template store<pN>(Ls, tid);
+      if (tid < Q) csl[(hb ^ 1) * Q + tid] = ncs;
+      state_dot(nh, nl, red + (hb ^ 1) * NW);
     }
     __syncthreads();
   }
