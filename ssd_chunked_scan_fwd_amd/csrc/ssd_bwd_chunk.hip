@@ -44,8 +44,9 @@ struct BwdCfg {
   static constexpr int offB = 0, offC = Q * pN, offX = 2 * Q * pN, offY = offX + Q * pP, offH = offY + Q * pP,
                        offL = offH + P * pN, halfElems = offL + P * pN;
   // fp32 after the tiles, two heads in flight: cs [2][Q], the per-token pair
-  // terms v and b [2][Q] each, the state dot products [2][NW].
-  static constexpr int floats = 6 * Q + 2 * NW;
+  // terms v and b [2][Q] each, the state dot products [2][NW]; and the row
+  // sums of the pair tiles, one partial per wave, [NW][Q].
+  static constexpr int floats = 6 * Q + 2 * NW + NW * Q;
   static constexpr size_t lds_bytes = (size_t)halfElems * 2 + (size_t)floats * 4;
   static_assert(Q == 64 || Q == 128, "chunk of 64 or 128 tokens");
   static_assert(P % 32 == 0 && N % 32 == 0, "head and state sizes in multiples of 32");
@@ -174,6 +175,7 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
   float* vb = csl + 2 * Q;                                    // [2][Q] col_k - row_k + c_k
   float* bb = vb + 2 * Q;                                     // [2][Q] b_u
   float* red = bb + 2 * Q;                                    // [2][NW]
+  float* rowp = red + 2 * NW;                                 // [NW][Q] row sums over this wave's keys
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g4 = lane >> 4;
@@ -242,11 +244,13 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     const float* cs = csl + hb * Q;
     const float anext = last_chunk ? 1.f : fast_exp2(la[(long)(tok0 + len) * H + h] * kLog2e);
     const float csu = cs[u];
+    for (int q = lane; q < Q; q += 64) rowp[w * Q + q] = 0.f;  // this wave's row only
 
     // ---- the strip as keys: query tiles ut >= i in pairs (one 32-token k block
     // of the pair-order operands). W1 = L o C B^T (bf16 hi and lo parts) and
     // W2 = L o dY X^T feed dX^T += dY^T W1 and dB^T += C^T W2; the column
-    // sums of S = W1 o dY X^T (queries u > s) feed d log a.
+    // sums of S = W1 o dY X^T (queries u > s) and its row sums (keys s < u of
+    // this strip, partial per wave) feed d log a.
     f32x4 dx[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) dx[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -267,14 +271,22 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
                             m2);
         const f32x4 csq = *reinterpret_cast<const f32x4*>(cs + 16 * ut + 4 * g4);
         const f32x4 mk = cbt(ut, true);
-        float a1[4], a2[4];
+        float a1[4], a2[4], sv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int uq = 16 * ut + 4 * g4 + r;  // query row; the key is the lane's token
           const float l = uq >= u ? fast_exp2(csq[r] - csu) : 0.f;
           a1[r] = l * mk[r];
           a2[r] = l * m2[r];
-          colsum += uq > u ? a1[r] * m2[r] : 0.f;
+          sv[r] = uq > u ? a1[r] * m2[r] : 0.f;
+          colsum += sv[r];
+        }
+        // row sums of the query rows over this strip's keys
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[r] = sum_row16(sv[r]);
+        if (c == 0) {
+          f32x4* rp = reinterpret_cast<f32x4*>(rowp + w * Q + 16 * ut + 4 * g4);
+          *rp += f32x4{sv[0], sv[1], sv[2], sv[3]};
         }
         w1h[2 * hf] = pack_bf16x2(a1[0], a1[1]);
         w1h[2 * hf + 1] = pack_bf16x2(a1[2], a1[3]);
@@ -296,9 +308,7 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
     }
 
     // ---- the strip as queries: key tiles st <= i in pairs. W2 = L o dY X^T in
-    // this orientation feeds dC^T += B^T W2^T; the row sums of S (keys s < u)
-    // feed d log a.
-    float rowsum = 0.f;
+    // this orientation feeds dC^T += B^T W2^T.
 #pragma unroll
     for (int kk = 0; kk < HALF; ++kk) {
       if (2 * kk > i) continue;
@@ -314,14 +324,12 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
           m2 = mfma16x16x32(frag_k_cols(Xs, pP, 16 * st, 32 * kp, lane), frag_k_cols(Ys, pP, 16 * i, 32 * kp, lane),
                             m2);
         const f32x4 csk = *reinterpret_cast<const f32x4*>(cs + 16 * st + 4 * g4);
-        const f32x4 mq = cbt(st, false);
         float a2[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int sk = 16 * st + 4 * g4 + r;  // key row; the query is the lane's token
           const float l = sk <= u ? fast_exp2(csu - csk[r]) : 0.f;
           a2[r] = l * m2[r];
-          rowsum += sk < u ? l * mq[r] * m2[r] : 0.f;
         }
         w2q[2 * hf] = pack_bf16x2(a2[0], a2[1]);
         w2q[2 * hf + 1] = pack_bf16x2(a2[2], a2[3]);
@@ -331,7 +339,6 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
       for (int m = 0; m < NT; ++m) dc[m] = mfma16x16x32(frag_k_rows_accpair(Bs, pN, 32 * kk, 16 * m, lane), bq, dc[m]);
     }
     colsum = sum_rows4(colsum);
-    rowsum = sum_rows4(rowsum);
 
     // The next head's inputs, fetched into registers while this head's state
     // terms are computed.
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
       }
       cc = sum_rows4(cc);
       if (g4 == 0) {
-        vb[hb * Q + u] = colsum - rowsum + cc;
+        vb[hb * Q + u] = colsum + cc;
         bb[hb * Q + u] = b * fu;
       }
       // dC^T += h^T (2^cs dY)^T ; dB^T += lam^T (e X)^T
@@ -418,7 +425,10 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const int t = lane * EPL + e;
-        v[e] = vh[t];
+        float rsum = 0.f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) rsum += rowp[k * Q + t];
+        v[e] = vh[t] - rsum;
         bv[e] = bh[t];
         pv[e] = sv;
         pb[e] = sb;
