@@ -28,6 +28,8 @@ gate around that recurrence (paper card Method 6, Paper vs code 3, 7, 8).
 
 ``backward`` is reverse mode through the same recurrence (its adjoint), the
 plain definition of the gradients; the pages give no backward algorithm.
+``mamba2_backward`` applies the chain rule through the Mamba-2 gate, skip and
+discretisation around it.
 
 Every function in this file is pinned by ``tests/test_oracle.py`` against the
 quadratic dual form, closed forms, causal linear attention, packing,
@@ -371,6 +373,71 @@ def backward(X, la, B, C, dY, dfinal=None, cu_seqlens=None, init=None, mutant: i
                 lam = a * lam
         dinit[si] = np.transpose(lam, (0, 2, 1))
     return dict(dX=dX, dlog_a=dla, dB=dB, dC=dC, dinit=dinit)
+
+
+# ---------------------------------------------------------------------------
+# Backward of the Mamba-2 block's call (mamba2_forward): the chain rule through
+# the gate, the skip and the discretisation around the recurrence's backward.
+# With dt' = softplus(dt + dt_bias), A = -exp(A_log), x~ = x dt', v = SSM(x~) +
+# D x and y = v silu(z):
+#   dz = dY v silu'(z),  silu'(g) = sig(g) (1 + g (1 - sig(g))),  dv = dY silu(z)
+#   (dx~, d log a, dB, dC, d h_init) = backward of the recurrence for cotangent dv
+#   dx = dx~ dt' + D dv,   dD = sum_{t,p} dv x
+#   d dt' = sum_p dx~ x + A d log a,   d dt = d dt' sig(dt + dt_bias)
+#   d dt_bias = sum_t d dt,   d A_log = A sum_t dt' d log a
+# (softplus' = sig; dA / dA_log = A).
+# ---------------------------------------------------------------------------
+MAMBA2_BACKWARD_MUTANTS = {
+    "gate_derivative_sigmoid": 1,   # dz with sig(z) in place of silu'(z)
+    "skip_grad_scaled": 2,          # the skip's dx multiplied by dt'
+    "softplus_derivative_dropped": 3,  # d dt = d dt'
+    "A_log_chain_dropped": 4,       # d A_log = sum_t dt' d log a (factor A dropped)
+}
+
+
+def _sigmoid(v):
+    return 0.5 * (1.0 + np.tanh(0.5 * _f64(v)))
+
+
+def mamba2_backward(X, dt, dt_bias, A_log, D, z, B, C, dY, dfinal=None, cu_seqlens=None, init=None,
+                    mutant: int = 0):
+    """Gradients of L = <dY, y> + <dfinal, final> for mamba2_forward with the same inputs.
+
+    Returns dict(dX, ddt, ddt_bias, dA_log, dD, dz, dB, dC, dinit), fp64; dD is None
+    without a skip, dz None without a gate; ddt_bias is returned whether or not a
+    bias was given (the gradient with respect to a zero bias).
+    """
+    x, dY = _f64(X), _f64(dY)
+    dtp, la = mamba2_discretize(dt, dt_bias, A_log)
+    A = -np.exp(_f64(A_log))
+    xs = x * dtp[..., None]
+    dz = None
+    dv = dY
+    if z is not None:
+        g = _f64(z)
+        sg = _sigmoid(g)
+        u, _ = forward(xs, la, B, C, cu_seqlens=cu_seqlens, init=init)
+        v = u + (0.0 if D is None else _f64(D)[None, None, :, None] * x)
+        dsilu = sg if mutant == MAMBA2_BACKWARD_MUTANTS["gate_derivative_sigmoid"] else sg * (1.0 + g * (1.0 - sg))
+        dz = dY * v * dsilu
+        dv = dY * (g * sg)
+    gs = backward(xs, la, B, C, dv, dfinal=dfinal, cu_seqlens=cu_seqlens, init=init)
+    dxs, dla = gs["dX"], gs["dlog_a"]
+    dX = dxs * dtp[..., None]
+    if D is not None:
+        skip = _f64(D)[None, None, :, None] * dv
+        if mutant == MAMBA2_BACKWARD_MUTANTS["skip_grad_scaled"]:
+            skip = skip * dtp[..., None]
+        dX = dX + skip
+    ddtp = np.sum(dxs * x, axis=-1) + A * dla
+    bias = np.zeros(dtp.shape[-1]) if dt_bias is None else _f64(dt_bias)
+    ddt = ddtp if mutant == MAMBA2_BACKWARD_MUTANTS["softplus_derivative_dropped"] else \
+        ddtp * _sigmoid(_f64(dt) + bias)
+    dA = np.sum(dla * dtp, axis=(0, 1))
+    dA_log = dA if mutant == MAMBA2_BACKWARD_MUTANTS["A_log_chain_dropped"] else dA * A
+    dD = None if D is None else np.sum(dv * x, axis=(0, 1, 3))
+    return dict(dX=dX, ddt=ddt, ddt_bias=np.sum(ddt, axis=(0, 1)), dA_log=dA_log, dD=dD, dz=dz,
+                dB=gs["dB"], dC=gs["dC"], dinit=gs["dinit"])
 
 
 def chunk_cumsum(la, segments) -> np.ndarray:

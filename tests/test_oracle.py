@@ -555,3 +555,91 @@ def _bwd_pins(mutant):
 def test_backward_mutants_are_caught(name):
     assert _bwd_pins(0) == []
     assert _bwd_pins(oracle.BACKWARD_MUTANTS[name]), f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# Backward of the Mamba-2 call: central differences of the pinned
+# mamba2_forward along one random direction per input.
+# ---------------------------------------------------------------------------
+def _m2_case(T=9, H=2, P=3, N=4, G=1, seed=61, lengths=None, skip=True, gate=True, bias=True):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((1, T, H, P))
+    dt = rng.uniform(-3.0, 1.0, size=(1, T, H))
+    dtb = rng.uniform(-1.0, 0.5, size=H) if bias else None
+    A_log = rng.uniform(-1.0, 1.5, size=H)
+    D = rng.standard_normal(H) if skip else None
+    z = rng.standard_normal((1, T, H, P)) * 2.0 if gate else None
+    B = rng.standard_normal((1, T, G, N))
+    C = rng.standard_normal((1, T, G, N))
+    dY = rng.standard_normal((1, T, H, P))
+    S = 1 if lengths is None else len(lengths)
+    dfin = rng.standard_normal((S, H, P, N))
+    init = rng.standard_normal((S, H, P, N))
+    cu = None if lengths is None else np.concatenate([[0], np.cumsum(lengths)])
+    return dict(X=X, dt=dt, dt_bias=dtb, A_log=A_log, D=D, z=z, B=B, C=C, init=init), dY, dfin, cu
+
+
+def _m2_fd_errors(g, case):
+    args, dY, dfin, cu = case
+
+    def loss(a):
+        Y, fin = oracle.mamba2_forward(a["X"], a["dt"], a["dt_bias"], a["A_log"], a["D"], a["z"], a["B"], a["C"],
+                                       cu_seqlens=cu, init=a["init"])
+        return float(np.sum(dY * Y) + np.sum(dfin * fin))
+
+    names = dict(X="dX", dt="ddt", dt_bias="ddt_bias", A_log="dA_log", D="dD", z="dz", B="dB", C="dC",
+                 init="dinit")
+    rng = np.random.default_rng(7)
+    out = {}
+    eps = 1e-6
+    for k, gk in names.items():
+        if args[k] is None:
+            continue
+        v = rng.standard_normal(np.shape(args[k]))
+        ap, am = dict(args), dict(args)
+        ap[k] = args[k] + eps * v
+        am[k] = args[k] - eps * v
+        fd = (loss(ap) - loss(am)) / (2 * eps)
+        an = float(np.sum(g[gk] * v))
+        out[k] = abs(fd - an) / max(abs(fd), 1e-12)
+    return out
+
+
+@pytest.mark.parametrize("skip,gate,bias", [(True, True, True), (False, True, False), (True, False, True),
+                                            (False, False, False)])
+def test_mamba2_backward_matches_finite_differences(skip, gate, bias):
+    case = _m2_case(skip=skip, gate=gate, bias=bias, seed=62 + 2 * skip + gate)
+    args, dY, dfin, cu = case
+    g = oracle.mamba2_backward(**args, dY=dY, dfinal=dfin, cu_seqlens=cu)
+    errs = _m2_fd_errors(g, case)
+    assert errs and all(e < 1e-6 for e in errs.values()), errs
+    assert (g["dD"] is None) == (not skip) and (g["dz"] is None) == (not gate)
+
+
+def test_mamba2_backward_packed_grouped():
+    case = _m2_case(T=11, H=4, G=2, lengths=[4, 1, 6], seed=70)
+    args, dY, dfin, cu = case
+    g = oracle.mamba2_backward(**args, dY=dY, dfinal=dfin, cu_seqlens=cu)
+    errs = _m2_fd_errors(g, case)
+    assert all(e < 1e-6 for e in errs.values()), errs
+
+
+def test_mamba2_backward_without_gate_and_skip_is_the_chain_rule_of_backward():
+    # no gate, no skip, no bias: dX = dx~ dt', and the recurrence gradients are backward()'s
+    case = _m2_case(T=7, seed=71, skip=False, gate=False, bias=False)
+    args, dY, dfin, cu = case
+    g = oracle.mamba2_backward(**args, dY=dY, dfinal=dfin)
+    dtp, la = oracle.mamba2_discretize(args["dt"], None, args["A_log"])
+    gs = oracle.backward(args["X"] * dtp[..., None], la, args["B"], args["C"], dY, dfinal=dfin, init=args["init"])
+    np.testing.assert_allclose(g["dX"], gs["dX"] * dtp[..., None], rtol=1e-13)
+    np.testing.assert_allclose(g["dB"], gs["dB"], rtol=1e-13)
+
+
+@pytest.mark.parametrize("name", sorted(oracle.MAMBA2_BACKWARD_MUTANTS))
+def test_mamba2_backward_mutants_are_caught(name):
+    case = _m2_case(seed=73)
+    args, dY, dfin, cu = case
+    ok = oracle.mamba2_backward(**args, dY=dY, dfinal=dfin)
+    assert all(e < 1e-6 for e in _m2_fd_errors(ok, case).values())
+    bad = oracle.mamba2_backward(**args, dY=dY, dfinal=dfin, mutant=oracle.MAMBA2_BACKWARD_MUTANTS[name])
+    assert any(e > 1e-4 for e in _m2_fd_errors(bad, case).values()), f"mutant {name} passed"
