@@ -10,9 +10,10 @@ Prints ONE JSON line with the headline throughput (tokens/s), the roofline of
 the dominant kernel (its algorithmic bytes / its average launch time, timed with
 HIP events on the launch stream), per-stage times, the decode-step throughput,
 the Mamba-2 block's call on the same shape (ssd_fwd_mamba2: raw step sizes,
-dt_bias, A_log, the D skip and the silu(z) gate) and its decode step, the
-backward pass (ssd_bwd) on the same shape, and the fp64 CPU oracle timed on
-this host as a baseline.
+dt_bias, A_log, the D skip and the silu(z) gate), its backward
+(ssd_bwd_mamba2) and its decode step, the backward pass (ssd_bwd) on the same
+shape, the state chain as one cooperative launch, and the fp64 CPU oracle
+timed on this host as a baseline.
 
 Per-stage times come from each stage's own entry point (the four-launch form
 of the stage API); the step itself runs three launches, chunk_state computing
@@ -289,6 +290,27 @@ def main() -> int:
         out["mamba2"] = {"workload": w.name + " (Mamba-2 call: dt, dt_bias, A_log, D, z)", "steps": args.steps,
                          "ms_per_step": round(m_ms, 5), "event_ms_per_step": round(a.elapsed_time(b) / args.steps, 5),
                          "tokens_per_s": round(tokens / (m_ms * 1e-3), 1)}
+        if not args.no_bwd:
+            # its backward (ssd_bwd_mamba2): every input's gradient from dY
+            ctm = synth.make_cotangents(w.batch, w.T, w.H, w.P, w.N, w.batch, w.torch_dtype, w.seed + 2)
+            mdY = ctm["dY"].to(dev)
+            mws = torch.empty(ssd.bwd_mamba2_workspace_bytes(shape, w.Q, ws.state_block), dtype=torch.uint8,
+                              device=dev)
+
+            def mbstep():
+                return ssd.bwd_mamba2(mX, mdt, mAl, mB, mC, mdY, dt_bias=mbias, D=mD, z=mz, chunk=w.Q,
+                                      state_block=ws.state_block, workspace=mws)
+
+            nb = max(1, min(args.bwd_steps, args.steps))
+            for _ in range(min(args.warmup, 10)):
+                mbstep()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(nb):
+                mbstep()
+            torch.cuda.synchronize()
+            out["mamba2"]["bwd_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / nb, 5)
+            del mdY, mws
         del mX, mdt, mbias, mAl, mD, mz, mB, mC
 
     if not args.no_chain:

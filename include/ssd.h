@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum {
   SSD_OK = 0,
@@ -297,6 +297,37 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
                    const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
                    int32_t state_block, void* dX, float* dlog_a, void* dB, void* dC, float* dinitial_state,
                    const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass of the Mamba-2 block's call (ssd_fwd_mamba2): the gradients of
+ * L = <dY, y> + <dfinal_state, final_state> with respect to every input. The
+ * chain rule runs through the gate, the skip and the discretisation (paper card
+ * Method 6 block sketch; Paper vs code items 3, 7, 8) around ssd_bwd:
+ *   dz = dY v silu'(z) with v the output before the gate, dv = dY silu(z);
+ *   ssd_bwd of the recurrence on x dt' (rounded to the input dtype) and
+ *   log a = dt' A with cotangent dv gives d(x dt'), d log a, dB, dC and the
+ *   initial-state gradient;
+ *   dX = d(x dt') dt' + D dv;  ddt = (sum_p d(x dt') x + A d log a) sig(dt + dt_bias);
+ *   dD = sum dv x;  ddt_bias = sum_t ddt;  dA_log = A sum_t dt' d log a.
+ * Inputs as for ssd_fwd_mamba2, plus dY [batch, seqlen, nheads, headdim]
+ * (dtype) and dfinal_state (fp32, final-state layout, NULL for zero).
+ * Outputs: dX, dz (dtype, X's layout; dz NULL exactly when z is NULL),
+ * ddt [batch, seqlen, nheads] fp32, ddt_bias, dA_log, dD [nheads] fp32 (dD NULL
+ * exactly when D is NULL; ddt_bias may be NULL), dB, dC (dtype, B's layout),
+ * dinitial_state (fp32, optional). headdim must be a multiple of 4, at most 256,
+ * and the shape one that ssd_bwd supports. With a gate the forward call runs
+ * once more (without the gate) for v. The workspace must hold
+ * ssd_bwd_mamba2_workspace_bytes(shape, chunk, state_block); it is all
+ * overwritten. Same stream, alignment and error rules as ssd_bwd.
+ */
+ssd_status ssd_bwd_mamba2_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_t state_block,
+                                          size_t* bytes);
+ssd_status ssd_bwd_mamba2(const void* X, const float* dt, const float* dt_bias, const float* A_log, const float* D,
+                          const void* z, const void* B, const void* C, const int32_t* cu_seqlens,
+                          const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
+                          int32_t state_block, void* dX, float* ddt, float* ddt_bias, float* dA_log, float* dD,
+                          void* dz, void* dB, void* dC, float* dinitial_state, const ssd_shape* shape,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step for `batch` independent streams: the loop body of

@@ -403,9 +403,10 @@ def mamba2_backward(X, dt, dt_bias, A_log, D, z, B, C, dY, dfinal=None, cu_seqle
                     mutant: int = 0):
     """Gradients of L = <dY, y> + <dfinal, final> for mamba2_forward with the same inputs.
 
-    Returns dict(dX, ddt, ddt_bias, dA_log, dD, dz, dB, dC, dinit), fp64; dD is None
-    without a skip, dz None without a gate; ddt_bias is returned whether or not a
-    bias was given (the gradient with respect to a zero bias).
+    Returns dict(dX, ddt, ddt_bias, dA_log, dD, dz, dB, dC, dinit, dxs), fp64; dD is
+    None without a skip, dz None without a gate; ddt_bias is returned whether or not
+    a bias was given (the gradient with respect to a zero bias); dxs is the
+    recurrence's gradient of its input x dt'.
     """
     x, dY = _f64(X), _f64(dY)
     dtp, la = mamba2_discretize(dt, dt_bias, A_log)
@@ -437,7 +438,7 @@ def mamba2_backward(X, dt, dt_bias, A_log, D, z, B, C, dY, dfinal=None, cu_seqle
     dA_log = dA if mutant == MAMBA2_BACKWARD_MUTANTS["A_log_chain_dropped"] else dA * A
     dD = None if D is None else np.sum(dv * x, axis=(0, 1, 3))
     return dict(dX=dX, ddt=ddt, ddt_bias=np.sum(ddt, axis=(0, 1)), dA_log=dA_log, dD=dD, dz=dz,
-                dB=gs["dB"], dC=gs["dC"], dinit=gs["dinit"])
+                dB=gs["dB"], dC=gs["dC"], dinit=gs["dinit"], dxs=dxs)
 
 
 def chunk_cumsum(la, segments) -> np.ndarray:

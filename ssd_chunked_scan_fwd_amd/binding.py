@@ -26,7 +26,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "ssd_fwd_layout",
            "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
            "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2",
-           "ssd_bwd_workspace_bytes", "ssd_bwd", "ssd_set_state_chain")
+           "ssd_bwd_workspace_bytes", "ssd_bwd", "ssd_set_state_chain", "ssd_bwd_mamba2_workspace_bytes",
+           "ssd_bwd_mamba2")
 
 
 class SSDError(RuntimeError):
@@ -96,6 +97,10 @@ def lib():
         L.ssd_step_mamba2.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, shp, vp]
         L.ssd_set_state_chain.restype = i32
         L.ssd_set_state_chain.argtypes = [i32]
+        L.ssd_bwd_mamba2_workspace_bytes.restype = ctypes.c_int
+        L.ssd_bwd_mamba2_workspace_bytes.argtypes = [shp, i32, i32, ctypes.POINTER(sz)]
+        L.ssd_bwd_mamba2.restype = ctypes.c_int
+        L.ssd_bwd_mamba2.argtypes = [vp] * 12 + [i32, i32] + [vp] * 9 + [shp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -395,3 +400,45 @@ def bwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor, 
           _ptr(dfinal_state), int(chunk), int(state_block), _ptr(dX), _ptr(dla), _ptr(dB), _ptr(dC), _ptr(dinit),
           ctypes.byref(shape), _ptr(workspace), workspace.numel(), _stream(X.device))
     return dict(dX=dX, dlog_a=dla, dB=dB, dC=dC, dinit=dinit)
+
+
+def bwd_mamba2_workspace_bytes(shape: Shape, chunk: int, state_block: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    _call("ssd_bwd_mamba2_workspace_bytes", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(n))
+    return int(n.value)
+
+
+def bwd_mamba2(X: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+               dY: torch.Tensor, dt_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
+               z: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None, chunk: int = 128,
+               state_block: int = 0, initial_state: Optional[torch.Tensor] = None,
+               dfinal_state: Optional[torch.Tensor] = None, want_dinit: bool = False,
+               workspace: Optional[torch.Tensor] = None):
+    """Backward pass of the Mamba-2 call (ssd_bwd_mamba2). Returns dict(dX, ddt, ddt_bias,
+    dA_log, dD or None, dz or None, dB, dC, dinit or None)."""
+    _check_inputs(X, None, B, C, cu_seqlens)
+    _check_mamba2(X, dt, dt_bias, A_log, D, z, X.shape[2])
+    if dY.dtype != X.dtype or not dY.is_cuda or not dY.is_contiguous() or dY.shape != X.shape:
+        raise ValueError("dY must be a contiguous device tensor of X's shape and dtype")
+    shape = make_shape(X, B, cu_seqlens)
+    _check_state(initial_state, shape, "initial_state")
+    _check_state(dfinal_state, shape, "dfinal_state")
+    nbytes = bwd_mamba2_workspace_bytes(shape, chunk, state_block)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    H = X.shape[2]
+    out = dict(dX=torch.empty_like(X), ddt=torch.empty_like(dt),
+               ddt_bias=torch.empty(H, dtype=torch.float32, device=X.device),
+               dA_log=torch.empty(H, dtype=torch.float32, device=X.device),
+               dD=None if D is None else torch.empty(H, dtype=torch.float32, device=X.device),
+               dz=None if z is None else torch.empty_like(z), dB=torch.empty_like(B), dC=torch.empty_like(C),
+               dinit=None)
+    if want_dinit:
+        nseq = X.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+        out["dinit"] = torch.empty(nseq, H, X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
+    _call("ssd_bwd_mamba2", _ptr(X), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(D), _ptr(z), _ptr(B), _ptr(C),
+          _ptr(cu_seqlens), _ptr(initial_state), _ptr(dY), _ptr(dfinal_state), int(chunk), int(state_block),
+          _ptr(out["dX"]), _ptr(out["ddt"]), _ptr(out["ddt_bias"]), _ptr(out["dA_log"]), _ptr(out["dD"]),
+          _ptr(out["dz"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dinit"]), ctypes.byref(shape),
+          _ptr(workspace), workspace.numel(), _stream(X.device))
+    return out

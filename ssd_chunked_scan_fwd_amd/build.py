@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssd_mi355x.so")
-SOURCES = ["ssd_api.cpp", "ssd_cumsum_passing.hip", "ssd_chunk_state.hip", "ssd_chunk_scan.hip", "ssd_bwd.hip", "ssd_bwd_chunk.hip"]
+SOURCES = ["ssd_api.cpp", "ssd_cumsum_passing.hip", "ssd_chunk_state.hip", "ssd_chunk_scan.hip", "ssd_bwd.hip", "ssd_bwd_chunk.hip", "ssd_bwd_mamba2.hip"]
 
 
 def hipcc() -> str:

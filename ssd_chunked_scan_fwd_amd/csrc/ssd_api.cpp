@@ -618,6 +618,106 @@ ssd_status ssd_step_mamba2(float* state, const void* x, const float* dt, const f
 
 int32_t ssd_set_state_chain(int32_t mode) { return g_state_chain.exchange(mode ? 1 : 0); }
 
+// Workspace of ssd_bwd_mamba2: one region that the ungated forward run (for v)
+// and then ssd_bwd use in turn, then v, log a, x dt', dv, the recurrence's
+// gradients of x dt' and log a, and the per-(token block, head) partial sums.
+struct M2BwdLayout {
+  size_t region, v, la, xs, dv, dxs, dla, part, total;
+};
+
+static ssd_status m2_bwd_layout(const ssd_shape* s, int32_t chunk, int32_t gs, M2BwdLayout* out) {
+  size_t bwd = 0, fwd = 0;
+  ssd_status st = ssd_bwd_workspace_bytes(s, chunk, gs, &bwd);
+  if (st != SSD_OK) return st;
+  st = ssd_fwd_workspace_bytes(s, chunk, gs, &fwd);
+  if (st != SSD_OK) return st;
+  if (s->headdim % 4 || s->headdim > 256) return SSD_ERR_UNSUPPORTED;  // four channels per thread
+  const size_t esz = s->dtype == SSD_DTYPE_BF16 ? 2 : 4;
+  const size_t tok = (size_t)s->batch * s->seqlen, H = s->nheads, P = s->headdim;
+  M2BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+  L.region = take(bwd > fwd ? bwd : fwd);
+  L.v = take(tok * H * P * esz);
+  L.la = take(tok * H * 4);
+  L.xs = take(tok * H * P * esz);
+  L.dv = take(tok * H * P * esz);
+  L.dxs = take(tok * H * P * esz);
+  L.dla = take(tok * H * 4);
+  L.part = take((size_t)ssd::m2_token_blocks((long)tok) * H * 3 * 4);
+  L.total = off;
+  *out = L;
+  return SSD_OK;
+}
+
+ssd_status ssd_bwd_mamba2_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_t state_block,
+                                          size_t* bytes) {
+  if (!shape || !bytes) return SSD_ERR_INVALID_ARGUMENT;
+  M2BwdLayout L;
+  const ssd_status st = m2_bwd_layout(shape, chunk, state_block, &L);
+  if (st != SSD_OK) return st;
+  *bytes = L.total;
+  return SSD_OK;
+}
+
+ssd_status ssd_bwd_mamba2(const void* X, const float* dt, const float* dt_bias, const float* A_log, const float* D,
+                          const void* z, const void* B, const void* C, const int32_t* cu_seqlens,
+                          const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
+                          int32_t state_block, void* dX, float* ddt, float* ddt_bias, float* dA_log, float* dD,
+                          void* dz, void* dB, void* dC, float* dinitial_state, const ssd_shape* shape,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !dt || !A_log || !B || !C || !dY || !dX || !ddt || !dA_log || !dB || !dC || !shape)
+    return SSD_ERR_INVALID_ARGUMENT;
+  if ((D == nullptr) != (dD == nullptr) || (z == nullptr) != (dz == nullptr)) return SSD_ERR_INVALID_ARGUMENT;
+  if (!workspace || ((uintptr_t)workspace & 255)) return SSD_ERR_INVALID_ARGUMENT;
+  M2BwdLayout L;
+  ssd_status st = m2_bwd_layout(shape, chunk, state_block, &L);
+  if (st != SSD_OK) return st;
+  if (workspace_bytes < L.total) return SSD_ERR_WORKSPACE_TOO_SMALL;
+  char* w = static_cast<char*>(workspace);
+  const size_t region_bytes = L.v - L.region;
+  hipStream_t hs = (hipStream_t)stream;
+  ssd::M2BwdArgs a{};
+  a.X = X;
+  a.dt = dt;
+  a.dt_bias = dt_bias;
+  a.A_log = A_log;
+  a.D = D;
+  a.z = z;
+  a.dY = dY;
+  a.v = w + L.v;
+  a.la = reinterpret_cast<float*>(w + L.la);
+  a.xs = w + L.xs;
+  a.dv = w + L.dv;
+  a.dz = dz;
+  a.dv_in = z ? static_cast<const void*>(w + L.dv) : dY;
+  a.dxs = w + L.dxs;
+  a.dla = reinterpret_cast<float*>(w + L.dla);
+  a.dXo = dX;
+  a.ddt = ddt;
+  a.ddt_bias = ddt_bias;
+  a.dA_log = dA_log;
+  a.dD = dD;
+  a.part = reinterpret_cast<float*>(w + L.part);
+  a.tokens = (long)shape->batch * shape->seqlen;
+  a.H = shape->nheads;
+  a.P = shape->headdim;
+  a.bf16 = shape->dtype == SSD_DTYPE_BF16 ? 1 : 0;
+  // v = SSM(x dt') + D x: the call itself without the gate, for dz.
+  if (z) {
+    st = ssd_fwd_mamba2(X, dt, dt_bias, A_log, D, nullptr, B, C, cu_seqlens, initial_state, chunk, state_block,
+                        w + L.v, nullptr, shape, w + L.region, region_bytes, stream);
+    if (st != SSD_OK) return st;
+  }
+  hipError_t e = ssd::launch_m2_prep(a, hs);
+  if (e != hipSuccess) return hip_status(e);
+  st = ssd_bwd(w + L.xs, a.la, B, C, cu_seqlens, initial_state, a.dv_in, dfinal_state, chunk, state_block,
+               w + L.dxs, reinterpret_cast<float*>(w + L.dla), dB, dC, dinitial_state, shape, w + L.region,
+               region_bytes, stream);
+  if (st != SSD_OK) return st;
+  return hip_status(ssd::launch_m2_epilogue(a, hs));
+}
+
 ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C, void* y,
                     const ssd_shape* shape, void* stream) {
   if (!shape || !state || !x || !log_a || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;

@@ -140,6 +140,27 @@ hipError_t launch_bwd_chunks(const BwdChunkArgs& a, hipStream_t stream);
 hipError_t launch_chunk_starts(const FwdDims& d, const void* X, const void* B, const Workspace& ws, void* out,
                                hipStream_t stream);
 
+// The chain rule of the Mamba-2 block's call around the recurrence's backward
+// (ssd_bwd_mamba2.hip). Device pointers; `tokens` = rows * T.
+struct M2BwdArgs {
+  const void* X;
+  const float *dt, *dt_bias, *A_log, *D;   // dt_bias and D may be null
+  const void *z, *dY, *v;                 // z null: no gate (then v, dv, dz unused)
+  float* la;                              // [tokens][H] log a (written by the prep kernel)
+  void *xs, *dv, *dz;                     // x dt', dY silu(z), the gate's gradient
+  const void* dv_in;                      // the recurrence's cotangent: dv, or dY without a gate
+  const void* dxs;                        // gradient of x dt' from the recurrence's backward
+  const float* dla;                       // gradient of log a
+  void* dXo;
+  float *ddt, *ddt_bias, *dA_log, *dD;    // ddt_bias and dD may be null
+  float* part;                            // [token blocks][H][3]
+  long tokens;
+  int H, P, bf16;
+};
+long m2_token_blocks(long tokens);
+hipError_t launch_m2_prep(const M2BwdArgs& a, hipStream_t stream);
+hipError_t launch_m2_epilogue(const M2BwdArgs& a, hipStream_t stream);
+
 // Bytes of dynamic LDS the bf16 kernels need (host-side checks).
 size_t chunk_scan_bf16_lds_bytes(int P, int N, int Q);
 size_t chunk_state_bf16_lds_bytes(int P, int N, int block_tokens);  // block_tokens: Gs*Q when fused, else 0

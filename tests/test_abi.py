@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = ssd.lib()
-    assert L.ssd_abi_version() == 4
+    assert L.ssd_abi_version() == 5
     for code, name in binding.STATUS.items():
         assert L.ssd_status_string(code).decode() == name
 
@@ -280,3 +280,29 @@ def test_state_chain_mode_switch():
     assert prev in (0, 1)
     assert ssd.set_state_chain(1) == 0
     assert ssd.set_state_chain(prev) == 1
+
+
+def test_bwd_mamba2_validates():
+    L = ssd.lib()
+    sh = shape(seqlen=4096, nheads=8)
+    n = ctypes.c_size_t(0)
+    assert L.ssd_bwd_mamba2_workspace_bytes(ctypes.byref(sh), 128, 0, ctypes.byref(n)) == OK and n.value > 0
+    # X dt dt_bias A_log D z B C cu init dY dfinal | chunk gs | dX ddt ddt_bias dA_log dD dz dB dC dinit | shape ws n stream
+    args = [FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, None, None, FAKE, None, 128, 0,
+            FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, None, ctypes.byref(sh), FAKE, n.value, None]
+    for i in (0, 1, 3, 6, 7, 10, 14, 15, 17, 20, 21, 23, 24):
+        a = list(args)
+        a[i] = None
+        assert L.ssd_bwd_mamba2(*a) == INVALID, i
+    for i, j in ((4, 18), (5, 19)):   # D needs dD and z needs dz, and the other way round
+        a = list(args)
+        a[i] = FAKE
+        assert L.ssd_bwd_mamba2(*a) == INVALID, i
+        a = list(args)
+        a[j] = FAKE
+        assert L.ssd_bwd_mamba2(*a) == INVALID, j
+    a = list(args)
+    a[25] = n.value - 1
+    assert L.ssd_bwd_mamba2(*a) == WS_SMALL
+    odd = shape(seqlen=512, nheads=8, headdim=18)
+    assert L.ssd_bwd_mamba2_workspace_bytes(ctypes.byref(odd), 64, 0, ctypes.byref(n)) != OK

@@ -1,0 +1,150 @@
+"""GPU parity of the Mamba-2 call's backward pass (ssd_bwd_mamba2) against the
+fp64 oracle (oracle.mamba2_backward: the chain rule through the gate, the skip
+and the discretisation around the recurrence's reverse mode).
+
+The HIP path runs the call once more without the gate (for the output before
+the gate), forms x dt', log a, dY silu(z) and the gate's gradient, runs
+ssd_bwd on them and finishes dX, d dt and the per-head sums (dD, d dt_bias,
+d A_log).
+
+Tolerances are those of the other parity tests, with the gated functional for
+the two outputs that are an element-wise scale of a recurrence result: dz = s v
+(s = dY silu'(z), v the call's output before the gate) with v as the unscaled
+reference, and dX = dt' dx~ + D dv (dt' per token, spanning two orders of
+magnitude) with dx~ as the unscaled reference; the unit scale is carried
+through the scale factor, as for the gated forward output. dB and dC, sums over
+heads of terms that carry those scales, take the same functional with s = 1
+(the plain bar with an allowance relative to |ref_i|).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import ssd_chunked_scan_fwd_amd as ssd
+from ssd_chunked_scan_fwd_amd import synth
+from oracle import oracle
+from parity import assert_close, assert_close_gated, dtype_name, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ssd.lib()
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _f(t):
+    return None if t is None else to_f64(t)
+
+
+def _dfinal(d, nseq, seed, T1=120):
+    """Final-state gradients at the scale a continuation produces: the oracle's
+    initial-state gradient of a seeded piece of T1 more tokens of the same call."""
+    b, _, H, P = d["X"].shape
+    N = d["B"].shape[-1]
+    c = synth.make_mamba2_inputs(nseq, T1, H, P, N, d["B"].shape[2], torch.float32, seed)
+    ct = synth.make_cotangents(nseq, T1, H, P, N, nseq, torch.float32, seed + 1)
+    g = oracle.mamba2_backward(_f(c["X"]), _f(c["dt"]), _f(d["dt_bias"]), _f(d["A_log"]), _f(d["D"]), _f(c["z"]),
+                               _f(c["B"]), _f(c["C"]), _f(ct["dY"]), init=np.zeros((nseq, H, P, N)))
+    return torch.from_numpy(g["dinit"]).float()
+
+
+def check(d, Q, what, gate=True, skip=True, bias=True, with_final=True, gs=0, seed=0):
+    X = d["X"]
+    b, T, H, P = X.shape
+    N = d["B"].shape[-1]
+    cu = d.get("cu_seqlens")
+    nseq = b if cu is None else cu.numel() - 1
+    z = d["z"] if gate else None
+    D = d["D"] if skip else None
+    dtb = d["dt_bias"] if bias else None
+    ct = synth.make_cotangents(b, T, H, P, N, nseq, dtype=X.dtype, seed=seed)
+    dfin = _dfinal(d, nseq, seed + 2) if with_final else None
+    say(f"[bwd-m2] {what}: X{tuple(X.shape)} {X.dtype} N={N} Q={Q} gate={gate} skip={skip} bias={bias} "
+        f"final={with_final} packed={cu is not None}")
+    dev = lambda t: None if t is None else t.cuda()
+    g = ssd.bwd_mamba2(dev(X), dev(d["dt"]), dev(d["A_log"]), dev(d["B"]), dev(d["C"]), dev(ct["dY"]),
+                       dt_bias=dev(dtb), D=dev(D), z=dev(z), cu_seqlens=dev(cu), chunk=Q, state_block=gs,
+                       dfinal_state=dev(dfin), want_dinit=True)
+    torch.cuda.synchronize()
+    r = oracle.mamba2_backward(_f(X), _f(d["dt"]), _f(dtb), _f(d["A_log"]), _f(D), _f(z), _f(d["B"]), _f(d["C"]),
+                               _f(ct["dY"]), dfinal=_f(dfin), cu_seqlens=None if cu is None else cu.numpy())
+    dt_name = dtype_name(X)
+    errs = {}
+    for k in ("dX", "ddt", "dA_log", "dB", "dC", "dinit", "dD", "dz", "ddt_bias"):
+        if r.get(k) is None:
+            assert g[k] is None, k
+            continue
+        if k == "dz":
+            # dz = s v with s = dY silu'(z) per element and v the output before the
+            # gate: v's unit scale is carried through the product, as for the gated
+            # forward output.
+            v, _ = oracle.mamba2_forward(_f(X), _f(d["dt"]), _f(dtb), _f(d["A_log"]), _f(D), None, _f(d["B"]),
+                                         _f(d["C"]), cu_seqlens=None if cu is None else cu.numpy())
+            zz = _f(z)
+            sg = 0.5 * (1.0 + np.tanh(0.5 * zz))
+            scale = _f(ct["dY"]) * sg * (1.0 + zz * (1.0 - sg))
+            errs[k] = assert_close_gated(_f(g[k]), r[k], v, scale, dt_name, f"{what} {k}")
+            errs[k]["max_unit"] = errs[k]["max_gated"]
+            continue
+        if k == "dX":
+            # dX = dt' dx~ + D dv: the per-token step size dt' spans two orders of
+            # magnitude, so dx~'s unit scale is carried through it (the skip term
+            # is formed in fp32 from the inputs and rounded once).
+            dtp, _ = oracle.mamba2_discretize(_f(d["dt"]), _f(dtb), _f(d["A_log"]))
+            errs[k] = assert_close_gated(_f(g[k]), r[k], r["dxs"], np.broadcast_to(dtp[..., None], r[k].shape),
+                                         dt_name, f"{what} {k}")
+            errs[k]["max_unit"] = errs[k]["max_gated"]
+            continue
+        if k in ("dB", "dC"):
+            # Sums over heads of terms carrying x dt' (dt' per token) and dY silu(z)
+            # (per element): heavy-tailed, so the bar takes an allowance relative
+            # to |ref_i| as well (the gated functional with s = 1).
+            errs[k] = assert_close_gated(_f(g[k]), r[k], r[k], np.ones_like(r[k]), dt_name, f"{what} {k}")
+            errs[k]["max_unit"] = errs[k]["max_gated"]
+            continue
+        errs[k] = assert_close(_f(g[k]), r[k], dt_name, f"{what} {k}")
+    say(f"[bwd-m2] {what}: " + " ".join(f"{k} rel_l2={e['rel_l2']:.2e} max_unit={e['max_unit']:.3f}"
+                                        for k, e in errs.items()))
+    return g
+
+
+@pytest.mark.parametrize("case", [
+    # (batch, T, H, P, N, G, dtype, Q)
+    (1, 300, 4, 64, 128, 1, torch.bfloat16, 128),   # the fused backward path, ragged tail
+    (2, 200, 4, 32, 64, 2, torch.bfloat16, 64),     # two groups
+    (1, 129, 2, 128, 32, 1, torch.bfloat16, 32),    # the general backward path
+    (1, 77, 3, 16, 16, 1, torch.float32, 16),       # fp32
+], ids=lambda c: "b{}-T{}-H{}-P{}-N{}-G{}-{}-Q{}".format(*c[:6], "bf16" if c[6] == torch.bfloat16 else "fp32", c[7]))
+def test_bwd_mamba2_shapes(case):
+    b, T, H, P, N, G, dt, Q = case
+    d = synth.make_mamba2_inputs(b, T, H, P, N, G, dt, seed=5000 + T)
+    check(d, Q, f"shape {case}", seed=21)
+
+
+@pytest.mark.parametrize("gate,skip,bias,final", [(False, True, True, True), (True, False, True, False),
+                                                  (True, True, False, True), (False, False, False, False)])
+def test_bwd_mamba2_optional_parts(gate, skip, bias, final):
+    d = synth.make_mamba2_inputs(1, 260, 4, 64, 64, 1, torch.bfloat16, seed=5100)
+    check(d, 64, "optional parts", gate=gate, skip=skip, bias=bias, with_final=final, seed=22)
+
+
+def test_bwd_mamba2_packed():
+    lengths = [1, 200, 64, 65, 3, 129, 1, 90]
+    d = synth.make_mamba2_inputs(1, sum(lengths), 3, 32, 64, 1, torch.bfloat16, seed=5200, lengths=lengths)
+    check(d, 64, f"packed {lengths}", gs=2, seed=23)
+
+
+def test_bwd_mamba2_long_sequence():
+    """T = 4096 at the headline head and state sizes (8 heads, state blocks of 8 chunks)."""
+    d = synth.make_mamba2_inputs(1, 4096, 8, 64, 128, 1, torch.bfloat16, seed=5300)
+    check(d, 128, "long sequence", seed=24)
