@@ -12,8 +12,8 @@ HIP events on the launch stream), per-stage times, the decode-step throughput,
 the Mamba-2 block's call on the same shape (ssd_fwd_mamba2: raw step sizes,
 dt_bias, A_log, the D skip and the silu(z) gate), its backward
 (ssd_bwd_mamba2) and its decode step, the backward pass (ssd_bwd) on the same
-shape, the state chain as one cooperative launch, and the fp64 CPU oracle
-timed on this host as a baseline.
+shape, optionally (--with-chain) the state chain as one cooperative launch,
+and the fp64 CPU oracle timed on this host as a baseline.
 
 Per-stage times come from each stage's own entry point (the four-launch form
 of the stage API); the step itself runs three launches, chunk_state computing
@@ -129,7 +129,8 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-mamba2", action="store_true", help="skip the Mamba-2 block-call timing")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass timing")
-    ap.add_argument("--no-chain", action="store_true", help="skip the cooperative state-chain timing")
+    ap.add_argument("--with-chain", action="store_true",
+                    help="also time the state chain as one cooperative launch (rocprofv3 cannot trace it)")
     ap.add_argument("--bwd-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=4096)
@@ -313,7 +314,7 @@ def main() -> int:
             del mdY, mws
         del mX, mdt, mbias, mAl, mD, mz, mB, mC
 
-    if not args.no_chain:
+    if args.with_chain:
         # The state chain as one cooperative launch (ssd_set_state_chain(1)),
         # against the default two launches: the same step, timed the same way.
         prev = ssd.set_state_chain(1)
