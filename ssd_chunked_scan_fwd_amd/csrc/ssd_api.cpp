@@ -631,7 +631,7 @@ static ssd_status m2_bwd_layout(const ssd_shape* s, int32_t chunk, int32_t gs, M
   if (st != SSD_OK) return st;
   st = ssd_fwd_workspace_bytes(s, chunk, gs, &fwd);
   if (st != SSD_OK) return st;
-  if (s->headdim % 4 || s->headdim > 256) return SSD_ERR_UNSUPPORTED;  // four channels per thread
+  if (s->headdim % 8) return SSD_ERR_UNSUPPORTED;  // eight channels per thread
   const size_t esz = s->dtype == SSD_DTYPE_BF16 ? 2 : 4;
   const size_t tok = (size_t)s->batch * s->seqlen, H = s->nheads, P = s->headdim;
   M2BwdLayout L{};

@@ -22,134 +22,194 @@ namespace ssd {
 
 namespace {
 
-constexpr int kM2Tokens = 64;  // tokens per workgroup of the prep and epilogue kernels
+constexpr int kM2Threads = 256;
+constexpr int kM2Tokens = 16;  // tokens per workgroup of the prep and epilogue kernels
+
+// Thread layout of the prep and epilogue kernels: each thread takes 8
+// consecutive channels of one (token, head); the P/8 threads of a (token,
+// head) are consecutive lanes, and a workgroup covers `hg` consecutive heads
+// of `tpr` tokens per round. The token rows [H][P] are contiguous in memory,
+// so every wave reads and writes one contiguous run of 16-byte pieces.
+struct M2Map {
+  int tpt, hg, tph, tpr;  // threads per (token, head), heads per workgroup, threads per token, tokens per round
+};
+
+__host__ __device__ inline M2Map m2_map(int H, int P) {
+  M2Map m;
+  m.tpt = P / 8;
+  m.hg = H < kM2Threads / m.tpt ? H : kM2Threads / m.tpt;
+  m.tph = m.hg * m.tpt;
+  m.tpr = kM2Threads / m.tph;
+  return m;
+}
 
 template <bool BF16>
 struct Elem {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
-  // Four consecutive values as fp32.
-  static __device__ __forceinline__ f32x4 load4(const T* p) {
+  // Eight consecutive values as fp32.
+  static __device__ __forceinline__ void load8(const T* p, f32x4 v[2]) {
     if constexpr (BF16) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-      return f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+      v[0] = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+      v[1] = f32x4{bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
     } else {
-      return *reinterpret_cast<const f32x4*>(p);
+      v[0] = reinterpret_cast<const f32x4*>(p)[0];
+      v[1] = reinterpret_cast<const f32x4*>(p)[1];
     }
   }
-  static __device__ __forceinline__ void store4(T* p, f32x4 v) {
+  static __device__ __forceinline__ void store8(T* p, f32x4 a, f32x4 b) {
     if constexpr (BF16) {
-      *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x4*>(p) =
+          u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
     } else {
-      *reinterpret_cast<f32x4*>(p) = v;
+      reinterpret_cast<f32x4*>(p)[0] = a;
+      reinterpret_cast<f32x4*>(p)[1] = b;
     }
   }
 };
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-v * kLog2e)); }
 
-// Workgroup (token block, head); P/4 threads per token, 4 channels each.
-// Writes log a and x~ = x dt'; with a gate also dv = dY silu(z) and
-// dz = dY v silu'(z) (v: the call's output before the gate).
+__device__ __forceinline__ float dot8(const f32x4 a[2], const f32x4 b[2]) {
+  return a[0][0] * b[0][0] + a[0][1] * b[0][1] + a[0][2] * b[0][2] + a[0][3] * b[0][3] + a[1][0] * b[1][0] +
+         a[1][1] * b[1][1] + a[1][2] * b[1][2] + a[1][3] * b[1][3];
+}
+
+// Workgroup (token block, head group). Writes log a and x~ = x dt'; with a
+// gate also dv = dY silu(z) and dz = dY v silu'(z) (v: the call's output
+// before the gate).
 template <bool BF16>
-__global__ __launch_bounds__(256) void m2_prep_kernel(const typename Elem<BF16>::T* __restrict__ X,
-                                                      const float* __restrict__ dt, const float* __restrict__ dt_bias,
-                                                      const float* __restrict__ A_log,
-                                                      const typename Elem<BF16>::T* __restrict__ z,
-                                                      const typename Elem<BF16>::T* __restrict__ dY,
-                                                      const typename Elem<BF16>::T* __restrict__ v,
-                                                      float* __restrict__ la, typename Elem<BF16>::T* __restrict__ xs,
-                                                      typename Elem<BF16>::T* __restrict__ dv,
-                                                      typename Elem<BF16>::T* __restrict__ dz, long tokens, int H,
-                                                      int P) {
+__global__ __launch_bounds__(kM2Threads) void m2_prep_kernel(const typename Elem<BF16>::T* __restrict__ X,
+                                                             const float* __restrict__ dt,
+                                                             const float* __restrict__ dt_bias,
+                                                             const float* __restrict__ A_log,
+                                                             const typename Elem<BF16>::T* __restrict__ z,
+                                                             const typename Elem<BF16>::T* __restrict__ dY,
+                                                             const typename Elem<BF16>::T* __restrict__ v,
+                                                             float* __restrict__ la,
+                                                             typename Elem<BF16>::T* __restrict__ xs,
+                                                             typename Elem<BF16>::T* __restrict__ dv,
+                                                             typename Elem<BF16>::T* __restrict__ dz, long tokens,
+                                                             int H, int P) {
   using E = Elem<BF16>;
-  const int h = blockIdx.y;
-  const int tpt = P / 4;                 // threads per token
-  const int per = 256 / tpt;             // tokens per pass
-  const int q = threadIdx.x % tpt, tl = threadIdx.x / tpt;
+  const M2Map mp = m2_map(H, P);
+  const int tid = threadIdx.x;
+  const int r = tid / mp.tph, q = tid % mp.tpt;
+  const int h = blockIdx.y * mp.hg + (tid % mp.tph) / mp.tpt;
+  if (r >= mp.tpr || h >= H) return;  // no barrier below
   const float A = -expf(A_log[h]);
   const float bias = dt_bias ? dt_bias[h] : 0.f;
-  for (int k = tl; k < kM2Tokens; k += per) {
-    const long t = (long)blockIdx.x * kM2Tokens + k;
+  const long t0 = (long)blockIdx.x * kM2Tokens;
+#pragma unroll 4
+  for (int k = r; k < kM2Tokens; k += mp.tpr) {
+    const long t = t0 + k;
     if (t >= tokens) break;
     const long th = t * H + h;
     const float dtp = softplus_f32(dt[th] + bias);
     if (q == 0) la[th] = dtp * A;
-    const long o = th * P + 4 * q;
-    const f32x4 x = E::load4(X + o);
-    E::store4(xs + o, x * dtp);
+    const long o = th * P + 8 * q;
+    f32x4 x[2];
+    E::load8(X + o, x);
+    E::store8(xs + o, x[0] * dtp, x[1] * dtp);
     if (z) {
-      const f32x4 g = E::load4(z + o), d = E::load4(dY + o), vv = E::load4(v + o);
-      f32x4 s, ds;
+      f32x4 g[2], d[2], vv[2], s[2], ds[2];
+      E::load8(z + o, g);
+      E::load8(dY + o, d);
+      E::load8(v + o, vv);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sg = sigmoid_f32(g[r]);
-        s[r] = g[r] * sg;
-        ds[r] = sg * (1.f + g[r] * (1.f - sg));
-      }
-      E::store4(dv + o, d * s);
-      E::store4(dz + o, d * vv * ds);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float sg = sigmoid_f32(g[i][c]);
+          s[i][c] = g[i][c] * sg;
+          ds[i][c] = sg * (1.f + g[i][c] * (1.f - sg));
+        }
+      E::store8(dv + o, d[0] * s[0], d[1] * s[1]);
+      E::store8(dz + o, d[0] * vv[0] * ds[0], d[1] * vv[1] * ds[1]);
     }
   }
 }
 
-// Workgroup (token block, head): dx = dx~ dt' + D dv and d dt per token, and
-// the block's sums of dv x, dt' d log a and d dt into part[block][h][3]. dv is
-// formed here again in fp32 from dY and z (the rounded copy is the
-// recurrence's cotangent only), so the skip term is not rounded twice.
+// Workgroup (token block, head group): dx = dx~ dt' + D dv and d dt per
+// token, and the block's sums of dv x, dt' d log a and d dt per head into
+// part[block][h][3]. dv is formed here again in fp32 from dY and z (the
+// rounded copy is the recurrence's cotangent only), so the skip term is not
+// rounded twice.
 template <bool BF16>
-__global__ __launch_bounds__(256) void m2_epilogue_kernel(
+__global__ __launch_bounds__(kM2Threads) void m2_epilogue_kernel(
     const typename Elem<BF16>::T* __restrict__ X, const float* __restrict__ dt, const float* __restrict__ dt_bias,
     const float* __restrict__ A_log, const float* __restrict__ D, const typename Elem<BF16>::T* __restrict__ dY,
     const typename Elem<BF16>::T* __restrict__ z, const typename Elem<BF16>::T* __restrict__ dxs,
     const float* __restrict__ dla, typename Elem<BF16>::T* __restrict__ dX, float* __restrict__ ddt,
     float* __restrict__ part, long tokens, int H, int P) {
   using E = Elem<BF16>;
-  const int h = blockIdx.y;
-  const int tpt = P / 4;
-  const int per = 256 / tpt;
-  const int q = threadIdx.x % tpt, tl = threadIdx.x / tpt;
-  const float A = -expf(A_log[h]);
-  const float bias = dt_bias ? dt_bias[h] : 0.f;
-  const float Dh = D ? D[h] : 0.f;
+  const M2Map mp = m2_map(H, P);
+  const int tid = threadIdx.x;
+  const int r = tid / mp.tph, hl = (tid % mp.tph) / mp.tpt, q = tid % mp.tpt;
+  const int h = blockIdx.y * mp.hg + hl;
+  const bool act = r < mp.tpr && h < H;  // whole (token, head) lane groups
   float sD = 0.f, sA = 0.f, sB = 0.f;
-  for (int k = tl; k < kM2Tokens; k += per) {
-    const long t = (long)blockIdx.x * kM2Tokens + k;
-    if (t >= tokens) break;
-    const long th = t * H + h;
-    const float raw = dt[th] + bias;
-    const float dtp = softplus_f32(raw);
-    const long o = th * P + 4 * q;
-    const f32x4 x = E::load4(X + o), g = E::load4(dxs + o);
-    f32x4 d = E::load4(dY + o);
-    if (z) {
-      const f32x4 zz = E::load4(z + o);
+  if (act) {
+    const float A = -expf(A_log[h]);
+    const float bias = dt_bias ? dt_bias[h] : 0.f;
+    const float Dh = D ? D[h] : 0.f;
+    const long t0 = (long)blockIdx.x * kM2Tokens;
+#pragma unroll 4
+    for (int k = r; k < kM2Tokens; k += mp.tpr) {
+      const long t = t0 + k;
+      if (t >= tokens) break;
+      const long th = t * H + h;
+      const float raw = dt[th] + bias;
+      const float dtp = softplus_f32(raw);
+      const long o = th * P + 8 * q;
+      f32x4 x[2], g[2], d[2];
+      E::load8(X + o, x);
+      E::load8(dxs + o, g);
+      E::load8(dY + o, d);
+      if (z) {
+        f32x4 zz[2];
+        E::load8(z + o, zz);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) d[r] *= zz[r] * sigmoid_f32(zz[r]);
-    }
-    E::store4(dX + o, g * dtp + d * Dh);
-    float r = g[0] * x[0] + g[1] * x[1] + g[2] * x[2] + g[3] * x[3];
-    sD += d[0] * x[0] + d[1] * x[1] + d[2] * x[2] + d[3] * x[3];
-    for (int off = 1; off < tpt; off <<= 1) r += __shfl_xor(r, off);  // the token's P/4 lanes
-    if (q == 0) {
-      const float l = dla[th];
-      const float g_dt = (r + A * l) * sigmoid_f32(raw);
-      ddt[th] = g_dt;
-      sA += dtp * l;
-      sB += g_dt;
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) d[i][c] *= zz[i][c] * sigmoid_f32(zz[i][c]);
+      }
+      E::store8(dX + o, g[0] * dtp + d[0] * Dh, g[1] * dtp + d[1] * Dh);
+      float rr = dot8(g, x);
+      sD += dot8(d, x);
+      for (int off = 1; off < mp.tpt; off <<= 1) rr += __shfl_xor(rr, off);  // the (token, head)'s lanes
+      if (q == 0) {
+        const float l = dla[th];
+        const float g_dt = (rr + A * l) * sigmoid_f32(raw);
+        ddt[th] = g_dt;
+        sA += dtp * l;
+        sB += g_dt;
+      }
     }
   }
-  __shared__ float red[3][256];
-  red[0][threadIdx.x] = sD;
-  red[1][threadIdx.x] = sA;
-  red[2][threadIdx.x] = sB;
+  for (int off = 1; off < mp.tpt; off <<= 1) sD += __shfl_xor(sD, off);
+  // Per head: the token rows' sums through LDS, in a fixed order.
+  __shared__ float red[kM2Threads / 2][3];
+  if (act && q == 0) {
+    const int e = r * mp.hg + hl;
+    red[e][0] = sD;
+    red[e][1] = sA;
+    red[e][2] = sB;
+  }
   __syncthreads();
-  for (int n = 128; n > 0; n >>= 1) {
-    if ((int)threadIdx.x < n)
-#pragma unroll
-      for (int j = 0; j < 3; ++j) red[j][threadIdx.x] += red[j][threadIdx.x + n];
-    __syncthreads();
+  const int hh = blockIdx.y * mp.hg + tid;
+  if (tid < mp.hg && hh < H) {
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+    for (int rr = 0; rr < mp.tpr; ++rr) {
+      s0 += red[rr * mp.hg + tid][0];
+      s1 += red[rr * mp.hg + tid][1];
+      s2 += red[rr * mp.hg + tid][2];
+    }
+    float* out = part + ((long)blockIdx.x * H + hh) * 3;
+    out[0] = s0;
+    out[1] = s1;
+    out[2] = s2;
   }
-  if (threadIdx.x < 3) part[((long)blockIdx.x * H + h) * 3 + threadIdx.x] = red[threadIdx.x][0];
 }
 
 // One workgroup per head: dD, dA_log = A sum dt' d log a, d dt_bias from the
@@ -183,16 +243,21 @@ __global__ __launch_bounds__(256) void m2_reduce_kernel(const float* __restrict_
 
 long m2_token_blocks(long tokens) { return (tokens + kM2Tokens - 1) / kM2Tokens; }
 
+static dim3 m2_grid(const M2BwdArgs& a) {
+  const M2Map mp = m2_map(a.H, a.P);
+  return dim3((unsigned)m2_token_blocks(a.tokens), (unsigned)((a.H + mp.hg - 1) / mp.hg));
+}
+
 hipError_t launch_m2_prep(const M2BwdArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)m2_token_blocks(a.tokens), (unsigned)a.H);
+  const dim3 grid = m2_grid(a);
   if (a.bf16) {
     using T = uint16_t;
-    hipLaunchKernelGGL(m2_prep_kernel<true>, grid, dim3(256), 0, stream, static_cast<const T*>(a.X), a.dt, a.dt_bias,
+    hipLaunchKernelGGL(m2_prep_kernel<true>, grid, dim3(kM2Threads), 0, stream, static_cast<const T*>(a.X), a.dt, a.dt_bias,
                        a.A_log, static_cast<const T*>(a.z), static_cast<const T*>(a.dY), static_cast<const T*>(a.v),
                        a.la, static_cast<T*>(a.xs), static_cast<T*>(a.dv), static_cast<T*>(a.dz), a.tokens, a.H, a.P);
   } else {
     using T = float;
-    hipLaunchKernelGGL(m2_prep_kernel<false>, grid, dim3(256), 0, stream, static_cast<const T*>(a.X), a.dt,
+    hipLaunchKernelGGL(m2_prep_kernel<false>, grid, dim3(kM2Threads), 0, stream, static_cast<const T*>(a.X), a.dt,
                        a.dt_bias, a.A_log, static_cast<const T*>(a.z), static_cast<const T*>(a.dY),
                        static_cast<const T*>(a.v), a.la, static_cast<T*>(a.xs), static_cast<T*>(a.dv),
                        static_cast<T*>(a.dz), a.tokens, a.H, a.P);
@@ -202,16 +267,16 @@ hipError_t launch_m2_prep(const M2BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_m2_epilogue(const M2BwdArgs& a, hipStream_t stream) {
   const long nblk = m2_token_blocks(a.tokens);
-  const dim3 grid((unsigned)nblk, (unsigned)a.H);
+  const dim3 grid = m2_grid(a);
   if (a.bf16) {
     using T = uint16_t;
-    hipLaunchKernelGGL(m2_epilogue_kernel<true>, grid, dim3(256), 0, stream, static_cast<const T*>(a.X), a.dt,
+    hipLaunchKernelGGL(m2_epilogue_kernel<true>, grid, dim3(kM2Threads), 0, stream, static_cast<const T*>(a.X), a.dt,
                        a.dt_bias, a.A_log, a.D, static_cast<const T*>(a.dY), static_cast<const T*>(a.z),
                        static_cast<const T*>(a.dxs), a.dla, static_cast<T*>(a.dXo), a.ddt, a.part, a.tokens, a.H,
                        a.P);
   } else {
     using T = float;
-    hipLaunchKernelGGL(m2_epilogue_kernel<false>, grid, dim3(256), 0, stream, static_cast<const T*>(a.X), a.dt,
+    hipLaunchKernelGGL(m2_epilogue_kernel<false>, grid, dim3(kM2Threads), 0, stream, static_cast<const T*>(a.X), a.dt,
                        a.dt_bias, a.A_log, a.D, static_cast<const T*>(a.dY), static_cast<const T*>(a.z),
                        static_cast<const T*>(a.dxs), a.dla, static_cast<T*>(a.dXo), a.ddt, a.part, a.tokens, a.H,
                        a.P);
