@@ -6,11 +6,35 @@ thin ctypes layer over it. Importing the package does not load the library:
 the first call does, and it raises if the library is missing.
 """
 from . import synth  # noqa: F401
-from .binding import (SSDError, Shape, Workspace, bwd, bwd_mamba2, bwd_mamba2_workspace_bytes,  # noqa: F401
-                      bwd_workspace_bytes, chunk_cumsum, chunk_scan, chunk_state, default_state_block, fwd, fwd_mamba2, layout, lib, make_shape,
-                      set_state_chain, state_passing, step, step_mamba2, workspace_bytes)
+from .binding import (  # noqa: F401
+    SSDError,
+    Shape,
+    Workspace,
+    bwd,
+    bwd_mamba2,
+    bwd_mamba2_workspace_bytes,
+    bwd_workspace_bytes,
+    chunk_cumsum,
+    chunk_scan,
+    chunk_state,
+    default_state_block,
+    fwd,
+    fwd_mamba2,
+    layout,
+    lib,
+    make_shape,
+    set_state_chain,
+    state_passing,
+    step,
+    step_mamba2,
+    workspace_bytes,
+)
 
-__all__ = ["synth", "fwd", "step", "fwd_mamba2", "step_mamba2", "bwd", "bwd_workspace_bytes", "bwd_mamba2",
-           "bwd_mamba2_workspace_bytes", "chunk_cumsum",
-           "chunk_state", "state_passing", "chunk_scan", "set_state_chain", "Workspace", "Shape", "SSDError",
-           "layout", "workspace_bytes", "make_shape", "lib", "default_state_block"]
+__all__ = [
+    "synth",
+    "fwd", "step", "fwd_mamba2", "step_mamba2",
+    "bwd", "bwd_workspace_bytes", "bwd_mamba2", "bwd_mamba2_workspace_bytes",
+    "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan",
+    "set_state_chain", "Workspace", "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib",
+    "default_state_block",
+]
