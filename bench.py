@@ -12,14 +12,17 @@ HIP events on the launch stream), per-stage times, the decode-step throughput,
 the Mamba-2 block's call on the same shape (ssd_fwd_mamba2: raw step sizes,
 dt_bias, A_log, the D skip and the silu(z) gate), its backward
 (ssd_bwd_mamba2) and its decode step, the backward pass (ssd_bwd) on the same
-shape, optionally (--with-chain) the state chain as one cooperative launch,
-and the fp64 CPU oracle timed on this host as a baseline.
+shape, the forward pass on the other timed workloads (the state-size sweep
+b 8, T 4096, N 64/128/256 with its slowdown against N = 64, and the packed
+variable-length H = 80 layer), optionally (--with-chain) the state chain as one
+cooperative launch, and the fp64 CPU oracle timed on this host as a baseline.
 
 Per-stage times come from each stage's own entry point (the four-launch form
 of the stage API); the step itself runs three launches, chunk_state computing
 the segment sums itself.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-mamba2] [--no-bwd]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-decode] [--no-mamba2]
+                    [--no-bwd] [--no-workloads]
 """
 from __future__ import annotations
 
@@ -132,6 +135,9 @@ def main() -> int:
     ap.add_argument("--with-chain", action="store_true",
                     help="also time the state chain as one cooperative launch (rocprofv3 cannot trace it)")
     ap.add_argument("--bwd-steps", type=int, default=100)
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the forward timing of the state-size sweep and the packed H=80 layer")
+    ap.add_argument("--wl-steps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--state-block", type=int, default=0, help="chunks per state block (0: library default)")
@@ -405,6 +411,43 @@ def main() -> int:
             out["decode"]["mamba2_us_per_step"] = round(m_ms * 1e3 / nsteps, 3)
             del xs, dts, zs, Bs, Cs
         del state
+
+    if not args.no_workloads:
+        # The forward pass on the state-size sweep (slowdown against N = 64) and
+        # on the packed variable-length layer shape: wall time per ssd_fwd call.
+        res = {}
+        for name in ("sweep-b8-T4096-N64", "sweep-b8-T4096-N128", "sweep-b8-T4096-N256", "packed-T32768-H80-N128"):
+            wl = synth.WORKLOADS[name]
+            log(f"[bench] forward on {name}: {args.wl_steps} steps")
+            dl = synth.workload_inputs(wl)
+            lX, lla, lB, lC = (dl[k].to(dev) for k in ("X", "log_a", "B", "C"))
+            lcu = dl["cu_seqlens"].to(dev) if dl.get("cu_seqlens") is not None else None
+            lsh = ssd.make_shape(lX, lB, lcu)
+            lws = ssd.Workspace(lsh, wl.Q, dev)
+            lY = torch.empty_like(lX)
+            nseq_l = wl.batch if lcu is None else lcu.numel() - 1
+            lfin = torch.empty(nseq_l, wl.H, wl.P, wl.N, dtype=torch.float32, device=dev)
+
+            def lstep():
+                ssd.fwd(lX, lla, lB, lC, cu_seqlens=lcu, chunk=wl.Q, state_block=lws.state_block, Y=lY,
+                        final_state=lfin, workspace=lws)
+
+            for _ in range(10):
+                lstep()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.wl_steps):
+                lstep()
+            torch.cuda.synchronize()
+            l_ms = (time.perf_counter() - t0) * 1e3 / max(args.wl_steps, 1)
+            ltok = wl.batch * wl.T
+            res[name] = {"ms_per_step": round(l_ms, 5), "tokens_per_s": round(ltok / (l_ms * 1e-3), 1),
+                         "state_block": lws.state_block}
+            del lX, lla, lB, lC, lcu, lws, lY, lfin
+        base = res["sweep-b8-T4096-N64"]["ms_per_step"]
+        for name in ("sweep-b8-T4096-N64", "sweep-b8-T4096-N128", "sweep-b8-T4096-N256"):
+            res[name]["slowdown_vs_N64"] = round(res[name]["ms_per_step"] / base, 3)
+        out["workloads"] = res
 
     if args.copy_probe > 0:
         n = args.copy_probe * (1 << 20) // 4
