@@ -58,6 +58,48 @@ def _dfinal(d, nseq, seed, T1=120):
     return torch.from_numpy(g["dinit"]).float()
 
 
+def compare(g, r, X, dt, dtb, A_log, D, z, B, C, dY, cu, what, keys=None):
+    """The GPU gradients `g` against the oracle's `r` on the same inputs."""
+    dt_name = dtype_name(X)
+    errs = {}
+    for k in keys or ("dX", "ddt", "dA_log", "dB", "dC", "dinit", "dD", "dz", "ddt_bias"):
+        if r.get(k) is None:
+            assert g[k] is None, k
+            continue
+        if k == "dz":
+            # dz = s v with s = dY silu'(z) per element and v the output before the
+            # gate: v's unit scale is carried through the product, as for the gated
+            # forward output.
+            v, _ = oracle.mamba2_forward(_f(X), _f(dt), _f(dtb), _f(A_log), _f(D), None, _f(B), _f(C),
+                                         cu_seqlens=None if cu is None else cu.numpy())
+            zz = _f(z)
+            sg = 0.5 * (1.0 + np.tanh(0.5 * zz))
+            scale = _f(dY) * sg * (1.0 + zz * (1.0 - sg))
+            errs[k] = assert_close_gated(_f(g[k]), r[k], v, scale, dt_name, f"{what} {k}")
+            errs[k]["max_unit"] = errs[k]["max_gated"]
+            continue
+        if k == "dX":
+            # dX = dt' dx~ + D dv: the per-token step size dt' spans two orders of
+            # magnitude, so dx~'s unit scale is carried through it (the skip term
+            # is formed in fp32 from the inputs and rounded once).
+            dtp, _ = oracle.mamba2_discretize(_f(dt), _f(dtb), _f(A_log))
+            errs[k] = assert_close_gated(_f(g[k]), r[k], r["dxs"], np.broadcast_to(dtp[..., None], r[k].shape),
+                                         dt_name, f"{what} {k}")
+            errs[k]["max_unit"] = errs[k]["max_gated"]
+            continue
+        if k in ("dB", "dC"):
+            # Sums over heads of terms carrying x dt' (dt' per token) and dY silu(z)
+            # (per element): heavy-tailed, so the bar takes an allowance relative
+            # to |ref_i| as well (the gated functional with s = 1).
+            errs[k] = assert_close_gated(_f(g[k]), r[k], r[k], np.ones_like(r[k]), dt_name, f"{what} {k}")
+            errs[k]["max_unit"] = errs[k]["max_gated"]
+            continue
+        errs[k] = assert_close(_f(g[k]), r[k], dt_name, f"{what} {k}")
+    say(f"[bwd-m2] {what}: " + " ".join(f"{k} rel_l2={e['rel_l2']:.2e} max_unit={e['max_unit']:.3f}"
+                                        for k, e in errs.items()))
+    return errs
+
+
 def check(d, Q, what, gate=True, skip=True, bias=True, with_final=True, gs=0, seed=0):
     X = d["X"]
     b, T, H, P = X.shape
@@ -78,43 +120,7 @@ def check(d, Q, what, gate=True, skip=True, bias=True, with_final=True, gs=0, se
     torch.cuda.synchronize()
     r = oracle.mamba2_backward(_f(X), _f(d["dt"]), _f(dtb), _f(d["A_log"]), _f(D), _f(z), _f(d["B"]), _f(d["C"]),
                                _f(ct["dY"]), dfinal=_f(dfin), cu_seqlens=None if cu is None else cu.numpy())
-    dt_name = dtype_name(X)
-    errs = {}
-    for k in ("dX", "ddt", "dA_log", "dB", "dC", "dinit", "dD", "dz", "ddt_bias"):
-        if r.get(k) is None:
-            assert g[k] is None, k
-            continue
-        if k == "dz":
-            # dz = s v with s = dY silu'(z) per element and v the output before the
-            # gate: v's unit scale is carried through the product, as for the gated
-            # forward output.
-            v, _ = oracle.mamba2_forward(_f(X), _f(d["dt"]), _f(dtb), _f(d["A_log"]), _f(D), None, _f(d["B"]),
-                                         _f(d["C"]), cu_seqlens=None if cu is None else cu.numpy())
-            zz = _f(z)
-            sg = 0.5 * (1.0 + np.tanh(0.5 * zz))
-            scale = _f(ct["dY"]) * sg * (1.0 + zz * (1.0 - sg))
-            errs[k] = assert_close_gated(_f(g[k]), r[k], v, scale, dt_name, f"{what} {k}")
-            errs[k]["max_unit"] = errs[k]["max_gated"]
-            continue
-        if k == "dX":
-            # dX = dt' dx~ + D dv: the per-token step size dt' spans two orders of
-            # magnitude, so dx~'s unit scale is carried through it (the skip term
-            # is formed in fp32 from the inputs and rounded once).
-            dtp, _ = oracle.mamba2_discretize(_f(d["dt"]), _f(dtb), _f(d["A_log"]))
-            errs[k] = assert_close_gated(_f(g[k]), r[k], r["dxs"], np.broadcast_to(dtp[..., None], r[k].shape),
-                                         dt_name, f"{what} {k}")
-            errs[k]["max_unit"] = errs[k]["max_gated"]
-            continue
-        if k in ("dB", "dC"):
-            # Sums over heads of terms carrying x dt' (dt' per token) and dY silu(z)
-            # (per element): heavy-tailed, so the bar takes an allowance relative
-            # to |ref_i| as well (the gated functional with s = 1).
-            errs[k] = assert_close_gated(_f(g[k]), r[k], r[k], np.ones_like(r[k]), dt_name, f"{what} {k}")
-            errs[k]["max_unit"] = errs[k]["max_gated"]
-            continue
-        errs[k] = assert_close(_f(g[k]), r[k], dt_name, f"{what} {k}")
-    say(f"[bwd-m2] {what}: " + " ".join(f"{k} rel_l2={e['rel_l2']:.2e} max_unit={e['max_unit']:.3f}"
-                                        for k, e in errs.items()))
+    compare(g, r, X, d["dt"], dtb, d["A_log"], D, z, d["B"], d["C"], ct["dY"], cu, what)
     return g
 
 
@@ -148,3 +154,51 @@ def test_bwd_mamba2_long_sequence():
     """T = 4096 at the headline head and state sizes (8 heads, state blocks of 8 chunks)."""
     d = synth.make_mamba2_inputs(1, 4096, 8, 64, 128, 1, torch.bfloat16, seed=5300)
     check(d, 128, "long sequence", seed=24)
+
+
+def test_bwd_mamba2_headline_sampled_heads():
+    """The Mamba-2 call's backward at the headline size (T = 16384, H = 32, P = 64, N = 128, Q = 128,
+    default state block, as bench.py times it), with gate, skip and bias. The per-head gradients
+    (dX, d dt, dz, dD, d dt_bias, d A_log) of two sampled heads depend on those heads alone, so the
+    oracle runs on them only; dB and dC sum over heads, so a second GPU call with dY zero outside the
+    sampled heads gives their share, which the oracle's dB and dC on the two heads must match."""
+    w = synth.WORKLOADS[synth.HEADLINE]
+    d = synth.make_mamba2_inputs(w.batch, w.T, w.H, w.P, w.N, w.G, w.torch_dtype, seed=w.seed)
+    X, B, C = d["X"], d["B"], d["C"]
+    b, T, H, P = X.shape
+    N = B.shape[-1]
+    heads = [0, 17]
+    ct = synth.make_cotangents(b, T, H, P, N, b, dtype=X.dtype, seed=14)
+    say(f"[bwd-m2] headline sampled heads {heads}: X{tuple(X.shape)} Q={w.Q}")
+    dev = lambda t: t.cuda()
+    args = dict(dt_bias=dev(d["dt_bias"]), D=dev(d["D"]), z=dev(d["z"]), chunk=w.Q)
+    Xg, dtg, Alg, Bg, Cg = dev(X), dev(d["dt"]), dev(d["A_log"]), dev(B), dev(C)
+    g = ssd.bwd_mamba2(Xg, dtg, Alg, Bg, Cg, dev(ct["dY"]), **args)
+    mask = torch.zeros(H, dtype=torch.bool)
+    mask[heads] = True
+    dY_s = ct["dY"].clone()
+    dY_s[:, :, ~mask] = 0
+    g_s = ssd.bwd_mamba2(Xg, dtg, Alg, Bg, Cg, dev(dY_s), **args)
+    torch.cuda.synchronize()
+    hs = lambda t: t[:, :, heads]
+    sel = dict(X=hs(X), dt=hs(d["dt"]), dtb=d["dt_bias"][heads], A_log=d["A_log"][heads], D=d["D"][heads],
+               z=hs(d["z"]), B=B, C=C, dY=hs(ct["dY"]), cu=None)
+    r = oracle.mamba2_backward(_f(sel["X"]), _f(sel["dt"]), _f(sel["dtb"]), _f(sel["A_log"]), _f(sel["D"]),
+                               _f(sel["z"]), _f(B), _f(C), _f(sel["dY"]))
+    gh = {"dX": hs(g["dX"]), "ddt": g["ddt"][:, :, heads], "dz": hs(g["dz"]), "dD": g["dD"][heads],
+          "ddt_bias": g["ddt_bias"][heads], "dA_log": g["dA_log"][heads], "dB": g_s["dB"], "dC": g_s["dC"]}
+    compare(gh, r, what="headline sampled heads", keys=("dX", "ddt", "dz", "dD", "ddt_bias", "dB", "dC"), **sel)
+    # d A_log = A sum_t dt'_t d log a_t sums 16384 terms that cancel to 1/217 and 1/3251 of their
+    # absolute sum on these two heads, so a bar relative to the result is not meaningful here (the
+    # smaller cases above hold it to the plain bar). Each term meeting the bf16 bar bounds the sum's
+    # error by 2e-2 of the terms' absolute sum, which the oracle gives with d log a from the
+    # recurrence's reverse mode on x dt', log a = dt' A and dv = dY silu(z).
+    dtp, la_ = oracle.mamba2_discretize(_f(sel["dt"]), _f(sel["dtb"]), _f(sel["A_log"]))
+    zz = _f(sel["z"])
+    dv = _f(sel["dY"]) * zz / (1.0 + np.exp(-zz))
+    dla = oracle.backward(_f(sel["X"]) * dtp[..., None], la_, _f(B), _f(C), dv)["dlog_a"]
+    A = -np.exp(_f(sel["A_log"]))
+    bound = 2e-2 * np.abs(A) * np.abs(dtp * dla).sum(axis=(0, 1))
+    err = np.abs(_f(gh["dA_log"]) - r["dA_log"])
+    say(f"[bwd-m2] headline sampled heads dA_log: error {err} against the summation bound {bound}")
+    assert np.all(np.isfinite(_f(gh["dA_log"]))) and np.all(err <= bound), (err, bound)
