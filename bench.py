@@ -393,6 +393,31 @@ def main() -> int:
                          "tokens_per_s": round(wd.batch * nsteps / (dec_ms * 1e-3), 1),
                          "us_per_step": round(dec_ms * 1e3 / nsteps, 3),
                          "gbs_per_step": round(per_step_bytes / (dec_ms * 1e-3 / nsteps) / 1e9, 1)}
+        # The same steps from a HIP graph: 64 consecutive steps captured once and
+        # replayed back to back (the inputs of steps 0..63 on every replay).
+        glen = min(64, nsteps)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for t in range(glen):
+                ssd.step(state, xs[t], las[t], Bs[t], Cs[t], y=y)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, capture_error_mode="relaxed"):
+            for t in range(glen):
+                ssd.step(state, xs[t], las[t], Bs[t], Cs[t], y=y)
+        reps = max(1, nsteps // glen)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out["decode"]["graph_us_per_step"] = round(a.elapsed_time(b) * 1e3 / (reps * glen), 3)
+        del graph
         del xs, las, Bs, Cs
         if not args.no_mamba2:
             md = synth.make_mamba2_decode_inputs(wd.batch, nsteps, wd.H, wd.P, wd.N, wd.G, wd.torch_dtype, wd.seed)
