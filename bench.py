@@ -9,9 +9,10 @@ accumulation; inputs are seeded synthetic and resident in HBM before timing.
 Prints ONE JSON line with the headline throughput (tokens/s), the roofline of
 the dominant kernel (its algorithmic bytes / its average launch time, timed with
 HIP events on the launch stream), per-stage times, the decode-step throughput,
-the Mamba-2 block's call on the same shape (ssd_fwd_mamba2: raw step sizes,
-dt_bias, A_log, the D skip and the silu(z) gate), its backward
-(ssd_bwd_mamba2) and its decode step, the backward pass (ssd_bwd) on the same
+the decode steps replayed from a HIP graph, the Mamba-2 block's call on the
+same shape (ssd_fwd_mamba2: raw step sizes, dt_bias, A_log, the D skip and the
+silu(z) gate), its backward (ssd_bwd_mamba2) and its decode step, the backward
+pass (ssd_bwd) on the same
 shape, the forward pass on the other timed workloads (the state-size sweep
 b 8, T 4096, N 64/128/256 with its slowdown against N = 64, and the packed
 variable-length H = 80 layer), optionally (--with-chain) the state chain as one

@@ -34,10 +34,13 @@
  *
  * Ownership and streams: every pointer is a caller-owned buffer; device
  * pointers for all tensors, host pointers for `shape` and `layout`. The
- * library allocates nothing, keeps no mutable global state, never
- * synchronises, and enqueues its kernels on `stream` (a hipStream_t; NULL is the
- * null stream). A call returns after enqueueing; errors of the kernels
- * themselves surface on the stream like any HIP error.
+ * library allocates nothing, never synchronises, issues no memset, and
+ * enqueues its kernels on `stream` (a hipStream_t; NULL is the null stream).
+ * Its only global state is the process-wide mode of ssd_set_state_chain. A
+ * call returns after enqueueing; errors of the kernels themselves surface on
+ * the stream like any HIP error. A call may be captured into a HIP graph: its
+ * replays compute what the call computes, from the buffers' contents at
+ * replay time.
  *
  * Errors: arguments are checked on the host before any HIP call. On
  * SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED or SSD_ERR_WORKSPACE_TOO_SMALL
