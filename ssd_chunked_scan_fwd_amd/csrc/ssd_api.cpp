@@ -415,10 +415,14 @@ ssd_status ssd_bwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_
   return SSD_OK;
 }
 
-ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
-                   const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
-                   int32_t state_block, void* dX, float* dlog_a, void* dB, void* dC, float* dinitial_state,
-                   const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+// The backward pass. fwd_run_done: the forward state run's block tables,
+// segment sums and block-entering states are already in the workspace (the
+// fused path skips that run); see ssd_bwd_mamba2.
+static ssd_status bwd_run(const void* X, const float* log_a, const void* B, const void* C,
+                          const int32_t* cu_seqlens, const float* initial_state, const void* dY,
+                          const float* dfinal_state, int32_t chunk, int32_t state_block, void* dX, float* dlog_a,
+                          void* dB, void* dC, float* dinitial_state, const ssd_shape* shape, void* workspace,
+                          size_t workspace_bytes, void* stream, bool fwd_run_done) {
   if (!X || !log_a || !B || !C || !dY || !dX || !dlog_a || !dB || !dC || !shape) return SSD_ERR_INVALID_ARGUMENT;
   if (((uintptr_t)initial_state | (uintptr_t)dfinal_state | (uintptr_t)dinitial_state) & 15)
     return SSD_ERR_INVALID_ARGUMENT;
@@ -469,7 +473,7 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
     }
     if (e == hipSuccess && L.gs > 1) e = ssd::launch_chunk_starts(pa.d, rev_dy, rev_c, pa.ws, rstart, hs);
     // Forward chunk start states and segment sums.
-    if (e == hipSuccess) {
+    if (e == hipSuccess && !fwd_run_done) {
       const ssd::SegArgs sa = ssd::seg_args(pf.d, log_a, cu_seqlens, ssd::Mamba2Args{});
       e = run_state_chain(pf, X, B, sa, cu_seqlens, initial_state, nullptr, hs);
     }
@@ -618,6 +622,14 @@ ssd_status ssd_step_mamba2(float* state, const void* x, const float* dt, const f
 
 int32_t ssd_set_state_chain(int32_t mode) { return g_state_chain.exchange(mode ? 1 : 0); }
 
+ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
+                   const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
+                   int32_t state_block, void* dX, float* dlog_a, void* dB, void* dC, float* dinitial_state,
+                   const ssd_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_run(X, log_a, B, C, cu_seqlens, initial_state, dY, dfinal_state, chunk, state_block, dX, dlog_a, dB, dC,
+                 dinitial_state, shape, workspace, workspace_bytes, stream, false);
+}
+
 // Workspace of ssd_bwd_mamba2: one region that the ungated forward run (for v)
 // and then ssd_bwd use in turn, then v, log a, x dt', dv, the recurrence's
 // gradients of x dt' and log a, and the per-(token block, head) partial sums.
@@ -703,17 +715,31 @@ ssd_status ssd_bwd_mamba2(const void* X, const float* dt, const float* dt_bias, 
   a.H = shape->nheads;
   a.P = shape->headdim;
   a.bf16 = shape->dtype == SSD_DTYPE_BF16 ? 1 : 0;
-  // v = SSM(x dt') + D x: the call itself without the gate, for dz.
+  // v = SSM(x dt') + D x: the call itself without the gate, for dz. On the
+  // fused backward path it runs in the backward's forward-run workspace, with
+  // the backward's state block: its block tables, segment sums (of dt' A, the
+  // backward's log a) and block-entering states are those of the backward's
+  // forward state run, which is then skipped.
+  bool fwd_run_done = false;
   if (z) {
-    st = ssd_fwd_mamba2(X, dt, dt_bias, A_log, D, nullptr, B, C, cu_seqlens, initial_state, chunk, state_block,
-                        w + L.v, nullptr, shape, w + L.region, region_bytes, stream);
+    BwdLayout Lb;
+    st = make_bwd_layout(shape, cu_seqlens, chunk, state_block, &Lb);
+    if (st != SSD_OK) return st;
+    if (Lb.fused) {
+      st = ssd_fwd_mamba2(X, dt, dt_bias, A_log, D, nullptr, B, C, cu_seqlens, initial_state, chunk, Lb.gs, w + L.v,
+                          nullptr, shape, w + L.region + Lb.fwd_f, Lb.f_bytes, stream);
+      fwd_run_done = true;
+    } else {
+      st = ssd_fwd_mamba2(X, dt, dt_bias, A_log, D, nullptr, B, C, cu_seqlens, initial_state, chunk, state_block,
+                          w + L.v, nullptr, shape, w + L.region, region_bytes, stream);
+    }
     if (st != SSD_OK) return st;
   }
   hipError_t e = ssd::launch_m2_prep(a, hs);
   if (e != hipSuccess) return hip_status(e);
-  st = ssd_bwd(w + L.xs, a.la, B, C, cu_seqlens, initial_state, a.dv_in, dfinal_state, chunk, state_block,
+  st = bwd_run(w + L.xs, a.la, B, C, cu_seqlens, initial_state, a.dv_in, dfinal_state, chunk, state_block,
                w + L.dxs, reinterpret_cast<float*>(w + L.dla), dB, dC, dinitial_state, shape, w + L.region,
-               region_bytes, stream);
+               region_bytes, stream, fwd_run_done);
   if (st != SSD_OK) return st;
   return hip_status(ssd::launch_m2_epilogue(a, hs));
 }
