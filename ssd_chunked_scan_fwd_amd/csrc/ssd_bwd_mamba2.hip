@@ -70,6 +70,21 @@ struct Elem {
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-v * kLog2e)); }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of n consecutive lanes, n in {2, 4, 8, 16}; every
+// lane of a group receives the group's sum (DPP within rows of 16 lanes).
+__device__ __forceinline__ float group_sum(float v, int n) {
+  v = dpp_add<0xB1>(v);                // quad_perm [1, 0, 3, 2]
+  if (n > 2) v = dpp_add<0x4E>(v);     // quad_perm [2, 3, 0, 1]
+  if (n > 4) v = dpp_add<0x141>(v);    // row_half_mirror
+  if (n > 8) v = dpp_add<0x140>(v);    // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float dot8(const f32x4 a[2], const f32x4 b[2]) {
   return a[0][0] * b[0][0] + a[0][1] * b[0][1] + a[0][2] * b[0][2] + a[0][3] * b[0][3] + a[1][0] * b[1][0] +
          a[1][1] * b[1][1] + a[1][2] * b[1][2] + a[1][3] * b[1][3];
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(kM2Threads) void m2_epilogue_kernel(
       E::store8(dX + o, g[0] * dtp + d[0] * Dh, g[1] * dtp + d[1] * Dh);
       float rr = dot8(g, x);
       sD += dot8(d, x);
-      for (int off = 1; off < mp.tpt; off <<= 1) rr += __shfl_xor(rr, off);  // the (token, head)'s lanes
+      rr = group_sum(rr, mp.tpt);  // over the (token, head)'s lanes
       if (q == 0) {
         const float l = dla[th];
         const float g_dt = (rr + A * l) * sigmoid_f32(raw);
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(kM2Threads) void m2_epilogue_kernel(
       }
     }
   }
-  for (int off = 1; off < mp.tpt; off <<= 1) sD += __shfl_xor(sD, off);
+  sD = group_sum(sD, mp.tpt);
   // Per head: the token rows' sums through LDS, in a fixed order.
   __shared__ float red[kM2Threads / 2][3];
   if (act && q == 0) {
