@@ -117,12 +117,15 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
                                                           const int32_t* __restrict__ cu,
                                                           const int32_t* __restrict__ cur, int S, int T, int Tr,
                                                           int Hin, int Hout, int row_bytes, int mode,
-                                                          int xblocks) {
-  const long tok = blockIdx.x / xblocks;  // flattened output token
-  const int xb = (int)(blockIdx.x % xblocks);
+                                                          int xblocks, int tpw, long ntok) {
+  // A token's row is Hout * pieces 16-byte pieces: xblocks workgroups per
+  // token for long rows, tpw tokens per workgroup for short ones.
   const int pieces = row_bytes / 16;  // per head
-  const int idx = xb * 256 + threadIdx.x;
-  if (idx >= Hout * pieces) return;
+  const int per_tok = Hout * pieces;
+  const long tok = (blockIdx.x / xblocks) * (long)tpw + (tpw > 1 ? threadIdx.x / per_tok : 0);  // output token
+  const int xb = (int)(blockIdx.x % xblocks);
+  const int idx = tpw > 1 ? (int)(threadIdx.x % per_tok) : xb * 256 + (int)threadIdx.x;
+  if (idx >= per_tok || tok >= ntok || (tpw > 1 && (int)threadIdx.x >= tpw * per_tok)) return;
   const int ho = idx / pieces, q = idx % pieces;
   const int hi = ho / (Hout / Hin);
   long src = tok;  // mode 0: same layout
@@ -373,10 +376,12 @@ hipError_t launch_gather_rows(const void* in, void* out, const int32_t* cu, cons
                               int Tr, int Hin, int Hout, int row_bytes, int mode, hipStream_t stream) {
   const int pieces = Hout * (row_bytes / 16);
   const int xblocks = (pieces + 255) / 256;
+  const int tpw = pieces < 256 ? 256 / pieces : 1;  // tokens per workgroup
   const long ntok = (long)rows * (mode == 1 ? Tr : T);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)(ntok * xblocks)), dim3(256), 0, stream,
+  const long groups = (ntok + tpw - 1) / tpw;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)(groups * xblocks)), dim3(256), 0, stream,
                      reinterpret_cast<const uint8_t*>(in), reinterpret_cast<uint8_t*>(out), cu, cur, S, T, Tr, Hin,
-                     Hout, row_bytes, mode, xblocks);
+                     Hout, row_bytes, mode, xblocks, tpw, ntok);
   return hipGetLastError();
 }
 
