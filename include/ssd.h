@@ -207,8 +207,9 @@ ssd_status ssd_fwd_ex(const void* X, const float* log_a, const void* B, const vo
  * ssd_chunk_cumsum -- segment sums of log a: the cumulative log decay
  *   restarted in every chunk, from which the 1-semiseparable mask
  *   L[i][j] = exp(cs_i - cs_j) (i >= j) and the chunk totals follow (paper card
- *   Method 5 pseudocode "decay_cumsum" and "chunk_decay"; Pitfalls: mask before
- *   exp). Writes table, block_table and cumsum.
+ *   Method 5, the within-chunk cumulative decay and the chunk totals; Pitfalls:
+ *   the mask comes before the exponential). Writes table, block_table and
+ *   cumsum.
  * ssd_chunk_state -- right factors: s_m = sum_j exp(total decay from j to the
  *   end of block m) x_j B_j^T per state block and head, batched matrix
  *   products over tokens (paper section 6, "Right Factors"). Writes

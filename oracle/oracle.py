@@ -20,7 +20,7 @@ Helpers here that are not the recurrence:
     (chunks restart at every sequence start; the last chunk of a sequence may
     be short).
   * ``chunk_cumsum`` -- the cumulative log decay restarted in every chunk
-    (paper card Method 5 pseudocode, "decay_cumsum"), a plain fp64 cumsum.
+    (paper card Method 5, the within-chunk cumulative decay), a plain fp64 cumsum.
 
 The Mamba-2 functions (``softplus``, ``silu``, ``mamba2_discretize``,
 ``mamba2_forward``, ``mamba2_step``) put the block's discretisation, skip and

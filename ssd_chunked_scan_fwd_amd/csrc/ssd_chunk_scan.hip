@@ -7,9 +7,9 @@
 //           + sum_{j <= i} exp2(cs_i - cs_j) (sum_n C[i][n] B[j][n]) X[j][p]
 //                                                                   (diagonal block)
 // ("Transformers are SSMs" paper card, Method 5 / paper section 6, "Diagonal
-// Blocks" and "Left Factors"; pseudocode lines "within_mask", "Y_within",
-// "decay_from_start", "Y_carry"). The mask is applied before the exponential
-// (paper card Pitfalls: "Mask before exp"), so no positive exponent is formed.
+// Blocks" and "Left Factors": the masked within-chunk product and the carry of
+// the entering state, decayed from the chunk start). The mask is applied before
+// the exponential (paper card, Pitfalls), so no positive exponent is formed.
 //
 // bf16 path, one workgroup of 8 waves per (state block, head), one workgroup
 // per CU. The block's entering state comes from the state-passing stage;

@@ -5,8 +5,8 @@
 // tail_j = log2-scaled total decay from token j to the end of the block. With
 // Gs = 1 this is exactly the chunk state of the pages' algorithm: the state at
 // the chunk end from a zero start ("Transformers are SSMs" paper card, Method 5
-// / paper section 6, "Right Factors": one batched matrix product per chunk;
-// pseudocode lines "decay_to_end" and "chunk_states"). With Gs > 1 it is the
+// / paper section 6, "Right Factors": one batched matrix product per chunk,
+// each token weighted by its decay to the chunk end). With Gs > 1 it is the
 // same right factor for a longer block, which the chunk-scan stage refines
 // chunk by chunk.
 //
