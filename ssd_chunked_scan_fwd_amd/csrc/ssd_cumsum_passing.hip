@@ -6,6 +6,8 @@
 // Method 5 / paper section 6: the cumulative log decay restarted in every
 // chunk gives the 1-semiseparable mask and each chunk's total decay; the
 // "Center Factors" step carries states across chunks with a scalar recurrence.
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 #include "ssd_passing.h"
@@ -122,6 +124,29 @@ hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float
 // feeds x dt' into the state, and finishes y with the skip D x and the gate
 // silu(z) (paper card Method 6 block sketch; Paper vs code items 3, 7).
 // ----------------------------------------------------------------------------
+// Sum over aligned groups of n consecutive lanes, n a power of two from 4 to
+// 64; every lane of a group receives the sum (DPP within rows of 16 lanes,
+// then lane swaps across rows).
+__device__ __forceinline__ float lanes_sum(float v, int n) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                                 0xF, 0xF, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});                // quad_perm [1, 0, 3, 2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});                // quad_perm [2, 3, 0, 1]
+  if (n > 4) v += dpp(v, std::integral_constant<int, 0x141>{});    // row_half_mirror
+  if (n > 8) v += dpp(v, std::integral_constant<int, 0x140>{});    // row_mirror
+  if (n > 16) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  }
+  if (n > 32) {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
+  return v;
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state,
                                                        const void* __restrict__ x,
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
       part += s[i] * cc[i];
     }
     *sp = s;
-    for (int off = tpr >> 1; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    part = lanes_sum(part, tpr);
     part += Dh * xp;
     if (zv) {
       const float zp = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(zv)[bh * P + p])
