@@ -69,22 +69,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-// Inclusive sum over lanes 0..l of a wave (DPP): shifts of 1, 2, 4 and 8
-// within each row of 16 lanes, then each row's total broadcast into the rows
-// above it.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_pick(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
-}
-__device__ __forceinline__ float wave_incl_scan(float v) {
-  v += dpp_pick<0x111, 0xF>(v);   // row_shr:1
-  v += dpp_pick<0x112, 0xF>(v);   // row_shr:2
-  v += dpp_pick<0x114, 0xF>(v);   // row_shr:4
-  v += dpp_pick<0x118, 0xF>(v);   // row_shr:8
-  v += dpp_pick<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-  v += dpp_pick<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-  return v;
-}
 __device__ __forceinline__ float sum_row16(float v) {
   v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
   v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]

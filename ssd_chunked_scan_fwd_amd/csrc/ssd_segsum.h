@@ -93,14 +93,9 @@ __device__ __forceinline__ float wave_segsum(F tval, int len, int Q, bool m2, fl
     const int j = jb + lane;
     if (jb < len) {
       const float t = tv[i];
-      float v = m2 ? t * A : t;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float u = __shfl_up(v, d);
-        if (lane >= d) v += u;
-      }
+      float v = wave_incl_scan(m2 ? t * A : t);
       v += carry;
-      carry = __shfl(v, min(len - jb, 64) - 1);
+      carry = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), min(len - jb, 64) - 1));
       if (j < Q) {
         const float c = (j < len ? v : carry) * kLog2e;
         const float k = m2 && j < len ? c - log2f(t) : c;
