@@ -318,9 +318,11 @@ ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void*
  * Outputs: dX, dz (dtype, X's layout; dz NULL exactly when z is NULL),
  * ddt [batch, seqlen, nheads] fp32, ddt_bias, dA_log, dD [nheads] fp32 (dD NULL
  * exactly when D is NULL; ddt_bias may be NULL), dB, dC (dtype, B's layout),
- * dinitial_state (fp32, optional). headdim must be a multiple of 4, at most 256,
- * and the shape one that ssd_bwd supports. With a gate the forward call runs
- * once more (without the gate) for v. The workspace must hold
+ * dinitial_state (fp32, optional). headdim must be a multiple of 8 (every
+ * headdim ssd_fwd supports is) and the shape one that ssd_bwd supports. With a
+ * gate the forward call runs once more (without the gate) for v, and where the
+ * fused backward path applies that run's state tables serve ssd_bwd's forward
+ * state run. The workspace must hold
  * ssd_bwd_mamba2_workspace_bytes(shape, chunk, state_block); it is all
  * overwritten. Same stream, alignment and error rules as ssd_bwd.
  */
