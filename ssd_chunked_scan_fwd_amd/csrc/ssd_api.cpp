@@ -508,10 +508,11 @@ static ssd_status bwd_run(const void* X, const float* log_a, const void* B, cons
       a.N = N;
       a.Q = chunk;
       a.nsl = L.nsl;
+      a.lam_first = lam_first;
+      a.dinit = dinitial_state;  // formed in the launch that sums the head slices
+      a.nseq = (int)nseq;
       e = ssd::launch_bwd_chunks(a, hs);
     }
-    if (e == hipSuccess && dinitial_state)
-      e = ssd::launch_dinit(log_a, lam_first, dinitial_state, cu_seqlens, (int)nseq, T, H, P * N, hs);
     return hip_status(e);
   }
   // Dimensions of the four internal runs of the general path.

@@ -616,14 +616,35 @@ hipError_t launch_chunk_starts(const FwdDims& d, const void* X, const void* B, c
   return launch_chunk_starts_q<128, 64>(d, X, B, ws, out, stream);
 }
 
-// out[t][g][n] = sum over slices of part[sl][t][g][n], rounded to bf16 (four per thread).
-__global__ __launch_bounds__(256) void slice_sum_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                        long n4, int nsl) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n4) return;
-  f32x4 a = reinterpret_cast<const f32x4*>(part)[i];
-  for (int s = 1; s < nsl; ++s) a += reinterpret_cast<const f32x4*>(part)[(long)s * n4 + i];
-  reinterpret_cast<u32x2*>(out)[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+// The tail of the fused backward, one launch: workgroups [0, sb) sum the dB
+// partials over the head slices, [sb, 2 sb) the dC partials (out[t][g][n] =
+// sum over slices of part[sl][t][g][n], rounded to bf16, four per thread;
+// sb = 0 with one slice), and the rest form the initial-state gradient,
+// dinit = exp(log a of the sequence's first token) * lam_first.
+__global__ __launch_bounds__(256) void bwd_tail_kernel(const float* __restrict__ part_b,
+                                                       const float* __restrict__ part_c, uint16_t* __restrict__ dB,
+                                                       uint16_t* __restrict__ dC, long n4, int nsl, long sb,
+                                                       const float* __restrict__ la,
+                                                       const float* __restrict__ lam_first,
+                                                       float* __restrict__ dinit, const int32_t* __restrict__ cu,
+                                                       int T, int H, int PN, long dtotal) {
+  const long blk = blockIdx.x;
+  if (blk < 2 * sb) {
+    const bool c = blk >= sb;
+    const float* part = c ? part_c : part_b;
+    const long i = (blk - (c ? sb : 0)) * 256 + threadIdx.x;
+    if (i >= n4) return;
+    f32x4 a = reinterpret_cast<const f32x4*>(part)[i];
+    for (int s = 1; s < nsl; ++s) a += reinterpret_cast<const f32x4*>(part)[(long)s * n4 + i];
+    reinterpret_cast<u32x2*>(c ? dC : dB)[i] = u32x2{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+    return;
+  }
+  const long i = (blk - 2 * sb) * 256 + threadIdx.x;
+  if (i >= dtotal) return;
+  const long sh = i / PN;
+  const int s = (int)(sh / H), h = (int)(sh % H);
+  const long first = cu ? (long)cu[s] : (long)s * T;
+  dinit[i] = __builtin_amdgcn_exp2f(la[first * H + h] * kLog2e) * lam_first[i];
 }
 
 template <int P, int N, int Q>
@@ -642,13 +663,14 @@ static hipError_t launch_bwd_chunk_t(const BwdChunkArgs& a, hipStream_t stream) 
                      reinterpret_cast<uint16_t*>(a.dX), a.dla, a.nsl == 1 ? a.dB : a.part_b,
                      a.nsl == 1 ? a.dC : a.part_c, a.tokens, a.H, a.G, a.nsl);
   e = hipGetLastError();
-  if (e != hipSuccess || a.nsl == 1) return e;
+  if (e != hipSuccess || (a.nsl == 1 && !a.dinit)) return e;
   const long n4 = a.tokens * a.G * a.N / 4;
-  const unsigned blocks = (unsigned)((n4 + 255) / 256);
-  hipLaunchKernelGGL(slice_sum_kernel, dim3(blocks), dim3(256), 0, stream, a.part_b,
-                     reinterpret_cast<uint16_t*>(a.dB), n4, a.nsl);
-  hipLaunchKernelGGL(slice_sum_kernel, dim3(blocks), dim3(256), 0, stream, a.part_c,
-                     reinterpret_cast<uint16_t*>(a.dC), n4, a.nsl);
+  const long sb = a.nsl > 1 ? (n4 + 255) / 256 : 0;
+  const long dtotal = a.dinit ? (long)a.nseq * a.H * a.P * a.N : 0;
+  const long blocks = 2 * sb + (dtotal + 255) / 256;
+  hipLaunchKernelGGL(bwd_tail_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a.part_b, a.part_c,
+                     reinterpret_cast<uint16_t*>(a.dB), reinterpret_cast<uint16_t*>(a.dC), n4, a.nsl, sb, a.la,
+                     a.lam_first, a.dinit, a.cu, a.T, a.H, a.P * a.N, dtotal);
   return hipGetLastError();
 }
 

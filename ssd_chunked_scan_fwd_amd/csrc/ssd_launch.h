@@ -130,6 +130,12 @@ struct BwdChunkArgs {
   float* dla;
   void *dB, *dC;                // bf16 [tokens][G][N]
   float *part_b, *part_c;       // fp32 [nsl][tokens][G][N] when nsl > 1
+  // Initial-state gradient, formed in the same tail launch as the slice sums
+  // when dinit is not null: dinit = exp(log a of each sequence's first token)
+  // * lam_first, [nseq][H][P*N] fp32.
+  const float* lam_first;
+  float* dinit;
+  int nseq;
   int H, G, P, N, Q, nsl;
 };
 bool bwd_chunk_supported(int P, int N, int Q, bool bf16);
