@@ -461,9 +461,9 @@ static ssd_status bwd_run(const void* X, const float* log_a, const void* B, cons
     void* fstart = L.gs > 1 ? w + L.cstart_f : pf.ws.start_states;
     hipError_t e = hipSuccess;
     if (packed) e = ssd::launch_padded_offsets(cu_seqlens, cur, S, chunk, hs);
-    if (e == hipSuccess) e = ssd::launch_gather_rows(dY, rev_dy, cu_seqlens, cur, S, rows, T, Tr, H, H, P * esz, 1, hs);
-    if (e == hipSuccess) e = ssd::launch_gather_rows(C, rev_c, cu_seqlens, cur, S, rows, T, Tr, G, G, N * esz, 1, hs);
-    if (e == hipSuccess) e = ssd::launch_reverse_log_decay(log_a, la_rev, cu_seqlens, cur, S, rows, T, Tr, H, hs);
+    if (e == hipSuccess)
+      e = ssd::launch_reverse_inputs(dY, rev_dy, P * esz, C, rev_c, N * esz, log_a, la_rev, cu_seqlens, cur, S, rows, T,
+                                     Tr, H, G, hs);
     // Adjoint states: the reversed run over dY (x role) and C (B role) from the
     // final-state gradient; its chunk start states are the adjoints at the
     // forward chunk ends.

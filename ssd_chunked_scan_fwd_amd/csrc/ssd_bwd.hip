@@ -113,17 +113,16 @@ __global__ __launch_bounds__(256) void padded_offsets_kernel(const int32_t* __re
 //           forward layout; padding positions are zero;
 //   mode 2: out is the forward layout ([rows * T]), in the padded reversed layout.
 // Rows move in 16-byte pieces (D * esz is a multiple of 16).
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
-                                                          const int32_t* __restrict__ cu,
-                                                          const int32_t* __restrict__ cur, int S, int T, int Tr,
-                                                          int Hin, int Hout, int row_bytes, int mode,
-                                                          int xblocks, int tpw, long ntok) {
+__device__ __forceinline__ void gather_rows_block(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                  const int32_t* __restrict__ cu, const int32_t* __restrict__ cur,
+                                                  int S, int T, int Tr, int Hin, int Hout, int row_bytes, int mode,
+                                                  int xblocks, int tpw, long ntok, long bid) {
   // A token's row is Hout * pieces 16-byte pieces: xblocks workgroups per
   // token for long rows, tpw tokens per workgroup for short ones.
   const int pieces = row_bytes / 16;  // per head
   const int per_tok = Hout * pieces;
-  const long tok = (blockIdx.x / xblocks) * (long)tpw + (tpw > 1 ? threadIdx.x / per_tok : 0);  // output token
-  const int xb = (int)(blockIdx.x % xblocks);
+  const long tok = (bid / xblocks) * (long)tpw + (tpw > 1 ? threadIdx.x / per_tok : 0);  // output token
+  const int xb = (int)(bid % xblocks);
   const int idx = tpw > 1 ? (int)(threadIdx.x % per_tok) : xb * 256 + (int)threadIdx.x;
   if (idx >= per_tok || tok >= ntok || (tpw > 1 && (int)threadIdx.x >= tpw * per_tok)) return;
   const int ho = idx / pieces, q = idx % pieces;
@@ -139,6 +138,14 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
   u32x4 v = {0u, 0u, 0u, 0u};
   if (src >= 0) v = *reinterpret_cast<const u32x4*>(in + (src * Hin + hi) * (long)row_bytes + q * 16);
   *reinterpret_cast<u32x4*>(out + (tok * Hout + ho) * (long)row_bytes + q * 16) = v;
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                          const int32_t* __restrict__ cu,
+                                                          const int32_t* __restrict__ cur, int S, int T, int Tr,
+                                                          int Hin, int Hout, int row_bytes, int mode,
+                                                          int xblocks, int tpw, long ntok) {
+  gather_rows_block(in, out, cu, cur, S, T, Tr, Hin, Hout, row_bytes, mode, xblocks, tpw, ntok, blockIdx.x);
 }
 
 // out[row, t, g, 0..D) = sum over the heads h of group g of in[row, rsrc(t), h, 0..D)
@@ -167,11 +174,10 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const float* __restrict_
 // Log decays of the reversed run, padded layout: 0 on padding and at the
 // first reversed token of each sequence, else la[src + 1] (the reversed
 // recurrence applies a_{t+1} to the adjoint of h_t).
-__global__ __launch_bounds__(256) void reverse_log_decay_kernel(const float* __restrict__ la, float* __restrict__ out,
-                                                                const int32_t* __restrict__ cu,
-                                                                const int32_t* __restrict__ cur, int S, int T, int Tr,
-                                                                int H, long ntok) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void reverse_log_decay_block(const float* __restrict__ la, float* __restrict__ out,
+                                                        const int32_t* __restrict__ cu, const int32_t* __restrict__ cur,
+                                                        int S, int T, int Tr, int H, long ntok, long bid) {
+  const long i = bid * 256 + threadIdx.x;
   if (i >= ntok * H) return;
   const long tok = i / H;
   const int h = (int)(i % H);
@@ -185,6 +191,46 @@ __global__ __launch_bounds__(256) void reverse_log_decay_kernel(const float* __r
     if (t + 1 < e) v = la[(src + 1) * H + h];
   }
   out[i] = v;
+}
+
+__global__ __launch_bounds__(256) void reverse_log_decay_kernel(const float* __restrict__ la, float* __restrict__ out,
+                                                                const int32_t* __restrict__ cu,
+                                                                const int32_t* __restrict__ cur, int S, int T, int Tr,
+                                                                int H, long ntok) {
+  reverse_log_decay_block(la, out, cu, cur, S, T, Tr, H, ntok, blockIdx.x);
+}
+
+// The fused backward's reversed inputs in one launch: workgroups [0, na) gather
+// the rows of dY, [na, na + nc) those of C, the rest reverse the log decay.
+struct GatherPlan {
+  int xblocks, tpw;
+  long ntok, blocks;
+};
+
+__host__ __device__ inline GatherPlan gather_plan(int Hout, int row_bytes, long ntok) {
+  GatherPlan g;
+  const int pieces = Hout * (row_bytes / 16);
+  g.xblocks = (pieces + 255) / 256;
+  g.tpw = pieces < 256 ? 256 / pieces : 1;  // tokens per workgroup
+  g.ntok = ntok;
+  g.blocks = (ntok + g.tpw - 1) / g.tpw * g.xblocks;
+  return g;
+}
+
+__global__ __launch_bounds__(256) void reverse_inputs_kernel(const uint8_t* __restrict__ dy, uint8_t* __restrict__ rev_dy,
+                                                             const uint8_t* __restrict__ c, uint8_t* __restrict__ rev_c,
+                                                             const float* __restrict__ la, float* __restrict__ la_rev,
+                                                             const int32_t* __restrict__ cu,
+                                                             const int32_t* __restrict__ cur, int S, int T, int Tr,
+                                                             int H, int G, int dy_bytes, int c_bytes, GatherPlan pa,
+                                                             GatherPlan pc) {
+  const long bid = blockIdx.x;
+  if (bid < pa.blocks)
+    gather_rows_block(dy, rev_dy, cu, cur, S, T, Tr, H, H, dy_bytes, 1, pa.xblocks, pa.tpw, pa.ntok, bid);
+  else if (bid < pa.blocks + pc.blocks)
+    gather_rows_block(c, rev_c, cu, cur, S, T, Tr, G, G, c_bytes, 1, pc.xblocks, pc.tpw, pc.ntok, bid - pa.blocks);
+  else
+    reverse_log_decay_block(la, la_rev, cu, cur, S, T, Tr, H, pa.ntok, bid - pa.blocks - pc.blocks);
 }
 
 // [S][H][A][Bdim] -> [S][H][Bdim][A] (fp32), for states handed to runs whose
@@ -403,6 +449,19 @@ hipError_t launch_reverse_log_decay(const float* la, float* out, const int32_t* 
   const long ntok = (long)rows * Tr;
   hipLaunchKernelGGL(reverse_log_decay_kernel, dim3((unsigned)((ntok * H + 255) / 256)), dim3(256), 0, stream, la,
                      out, cu, cur, S, T, Tr, H, ntok);
+  return hipGetLastError();
+}
+
+hipError_t launch_reverse_inputs(const void* dY, void* rev_dy, int dy_bytes, const void* C, void* rev_c, int c_bytes,
+                                 const float* la, float* la_rev, const int32_t* cu, const int32_t* cur, int S, int rows,
+                                 int T, int Tr, int H, int G, hipStream_t stream) {
+  const long ntok = (long)rows * Tr;
+  const GatherPlan pa = gather_plan(H, dy_bytes, ntok), pc = gather_plan(G, c_bytes, ntok);
+  const long blocks = pa.blocks + pc.blocks + (ntok * H + 255) / 256;
+  hipLaunchKernelGGL(reverse_inputs_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const uint8_t*>(dY), reinterpret_cast<uint8_t*>(rev_dy),
+                     reinterpret_cast<const uint8_t*>(C), reinterpret_cast<uint8_t*>(rev_c), la, la_rev, cu, cur, S,
+                     T, Tr, H, G, dy_bytes, c_bytes, pa, pc);
   return hipGetLastError();
 }
 

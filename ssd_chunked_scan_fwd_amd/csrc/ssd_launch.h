@@ -95,6 +95,11 @@ hipError_t launch_group_sum(const float* in, void* out, const int32_t* cu, const
 hipError_t launch_reverse_log_decay(const float* la, float* out, const int32_t* cu, const int32_t* cur, int S,
                                     int rows, int T, int Tr, int H, hipStream_t stream);
 hipError_t launch_transpose_states(const float* in, float* out, long nmat, int A, int Bd, hipStream_t stream);
+// dY and C into the padded time-reversed layout and the shifted reversed log
+// decay, in one launch (the fused backward's first step).
+hipError_t launch_reverse_inputs(const void* dY, void* rev_dy, int dy_bytes, const void* C, void* rev_c, int c_bytes,
+                                 const float* la, float* la_rev, const int32_t* cu, const int32_t* cur, int S, int rows,
+                                 int T, int Tr, int H, int G, hipStream_t stream);
 hipError_t launch_dinit(const float* la, const float* lam_first, float* dinit, const int32_t* cu, int nseq, int T,
                         int H, int PN, hipStream_t stream);
 
