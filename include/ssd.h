@@ -36,7 +36,8 @@
  * pointers for all tensors, host pointers for `shape` and `layout`. The
  * library allocates nothing, never synchronises, issues no memset, and
  * enqueues its kernels on `stream` (a hipStream_t; NULL is the null stream).
- * Its only global state is the process-wide mode of ssd_set_state_chain. A
+ * Its only global state is the process-wide mode of ssd_set_state_chain (an
+ * atomic). A
  * call returns after enqueueing; errors of the kernels themselves surface on
  * the stream like any HIP error. A call may be captured into a HIP graph: its
  * replays compute what the call computes, from the buffers' contents at
@@ -165,8 +166,22 @@ ssd_status ssd_fwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_
  *          itself costs more than the launch it saves on ROCm 7 (about
  *          74 us per call at T = 16384, H = 32), hence not the default.
  * Both give bit-identical results. Process-wide; returns the previous mode.
+ * Cooperative launches are not for profiled runs: rocprofv3 has ended with a
+ * segmentation fault in its exit path after a program that made them.
  */
 int32_t ssd_set_state_chain(int32_t mode);
+
+/*
+ * Whether, in mode 1, a forward call with this shape, chunk length and state
+ * block (<= 0: the default) would run its state chain as the cooperative
+ * launch on the current device, given a stream that is not being captured:
+ * *cooperative = 1 if so, 0 if it would take the two launches. Asks the
+ * runtime for the kernel's occupancy on every call and keeps nothing.
+ * Packed shapes (num_seqs > 0) are sized as calls with cu_seqlens. Returns
+ * the forward call's shape errors, or SSD_ERR_HIP if the runtime query fails.
+ */
+ssd_status ssd_state_chain_cooperative(const ssd_shape* shape, int32_t chunk, int32_t state_block,
+                                       int32_t* cooperative);
 
 /*
  * Forward pass: Y and final states from zero initial states, with the default
@@ -340,7 +355,8 @@ ssd_status ssd_bwd_mamba2(const void* X, const float* dt, const float* dt_bias, 
  * the recurrence with a constant-size state (paper card Method 8 and its cost
  * table: about N^2 work per step; the page-1 summary: generation needs only a
  * constant-size state).
- *   state [batch, H, P, N] fp32, updated in place: s = exp(la) s + x B^T
+ *   state [batch, H, P, N] fp32, updated in place: s = exp(la) s + x B^T;
+ *         16-byte aligned (SSD_ERR_INVALID_ARGUMENT otherwise)
  *   x [batch, H, P] dtype, log_a [batch, H] fp32, B, C [batch, G, N] dtype
  *   y [batch, H, P] dtype (written), read from the updated state.
  * shape->seqlen and shape->num_seqs are ignored.
@@ -352,7 +368,7 @@ ssd_status ssd_step(float* state, const void* x, const float* log_a, const void*
  * The Mamba-2 block's decode step (the loop body of ssd_fwd_mamba2):
  *   dt' = softplus(dt + dt_bias), state = exp(dt' A) state + (x dt') B^T,
  *   y = C^T state + D x, y = y * silu(z).
- *   state [batch, H, P, N] fp32 in place; x, z [batch, H, P] dtype (z may be NULL);
+ *   state [batch, H, P, N] fp32 in place, 16-byte aligned; x, z [batch, H, P] dtype (z may be NULL);
  *   dt [batch, H] fp32 raw; dt_bias (may be NULL), A_log, D (may be NULL) [H] fp32;
  *   B, C [batch, G, N] dtype; y [batch, H, P] dtype (written).
  * A prompt run through ssd_fwd_mamba2 hands its final_state to this step.

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     lib,
     make_shape,
     set_state_chain,
+    state_chain_cooperative,
     state_passing,
     step,
     step_mamba2,
@@ -35,6 +36,6 @@ __all__ = [
     "fwd", "step", "fwd_mamba2", "step_mamba2",
     "bwd", "bwd_workspace_bytes", "bwd_mamba2", "bwd_mamba2_workspace_bytes",
     "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan",
-    "set_state_chain", "Workspace", "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib",
+    "set_state_chain", "state_chain_cooperative", "Workspace", "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib",
     "default_state_block",
 ]

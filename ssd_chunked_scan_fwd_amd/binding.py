@@ -26,8 +26,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "ssd_fwd_layout",
            "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
            "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2",
-           "ssd_bwd_workspace_bytes", "ssd_bwd", "ssd_set_state_chain", "ssd_bwd_mamba2_workspace_bytes",
-           "ssd_bwd_mamba2")
+           "ssd_bwd_workspace_bytes", "ssd_bwd", "ssd_set_state_chain", "ssd_state_chain_cooperative",
+           "ssd_bwd_mamba2_workspace_bytes", "ssd_bwd_mamba2")
 
 
 class SSDError(RuntimeError):
@@ -97,6 +97,8 @@ def lib():
         L.ssd_step_mamba2.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, shp, vp]
         L.ssd_set_state_chain.restype = i32
         L.ssd_set_state_chain.argtypes = [i32]
+        L.ssd_state_chain_cooperative.restype = ctypes.c_int
+        L.ssd_state_chain_cooperative.argtypes = [shp, i32, i32, ctypes.POINTER(i32)]
         L.ssd_bwd_mamba2_workspace_bytes.restype = ctypes.c_int
         L.ssd_bwd_mamba2_workspace_bytes.argtypes = [shp, i32, i32, ctypes.POINTER(sz)]
         L.ssd_bwd_mamba2.restype = ctypes.c_int
@@ -203,25 +205,78 @@ class Workspace:
                           (n, s.nheads, s.headdim, s.dstate))
 
 
+def _expect(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, device=None, align: int = 0):
+    """Raise ValueError unless `t` (None passes) has the given shape, dtype,
+    contiguity and device."""
+    _expect_all([(t, name, shape, dtype, align)], device)
+
+
+def _expect_all(specs, device=None):
+    """Check every (tensor, name, shape, dtype, align) in `specs`: first the
+    structure of all of them (shape, dtype, contiguity), then their device and
+    alignment, so a mismatched tensor is reported as such wherever it lives."""
+    specs = [sp for sp in specs if sp[0] is not None]
+    for t, name, shape, dtype, _ in specs:
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for t, name, _, _, align in specs:
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if align and t.data_ptr() % align:
+            raise ValueError(f"{name} must be {align}-byte aligned")
+
+
 def _check_inputs(X, log_a, B, C, cu_seqlens):
-    for name, t in (("X", X), ("B", B), ("C", C)):
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if log_a is not None and (log_a.dtype != torch.float32 or not log_a.is_contiguous() or not log_a.is_cuda):
-        raise ValueError("log_a must be a contiguous fp32 device tensor")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise ValueError("cu_seqlens must be an int32 device tensor")
-    if X is not None and B is not None and (X.dtype != B.dtype or (C is not None and C.dtype != X.dtype)):
-        raise ValueError("X, B and C must share one dtype")
+    """The forward inputs against one another: X [b, T, H, P], log_a [b, T, H]
+    fp32, B and C [b, T, G, N] of X's dtype with H % G == 0, cu_seqlens int32
+    [S + 1] with b == 1. Returns their specs for _expect_all."""
+    if not isinstance(X, torch.Tensor) or X.dim() != 4:
+        raise ValueError("X must be a 4-d tensor [batch, seqlen, nheads, headdim]")
+    if X.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"X has dtype {X.dtype}; bfloat16 and float32 are supported")
+    b, T, H, P = X.shape
+    if not isinstance(B, torch.Tensor) or B.dim() != 4 or tuple(B.shape[:2]) != (b, T):
+        raise ValueError(f"B must be a 4-d tensor [{b}, {T}, ngroups, dstate]")
+    G, N = B.shape[2], B.shape[3]
+    if G < 1 or H % G:
+        raise ValueError(f"nheads {H} must be a multiple of ngroups {G}")
+    if cu_seqlens is not None:
+        if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a 1-d tensor of num_seqs + 1 >= 2 entries")
+        if b != 1:
+            raise ValueError("packed sequences (cu_seqlens) need batch 1")
+    return [(X, "X", None, None, 0), (B, "B", (b, T, G, N), X.dtype, 0), (C, "C", (b, T, G, N), X.dtype, 0),
+            (log_a, "log_a", (b, T, H), torch.float32, 0), (cu_seqlens, "cu_seqlens", None, torch.int32, 0)]
 
 
-def _check_state(t: Optional[torch.Tensor], shape: Shape, name: str):
-    if t is None:
-        return
-    nseq = shape.num_seqs if shape.num_seqs > 0 else shape.batch
-    want = (nseq, shape.nheads, shape.headdim, shape.dstate)
-    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != want:
-        raise ValueError(f"{name} must be a contiguous fp32 device tensor of shape {want}")
+def _nseq(shape: Shape) -> int:
+    return shape.num_seqs if shape.num_seqs > 0 else shape.batch
+
+
+def _state_spec(t: Optional[torch.Tensor], shape: Shape, name: str):
+    """A state tensor: fp32 [rows or sequences, H, P, N], 16-byte aligned."""
+    return (t, name, (_nseq(shape), shape.nheads, shape.headdim, shape.dstate), torch.float32, 16)
+
+
+def _check_state(t: Optional[torch.Tensor], shape: Shape, name: str, device=None):
+    _expect_all([_state_spec(t, shape, name)], device)
+
+
+def _check_workspace(ws: "Workspace", shape: Shape, chunk: int):
+    if not isinstance(ws, Workspace):
+        raise ValueError("workspace must be a Workspace")
+    mine = tuple(getattr(ws.shape, f) for f, _ in Shape._fields_)
+    theirs = tuple(getattr(shape, f) for f, _ in Shape._fields_)
+    if mine != theirs or ws.chunk != int(chunk):
+        raise ValueError("the workspace was made for another shape or chunk length")
 
 
 def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
@@ -235,18 +290,21 @@ def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
     initial_state: fp32 [rows or sequences, H, P, N] the state each row (each
     packed sequence) starts from; None for zero states.
     """
-    _check_inputs(X, log_a, B, C, cu_seqlens)
+    specs = _check_inputs(X, log_a, B, C, cu_seqlens)
     shape = make_shape(X, B, cu_seqlens)
-    _check_state(initial_state, shape, "initial_state")
+    if workspace is not None:
+        _check_workspace(workspace, shape, chunk)
+        if state_block > 0 and state_block != workspace.state_block:
+            raise ValueError("state_block differs from the workspace's")
+    _expect_all(specs + [_state_spec(initial_state, shape, "initial_state"), (Y, "Y", tuple(X.shape), X.dtype, 0),
+                         _state_spec(final_state, shape, "final_state")], X.device)
     if Y is None:
         Y = torch.empty_like(X)
     if final_state is None and want_final:
-        nseq = X.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
-        final_state = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
+        final_state = torch.empty(_nseq(shape), X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32,
+                                  device=X.device)
     if workspace is None:
         workspace = Workspace(shape, chunk, X.device, state_block)
-    elif state_block > 0 and state_block != workspace.state_block:
-        raise ValueError("state_block differs from the workspace's")
     _call("ssd_fwd_ex", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), _ptr(initial_state), int(chunk),
           workspace.state_block,
           _ptr(Y), _ptr(final_state), ctypes.byref(shape), _ptr(workspace.buffer), workspace.nbytes,
@@ -254,38 +312,73 @@ def fwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
     return Y, final_state
 
 
+def _stage_check(shape: Shape, ws: Workspace, X=None, log_a=None, B=None, C=None, Y=None, cu_seqlens=None):
+    """Tensors handed to a single stage against the shape its workspace was made for."""
+    _check_workspace(ws, shape, ws.chunk)
+    dt = torch.bfloat16 if shape.dtype == DTYPE_BF16 else torch.float32
+    b, T, H, G, P, N = shape.batch, shape.seqlen, shape.nheads, shape.ngroups, shape.headdim, shape.dstate
+    want_cu = shape.num_seqs + 1 if shape.num_seqs > 0 else None
+    if (cu_seqlens is None) != (want_cu is None):
+        raise ValueError("cu_seqlens must be given exactly when the shape is packed (num_seqs > 0)")
+    _expect_all([(X, "X", (b, T, H, P), dt, 0), (Y, "Y", (b, T, H, P), dt, 0), (B, "B", (b, T, G, N), dt, 0),
+                 (C, "C", (b, T, G, N), dt, 0), (log_a, "log_a", (b, T, H), torch.float32, 0),
+                 (cu_seqlens, "cu_seqlens", (want_cu,) if want_cu else None, torch.int32, 0)], ws.buffer.device)
+
+
 def chunk_cumsum(log_a, cu_seqlens, shape: Shape, ws: Workspace):
+    _stage_check(shape, ws, log_a=log_a, cu_seqlens=cu_seqlens)
     _call("ssd_chunk_cumsum", _ptr(log_a), _ptr(cu_seqlens), ws.chunk, ws.state_block, ctypes.byref(shape),
           _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
 
 
 def chunk_state(X, B, cu_seqlens, shape: Shape, ws: Workspace):
+    _stage_check(shape, ws, X=X, B=B, cu_seqlens=cu_seqlens)
     _call("ssd_chunk_state", _ptr(X), _ptr(B), _ptr(cu_seqlens), ws.chunk, ws.state_block, ctypes.byref(shape),
           _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
 
 
 def state_passing(cu_seqlens, final_state, shape: Shape, ws: Workspace, initial_state=None):
-    _check_state(initial_state, shape, "initial_state")
+    _stage_check(shape, ws, cu_seqlens=cu_seqlens)
+    _expect_all([_state_spec(initial_state, shape, "initial_state"), _state_spec(final_state, shape, "final_state")],
+                ws.buffer.device)
     _call("ssd_state_passing", _ptr(cu_seqlens), _ptr(initial_state), ws.chunk, ws.state_block, _ptr(final_state),
           ctypes.byref(shape), _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
 
 
 def chunk_scan(X, B, C, cu_seqlens, Y, shape: Shape, ws: Workspace):
+    _stage_check(shape, ws, X=X, B=B, C=C, Y=Y, cu_seqlens=cu_seqlens)
     _call("ssd_chunk_scan", _ptr(X), _ptr(B), _ptr(C), _ptr(cu_seqlens), ws.chunk, ws.state_block, _ptr(Y),
           ctypes.byref(shape), _ptr(ws.buffer), ws.nbytes, _stream(ws.buffer.device))
+
+
+def _check_step(state, x, B, C, y, log_a=None):
+    """Decode-step tensors: x [b, H, P], state fp32 [b, H, P, N] (16-byte aligned),
+    B and C [b, G, N] of x's dtype, log_a fp32 [b, H], y like x."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 3:
+        raise ValueError("x must be a 3-d tensor [batch, nheads, headdim]")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"x has dtype {x.dtype}; bfloat16 and float32 are supported")
+    b, H, P = x.shape
+    if not isinstance(B, torch.Tensor) or B.dim() != 3 or B.shape[0] != b:
+        raise ValueError(f"B must be a 3-d tensor [{b}, ngroups, dstate]")
+    G, N = B.shape[1], B.shape[2]
+    if G < 1 or H % G:
+        raise ValueError(f"nheads {H} must be a multiple of ngroups {G}")
+    if state is None:
+        raise ValueError("state is required")
+    specs = [(x, "x", None, None, 0), (B, "B", (b, G, N), x.dtype, 0), (C, "C", (b, G, N), x.dtype, 0),
+             (state, "state", (b, H, P, N), torch.float32, 16), (log_a, "log_a", (b, H), torch.float32, 0),
+             (y, "y", (b, H, P), x.dtype, 0)]
+    return Shape(b, 1, H, G, P, N, 0, _dtype_code(x.dtype)), specs
 
 
 def step(state: torch.Tensor, x: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
          y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step (ssd_step): updates `state` in place and returns y."""
-    for name, t in (("state", state), ("x", x), ("B", B), ("C", C)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if state.dtype != torch.float32 or log_a.dtype != torch.float32:
-        raise ValueError("state and log_a must be fp32")
-    b, H, P = x.shape
-    G, N = B.shape[1], B.shape[2]
-    shape = Shape(b, 1, H, G, P, N, 0, _dtype_code(x.dtype))
+    if log_a is None:
+        raise ValueError("log_a is required")
+    shape, specs = _check_step(state, x, B, C, y, log_a)
+    _expect_all(specs, x.device)
     if y is None:
         y = torch.empty_like(x)
     _call("ssd_step", _ptr(state), _ptr(x), _ptr(log_a), _ptr(B), _ptr(C), _ptr(y), ctypes.byref(shape),
@@ -294,18 +387,13 @@ def step(state: torch.Tensor, x: torch.Tensor, log_a: torch.Tensor, B: torch.Ten
 
 
 def _check_mamba2(X, dt, dt_bias, A_log, D, z, H: int):
-    lead = tuple(X.shape[:-1])
-    if dt.dtype != torch.float32 or not dt.is_cuda or not dt.is_contiguous() or tuple(dt.shape) != lead:
-        raise ValueError(f"dt must be a contiguous fp32 device tensor of shape {lead}")
-    for name, t, need in (("dt_bias", dt_bias, False), ("A_log", A_log, True), ("D", D, False)):
-        if t is None:
-            if need:
-                raise ValueError(f"{name} is required")
-            continue
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != (H,):
-            raise ValueError(f"{name} must be a contiguous fp32 device tensor of shape ({H},)")
-    if z is not None and (z.dtype != X.dtype or not z.is_cuda or not z.is_contiguous() or z.shape != X.shape):
-        raise ValueError("z must be a contiguous device tensor of X's shape and dtype")
+    """Specs of the Mamba-2 call's extra tensors: dt [*X.shape[:-1]] fp32, dt_bias,
+    A_log, D [H] fp32, z like X."""
+    if dt is None or A_log is None:
+        raise ValueError("dt and A_log are required")
+    return [(dt, "dt", tuple(X.shape[:-1]), torch.float32, 0), (dt_bias, "dt_bias", (H,), torch.float32, 0),
+            (A_log, "A_log", (H,), torch.float32, 0), (D, "D", (H,), torch.float32, 0),
+            (z, "z", tuple(X.shape), X.dtype, 0)]
 
 
 def fwd_mamba2(X: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
@@ -320,19 +408,21 @@ def fwd_mamba2(X: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.
     A_log and D are fp32 [H]; z (the gate) has X's shape and dtype. The other
     arguments are those of fwd().
     """
-    _check_inputs(X, None, B, C, cu_seqlens)
-    _check_mamba2(X, dt, dt_bias, A_log, D, z, X.shape[2])
+    specs = _check_inputs(X, None, B, C, cu_seqlens) + _check_mamba2(X, dt, dt_bias, A_log, D, z, X.shape[2])
     shape = make_shape(X, B, cu_seqlens)
-    _check_state(initial_state, shape, "initial_state")
+    if workspace is not None:
+        _check_workspace(workspace, shape, chunk)
+        if state_block > 0 and state_block != workspace.state_block:
+            raise ValueError("state_block differs from the workspace's")
+    _expect_all(specs + [_state_spec(initial_state, shape, "initial_state"), (Y, "Y", tuple(X.shape), X.dtype, 0),
+                         _state_spec(final_state, shape, "final_state")], X.device)
     if Y is None:
         Y = torch.empty_like(X)
     if final_state is None and want_final:
-        nseq = X.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
-        final_state = torch.empty(nseq, X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32, device=X.device)
+        final_state = torch.empty(_nseq(shape), X.shape[2], X.shape[3], B.shape[3], dtype=torch.float32,
+                                  device=X.device)
     if workspace is None:
         workspace = Workspace(shape, chunk, X.device, state_block)
-    elif state_block > 0 and state_block != workspace.state_block:
-        raise ValueError("state_block differs from the workspace's")
     _call("ssd_fwd_mamba2", _ptr(X), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(D), _ptr(z), _ptr(B), _ptr(C),
           _ptr(cu_seqlens), _ptr(initial_state), int(chunk), workspace.state_block, _ptr(Y), _ptr(final_state),
           ctypes.byref(shape), _ptr(workspace.buffer), workspace.nbytes, _stream(X.device))
@@ -343,17 +433,8 @@ def step_mamba2(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: t
                 C: torch.Tensor, dt_bias: Optional[torch.Tensor] = None, D: Optional[torch.Tensor] = None,
                 z: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One Mamba-2 decode step (ssd_step_mamba2): updates `state` in place and returns y."""
-    for name, t in (("state", state), ("x", x), ("B", B), ("C", C)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-    if state.dtype != torch.float32:
-        raise ValueError("state must be fp32")
-    b, H, P = x.shape
-    _check_mamba2(x, dt, dt_bias, A_log, D, z, H)
-    G, N = B.shape[1], B.shape[2]
-    if tuple(state.shape) != (b, H, P, N):
-        raise ValueError(f"state must have shape {(b, H, P, N)}")
-    shape = Shape(b, 1, H, G, P, N, 0, _dtype_code(x.dtype))
+    shape, specs = _check_step(state, x, B, C, y)
+    _expect_all(specs + _check_mamba2(x, dt, dt_bias, A_log, D, z, x.shape[1]), x.device)
     if y is None:
         y = torch.empty_like(x)
     _call("ssd_step_mamba2", _ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A_log), _ptr(D), _ptr(z),
@@ -363,8 +444,16 @@ def step_mamba2(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: t
 
 def set_state_chain(mode: int) -> int:
     """ssd_set_state_chain: 1 runs the state chain as one cooperative launch when
-    it fits (the default), 0 always as two launches. Returns the previous mode."""
+    it fits, 0 (the default) always as two launches. Returns the previous mode."""
     return int(lib().ssd_set_state_chain(int(mode)))
+
+
+def state_chain_cooperative(shape: Shape, chunk: int, state_block: int = 0) -> bool:
+    """ssd_state_chain_cooperative: whether mode 1 runs this shape's state chain as
+    the cooperative launch on the current device (uncaptured stream)."""
+    r = ctypes.c_int32(0)
+    _call("ssd_state_chain_cooperative", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(r))
+    return bool(r.value)
 
 
 def bwd_workspace_bytes(shape: Shape, chunk: int, state_block: int = 0) -> int:
@@ -379,13 +468,14 @@ def bwd(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor, 
         want_dinit: bool = False, workspace: Optional[torch.Tensor] = None):
     """Backward pass (ssd_bwd): gradients of <dY, Y> + <dfinal_state, final_state>
     for the forward pass with these inputs. Returns dict(dX, dlog_a, dB, dC, dinit or None)."""
-    _check_inputs(X, log_a, B, C, cu_seqlens)
-    if dY.dtype != X.dtype or not dY.is_cuda or not dY.is_contiguous() or dY.shape != X.shape:
-        raise ValueError("dY must be a contiguous device tensor of X's shape and dtype")
+    specs = _check_inputs(X, log_a, B, C, cu_seqlens)
+    if dY is None:
+        raise ValueError("dY is required")
     shape = make_shape(X, B, cu_seqlens)
-    _check_state(initial_state, shape, "initial_state")
-    _check_state(dfinal_state, shape, "dfinal_state")
+    _expect_all(specs + [(dY, "dY", tuple(X.shape), X.dtype, 0), _state_spec(initial_state, shape, "initial_state"),
+                         _state_spec(dfinal_state, shape, "dfinal_state")], X.device)
     nbytes = bwd_workspace_bytes(shape, chunk, state_block)
+    _expect(workspace, "workspace", dtype=torch.uint8, device=X.device, align=256)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
     dX = torch.empty_like(X)
@@ -416,14 +506,14 @@ def bwd_mamba2(X: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.
                workspace: Optional[torch.Tensor] = None):
     """Backward pass of the Mamba-2 call (ssd_bwd_mamba2). Returns dict(dX, ddt, ddt_bias,
     dA_log, dD or None, dz or None, dB, dC, dinit or None)."""
-    _check_inputs(X, None, B, C, cu_seqlens)
-    _check_mamba2(X, dt, dt_bias, A_log, D, z, X.shape[2])
-    if dY.dtype != X.dtype or not dY.is_cuda or not dY.is_contiguous() or dY.shape != X.shape:
-        raise ValueError("dY must be a contiguous device tensor of X's shape and dtype")
+    specs = _check_inputs(X, None, B, C, cu_seqlens) + _check_mamba2(X, dt, dt_bias, A_log, D, z, X.shape[2])
+    if dY is None:
+        raise ValueError("dY is required")
     shape = make_shape(X, B, cu_seqlens)
-    _check_state(initial_state, shape, "initial_state")
-    _check_state(dfinal_state, shape, "dfinal_state")
+    _expect_all(specs + [(dY, "dY", tuple(X.shape), X.dtype, 0), _state_spec(initial_state, shape, "initial_state"),
+                         _state_spec(dfinal_state, shape, "dfinal_state")], X.device)
     nbytes = bwd_mamba2_workspace_bytes(shape, chunk, state_block)
+    _expect(workspace, "workspace", dtype=torch.uint8, device=X.device, align=256)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=X.device)
     H = X.shape[2]

@@ -607,6 +607,7 @@ ssd_status ssd_step_mamba2(float* state, const void* x, const float* dt, const f
                            const float* D, const void* z, const void* B, const void* C, void* y,
                            const ssd_shape* shape, void* stream) {
   if (!shape || !state || !x || !dt || !A_log || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)state & 15) return SSD_ERR_INVALID_ARGUMENT;  // the state moves in 16-byte pieces
   const ssd_shape* s = shape;
   const ssd_status st = check_step(s);
   if (st != SSD_OK) return st;
@@ -622,6 +623,31 @@ ssd_status ssd_step_mamba2(float* state, const void* x, const float* dt, const f
 }
 
 int32_t ssd_set_state_chain(int32_t mode) { return g_state_chain.exchange(mode ? 1 : 0); }
+
+ssd_status ssd_state_chain_cooperative(const ssd_shape* shape, int32_t chunk, int32_t state_block,
+                                       int32_t* cooperative) {
+  if (!cooperative) return SSD_ERR_INVALID_ARGUMENT;
+  // packed shapes (num_seqs > 0) size their slots as a call with cu_seqlens does
+  static const int32_t kPackedMarker = 0;
+  const int32_t* cu = (shape && shape->num_seqs > 0) ? &kPackedMarker : nullptr;
+  ssd_status st = check_shape(shape, cu, chunk);
+  if (st != SSD_OK) return st;
+  const int32_t gs = state_block > 0 ? state_block : default_state_block(shape, cu, chunk);
+  st = check_state_block(shape, gs);
+  if (st != SSD_OK) return st;
+  ssd_layout L;
+  st = make_layout(shape, cu, chunk, gs, &L);
+  if (st != SSD_OK) return st;
+  const ssd_shape* s = shape;
+  const ssd::FwdDims d{s->batch, s->seqlen, s->nheads, s->ngroups, s->headdim, s->dstate, chunk, gs,
+                       cu ? s->num_seqs : 0, s->dtype == SSD_DTYPE_BF16 ? 1 : 0,
+                       (long)L.slots_per_row, (long)L.nslots, (long)L.blocks_per_row, (long)L.nblocks};
+  bool coop = false;
+  const hipError_t e = ssd::chunk_state_chain_cooperative(d, &coop);
+  if (e != hipSuccess) return SSD_ERR_HIP;
+  *cooperative = coop ? 1 : 0;
+  return SSD_OK;
+}
 
 ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
                    const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
@@ -748,6 +774,7 @@ ssd_status ssd_bwd_mamba2(const void* X, const float* dt, const float* dt_bias, 
 ssd_status ssd_step(float* state, const void* x, const float* log_a, const void* B, const void* C, void* y,
                     const ssd_shape* shape, void* stream) {
   if (!shape || !state || !x || !log_a || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+  if ((uintptr_t)state & 15) return SSD_ERR_INVALID_ARGUMENT;  // the state moves in 16-byte pieces
   const ssd_shape* s = shape;
   const ssd_status st = check_step(s);
   if (st != SSD_OK) return st;

@@ -26,8 +26,11 @@
 // queries (dC: keys up to the strip); the pair tiles of both roles are computed
 // by the owner in the orientation whose accumulator layout is directly the
 // B operand of the next product, so L o C B^T and L o dY X^T never go through
-// LDS. Waves w and w + Q/32 share a SIMD and own strips w and Q/16 - 1 - w,
-// which evens out the causal work.
+// LDS. Both enter their products as bf16 hi and lo pairs (two MFMAs on the same
+// other operand), so the pair tiles are not rounded to bf16 once: the masked
+// decayed products carry the full fp32 value into dX, dB and dC. Waves w and
+// w + Q/32 share a SIMD and own strips w and Q/16 - 1 - w, which evens out the
+// causal work.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 #include "ssd_segsum.h"
@@ -258,11 +261,12 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
 #pragma unroll
     for (int kk = 0; kk < HALF; ++kk) {
       if (2 * kk + 1 < i) continue;
-      uint32_t w1h[4], w1l[4], w2[4];
+      uint32_t w1h[4], w1l[4], w2[4], w2l[4];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int ut = 2 * kk + hf;
         w1h[2 * hf] = w1h[2 * hf + 1] = w1l[2 * hf] = w1l[2 * hf + 1] = w2[2 * hf] = w2[2 * hf + 1] = 0u;
+        w2l[2 * hf] = w2l[2 * hf + 1] = 0u;
         if (ut < i) continue;  // queries before the strip: zero
         f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -294,9 +298,11 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
         w1l[2 * hf + 1] = pack_bf16x2(a1[2] - bf16_lo(w1h[2 * hf + 1]), a1[3] - bf16_hi(w1h[2 * hf + 1]));
         w2[2 * hf] = pack_bf16x2(a2[0], a2[1]);
         w2[2 * hf + 1] = pack_bf16x2(a2[2], a2[3]);
+        w2l[2 * hf] = pack_bf16x2(a2[0] - bf16_lo(w2[2 * hf]), a2[1] - bf16_hi(w2[2 * hf]));
+        w2l[2 * hf + 1] = pack_bf16x2(a2[2] - bf16_lo(w2[2 * hf + 1]), a2[3] - bf16_hi(w2[2 * hf + 1]));
       }
       const u32x4 bh = {w1h[0], w1h[1], w1h[2], w1h[3]}, bl = {w1l[0], w1l[1], w1l[2], w1l[3]};
-      const u32x4 b2 = {w2[0], w2[1], w2[2], w2[3]};
+      const u32x4 b2 = {w2[0], w2[1], w2[2], w2[3]}, b2l = {w2l[0], w2l[1], w2l[2], w2l[3]};
 #pragma unroll
       for (int pt = 0; pt < PT; ++pt) {
         const u32x4 ya = frag_k_rows_accpair(Ys, pP, 32 * kk, 16 * pt, lane);
@@ -304,7 +310,11 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
         dx[pt] = mfma16x16x32(ya, bl, dx[pt]);
       }
 #pragma unroll
-      for (int m = 0; m < NT; ++m) db[m] = mfma16x16x32(frag_k_rows_accpair(Cs, pN, 32 * kk, 16 * m, lane), b2, db[m]);
+      for (int m = 0; m < NT; ++m) {
+        const u32x4 ca = frag_k_rows_accpair(Cs, pN, 32 * kk, 16 * m, lane);
+        db[m] = mfma16x16x32(ca, b2, db[m]);
+        db[m] = mfma16x16x32(ca, b2l, db[m]);
+      }
     }
 
     // ---- the strip as queries: key tiles st <= i in pairs. W2 = L o dY X^T in
@@ -312,11 +322,11 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
 #pragma unroll
     for (int kk = 0; kk < HALF; ++kk) {
       if (2 * kk > i) continue;
-      uint32_t w2q[4];
+      uint32_t w2q[4], w2ql[4];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int st = 2 * kk + hf;
-        w2q[2 * hf] = w2q[2 * hf + 1] = 0u;
+        w2q[2 * hf] = w2q[2 * hf + 1] = w2ql[2 * hf] = w2ql[2 * hf + 1] = 0u;
         if (st > i) continue;  // keys after the strip: zero
         f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -333,10 +343,16 @@ __global__ __launch_bounds__(Q / 16 * 64, 1) void bwd_chunk_kernel(
         }
         w2q[2 * hf] = pack_bf16x2(a2[0], a2[1]);
         w2q[2 * hf + 1] = pack_bf16x2(a2[2], a2[3]);
+        w2ql[2 * hf] = pack_bf16x2(a2[0] - bf16_lo(w2q[2 * hf]), a2[1] - bf16_hi(w2q[2 * hf]));
+        w2ql[2 * hf + 1] = pack_bf16x2(a2[2] - bf16_lo(w2q[2 * hf + 1]), a2[3] - bf16_hi(w2q[2 * hf + 1]));
       }
-      const u32x4 bq = {w2q[0], w2q[1], w2q[2], w2q[3]};
+      const u32x4 bq = {w2q[0], w2q[1], w2q[2], w2q[3]}, bql = {w2ql[0], w2ql[1], w2ql[2], w2ql[3]};
 #pragma unroll
-      for (int m = 0; m < NT; ++m) dc[m] = mfma16x16x32(frag_k_rows_accpair(Bs, pN, 32 * kk, 16 * m, lane), bq, dc[m]);
+      for (int m = 0; m < NT; ++m) {
+        const u32x4 ba = frag_k_rows_accpair(Bs, pN, 32 * kk, 16 * m, lane);
+        dc[m] = mfma16x16x32(ba, bq, dc[m]);
+        dc[m] = mfma16x16x32(ba, bql, dc[m]);
+      }
     }
     colsum = sum_rows4(colsum);
 

@@ -433,36 +433,38 @@ static hipError_t dispatch_state_n(const FwdDims& d, const void* X, const void* 
   }
 }
 
+// Whether the grid of the cooperative chain kernel for these dimensions can be
+// resident all at once on the current device (asked on every call: nothing is
+// cached, so concurrent host threads share no state here).
+template <int P, int N>
+static hipError_t chain_fits_device(const FwdDims& d, bool* fits) {
+  *fits = false;
+  const size_t lds = chunk_state_bf16_lds_bytes(P, N, d.state_block * d.Q);
+  auto kern = chunk_state_chain_kernel<P, N>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  int per_cu = 0, ncu = 0, dev = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kStateThreads, lds);
+  if (e == hipSuccess) e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  *fits = d.nblocks * d.H <= (long)per_cu * ncu;
+  return hipSuccess;
+}
+
 template <int P, int N>
 static hipError_t launch_chain_t(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
                                  hipStream_t stream, const SegArgs& sa, const float* init, float* final_state,
                                  bool* launched) {
+  bool fits = false;
+  hipError_t e = chain_fits_device<P, N>(d, &fits);
+  if (e != hipSuccess || !fits) return e;  // not all resident: the caller runs two launches
   const size_t lds = chunk_state_bf16_lds_bytes(P, N, d.state_block * d.Q);
   auto kern = chunk_state_chain_kernel<P, N>;
-  // Resident workgroups per CU for this kernel and LDS size (asked once).
-  static int per_cu = -1;
-  static size_t per_cu_lds = 0;
-  if (per_cu < 0 || per_cu_lds != lds) {
-    if (lds > 64 * 1024) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    int n = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kStateThreads, lds);
-    if (e != hipSuccess) return e;
-    per_cu = n;
-    per_cu_lds = lds;
-  }
-  static int ncu = 0;
-  if (ncu == 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-  }
   const long grid = d.nblocks * d.H;
-  if (grid > (long)per_cu * ncu) return hipSuccess;  // not all resident: the caller runs two launches
   const uint16_t* Xp = reinterpret_cast<const uint16_t*>(X);
   const uint16_t* Bp = reinterpret_cast<const uint16_t*>(B);
   int4* table = ws.table;
@@ -479,14 +481,28 @@ static hipError_t launch_chain_t(const FwdDims& d, const void* X, const void* B,
   int nseq = sa.cu ? d.num_seqs : d.batch;
   void* args[] = {&Xp, &Bp, &table, &btable, &cs, &ck, &bstates, &bdecay, &H, &G, &Q, &Gs, &sac, &start, &fin, &ini,
                   &nseq};
-  hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)grid),
-                                            dim3(kStateThreads), args, (unsigned)lds, stream);
+  e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)grid), dim3(kStateThreads), args,
+                                 (unsigned)lds, stream);
   if (e == hipSuccess) *launched = true;
   return e;
 }
 
 bool chunk_state_chain_fits(const FwdDims& d) {
   return d.bf16 && (d.P * d.N == 8192 || d.P * d.N == 4096 || d.P * d.N == 16384) && d.P >= 32 && d.N >= 64;
+}
+
+hipError_t chunk_state_chain_cooperative(const FwdDims& d, bool* cooperative) {
+  *cooperative = false;
+  if (!chunk_state_chain_fits(d)) return hipSuccess;
+  switch (d.P * 1000 + d.N) {
+    case 32064: return chain_fits_device<32, 64>(d, cooperative);
+    case 32128: return chain_fits_device<32, 128>(d, cooperative);
+    case 64064: return chain_fits_device<64, 64>(d, cooperative);
+    case 64128: return chain_fits_device<64, 128>(d, cooperative);
+    case 128064: return chain_fits_device<128, 64>(d, cooperative);
+    case 128128: return chain_fits_device<128, 128>(d, cooperative);
+    default: return hipSuccess;
+  }
 }
 
 hipError_t launch_chunk_state_chain(const FwdDims& d, const void* X, const void* B, const Workspace& ws,

@@ -76,6 +76,9 @@ hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float
 hipError_t launch_chunk_state_chain(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
                                     hipStream_t stream, const SegArgs& sa, const float* init, float* final_state,
                                     bool* launched);
+// Whether launch_chunk_state_chain would launch the cooperative kernel for
+// these dimensions on the current device (on a stream not being captured).
+hipError_t chunk_state_chain_cooperative(const FwdDims& d, bool* cooperative);
 hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                              const Workspace& ws, hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});
 hipError_t launch_ssd_step(int batch, int H, int G, int P, int N, int bf16, float* state,

@@ -7,14 +7,22 @@ Tolerances (written here once, used by every parity test):
     with the output scaled by its RMS).
 Both are applied separately to Y and to the final states.
 
+Heavy-tailed bf16 outputs (assert_close_rounded): where |ref_i| reaches far
+above rms(ref), rounding even the exact value to bf16 once moves it by up to
+2^-8 |ref_i|, beyond 5e-2 rms(ref) once |ref_i| > 12.8 rms(ref); such outputs
+take the plain bar with that rounding added: |d_i| <= 5e-2 rms(ref) + 2^-8 |ref_i|.
+
 Gated outputs (the Mamba-2 block's y = u * silu(z), u = SSM output + skip):
 the gate scales each element by s_i = silu(z_i), which stretches the tails of
 the output (|y_i| far above rms(y) wherever |s_i| is large), so the output's own
 bf16 rounding alone can exceed 5e-2 rms(y). The unit scale of element i is
-carried through the gate instead: with r = rms(u_ref),
-  * bf16: ||d||_2 / ||ref||_2 <= 2e-2 and max_i |d_i| / (|s_i| r + |ref_i|) <= 5e-2;
-  * fp32: max_i |d_i| / (|s_i| r + |ref_i|) <= 1e-4.
-With s = 1 this is the ungated bar with an allowance relative to |ref_i|.
+carried through the gate instead, plus the output's own rounding: with
+r = rms(u_ref),
+  * bf16: ||d||_2 / ||ref||_2 <= 2e-2 and |d_i| <= 5e-2 |s_i| r + 2^-8 |ref_i|
+    (2^-8 is the unit roundoff of bf16: the most that rounding the exact
+    output once can move it);
+  * fp32: |d_i| <= 1e-4 max(|s_i| r, |ref_i|, rms(ref)) (the plain fp32 bar's
+    floor at rms(ref) kept).
 """
 from __future__ import annotations
 
@@ -50,6 +58,30 @@ def assert_close(gpu, ref, dtype: str, what: str = ""):
     return e
 
 
+def rounded_errors(gpu, ref):
+    """The plain bar with the output's own rounding added: max_rounded is the
+    largest |d_i| / (5e-2 rms(ref) + 2^-8 |ref_i|) (<= 1 passes)."""
+    g = np.asarray(gpu, np.float64).ravel()
+    r = np.asarray(ref, np.float64).ravel()
+    d = np.abs(g - r)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    return dict(errors(g, r), max_rounded=float(np.max(d / (BF16_MAXABS_UNIT * rms + (2.0 ** -8) * np.abs(r) + 1e-300)))
+                if d.size else 0.0)
+
+
+def assert_close_rounded(gpu, ref, dtype: str, what: str = ""):
+    """Heavy-tailed bf16 outputs (|ref_i| far above 12.8 rms(ref), where rounding
+    the exact value once can move it by more than 5e-2 rms): the plain bar plus
+    the output's own rounding, |d_i| <= 5e-2 rms(ref) + 2^-8 |ref_i|, and
+    rel-L2 <= 2e-2. fp32 outputs take the plain fp32 bar."""
+    if dtype == "fp32":
+        return assert_close(gpu, ref, dtype, what)
+    e = rounded_errors(gpu, ref)
+    assert e["finite"], f"{what}: non-finite values"
+    assert e["rel_l2"] <= BF16_RELL2 and e["max_rounded"] <= 1.0, f"{what}: {e}"
+    return e
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").double().numpy()
 
@@ -58,17 +90,26 @@ def dtype_name(t: torch.Tensor) -> str:
     return "fp32" if t.dtype == torch.float32 else "bf16"
 
 
+BF16_UNIT_ROUNDOFF = 2.0 ** -8
+
+
 def gated_errors(gpu, ref, ref_ungated, s):
+    """max_gated is the largest |d_i| over its allowance, in units of the bar:
+    bf16 allowance 5e-2 |s_i| r + 2^-8 |ref_i| (<= 1 passes); fp32 allowance
+    1e-4 max(|s_i| r, |ref_i|, rms(ref)) (<= 1 passes)."""
     g = np.asarray(gpu, np.float64).ravel()
     r = np.asarray(ref, np.float64).ravel()
     u = np.asarray(ref_ungated, np.float64).ravel()
     sc = np.abs(np.asarray(s, np.float64).ravel())
     d = np.abs(g - r)
     ru = float(np.sqrt(np.mean(u * u))) if u.size else 0.0
-    den = sc * ru + np.abs(r) + 1e-30
+    bf = BF16_MAXABS_UNIT * sc * ru + BF16_UNIT_ROUNDOFF * np.abs(r) + 1e-300
+    rr = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    f32 = FP32_MAXREL * np.maximum(np.maximum(sc * ru, np.abs(r)), rr) + 1e-300
     return dict(
         rel_l2=float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)),
-        max_gated=float(np.max(d / den)) if d.size else 0.0,
+        max_gated=float(np.max(d / bf)) if d.size else 0.0,
+        max_gated_f32=float(np.max(d / f32)) if d.size else 0.0,
         finite=bool(np.all(np.isfinite(g))),
     )
 
@@ -77,7 +118,7 @@ def assert_close_gated(gpu, ref, ref_ungated, s, dtype: str, what: str = ""):
     e = gated_errors(gpu, ref, ref_ungated, s)
     assert e["finite"], f"{what}: non-finite values"
     if dtype == "fp32":
-        assert e["max_gated"] <= FP32_MAXREL, f"{what}: {e}"
+        assert e["max_gated_f32"] <= 1.0, f"{what}: {e}"
     else:
-        assert e["rel_l2"] <= BF16_RELL2 and e["max_gated"] <= BF16_MAXABS_UNIT, f"{what}: {e}"
+        assert e["rel_l2"] <= BF16_RELL2 and e["max_gated"] <= 1.0, f"{what}: {e}"
     return e

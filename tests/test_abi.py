@@ -306,3 +306,151 @@ def test_bwd_mamba2_validates():
     assert L.ssd_bwd_mamba2(*a) == WS_SMALL
     odd = shape(seqlen=512, nheads=8, headdim=18)
     assert L.ssd_bwd_mamba2_workspace_bytes(ctypes.byref(odd), 64, 0, ctypes.byref(n)) != OK
+
+
+def test_step_rejects_unaligned_state():
+    L = ssd.lib()
+    sh = shape(batch=64, nheads=80)
+    odd = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    assert L.ssd_step(odd, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(sh), None) == INVALID
+    assert L.ssd_step_mamba2(odd, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, FAKE, ctypes.byref(sh),
+                             None) == INVALID
+
+
+# ---- the binding's own checks: every tensor against the shape it implies ----
+# Host tensors are used throughout: structure (shape, dtype, contiguity) is
+# checked before the device, so each case below must be refused for the
+# mismatch itself, and the well-formed call only for living on the host.
+
+def _fwd_args(b=1, T=64, H=4, P=16, G=2, N=32, dt=None):
+    import torch
+    dt = dt or torch.bfloat16
+    return dict(X=torch.zeros(b, T, H, P, dtype=dt), log_a=torch.zeros(b, T, H), B=torch.zeros(b, T, G, N, dtype=dt),
+                C=torch.zeros(b, T, G, N, dtype=dt))
+
+
+def _refused(fn, what, **kw):
+    with pytest.raises(ValueError) as e:
+        fn(**kw)
+    msg = str(e.value)
+    assert what in msg and "device tensor" not in msg, msg
+
+
+def _fwd_cases():
+    import torch
+    bf = torch.bfloat16
+    return {
+        "B rows": (dict(B=torch.zeros(1, 63, 2, 32, dtype=bf)), "B"),
+        "C shape": (dict(C=torch.zeros(1, 64, 2, 16, dtype=bf)), "C"),
+        "C groups": (dict(C=torch.zeros(1, 64, 1, 32, dtype=bf)), "C"),
+        "C dtype": (dict(C=torch.zeros(1, 64, 2, 32)), "C"),
+        "log_a shape": (dict(log_a=torch.zeros(1, 64, 2)), "log_a"),
+        "log_a dtype": (dict(log_a=torch.zeros(1, 64, 4, dtype=bf)), "log_a"),
+        "log_a heads": (dict(log_a=torch.zeros(1, 64, 4, 1)), "log_a"),
+        "groups": (dict(B=torch.zeros(1, 64, 3, 32, dtype=bf), C=torch.zeros(1, 64, 3, 32, dtype=bf)), "ngroups"),
+        "X strided": (dict(X=torch.zeros(1, 64, 4, 32, dtype=bf)[..., ::2]), "X"),
+        "Y shape": (dict(Y=torch.zeros(1, 64, 4, 8, dtype=bf)), "Y"),
+        "Y dtype": (dict(Y=torch.zeros(1, 64, 4, 16)), "Y"),
+        "final shape": (dict(final_state=torch.zeros(1, 4, 32, 16)), "final_state"),
+        "final dtype": (dict(final_state=torch.zeros(1, 4, 16, 32, dtype=bf)), "final_state"),
+        "initial shape": (dict(initial_state=torch.zeros(2, 4, 16, 32)), "initial_state"),
+        "cu dtype": (dict(cu_seqlens=torch.tensor([0, 64], dtype=torch.int64)), "cu_seqlens"),
+        "cu strided": (dict(cu_seqlens=torch.tensor([0, 9, 32, 50, 64], dtype=torch.int32)[::2]), "cu_seqlens"),
+    }
+
+
+@pytest.mark.parametrize("case", sorted(_fwd_cases()))
+def test_binding_fwd_refuses_mismatched_tensors(case):
+    kw, what = _fwd_cases()[case]
+    args = _fwd_args()
+    args.update(kw)
+    _refused(ssd.fwd, what, chunk=32, **args)
+
+
+def test_binding_fwd_refuses_batch_with_cu_seqlens():
+    import torch
+    args = _fwd_args(b=2)
+    _refused(ssd.fwd, "batch 1", chunk=32, cu_seqlens=torch.tensor([0, 64], dtype=torch.int32), **args)
+
+
+def test_binding_fwd_well_formed_host_call_is_refused_for_the_device_only():
+    with pytest.raises(ValueError, match="device tensor"):
+        ssd.fwd(chunk=32, **_fwd_args())
+
+
+def test_binding_workspace_must_match_the_call():
+    import torch
+    a = _fwd_args()
+    other = ssd.make_shape(torch.zeros(1, 128, 4, 16, dtype=torch.bfloat16), a["B"])
+    ws = ssd.Workspace(other, 32, "cpu", 1)
+    _refused(ssd.fwd, "workspace", chunk=32, workspace=ws, **a)
+    sh = ssd.make_shape(a["X"], a["B"])
+    ws = ssd.Workspace(sh, 32, "cpu", 1)
+    _refused(ssd.fwd, "workspace", chunk=64, workspace=ws, **a)
+
+
+def test_binding_stage_wrappers_check_tensors():
+    import torch
+    a = _fwd_args()
+    sh = ssd.make_shape(a["X"], a["B"])
+    ws = ssd.Workspace(sh, 32, "cpu", 1)
+    _refused(lambda: ssd.chunk_cumsum(torch.zeros(1, 64, 2), None, sh, ws), "log_a")
+    _refused(lambda: ssd.chunk_state(a["X"], torch.zeros(1, 64, 2, 16, dtype=torch.bfloat16), None, sh, ws), "B")
+    _refused(lambda: ssd.chunk_scan(a["X"], a["B"], a["C"], None, torch.zeros(1, 64, 4, 16), sh, ws), "Y")
+    _refused(lambda: ssd.state_passing(None, torch.zeros(1, 4, 32, 16), sh, ws), "final_state")
+    _refused(lambda: ssd.chunk_cumsum(a["log_a"], torch.tensor([0, 64], dtype=torch.int32), sh, ws), "cu_seqlens")
+    other = ssd.make_shape(torch.zeros(1, 64, 4, 16, dtype=torch.bfloat16), torch.zeros(1, 64, 1, 32))
+    _refused(lambda: ssd.chunk_cumsum(a["log_a"], None, other, ws), "workspace")
+
+
+def _step_args(b=3, H=4, P=16, G=2, N=32):
+    import torch
+    bf = torch.bfloat16
+    return dict(state=torch.zeros(b, H, P, N), x=torch.zeros(b, H, P, dtype=bf), log_a=torch.zeros(b, H),
+                B=torch.zeros(b, G, N, dtype=bf), C=torch.zeros(b, G, N, dtype=bf))
+
+
+@pytest.mark.parametrize("kw,what", [
+    (dict(state=("zeros", (3, 4, 32, 16))), "state"),
+    (dict(state=("zeros_bf", (3, 4, 16, 32))), "state"),
+    (dict(log_a=("zeros", (3, 2))), "log_a"),
+    (dict(B=("zeros_bf", (2, 2, 32))), "B"),
+    (dict(C=("zeros_bf", (3, 1, 32))), "C"),
+    (dict(C=("zeros", (3, 2, 32))), "C"),
+    (dict(y=("zeros_bf", (3, 4, 8))), "y"),
+], ids=["state-shape", "state-dtype", "log_a", "B-rows", "C-groups", "C-dtype", "y"])
+def test_binding_step_refuses_mismatched_tensors(kw, what):
+    import torch
+    make = dict(zeros=lambda s: torch.zeros(*s), zeros_bf=lambda s: torch.zeros(*s, dtype=torch.bfloat16))
+    args = _step_args()
+    for k, (f, s) in kw.items():
+        args[k] = make[f](s)
+    _refused(ssd.step, what, **args)
+
+
+def test_binding_step_mamba2_and_bwd_check_tensors():
+    import torch
+    a = _step_args()
+    H = 4
+    _refused(ssd.step_mamba2, "dt", state=a["state"], x=a["x"], dt=torch.zeros(3, 2), A_log=torch.zeros(H),
+             B=a["B"], C=a["C"])
+    _refused(ssd.step_mamba2, "z", state=a["state"], x=a["x"], dt=torch.zeros(3, H), A_log=torch.zeros(H),
+             B=a["B"], C=a["C"], z=torch.zeros(3, H, 16))
+    f = _fwd_args()
+    _refused(ssd.bwd, "dY", dY=torch.zeros(1, 64, 4, 8, dtype=torch.bfloat16), chunk=32, **f)
+    _refused(ssd.bwd, "dfinal_state", dY=torch.zeros_like(f["X"]), dfinal_state=torch.zeros(1, 4, 32, 16), chunk=32,
+             **f)
+    m = dict(X=f["X"], B=f["B"], C=f["C"], dt=torch.zeros(1, 64, H), A_log=torch.zeros(H))
+    _refused(ssd.fwd_mamba2, "A_log", **dict(m, A_log=torch.zeros(H + 1)), chunk=32)
+    _refused(ssd.fwd_mamba2, "D", **m, D=torch.zeros(H, dtype=torch.bfloat16), chunk=32)
+    _refused(ssd.bwd_mamba2, "dY", **m, dY=torch.zeros(1, 64, 4, 16), chunk=32)
+
+
+def test_state_chain_cooperative_query_validates():
+    L = ssd.lib()
+    r = ctypes.c_int32(7)
+    assert L.ssd_state_chain_cooperative(ctypes.byref(shape()), 128, 0, None) == INVALID
+    assert L.ssd_state_chain_cooperative(None, 128, 0, ctypes.byref(r)) == INVALID
+    assert L.ssd_state_chain_cooperative(ctypes.byref(shape(headdim=48)), 128, 0, ctypes.byref(r)) == UNSUPPORTED
+    assert L.ssd_state_chain_cooperative(ctypes.byref(shape()), 128, 3, ctypes.byref(r)) == UNSUPPORTED
+    assert r.value == 7   # untouched on error

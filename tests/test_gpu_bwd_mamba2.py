@@ -12,9 +12,26 @@ the two outputs that are an element-wise scale of a recurrence result: dz = s v
 (s = dY silu'(z), v the call's output before the gate) with v as the unscaled
 reference, and dX = dt' dx~ + D dv (dt' per token, spanning two orders of
 magnitude) with dx~ as the unscaled reference; the unit scale is carried
-through the scale factor, as for the gated forward output. dB and dC, sums over
-heads of terms that carry those scales, take the same functional with s = 1
-(the plain bar with an allowance relative to |ref_i|).
+through the scale factor, as for the gated forward output, and the only
+allowance relative to the value is the output's own bf16 rounding. Every other
+gradient takes the plain bar.
+
+dB and dC take the plain bar in two parts. The call hands x dt' and dY silu(z)
+to the recurrence's backward in the input dtype, rounded once each (the pages'
+SSD call takes its input already discretised, in one dtype), and the two
+gradients carry that rounding at each token's own scale, which spans more than
+an order of magnitude of rms: the fp64 oracle fed those same stored values
+lands 0.068 (dB) and 0.080 (dC) of rms from the exact result at the headline
+size, over the 5e-2 max-abs bar, with no GPU arithmetic involved. Their
+largest elements also reach 17 rms, where the output's own bf16 rounding
+alone can exceed 5e-2 rms (the exact dB and dC rounded once measure 0.060 and
+0.062). So
+  * rel-L2 <= 2e-2 against the exact oracle, and
+  * against the oracle's reverse mode on the stored values (x dt' and
+    dY silu(z) rounded to the input dtype by the test itself, from the same
+    inputs), rel-L2 <= 2e-2 and |d_i| <= 5e-2 rms + 2^-8 |ref_i|: the plain bar
+    plus the output's own rounding, so what remains is the error of the
+    kernels' own arithmetic.
 """
 import sys
 
@@ -25,7 +42,8 @@ import torch
 import ssd_chunked_scan_fwd_amd as ssd
 from ssd_chunked_scan_fwd_amd import synth
 from oracle import oracle
-from parity import assert_close, assert_close_gated, dtype_name, to_f64
+from parity import (BF16_RELL2, FP32_MAXREL, assert_close, assert_close_gated, assert_close_rounded, dtype_name,
+                    errors, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,10 +76,27 @@ def _dfinal(d, nseq, seed, T1=120):
     return torch.from_numpy(g["dinit"]).float()
 
 
-def compare(g, r, X, dt, dtb, A_log, D, z, B, C, dY, cu, what, keys=None):
+def _stored(a, like):
+    """`a` rounded once to the dtype of tensor `like` (round to nearest even), in fp64."""
+    return torch.from_numpy(np.asarray(a, np.float64)).to(like.dtype).double().numpy()
+
+
+def stored_reference(X, dt, dtb, A_log, z, B, C, dY, dfinal, cu, init=None):
+    """The oracle's reverse mode of the recurrence on the values the call hands it:
+    x dt' and (with a gate) dY silu(z), each rounded once to the input dtype, and
+    log a = dt' A."""
+    dtp, la = oracle.mamba2_discretize(_f(dt), _f(dtb), _f(A_log))
+    xs = _stored(_f(X) * dtp[..., None], X)
+    dv = _f(dY) if z is None else _stored(_f(dY) * oracle.silu(_f(z)), X)
+    return oracle.backward(xs, la, _f(B), _f(C), dv, dfinal=_f(dfinal), init=_f(init),
+                           cu_seqlens=None if cu is None else cu.numpy())
+
+
+def compare(g, r, X, dt, dtb, A_log, D, z, B, C, dY, cu, what, keys=None, dfinal=None, init=None):
     """The GPU gradients `g` against the oracle's `r` on the same inputs."""
     dt_name = dtype_name(X)
     errs = {}
+    rs = None
     for k in keys or ("dX", "ddt", "dA_log", "dB", "dC", "dinit", "dD", "dz", "ddt_bias"):
         if r.get(k) is None:
             assert g[k] is None, k
@@ -88,15 +123,19 @@ def compare(g, r, X, dt, dtb, A_log, D, z, B, C, dY, cu, what, keys=None):
             errs[k]["max_unit"] = errs[k]["max_gated"]
             continue
         if k in ("dB", "dC"):
-            # Sums over heads of terms carrying x dt' (dt' per token) and dY silu(z)
-            # (per element): heavy-tailed, so the bar takes an allowance relative
-            # to |ref_i| as well (the gated functional with s = 1).
-            errs[k] = assert_close_gated(_f(g[k]), r[k], r[k], np.ones_like(r[k]), dt_name, f"{what} {k}")
-            errs[k]["max_unit"] = errs[k]["max_gated"]
+            e = errors(_f(g[k]), r[k])
+            lim = FP32_MAXREL if dt_name == "fp32" else BF16_RELL2
+            assert e["finite"] and e["rel_l2"] <= lim, f"{what} {k} against the exact oracle: {e}"
+            if rs is None:
+                rs = stored_reference(X, dt, dtb, A_log, z, B, C, dY, dfinal, cu, init)
+            es = assert_close_rounded(_f(g[k]), rs[k], dt_name, f"{what} {k} against the stored-value reference")
+            errs[k] = dict(e, max_unit_stored=es["max_unit"], rel_l2_stored=es["rel_l2"])
             continue
         errs[k] = assert_close(_f(g[k]), r[k], dt_name, f"{what} {k}")
-    say(f"[bwd-m2] {what}: " + " ".join(f"{k} rel_l2={e['rel_l2']:.2e} max_unit={e['max_unit']:.3f}"
-                                        for k, e in errs.items()))
+    say(f"[bwd-m2] {what}: " + " ".join(
+        f"{k} rel_l2={e['rel_l2']:.2e} max_unit={e['max_unit']:.3f}"
+        + (f" (stored-value reference: rel_l2={e['rel_l2_stored']:.2e} max_unit={e['max_unit_stored']:.3f})"
+           if "max_unit_stored" in e else "") for k, e in errs.items()))
     return errs
 
 
@@ -120,7 +159,7 @@ def check(d, Q, what, gate=True, skip=True, bias=True, with_final=True, gs=0, se
     torch.cuda.synchronize()
     r = oracle.mamba2_backward(_f(X), _f(d["dt"]), _f(dtb), _f(d["A_log"]), _f(D), _f(z), _f(d["B"]), _f(d["C"]),
                                _f(ct["dY"]), dfinal=_f(dfin), cu_seqlens=None if cu is None else cu.numpy())
-    compare(g, r, X, d["dt"], dtb, d["A_log"], D, z, d["B"], d["C"], ct["dY"], cu, what)
+    compare(g, r, X, d["dt"], dtb, d["A_log"], D, z, d["B"], d["C"], ct["dY"], cu, what, dfinal=dfin)
     return g
 
 
@@ -188,17 +227,32 @@ def test_bwd_mamba2_headline_sampled_heads():
     gh = {"dX": hs(g["dX"]), "ddt": g["ddt"][:, :, heads], "dz": hs(g["dz"]), "dD": g["dD"][heads],
           "ddt_bias": g["ddt_bias"][heads], "dA_log": g["dA_log"][heads], "dB": g_s["dB"], "dC": g_s["dC"]}
     compare(gh, r, what="headline sampled heads", keys=("dX", "ddt", "dz", "dD", "ddt_bias", "dB", "dC"), **sel)
-    # d A_log = A sum_t dt'_t d log a_t sums 16384 terms that cancel to 1/217 and 1/3251 of their
-    # absolute sum on these two heads, so a bar relative to the result is not meaningful here (the
-    # smaller cases above hold it to the plain bar). Each term meeting the bf16 bar bounds the sum's
-    # error by 2e-2 of the terms' absolute sum, which the oracle gives with d log a from the
-    # recurrence's reverse mode on x dt', log a = dt' A and dv = dY silu(z).
-    dtp, la_ = oracle.mamba2_discretize(_f(sel["dt"]), _f(sel["dtb"]), _f(sel["A_log"]))
-    zz = _f(sel["z"])
-    dv = _f(sel["dY"]) * zz / (1.0 + np.exp(-zz))
-    dla = oracle.backward(_f(sel["X"]) * dtp[..., None], la_, _f(B), _f(C), dv)["dlog_a"]
-    A = -np.exp(_f(sel["A_log"]))
-    bound = 2e-2 * np.abs(A) * np.abs(dtp * dla).sum(axis=(0, 1))
-    err = np.abs(_f(gh["dA_log"]) - r["dA_log"])
-    say(f"[bwd-m2] headline sampled heads dA_log: error {err} against the summation bound {bound}")
-    assert np.all(np.isfinite(_f(gh["dA_log"]))) and np.all(err <= bound), (err, bound)
+    # d A_log = A sum_t dt'_t d log a_t sums 16384 terms that cancel to a small fraction of their
+    # absolute sum here, so its bf16 value is not held to a bar at this size; the fp32 test
+    # below holds it to a bar relative to its value at the same length.
+    say(f"[bwd-m2] headline sampled heads dA_log: gpu {_f(gh['dA_log'])} oracle {r['dA_log']}")
+
+
+def test_bwd_mamba2_full_length_fp32():
+    """The Mamba-2 call's backward over a full-length sequence (T = 16384, P = 64, N = 128)
+    on the fp32 path, two heads, chunk 64, gate, skip and bias on: every gradient against the
+    oracle at the fp32 bar, and d A_log = A sum_t dt'_t d log a_t, a sum of 16384 terms that
+    cancel, held to 2e-2 of its own value and to its sign (a zero, a wrong sign or a dropped
+    factor fails)."""
+    d = synth.make_mamba2_inputs(1, 16384, 2, 64, 128, 1, torch.float32, seed=5400)
+    X, B, C = d["X"], d["B"], d["C"]
+    ct = synth.make_cotangents(1, 16384, 2, 64, 128, 1, dtype=torch.float32, seed=25)
+    say("[bwd-m2] full length fp32: X(1, 16384, 2, 64) N=128 Q=64")
+    dev = lambda t: t.cuda()
+    g = ssd.bwd_mamba2(dev(X), dev(d["dt"]), dev(d["A_log"]), dev(B), dev(C), dev(ct["dY"]),
+                       dt_bias=dev(d["dt_bias"]), D=dev(d["D"]), z=dev(d["z"]), chunk=64)
+    torch.cuda.synchronize()
+    r = oracle.mamba2_backward(_f(X), _f(d["dt"]), _f(d["dt_bias"]), _f(d["A_log"]), _f(d["D"]), _f(d["z"]), _f(B),
+                               _f(C), _f(ct["dY"]))
+    compare(g, r, X, d["dt"], d["dt_bias"], d["A_log"], d["D"], d["z"], B, C, ct["dY"], None, "full length fp32",
+            keys=("dX", "ddt", "dz", "dD", "ddt_bias", "dB", "dC"))
+    got, ref = _f(g["dA_log"]), r["dA_log"]
+    err = np.abs(got - ref)
+    say(f"[bwd-m2] full length fp32 dA_log: gpu {got} oracle {ref} relative error {err / np.abs(ref)}")
+    assert np.all(np.isfinite(got)) and np.all(np.sign(got) == np.sign(ref)), (got, ref)
+    assert np.all(err <= 2e-2 * np.abs(ref)), (got, ref)
