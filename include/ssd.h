@@ -198,6 +198,27 @@ ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void*
                    void* stream);
 
 /*
+ * Forward pass with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): ssd_fwd with the library's own scratch as the
+ * workspace. The scratch is one static device array of
+ * SSD_NOALLOC_SCRATCH_BYTES per GPU, allocated when the library's code object
+ * loads and held until the process ends; nothing is allocated or freed per
+ * call. Calls whose ssd_fwd_workspace_bytes(shape, chunk, 0) exceeds it return
+ * SSD_ERR_WORKSPACE_TOO_SMALL before any HIP call (the headline shape, 16384
+ * tokens x 32 heads x 64 x 128, needs 27.4 MB; larger calls use ssd_fwd). Every
+ * call on one GPU uses that GPU's array: calls that overlap on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller. Each
+ * call writes every part of the scratch it reads, so nothing needs clearing.
+ * Arguments, results and other errors are those of ssd_fwd (SSD_ERR_HIP also
+ * when the scratch's address cannot be obtained).
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)
+ssd_status ssd_fwd_noalloc(const void* X, const float* log_a, const void* B, const void* C,
+                           const int32_t* cu_seqlens, int32_t chunk, void* Y, float* final_state,
+                           const ssd_shape* shape, void* stream);
+
+/*
  * Forward pass with an initial state and an explicit state block
  * (state_block <= 0: the default).
  *   initial_state  device, fp32 [batch or num_seqs, nheads, headdim, dstate]

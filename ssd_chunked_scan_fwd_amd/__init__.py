@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     default_state_block,
     fwd,
     fwd_mamba2,
+    fwd_noalloc,
     layout,
     lib,
     make_shape,
@@ -33,7 +34,7 @@ from .binding import (  # noqa: F401
 
 __all__ = [
     "synth",
-    "fwd", "step", "fwd_mamba2", "step_mamba2",
+    "fwd", "step", "fwd_mamba2", "step_mamba2", "fwd_noalloc",
     "bwd", "bwd_workspace_bytes", "bwd_mamba2", "bwd_mamba2_workspace_bytes",
     "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan",
     "set_state_chain", "state_chain_cooperative", "Workspace", "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib",

@@ -27,7 +27,7 @@ EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "s
            "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
            "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2",
            "ssd_bwd_workspace_bytes", "ssd_bwd", "ssd_set_state_chain", "ssd_state_chain_cooperative",
-           "ssd_bwd_mamba2_workspace_bytes", "ssd_bwd_mamba2")
+           "ssd_bwd_mamba2_workspace_bytes", "ssd_bwd_mamba2", "ssd_fwd_noalloc")
 
 
 class SSDError(RuntimeError):
@@ -75,6 +75,8 @@ def lib():
         L.ssd_fwd_workspace_bytes.argtypes = [shp, i32, i32, ctypes.POINTER(sz)]
         L.ssd_fwd.restype = ctypes.c_int
         L.ssd_fwd.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, shp, vp, sz, vp]
+        L.ssd_fwd_noalloc.restype = ctypes.c_int
+        L.ssd_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, shp, vp]
         L.ssd_fwd_ex.restype = ctypes.c_int
         L.ssd_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, shp, vp, sz, vp]
         L.ssd_chunk_cumsum.restype = ctypes.c_int
@@ -323,6 +325,26 @@ def _stage_check(shape: Shape, ws: Workspace, X=None, log_a=None, B=None, C=None
     _expect_all([(X, "X", (b, T, H, P), dt, 0), (Y, "Y", (b, T, H, P), dt, 0), (B, "B", (b, T, G, N), dt, 0),
                  (C, "C", (b, T, G, N), dt, 0), (log_a, "log_a", (b, T, H), torch.float32, 0),
                  (cu_seqlens, "cu_seqlens", (want_cu,) if want_cu else None, torch.int32, 0)], ws.buffer.device)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SSD_NOALLOC_SCRATCH_BYTES
+
+
+def fwd_noalloc(X: torch.Tensor, log_a: torch.Tensor, B: torch.Tensor, C: torch.Tensor, Y: torch.Tensor,
+                final_state: Optional[torch.Tensor] = None, cu_seqlens: Optional[torch.Tensor] = None,
+                chunk: int = 128) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """ssd_fwd_noalloc: the forward pass in the library's static per-GPU scratch (no
+    workspace; nothing allocated here either, so Y, and final_state when wanted,
+    are the caller's). Calls that overlap on one GPU race on that scratch."""
+    specs = _check_inputs(X, log_a, B, C, cu_seqlens)
+    shape = make_shape(X, B, cu_seqlens)
+    if Y is None:
+        raise ValueError("Y is required")
+    _expect_all(specs + [(Y, "Y", tuple(X.shape), X.dtype, 0), _state_spec(final_state, shape, "final_state")],
+                X.device)
+    _call("ssd_fwd_noalloc", _ptr(X), _ptr(log_a), _ptr(B), _ptr(C), _ptr(cu_seqlens), int(chunk), _ptr(Y),
+          _ptr(final_state), ctypes.byref(shape), _stream(X.device))
+    return Y, final_state
 
 
 def chunk_cumsum(log_a, cu_seqlens, shape: Shape, ws: Workspace):

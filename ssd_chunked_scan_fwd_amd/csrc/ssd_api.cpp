@@ -10,6 +10,7 @@
 #include <cstdint>
 
 #include <atomic>
+#include <mutex>
 
 #include "ssd.h"
 #include "ssd_launch.h"
@@ -402,6 +403,65 @@ ssd_status ssd_fwd(const void* X, const float* log_a, const void* B, const void*
                    size_t workspace_bytes, void* stream) {
   return ssd_fwd_ex(X, log_a, B, C, cu_seqlens, nullptr, chunk, 0, Y, final_state, shape, workspace,
                     workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// Scratch of ssd_fwd_noalloc: one array per GPU, allocated when the code
+// object loads and held until the process ends. In host code `scratch` only
+// names the symbol; its device address on each GPU comes from
+// hipGetSymbolAddress, asked once per device with that device current and kept
+// in g_scratch_ptr. Kernels receive that address, never the name.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device.
+hipError_t scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_fwd_noalloc(const void* X, const float* log_a, const void* B, const void* C,
+                           const int32_t* cu_seqlens, int32_t chunk, void* Y, float* final_state,
+                           const ssd_shape* shape, void* stream) {
+  // Host-side checks first, as in ssd_fwd: a workspace of the scratch's size at
+  // a stand-in address (never dereferenced) makes prepare() check the shape,
+  // pointers and alignment, and report a layout larger than the scratch.
+  Prepared pp;
+  void* const probe = reinterpret_cast<void*>((uintptr_t)256);
+  ssd_status st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, 0, shape, probe, SSD_NOALLOC_SCRATCH_BYTES,
+                          &pp, false, nullptr, final_state);
+  if (st != SSD_OK) return st;
+  void* ws = nullptr;
+  if (scratch_ptr(&ws) != hipSuccess) return SSD_ERR_HIP;
+  ssd_layout L;
+  st = make_layout(shape, cu_seqlens, chunk, pp.d.state_block, &L);
+  if (st != SSD_OK) return st;
+  st = prepare(kAll, X, log_a, B, C, Y, cu_seqlens, chunk, pp.d.state_block, shape, ws, L.total_bytes, &pp, false,
+               nullptr, final_state);
+  if (st != SSD_OK) return st;
+  return hip_status(run_forward(pp, X, log_a, B, C, cu_seqlens, nullptr, Y, final_state, (hipStream_t)stream));
 }
 
 ssd_status ssd_bwd_workspace_bytes(const ssd_shape* shape, int32_t chunk, int32_t state_block, size_t* bytes) {

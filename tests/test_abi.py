@@ -454,3 +454,30 @@ def test_state_chain_cooperative_query_validates():
     assert L.ssd_state_chain_cooperative(ctypes.byref(shape(headdim=48)), 128, 0, ctypes.byref(r)) == UNSUPPORTED
     assert L.ssd_state_chain_cooperative(ctypes.byref(shape()), 128, 3, ctypes.byref(r)) == UNSUPPORTED
     assert r.value == 7   # untouched on error
+
+
+def test_fwd_noalloc_validates_and_bounds_its_scratch():
+    """ssd_fwd_noalloc checks its arguments like ssd_fwd, and refuses a call whose
+    workspace would exceed the static scratch, all before any HIP call."""
+    L = ssd.lib()
+    sh = shape()
+    _, need = ws_bytes(sh, 128, 0)
+    assert need <= binding.NOALLOC_SCRATCH_BYTES   # the headline shape fits
+    args = [FAKE, FAKE, FAKE, FAKE, None, 128, FAKE, FAKE, ctypes.byref(sh), None]
+    for i in (0, 1, 2, 3, 6, 8):   # X, log_a, B, C, Y, shape
+        a = list(args)
+        a[i] = None
+        assert L.ssd_fwd_noalloc(*a) == INVALID, i
+    a = list(args)
+    a[5] = 96
+    assert L.ssd_fwd_noalloc(*a) == UNSUPPORTED
+    odd = ctypes.c_void_p(0x1008)
+    a = list(args)
+    a[7] = odd   # final_state moves in 16-byte pieces
+    assert L.ssd_fwd_noalloc(*a) == INVALID
+    big = shape(seqlen=32768, nheads=80, num_seqs=7)   # the packed H = 80 layer: ~175 MB of workspace
+    _, need_big = ws_bytes(big, 128, 0)
+    assert need_big > binding.NOALLOC_SCRATCH_BYTES
+    assert L.ssd_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, None, ctypes.byref(big), None) == WS_SMALL
+    hdr = open(HEADER).read()
+    assert "#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr and binding.NOALLOC_SCRATCH_BYTES == 64 << 20
