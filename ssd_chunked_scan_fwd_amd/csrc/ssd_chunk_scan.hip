@@ -66,6 +66,7 @@ struct ScanCfg {
   static constexpr int BP = lds_pitch(N);   // B rows
   static constexpr int XP = lds_pitch(P);   // X rows, weighted X rows
   static constexpr int HP = lds_pitch(P);   // transposed state rows [N][HP] (rows stored at perm32(n))
+  static_assert(HP >= P + kHalfShift, "the half shift stays inside the row padding");
   static constexpr int TP = P / 16, TN = N / 16, NB = N / 32;
   static constexpr int WN = TN < 4 ? TN : 4;
   static constexpr int WP = (kScanWaves / WN) < TP ? (kScanWaves / WN) : TP;
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 #pragma unroll
         for (int b = 0; b < K::TNW; ++b) {
           const u32x2 v = {pack_bf16x2(hacc[a][b][0], hacc[a][b][1]), pack_bf16x2(hacc[a][b][2], hacc[a][b][3])};
-          *reinterpret_cast<u32x2*>(hsT + perm32((n0t + b) * 16 + l16) * K::HP + (p0t + a) * 16 + 4 * g4) = v;
+          *reinterpret_cast<u32x2*>(hsT + hs_row(perm32((n0t + b) * 16 + l16), K::HP) + (p0t + a) * 16 + 4 * g4) = v;
         }
     }
     u32x4 cf[ITW][K::NB];
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
         acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int nb = 0; nb < K::NB; ++nb)
-          acc[pt] = mfma16x16x32(frag_k_rows_accpair(hsT, K::HP, nb * 32, pt * 16, lane), cf[k][nb], acc[pt]);
+          acc[pt] = mfma16x16x32(frag_k_rows_accpair_hs(hsT, K::HP, nb * 32, pt * 16, lane), cf[k][nb], acc[pt]);
       }
       const float mref = csl[16 * it];
       const float em = fast_exp2(mref);
@@ -518,6 +519,7 @@ struct PairCfg {
   static constexpr int BP = lds_pitch(N);   // B rows
   static constexpr int XP = lds_pitch(P);   // X rows of each head
   static constexpr int HP = lds_pitch(P);   // transposed state rows of each head [N][HP] (rows at perm32(n))
+  static_assert(HP >= P + kHalfShift, "the half shift stays inside the row padding");
   static constexpr int TP = P / 16, TN = N / 16, NB = N / 32;
   // State tiles: whole P tiles per wave first, so that each decay-weighted X
   // fragment of the state update is formed by as few waves as possible.
@@ -707,7 +709,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
           for (int b = 0; b < K::TNW; ++b) {
             const u32x2 v = {pack_bf16x2(hacc[hd][a][b][0], hacc[hd][a][b][1]),
                              pack_bf16x2(hacc[hd][a][b][2], hacc[hd][a][b][3])};
-            *reinterpret_cast<u32x2*>(hsT + hd * N * K::HP + perm32((n0t + b) * 16 + l16) * K::HP + (p0t + a) * 16 +
+            *reinterpret_cast<u32x2*>(hsT + hd * N * K::HP + hs_row(perm32((n0t + b) * 16 + l16), K::HP) + (p0t + a) * 16 +
                                       4 * g4) = v;
           }
     }
@@ -730,7 +732,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
           acc[hd][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int nb = 0; nb < K::NB; ++nb)
-            acc[hd][pt] = mfma16x16x32(frag_k_rows_accpair(hsT + hd * N * K::HP, K::HP, nb * 32, pt * 16, lane), cf[nb],
+            acc[hd][pt] = mfma16x16x32(frag_k_rows_accpair_hs(hsT + hd * N * K::HP, K::HP, nb * 32, pt * 16, lane), cf[nb],
                                        acc[hd][pt]);
         }
       const float mref[2] = {csl[16 * it], csl[Q + 16 * it]};

@@ -201,6 +201,24 @@ __device__ __forceinline__ int perm32(int r) {
   return (r & ~31) | (((r >> 2) & 1) << 4) | (((r >> 3) & 3) << 2) | (r & 3);
 }
 
+// Transposed-state tiles ([n][p] rows stored at perm32(n)) shift the upper 16
+// rows of every 32-row block by 8 elements (inside the row padding): the
+// state's 8-byte row stores by 32 lanes (16 rows, two pieces each) then cover
+// all 64 banks once, where rows r and r + 16 would otherwise share banks. A
+// transposed read stays within one 16-row half, so its pattern only moves.
+constexpr int kHalfShift = 8;
+__host__ __device__ constexpr int hs_row(int r, int pitch) { return r * pitch + ((r >> 4) & 1) * kHalfShift; }
+
+// frag_k_rows_accpair on a tile stored with that shift: slots 4..7 come from
+// the shifted half.
+__device__ __forceinline__ u32x4 frag_k_rows_accpair_hs(const uint16_t* W, int pitch, int row0, int col0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const uint16_t* p0 = W + (row0 + 4 * g + (i >> 2)) * pitch + col0 + 4 * (i & 3);
+  const u32x2 lo = lds_read_tr16(p0);
+  const u32x2 hi = lds_read_tr16(p0 + 16 * pitch + kHalfShift);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
 // Scale the 8 bf16 values of an operand by 8 fp32 weights and round back to bf16.
 __device__ __forceinline__ u32x4 scale_frag(u32x4 v, const float* w) {
   u32x4 r;
