@@ -47,6 +47,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
+# SSD_ORACLE_LIBRARY names a prebuilt oracle library to load instead (the
+# sanitizer build, build_sanitized()).
+_LIB_OVERRIDE = os.environ.get("SSD_ORACLE_LIBRARY")
 _lib = None
 
 # Mutant codes (see ssd_oracle.c); used only by the pin-strength tests.
@@ -73,12 +76,27 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(out_path: str) -> str:
+    """The same oracle built with clang, AddressSanitizer and
+    UndefinedBehaviorSanitizer (one ASan runtime with the HIP library's
+    checking build), for the CPU sanitizer run."""
+    clang = "/opt/rocm/llvm/bin/clang"
+    cmd = [clang, "-O1", "-g", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           "-shared-libasan", "-o", out_path, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB_PATH):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB_PATH)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int)
         lib.ssd_oracle_scan.restype = ctypes.c_int

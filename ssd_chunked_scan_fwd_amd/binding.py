@@ -14,7 +14,9 @@ from typing import Optional, Tuple
 import torch
 
 _LIB_NAME = "libssd_mi355x.so"
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
+# SSD_MI355X_LIBRARY names another build of the same library (the sanitizer
+# build the CPU checks load); by default the in-tree one.
+_LIB_PATH = os.environ.get("SSD_MI355X_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
 _lib = None
 
 SSD_OK = 0

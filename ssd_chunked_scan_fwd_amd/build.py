@@ -33,28 +33,45 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+# Host-side sanitizers for the checking build (build(sanitize=True)): every
+# flag applies to the host pass only (-Xarch_host); device code is unchanged.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZE_DIR = os.path.join(BUILD, "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libssd_mi355x.so")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out_dir = SANITIZE_DIR if sanitize else BUILD
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc()] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON + (SANITIZE if sanitize else []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {src}\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, sanitize: bool = False) -> str:
+    """Build libssd_mi355x.so next to this file; with sanitize, a checking build
+    with AddressSanitizer and UndefinedBehaviorSanitizer on the host code, in
+    _build/sanitize/ (loaded by the tests through SSD_MI355X_LIBRARY, with the
+    clang ASan runtime preloaded)."""
+    out_dir = SANITIZE_DIR if sanitize else BUILD
+    lib = SANITIZE_LIB if sanitize else LIB
+    os.makedirs(out_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + \
+        (SANITIZE + ["-shared-libasan"] if sanitize else []) + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(int(sys.argv[1]) if len(sys.argv) > 1 else 8))
+    args = [a for a in sys.argv[1:] if a != "--sanitize"]
+    print(build(int(args[0]) if args else 8, sanitize="--sanitize" in sys.argv[1:]))
