@@ -123,6 +123,185 @@ def useful_flops(w, chunk_lengths) -> float:
     return f
 
 
+# The pages' own speed figures, restated: ratios the authors measured on
+# hardware and at a precision the pages do not give. Context, not a target.
+PAGES_REPORTED = {
+    "ssd_vs_mamba1_fused_scan": "2-8x faster than Mamba's fused selective scan at state size 64 "
+                                "(paper card TL;DR; paper section 9.3, fig. 10)",
+    "ssd_vs_flashattention2": "faster than FlashAttention-2 from sequence length 2K on; about 6x at 16K "
+                              "(paper card TL;DR, section 9.3 fig. 10; zh-note speed table)",
+    "state_size": "states 8x larger than Mamba's with limited slowdown (zh-note speed table; alex-wiki "
+                  "Evidence And Results)",
+    "hardware": "unstated",
+    "precision": "unstated",
+}
+
+# Every forward configuration, in the order of the workload table.
+CONFIGS = ["tiny-fp32-T256", "b2-T2048-H24-N64", "long-T16384-H32-N128", "sweep-b8-T4096-N64",
+           "sweep-b8-T4096-N128", "sweep-b8-T4096-N256", "packed-T32768-H80-N128"]
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (the fp32 path runs on FMA, not MFMA)
+FLUSH_BYTES = 1 << 30             # written between cold calls: evicts L2 and the 256 MB Infinity Cache
+
+
+def chunk_lengths_of(w, lengths=None):
+    """Chunk lengths of a workload: chunks restart at every sequence start."""
+    seqs = list(lengths) if lengths is not None else [w.T] * w.batch
+    out = []
+    for L in seqs:
+        out += [min(w.Q, L - k * w.Q) for k in range(-(-int(L) // w.Q))]
+    return out
+
+
+def compulsory_bytes(w, nseq: int) -> int:
+    """X and Y, B and C at the dtype size, log a (fp32) and the final states (fp32)."""
+    esz = 2 if w.dtype == "bf16" else 4
+    tok = w.batch * w.T
+    return tok * w.H * w.P * esz * 2 + tok * w.G * w.N * esz * 2 + tok * w.H * 4 + nseq * w.H * w.P * w.N * 4
+
+
+def graph_of(torch, fn, n: int = 1):
+    """fn() run n times, captured once into a HIP graph (after one eager run on
+    a side stream): replays measure GPU time without the host's per-call
+    argument checks and launch overhead."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def settle_calls(torch, fn, min_calls: int, seconds: float = 0.15):
+    """Run fn back to back for at least min_calls calls and `seconds` of wall time."""
+    t0, k = time.perf_counter(), 0
+    while k < min_calls or time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        k += 8
+        torch.cuda.synchronize()
+
+
+def timed_calls(torch, stream, fn, n, before=None):
+    """Per-call durations (us) of n calls of fn, each between its own HIP events on
+    `stream`; `before(i)` runs untimed ahead of call i."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        if before is not None:
+            before(i)
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def oracle_sample(oracle, w, d, budget_s: float):
+    """The fp64 oracle on a bounded sample of a workload: the first k heads (k
+    doubled until the time budget is used or all heads are in), run back to
+    back; tokens/s scaled to all H heads."""
+    X, la, B, C = (d[k].double().numpy() for k in ("X", "log_a", "B", "C"))
+    cu = d.get("cu_seqlens")
+    cu = None if cu is None else cu.numpy()
+    nseq = w.batch if cu is None else len(cu) - 1
+    cores = len(os.sched_getaffinity(0))
+    k, best = 1, None
+    while True:
+        th = max(1, min(cores, nseq * k))
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.scan(X[:, :, :k], la[:, :, :k], B, C, segments=oracle.sequence_segments(w.batch, w.T, cu),
+                        threads=th)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s / 4 or runs >= 50:
+                break
+        best = (k, th, runs, el)
+        if k >= w.H or el * 2 > budget_s:
+            break
+        k = min(w.H, 2 * k)
+    k, th, runs, el = best
+    tok = w.batch * w.T
+    return {"tokens_per_s": round(tok * runs / el * k / w.H, 1), "cores": th,
+            "sample": f"{k} of {w.H} heads, {runs} run(s) in {el:.2f} s, scaled to {w.H} heads"}
+
+
+def measure_config(ctx, name, steps, warmup, cpu_budget):
+    """Forward pass of one workload: per-call HIP-event times of the call replayed
+    from a HIP graph, warm (back to back) and cold (1 GB written before each
+    call), the mean of direct calls back to back, rates, roofline fractions, and
+    the oracle on a bounded sample of it."""
+    torch, ssd, synth, dev, stream, flush = ctx["torch"], ctx["ssd"], ctx["synth"], ctx["dev"], ctx["stream"], \
+        ctx["flush"]
+    w = synth.WORKLOADS[name]
+    d = synth.workload_inputs(w)
+    X, la, B, C = (d[k].to(dev) for k in ("X", "log_a", "B", "C"))
+    cu = d["cu_seqlens"].to(dev) if d.get("cu_seqlens") is not None else None
+    lengths = None if cu is None else [int(v) for v in (d["cu_seqlens"][1:] - d["cu_seqlens"][:-1])]
+    nseq = w.batch if cu is None else cu.numel() - 1
+    sh = ssd.make_shape(X, B, cu)
+    ws = ssd.Workspace(sh, w.Q, dev)
+    Y = torch.empty_like(X)
+    fin = torch.empty(nseq, w.H, w.P, w.N, dtype=torch.float32, device=dev)
+
+    def step():
+        ssd.fwd(X, la, B, C, cu_seqlens=cu, chunk=w.Q, state_block=ws.state_block, Y=Y, final_state=fin,
+                workspace=ws)
+
+    # Warm-up by sustained work: the GPU clock settles only after some tens of
+    # milliseconds under load (fewer warm-up calls read slower steps).
+    settle_calls(torch, step, warmup)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    b2b = a.elapsed_time(b) * 1e3 / steps
+    g = graph_of(torch, step)
+    settle_calls(torch, g.replay, warmup)
+    warm = timed_calls(torch, stream, g.replay, steps)
+    cold = timed_calls(torch, stream, g.replay, steps, before=lambda i: flush.fill_(i % 251))
+    del g
+    tok = w.batch * w.T
+    flops = useful_flops(w, chunk_lengths_of(w, lengths))
+    comp = compulsory_bytes(w, nseq)
+    sb = stage_bytes(w, ws.layout.nslots, ws.layout.nblocks, nseq)
+    pipe = sb["chunk_state_fused"] + sb["state_passing"] + sb["chunk_scan"]
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+    r = {"dtype": w.dtype, "batch": w.batch, "T": w.T, "H": w.H, "P": w.P, "N": w.N, "G": w.G, "chunk": w.Q,
+         "num_seqs": nseq if cu is not None else 0, "state_block": ws.state_block, "steps": steps}
+    for tag, us in (("warm", median(warm)), ("cold", median(cold))):
+        r[f"{tag}_us_median"] = round(us, 2)
+        r[f"{tag}_tokens_per_s"] = round(tok / (us * 1e-6), 1)
+        r[f"{tag}_useful_tflops"] = round(flops / (us * 1e-6) / 1e12, 2)
+        r[f"{tag}_{'mfma' if w.dtype == 'bf16' else 'fp32_vector'}_frac"] = round(flops / (us * 1e-6) / 1e12 / peak, 5)
+        r[f"{tag}_compulsory_hbm_frac"] = round(comp / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        r[f"{tag}_pipeline_hbm_frac"] = round(pipe / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    r["back_to_back_us_mean"] = round(b2b, 2)
+    r["useful_gflop"] = round(flops / 1e9, 4)
+    r["compulsory_mb"] = round(comp / 1e6, 2)
+    r["pipeline_mb"] = round(pipe / 1e6, 2)
+    if cpu_budget > 0:
+        from oracle import oracle
+        o = oracle_sample(oracle, w, d, cpu_budget)
+        r["oracle"] = o
+        r["gpu_warm_vs_oracle"] = round(r["warm_tokens_per_s"] / o["tokens_per_s"], 1)
+    del X, la, B, C, cu, ws, Y, fin
+    return r
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,14 +316,23 @@ def main() -> int:
                     help="also time the state chain as one cooperative launch (rocprofv3 cannot trace it)")
     ap.add_argument("--bwd-steps", type=int, default=100)
     ap.add_argument("--no-workloads", action="store_true",
-                    help="skip the forward timing of the state-size sweep and the packed H=80 layer")
-    ap.add_argument("--wl-steps", type=int, default=50)
+                    help="skip the per-config forward timing (every workload, warm and cold)")
+    ap.add_argument("--wl-steps", type=int, default=50, help="timed calls per config, warm and cold each")
+    ap.add_argument("--wl-cpu-seconds", type=float, default=2.0,
+                    help="oracle time budget per config (bounded head sample); 0 skips it")
+    ap.add_argument("--profile-config", default="", metavar="NAME",
+                    help="run only NAME's forward pass (warm-up, then --wl-steps calls) and print a short JSON "
+                         "line: the command the per-config rocprofv3 traces are taken with")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="run only the decode steps (and --copy-probe): the command of the decode counter passes")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the oracle baseline")
     ap.add_argument("--decode-steps", type=int, default=4096)
     ap.add_argument("--state-block", type=int, default=0, help="chunks per state block (0: library default)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the run, launch one elementwise copy of MIB MiB (read MIB, write MIB): the "
                          "calibration kernel of the FETCH_SIZE / WRITE_SIZE counter passes")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time stages by back-to-back eager launches and skip graph replays (counter passes)")
     ap.add_argument("--print-digest", action="store_true", help="print the source digest of each stage and exit")
     args = ap.parse_args()
 
@@ -168,6 +356,34 @@ def main() -> int:
         return 2
     dev = torch.device("cuda:0")
     ssd.lib()  # fail loudly when the HIP library is missing
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    ctx = {"torch": torch, "ssd": ssd, "synth": synth, "dev": dev, "stream": torch.cuda.current_stream(dev),
+           "flush": flush}
+
+    if args.profile_decode:
+        wd = synth.WORKLOADS["decode-b64-H80-N128"]
+        n = min(args.decode_steps, 64)
+        log(f"[bench] profile run: {n} decode steps of {wd.name}")
+        dd = synth.make_decode_inputs(wd.batch, n, wd.H, wd.P, wd.N, wd.G, wd.torch_dtype, wd.seed)
+        xs, las, Bs, Cs = (dd[k].to(dev) for k in ("x", "log_a", "B", "C"))
+        state = torch.zeros(wd.batch, wd.H, wd.P, wd.N, dtype=torch.float32, device=dev)
+        y = torch.empty(wd.batch, wd.H, wd.P, dtype=xs.dtype, device=dev)
+        for t in range(n):
+            ssd.step(state, xs[t], las[t], Bs[t], Cs[t], y=y)
+        torch.cuda.synchronize()
+        if args.copy_probe > 0:
+            src = torch.ones(args.copy_probe * (1 << 20) // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+        print(json.dumps({"profile_decode": wd.name, "steps": n}), flush=True)
+        return 0
+
+    if args.profile_config:
+        log(f"[bench] profile run: forward on {args.profile_config}")
+        r = measure_config(ctx, args.profile_config, args.wl_steps, 10, 0.0)
+        print(json.dumps({"profile_config": args.profile_config, "result": r}), flush=True)
+        return 0
 
     w = synth.WORKLOADS[synth.HEADLINE]
     log(f"[bench] workload {w.name}: generating inputs")
@@ -199,12 +415,26 @@ def main() -> int:
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / args.steps
     ev_ms = e0.elapsed_time(e1) / args.steps
+    # the same step replayed from a HIP graph (GPU time without host overhead)
+    graph_ms = ev_ms
+    if not args.no_graph:
+        gstep = graph_of(torch, step, 10)
+        for _ in range(5):
+            gstep.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(max(1, args.steps // 10)):
+            gstep.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = e0.elapsed_time(e1) / (max(1, args.steps // 10) * 10)
+        del gstep
     ms_per_step = wall_ms
     tokens = w.batch * w.T
     value = tokens / (ms_per_step * 1e-3)
 
     # per-stage average launch time: HIP events on the launch stream around
-    # stage_reps back-to-back launches of the stage's own entry point
+    # graph replays of the stage's own entry point
     log(f"[bench] per-stage timing, {args.stage_reps} launches each")
     stages = [
         ("chunk_cumsum", lambda: ssd.chunk_cumsum(la, None, shape, ws)),
@@ -212,24 +442,42 @@ def main() -> int:
         ("state_passing", lambda: ssd.state_passing(None, fin, shape, ws)),
         ("chunk_scan", lambda: ssd.chunk_scan(X, B, C, None, Y, shape, ws)),
     ]
+    # Each stage's launches captured in a HIP graph (20 per graph) and replayed,
+    # so the figure is GPU time rather than the host's per-call overhead.
     acc = {}
+    per_graph = 20
+    reps = max(1, args.stage_reps // per_graph)
     for name, fn in stages:
-        for _ in range(min(20, args.stage_reps)):
-            fn()
+        if args.no_graph:
+            for _ in range(min(20, args.stage_reps)):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.stage_reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            acc[name] = a.elapsed_time(b) / max(args.stage_reps, 1)
+            continue
+        g = graph_of(torch, fn, per_graph)
+        for _ in range(2):
+            g.replay()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
         a.record(stream)
-        for _ in range(args.stage_reps):
-            fn()
+        for _ in range(reps):
+            g.replay()
         b.record(stream)
         torch.cuda.synchronize()
-        acc[name] = a.elapsed_time(b)
-    stage_us = {k: v * 1e3 / max(args.stage_reps, 1) for k, v in acc.items()}
+        acc[name] = a.elapsed_time(b) / (reps * per_graph)
+        del g
+    stage_us = {k: v * 1e3 for k, v in acc.items()}
     sbytes = stage_bytes(w, ws.layout.nslots, ws.layout.nblocks, w.batch)
     dominant = max(stage_us, key=stage_us.get)
     # The step runs three launches: chunk_state in its fused form (segment sums
     # computed in the kernel), state_passing, chunk_scan. The fused kernel has no
     # entry point of its own; its time is the step's event time less the other two.
-    fused_us = ev_ms * 1e3 - stage_us["state_passing"] - stage_us["chunk_scan"]
+    fused_us = graph_ms * 1e3 - stage_us["state_passing"] - stage_us["chunk_scan"]
     achieved = sbytes[dominant] / (stage_us[dominant] * 1e-6) / 1e9
     chunk_lengths = [min(w.Q, w.T - k * w.Q) for k in range(-(-w.T // w.Q))] * w.batch
     flops = useful_flops(w, chunk_lengths)
@@ -264,12 +512,14 @@ def main() -> int:
         "stage_bytes": sbytes,
         "stage_gbs": {k: round(sbytes[k] / (stage_us[k] * 1e-6) / 1e9, 1) for k in stage_us},
         "event_ms_per_step": round(ev_ms, 5),
+        "graph_ms_per_step": round(graph_ms, 5),
         "useful_tflops": round(tflops, 2),
         "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 5),
         "compulsory_bytes": compulsory,
         "compulsory_hbm_frac": round(compulsory / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "pipeline_bytes": pipeline_bytes,
         "pipeline_hbm_frac": round(pipeline_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "pages_reported": PAGES_REPORTED,
     }
 
     if not args.no_mamba2:
@@ -419,6 +669,21 @@ def main() -> int:
         torch.cuda.synchronize()
         out["decode"]["graph_us_per_step"] = round(a.elapsed_time(b) * 1e3 / (reps * glen), 3)
         del graph
+        # Cold steps: 1 GB written before each, so the 168 MB state comes from
+        # HBM and not from the Infinity Cache; a cold step as fast as a warm one
+        # means the warm rate is HBM traffic.
+        ncold = min(50, nsteps)
+        cold = []
+        for t in range(ncold):
+            flush.fill_(t % 251)
+            e0c, e1c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0c.record(stream)
+            ssd.step(state, xs[t], las[t], Bs[t], Cs[t], y=y)
+            e1c.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0c.elapsed_time(e1c) * 1e3)
+        out["decode"]["cold_us_per_step_median"] = round(median(cold), 3)
+        out["decode"]["cold_gbs_per_step"] = round(per_step_bytes / (median(cold) * 1e-6) / 1e9, 1)
         del xs, las, Bs, Cs
         if not args.no_mamba2:
             md = synth.make_mamba2_decode_inputs(wd.batch, nsteps, wd.H, wd.P, wd.N, wd.G, wd.torch_dtype, wd.seed)
@@ -439,41 +704,20 @@ def main() -> int:
         del state
 
     if not args.no_workloads:
-        # The forward pass on the state-size sweep (slowdown against N = 64) and
-        # on the packed variable-length layer shape: wall time per ssd_fwd call.
+        # Every forward configuration, warm and cold, with its oracle sample.
         res = {}
-        for name in ("sweep-b8-T4096-N64", "sweep-b8-T4096-N128", "sweep-b8-T4096-N256", "packed-T32768-H80-N128"):
-            wl = synth.WORKLOADS[name]
-            log(f"[bench] forward on {name}: {args.wl_steps} steps")
-            dl = synth.workload_inputs(wl)
-            lX, lla, lB, lC = (dl[k].to(dev) for k in ("X", "log_a", "B", "C"))
-            lcu = dl["cu_seqlens"].to(dev) if dl.get("cu_seqlens") is not None else None
-            lsh = ssd.make_shape(lX, lB, lcu)
-            lws = ssd.Workspace(lsh, wl.Q, dev)
-            lY = torch.empty_like(lX)
-            nseq_l = wl.batch if lcu is None else lcu.numel() - 1
-            lfin = torch.empty(nseq_l, wl.H, wl.P, wl.N, dtype=torch.float32, device=dev)
-
-            def lstep():
-                ssd.fwd(lX, lla, lB, lC, cu_seqlens=lcu, chunk=wl.Q, state_block=lws.state_block, Y=lY,
-                        final_state=lfin, workspace=lws)
-
-            for _ in range(10):
-                lstep()
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(args.wl_steps):
-                lstep()
-            torch.cuda.synchronize()
-            l_ms = (time.perf_counter() - t0) * 1e3 / max(args.wl_steps, 1)
-            ltok = wl.batch * wl.T
-            res[name] = {"ms_per_step": round(l_ms, 5), "tokens_per_s": round(ltok / (l_ms * 1e-3), 1),
-                         "state_block": lws.state_block}
-            del lX, lla, lB, lC, lcu, lws, lY, lfin
-        base = res["sweep-b8-T4096-N64"]["ms_per_step"]
+        for name in CONFIGS:
+            log(f"[bench] config {name}: {args.wl_steps} warm + {args.wl_steps} cold calls")
+            res[name] = measure_config(ctx, name, args.wl_steps, 10,
+                                       0.0 if args.no_cpu_baseline else args.wl_cpu_seconds)
+        base = res["sweep-b8-T4096-N64"]["warm_us_median"]
         for name in ("sweep-b8-T4096-N64", "sweep-b8-T4096-N128", "sweep-b8-T4096-N256"):
-            res[name]["slowdown_vs_N64"] = round(res[name]["ms_per_step"] / base, 3)
-        out["workloads"] = res
+            res[name]["slowdown_vs_N64"] = round(res[name]["warm_us_median"] / base, 3)
+        out["configs"] = res
+        hl = res.get(w.name)
+        if hl:
+            out["cold_ms_per_step"] = round(hl["cold_us_median"] * 1e-3, 5)
+            out["cold_tokens_per_s"] = hl["cold_tokens_per_s"]
 
     if args.copy_probe > 0:
         n = args.copy_probe * (1 << 20) // 4

@@ -81,3 +81,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_config_helpers():
+    from ssd_chunked_scan_fwd_amd import synth
+    w = synth.WORKLOADS["long-T16384-H32-N128"]
+    # compulsory bytes at the headline: X and Y (bf16), B and C (bf16), log a and the final state (fp32)
+    assert bench.compulsory_bytes(w, 1) == 145_752_064
+    assert bench.chunk_lengths_of(w) == [128] * 128
+    p = synth.WORKLOADS["packed-T32768-H80-N128"]
+    lens = [700, 1, 129, 31938]
+    cl = bench.chunk_lengths_of(p, lens)
+    assert sum(cl) == sum(lens) and cl[:8] == [128] * 5 + [60, 1, 128] and max(cl) <= 128
+    assert bench.median([3, 1, 2]) == 2 and bench.median([4, 1, 3, 2]) == 2.5
+    assert set(bench.CONFIGS) == {k for k, v in synth.WORKLOADS.items() if not v.steps}
+    assert bench.PAGES_REPORTED["hardware"] == "unstated"
