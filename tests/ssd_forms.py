@@ -10,10 +10,15 @@ from the recurrence the oracle implements, so agreement is evidence for both:
   L_ij = a_i x ... x a_{j+1}). Built by brute force: every entry of L is an
   explicit product of decays, and the final state is the weighted sum of the
   rank-one inputs x_s B_s^T.
-* ``chunked_form`` -- the four-term block decomposition (paper card Method 5,
-  paper section 6: diagonal blocks, right factors, centre factors, left
-  factors), written fresh from the mathematics with numpy einsums. It accepts
-  chunk lengths that do not divide T (the last chunk is short).
+* ``chunked_form`` -- the block structure of M = L o C B^T cut into chunks
+  (paper card Method 3 and Method 5, paper sections 5.2 and 6): within a
+  chunk, M is used as it is; between an earlier chunk k' and a later chunk k
+  every block of M is a rank-N product left(k) * decay(k' -> k) * right(k')^T,
+  with the decays taken from a cumulative log decay over the whole row. Y is
+  the sum of those block products over all chunk pairs, computed pair by pair
+  with no state carried from chunk to chunk; the state at each chunk's end from
+  a zero start and the state entering each chunk are read off the same
+  factors. It accepts chunk lengths that do not divide T.
 """
 from __future__ import annotations
 
@@ -58,7 +63,7 @@ def dual_form(X, la, B, C):
 
 
 def chunked_form(X, la, B, C, Q: int, init=None):
-    """Chunked block decomposition for one row: X [T,H,P], la [T,H], B, C [T,G,N].
+    """Chunk-pair block factorisation for one row: X [T,H,P], la [T,H], B, C [T,G,N].
 
     Returns (Y [T,H,P], final [H,P,N], start_states [K,H,P,N], chunk_states [K,H,P,N]).
     """
@@ -68,38 +73,50 @@ def chunked_form(X, la, B, C, Q: int, init=None):
     C = np.asarray(C, np.float64)
     T, H, P = X.shape
     G, N = B.shape[1], B.shape[2]
-    heads_g = np.array([_group_of(h, H, G) for h in range(H)])
-    Bh = B[:, heads_g, :]                      # [T,H,N] per-head view
-    Ch = C[:, heads_g, :]
-    bounds = [(c0, min(c0 + Q, T)) for c0 in range(0, T, Q)]
-    K = len(bounds)
+    edges = list(range(0, T, Q)) + [T]
+    K = len(edges) - 1
+    # Whole-row cumulative log decay with a leading zero: the decay from just
+    # after position s to position t (s < t) is exp(g[t+1] - g[s+1]); before
+    # the first token g = 0, the state the initial state decays from.
+    g = np.concatenate([np.zeros((1, H)), np.cumsum(la, axis=0)], axis=0)    # [T+1, H]
     Y = np.zeros((T, H, P))
     chunk_states = np.zeros((K, H, P, N))
-    chunk_total = np.zeros((K, H))
-    css = []
-    for k, (c0, c1) in enumerate(bounds):
-        cs = np.cumsum(la[c0:c1], axis=0)               # [q,H], restarted per chunk
-        css.append(cs)
-        q = c1 - c0
-        # Diagonal block: exp(segsum) masked below the diagonal before the exp.
-        diff = cs[:, None, :] - cs[None, :, :]           # [i,j,H] = cs_i - cs_j
-        lower = np.tril(np.ones((q, q), bool))
-        seg = np.where(lower[:, :, None], diff, -np.inf)
-        Lm = np.exp(seg)                                 # zero above the diagonal
-        S = np.einsum("ihn,jhn->ijh", Ch[c0:c1], Bh[c0:c1])
-        Y[c0:c1] += np.einsum("ijh,ijh,jhp->ihp", Lm, S, X[c0:c1])
-        # Right factor: state at the chunk end from a zero start.
-        to_end = np.exp(cs[-1][None, :] - cs)            # [q,H]
-        chunk_states[k] = np.einsum("jh,jhp,jhn->hpn", to_end, X[c0:c1], Bh[c0:c1])
-        chunk_total[k] = cs[-1]
-    # Centre factor: scalar recurrence over chunk states.
-    state = np.zeros((H, P, N)) if init is None else np.array(init, np.float64)
     start_states = np.zeros((K, H, P, N))
-    for k in range(K):
-        start_states[k] = state
-        state = np.exp(chunk_total[k])[:, None, None] * state + chunk_states[k]
-    # Left factor: carried-in state seen through exp(cumsum) at each position.
-    for k, (c0, c1) in enumerate(bounds):
-        from_start = np.exp(css[k])                      # [q,H]
-        Y[c0:c1] += np.einsum("ih,ihn,hpn->ihp", from_start, Ch[c0:c1], start_states[k])
-    return Y, state, start_states, chunk_states
+    h0 = None if init is None else np.asarray(init, np.float64)
+    for h in range(H):
+        grp = _group_of(h, H, G)
+        Bg, Cg = B[:, grp, :], C[:, grp, :]
+        # left(k):  rows i of chunk k, C_i scaled by the decay from the chunk's start
+        # right(k): rows j of chunk k, B_j scaled by the decay from j to the chunk's end
+        left, right = [], []
+        for k in range(K):
+            b, e = edges[k], edges[k + 1]
+            left.append(np.exp(g[b + 1:e + 1, h] - g[b, h])[:, None] * Cg[b:e])
+            right.append(np.exp(g[e, h] - g[b + 1:e + 1, h])[:, None] * Bg[b:e])
+        for k in range(K):
+            b, e = edges[k], edges[k + 1]
+            # the block of M on the diagonal, entry by entry
+            idx = np.arange(b, e)
+            decay = np.exp(g[idx + 1, h][:, None] - g[idx + 1, h][None, :])
+            blk = np.tril(decay) * (Cg[b:e] @ Bg[b:e].T)
+            Y[b:e, h] += blk @ X[b:e, h]
+            # the state at this chunk's end from a zero start: (right factor)^T x
+            chunk_states[k, h] = X[b:e, h].T @ right[k]
+            # every earlier chunk k2 < k: the rank-N block product, and its share of the
+            # state entering chunk k
+            for k2 in range(k):
+                e2 = edges[k2 + 1]
+                between = np.exp(g[b, h] - g[e2, h])          # decay from the end of k2 to the start of k
+                Y[b:e, h] += between * (left[k] @ (right[k2].T @ X[edges[k2]:e2, h]))
+                start_states[k, h] += between * chunk_states[k2, h]
+            if h0 is not None:
+                # the initial state, decayed over every token before chunk k
+                start_states[k, h] += np.exp(g[b, h]) * h0[h]
+                Y[b:e, h] += left[k] @ (np.exp(g[b, h]) * h0[h]).T
+    final = np.zeros((H, P, N))
+    for h in range(H):
+        for k in range(K):
+            final[h] += np.exp(g[T, h] - g[edges[k + 1], h]) * chunk_states[k, h]
+        if h0 is not None:
+            final[h] += np.exp(g[T, h]) * h0[h]
+    return Y, final, start_states, chunk_states

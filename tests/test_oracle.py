@@ -91,6 +91,26 @@ def test_chunked_form_every_chunk_length(Q):
     assert _relmax(fin[0], fc) <= 1e-12
 
 
+@pytest.mark.parametrize("Q", [1, 7, 16])
+def test_chunked_form_from_an_initial_state(Q):
+    """The chunk-pair form with an entering state equals the oracle continued from it
+    (outputs, final state, and the state entering every chunk)."""
+    T, H, P, N = 40, 2, 3, 5
+    X, la, B, C = _rand(T, H, P, N, seed=12)
+    h0 = np.random.default_rng(3).standard_normal((1, H, P, N))
+    Y, fin, _ = oracle.scan(X, la, B, C, init=h0)
+    Yc, fc, starts, _ = chunked_form(X[0], la[0], B[0], C[0], Q, init=h0[0])
+    assert _relmax(Y[0], Yc) <= 1e-12
+    assert _relmax(fin[0], fc) <= 1e-12
+    assert _relmax(starts[0], h0[0]) <= 1e-15
+    segs = oracle.chunk_segments(1, T, Q)
+    snap = -np.ones(T, np.int32)
+    for k, (_, b, e) in enumerate(segs[:-1]):
+        snap[e - 1] = k + 1
+    _, _, snaps = oracle.scan(X, la, B, C, init=h0, want_y=False, snap_slot=snap, nsnaps=len(segs))
+    assert _relmax(snaps[1:], starts[1:]) <= 1e-12
+
+
 def test_chunked_intermediates_match_oracle_snapshots():
     """Chunk states = oracle restarted per chunk; start states = oracle state at chunk ends."""
     T, Q, H, P, N = 50, 16, 2, 3, 4
