@@ -119,7 +119,11 @@ hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float
 // ssd_step: one decode step. One workgroup per (row, head); N/4 consecutive
 // lanes share a state row p, each owning 4 consecutive n. The state is read
 // and written once (fp32); y[p] = sum_n state'[p][n] C[n] is reduced across
-// the lanes of the row. The Mamba-2 block's step (dt != null) discretises
+// the lanes of the row. The state streams through with non-temporal loads and
+// stores: a model's per-layer decode states together exceed the Infinity Cache,
+// so each step's state comes from HBM, and streaming accesses move it at a
+// higher rate there (a cached read and write of one resident state is faster
+// only while that state stays in the cache). The Mamba-2 block's step (dt != null) discretises
 // first, dt' = softplus(dt + dt_bias), a = exp(dt' A) with A = -exp(A_log),
 // feeds x dt' into the state, and finishes y with the skip D x and the gate
 // silu(z) (paper card Method 6 block sketch; Paper vs code items 3, 7).
@@ -192,29 +196,50 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(float* __restrict__ state
     for (int i = 0; i < 4; ++i) { bb[i] = fb[i]; cc[i] = fc[i]; }
   }
 
-  for (int p = p0; p < P; p += rpp) {
-    const float xp = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[bh * P + p])
-                          : reinterpret_cast<const float*>(x)[bh * P + p];
-    const float xs = xp * xscale;
-    f32x4* sp = reinterpret_cast<f32x4*>(st + (long)p * N + 4 * c4);
-    f32x4 s = *sp;
-    float part = 0.f;
+  // Up to 8 state rows per thread per round: every row's load is issued
+  // before the first is used, so each lane keeps 8 loads in flight; rows past
+  // P are neither read nor written (their addresses are clamped to row P - 1).
+  constexpr int kRows = 8;
+  for (int pb = p0; pb < P; pb += kRows * rpp) {
+    f32x4* sp[kRows];
+    f32x4 s[kRows];
+    float xr[kRows];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = a * s[i] + xs * bb[i];
-      part += s[i] * cc[i];
+    for (int k = 0; k < kRows; ++k) {
+      const int p = pb + k * rpp;
+      sp[k] = reinterpret_cast<f32x4*>(st + (long)min(p, P - 1) * N + 4 * c4);
+      if (p < P) s[k] = __builtin_nontemporal_load(sp[k]);
     }
-    *sp = s;
-    part = lanes_sum(part, tpr);
-    part += Dh * xp;
-    if (zv) {
-      const float zp = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(zv)[bh * P + p])
-                            : reinterpret_cast<const float*>(zv)[bh * P + p];
-      part *= silu_f32(zp);
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int p = min(pb + k * rpp, P - 1);
+      xr[k] = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[bh * P + p])
+                   : reinterpret_cast<const float*>(x)[bh * P + p];
     }
-    if (c4 == 0) {
-      if (BF16) reinterpret_cast<uint16_t*>(y)[bh * P + p] = f32_to_bf16(part);
-      else reinterpret_cast<float*>(y)[bh * P + p] = part;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int p = pb + k * rpp;
+      if (p >= P) break;
+      const float xp = xr[k];
+      const float xs = xp * xscale;
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[k][i] = a * s[k][i] + xs * bb[i];
+        part += s[k][i] * cc[i];
+      }
+      __builtin_nontemporal_store(s[k], sp[k]);
+      part = lanes_sum(part, tpr);
+      part += Dh * xp;
+      if (zv) {
+        const float zp = BF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(zv)[bh * P + p])
+                              : reinterpret_cast<const float*>(zv)[bh * P + p];
+        part *= silu_f32(zp);
+      }
+      if (c4 == 0) {
+        if (BF16) reinterpret_cast<uint16_t*>(y)[bh * P + p] = f32_to_bf16(part);
+        else reinterpret_cast<float*>(y)[bh * P + p] = part;
+      }
     }
   }
 }
