@@ -684,6 +684,9 @@ def main() -> int:
             cold.append(e0c.elapsed_time(e1c) * 1e3)
         out["decode"]["cold_us_per_step_median"] = round(median(cold), 3)
         out["decode"]["cold_gbs_per_step"] = round(per_step_bytes / (median(cold) * 1e-6) / 1e9, 1)
+        # The cold step is the HBM figure: a model's per-layer decode states
+        # together exceed the Infinity Cache.
+        out["decode"]["cold_hbm_frac"] = round(per_step_bytes / (median(cold) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         del xs, las, Bs, Cs
         if not args.no_mamba2:
             md = synth.make_mamba2_decode_inputs(wd.batch, nsteps, wd.H, wd.P, wd.N, wd.G, wd.torch_dtype, wd.seed)
