@@ -404,14 +404,15 @@ def test_prefill_then_decode_handoff():
 
 
 def test_decode_workload_full_size_sampled():
-    """All 4096 steps at batch 64, 80 heads; the oracle follows 24 sampled (row, head) streams."""
+    """All 4096 steps at batch 64, 80 heads; the oracle follows 256 sampled (row, head)
+    streams, four heads of every row."""
     w = synth.WORKLOADS["decode-b64-H80-N128"]
     say(f"[parity] decode workload {w}")
     d = synth.workload_inputs(w)
     dd = to_dev(d)
     state = torch.zeros(w.batch, w.H, w.P, w.N, dtype=torch.float32, device="cuda")
     rng = np.random.default_rng(7)
-    pairs = [(int(r), int(h)) for r, h in zip(rng.integers(0, w.batch, 24), rng.integers(0, w.H, 24))]
+    pairs = [(r, int(h)) for r in range(w.batch) for h in rng.choice(w.H, 4, replace=False)]
     ys = torch.empty(w.steps, len(pairs), w.P, dtype=torch.bfloat16, device="cuda")
     rows = torch.tensor([p[0] for p in pairs], device="cuda")
     heads = torch.tensor([p[1] for p in pairs], device="cuda")
@@ -430,3 +431,46 @@ def test_decode_workload_full_size_sampled():
     Yr, fr = oracle.forward(X, la, B, C)
     assert_close(to_f64(ys).transpose(1, 0, 2), Yr[:, :, 0, :], "bf16", "decode y")
     assert_close(to_f64(state[rows, heads]), fr[:, 0], "bf16", "decode state")
+
+
+def _gpu_errors(got, ref, rows_per_slice=8):
+    """max |d| / rms(ref) and ||d|| / ||ref|| of two device tensors with the same first
+    (row) dimension, accumulated in fp64 over slices of rows to bound device memory."""
+    dmax, dsq, rsq, n = 0.0, 0.0, 0.0, 0
+    for r0 in range(0, ref.shape[0], rows_per_slice):
+        g, r = got[r0:r0 + rows_per_slice].double(), ref[r0:r0 + rows_per_slice].double()
+        d = g - r
+        dmax = max(dmax, d.abs().max().item())
+        dsq += d.pow(2).sum().item()
+        rsq += r.pow(2).sum().item()
+        n += r.numel()
+    rms = (rsq / n) ** 0.5
+    return dmax / max(rms, 1e-300), dsq ** 0.5 / max(rsq ** 0.5, 1e-300)
+
+
+def test_decode_workload_matches_chunked_forward():
+    """Every one of the 5120 (row, head) streams of the decode workload: 4096 decode steps
+    from a zero state give the outputs and final state of the chunked forward pass run on
+    the same inputs as 64 sequences of 4096 tokens (the recurrence and its chunked form
+    are the same map). Both are held to the bf16 bar against each other; the oracle
+    itself is checked on sampled streams above and on the chunked path's workloads."""
+    from parity import BF16_MAXABS_UNIT, BF16_RELL2
+    w = synth.WORKLOADS["decode-b64-H80-N128"]
+    say(f"[parity] decode workload against the chunked forward, all streams")
+    d = synth.workload_inputs(w)
+    dd = to_dev(d)
+    state = torch.zeros(w.batch, w.H, w.P, w.N, dtype=torch.float32, device="cuda")
+    ys = torch.empty(w.steps, w.batch, w.H, w.P, dtype=torch.bfloat16, device="cuda")
+    for t in range(w.steps):
+        ssd.step(state, dd["x"][t], dd["log_a"][t], dd["B"][t], dd["C"][t], y=ys[t])
+    X = dd["x"].permute(1, 0, 2, 3).contiguous()
+    la = dd["log_a"].permute(1, 0, 2).contiguous()
+    B = dd["B"].permute(1, 0, 2, 3).contiguous()
+    C = dd["C"].permute(1, 0, 2, 3).contiguous()
+    Y, fin = ssd.fwd(X, la, B, C, chunk=128)
+    torch.cuda.synchronize()
+    my, ly = _gpu_errors(ys.permute(1, 0, 2, 3), Y)
+    mf, lf = _gpu_errors(state, fin)
+    say(f"[parity] decode vs chunked: y max|d|/rms {my:.3e} rel-L2 {ly:.3e}; state max|d|/rms {mf:.3e} rel-L2 {lf:.3e}")
+    assert my <= BF16_MAXABS_UNIT and ly <= BF16_RELL2
+    assert mf <= BF16_MAXABS_UNIT and lf <= BF16_RELL2
