@@ -434,26 +434,35 @@ def test_decode_workload_full_size_sampled():
 
 
 def _gpu_errors(got, ref, rows_per_slice=8):
-    """max |d| / rms(ref) and ||d|| / ||ref|| of two device tensors with the same first
-    (row) dimension, accumulated in fp64 over slices of rows to bound device memory."""
-    dmax, dsq, rsq, n = 0.0, 0.0, 0.0, 0
+    """For two device tensors with the same first (row) dimension, accumulated in fp64
+    over slices of rows to bound device memory: max |d| / rms(ref), ||d|| / ||ref||, and
+    the largest |d_i| / (5e-2 rms(ref) + 2^-8 |ref_i|) (the plain bf16 bar plus one
+    rounding of the element itself; <= 1 passes)."""
+    from parity import BF16_MAXABS_UNIT, BF16_UNIT_ROUNDOFF
+    rsq, n = 0.0, 0
     for r0 in range(0, ref.shape[0], rows_per_slice):
-        g, r = got[r0:r0 + rows_per_slice].double(), ref[r0:r0 + rows_per_slice].double()
-        d = g - r
-        dmax = max(dmax, d.abs().max().item())
-        dsq += d.pow(2).sum().item()
+        r = ref[r0:r0 + rows_per_slice].double()
         rsq += r.pow(2).sum().item()
         n += r.numel()
     rms = (rsq / n) ** 0.5
-    return dmax / max(rms, 1e-300), dsq ** 0.5 / max(rsq ** 0.5, 1e-300)
+    dmax, dsq, worst = 0.0, 0.0, 0.0
+    for r0 in range(0, ref.shape[0], rows_per_slice):
+        g, r = got[r0:r0 + rows_per_slice].double(), ref[r0:r0 + rows_per_slice].double()
+        d = (g - r).abs()
+        dmax = max(dmax, d.max().item())
+        dsq += d.pow(2).sum().item()
+        worst = max(worst, (d / (BF16_MAXABS_UNIT * rms + BF16_UNIT_ROUNDOFF * r.abs())).max().item())
+    return dmax / max(rms, 1e-300), dsq ** 0.5 / max(rsq ** 0.5, 1e-300), worst
 
 
 def test_decode_workload_matches_chunked_forward():
     """Every one of the 5120 (row, head) streams of the decode workload: 4096 decode steps
     from a zero state give the outputs and final state of the chunked forward pass run on
     the same inputs as 64 sequences of 4096 tokens (the recurrence and its chunked form
-    are the same map). Both are held to the bf16 bar against each other; the oracle
-    itself is checked on sampled streams above and on the chunked path's workloads."""
+    are the same map). Each side is rounded to bf16 on its own, so y is held to the bf16
+    bar plus one rounding of the element (rel-L2 <= 2e-2, |d_i| <= 5e-2 rms + 2^-8 |y_i|)
+    and the fp32 states to the plain bf16 bar; the oracle itself is checked on sampled
+    streams above and on the chunked path's workloads."""
     from parity import BF16_MAXABS_UNIT, BF16_RELL2
     w = synth.WORKLOADS["decode-b64-H80-N128"]
     say(f"[parity] decode workload against the chunked forward, all streams")
@@ -469,8 +478,9 @@ def test_decode_workload_matches_chunked_forward():
     C = dd["C"].permute(1, 0, 2, 3).contiguous()
     Y, fin = ssd.fwd(X, la, B, C, chunk=128)
     torch.cuda.synchronize()
-    my, ly = _gpu_errors(ys.permute(1, 0, 2, 3), Y)
-    mf, lf = _gpu_errors(state, fin)
-    say(f"[parity] decode vs chunked: y max|d|/rms {my:.3e} rel-L2 {ly:.3e}; state max|d|/rms {mf:.3e} rel-L2 {lf:.3e}")
-    assert my <= BF16_MAXABS_UNIT and ly <= BF16_RELL2
+    my, ly, wy = _gpu_errors(ys.permute(1, 0, 2, 3), Y)
+    mf, lf, _ = _gpu_errors(state, fin)
+    say(f"[parity] decode vs chunked: y max|d|/rms {my:.3e} rel-L2 {ly:.3e} rounded-bar {wy:.3f}; "
+        f"state max|d|/rms {mf:.3e} rel-L2 {lf:.3e}")
+    assert wy <= 1 and ly <= BF16_RELL2
     assert mf <= BF16_MAXABS_UNIT and lf <= BF16_RELL2
