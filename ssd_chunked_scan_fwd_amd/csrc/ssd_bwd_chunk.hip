@@ -705,12 +705,28 @@ bool bwd_chunk_supported(int P, int N, int Q, bool bf16) {
   return ((P == 32 || P == 64) && (N == 64 || N == 128)) || (P == 128 && N == 64);
 }
 
+// Head slices per (chunk, group). One workgroup runs per CU at a time (256
+// CUs), so a launch of wgs * nsl workgroups takes about ceil(wgs * nsl / 256)
+// rounds of ceil(hpg / nsl) heads each. Every slice beyond the first also
+// writes, and the tail kernel reads, dB and dC partials of its chunks; those of
+// 256 chunks cost about one such head-round. The count with the lowest cost
+// wins (the smaller on ties), at most 8: for 128 chunks of 32 heads in one
+// group, 2 slices (256 workgroups of 16 heads); for 261 chunks of 80 heads, 8,
+// where one slice would leave 5 workgroups of all 80 heads to a second round.
 int bwd_chunk_slices(long nslots, int G, int H) {
   const int hpg = H / G;
   const long wgs = nslots * G;
-  long nsl = (256 + wgs - 1) / wgs;  // at least one workgroup per compute unit
-  if (nsl > hpg) nsl = hpg;
-  return nsl < 1 ? 1 : (int)nsl;
+  int best = 1;
+  long best_cost = -1;
+  for (int nsl = 1; nsl <= (hpg < 8 ? hpg : 8); ++nsl) {
+    const long rounds = (wgs * nsl + 255) / 256;
+    const long cost = rounds * ((hpg + nsl - 1) / nsl) * 256 + (long)(nsl - 1) * wgs;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = nsl;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_bwd_chunks(const BwdChunkArgs& a, hipStream_t stream) {
