@@ -518,8 +518,11 @@ __global__ __launch_bounds__(256, 2) void chunk_starts_kernel(const uint16_t* __
                                                              uint16_t* __restrict__ out, int H, int G) {
   constexpr int PT = P / 16, NTW = N / 64, pN = lds_pitch(N), pP = lds_pitch(P);
   static_assert(N % 64 == 0 && P % 16 == 0, "state tiles over four waves");
-  const long blk = blockIdx.x / H;
-  const int h = (int)(blockIdx.x % H);
+  // XCD-aware order: each XCD runs whole blocks, so a block's B rows are read
+  // into one L2 rather than into every XCD's.
+  const long unit = xcd_unit(blockIdx.x, gridDim.x);
+  const long blk = unit / H;
+  const int h = (int)(unit % H);
   const int4 br = btable[blk];
   const int nch = br.z;
   if (nch <= 0) return;

@@ -38,6 +38,14 @@ namespace {
 
 constexpr int kStateThreads = 512;  // 8 waves
 
+__host__ __device__ constexpr int state_pass_rows(int N) { return N > 128 ? 64 : kPassRows; }
+// Waves per SIMD the register budget is cut for (the second launch bound):
+// two for the largest states (P * N of 16384 with 128-row passes, or 32768),
+// else four: with 64-row passes two workgroups then share a CU (their LDS fits).
+__host__ __device__ constexpr int state_min_waves(int P, int N) {
+  return (P * N >= 32768 || (P * N >= 16384 && N <= 128)) ? 2 : 4;
+}
+
 template <int P, int N>
 struct StateCfg {
   static constexpr int BP = lds_pitch(N), XP = lds_pitch(P);
@@ -50,8 +58,11 @@ struct StateCfg {
   static constexpr int WP = (MW / WN) < TP ? (MW / WN) : TP;
   static constexpr int TPW = TP / WP, TNW = TN / WN;
   static constexpr int CBN = N / 8, CBP = P / 8;
-  static constexpr int RB = (kPassRows * CBN + kStateThreads - 1) / kStateThreads;
-  static constexpr int RX = (kPassRows * CBP + kStateThreads - 1) / kStateThreads;
+  // Rows per pass: 128, or 64 for states beyond N = 128, whose B rows would
+  // otherwise hold 70 KB of LDS and leave one workgroup per CU.
+  static constexpr int PR = state_pass_rows(N);
+  static constexpr int RB = (PR * CBN + kStateThreads - 1) / kStateThreads;
+  static constexpr int RX = (PR * CBP + kStateThreads - 1) / kStateThreads;
 };
 
 }  // namespace
@@ -59,7 +70,8 @@ struct StateCfg {
 // The fused form (segment sums computed here) also keeps the key-side
 // exponents of the block's chunks, [Gs * Q] fp32.
 size_t chunk_state_bf16_lds_bytes(int P, int N, int block_tokens) {
-  return ((size_t)kPassRows * lds_pitch(N) + (size_t)kPassRows * lds_pitch(P)) * 2 + 16 * 16 + 16 * 4 +
+  const size_t pr = (size_t)state_pass_rows(N);
+  return (pr * lds_pitch(N) + pr * lds_pitch(P)) * 2 + 16 * 16 + 16 * 4 +
          (size_t)block_tokens * 4;
 }
 
@@ -88,9 +100,9 @@ __device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X
   const int g = h / (H / G);
 
   extern __shared__ uint16_t lds[];
-  uint16_t* bs = lds;                          // [128][BP] B rows of the pass
-  uint16_t* xw = bs + kPassRows * K::BP;       // [128][XP] X rows times their decay to the block end
-  int4* recs = reinterpret_cast<int4*>(xw + kPassRows * K::XP);   // [16] chunk records of the block
+  uint16_t* bs = lds;                          // [PR][BP] B rows of the pass
+  uint16_t* xw = bs + K::PR * K::BP;       // [PR][XP] X rows times their decay to the block end
+  int4* recs = reinterpret_cast<int4*>(xw + K::PR * K::XP);   // [16] chunk records of the block
   float* lastcs = reinterpret_cast<float*>(recs + 16);             // [16] chunk totals (log2)
   float* ckl = lastcs + 16;                                        // [Gs][Q] key-side exponents (FUSED)
 
@@ -106,14 +118,14 @@ __device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X
 #pragma unroll
   for (int u = 0; u < K::RB; ++u) {
     const int idx = tid + kStateThreads * u;
-    brow[u] = idx < kPassRows * K::CBN ? idx / K::CBN : kPassRows;
-    boff[u] = brow[u] < kPassRows ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
+    brow[u] = idx < K::PR * K::CBN ? idx / K::CBN : K::PR;
+    boff[u] = brow[u] < K::PR ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
   }
 #pragma unroll
   for (int u = 0; u < K::RX; ++u) {
     const int idx = tid + kStateThreads * u;
-    xrow[u] = idx < kPassRows * K::CBP ? idx / K::CBP : kPassRows;
-    xoff[u] = xrow[u] < kPassRows ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
+    xrow[u] = idx < K::PR * K::CBP ? idx / K::CBP : K::PR;
+    xoff[u] = xrow[u] < K::PR ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
   }
 
   // The block's chunk records and totals.
@@ -130,7 +142,7 @@ __device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X
     }
   }
   __syncthreads();
-  // One pass = rows r0 .. r0+127 of chunk c; the next pass is loaded while the
+  // One pass = rows r0 .. r0+PR-1 of chunk c; the next pass is loaded while the
   // current one is multiplied.
   u32x4 pb[K::RB], px[K::RX];
   float pcs[K::RX];
@@ -148,7 +160,7 @@ __device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X
     if constexpr (!FUSED) {
       const rsrc_t rc = make_rsrc(ck + (slot * H + h) * (long)Q + r0, valid ? (uint32_t)((Q - r0) * 4) : 0u);
 #pragma unroll
-      for (int u = 0; u < K::RX; ++u) pcs[u] = buf_load_f32(rc, xrow[u] < kPassRows ? (uint32_t)(xrow[u] * 4) : kOffNone);
+      for (int u = 0; u < K::RX; ++u) pcs[u] = buf_load_f32(rc, xrow[u] < K::PR ? (uint32_t)(xrow[u] * 4) : kOffNone);
     }
   };
 
@@ -196,25 +208,25 @@ __device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X
     prefix += a_last;
     const float shift = (total - prefix) + a_last;  // weight of row j: exp2(shift - ck_j)
     const SlotRec cur = rec;
-    for (int r0 = 0; r0 < cur.len; r0 += kPassRows) {
-      const int rows = min(kPassRows, cur.len - r0);
+    for (int r0 = 0; r0 < cur.len; r0 += K::PR) {
+      const int rows = min(K::PR, cur.len - r0);
       __syncthreads();
       // Row weights first: in the fused form they come from LDS and need not
       // wait for the pass loads.
       float wr[K::RX];
 #pragma unroll
       for (int u = 0; u < K::RX; ++u) {
-        const float kj = FUSED ? ckl[c * Q + min(r0 + min(xrow[u], kPassRows - 1), Q - 1)] : pcs[u];
+        const float kj = FUSED ? ckl[c * Q + min(r0 + min(xrow[u], K::PR - 1), Q - 1)] : pcs[u];
         const float e = fast_exp2(shift - kj);
         wr[u] = xrow[u] < rows ? e : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < K::RB; ++u)
-        if (brow[u] < kPassRows)
+        if (brow[u] < K::PR)
           *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + kStateThreads * u) % K::CBN) * 8) = pb[u];
 #pragma unroll
       for (int u = 0; u < K::RX; ++u) {
-        if (xrow[u] < kPassRows) {
+        if (xrow[u] < K::PR) {
           const float w = wr[u];
           u32x4 v;
 #pragma unroll
@@ -223,15 +235,15 @@ __device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X
         }
       }
       // prefetch the next pass: next rows of this chunk, else the next chunk
-      const bool in_chunk = r0 + kPassRows < cur.len;
+      const bool in_chunk = r0 + K::PR < cur.len;
       const bool more = in_chunk || c + 1 < blk.nchunks;
       if (!in_chunk) rec = rec_of(more ? c + 1 : c);
-      load_pass(in_chunk ? cur : rec, in_chunk ? slot : slot + (more ? 1 : 0), in_chunk ? r0 + kPassRows : 0, more);
+      load_pass(in_chunk ? cur : rec, in_chunk ? slot : slot + (more ? 1 : 0), in_chunk ? r0 + K::PR : 0, more);
       __syncthreads();
       if (active) {
         const int nkb = (rows + 31) / 32;
 #pragma unroll
-        for (int kb = 0; kb < kPassRows / 32; ++kb) {
+        for (int kb = 0; kb < K::PR / 32; ++kb) {
           if (kb >= nkb) break;
           u32x4 xa[K::TPW], bb[K::TNW];
 #pragma unroll
@@ -263,7 +275,7 @@ __device__ __forceinline__ void chunk_state_block(const uint16_t* __restrict__ X
 }
 
 template <int P, int N, bool FUSED>
-__global__ __launch_bounds__(kStateThreads, (P * N >= 16384) ? 2 : 4) void chunk_state_bf16_kernel(
+__global__ __launch_bounds__(kStateThreads, state_min_waves(P, N)) void chunk_state_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, int4* __restrict__ ctable,
     int4* __restrict__ btable, float* __restrict__ cs, float* __restrict__ ck,
     float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q, int Gs, SegArgs sa) {
