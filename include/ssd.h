@@ -106,7 +106,13 @@ typedef struct {
  *   table        int32 [nslots][4]: sequence, first token (flattened: row * seqlen + t),
  *                length (0: empty slot), chunk index in sequence
  *   block_table  int32 [nblocks][4]: sequence, first chunk slot, number of chunks
- *                (0: empty slot), 0
+ *                (0: empty slot), and a launch-order word: 0 as the records are
+ *                written; when block slots differ in length (packed sequences, or
+ *                rows not a whole number of state blocks) the state-passing stage
+ *                sets record r's word to (slot + 1) | (nfull << 16), slot being the
+ *                block with rank r by chunk count (most first) and nfull the number
+ *                of slots with the largest count; ssd_chunk_scan then takes the
+ *                blocks in that order (short sequence-end blocks last)
  *   cumsum       fp32  [nslots][H][chunk]: log2(e) * cumulative log_a, restarted per chunk,
  *                positions past the chunk's length repeat its total
  *   key_cumsum   fp32  [nslots][H][chunk]: ssd_fwd_mamba2 only, cumsum_j - log2(dt'_j), the

@@ -556,14 +556,16 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
     const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
-    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q) {
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q,
+    int ranked) {
   constexpr bool GATE = OUT == kOutGated;  // silu(z) gate on the output
   constexpr bool YF32 = OUT == kOutF32;    // fp32 output (partials summed before one rounding)
   using K = PairCfg<P, N>;
   const int HH = H / 2;
-  const long unit = xcd_unit(blockIdx.x, gridDim.x);
-  const int h0 = 2 * (int)(unit % HH);
-  const long m = unit / HH;
+  long m;
+  int hp;
+  scan_unit(btable, blockIdx.x, gridDim.x, HH, ranked, m, hp);
+  const int h0 = 2 * hp;
   const BlockRec blk = load_block(btable, m);
   if (blk.nchunks <= 0) return;
   const int g = h0 / (H / G);
@@ -1018,7 +1020,7 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
                          reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
                          reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
                          reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
-                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q);
+                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q, (int)ranked_blocks(d));
       return hipGetLastError();
     }
   }

@@ -81,6 +81,54 @@ hipError_t launch_chunk_cumsum(const FwdDims& d, const float* log_a, const int32
 // (sequence, head) and moves them with 16-byte loads; the block loop is
 // unrolled so that the loads of sixteen blocks are in flight together.
 // ----------------------------------------------------------------------------
+// The chunk-scan stage's launch order (scan_unit): the last workgroup of the
+// state-passing launch ranks the block slots by chunk count, most first, ties
+// by slot (a counting sort over the 17 possible counts), and writes
+// btable[rank].w = (slot + 1) | (nfull << 16), nfull = the number of slots with
+// the largest count. Slot counts from 2^15 on keep the records' w = 0 (the
+// plain XCD order). 256 threads.
+__device__ void rank_blocks(int4* __restrict__ btable, long nblocks) {
+  __shared__ int cnt[17], start[17], wcnt[4][17], top;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (nblocks >= 32768) return;
+  auto count_of = [&](long m) { return min(max(btable[m].z, 0), 16); };
+  if (tid < 17) cnt[tid] = 0;
+  __syncthreads();
+  for (long m = tid; m < nblocks; m += 256) atomicAdd(&cnt[count_of(m)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0, t = -1;
+    for (int v = 16; v >= 0; --v) {
+      start[v] = acc;
+      acc += cnt[v];
+      if (t < 0 && cnt[v] > 0) t = v;
+    }
+    top = t;
+  }
+  __syncthreads();
+  const int nfull = cnt[top];
+  for (long c0 = 0; c0 < nblocks; c0 += 256) {
+    const long m = c0 + tid;
+    const int v = m < nblocks ? count_of(m) : -1;
+    int below = 0;  // slots of this wave below this lane with the same count
+#pragma unroll
+    for (int b = 0; b <= 16; ++b) {
+      const uint64_t bal = __ballot(v == b);
+      if (v == b) below = __popcll(bal & ((1ull << lane) - 1));
+      if (lane == 0) wcnt[wave][b] = __popcll(bal);
+    }
+    __syncthreads();
+    if (v >= 0) {
+      int pos = start[v] + below;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][v];
+      btable[pos].w = (int)(m + 1) | (nfull << 16);
+    }
+    __syncthreads();
+    if (tid < 17) start[tid] += wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    __syncthreads();
+  }
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restrict__ states,
                                                             const float* __restrict__ bdecay,
@@ -88,7 +136,12 @@ __global__ __launch_bounds__(256) void state_passing_kernel(const float* __restr
                                                             float* __restrict__ final_state,
                                                             const float* __restrict__ init,
                                                             const int32_t* __restrict__ cu,
-                                                            long blocks_per_row, int H, int PN, int span) {
+                                                            long blocks_per_row, int H, int PN, int span,
+                                                            int4* __restrict__ btable, long nblocks, int rank) {
+  if (rank && blockIdx.x == gridDim.x - 1) {  // the extra workgroup: the chunk-scan order
+    rank_blocks(btable, nblocks);
+    return;
+  }
   const int eblocks = (PN / kPassElems + 255) / 256;
   const long unit = blockIdx.x;
   const int e = (int)(unit % eblocks) * (256 * kPassElems) + threadIdx.x * kPassElems;
@@ -103,14 +156,17 @@ hipError_t launch_state_passing(const FwdDims& d, const int32_t* cu, const float
   const int PN = d.P * d.N;
   const int nseq = cu ? d.num_seqs : d.batch;
   const long eblocks = (PN / kPassElems + 255) / 256;
-  dim3 grid((unsigned)(eblocks * d.H * nseq));
+  const int rank = ranked_blocks(d) ? 1 : 0;
+  dim3 grid((unsigned)(eblocks * d.H * nseq + rank));  // + the workgroup that ranks the blocks
   const int span = d.state_block * d.Q;
   if (d.bf16) {
     hipLaunchKernelGGL(state_passing_kernel<true>, grid, dim3(256), 0, stream, ws.bstates, ws.bdecay,
-                       ws.start_states, final_state, init, cu, d.blocks_per_row, d.H, PN, span);
+                       ws.start_states, final_state, init, cu, d.blocks_per_row, d.H, PN, span, ws.btable,
+                       (long)d.nblocks, rank);
   } else {
     hipLaunchKernelGGL(state_passing_kernel<false>, grid, dim3(256), 0, stream, ws.bstates, ws.bdecay,
-                       ws.start_states, final_state, init, cu, d.blocks_per_row, d.H, PN, span);
+                       ws.start_states, final_state, init, cu, d.blocks_per_row, d.H, PN, span, ws.btable,
+                       (long)d.nblocks, rank);
   }
   return hipGetLastError();
 }

@@ -114,6 +114,53 @@ __device__ __forceinline__ long xcd_unit(long bid, long n) {
   return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
 }
 
+// The unit (state block slot m, head group k of `per` per block) that
+// workgroup `bid` of the chunk-scan stage takes, n = slots * per workgroups.
+// When the state-passing stage has ranked the block slots (btable[r].w =
+// (slot + 1) | (nfull << 16) for rank r, slots with the most chunks first and
+// nfull of them full), each XCD gets an equal share of the full blocks' units,
+// in contiguous runs (one block's heads stay on one XCD's L2), ahead of an
+// equal share of the others, which are dealt round robin by decreasing length:
+// with one workgroup per CU the short sequence-end blocks then fill the last
+// round instead of full blocks landing there. With every block full this is
+// xcd_unit's order; without a ranking (ranked = 0, or w = 0) it is
+// xcd_unit's order.
+__device__ __forceinline__ void scan_unit(const int4* __restrict__ btable, long bid, long n, int per, int ranked,
+                                          long& m, int& k) {
+  const int w0 = ranked ? btable[0].w : 0;
+  if (w0 == 0) {
+    const long u = xcd_unit(bid, n);
+    m = u / per;
+    k = (int)(u % per);
+    return;
+  }
+  const long F = (long)(w0 >> 16) * per;  // units of full blocks, ranked first
+  const int x = (int)(bid % kXcds);
+  const long l = bid / kXcds;
+  const long fq = F / kXcds;
+  const int fr = (int)(F % kXcds);
+  const long fx = fq + (x < fr ? 1 : 0);
+  long g;
+  if (l < fx) {
+    g = x * fq + (x < fr ? x : fr) + l;
+  } else {
+    // XCD xx holds ceil((n - xx) / 8) workgroups, fq + (xx < fr) of them full;
+    // the rest counts differ by at most one between XCDs.
+    auto rest = [&](int xx) { return (n - xx + kXcds - 1) / kXcds - (fq + (xx < fr ? 1 : 0)); };
+    long mn = rest(0);
+    for (int xx = 1; xx < kXcds; ++xx) mn = rest(xx) < mn ? rest(xx) : mn;
+    const long j = l - fx;
+    long sig = j * kXcds + x;
+    if (j >= mn) {
+      sig = kXcds * mn;
+      for (int xx = 0; xx < x; ++xx) sig += rest(xx) > mn ? 1 : 0;
+    }
+    g = F + sig;
+  }
+  m = (long)(btable[g / per].w & 0xFFFF) - 1;
+  k = (int)(g % per);
+}
+
 // Chunk-slot record written by the cumsum stage: sequence (row when unpacked),
 // first token in the row, number of tokens (0: empty slot), chunk index in sequence.
 struct SlotRec {

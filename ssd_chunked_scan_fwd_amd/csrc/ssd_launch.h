@@ -22,6 +22,13 @@ struct FwdDims {
   int y_f32 = 0;          // bf16 inputs only: write Y in fp32 (partials the backward pass sums)
 };
 
+// Whether block slots can differ in length (packed sequences, or rows that
+// are not a whole number of state blocks): then the state-passing stage ranks
+// them and the chunk-scan stage takes them in that order (scan_unit).
+inline bool ranked_blocks(const FwdDims& d) {
+  return d.nblocks < 32768 && (d.num_seqs > 0 || d.T % (d.state_block * d.Q) != 0);
+}
+
 struct Workspace {
   int4* table;            // [nslots] chunk records
   int4* btable;           // [nblocks] state-block records
