@@ -279,6 +279,41 @@ def test_stage_intermediates(packed, dt, Q, gs):
     assert torch.equal(Y, Y2) and torch.equal(fin, fin2)
 
 
+def expected_launch_order(counts):
+    """The chunk-scan launch order the state-passing stage writes into the block
+    records' fourth word: slots ranked by chunk count, most first, ties by slot,
+    as (slot + 1) | (nfull << 16) with nfull the number of slots holding the
+    largest count."""
+    c = np.clip(np.asarray(counts, np.int64), 0, 16)
+    order = sorted(range(len(c)), key=lambda m: (-c[m], m))
+    nfull = int(np.sum(c == c.max()))
+    return np.array([(m + 1) | (nfull << 16) for m in order], np.int64)
+
+
+@pytest.mark.parametrize("case", ["packed", "ragged rows", "whole blocks"])
+def test_block_launch_order(case):
+    """Block slots of unequal length are ranked (longest first) for the
+    chunk-scan stage; rows made of whole state blocks keep the plain order (the
+    word stays 0). Y is the same either way."""
+    if case == "packed":
+        d = synth.make_forward_inputs(1, 3 * 1024 + 700, 4, 64, 128, 1, dtype=torch.bfloat16, seed=61,
+                                      lengths=[1024 + 5, 300, 2048 + 128 + 7, 700 - 440])
+    else:
+        T = 2 * 1024 + (300 if case == "ragged rows" else 0)
+        d = synth.make_forward_inputs(3, T, 4, 64, 128, 1, dtype=torch.bfloat16, seed=62)
+    say(f"[parity] block launch order: {case}")
+    ws, Y, fin = stage_run(d, 128, 8)
+    bt = ws.block_table().cpu().numpy().astype(np.int64)
+    if case == "whole blocks":
+        assert np.all(bt[:, 3] == 0)
+    else:
+        assert np.array_equal(bt[:, 3], expected_launch_order(bt[:, 2]))
+    Yr, fr = oracle_fwd(d)
+    dts = dtype_name(d["X"])
+    assert_close(to_f64(Y), Yr, dts, "Y")
+    assert_close(to_f64(fin), fr, dts, "final")
+
+
 @pytest.mark.parametrize("gs", [1, 2, 4, 8, 16])
 def test_state_block_invariance(gs):
     d = synth.make_forward_inputs(2, 3000, 4, 64, 128, 1, dtype=torch.bfloat16, seed=44)
