@@ -547,13 +547,18 @@ __global__ __launch_bounds__(256, 2) void chunk_starts_kernel(const uint16_t* __
         hs[a][pt] = f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
       }
   }
-  // Chunk j + 1's X and B are fetched into registers while chunk j is multiplied.
+  // Chunk j + 1's X and B, and its segment sums, are fetched into registers
+  // while chunk j is multiplied.
   StageT<Q, P, 256> sx;
   StageT<Q, N, 256> sb;
+  float pcs = 0.f, plast = 0.f;
   auto fetch = [&](long slot) {
     const int4 rec = table[slot];
     sx.load(make_rsrc(X + ((long)rec.y * H + h) * P, (uint32_t)rec.z * xstride), xstride, tid);
     sb.load(make_rsrc(Bm + ((long)rec.y * G + g) * N, (uint32_t)rec.z * bstride), bstride, tid);
+    const rsrc_t rc = make_rsrc(cs + (slot * H + h) * (long)Q, (uint32_t)(Q * 4));
+    pcs = buf_load_f32(rc, tid < Q ? (uint32_t)(tid * 4) : kOffNone);
+    plast = buf_load_f32(rc, (uint32_t)((Q - 1) * 4));  // positions past the chunk's end repeat its total
   };
   if (nch > 1) fetch(slot0);
   for (int j = 0; j < nch; ++j) {
@@ -570,9 +575,8 @@ __global__ __launch_bounds__(256, 2) void chunk_starts_kernel(const uint16_t* __
     if (j == nch - 1) break;
     sx.template store<pP>(Xs, tid);
     sb.template store<pN>(Bs, tid);
-    const float* csj = cs + (slot * H + h) * (long)Q;
-    const float cs_last = csj[Q - 1];  // positions past the chunk's end repeat its total
-    for (int i = tid; i < Q; i += 256) wt[i] = fast_exp2(cs_last - csj[i]);
+    const float cs_last = plast;
+    if (tid < Q) wt[tid] = fast_exp2(cs_last - pcs);
     __syncthreads();
     if (j + 2 < nch) fetch(slot + 1);
     const float aj = fast_exp2(cs_last);
