@@ -251,7 +251,11 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 
   // Registers holding the next chunk.
   u32x4 pb[K::RB], px[K::RX];
-  u32x4 pcf[ITW][K::NB];    // C fragments of this wave's query tiles
+  // C fragments of this wave's query tiles: prefetched with the next chunk up
+  // to N = 128; beyond, loaded at the start of their chunk (the registers of a
+  // second set would spill).
+  constexpr bool kPrefetchC = N <= 128;
+  u32x4 pcf[kPrefetchC ? ITW : 1][kPrefetchC ? K::NB : 1];
   float pcs_t = 0.f, pck_t = 0.f, pcs_last = 0.f;
   constexpr int VE = kVTable ? 2 : 1;    // v-table entries per thread: nIt*Q <= VE*512
   float pcs_v[VE], pcs_vm[VE];
@@ -274,10 +278,12 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
       px[u] = buf_load16(rx, xoff[u]);
       pcs_x[u] = buf_load_f32(rk, (uint32_t)(min(xrow[u], Q - 1) * 4));
     }
+    if constexpr (kPrefetchC) {
 #pragma unroll
-    for (int k = 0; k < ITW; ++k)
+      for (int k = 0; k < ITW; ++k)
 #pragma unroll
-      for (int nb = 0; nb < K::NB; ++nb) pcf[k][nb] = buf_load16(rcc, cfoff[k] + nb * 64);
+        for (int nb = 0; nb < K::NB; ++nb) pcf[k][nb] = buf_load16(rcc, cfoff[k] + nb * 64);
+    }
     pcs_last = buf_load_f32(rc, (uint32_t)((Q - 1) * 4));
     pcs_t = buf_load_f32(rc, (uint32_t)(tid * 4));            // zero for tid >= Q
     pck_t = buf_load_f32(rk, (uint32_t)(tid * 4));
@@ -307,6 +313,19 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
     const float cs_last = pcs_last;
 
     __syncthreads();  // every wave is done with the previous chunk's tiles
+    u32x4 cf[ITW][K::NB];
+    if constexpr (kPrefetchC) {
+#pragma unroll
+      for (int k = 0; k < ITW; ++k)
+#pragma unroll
+        for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = pcf[k][nb];
+    } else {
+      const rsrc_t rcc = make_rsrc(C + (tok0 * G + g) * N, (uint32_t)(len * ldb * 2));
+#pragma unroll
+      for (int k = 0; k < ITW; ++k)
+#pragma unroll
+        for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = buf_load16(rcc, cfoff[k] + nb * 64);
+    }
     // B, X and decay-weighted X rows of the first pass.
 #pragma unroll
     for (int u = 0; u < K::RB; ++u)
@@ -368,11 +387,6 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
           *reinterpret_cast<u32x2*>(hsT + hs_row(perm32((n0t + b) * 16 + l16), K::HP) + (p0t + a) * 16 + 4 * g4) = v;
         }
     }
-    u32x4 cf[ITW][K::NB];
-#pragma unroll
-    for (int k = 0; k < ITW; ++k)
-#pragma unroll
-      for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = pcf[k][nb];
     const bool more = c + 1 < blk.nchunks;
     rec = rec_of(more ? c + 1 : c);
     prefetch(rec, slot + (more ? 1 : 0), more);
