@@ -157,9 +157,10 @@ __device__ __forceinline__ void store_yT(const f32x4 (&acc)[TP], rsrc_t ry, uint
 
 }  // namespace
 
-// Chunks of up to 128 tokens keep a separate decay-weighted copy of X; longer
-// chunks weight X in place after the outputs are done (two more barriers).
-static bool scan_in_place(int P, int N, int Q) { return Q > 128 || N > 128 || P > 64; }
+// Chunks of up to 128 tokens with P <= 64 keep a separate decay-weighted copy
+// of X (at N = 256 the tiles then fill 153 KB); the others weight X in place
+// after the outputs are done (two more barriers).
+static bool scan_in_place(int P, int N, int Q) { return Q > 128 || P > 64; }
 
 // The v_j table ([Q/16][Q] fp32) is kept for chunks of up to 128 tokens;
 // longer chunks compute v_j where it is used. cs and ck take [Q] each.
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   const int nIt = Q / 16;
 
   // Weight X in place after the outputs when a second copy does not fit.
-  constexpr bool kInPlace = ITW > 1 || N > 128 || P > 64;
+  constexpr bool kInPlace = ITW > 1 || P > 64;
   extern __shared__ uint16_t lds[];
   uint16_t* bs = lds;                                 // [Q][BP]  B rows
   uint16_t* xs = bs + Q * K::BP;                      // [Q][XP]  X rows
