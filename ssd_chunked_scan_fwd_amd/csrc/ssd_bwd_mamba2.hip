@@ -46,27 +46,52 @@ __host__ __device__ inline M2Map m2_map(int H, int P) {
 template <bool BF16>
 struct Elem {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
-  // Eight consecutive values as fp32.
-  static __device__ __forceinline__ void load8(const T* p, f32x4 v[2]) {
+  static constexpr int kWords = BF16 ? 1 : 2;  // 16-byte pieces per eight values
+  // Eight consecutive values, as loaded (zeros past the buffer range).
+  struct Raw {
+    u32x4 w[kWords];
+  };
+  static __device__ __forceinline__ Raw load(rsrc_t r, uint32_t off) {
+    Raw v;
+#pragma unroll
+    for (int i = 0; i < kWords; ++i) v.w[i] = buf_load16(r, off == kOffNone ? kOffNone : off + 16 * i);
+    return v;
+  }
+  static __device__ __forceinline__ void to_f32(const Raw& w, f32x4 v[2]) {
     if constexpr (BF16) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
-      v[0] = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-      v[1] = f32x4{bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+      const u32x4 a = w.w[0];
+      v[0] = f32x4{bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y)};
+      v[1] = f32x4{bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w)};
     } else {
-      v[0] = reinterpret_cast<const f32x4*>(p)[0];
-      v[1] = reinterpret_cast<const f32x4*>(p)[1];
+      v[0] = __builtin_bit_cast(f32x4, w.w[0]);
+      v[1] = __builtin_bit_cast(f32x4, w.w[1]);
     }
   }
-  static __device__ __forceinline__ void store8(T* p, f32x4 a, f32x4 b) {
+  // Stores at offsets past the range (kOffNone included) are dropped.
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, f32x4 a, f32x4 b) {
     if constexpr (BF16) {
-      *reinterpret_cast<u32x4*>(p) =
-          u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+      buf_store16(u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])},
+                  r, off);
     } else {
-      reinterpret_cast<f32x4*>(p)[0] = a;
-      reinterpret_cast<f32x4*>(p)[1] = b;
+      buf_store16(__builtin_bit_cast(u32x4, a), r, off);
+      buf_store16(__builtin_bit_cast(u32x4, b), r, off == kOffNone ? kOffNone : off + 16);
     }
   }
 };
+
+// Token rows of one thread whose loads are issued together: the loop over a
+// workgroup's rows runs in steps of kM2Rows rows, every load of a step before
+// any use, so that each thread keeps kM2Rows x (streams) 16-byte loads in
+// flight. Rows past the input's end read zeros through the buffer ranges.
+constexpr int kM2Rows = 4;
+
+// Buffer range of a workgroup's token rows of a [tokens][H][P] tensor (an
+// empty range for an absent tensor).
+template <typename T>
+__device__ __forceinline__ rsrc_t rows_rsrc(const T* base, long t0, int ntok, int H, int P) {
+  if (!base) return make_rsrc(nullptr, 0u);
+  return make_rsrc(base + t0 * H * P, (uint32_t)((long)ntok * H * P * sizeof(T)));
+}
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.f + fast_exp2(-v * kLog2e)); }
 
@@ -107,6 +132,8 @@ __global__ __launch_bounds__(kM2Threads) void m2_prep_kernel(const typename Elem
                                                              typename Elem<BF16>::T* __restrict__ dz, long tokens,
                                                              int H, int P) {
   using E = Elem<BF16>;
+  using T = typename E::T;
+  using Raw = typename E::Raw;
   const M2Map mp = m2_map(H, P);
   const int tid = threadIdx.x;
   const int r = tid / mp.tph, q = tid % mp.tpt;
@@ -115,32 +142,53 @@ __global__ __launch_bounds__(kM2Threads) void m2_prep_kernel(const typename Elem
   const float A = -expf(A_log[h]);
   const float bias = dt_bias ? dt_bias[h] : 0.f;
   const long t0 = (long)blockIdx.x * kM2Tokens;
-#pragma unroll 4
-  for (int k = r; k < kM2Tokens; k += mp.tpr) {
-    const long t = t0 + k;
-    if (t >= tokens) break;
-    const long th = t * H + h;
-    const float dtp = softplus_f32(dt[th] + bias);
-    if (q == 0) la[th] = dtp * A;
-    const long o = th * P + 8 * q;
-    f32x4 x[2];
-    E::load8(X + o, x);
-    E::store8(xs + o, x[0] * dtp, x[1] * dtp);
-    if (z) {
-      f32x4 g[2], d[2], vv[2], s[2], ds[2];
-      E::load8(z + o, g);
-      E::load8(dY + o, d);
-      E::load8(v + o, vv);
+  const int ntok = (int)(tokens - t0 < kM2Tokens ? tokens - t0 : kM2Tokens);
+  const rsrc_t rx = rows_rsrc(X, t0, ntok, H, P), rxs = rows_rsrc<T>(xs, t0, ntok, H, P);
+  const rsrc_t rz = rows_rsrc(z, t0, ntok, H, P), rd = rows_rsrc(dY, t0, ntok, H, P);
+  const rsrc_t rv = rows_rsrc(v, t0, ntok, H, P);
+  const rsrc_t rdv = rows_rsrc<T>(dv, t0, ntok, H, P), rdz = rows_rsrc<T>(dz, t0, ntok, H, P);
+  const rsrc_t rdt = rows_rsrc(dt, t0, ntok, H, 1);
+  for (int k0 = r; k0 < kM2Tokens; k0 += kM2Rows * mp.tpr) {
+    uint32_t off[kM2Rows];
+    float dtr[kM2Rows];
+    Raw xr[kM2Rows], gr[kM2Rows], dr[kM2Rows], vr[kM2Rows];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < kM2Rows; ++j) {
+      const int k = k0 + j * mp.tpr;
+      const bool in = k < ntok;
+      off[j] = in ? (uint32_t)(((k * H + h) * P + 8 * q) * sizeof(T)) : kOffNone;
+      dtr[j] = buf_load_f32(rdt, in ? (uint32_t)((k * H + h) * 4) : kOffNone);
+      xr[j] = E::load(rx, off[j]);
+      if (z) {
+        gr[j] = E::load(rz, off[j]);
+        dr[j] = E::load(rd, off[j]);
+        vr[j] = E::load(rv, off[j]);
+      }
+    }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float sg = sigmoid_f32(g[i][c]);
-          s[i][c] = g[i][c] * sg;
-          ds[i][c] = sg * (1.f + g[i][c] * (1.f - sg));
-        }
-      E::store8(dv + o, d[0] * s[0], d[1] * s[1]);
-      E::store8(dz + o, d[0] * vv[0] * ds[0], d[1] * vv[1] * ds[1]);
+    for (int j = 0; j < kM2Rows; ++j) {
+      const int k = k0 + j * mp.tpr;
+      const float dtp = softplus_f32(dtr[j] + bias);
+      if (q == 0 && k < ntok) la[(t0 + k) * H + h] = dtp * A;
+      f32x4 x[2];
+      E::to_f32(xr[j], x);
+      E::store(rxs, off[j], x[0] * dtp, x[1] * dtp);
+      if (z) {
+        f32x4 g[2], d[2], vv[2], sw[2], ds[2];
+        E::to_f32(gr[j], g);
+        E::to_f32(dr[j], d);
+        E::to_f32(vr[j], vv);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float sg = sigmoid_f32(g[i][c]);
+            sw[i][c] = g[i][c] * sg;
+            ds[i][c] = sg * (1.f + g[i][c] * (1.f - sg));
+          }
+        E::store(rdv, off[j], d[0] * sw[0], d[1] * sw[1]);
+        E::store(rdz, off[j], d[0] * vv[0] * ds[0], d[1] * vv[1] * ds[1]);
+      }
     }
   }
 }
@@ -158,6 +206,8 @@ __global__ __launch_bounds__(kM2Threads) void m2_epilogue_kernel(
     const float* __restrict__ dla, typename Elem<BF16>::T* __restrict__ dX, float* __restrict__ ddt,
     float* __restrict__ part, long tokens, int H, int P) {
   using E = Elem<BF16>;
+  using T = typename E::T;
+  using Raw = typename E::Raw;
   const M2Map mp = m2_map(H, P);
   const int tid = threadIdx.x;
   const int r = tid / mp.tph, hl = (tid % mp.tph) / mp.tpt, q = tid % mp.tpt;
@@ -169,36 +219,56 @@ __global__ __launch_bounds__(kM2Threads) void m2_epilogue_kernel(
     const float bias = dt_bias ? dt_bias[h] : 0.f;
     const float Dh = D ? D[h] : 0.f;
     const long t0 = (long)blockIdx.x * kM2Tokens;
-#pragma unroll 4
-    for (int k = r; k < kM2Tokens; k += mp.tpr) {
-      const long t = t0 + k;
-      if (t >= tokens) break;
-      const long th = t * H + h;
-      const float raw = dt[th] + bias;
-      const float dtp = softplus_f32(raw);
-      const long o = th * P + 8 * q;
-      f32x4 x[2], g[2], d[2];
-      E::load8(X + o, x);
-      E::load8(dxs + o, g);
-      E::load8(dY + o, d);
-      if (z) {
-        f32x4 zz[2];
-        E::load8(z + o, zz);
+    const int ntok = (int)(tokens - t0 < kM2Tokens ? tokens - t0 : kM2Tokens);
+    const rsrc_t rx = rows_rsrc(X, t0, ntok, H, P), rg = rows_rsrc(dxs, t0, ntok, H, P);
+    const rsrc_t rd = rows_rsrc(dY, t0, ntok, H, P), rz = rows_rsrc(z, t0, ntok, H, P);
+    const rsrc_t rdx = rows_rsrc<T>(dX, t0, ntok, H, P);
+    const rsrc_t rdt = rows_rsrc(dt, t0, ntok, H, 1), rla = rows_rsrc(dla, t0, ntok, H, 1);
+    for (int k0 = r; k0 < kM2Tokens; k0 += kM2Rows * mp.tpr) {
+      uint32_t off[kM2Rows];
+      float dtr[kM2Rows], lr[kM2Rows];
+      Raw xr[kM2Rows], gr[kM2Rows], dr[kM2Rows], zr[kM2Rows];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) d[i][c] *= zz[i][c] * sigmoid_f32(zz[i][c]);
+      for (int j = 0; j < kM2Rows; ++j) {
+        const int k = k0 + j * mp.tpr;
+        const bool in = k < ntok;
+        const uint32_t th4 = in ? (uint32_t)((k * H + h) * 4) : kOffNone;
+        off[j] = in ? (uint32_t)(((k * H + h) * P + 8 * q) * sizeof(T)) : kOffNone;
+        dtr[j] = buf_load_f32(rdt, th4);
+        lr[j] = buf_load_f32(rla, th4);
+        xr[j] = E::load(rx, off[j]);
+        gr[j] = E::load(rg, off[j]);
+        dr[j] = E::load(rd, off[j]);
+        if (z) zr[j] = E::load(rz, off[j]);
       }
-      E::store8(dX + o, g[0] * dtp + d[0] * Dh, g[1] * dtp + d[1] * Dh);
-      float rr = dot8(g, x);
-      sD += dot8(d, x);
-      rr = group_sum(rr, mp.tpt);  // over the (token, head)'s lanes
-      if (q == 0) {
-        const float l = dla[th];
-        const float g_dt = (rr + A * l) * sigmoid_f32(raw);
-        ddt[th] = g_dt;
-        sA += dtp * l;
-        sB += g_dt;
+#pragma unroll
+      for (int j = 0; j < kM2Rows; ++j) {
+        const int k = k0 + j * mp.tpr;
+        const float raw = dtr[j] + bias;
+        const float dtp = softplus_f32(raw);
+        f32x4 x[2], g[2], d[2];
+        E::to_f32(xr[j], x);
+        E::to_f32(gr[j], g);
+        E::to_f32(dr[j], d);
+        if (z) {
+          f32x4 zz[2];
+          E::to_f32(zr[j], zz);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) d[i][c] *= zz[i][c] * sigmoid_f32(zz[i][c]);
+        }
+        E::store(rdx, off[j], g[0] * dtp + d[0] * Dh, g[1] * dtp + d[1] * Dh);
+        float rr = dot8(g, x);
+        sD += dot8(d, x);     // zero for rows past the end
+        rr = group_sum(rr, mp.tpt);  // over the (token, head)'s lanes
+        if (q == 0 && k < ntok) {
+          const float l = lr[j];
+          const float g_dt = (rr + A * l) * sigmoid_f32(raw);
+          ddt[(t0 + k) * H + h] = g_dt;
+          sA += dtp * l;
+          sB += g_dt;
+        }
       }
     }
   }
