@@ -253,10 +253,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   // Registers holding the next chunk.
   u32x4 pb[K::RB], px[K::RX];
   // C fragments of this wave's query tiles: prefetched with the next chunk up
-  // to N = 128; beyond, loaded at the start of their chunk (the registers of a
-  // second set would spill).
+  // to N = 128; beyond, loaded once this chunk's outputs are done (the
+  // registers of a second set held through the output phase would spill).
   constexpr bool kPrefetchC = N <= 128;
-  u32x4 pcf[kPrefetchC ? ITW : 1][kPrefetchC ? K::NB : 1];
+  u32x4 pcf[ITW][K::NB];
   float pcs_t = 0.f, pck_t = 0.f, pcs_last = 0.f;
   constexpr int VE = kVTable ? 2 : 1;    // v-table entries per thread: nIt*Q <= VE*512
   float pcs_v[VE], pcs_vm[VE];
@@ -306,6 +306,14 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
   };
   SlotRec rec = rec_of(0);
   prefetch(rec, blk.slot0, true);
+  auto load_c = [&](const SlotRec& r, bool valid) {
+    const rsrc_t rcc = make_rsrc(C + ((long)r.tok0 * G + g) * N, valid ? (uint32_t)(r.len * ldb * 2) : 0u);
+#pragma unroll
+    for (int k = 0; k < ITW; ++k)
+#pragma unroll
+      for (int nb = 0; nb < K::NB; ++nb) pcf[k][nb] = buf_load16(rcc, cfoff[k] + nb * 64);
+  };
+  if constexpr (!kPrefetchC) load_c(rec, true);
 
   for (int c = 0; c < blk.nchunks; ++c) {
     const long slot = blk.slot0 + c;
@@ -315,18 +323,10 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
 
     __syncthreads();  // every wave is done with the previous chunk's tiles
     u32x4 cf[ITW][K::NB];
-    if constexpr (kPrefetchC) {
 #pragma unroll
-      for (int k = 0; k < ITW; ++k)
+    for (int k = 0; k < ITW; ++k)
 #pragma unroll
-        for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = pcf[k][nb];
-    } else {
-      const rsrc_t rcc = make_rsrc(C + (tok0 * G + g) * N, (uint32_t)(len * ldb * 2));
-#pragma unroll
-      for (int k = 0; k < ITW; ++k)
-#pragma unroll
-        for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = buf_load16(rcc, cfoff[k] + nb * 64);
-    }
+      for (int nb = 0; nb < K::NB; ++nb) cf[k][nb] = pcf[k][nb];
     // B, X and decay-weighted X rows of the first pass.
 #pragma unroll
     for (int u = 0; u < K::RB; ++u)
@@ -480,6 +480,8 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_bf16_kernel(
       else
         store_yT<K::TP, GATE>(acc, make_rsrc(Y + (tok0 * H + h) * P, (uint32_t)(len * ldx * 2)), yrow, g4, zp);
     }
+
+    if constexpr (!kPrefetchC) load_c(rec, more);
 
     // ---------------- state entering the next chunk of the block
     if (kInPlace && c + 1 < blk.nchunks) {  // weight X in place once every wave is done with it
