@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 typedef enum {
   SSD_OK = 0,
@@ -188,6 +188,33 @@ int32_t ssd_set_state_chain(int32_t mode);
  */
 ssd_status ssd_state_chain_cooperative(const ssd_shape* shape, int32_t chunk, int32_t state_block,
                                        int32_t* cooperative);
+
+/*
+ * Which chunk_scan kernel (diagonal blocks and left factors, paper card
+ * Method 5 / paper section 6, "Diagonal Blocks" and "Left Factors") a forward
+ * call with this shape, chunk length and state block (<= 0: the default)
+ * runs. *kernel receives one of:
+ *   SSD_SCAN_F32        fp32 inputs;
+ *   SSD_SCAN_SINGLE     bf16, one head per workgroup (odd heads per group,
+ *                       headdim 128, dstate 256 or chunk 256);
+ *   SSD_SCAN_PAIR       bf16, two heads of one group per workgroup walking
+ *                       whole chunks, one workgroup per CU;
+ *   SSD_SCAN_HALF_PAIR  bf16, two heads per workgroup walking each chunk in
+ *                       halves of 64 tokens with the state carried between
+ *                       them, two workgroups per CU (chunk 64 or 128, headdim
+ *                       <= 64, dstate <= 128, and at least 512 (state block,
+ *                       head pair) units).
+ * All give results within the same tolerance of the exact recurrence; the
+ * two pair kernels round differently (the second half of a chunk sees the
+ * first through the bf16 state). Host-only: makes no HIP call and keeps
+ * nothing. Packed shapes (num_seqs > 0) are sized as calls with cu_seqlens.
+ * Returns the forward call's shape and state-block errors.
+ */
+#define SSD_SCAN_F32 0
+#define SSD_SCAN_SINGLE 1
+#define SSD_SCAN_PAIR 2
+#define SSD_SCAN_HALF_PAIR 3
+ssd_status ssd_chunk_scan_kernel(const ssd_shape* shape, int32_t chunk, int32_t state_block, int32_t* kernel);
 
 /*
  * Forward pass: Y and final states from zero initial states, with the default

@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     make_shape,
     set_state_chain,
     state_chain_cooperative,
+    chunk_scan_kernel,
     state_passing,
     step,
     step_mamba2,
@@ -37,6 +38,6 @@ __all__ = [
     "fwd", "step", "fwd_mamba2", "step_mamba2", "fwd_noalloc",
     "bwd", "bwd_workspace_bytes", "bwd_mamba2", "bwd_mamba2_workspace_bytes",
     "chunk_cumsum", "chunk_state", "state_passing", "chunk_scan",
-    "set_state_chain", "state_chain_cooperative", "Workspace", "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib",
+    "set_state_chain", "state_chain_cooperative", "chunk_scan_kernel", "Workspace", "Shape", "SSDError", "layout", "workspace_bytes", "make_shape", "lib",
     "default_state_block",
 ]

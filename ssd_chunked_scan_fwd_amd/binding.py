@@ -29,7 +29,7 @@ EXPORTS = ("ssd_abi_version", "ssd_status_string", "ssd_default_state_block", "s
            "ssd_fwd_workspace_bytes", "ssd_fwd", "ssd_fwd_ex", "ssd_chunk_cumsum", "ssd_chunk_state",
            "ssd_state_passing", "ssd_chunk_scan", "ssd_step", "ssd_fwd_mamba2", "ssd_step_mamba2",
            "ssd_bwd_workspace_bytes", "ssd_bwd", "ssd_set_state_chain", "ssd_state_chain_cooperative",
-           "ssd_bwd_mamba2_workspace_bytes", "ssd_bwd_mamba2", "ssd_fwd_noalloc")
+           "ssd_chunk_scan_kernel", "ssd_bwd_mamba2_workspace_bytes", "ssd_bwd_mamba2", "ssd_fwd_noalloc")
 
 
 class SSDError(RuntimeError):
@@ -103,6 +103,8 @@ def lib():
         L.ssd_set_state_chain.argtypes = [i32]
         L.ssd_state_chain_cooperative.restype = ctypes.c_int
         L.ssd_state_chain_cooperative.argtypes = [shp, i32, i32, ctypes.POINTER(i32)]
+        L.ssd_chunk_scan_kernel.restype = ctypes.c_int
+        L.ssd_chunk_scan_kernel.argtypes = [shp, i32, i32, ctypes.POINTER(i32)]
         L.ssd_bwd_mamba2_workspace_bytes.restype = ctypes.c_int
         L.ssd_bwd_mamba2_workspace_bytes.argtypes = [shp, i32, i32, ctypes.POINTER(sz)]
         L.ssd_bwd_mamba2.restype = ctypes.c_int
@@ -478,6 +480,19 @@ def state_chain_cooperative(shape: Shape, chunk: int, state_block: int = 0) -> b
     r = ctypes.c_int32(0)
     _call("ssd_state_chain_cooperative", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(r))
     return bool(r.value)
+
+
+SCAN_KERNELS = ("f32", "single", "pair", "half_pair")
+
+
+def chunk_scan_kernel(shape: Shape, chunk: int, state_block: int = 0) -> str:
+    """ssd_chunk_scan_kernel: the chunk_scan kernel a forward call with this shape
+    runs: "f32", "single" (one head per workgroup), "pair" (two heads, whole
+    chunks, one workgroup per CU) or "half_pair" (two heads, chunks in halves of
+    64 tokens, two workgroups per CU)."""
+    r = ctypes.c_int32(-1)
+    _call("ssd_chunk_scan_kernel", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(r))
+    return SCAN_KERNELS[r.value]
 
 
 def bwd_workspace_bytes(shape: Shape, chunk: int, state_block: int = 0) -> int:

@@ -709,6 +709,26 @@ ssd_status ssd_state_chain_cooperative(const ssd_shape* shape, int32_t chunk, in
   return SSD_OK;
 }
 
+ssd_status ssd_chunk_scan_kernel(const ssd_shape* shape, int32_t chunk, int32_t state_block, int32_t* kernel) {
+  if (!kernel) return SSD_ERR_INVALID_ARGUMENT;
+  static const int32_t kPackedMarker = 0;
+  const int32_t* cu = (shape && shape->num_seqs > 0) ? &kPackedMarker : nullptr;
+  ssd_status st = check_shape(shape, cu, chunk);
+  if (st != SSD_OK) return st;
+  const int32_t gs = state_block > 0 ? state_block : default_state_block(shape, cu, chunk);
+  st = check_state_block(shape, gs);
+  if (st != SSD_OK) return st;
+  ssd_layout L;
+  st = make_layout(shape, cu, chunk, gs, &L);
+  if (st != SSD_OK) return st;
+  const ssd_shape* s = shape;
+  const ssd::FwdDims d{s->batch, s->seqlen, s->nheads, s->ngroups, s->headdim, s->dstate, chunk, gs,
+                       cu ? s->num_seqs : 0, s->dtype == SSD_DTYPE_BF16 ? 1 : 0,
+                       (long)L.slots_per_row, (long)L.nslots, (long)L.blocks_per_row, (long)L.nblocks};
+  *kernel = ssd::chunk_scan_kind(d);
+  return SSD_OK;
+}
+
 ssd_status ssd_bwd(const void* X, const float* log_a, const void* B, const void* C, const int32_t* cu_seqlens,
                    const float* initial_state, const void* dY, const float* dfinal_state, int32_t chunk,
                    int32_t state_block, void* dX, float* dlog_a, void* dB, void* dC, float* dinitial_state,

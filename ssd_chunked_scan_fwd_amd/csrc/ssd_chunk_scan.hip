@@ -910,6 +910,397 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
 }
 
 // ----------------------------------------------------------------------------
+// Two heads, four waves, chunks walked in halves of 64 tokens. The second half
+// of a 128-token chunk sees the first half through the carried state: with cs
+// rebased to the half's start (cs' = cs - cs_63), rows i >= 64 take
+// exp2(cs'_i) C_i h_mid with h_mid = exp2(cs_63) h + sum_{j < 64}
+// exp2(cs_63 - ck_j) X_j B_j^T, the same decomposition one level down (paper
+// section 6: the off-diagonal blocks of a chunk factor through the state).
+// The tiles of one half fill 80 KB of LDS, so two workgroups share a CU and
+// their chains of halves overlap, where the eight-wave kernel runs one chain
+// per CU.
+// ----------------------------------------------------------------------------
+constexpr int kHalfRows = 64;
+constexpr int kHalfWaves = 4;
+constexpr int kHalfThreads = kHalfWaves * 64;
+
+template <int P, int N>
+struct HalfCfg {
+  static constexpr int BP = lds_pitch(N);
+  static constexpr int XP = lds_pitch(P);
+  static constexpr int HP = lds_pitch(P);
+  static_assert(HP >= P + kHalfShift, "the half shift stays inside the row padding");
+  static constexpr int TP = P / 16, TN = N / 16, NB = N / 32;
+  static constexpr int WP = TP < kHalfWaves ? TP : kHalfWaves;
+  static constexpr int WN = TN < kHalfWaves / WP ? TN : kHalfWaves / WP;
+  static constexpr int TPW = TP / WP, TNW = TN / WN;
+  static constexpr int CBN = N / 8, CBP = P / 8;
+  static constexpr int RB = (kHalfRows * CBN + kHalfThreads - 1) / kHalfThreads;
+  static constexpr int RX = (kHalfRows * CBP + kHalfThreads - 1) / kHalfThreads;
+};
+
+// LDS: B rows of a half, X rows of both heads, both entering states, 16 chunk
+// records and cs, ck and the state-update weights of both heads ([2][64]).
+static size_t chunk_scan_half_lds_bytes(int P, int N) {
+  const size_t el = (size_t)kHalfRows * lds_pitch(N) + 2 * (size_t)kHalfRows * lds_pitch(P) +
+                    2 * (size_t)N * lds_pitch(P);
+  return el * 2 + 16 * 16 + (size_t)3 * 2 * kHalfRows * 4;
+}
+
+// Two such workgroups must fit one CU's LDS.
+static bool chunk_scan_half_fits(int P, int N, int Q, int H, int G) {
+  return pair_shape(P, N) && (H / G) % 2 == 0 && (Q == 64 || Q == 128) &&
+         2 * chunk_scan_half_lds_bytes(P, N) <= kMaxLdsBytes;
+}
+
+// The half-chunk kernel needs two units per CU to fill the chip (256 CUs);
+// with fewer, the eight-wave kernel, one per CU, is faster (T = 16384, H = 32,
+// N = 128: 56 against 48 us for 256 units).
+constexpr long kHalfMinUnits = 2 * 256;
+
+int chunk_scan_kind(const FwdDims& d) {
+  if (!d.bf16) return kScanF32;
+  const long units = d.nblocks * (d.H / 2);
+  if (chunk_scan_half_fits(d.P, d.N, d.Q, d.H, d.G) && units >= kHalfMinUnits) return kScanHalfPair;
+  if (chunk_scan_pair_fits(d.P, d.N, d.Q, d.H, d.G)) return kScanPair;
+  return kScanSingle;
+}
+
+template <int P, int N, int OUT>
+__global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
+    const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
+    const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
+    const uint16_t* __restrict__ Z, const float* __restrict__ Dskip, int H, int G, int Q,
+    int ranked) {
+  constexpr bool GATE = OUT == kOutGated;
+  constexpr bool YF32 = OUT == kOutF32;
+  constexpr int R = kHalfRows;
+  using K = HalfCfg<P, N>;
+  const int HH = H / 2;
+  long m;
+  int hp;
+  scan_unit(btable, blockIdx.x, gridDim.x, HH, ranked, m, hp);
+  const int h0 = 2 * hp;
+  const BlockRec blk = load_block(btable, m);
+  if (blk.nchunks <= 0) return;
+  const int g = h0 / (H / G);
+
+  extern __shared__ uint16_t lds[];
+  uint16_t* bs = lds;                                   // [R][BP]      B rows of the half
+  uint16_t* xs = bs + R * K::BP;                        // [2][R][XP]   X rows of both heads
+  uint16_t* hsT = xs + 2 * R * K::XP;                   // [2][N][HP]   entering states, transposed
+  int4* recs = reinterpret_cast<int4*>(hsT + 2 * N * K::HP);  // [16] chunk records
+  float* csl = reinterpret_cast<float*>(recs + 16);     // [2][R] cs rebased to the half's start
+  float* wt = csl + 2 * R;                              // [2][R] exp2(cs_end - ck_j)
+  float* ckl = wt + 2 * R;                              // [2][R] ck rebased to the half's start
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const long ldb = (long)G * N, ldx = (long)H * P;
+  const float Dh[2] = {Dskip ? Dskip[h0] : 0.f, Dskip ? Dskip[h0 + 1] : 0.f};
+  const int it = wave;  // query tile of the half
+
+  uint32_t boff[K::RB], xoff[K::RX];
+  int brow[K::RB], xrow[K::RX];
+#pragma unroll
+  for (int u = 0; u < K::RB; ++u) {
+    const int idx = tid + kHalfThreads * u;
+    brow[u] = idx < R * K::CBN ? idx / K::CBN : R;
+    boff[u] = brow[u] < R ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
+  }
+#pragma unroll
+  for (int u = 0; u < K::RX; ++u) {
+    const int idx = tid + kHalfThreads * u;
+    xrow[u] = idx < R * K::CBP ? idx / K::CBP : R;
+    xoff[u] = xrow[u] < R ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
+  }
+  const uint32_t cfoff = (uint32_t)(((it * 16 + l16) * ldb + 8 * g4) * 2);
+  // This thread's entry of the chunk's cs / ck tables of both heads ([2][Q]).
+  const int th = tid / Q, trow = tid % Q;
+  const uint32_t csoff = tid < 2 * Q ? (uint32_t)(tid * 4) : kOffNone;
+
+  const int wn = wave % K::WN, wp = wave / K::WN;
+  const bool sact = wp < K::WP;
+  const int p0t = wp * K::TPW, n0t = wn * K::TNW;
+  f32x4 hacc[2][K::TPW][K::TNW];
+#pragma unroll
+  for (int hd = 0; hd < 2; ++hd) {
+    const rsrc_t rs = make_rsrc(start + (m * H + h0 + hd) * (long)(P * N), (uint32_t)(P * N * 2));
+#pragma unroll
+    for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+      for (int b = 0; b < K::TNW; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hacc[hd][a][b][r] = bf16_to_f32(buf_load_u16(
+              rs, sact ? (uint32_t)((((p0t + a) * 16 + 4 * g4 + r) * N + (n0t + b) * 16 + l16) * 2) : kOffNone));
+  }
+
+  // The next half's rows and C fragments in flight; its chunk's cs / ck entry
+  // and the chunk's cs at the half's base and end rows of both heads.
+  u32x4 pb[K::RB], px[2][K::RX], pcf[K::NB];
+  float pcs = 0.f, pck = 0.f, pbase[2] = {0.f, 0.f}, pend[2] = {0.f, 0.f};
+  struct Next {
+    rsrc_t rb, rx0, rx1, rc, rcs, rck;
+    uint32_t obase, oend;
+  };
+  // Half `sh` of chunk record r in slot `slot` (valid = false: nothing left).
+  auto next_rsrc = [&](const SlotRec& r, long slot, int sh, bool valid) {
+    const int len = valid ? min(R, r.len - R * sh) : 0;
+    const long t0 = (long)r.tok0 + R * sh;
+    Next n;
+    n.rb = make_rsrc(B + (t0 * G + g) * N, (uint32_t)(len * ldb * 2));
+    n.rc = make_rsrc(C + (t0 * G + g) * N, (uint32_t)(len * ldb * 2));
+    n.rx0 = make_rsrc(X + (t0 * H + h0) * P, (uint32_t)(len * ldx * 2));
+    n.rx1 = make_rsrc(X + (t0 * H + h0 + 1) * P, (uint32_t)(len * ldx * 2));
+    n.rcs = make_rsrc(cs + (slot * H + h0) * (long)Q, valid ? (uint32_t)(2 * Q * 4) : 0u);
+    n.rck = make_rsrc(ck + (slot * H + h0) * (long)Q, valid ? (uint32_t)(2 * Q * 4) : 0u);
+    n.obase = sh ? (uint32_t)((R - 1) * 4) : kOffNone;     // cs_63 for the second half, else 0
+    n.oend = (uint32_t)((min(R * sh + R, Q) - 1) * 4);     // cs at the half's last row
+    return n;
+  };
+  auto load_b = [&](const Next& n) {
+#pragma unroll
+    for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(n.rb, boff[u]);
+  };
+  auto load_x = [&](const Next& n) {
+#pragma unroll
+    for (int u = 0; u < K::RX; ++u) {
+      px[0][u] = buf_load16(n.rx0, xoff[u]);
+      px[1][u] = buf_load16(n.rx1, xoff[u]);
+    }
+    pcs = buf_load_f32(n.rcs, csoff);
+    pck = buf_load_f32(n.rck, csoff);
+    pbase[0] = buf_load_f32(n.rcs, n.obase);
+    pbase[1] = buf_load_f32(n.rcs, n.obase == kOffNone ? kOffNone : n.obase + (uint32_t)(Q * 4));
+    pend[0] = buf_load_f32(n.rcs, n.oend);
+    pend[1] = buf_load_f32(n.rcs, n.oend + (uint32_t)(Q * 4));
+  };
+  auto load_c = [&](const Next& n) {
+#pragma unroll
+    for (int nb = 0; nb < K::NB; ++nb) pcf[nb] = buf_load16(n.rc, cfoff + nb * 64);
+  };
+
+  if (tid < blk.nchunks) recs[tid] = ctable[blk.slot0 + tid];
+  __syncthreads();
+  auto rec_of = [&](int c) {
+    const int4 v = recs[c];
+    return SlotRec{uniform(v.x), uniform(v.y), uniform(v.z), uniform(v.w)};
+  };
+  SlotRec rec = rec_of(0);
+  {
+    const Next n0 = next_rsrc(rec, blk.slot0, 0, true);
+    load_b(n0);
+    load_x(n0);
+    load_c(n0);
+  }
+
+  int c = 0, sh = 0;
+  for (;;) {
+    const int len = min(R, rec.len - R * sh);
+    const long tok0 = (long)rec.tok0 + R * sh;
+    const float base0 = pbase[0], base1 = pbase[1], end0 = pend[0], end1 = pend[1];
+    // The half after this one: the chunk's second half, or the next chunk.
+    const bool second = sh == 0 && rec.len > R;
+    const bool more = second || c + 1 < blk.nchunks;
+    const int nc = second ? c : c + 1;
+    const SlotRec nrec = second ? rec : rec_of(more ? nc : c);
+    const Next nx = next_rsrc(nrec, blk.slot0 + (more ? nc : c), second ? 1 : 0, more);
+
+    __syncthreads();  // every wave is done with the previous half's tiles
+#pragma unroll
+    for (int u = 0; u < K::RB; ++u)
+      if (brow[u] < R)
+        *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + kHalfThreads * u) % K::CBN) * 8) = pb[u];
+#pragma unroll
+    for (int u = 0; u < K::RX; ++u)
+      if (xrow[u] < R) {
+        const int o = xrow[u] * K::XP + ((tid + kHalfThreads * u) % K::CBP) * 8;
+        *reinterpret_cast<u32x4*>(xs + o) = px[0][u];
+        *reinterpret_cast<u32x4*>(xs + R * K::XP + o) = px[1][u];
+      }
+    if (tid < 2 * Q && (trow / R) == sh) {
+      const int e = th * R + (trow % R);
+      const float bse = th ? base1 : base0;
+      csl[e] = pcs - bse;
+      ckl[e] = pck - bse;
+      wt[e] = fast_exp2((th ? end1 : end0) - pck);
+    }
+    if (sact) {
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+          for (int b = 0; b < K::TNW; ++b) {
+            const u32x2 v = {pack_bf16x2(hacc[hd][a][b][0], hacc[hd][a][b][1]),
+                             pack_bf16x2(hacc[hd][a][b][2], hacc[hd][a][b][3])};
+            *reinterpret_cast<u32x2*>(hsT + hd * N * K::HP + hs_row(perm32((n0t + b) * 16 + l16), K::HP) + (p0t + a) * 16 +
+                                      4 * g4) = v;
+          }
+    }
+    __syncthreads();
+    const u32x4* cf = pcf;  // this half's C fragments, until the outputs are stored
+
+    // ---------------- outputs of this wave's query tile, both heads
+    load_b(nx);
+    if (it * 16 < len) {
+      f32x4 acc[2][K::TP];
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) {
+          acc[hd][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int nb = 0; nb < K::NB; ++nb)
+            acc[hd][pt] = mfma16x16x32(frag_k_rows_accpair_hs(hsT + hd * N * K::HP, K::HP, nb * 32, pt * 16, lane), cf[nb],
+                                       acc[hd][pt]);
+        }
+      const float mref[2] = {csl[16 * it], csl[R + 16 * it]};
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        const float em = fast_exp2(mref[hd]);
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] *= em;
+      }
+      const int irow = it * 16 + l16;
+      const float csi[2] = {csl[irow], csl[R + irow]};
+      const int kbd = it >> 1;  // key block holding the diagonal tile
+
+      auto s_block = [&](int kb, f32x4 sv[2]) {
+        u32x4 bfr[2][K::NB];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int nb = 0; nb < K::NB; ++nb) bfr[half][nb] = frag_k_cols(bs, K::BP, (2 * kb + half) * 16, nb * 32, lane);
+        sv[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sv[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int nb = 0; nb < K::NB; ++nb)
+#pragma unroll
+          for (int half = 0; half < 2; ++half) sv[half] = mfma16x16x32(bfr[half][nb], cf[nb], sv[half]);
+      };
+      // Decay (v_j = exp2(m - ck_j) before the diagonal block, the exact
+      // masked exp2(cs_i - ck_j) on it), hi/lo split and Y += M X.
+      auto y_block = [&](int kb, const f32x4 sv[2], bool diag) {
+#pragma unroll
+        for (int hd = 0; hd < 2; ++hd) {
+          const float* kl = ckl + hd * R;
+          uint32_t mw[4], ml[4];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int j0 = (2 * kb + half) * 16 + 4 * g4;
+            const f32x4 cj = *reinterpret_cast<const f32x4*>(kl + j0);
+            float v[4];
+            if (diag) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                v[r] = (j0 + r <= irow ? sv[half][r] * fast_exp2(csi[hd] - cj[r]) : 0.f) + (j0 + r == irow ? Dh[hd] : 0.f);
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] = sv[half][r] * fast_exp2(mref[hd] - cj[r]);
+            }
+            mw[2 * half] = pack_bf16x2(v[0], v[1]);
+            mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
+            ml[2 * half] = pack_bf16x2(v[0] - bf16_lo(mw[2 * half]), v[1] - bf16_hi(mw[2 * half]));
+            ml[2 * half + 1] = pack_bf16x2(v[2] - bf16_lo(mw[2 * half + 1]), v[3] - bf16_hi(mw[2 * half + 1]));
+          }
+          const u32x4 ah = u32x4{mw[0], mw[1], mw[2], mw[3]};
+          const u32x4 al = u32x4{ml[0], ml[1], ml[2], ml[3]};
+          u32x4 xf[K::TP];
+#pragma unroll
+          for (int pt = 0; pt < K::TP; ++pt)
+            xf[pt] = frag_k_rows_accpair(xs + hd * R * K::XP, K::XP, 32 * kb, pt * 16, lane);
+#pragma unroll
+          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(xf[pt], ah, acc[hd][pt]);
+#pragma unroll
+          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(xf[pt], al, acc[hd][pt]);
+        }
+      };
+
+      f32x4 sa[2], sb[2];
+      s_block(0, sa);
+      if (kbd > 0) {
+        s_block(1, sb);
+        y_block(0, sa, false);
+      }
+      const uint32_t yrow = (uint32_t)((it * 16 + l16) * ldx);
+      ZPieces<K::TP> zp[2];
+      if (GATE) {
+#pragma unroll
+        for (int hd = 0; hd < 2; ++hd)
+          load_zT<K::TP>(zp[hd], make_rsrc(Z + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow, g4);
+      }
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        const float u = fast_exp2(csi[hd] - mref[hd]);
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] *= u;
+      }
+      const f32x4 sd[2] = {kbd ? sb[0] : sa[0], kbd ? sb[1] : sa[1]};
+      y_block(kbd, sd, true);
+
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+        if constexpr (YF32)
+          store_yT_f32<K::TP>(acc[hd],
+                              make_rsrc(reinterpret_cast<float*>(Y) + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 4)),
+                              yrow, g4);
+        else
+          store_yT<K::TP, GATE>(acc[hd], make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow,
+                                g4, zp[hd]);
+      // The next half's X rows and C fragments, issued once this half's
+      // outputs are out (one register set of C fragments; the loads' latency
+      // runs under the state update and the staging).
+      load_x(nx);
+      load_c(nx);
+    } else {
+      load_x(nx);
+      load_c(nx);
+    }
+
+    // ---------------- state entering the next half
+    if (more && sact) {
+      const float d0 = fast_exp2(end0 - base0), d1 = fast_exp2(end1 - base1);
+#pragma unroll
+      for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+        for (int b = 0; b < K::TNW; ++b) {
+          hacc[0][a][b] *= d0;
+          hacc[1][a][b] *= d1;
+        }
+      const int nkb = (len + 31) / 32;
+#pragma unroll
+      for (int kb = 0; kb < R / 32; ++kb) {
+        if (kb >= nkb) break;
+        u32x4 bb[K::TNW];
+#pragma unroll
+        for (int b = 0; b < K::TNW; ++b) bb[b] = frag_k_rows_accpair(bs, K::BP, 32 * kb, (n0t + b) * 16, lane);
+#pragma unroll
+        for (int hd = 0; hd < 2; ++hd) {
+          const f32x4 wlo = *reinterpret_cast<const f32x4*>(wt + hd * R + 32 * kb + 4 * g4);
+          const f32x4 whi = *reinterpret_cast<const f32x4*>(wt + hd * R + 32 * kb + 16 + 4 * g4);
+          const float w8[8] = {wlo[0], wlo[1], wlo[2], wlo[3], whi[0], whi[1], whi[2], whi[3]};
+#pragma unroll
+          for (int a = 0; a < K::TPW; ++a) {
+            const u32x4 xa =
+                scale_frag(frag_k_rows_accpair(xs + hd * R * K::XP, K::XP, 32 * kb, (p0t + a) * 16, lane), w8);
+#pragma unroll
+            for (int b = 0; b < K::TNW; ++b) hacc[hd][a][b] = mfma16x16x32(xa, bb[b], hacc[hd][a][b]);
+          }
+        }
+      }
+    }
+    if (!more) break;
+    if (!second) ++c;
+    sh = second ? 1 : 0;
+    rec = nrec;
+  }
+}
+
+// ----------------------------------------------------------------------------
 // fp32 path (plain FMA, fp32 accumulation; one chunk per state block). Query
 // rows in blocks of 32; for
 // each key block j0 <= i0 the masked, decayed block of C B^T is formed in LDS
@@ -1025,7 +1416,22 @@ template <int P, int N, int OUT>
 static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                                    const Workspace& ws, hipStream_t stream, const Mamba2Args& m2) {
   if constexpr (pair_shape(P, N)) {
-    if (chunk_scan_pair_fits(P, N, d.Q, d.H, d.G)) {
+    if (chunk_scan_kind(d) == kScanHalfPair) {
+      const size_t lds = chunk_scan_half_lds_bytes(P, N);
+      auto kern = chunk_scan_half_kernel<P, N, OUT>;
+      if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(kHalfThreads), lds, stream,
+                         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
+                         reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
+                         reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
+                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q, (int)ranked_blocks(d));
+      return hipGetLastError();
+    }
+    if (chunk_scan_kind(d) == kScanPair) {
       const size_t lds = chunk_scan_pair_lds_bytes(P, N, d.Q);
       auto kern = chunk_scan_pair_kernel<P, N, OUT>;
       if (lds > 64 * 1024) {

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = ssd.lib()
-    assert L.ssd_abi_version() == 5
+    assert L.ssd_abi_version() == 6
     for code, name in binding.STATUS.items():
         assert L.ssd_status_string(code).decode() == name
 
@@ -481,3 +481,35 @@ def test_fwd_noalloc_validates_and_bounds_its_scratch():
     assert L.ssd_fwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 128, FAKE, None, ctypes.byref(big), None) == WS_SMALL
     hdr = open(HEADER).read()
     assert "#define SSD_NOALLOC_SCRATCH_BYTES (64u << 20)" in hdr and binding.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+def test_chunk_scan_kernel_query():
+    """ssd_chunk_scan_kernel names the chunk_scan kernel a call takes, with the
+    forward call's own shape checks; host logic only."""
+    L = ssd.lib()
+    r = ctypes.c_int32(9)
+    assert L.ssd_chunk_scan_kernel(ctypes.byref(shape()), 128, 0, None) == INVALID
+    assert L.ssd_chunk_scan_kernel(None, 128, 0, ctypes.byref(r)) == INVALID
+    assert L.ssd_chunk_scan_kernel(ctypes.byref(shape(headdim=48)), 128, 0, ctypes.byref(r)) == UNSUPPORTED
+    assert L.ssd_chunk_scan_kernel(ctypes.byref(shape()), 128, 3, ctypes.byref(r)) == UNSUPPORTED
+    assert r.value == 9   # untouched on error
+    k = binding.chunk_scan_kernel
+    # T = 16384, H = 32 at the default state block of 8 chunks: 256 units, one per CU
+    assert k(shape(), 128) == "pair"
+    # the same with state blocks of 4 chunks: 512 units, two per CU
+    assert k(shape(), 128, 4) == "half_pair"
+    # the state-size sweep (b 8, T 4096, H 32): 512 units at the default
+    assert k(shape(batch=8, seqlen=4096, dstate=64), 128) == "half_pair"
+    assert k(shape(batch=8, seqlen=4096, dstate=128), 128) == "half_pair"
+    assert k(shape(batch=8, seqlen=4096, dstate=256), 128) == "single"
+    # packed H = 80 layer
+    assert k(shape(seqlen=32768, nheads=80, num_seqs=7), 128) == "half_pair"
+    # chunks of 64 need 512 units too; chunks of 32 or 256 never take halves
+    assert k(shape(batch=2, seqlen=2048, nheads=24, dstate=64), 64) == "pair"
+    assert k(shape(batch=2, seqlen=2048, nheads=32, dstate=64), 64, 1) == "half_pair"
+    assert k(shape(batch=2, seqlen=2048, nheads=32, dstate=64), 32, 1) == "pair"
+    assert k(shape(batch=8, seqlen=4096), 256) == "single"
+    # odd heads per group, P = 128, fp32
+    assert k(shape(nheads=3), 128, 1) == "single"
+    assert k(shape(batch=8, seqlen=4096, headdim=128, dstate=64), 128) == "single"
+    assert k(shape(dtype=0), 128) == "f32"
