@@ -187,6 +187,16 @@ def settle_calls(torch, fn, min_calls: int, seconds: float = 0.15):
         torch.cuda.synchronize()
 
 
+def copy_probe(torch, dev, mib: int) -> None:
+    """One elementwise copy (torch.neg, fp32) of `mib` MiB in and out: the known
+    bytes that scale the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    if mib > 0:
+        src = torch.ones(mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+
+
 def timed_calls(torch, stream, fn, n, before=None):
     """Per-call durations (us) of n calls of fn, each between its own HIP events on
     `stream`; `before(i)` runs untimed ahead of call i."""
@@ -371,17 +381,14 @@ def main() -> int:
         for t in range(n):
             ssd.step(state, xs[t], las[t], Bs[t], Cs[t], y=y)
         torch.cuda.synchronize()
-        if args.copy_probe > 0:
-            src = torch.ones(args.copy_probe * (1 << 20) // 4, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            torch.neg(src, out=dst)
-            torch.cuda.synchronize()
+        copy_probe(torch, dev, args.copy_probe)
         print(json.dumps({"profile_decode": wd.name, "steps": n}), flush=True)
         return 0
 
     if args.profile_config:
         log(f"[bench] profile run: forward on {args.profile_config}")
         r = measure_config(ctx, args.profile_config, args.wl_steps, 10, 0.0)
+        copy_probe(torch, dev, args.copy_probe)
         print(json.dumps({"profile_config": args.profile_config, "result": r}), flush=True)
         return 0
 
