@@ -60,13 +60,20 @@ ssd_status check_shape(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
 
 int32_t default_state_block(const ssd_shape* s, const int32_t* cu, int32_t chunk) {
   if (s->dtype != SSD_DTYPE_BF16) return 1;
-  // Longer state blocks cut the right-factor and state traffic; keep at least
-  // about two (state block, head) workgroups per CU (256 CUs).
+  // Longer state blocks cut the right-factor and state traffic and the
+  // chunk-state stage's per-block set-up; keep at least 384 (state block,
+  // head) workgroups, about one and a half per CU (256 CUs). States of 64 KB
+  // (headdim * dstate >= 16384) double that traffic, so they take blocks of up
+  // to 16 chunks, the others up to 8. Measured forward calls (us) by block size
+  // 2 / 4 / 8 / 16: b 2, T 2048, H 24, N 64, chunk 64: 35.9 / 32.6 / 40.6 / 66.0;
+  // T 16384, H 32, N 128: 101.8 / 83.9 / 79.5 / 119.6; b 8, T 4096, H 32, N 256:
+  // 440.7 / 349.5 / 288.9 / 260.3; packed T 32768, H 80: 595.7 / 473.5 / 425.5 / 464.3.
   const int64_t T = s->seqlen;
   const int64_t chunks = cu ? (T / chunk + s->num_seqs) : (int64_t)s->batch * ((T + chunk - 1) / chunk);
   const int64_t units = chunks * s->nheads;
+  const int32_t cap = (int64_t)s->headdim * s->dstate >= 16384 ? 16 : 8;
   int32_t gs = 1;
-  while (gs < 8 && units / (2 * gs) >= 512) gs *= 2;
+  while (gs < cap && units / (2 * gs) >= 384) gs *= 2;
   return gs;
 }
 

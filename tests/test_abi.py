@@ -102,6 +102,14 @@ def test_default_state_block():
     assert ssd.layout(shape(), 128, 0).nblocks == 128 // gs
     # small problems keep one chunk per state block
     assert L.ssd_default_state_block(ctypes.byref(shape(seqlen=256, nheads=2)), 128) == 1
+    # the measured choices: b 2, T 2048, H 24, N 64, chunk 64 -> 4; the headline -> 8;
+    # the N = 256 sweep (64 KB states) -> 16; the packed H = 80 layer -> 8
+    d = lambda sh, q: L.ssd_default_state_block(ctypes.byref(sh), q)
+    assert d(shape(batch=2, seqlen=2048, nheads=24, dstate=64), 64) == 4
+    assert d(shape(), 128) == 8
+    assert d(shape(batch=8, seqlen=4096, dstate=256), 128) == 16
+    assert d(shape(batch=8, seqlen=4096, dstate=128), 128) == 8
+    assert d(shape(seqlen=32768, nheads=80, num_seqs=5), 128) == 8
 
 
 @pytest.mark.parametrize("kw,gs,code", [(dict(), 3, UNSUPPORTED), (dict(), 32, UNSUPPORTED),
