@@ -196,14 +196,16 @@ ssd_status ssd_state_chain_cooperative(const ssd_shape* shape, int32_t chunk, in
  * runs. *kernel receives one of:
  *   SSD_SCAN_F32        fp32 inputs;
  *   SSD_SCAN_SINGLE     bf16, one head per workgroup (odd heads per group,
- *                       headdim 128, dstate 256 or chunk 256);
+ *                       headdim 128 or chunk 256);
  *   SSD_SCAN_PAIR       bf16, two heads of one group per workgroup walking
  *                       whole chunks, one workgroup per CU;
  *   SSD_SCAN_HALF_PAIR  bf16, two heads per workgroup walking each chunk in
  *                       halves of 64 tokens with the state carried between
  *                       them, two workgroups per CU (chunk 64 or 128, headdim
  *                       <= 64, dstate <= 128, and at least 512 (state block,
- *                       head pair) units).
+ *                       head pair) units);
+ *   SSD_SCAN_HALF_PAIR_WIDE  the same walk for dstate 256 (headdim <= 64,
+ *                       chunk 64 or 128), eight waves, one workgroup per CU.
  * All give results within the same tolerance of the exact recurrence; the
  * two pair kernels round differently (the second half of a chunk sees the
  * first through the bf16 state). Host-only: makes no HIP call and keeps
@@ -214,6 +216,7 @@ ssd_status ssd_state_chain_cooperative(const ssd_shape* shape, int32_t chunk, in
 #define SSD_SCAN_SINGLE 1
 #define SSD_SCAN_PAIR 2
 #define SSD_SCAN_HALF_PAIR 3
+#define SSD_SCAN_HALF_PAIR_WIDE 4
 ssd_status ssd_chunk_scan_kernel(const ssd_shape* shape, int32_t chunk, int32_t state_block, int32_t* kernel);
 
 /*

@@ -482,14 +482,15 @@ def state_chain_cooperative(shape: Shape, chunk: int, state_block: int = 0) -> b
     return bool(r.value)
 
 
-SCAN_KERNELS = ("f32", "single", "pair", "half_pair")
+SCAN_KERNELS = ("f32", "single", "pair", "half_pair", "half_pair_wide")
 
 
 def chunk_scan_kernel(shape: Shape, chunk: int, state_block: int = 0) -> str:
     """ssd_chunk_scan_kernel: the chunk_scan kernel a forward call with this shape
     runs: "f32", "single" (one head per workgroup), "pair" (two heads, whole
-    chunks, one workgroup per CU) or "half_pair" (two heads, chunks in halves of
-    64 tokens, two workgroups per CU)."""
+    chunks, one workgroup per CU), "half_pair" (two heads, chunks in halves of
+    64 tokens, two workgroups per CU) or "half_pair_wide" (the same walk at
+    dstate 256, one workgroup per CU)."""
     r = ctypes.c_int32(-1)
     _call("ssd_chunk_scan_kernel", ctypes.byref(shape), int(chunk), int(state_block), ctypes.byref(r))
     return SCAN_KERNELS[r.value]

@@ -921,22 +921,23 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
 // per CU.
 // ----------------------------------------------------------------------------
 constexpr int kHalfRows = 64;
-constexpr int kHalfWaves = 4;
-constexpr int kHalfThreads = kHalfWaves * 64;
 
-template <int P, int N>
+// NW waves: 4 (each wave one query tile of the half for both heads) or 8 (each
+// wave one query tile for one head; the wider states, N = 256).
+template <int P, int N, int NW>
 struct HalfCfg {
+  static constexpr int NT = NW * 64;
   static constexpr int BP = lds_pitch(N);
   static constexpr int XP = lds_pitch(P);
   static constexpr int HP = lds_pitch(P);
   static_assert(HP >= P + kHalfShift, "the half shift stays inside the row padding");
   static constexpr int TP = P / 16, TN = N / 16, NB = N / 32;
-  static constexpr int WP = TP < kHalfWaves ? TP : kHalfWaves;
-  static constexpr int WN = TN < kHalfWaves / WP ? TN : kHalfWaves / WP;
+  static constexpr int WP = TP < NW ? TP : NW;
+  static constexpr int WN = TN < NW / WP ? TN : NW / WP;
   static constexpr int TPW = TP / WP, TNW = TN / WN;
   static constexpr int CBN = N / 8, CBP = P / 8;
-  static constexpr int RB = (kHalfRows * CBN + kHalfThreads - 1) / kHalfThreads;
-  static constexpr int RX = (kHalfRows * CBP + kHalfThreads - 1) / kHalfThreads;
+  static constexpr int RB = (kHalfRows * CBN + NT - 1) / NT;
+  static constexpr int RX = (kHalfRows * CBP + NT - 1) / NT;
 };
 
 // LDS: B rows of a half, X rows of both heads, both entering states, 16 chunk
@@ -947,27 +948,40 @@ static size_t chunk_scan_half_lds_bytes(int P, int N) {
   return el * 2 + 16 * 16 + (size_t)3 * 2 * kHalfRows * 4;
 }
 
-// Two such workgroups must fit one CU's LDS.
+// Four-wave form: two such workgroups must fit one CU's LDS.
 static bool chunk_scan_half_fits(int P, int N, int Q, int H, int G) {
   return pair_shape(P, N) && (H / G) % 2 == 0 && (Q == 64 || Q == 128) &&
          2 * chunk_scan_half_lds_bytes(P, N) <= kMaxLdsBytes;
 }
 
-// The half-chunk kernel needs two units per CU to fill the chip (256 CUs);
-// with fewer, the eight-wave kernel, one per CU, is faster (T = 16384, H = 32,
-// N = 128: 56 against 48 us for 256 units).
+// Eight-wave form for N = 256 (P <= 64): one workgroup per CU.
+static constexpr bool half_wide_shape(int P, int N) { return P <= 64 && N == 256; }
+static bool chunk_scan_half_wide_fits(int P, int N, int Q, int H, int G) {
+  return half_wide_shape(P, N) && (H / G) % 2 == 0 && (Q == 64 || Q == 128) &&
+         chunk_scan_half_lds_bytes(P, N) <= kMaxLdsBytes;
+}
+
+// The four-wave half-chunk kernel needs two units per CU to fill the chip
+// (256 CUs); with fewer, the eight-wave whole-chunk kernel, one per CU, is
+// faster (T = 16384, H = 32, N = 128: 56 against 48 us for 256 units). At
+// N = 256 the eight-wave half-chunk form replaces the single-head kernel
+// (b 8, T 4096, H 32: 173 against 194 us at state blocks of 16 chunks): it
+// stages each half's B rows once for both heads.
 constexpr long kHalfMinUnits = 2 * 256;
 
 int chunk_scan_kind(const FwdDims& d) {
   if (!d.bf16) return kScanF32;
   const long units = d.nblocks * (d.H / 2);
   if (chunk_scan_half_fits(d.P, d.N, d.Q, d.H, d.G) && units >= kHalfMinUnits) return kScanHalfPair;
+  if (chunk_scan_half_wide_fits(d.P, d.N, d.Q, d.H, d.G)) return kScanHalfPairWide;
   if (chunk_scan_pair_fits(d.P, d.N, d.Q, d.H, d.G)) return kScanPair;
   return kScanSingle;
 }
 
-template <int P, int N, int OUT>
-__global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
+// HW: heads per wave in the output phase (2: four waves; 1: eight waves, each
+// (query tile, head) on its own wave, S^T formed by both waves of a tile).
+template <int P, int N, int OUT, int HW>
+__global__ __launch_bounds__((HW == 2 ? 4 : 8) * 64, 2) void chunk_scan_half_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, const uint16_t* __restrict__ C,
     const int4* __restrict__ ctable, const int4* __restrict__ btable, const float* __restrict__ cs,
     const float* __restrict__ ck, const uint16_t* __restrict__ start, uint16_t* __restrict__ Y,
@@ -976,7 +990,8 @@ __global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
   constexpr bool GATE = OUT == kOutGated;
   constexpr bool YF32 = OUT == kOutF32;
   constexpr int R = kHalfRows;
-  using K = HalfCfg<P, N>;
+  constexpr int NW = HW == 2 ? 4 : 8;
+  using K = HalfCfg<P, N, NW>;
   const int HH = H / 2;
   long m;
   int hp;
@@ -1000,19 +1015,20 @@ __global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
   const int l16 = lane & 15, g4 = lane >> 4;
   const long ldb = (long)G * N, ldx = (long)H * P;
   const float Dh[2] = {Dskip ? Dskip[h0] : 0.f, Dskip ? Dskip[h0 + 1] : 0.f};
-  const int it = wave;  // query tile of the half
+  const int it = wave & 3;                  // query tile of the half
+  const int h1 = HW == 2 ? 0 : wave >> 2;   // first head of this wave's outputs
 
   uint32_t boff[K::RB], xoff[K::RX];
   int brow[K::RB], xrow[K::RX];
 #pragma unroll
   for (int u = 0; u < K::RB; ++u) {
-    const int idx = tid + kHalfThreads * u;
+    const int idx = tid + K::NT * u;
     brow[u] = idx < R * K::CBN ? idx / K::CBN : R;
     boff[u] = brow[u] < R ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
   }
 #pragma unroll
   for (int u = 0; u < K::RX; ++u) {
-    const int idx = tid + kHalfThreads * u;
+    const int idx = tid + K::NT * u;
     xrow[u] = idx < R * K::CBP ? idx / K::CBP : R;
     xoff[u] = xrow[u] < R ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
   }
@@ -1113,11 +1129,11 @@ __global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
 #pragma unroll
     for (int u = 0; u < K::RB; ++u)
       if (brow[u] < R)
-        *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + kHalfThreads * u) % K::CBN) * 8) = pb[u];
+        *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + K::NT * u) % K::CBN) * 8) = pb[u];
 #pragma unroll
     for (int u = 0; u < K::RX; ++u)
       if (xrow[u] < R) {
-        const int o = xrow[u] * K::XP + ((tid + kHalfThreads * u) % K::CBP) * 8;
+        const int o = xrow[u] * K::XP + ((tid + K::NT * u) % K::CBP) * 8;
         *reinterpret_cast<u32x4*>(xs + o) = px[0][u];
         *reinterpret_cast<u32x4*>(xs + R * K::XP + o) = px[1][u];
       }
@@ -1144,49 +1160,57 @@ __global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
     __syncthreads();
     const u32x4* cf = pcf;  // this half's C fragments, until the outputs are stored
 
-    // ---------------- outputs of this wave's query tile, both heads
+    // ---------------- outputs of this wave's query tile (both heads, or head h1)
     load_b(nx);
     if (it * 16 < len) {
-      f32x4 acc[2][K::TP];
+      f32x4 acc[HW][K::TP];
 #pragma unroll
-      for (int hd = 0; hd < 2; ++hd)
+      for (int q = 0; q < HW; ++q)
 #pragma unroll
         for (int pt = 0; pt < K::TP; ++pt) {
-          acc[hd][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[q][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int nb = 0; nb < K::NB; ++nb)
-            acc[hd][pt] = mfma16x16x32(frag_k_rows_accpair_hs(hsT + hd * N * K::HP, K::HP, nb * 32, pt * 16, lane), cf[nb],
-                                       acc[hd][pt]);
+            acc[q][pt] = mfma16x16x32(frag_k_rows_accpair_hs(hsT + (h1 + q) * N * K::HP, K::HP, nb * 32, pt * 16, lane),
+                                      cf[nb], acc[q][pt]);
         }
-      const float mref[2] = {csl[16 * it], csl[R + 16 * it]};
-#pragma unroll
-      for (int hd = 0; hd < 2; ++hd) {
-        const float em = fast_exp2(mref[hd]);
-#pragma unroll
-        for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] *= em;
-      }
+      float mref[HW], csi[HW];
       const int irow = it * 16 + l16;
-      const float csi[2] = {csl[irow], csl[R + irow]};
+#pragma unroll
+      for (int q = 0; q < HW; ++q) {
+        mref[q] = csl[(h1 + q) * R + 16 * it];
+        csi[q] = csl[(h1 + q) * R + irow];
+        const float em = fast_exp2(mref[q]);
+#pragma unroll
+        for (int pt = 0; pt < K::TP; ++pt) acc[q][pt] *= em;
+      }
       const int kbd = it >> 1;  // key block holding the diagonal tile
 
       auto s_block = [&](int kb, f32x4 sv[2]) {
-        u32x4 bfr[2][K::NB];
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-          for (int nb = 0; nb < K::NB; ++nb) bfr[half][nb] = frag_k_cols(bs, K::BP, (2 * kb + half) * 16, nb * 32, lane);
         sv[0] = f32x4{0.f, 0.f, 0.f, 0.f};
         sv[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr int NG = K::NB > 4 ? 2 : 1;  // groups of B fragments in registers at once
 #pragma unroll
-        for (int nb = 0; nb < K::NB; ++nb)
+        for (int ng = 0; ng < NG; ++ng) {
+          u32x4 bfr[2][K::NB / NG];
 #pragma unroll
-          for (int half = 0; half < 2; ++half) sv[half] = mfma16x16x32(bfr[half][nb], cf[nb], sv[half]);
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int nb = 0; nb < K::NB / NG; ++nb)
+              bfr[half][nb] = frag_k_cols(bs, K::BP, (2 * kb + half) * 16, (ng * (K::NB / NG) + nb) * 32, lane);
+#pragma unroll
+          for (int nb = 0; nb < K::NB / NG; ++nb)
+#pragma unroll
+            for (int half = 0; half < 2; ++half)
+              sv[half] = mfma16x16x32(bfr[half][nb], cf[ng * (K::NB / NG) + nb], sv[half]);
+        }
       };
       // Decay (v_j = exp2(m - ck_j) before the diagonal block, the exact
       // masked exp2(cs_i - ck_j) on it), hi/lo split and Y += M X.
       auto y_block = [&](int kb, const f32x4 sv[2], bool diag) {
 #pragma unroll
-        for (int hd = 0; hd < 2; ++hd) {
+        for (int q = 0; q < HW; ++q) {
+          const int hd = h1 + q;
           const float* kl = ckl + hd * R;
           uint32_t mw[4], ml[4];
 #pragma unroll
@@ -1197,10 +1221,10 @@ __global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
             if (diag) {
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                v[r] = (j0 + r <= irow ? sv[half][r] * fast_exp2(csi[hd] - cj[r]) : 0.f) + (j0 + r == irow ? Dh[hd] : 0.f);
+                v[r] = (j0 + r <= irow ? sv[half][r] * fast_exp2(csi[q] - cj[r]) : 0.f) + (j0 + r == irow ? Dh[hd] : 0.f);
             } else {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) v[r] = sv[half][r] * fast_exp2(mref[hd] - cj[r]);
+              for (int r = 0; r < 4; ++r) v[r] = sv[half][r] * fast_exp2(mref[q] - cj[r]);
             }
             mw[2 * half] = pack_bf16x2(v[0], v[1]);
             mw[2 * half + 1] = pack_bf16x2(v[2], v[3]);
@@ -1214,9 +1238,9 @@ __global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
           for (int pt = 0; pt < K::TP; ++pt)
             xf[pt] = frag_k_rows_accpair(xs + hd * R * K::XP, K::XP, 32 * kb, pt * 16, lane);
 #pragma unroll
-          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(xf[pt], ah, acc[hd][pt]);
+          for (int pt = 0; pt < K::TP; ++pt) acc[q][pt] = mfma16x16x32(xf[pt], ah, acc[q][pt]);
 #pragma unroll
-          for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] = mfma16x16x32(xf[pt], al, acc[hd][pt]);
+          for (int pt = 0; pt < K::TP; ++pt) acc[q][pt] = mfma16x16x32(xf[pt], al, acc[q][pt]);
         }
       };
 
@@ -1227,30 +1251,31 @@ __global__ __launch_bounds__(kHalfThreads, 2) void chunk_scan_half_kernel(
         y_block(0, sa, false);
       }
       const uint32_t yrow = (uint32_t)((it * 16 + l16) * ldx);
-      ZPieces<K::TP> zp[2];
+      ZPieces<K::TP> zp[HW];
       if (GATE) {
 #pragma unroll
-        for (int hd = 0; hd < 2; ++hd)
-          load_zT<K::TP>(zp[hd], make_rsrc(Z + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow, g4);
+        for (int q = 0; q < HW; ++q)
+          load_zT<K::TP>(zp[q], make_rsrc(Z + (tok0 * H + h0 + h1 + q) * P, (uint32_t)(len * ldx * 2)), yrow, g4);
       }
 #pragma unroll
-      for (int hd = 0; hd < 2; ++hd) {
-        const float u = fast_exp2(csi[hd] - mref[hd]);
+      for (int q = 0; q < HW; ++q) {
+        const float u = fast_exp2(csi[q] - mref[q]);
 #pragma unroll
-        for (int pt = 0; pt < K::TP; ++pt) acc[hd][pt] *= u;
+        for (int pt = 0; pt < K::TP; ++pt) acc[q][pt] *= u;
       }
       const f32x4 sd[2] = {kbd ? sb[0] : sa[0], kbd ? sb[1] : sa[1]};
       y_block(kbd, sd, true);
 
 #pragma unroll
-      for (int hd = 0; hd < 2; ++hd)
+      for (int q = 0; q < HW; ++q)
         if constexpr (YF32)
-          store_yT_f32<K::TP>(acc[hd],
-                              make_rsrc(reinterpret_cast<float*>(Y) + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 4)),
+          store_yT_f32<K::TP>(acc[q],
+                              make_rsrc(reinterpret_cast<float*>(Y) + (tok0 * H + h0 + h1 + q) * P,
+                                        (uint32_t)(len * ldx * 4)),
                               yrow, g4);
         else
-          store_yT<K::TP, GATE>(acc[hd], make_rsrc(Y + (tok0 * H + h0 + hd) * P, (uint32_t)(len * ldx * 2)), yrow,
-                                g4, zp[hd]);
+          store_yT<K::TP, GATE>(acc[q], make_rsrc(Y + (tok0 * H + h0 + h1 + q) * P, (uint32_t)(len * ldx * 2)),
+                                yrow, g4, zp[q]);
       // The next half's X rows and C fragments, issued once this half's
       // outputs are out (one register set of C fragments; the loads' latency
       // runs under the state update and the staging).
@@ -1418,13 +1443,13 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
   if constexpr (pair_shape(P, N)) {
     if (chunk_scan_kind(d) == kScanHalfPair) {
       const size_t lds = chunk_scan_half_lds_bytes(P, N);
-      auto kern = chunk_scan_half_kernel<P, N, OUT>;
+      auto kern = chunk_scan_half_kernel<P, N, OUT, 2>;
       if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
       }
-      hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(kHalfThreads), lds, stream,
+      hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(4 * 64), lds, stream,
                          reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
                          reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
                          reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
@@ -1440,6 +1465,21 @@ static hipError_t launch_scan_bf16(const FwdDims& d, const void* X, const void* 
         if (e != hipSuccess) return e;
       }
       hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(kScanThreads), lds, stream,
+                         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
+                         reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
+                         reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),
+                         reinterpret_cast<const uint16_t*>(m2.z), m2.D, d.H, d.G, d.Q, (int)ranked_blocks(d));
+      return hipGetLastError();
+    }
+  }
+  if constexpr (half_wide_shape(P, N)) {
+    if (chunk_scan_kind(d) == kScanHalfPairWide) {
+      const size_t lds = chunk_scan_half_lds_bytes(P, N);
+      auto kern = chunk_scan_half_kernel<P, N, OUT, 1>;
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(8 * 64), lds, stream,
                          reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B),
                          reinterpret_cast<const uint16_t*>(C), ws.table, ws.btable, ws.cs, ws.ck,
                          reinterpret_cast<const uint16_t*>(ws.start_states), reinterpret_cast<uint16_t*>(Y),

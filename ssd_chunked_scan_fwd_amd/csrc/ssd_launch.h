@@ -89,8 +89,9 @@ hipError_t chunk_state_chain_cooperative(const FwdDims& d, bool* cooperative);
 // Which chunk_scan kernel a call takes (values of the public SSD_SCAN_* codes):
 // fp32; bf16 one head per workgroup; two heads per workgroup walking whole
 // chunks (eight waves, one workgroup per CU); two heads per workgroup walking
-// chunks in halves of 64 tokens (four waves, two workgroups per CU).
-constexpr int kScanF32 = 0, kScanSingle = 1, kScanPair = 2, kScanHalfPair = 3;
+// chunks in halves of 64 tokens (four waves, two workgroups per CU; or, for
+// dstate 256, eight waves, one per CU).
+constexpr int kScanF32 = 0, kScanSingle = 1, kScanPair = 2, kScanHalfPair = 3, kScanHalfPairWide = 4;
 int chunk_scan_kind(const FwdDims& d);
 hipError_t launch_chunk_scan(const FwdDims& d, const void* X, const void* B, const void* C, void* Y,
                              const Workspace& ws, hipStream_t stream, const Mamba2Args& m2 = Mamba2Args{});

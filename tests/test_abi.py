@@ -509,7 +509,9 @@ def test_chunk_scan_kernel_query():
     # the state-size sweep (b 8, T 4096, H 32): 512 units at the default
     assert k(shape(batch=8, seqlen=4096, dstate=64), 128) == "half_pair"
     assert k(shape(batch=8, seqlen=4096, dstate=128), 128) == "half_pair"
-    assert k(shape(batch=8, seqlen=4096, dstate=256), 128) == "single"
+    assert k(shape(batch=8, seqlen=4096, dstate=256), 128) == "half_pair_wide"
+    assert k(shape(batch=8, seqlen=4096, dstate=256, nheads=3), 128) == "single"
+    assert k(shape(batch=8, seqlen=4096, dstate=256), 32) == "single"
     # packed H = 80 layer
     assert k(shape(seqlen=32768, nheads=80, num_seqs=7), 128) == "half_pair"
     # chunks of 64 need 512 units too; chunks of 32 or 256 never take halves

@@ -537,16 +537,50 @@ HALF_CASES = [
     (2, 700, 64, 16, 32, 2, 64, 1, None),         # P = 16, N = 32, two groups
     (1, 1500, 64, 64, 128, 1, 128, 1, (1, 300)),  # packed: sequences of 1..300 tokens
 ]
+# N = 256 takes the eight-wave form of the same kernel whatever the unit count.
+HALF_WIDE_CASES = [
+    (1, 300, 2, 64, 256, 1, 128, 0, None),        # last chunk 44 tokens
+    (2, 700, 4, 32, 256, 2, 64, 2, None),         # P = 32, chunks of 64, two groups
+    (1, 1000, 2, 16, 256, 1, 128, 4, None),       # P = 16, last chunk 104 tokens
+    (1, 1200, 4, 64, 256, 1, 128, 2, (1, 300)),   # packed
+]
 
 
-@pytest.mark.parametrize("case", HALF_CASES, ids=lambda c: "b{}-T{}-H{}-P{}-N{}-G{}-Q{}-gs{}{}".format(
-    *c[:8], "-packed" if c[8] else ""))
+@pytest.mark.parametrize("case", [c + ("half_pair",) for c in HALF_CASES] +
+                         [c + ("half_pair_wide",) for c in HALF_WIDE_CASES],
+                         ids=lambda c: "b{}-T{}-H{}-P{}-N{}-G{}-Q{}-gs{}{}".format(*c[:8], "-packed" if c[8] else ""))
 def test_half_chunk_kernel(case):
-    b, T, H, P, N, G, Q, gs, varlen = case
+    b, T, H, P, N, G, Q, gs, varlen, kind = case
     d = synth.make_forward_inputs(b, T, H, P, N, G, dtype=torch.bfloat16, seed=3000 + T + N, varlen=varlen)
     sh = ssd.make_shape(d["X"], d["B"], d.get("cu_seqlens"))
-    assert ssd.chunk_scan_kernel(sh, Q, gs) == "half_pair"
-    check_fwd(d, Q, f"half-chunk {case}", gs=gs)
+    assert ssd.chunk_scan_kernel(sh, Q, gs) == kind
+    check_fwd(d, Q, f"half-chunk {kind} {case}", gs=gs)
+
+
+def test_wide_kernel_mamba2_and_single_head_fallback():
+    """N = 256: the eight-wave half-chunk kernel in the Mamba-2 call (gate, skip,
+    dt' weights) from initial states, and odd heads per group still on the
+    single-head kernel, both against the oracle."""
+    from parity import assert_close_gated
+    b, T, H, P, N, Q = 2, 500, 4, 64, 256, 128
+    m = synth.make_mamba2_inputs(b, T, H, P, N, 1, dtype=torch.bfloat16, seed=3201)
+    sh = ssd.make_shape(m["X"], m["B"])
+    assert ssd.chunk_scan_kernel(sh, Q, 0) == "half_pair_wide"
+    h0 = _init_states(b, H, P, N, 3202)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in m.items()}
+    say(f"[parity] wide half-chunk Mamba-2 call b={b} T={T} H={H} N={N}")
+    Y, fin = ssd.fwd_mamba2(dev["X"], dev["dt"], dev["A_log"], dev["B"], dev["C"], dt_bias=dev["dt_bias"],
+                            D=dev["D"], z=dev["z"], chunk=Q, initial_state=h0.cuda())
+    torch.cuda.synchronize()
+    args = (to_f64(m["X"]), to_f64(m["dt"]), to_f64(m["dt_bias"]), to_f64(m["A_log"]), to_f64(m["D"]))
+    init = h0.double().numpy()
+    Yr, fr = oracle.mamba2_forward(*args, to_f64(m["z"]), to_f64(m["B"]), to_f64(m["C"]), init=init)
+    Yu, _ = oracle.mamba2_forward(*args, None, to_f64(m["B"]), to_f64(m["C"]), init=init)
+    assert_close_gated(to_f64(Y), Yr, Yu, oracle.silu(to_f64(m["z"])), "bf16", "wide Mamba-2 Y")
+    assert_close(to_f64(fin), fr, "bf16", "wide Mamba-2 final")
+    d = synth.make_forward_inputs(1, 300, 3, 64, 256, 1, dtype=torch.bfloat16, seed=3203)
+    assert ssd.chunk_scan_kernel(ssd.make_shape(d["X"], d["B"]), 128, 0) == "single"
+    check_fwd(d, 128, "N = 256, odd heads per group (single-head kernel)")
 
 
 def test_half_chunk_kernel_initial_state_and_gate():
