@@ -910,15 +910,18 @@ __global__ __launch_bounds__(kScanThreads, 1) void chunk_scan_pair_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// Two heads, four waves, chunks walked in halves of 64 tokens. The second half
-// of a 128-token chunk sees the first half through the carried state: with cs
-// rebased to the half's start (cs' = cs - cs_63), rows i >= 64 take
+// Two heads per workgroup, chunks walked in halves of 64 tokens. The second
+// half of a 128-token chunk sees the first half through the carried state:
+// with cs rebased to the half's start (cs' = cs - cs_63), rows i >= 64 take
 // exp2(cs'_i) C_i h_mid with h_mid = exp2(cs_63) h + sum_{j < 64}
 // exp2(cs_63 - ck_j) X_j B_j^T, the same decomposition one level down (paper
 // section 6: the off-diagonal blocks of a chunk factor through the state).
-// The tiles of one half fill 80 KB of LDS, so two workgroups share a CU and
-// their chains of halves overlap, where the eight-wave kernel runs one chain
-// per CU.
+// Up to N = 128 the tiles of one half fill 80 KB of LDS and four waves carry
+// them, so two workgroups share a CU and their chains of halves overlap, where
+// the eight-wave whole-chunk kernel runs one chain per CU. At N = 256 (139 KB,
+// one workgroup per CU) eight waves each take one (query tile, head): each
+// half's B rows are staged once for both heads, where the single-head kernel
+// stages them per head.
 // ----------------------------------------------------------------------------
 constexpr int kHalfRows = 64;
 
