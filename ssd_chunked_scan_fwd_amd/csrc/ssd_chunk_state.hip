@@ -283,6 +283,260 @@ __global__ __launch_bounds__(kStateThreads, state_min_waves(P, N)) void chunk_st
                                  xcd_unit(blockIdx.x, gridDim.x));
 }
 
+// Two heads of one group per workgroup, 64-row passes: each pass stages the B
+// rows once for both heads. The eight waves hold both heads' states (four
+// waves per head). Each state tile accumulates its products in the same
+// token order as chunk_state_block, so the results are bitwise the same. With
+// more (block, head) units than one round of the one-head form (two
+// workgroups per CU), this form runs half the workgroups, each pass half as
+// many rows for two heads (b 8, T 4096, H 32, N 128: forward call 155.6 ->
+// 141.1 us; packed H = 80 layer 423.7 -> 394.3 us; 47 KB of LDS and 96
+// registers at P = 64, N = 128, two workgroups per CU).
+template <int P, int N>
+struct PairStateCfg {
+  static constexpr int BP = lds_pitch(N), XP = lds_pitch(P);
+  static constexpr int TP = P / 16, TN = N / 16;
+  static constexpr int WN = TN < 2 ? TN : 2;
+  static constexpr int WP = (4 / WN) < TP ? (4 / WN) : TP;
+  static constexpr int TPW = TP / WP, TNW = TN / WN;
+  static constexpr int CBN = N / 8, CBP = P / 8;
+  static constexpr int PR = 64;
+  static constexpr int RB = (PR * CBN + kStateThreads - 1) / kStateThreads;
+  static constexpr int RX = (PR * CBP + kStateThreads - 1) / kStateThreads;
+};
+
+size_t chunk_state_pair_lds_bytes(int P, int N, int block_tokens) {
+  return ((size_t)64 * lds_pitch(N) + 2 * (size_t)64 * lds_pitch(P)) * 2 + 16 * 16 + 2 * 16 * 4 +
+         2 * (size_t)block_tokens * 4;
+}
+
+template <int P, int N, bool FUSED>
+__device__ __forceinline__ void chunk_state_pair_block(const uint16_t* __restrict__ X, const uint16_t* __restrict__ B,
+                                                       int4* __restrict__ ctable, int4* __restrict__ btable,
+                                                       float* __restrict__ cs, float* __restrict__ ck,
+                                                       float* __restrict__ bstates, float* __restrict__ bdecay,
+                                                       int H, int G, int Q, int Gs, const SegArgs& sa, long unit) {
+  using K = PairStateCfg<P, N>;
+  const int HH = H / 2;
+  const int hp = (int)(unit % HH);
+  const long m = unit / HH;
+  const int h0 = 2 * hp;
+  BlockRec blk;
+  if constexpr (FUSED) {
+    const int row = (int)(m / sa.blocks_per_row);
+    const int4 b = block_record(sa.cu, sa.S, row, m - row * sa.blocks_per_row, Q, Gs, sa.slots_per_row);
+    if (hp == 0 && threadIdx.x == 0) btable[m] = b;
+    blk = BlockRec{b.x, b.y, b.z};
+  } else {
+    blk = load_block(btable, m);
+  }
+  if (blk.nchunks <= 0) return;
+  const int g = h0 / (H / G);
+  const int GQ = Gs * Q;
+
+  extern __shared__ uint16_t lds[];
+  uint16_t* bs = lds;                                             // [64][BP] B rows of the pass
+  uint16_t* xw = bs + K::PR * K::BP;                              // [2][64][XP] weighted X rows of both heads
+  int4* recs = reinterpret_cast<int4*>(xw + 2 * K::PR * K::XP);   // [16] chunk records of the block
+  float* lastcs = reinterpret_cast<float*>(recs + 16);            // [2][16] chunk totals (log2)
+  float* ckl = lastcs + 32;                                       // [2][Gs * Q] key-side exponents (FUSED)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int hw = wave >> 2;  // head of this wave's state tiles
+  const int wq = wave & 3;
+  const int wn = wq % K::WN, wp = wq / K::WN;
+  const bool active = wp < K::WP;
+  const int p0t = wp * K::TPW, n0t = wn * K::TNW;
+  const long ldb = (long)G * N, ldx = (long)H * P;
+
+  uint32_t boff[K::RB], xoff[K::RX];
+  int brow[K::RB], xrow[K::RX];
+#pragma unroll
+  for (int u = 0; u < K::RB; ++u) {
+    const int idx = tid + kStateThreads * u;
+    brow[u] = idx < K::PR * K::CBN ? idx / K::CBN : K::PR;
+    boff[u] = brow[u] < K::PR ? (uint32_t)((brow[u] * ldb + (idx % K::CBN) * 8) * 2) : kOffNone;
+  }
+#pragma unroll
+  for (int u = 0; u < K::RX; ++u) {
+    const int idx = tid + kStateThreads * u;
+    xrow[u] = idx < K::PR * K::CBP ? idx / K::CBP : K::PR;
+    xoff[u] = xrow[u] < K::PR ? (uint32_t)((xrow[u] * ldx + (idx % K::CBP) * 8) * 2) : kOffNone;
+  }
+
+  if (tid < blk.nchunks) {
+    if constexpr (FUSED) {
+      const long slot = blk.slot0 + tid;
+      const int row = (int)(slot / sa.slots_per_row);
+      const int4 r = chunk_record(sa.cu, sa.S, row, slot - row * sa.slots_per_row, sa.T, Q, sa.slots_per_row);
+      recs[tid] = r;
+      if (hp == 0) ctable[slot] = r;
+    } else {
+      recs[tid] = ctable[blk.slot0 + tid];
+      lastcs[tid] = cs[((blk.slot0 + tid) * H + h0) * (long)Q + Q - 1];
+      lastcs[16 + tid] = cs[((blk.slot0 + tid) * H + h0 + 1) * (long)Q + Q - 1];
+    }
+  }
+  __syncthreads();
+  u32x4 pb[K::RB], px[2][K::RX];
+  float pcs[2][K::RX];
+  auto load_pass = [&](const SlotRec& r, long slot, int r0, bool valid) {
+    const int rows = valid ? r.len - r0 : 0;
+    const rsrc_t rb = make_rsrc(B + (((long)r.tok0 + r0) * G + g) * N, (uint32_t)(rows * ldb * 2));
+    const rsrc_t rx0 = make_rsrc(X + (((long)r.tok0 + r0) * H + h0) * P, (uint32_t)(rows * ldx * 2));
+    const rsrc_t rx1 = make_rsrc(X + (((long)r.tok0 + r0) * H + h0 + 1) * P, (uint32_t)(rows * ldx * 2));
+#pragma unroll
+    for (int u = 0; u < K::RB; ++u) pb[u] = buf_load16(rb, boff[u]);
+#pragma unroll
+    for (int u = 0; u < K::RX; ++u) {
+      px[0][u] = buf_load16(rx0, xoff[u]);
+      px[1][u] = buf_load16(rx1, xoff[u]);
+    }
+    if constexpr (!FUSED) {
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd) {
+        const rsrc_t rc = make_rsrc(ck + (slot * H + h0 + hd) * (long)Q + r0, valid ? (uint32_t)((Q - r0) * 4) : 0u);
+#pragma unroll
+        for (int u = 0; u < K::RX; ++u)
+          pcs[hd][u] = buf_load_f32(rc, xrow[u] < K::PR ? (uint32_t)(xrow[u] * 4) : kOffNone);
+      }
+    }
+  };
+  auto rec_of = [&](int c) {
+    const int4 v = recs[c];
+    return SlotRec{uniform(v.x), uniform(v.y), uniform(v.z), uniform(v.w)};
+  };
+  SlotRec rec = rec_of(0);
+  load_pass(rec, blk.slot0, 0, true);
+  if constexpr (FUSED) {
+    // Segment sums of both heads' chunks (wave w takes (chunk, head) tasks w, w + 8, ...).
+    const bool m2 = sa.dt != nullptr;
+    const float A0 = m2 ? -expf(sa.A_log[h0]) : 1.f, A1 = m2 ? -expf(sa.A_log[h0 + 1]) : 1.f;
+    const float b0 = (m2 && sa.dt_bias) ? sa.dt_bias[h0] : 0.f, b1 = (m2 && sa.dt_bias) ? sa.dt_bias[h0 + 1] : 0.f;
+    for (int t = wave; t < 2 * blk.nchunks; t += kStateThreads / 64) {
+      const int hd = t & 1, c = t >> 1;
+      const int h = h0 + hd;
+      const float A = hd ? A1 : A0;
+      const float bias = hd ? b1 : b0;
+      const int4 r = recs[c];
+      const long slot = blk.slot0 + c;
+      const float* src = (m2 ? sa.dt : sa.la) + (long)r.y * H + h;
+      const float tot = wave_segsum(
+          [&](int j) {
+            const float v = src[(long)j * H];
+            return m2 ? softplus_f32(v + bias) : v;
+          },
+          r.z, Q, m2, A, cs + (slot * H + h) * (long)Q, m2 ? ck + (slot * H + h) * (long)Q : nullptr,
+          ckl + hd * GQ + c * Q, lane);
+      if (lane == 0) lastcs[hd * 16 + c] = tot;
+    }
+    __syncthreads();
+  }
+  float total[2] = {0.f, 0.f};
+  for (int c = 0; c < blk.nchunks; ++c) {
+    total[0] += lastcs[c];
+    total[1] += lastcs[16 + c];
+  }
+
+  f32x4 acc[K::TPW][K::TNW];
+#pragma unroll
+  for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+    for (int b = 0; b < K::TNW; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float prefix[2] = {0.f, 0.f};
+  for (int c = 0; c < blk.nchunks; ++c) {
+    const long slot = blk.slot0 + c;
+    float shift[2];
+#pragma unroll
+    for (int hd = 0; hd < 2; ++hd) {
+      const float a_last = lastcs[hd * 16 + c];
+      prefix[hd] += a_last;
+      shift[hd] = (total[hd] - prefix[hd]) + a_last;  // weight of row j: exp2(shift - ck_j)
+    }
+    const SlotRec cur = rec;
+    for (int r0 = 0; r0 < cur.len; r0 += K::PR) {
+      const int rows = min(K::PR, cur.len - r0);
+      __syncthreads();
+      float wr[2][K::RX];
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int u = 0; u < K::RX; ++u) {
+          const float kj = FUSED ? ckl[hd * GQ + c * Q + min(r0 + min(xrow[u], K::PR - 1), Q - 1)] : pcs[hd][u];
+          const float e = fast_exp2(shift[hd] - kj);
+          wr[hd][u] = xrow[u] < rows ? e : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < K::RB; ++u)
+        if (brow[u] < K::PR)
+          *reinterpret_cast<u32x4*>(bs + brow[u] * K::BP + ((tid + kStateThreads * u) % K::CBN) * 8) = pb[u];
+#pragma unroll
+      for (int hd = 0; hd < 2; ++hd)
+#pragma unroll
+        for (int u = 0; u < K::RX; ++u) {
+          if (xrow[u] < K::PR) {
+            const float w = wr[hd][u];
+            u32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = pack_bf16x2(bf16_lo(px[hd][u][q]) * w, bf16_hi(px[hd][u][q]) * w);
+            *reinterpret_cast<u32x4*>(xw + hd * K::PR * K::XP + xrow[u] * K::XP +
+                                      ((tid + kStateThreads * u) % K::CBP) * 8) = v;
+          }
+        }
+      const bool in_chunk = r0 + K::PR < cur.len;
+      const bool more = in_chunk || c + 1 < blk.nchunks;
+      if (!in_chunk) rec = rec_of(more ? c + 1 : c);
+      load_pass(in_chunk ? cur : rec, in_chunk ? slot : slot + (more ? 1 : 0), in_chunk ? r0 + K::PR : 0, more);
+      __syncthreads();
+      if (active) {
+        const int nkb = (rows + 31) / 32;
+        const uint16_t* xh = xw + hw * K::PR * K::XP;
+#pragma unroll
+        for (int kb = 0; kb < K::PR / 32; ++kb) {
+          if (kb >= nkb) break;
+          u32x4 xa[K::TPW], bb[K::TNW];
+#pragma unroll
+          for (int a = 0; a < K::TPW; ++a) xa[a] = frag_k_rows_accpair(xh, K::XP, 32 * kb, (p0t + a) * 16, lane);
+#pragma unroll
+          for (int b = 0; b < K::TNW; ++b) bb[b] = frag_k_rows_accpair(bs, K::BP, 32 * kb, (n0t + b) * 16, lane);
+#pragma unroll
+          for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+            for (int b = 0; b < K::TNW; ++b) acc[a][b] = mfma16x16x32(xa[a], bb[b], acc[a][b]);
+        }
+      }
+    }
+  }
+
+  if (tid == 0) {
+    bdecay[m * H + h0] = total[0];
+    bdecay[m * H + h0 + 1] = total[1];
+  }
+  if (!active) return;
+  float* out = bstates + (m * H + h0 + hw) * (long)(P * N);
+#pragma unroll
+  for (int a = 0; a < K::TPW; ++a)
+#pragma unroll
+    for (int b = 0; b < K::TNW; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = (p0t + a) * 16 + 4 * g4 + r;
+        const int n = (n0t + b) * 16 + l16;
+        out[p * N + n] = acc[a][b][r];
+      }
+}
+
+template <int P, int N, bool FUSED>
+__global__ __launch_bounds__(kStateThreads, 4) void chunk_state_pair_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ B, int4* __restrict__ ctable,
+    int4* __restrict__ btable, float* __restrict__ cs, float* __restrict__ ck,
+    float* __restrict__ bstates, float* __restrict__ bdecay, int H, int G, int Q, int Gs, SegArgs sa) {
+  chunk_state_pair_block<P, N, FUSED>(X, B, ctable, btable, cs, ck, bstates, bdecay, H, G, Q, Gs, sa,
+                                      xcd_unit(blockIdx.x, gridDim.x));
+}
+
 // The state chain in one launch: every workgroup computes its block's right
 // factor as above, a grid-wide barrier (cooperative launch: all workgroups are
 // resident) makes them visible, and the same grid then runs the centre-factor
@@ -410,9 +664,31 @@ __global__ __launch_bounds__(256) void chunk_state_f32_kernel(const float* __res
 
 // ----------------------------------------------------------------------------
 
+// The head-pair form: heads in pairs within a group, states of up to 64 x 128,
+// and more (block, head) units than one round of the one-head form (two
+// workgroups per CU on 256 CUs).
+static bool chunk_state_pair_use(const FwdDims& d) {
+  return d.P <= 64 && d.N <= 128 && (d.H / d.G) % 2 == 0 && d.nblocks * d.H > 2 * 256;
+}
+
 template <int P, int N, bool FUSED>
 static hipError_t launch_state_bf16(const FwdDims& d, const void* X, const void* B, const Workspace& ws,
                                     hipStream_t stream, const SegArgs& sa) {
+  if constexpr (P <= 64 && N <= 128) {
+    if (chunk_state_pair_use(d)) {
+      const size_t lds = chunk_state_pair_lds_bytes(P, N, FUSED ? d.state_block * d.Q : 0);
+      auto kern = chunk_state_pair_kernel<P, N, FUSED>;
+      if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL(kern, dim3((unsigned)(d.nblocks * (d.H / 2))), dim3(kStateThreads), lds, stream,
+                         reinterpret_cast<const uint16_t*>(X), reinterpret_cast<const uint16_t*>(B), ws.table,
+                         ws.btable, ws.cs, ws.ck, ws.bstates, ws.bdecay, d.H, d.G, d.Q, d.state_block, sa);
+      return hipGetLastError();
+    }
+  }
   const size_t lds = chunk_state_bf16_lds_bytes(P, N, FUSED ? d.state_block * d.Q : 0);
   auto kern = chunk_state_bf16_kernel<P, N, FUSED>;
   if (lds > 64 * 1024) {

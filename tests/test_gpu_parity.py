@@ -208,6 +208,39 @@ def _slots(units, span, rows, T, cu):
     return out
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_head_pair_chunk_state(packed):
+    """Shapes with more than 512 (state block, head) units and heads in pairs take
+    the head-pair chunk_state (two heads per workgroup, 64-row passes): its right
+    factors against the oracle restarted at every block start, and the stage
+    entry point (segment sums from the cumsum stage) bitwise equal to the fused
+    form inside ssd_fwd."""
+    if packed:
+        lengths = [300, 17, 64, 65, 129, 400, 25]
+        rows, T, H, P, N, Q, gs = 1, sum(lengths), 64, 32, 64, 64, 2
+    else:
+        lengths = None
+        rows, T, H, P, N, Q, gs = 2, 1100, 32, 64, 128, 128, 1
+    d = synth.make_forward_inputs(rows, T, H, P, N, 1, dtype=torch.bfloat16, seed=3301, lengths=lengths)
+    say(f"[parity] head-pair chunk_state packed={packed} H={H} P={P} N={N} Q={Q} state_block={gs}")
+    ws, Y, fin = stage_run(d, Q, gs)
+    assert ws.layout.nblocks * H > 512 and H % 2 == 0
+    cu = None if d["cu_seqlens"] is None else d["cu_seqlens"].numpy()
+    X, la, B, C = (to_f64(d[k]) for k in ("X", "log_a", "B", "C"))
+    blocks = oracle.chunk_segments(rows, T, Q * gs, cu)
+    bslots = _slots(blocks, Q * gs, rows, T, cu)
+    _, bst_ref, _ = oracle.scan(X, la, B, C, segments=blocks, want_y=False)
+    bst = ws.block_states().clone()
+    bdec = ws.block_decay().clone()
+    assert_close(bst.cpu().numpy()[bslots], bst_ref, "bf16", "head-pair block states")
+    dd = to_dev(d)
+    ssd.fwd(dd["X"], dd["log_a"], dd["B"], dd["C"], cu_seqlens=dd.get("cu_seqlens"), chunk=Q, state_block=gs,
+            workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ws.block_states()[bslots], bst[bslots])
+    assert torch.equal(ws.block_decay()[bslots], bdec[bslots])
+
+
 @pytest.mark.parametrize("packed,dt,Q,gs", [(False, torch.bfloat16, 64, 1), (True, torch.bfloat16, 64, 1),
                                             (False, torch.bfloat16, 32, 4), (True, torch.bfloat16, 32, 2),
                                             (False, torch.float32, 32, 1), (True, torch.float32, 16, 1)])
