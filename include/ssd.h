@@ -196,7 +196,8 @@ ssd_status ssd_state_chain_cooperative(const ssd_shape* shape, int32_t chunk, in
  * runs. *kernel receives one of:
  *   SSD_SCAN_F32        fp32 inputs;
  *   SSD_SCAN_SINGLE     bf16, one head per workgroup (odd heads per group,
- *                       headdim 128 or chunk 256);
+ *                       headdim 128, chunk 256, and at dstate 256 any chunk
+ *                       other than 64 and 128);
  *   SSD_SCAN_PAIR       bf16, two heads of one group per workgroup walking
  *                       whole chunks, one workgroup per CU;
  *   SSD_SCAN_HALF_PAIR  bf16, two heads per workgroup walking each chunk in
