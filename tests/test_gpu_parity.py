@@ -569,6 +569,7 @@ HALF_CASES = [
     (4, 1000, 64, 32, 128, 1, 128, 2, None),      # last chunk 104 tokens, two chunks per block
     (2, 700, 64, 16, 32, 2, 64, 1, None),         # P = 16, N = 32, two groups
     (1, 1500, 64, 64, 128, 1, 128, 1, (1, 300)),  # packed: sequences of 1..300 tokens
+    (1, 1500, 64, 64, 64, 1, 64, 2, (1, 200)),    # packed, chunks of 64, two chunks per state block
 ]
 # N = 256 takes the eight-wave form of the same kernel whatever the unit count.
 HALF_WIDE_CASES = [
