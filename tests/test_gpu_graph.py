@@ -64,19 +64,25 @@ def replay_and_check(g, outs, refs, between):
             assert_bitwise(o, r, f"replay {i}, output {k}")
 
 
-def test_forward_graph():
-    d = synth.make_forward_inputs(1, 3000, 8, 64, 128, 1, dtype=torch.bfloat16, seed=6100)
+# (T, H, N, state block, chunk_scan kernel): the whole-chunk two-head kernel;
+# the half-chunk kernel with the head-pair chunk_state (768 units); the wide
+# half-chunk kernel at N = 256.
+@pytest.mark.parametrize("T,H,N,gs,kind", [(3000, 8, 128, 0, "pair"), (3000, 64, 128, 1, "half_pair"),
+                                           (1000, 4, 256, 0, "half_pair_wide")])
+def test_forward_graph(T, H, N, gs, kind):
+    d = synth.make_forward_inputs(1, T, H, 64, N, 1, dtype=torch.bfloat16, seed=6100)
     X, la, B, C = (d[k].cuda() for k in ("X", "log_a", "B", "C"))
     shape = ssd.make_shape(X, B, None)
-    ws = ssd.Workspace(shape, 128, X.device)
+    assert ssd.chunk_scan_kernel(shape, 128, gs) == kind
+    ws = ssd.Workspace(shape, 128, X.device, gs)
     Y0, f0 = ssd.fwd(X, la, B, C, chunk=128, workspace=ws)
     torch.cuda.synchronize()
     Y0, f0 = Y0.clone(), f0.clone()
     Yg, fg = torch.empty_like(Y0), torch.empty_like(f0)
     g, _ = capture(lambda: ssd.fwd(X, la, B, C, chunk=128, Y=Yg, final_state=fg, workspace=ws))
-    e = synth.make_forward_inputs(1, 3000, 8, 64, 128, 1, dtype=torch.bfloat16, seed=6101)
+    e = synth.make_forward_inputs(1, T, H, 64, N, 1, dtype=torch.bfloat16, seed=6101)
     Xe, lae, Be, Ce = (e[k].cuda() for k in ("X", "log_a", "B", "C"))
-    say("[graph] forward T=3000 H=8")
+    say(f"[graph] forward T={T} H={H} N={N} ({kind})")
     replay_and_check(g, [Yg, fg], [Y0, f0], lambda i: ssd.fwd(Xe, lae, Be, Ce, chunk=128, workspace=ws))
 
 
