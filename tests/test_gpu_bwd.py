@@ -114,6 +114,16 @@ def test_bwd_packed(dt, Q, gs):
     check_bwd(d, Q, f"packed {lengths}", gs=gs, seed=9)
 
 
+def test_bwd_head_pair_state_runs():
+    """More (state block, head) units than one round of the one-head chunk_state:
+    both state runs of the backward take the head-pair form (two heads per
+    workgroup), with state blocks of two chunks (chunk_starts expands them)."""
+    d = synth.make_forward_inputs(1, 2048, 96, 32, 64, 1, dtype=torch.bfloat16, seed=8801)
+    sh = ssd.make_shape(d["X"], d["B"])
+    assert ssd.layout(sh, 128, 2).nblocks * 96 > 512
+    check_bwd(d, 128, "head-pair state runs", gs=2, seed=8802)
+
+
 def test_bwd_long_sequence():
     """T = 4096 with the headline head size and state size (8 heads, 4 state blocks of 8 chunks)."""
     d = synth.make_forward_inputs(1, 4096, 8, 64, 128, 1, dtype=torch.bfloat16, seed=3300)
